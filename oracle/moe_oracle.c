@@ -1,0 +1,369 @@
+/*
+ * CPU oracle for the MoE expert layer on one GPU's share of the experts.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or calls this file:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It shares no code,
+ * header, table or constant with the HIP library.
+ *
+ * It is the plain definition of what the layer computes, written as slow per-token and
+ * per-expert loops in fp64 on the bf16 input values, so that a reader can check it against
+ * the pages by eye:
+ *   - "Mega MoE" page, Pipeline: x -> dispatch + L1 grouped GEMM (NT) -> SwiGLU ->
+ *     L2 grouped GEMM (NT) + combine -> y, where the combine is a top-k weighted
+ *     scatter-add that sums the num_topk contributions of each token.
+ *   - "Mega MoE" page, Implementation Map: a dispatch prologue builds the routing tables.
+ *   - "How Mega MoE Overlaps ..." page, Block-M alignment: each expert's token count is padded
+ *     up to the GEMM block size.
+ *   - "Mega MoE" page, Pipeline (backward): L2 dgrad, SwiGLU transpose, dW2 with a variable K,
+ *     and dW1 (TN) on the recomputed dispatched x.
+ *
+ * Readings where the pages are silent or leave a step open:
+ *   - weights are taken in the logical x @ W layouts W1 [EL, H, 2I] and W2 [EL, I, H];
+ *   - columns [0, I) of the L1 output are the gate, [I, 2I) the up projection,
+ *     a = silu(gate) * up with silu(g) = g / (1 + exp(-g));
+ *   - a pair (t, j) is local when 0 <= id < E and e_lo <= id < e_lo + EL; ids outside
+ *     [0, E) are dropped and counted; a duplicated id gives two independent pairs;
+ *   - rows inside an expert's segment are in ascending pair order p = t * k + j;
+ *   - topk_weights are used as given and applied in the combine;
+ *   - y of a token with no local pair is zero;
+ *   - the backward gradient of the L2 output row of pair p is w_p * dy[t].
+ *
+ * All int32 tables use -1 for "no entry".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16_value(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* Expert slot of a pair, or -1 when the pair is not handled by this GPU. */
+static int local_expert(int32_t id, int E, int e_lo, int EL) {
+    if (id < 0 || id >= E) return -1;
+    int e = id - e_lo;
+    return (e >= 0 && e < EL) ? e : -1;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Row capacity of the tables: all T*k pairs local, plus up to BM-1 padding rows per expert,
+ * rounded up to a whole block. */
+int64_t oracle_rows_capacity(int T, int k, int EL, int BM) {
+    int64_t r = (int64_t)T * k + (int64_t)EL * (BM - 1);
+    return (r + BM - 1) / BM * BM;
+}
+
+/*
+ * Routing tables (dispatch prologue; Block-M alignment).
+ *   counts[EL]            rows of each local expert
+ *   padded_offsets[EL+1]  start row of each expert's segment; segments are padded to BM
+ *   row_pair[R_max]       pair id held by each row, -1 for padding and unused rows
+ *   pair_row[T*k]         row of each pair, -1 for pairs that are not local
+ *   tile_expert[R_max/BM] expert owning each block of BM rows, -1 past the last segment
+ *   tok_nloc[T]           number of local pairs of each token
+ *   meta[0] = padded row total R, meta[1] = number of ids outside [0, E)
+ */
+int oracle_route(int T, int k, int E, int e_lo, int EL, int BM, const int32_t* topk_idx,
+                 int32_t* counts, int32_t* padded_offsets, int32_t* row_pair, int32_t* pair_row,
+                 int32_t* tile_expert, int32_t* tok_nloc, int32_t* meta) {
+    if (T < 0 || k <= 0 || E <= 0 || EL <= 0 || e_lo < 0 || BM <= 0) return -1;
+    const int64_t npairs = (int64_t)T * k;
+    const int64_t R_max = oracle_rows_capacity(T, k, EL, BM);
+
+    int32_t dropped = 0;
+    for (int e = 0; e < EL; ++e) counts[e] = 0;
+    for (int64_t p = 0; p < npairs; ++p) {
+        int32_t id = topk_idx[p];
+        if (id < 0 || id >= E) ++dropped;
+        int e = local_expert(id, E, e_lo, EL);
+        if (e >= 0) ++counts[e];
+    }
+
+    padded_offsets[0] = 0;
+    for (int e = 0; e < EL; ++e) {
+        int32_t padded = (counts[e] + BM - 1) / BM * BM;
+        padded_offsets[e + 1] = padded_offsets[e] + padded;
+    }
+
+    for (int64_t r = 0; r < R_max; ++r) row_pair[r] = -1;
+    int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)EL);
+    if (!next) return -2;
+    for (int e = 0; e < EL; ++e) next[e] = padded_offsets[e];
+    for (int64_t p = 0; p < npairs; ++p) {
+        int e = local_expert(topk_idx[p], E, e_lo, EL);
+        if (e < 0) {
+            pair_row[p] = -1;
+            continue;
+        }
+        int32_t row = next[e]++;
+        row_pair[row] = (int32_t)p;
+        pair_row[p] = row;
+    }
+    free(next);
+
+    for (int64_t m = 0; m < R_max / BM; ++m) {
+        int64_t r0 = m * BM;
+        tile_expert[m] = -1;
+        for (int e = 0; e < EL; ++e)
+            if (padded_offsets[e] <= r0 && r0 < padded_offsets[e + 1]) tile_expert[m] = e;
+    }
+
+    for (int t = 0; t < T; ++t) {
+        int32_t n = 0;
+        for (int j = 0; j < k; ++j) n += local_expert(topk_idx[(int64_t)t * k + j], E, e_lo, EL) >= 0;
+        tok_nloc[t] = n;
+    }
+    meta[0] = padded_offsets[EL];
+    meta[1] = dropped;
+    return 0;
+}
+
+/* L1 row of one pair: h[n] = sum_q x[t,q] * W1[e,q,n] for n < 2I (the dispatched token row
+ * times the expert's [gate | up] weight). */
+static void l1_row(const uint16_t* xrow, const uint16_t* W1e, int H, int I, double* h) {
+    const int N = 2 * I;
+    for (int n = 0; n < N; ++n) h[n] = 0.0;
+    for (int q = 0; q < H; ++q) {
+        const double xq = bf16_value(xrow[q]);
+        const uint16_t* wrow = W1e + (size_t)q * N;
+        for (int n = 0; n < N; ++n) h[n] += xq * bf16_value(wrow[n]);
+    }
+}
+
+/*
+ * Forward for a list of tokens: y[i, :] = sum over local pairs (t_i, j) of
+ *   topk_weights[t_i, j] * ( SwiGLU(x[t_i] @ W1[e]) @ W2[e] ).
+ * y is [ntok, H] fp64.
+ */
+int oracle_forward(int T, int H, int I, int E, int e_lo, int EL, int k, const uint16_t* x,
+                   const int32_t* topk_idx, const float* topk_w, const uint16_t* W1,
+                   const uint16_t* W2, const int32_t* tokens, int ntok, double* y) {
+    if (H <= 0 || I <= 0 || k <= 0) return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        double* o = (double*)malloc(sizeof(double) * (size_t)H);
+        const int ok = h && a && o;
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < ntok; ++i) {
+            if (!ok) continue;
+            {
+                const int t = tokens[i];
+                double* acc = y + (size_t)i * H;
+                for (int m = 0; m < H; ++m) acc[m] = 0.0;
+                if (t < 0 || t >= T) continue;
+                for (int j = 0; j < k; ++j) {
+                    const int e = local_expert(topk_idx[(int64_t)t * k + j], E, e_lo, EL);
+                    if (e < 0) continue;
+                    l1_row(x + (size_t)t * H, W1 + (size_t)e * H * 2 * I, H, I, h);
+                    for (int c = 0; c < I; ++c) a[c] = silu(h[c]) * h[I + c];
+                    for (int m = 0; m < H; ++m) o[m] = 0.0;
+                    const uint16_t* W2e = W2 + (size_t)e * I * H;
+                    for (int c = 0; c < I; ++c) {
+                        const uint16_t* wrow = W2e + (size_t)c * H;
+                        for (int m = 0; m < H; ++m) o[m] += a[c] * bf16_value(wrow[m]);
+                    }
+                    const double w = (double)topk_w[(int64_t)t * k + j];
+                    for (int m = 0; m < H; ++m) acc[m] += w * o[m];
+                }
+            }
+        }
+        free(h);
+        free(a);
+        free(o);
+    }
+    return err;
+}
+
+/* L1 output (pre-activation [gate | up], [npairs_list, 2I]) and its SwiGLU ([.., I]) for a
+ * list of pair ids; rows of non-local pairs are zero. */
+int oracle_l1_rows(int T, int H, int I, int E, int e_lo, int EL, int k, const uint16_t* x,
+                   const int32_t* topk_idx, const uint16_t* W1, const int32_t* pairs, int np,
+                   double* h_out, double* a_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < np; ++i) {
+        double* h = h_out + (size_t)i * 2 * I;
+        double* a = a_out + (size_t)i * I;
+        const int64_t p = pairs[i];
+        const int e = (p >= 0 && p < (int64_t)T * k) ? local_expert(topk_idx[p], E, e_lo, EL) : -1;
+        if (e < 0) {
+            for (int n = 0; n < 2 * I; ++n) h[n] = 0.0;
+            for (int c = 0; c < I; ++c) a[c] = 0.0;
+            continue;
+        }
+        l1_row(x + (size_t)(p / k) * H, W1 + (size_t)e * H * 2 * I, H, I, h);
+        for (int c = 0; c < I; ++c) a[c] = silu(h[c]) * h[I + c];
+    }
+    return 0;
+}
+
+/* SwiGLU on given bf16 [gate | up] rows: a[r, c] = silu(hgu[r, c]) * hgu[r, I + c]. */
+int oracle_swiglu(int64_t nrows, int I, const uint16_t* hgu, double* a) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int c = 0; c < I; ++c)
+            a[r * I + c] = silu(bf16_value(hgu[r * 2 * I + c])) * bf16_value(hgu[r * 2 * I + I + c]);
+    return 0;
+}
+
+/* SwiGLU backward on given bf16 [gate | up] rows and an upstream gradient da [nrows, I]:
+ * with s = sigmoid(g): dgate = da * up * s * (1 + g * (1 - s)), dup = da * g * s. */
+int oracle_swiglu_bwd(int64_t nrows, int I, const uint16_t* hgu, const uint16_t* da,
+                      double* dhgu) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int c = 0; c < I; ++c) {
+            const double g = bf16_value(hgu[r * 2 * I + c]);
+            const double u = bf16_value(hgu[r * 2 * I + I + c]);
+            const double d = bf16_value(da[r * I + c]);
+            const double s = 1.0 / (1.0 + exp(-g));
+            dhgu[r * 2 * I + c] = d * u * s * (1.0 + g * (1.0 - s));
+            dhgu[r * 2 * I + I + c] = d * g * s;
+        }
+    return 0;
+}
+
+/* Backward of one pair: from the upstream gradient dy[t], the L2 dgrad
+ * dA[c] = sum_m (w_p * dy[t, m]) * W2[e, c, m], then the SwiGLU transpose into dHgu [2I]. */
+static void pair_backward(const uint16_t* dyrow, double w, const uint16_t* W2e, int H, int I,
+                          const double* h, double* dO, double* dA, double* dhgu) {
+    for (int m = 0; m < H; ++m) dO[m] = w * bf16_value(dyrow[m]);
+    for (int c = 0; c < I; ++c) {
+        const uint16_t* wrow = W2e + (size_t)c * H;
+        double s = 0.0;
+        for (int m = 0; m < H; ++m) s += dO[m] * bf16_value(wrow[m]);
+        dA[c] = s;
+    }
+    for (int c = 0; c < I; ++c) {
+        const double g = h[c], u = h[I + c];
+        const double sg = 1.0 / (1.0 + exp(-g));
+        dhgu[c] = dA[c] * u * sg * (1.0 + g * (1.0 - sg));
+        dhgu[I + c] = dA[c] * g * sg;
+    }
+}
+
+/* Per-pair backward intermediates for a list of pair ids: dA [np, I], dHgu [np, 2I]. */
+int oracle_backward_rows(int T, int H, int I, int E, int e_lo, int EL, int k,
+                         const uint16_t* x, const int32_t* topk_idx, const float* topk_w,
+                         const uint16_t* W1, const uint16_t* W2, const uint16_t* dy,
+                         const int32_t* pairs, int np, double* dA_out, double* dhgu_out) {
+    int err = 0;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+        double* dO = (double*)malloc(sizeof(double) * (size_t)H);
+        const int ok = h && dO;
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < np; ++i) {
+            if (!ok) continue;
+            {
+                double* dA = dA_out + (size_t)i * I;
+                double* dhgu = dhgu_out + (size_t)i * 2 * I;
+                const int64_t p = pairs[i];
+                const int e = (p >= 0 && p < (int64_t)T * k) ? local_expert(topk_idx[p], E, e_lo, EL) : -1;
+                if (e < 0) {
+                    for (int c = 0; c < I; ++c) dA[c] = 0.0;
+                    for (int n = 0; n < 2 * I; ++n) dhgu[n] = 0.0;
+                    continue;
+                }
+                const int64_t t = p / k;
+                l1_row(x + (size_t)t * H, W1 + (size_t)e * H * 2 * I, H, I, h);
+                pair_backward(dy + (size_t)t * H, (double)topk_w[p], W2 + (size_t)e * I * H, H, I,
+                              h, dO, dA, dhgu);
+            }
+        }
+        free(h);
+        free(dO);
+    }
+    return err;
+}
+
+/*
+ * Weight gradients of a list of local experts (variable K: an expert's K is its row count).
+ *   dW2[e, c, m] = sum over pairs p of e of a_p[c] * (w_p * dy[t_p, m])      [I, H]
+ *   dW1[e, q, n] = sum over pairs p of e of x[t_p, q] * dHgu_p[n]           [H, 2I]
+ * Pairs are accumulated in ascending pair order; an expert with no pair gets exact zeros.
+ * Outputs are [nexp, H, 2I] and [nexp, I, H] fp64, in the logical weight layouts.
+ */
+int oracle_backward(int T, int H, int I, int E, int e_lo, int EL, int k, const uint16_t* x,
+                    const int32_t* topk_idx, const float* topk_w, const uint16_t* W1,
+                    const uint16_t* W2, const uint16_t* dy, const int32_t* experts, int nexp,
+                    double* dW1, double* dW2) {
+    int err = 0;
+    const int64_t npairs = (int64_t)T * k;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        double* dO = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dA = (double*)malloc(sizeof(double) * (size_t)I);
+        double* dhgu = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+        const int ok = h && a && dO && dA && dhgu;
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int s = 0; s < nexp; ++s) {
+            if (!ok) continue;
+            {
+                const int e = experts[s];
+                double* g1 = dW1 + (size_t)s * H * 2 * I;
+                double* g2 = dW2 + (size_t)s * I * H;
+                memset(g1, 0, sizeof(double) * (size_t)H * 2 * I);
+                memset(g2, 0, sizeof(double) * (size_t)I * H);
+                if (e < 0 || e >= EL) continue;
+                for (int64_t p = 0; p < npairs; ++p) {
+                    if (local_expert(topk_idx[p], E, e_lo, EL) != e) continue;
+                    const int64_t t = p / k;
+                    const uint16_t* xrow = x + (size_t)t * H;
+                    l1_row(xrow, W1 + (size_t)e * H * 2 * I, H, I, h);
+                    for (int c = 0; c < I; ++c) a[c] = silu(h[c]) * h[I + c];
+                    pair_backward(dy + (size_t)t * H, (double)topk_w[p], W2 + (size_t)e * I * H,
+                                  H, I, h, dO, dA, dhgu);
+                    for (int c = 0; c < I; ++c) {
+                        double* row = g2 + (size_t)c * H;
+                        for (int m = 0; m < H; ++m) row[m] += a[c] * dO[m];
+                    }
+                    for (int q = 0; q < H; ++q) {
+                        const double xq = bf16_value(xrow[q]);
+                        double* row = g1 + (size_t)q * 2 * I;
+                        for (int n = 0; n < 2 * I; ++n) row[n] += xq * dhgu[n];
+                    }
+                }
+            }
+        }
+        free(h);
+        free(a);
+        free(dO);
+        free(dA);
+        free(dhgu);
+    }
+    return err;
+}
