@@ -1,0 +1,215 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) MoE expert-layer library, one GPU's share of the
+ * experts.
+ *
+ * The layer follows the "Mega MoE" page (Primus-Turbo, docs/README_Mega_MoE.md), section
+ * Pipeline: a dispatch prologue builds routing tables from external top-k routing; the
+ * dispatched token rows go through an L1 grouped GEMM (NT) into a [gate | up] projection;
+ * SwiGLU; an L2 grouped GEMM (NT); and a combine that weights each row by its top-k weight
+ * and sums the contributions of each token (a weighted scatter-add).  The backward entry
+ * points follow the same section's backward: L2 dgrad (NN), the SwiGLU transpose, dW2 with a
+ * variable K (the row count of each expert) and dW1 (TN) on re-gathered token rows, as in
+ * the page's Core Design section 2 (recompute the dispatched x instead of saving it).
+ * Per-expert row counts are padded to the GEMM block (block-M alignment, "How Mega MoE
+ * Overlaps Expert Parallelism Communication with Computation in DeepGEMM" page, section
+ * Block-M Alignment), so every launch has a shape fixed on the host and nothing waits on the
+ * host ("Mega MoE" page, Core Design section 3): every call only enqueues work on `stream`
+ * and returns; the whole sequence can be captured into a HIP graph.
+ *
+ * Conventions shared by all entry points
+ *   - Pointers marked [device] are device addresses; [host] are host addresses.
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ *   - Ownership: the caller owns every buffer (inputs, weights, outputs, workspace) and must
+ *     keep it alive until the enqueued work completes.  The library allocates nothing, frees
+ *     nothing, copies nothing between host and device and keeps no state between calls, so
+ *     calls with distinct workspaces may run concurrently on different streams.
+ *   - Workspace: `ws` is a device buffer of at least moe_workspace_bytes(shape) bytes, 256-B
+ *     aligned.  The stages of one layer communicate through it and rely on stream order:
+ *     moe_route_prologue, then moe_dispatch_gemm1, then moe_gemm2_combine, on one stream.
+ *   - Errors: argument checks run on the host before any launch and return a negative
+ *     moe_status without enqueuing anything.  A launch failure returns MOE_ERR_LAUNCH.
+ *     Data-dependent conditions never trap on the device: an expert id outside [0, E) is
+ *     ignored and counted (moe_workspace_layout().meta, entry 1).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,       /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,      /* a size is out of the supported range */
+    MOE_ERR_BLOCK_M = -3,    /* block_m is not 32, 64, 128 or 256 */
+    MOE_ERR_WORKSPACE = -4,  /* ws_bytes < moe_workspace_bytes(shape), or ws lacks train buffers */
+    MOE_ERR_ALIGN = -5,      /* a pointer is not 16-byte aligned (ws: 256-byte) */
+    MOE_ERR_LAUNCH = -6,     /* the HIP runtime rejected a launch */
+    MOE_ERR_DEVICE = -7      /* the current device is not a gfx950 GPU, or HIP failed */
+} moe_status;
+
+/*
+ * Layer shape (host struct).
+ *   T        tokens on this GPU (>= 0)
+ *   H        hidden size (multiple of 128)
+ *   I        intermediate size; the L1 output is [gate | up], 2*I wide (multiple of 64;
+ *            multiple of 128 for the backward entry points)
+ *   E        experts in routing; ids in [0, E) are valid
+ *   e_lo     first expert owned by this GPU; it owns ids [e_lo, e_lo + EL), e_lo + EL <= E
+ *   EL       experts owned by this GPU (1 .. 1024)
+ *   k        top-k slots per token (1 .. 32)
+ *   block_m  GEMM row block; each expert's row count is padded up to a multiple of it
+ *   train    nonzero: the workspace also holds the activations saved for the backward
+ *            (pre-activation [gate | up] rows) and the backward's row gradients
+ */
+typedef struct moe_shape {
+    int32_t T, H, I, E, e_lo, EL, k, block_m, train;
+} moe_shape;
+
+/*
+ * Workspace layout: byte offsets of each region from the start of `ws`.
+ *   rows_capacity  R_max = round_up(T*k + EL*(block_m - 1), block_m), the static bound on
+ *                  padded rows every row-indexed region and grid is sized from
+ *   counts         int32 [EL]           rows of each local expert
+ *   padded_offsets int32 [EL + 1]       first row of each expert's segment (multiples of block_m)
+ *   row_pair       int32 [R_max]        pair id p = t*k + j held by each row, -1 = padding/unused
+ *   pair_row       int32 [T*k]          row of each pair, -1 = pair not handled by this GPU
+ *   tile_expert    int32 [R_max/block_m] expert of each row block, -1 past the last segment
+ *   tok_nloc       int32 [T]            local pairs of each token
+ *   meta           int32 [4]            [0] padded row total R, [1] ids outside [0, E)
+ *   act            bf16  [R_max, I]     SwiGLU output rows (L2 input)
+ *   stage          fp32  [R_max, H]     weighted L2 rows of tokens with several local pairs
+ *   hgu            bf16  [R_max, 2I]    pre-activation rows (train only, else 0)
+ *   dact           bf16  [R_max, I]     L2 dgrad rows (train only, else 0)
+ *   dhgu           bf16  [R_max, 2I]    [gate | up] gradient rows (train only, else 0)
+ *   scratch        prologue scratch (per-chunk expert histograms)
+ */
+typedef struct moe_ws_layout {
+    size_t total_bytes;
+    int64_t rows_capacity;
+    int64_t num_blocks;
+    size_t counts, padded_offsets, row_pair, pair_row, tile_expert, tok_nloc, meta;
+    size_t act, stage, hgu, dact, dhgu, scratch;
+} moe_ws_layout;
+
+/* Message for a status code (static string). */
+const char* moe_status_string(int32_t status);
+
+/* Pure host functions of the shape. moe_workspace_bytes returns 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape* shape);
+int32_t moe_workspace_layout(const moe_shape* shape, moe_ws_layout* out /* [host] */);
+
+/* A block_m for a shape: the smallest of 64/128/256 whose padding stays small for the mean
+ * rows per expert (the analogue of the block-M query on the "How Mega MoE Overlaps ..." page,
+ * Block-M Alignment).  Returns 64 for an invalid shape. */
+int32_t moe_preferred_block_m(const moe_shape* shape);
+
+/*
+ * One-time weight transform (untimed): the logical x @ W layouts become K-major ("NT")
+ * layouts, as in the weight transform step of the "How Mega MoE Overlaps ..." page's
+ * example.
+ *   w1  [device] bf16 [EL, H, 2I]  ->  w1p [device] bf16 [EL, 2I, H]
+ *   w2  [device] bf16 [EL, I, H]   ->  w2p [device] bf16 [EL, H, I]
+ * Either pair may be NULL/NULL to skip it.
+ */
+int32_t moe_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2,
+                         uint16_t* w1p, uint16_t* w2p, void* stream);
+
+/*
+ * Dispatch prologue ("Mega MoE" page, Implementation Map: routing tables): from topk_idx
+ * [device] int32 [T, k] builds counts, padded_offsets, row_pair, pair_row, tile_expert,
+ * tok_nloc and meta in ws.  Rows inside an expert's segment are in ascending pair order, so
+ * the tables are deterministic.  A pair is local when e_lo <= id < e_lo + EL.
+ */
+int32_t moe_route_prologue(const moe_shape* shape, const int32_t* topk_idx, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Dispatch + L1 grouped GEMM, NT ("Mega MoE" page, Pipeline, dispatch_grouped_gemm): for every
+ * row r of a real block, h[r] = x[row_pair[r] / k] @ W1[e]^T over w1p [device] bf16
+ * [EL, 2I, H], with x [device] bf16 [T, H] gathered through row_pair inside the tile load
+ * (padding rows are zero).  Writes, for rows [0, R):
+ *   act_out [device] bf16 [R_max, I]  = silu(h[:, :I]) * h[:, I:]   (SwiGLU in the epilogue)
+ *   hgu_out [device] bf16 [R_max, 2I] = h                            (pre-activation)
+ * Either output may be NULL, not both.  Pass ws-relative regions (layout act / hgu) to feed
+ * moe_gemm2_combine and the backward.
+ */
+int32_t moe_dispatch_gemm1(const moe_shape* shape, const uint16_t* x, const uint16_t* w1p,
+                           void* ws, size_t ws_bytes, uint16_t* act_out, uint16_t* hgu_out,
+                           void* stream);
+
+/*
+ * SwiGLU ("Mega MoE" page, Pipeline; Implementation Map, SwiGLU fwd): act[r, c] =
+ * silu(hgu[r, c]) * hgu[r, I + c] for rows [0, R) (R read from ws on the device).
+ *   hgu [device] bf16 [R_max, 2I], act [device] bf16 [R_max, I]
+ */
+int32_t moe_swiglu(const moe_shape* shape, const uint16_t* hgu, const void* ws,
+                   size_t ws_bytes, uint16_t* act, void* stream);
+
+/*
+ * L2 grouped GEMM, NT + combine ("Mega MoE" page, Pipeline, grouped_gemm_combine, top-k
+ * reduce as a weighted scatter-add): o[r] = act[r] @ W2[e]^T over w2p [device] bf16
+ * [EL, H, I], then y[t] = sum over the local pairs (t, j) of topk_w[t, j] * o[row of (t, j)],
+ * accumulated in fp32 and written as bf16; tokens with no local pair get y[t] = 0.
+ *   act [device] bf16 [R_max, I]; topk_w [device] fp32 [T, k]; y [device] bf16 [T, H]
+ */
+int32_t moe_gemm2_combine(const moe_shape* shape, const uint16_t* act, const uint16_t* w2p,
+                          const float* topk_w, void* ws, size_t ws_bytes, uint16_t* y,
+                          void* stream);
+
+/*
+ * Fused forward: prologue, dispatch + L1 + SwiGLU, L2 + combine, in one call on one stream.
+ * With shape->train nonzero the pre-activation rows are also kept in ws (layout hgu) for the
+ * backward entry points.
+ *   x [device] bf16 [T, H]; topk_idx [device] int32 [T, k]; topk_w [device] fp32 [T, k];
+ *   w1p [device] bf16 [EL, 2I, H]; w2p [device] bf16 [EL, H, I]; y [device] bf16 [T, H]
+ */
+int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* topk_idx,
+                    const float* topk_w, const uint16_t* w1p, const uint16_t* w2p, void* ws,
+                    size_t ws_bytes, uint16_t* y, void* stream);
+
+/*
+ * Backward entry points ("Mega MoE" page, Pipeline, backward).  They need a workspace with
+ * shape->train nonzero that a moe_forward of the same inputs filled (tables, act, hgu).
+ *
+ * L2 dgrad, NN: dact[r] = topk_w[p] * (dy[t] @ W2[e]) with p = row_pair[r], t = p / k, read
+ * through w2p [EL, H, I] as the [K = H, N = I] operand.  With fuse_swiglu_bwd nonzero the
+ * epilogue applies the SwiGLU transpose and writes ws dhgu directly; else it writes ws dact.
+ *   dy [device] bf16 [T, H]; topk_w [device] fp32 [T, k]
+ */
+int32_t moe_bwd_gemm2_dgrad(const moe_shape* shape, const uint16_t* dy, const float* topk_w,
+                            const uint16_t* w2p, void* ws, size_t ws_bytes,
+                            int32_t fuse_swiglu_bwd, void* stream);
+
+/* SwiGLU transpose ("Mega MoE" page, SwiGLU bwd): from ws dact and ws hgu, with
+ * s = sigmoid(g): dgate = dact * u * s * (1 + g * (1 - s)), dup = dact * g * s -> ws dhgu. */
+int32_t moe_swiglu_bwd(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream);
+
+/* dW2 with variable K ("Mega MoE" page, backward: dW2 (variable-K)):
+ * dw2p[e] [H, I] = sum over rows r of e of (topk_w[p] * dy[t])^T (x) act[r]; K = count of e.
+ * An expert without rows gets exact zeros.  dw2p [device] bf16 [EL, H, I]. */
+int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, const float* topk_w, void* ws,
+                   size_t ws_bytes, uint16_t* dw2p, void* stream);
+
+/* dW1, TN with variable K ("Mega MoE" page, backward: dW1 (TN); Core Design section 2):
+ * dw1p[e] [2I, H] = sum over rows r of e of dhgu[r]^T (x) x[row_pair[r] / k], re-gathering
+ * the token rows instead of saving them.  dw1p [device] bf16 [EL, 2I, H]. */
+int32_t moe_wgrad1(const moe_shape* shape, const uint16_t* x, void* ws, size_t ws_bytes,
+                   uint16_t* dw1p, void* stream);
+
+/* Fused backward: L2 dgrad with the SwiGLU transpose in its epilogue, dW2, dW1. */
+int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* dy,
+                     const float* topk_w, const uint16_t* w2p, void* ws, size_t ws_bytes,
+                     uint16_t* dw1p, uint16_t* dw2p, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

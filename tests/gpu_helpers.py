@@ -1,0 +1,77 @@
+"""Helpers shared by the GPU tests: moving the seeded inputs to the device and running the
+library through its binding.  No arithmetic of the layer lives here."""
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+import token_dispatch_grouped_route_amd as moe
+
+TABLES = ("counts", "padded_offsets", "row_pair", "pair_row", "tile_expert", "tok_nloc")
+
+
+def bf16_dev(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bits_host(t):
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f64_host(t):
+    return t.float().cpu().double().numpy()
+
+
+def rel_max_err(got, ref):
+    """max |got - ref| / rms(ref) over the whole array (the acceptance measure)."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    if rms == 0:
+        return float(np.max(np.abs(got))) if got.size else 0.0
+    return float(np.max(np.abs(got - ref)) / rms)
+
+
+def layer(w, d, block_m, train=False, weights=True):
+    """Device copies of the inputs, packed weights, a workspace and the output buffer."""
+    shape = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=block_m, e_lo=w.e_lo, train=train)
+    ns = SimpleNamespace(w=w, shape=shape)
+    ns.idx = torch.from_numpy(np.ascontiguousarray(d["topk_idx"], np.int32)).cuda()
+    ns.wts = torch.from_numpy(np.ascontiguousarray(d["topk_weights"], np.float32)).cuda()
+    ns.x = bf16_dev(d["x"])
+    if "dy" in d:
+        ns.dy = bf16_dev(d["dy"])
+    if weights:
+        ns.W1p = torch.empty(w.EL, 2 * w.I, w.H, dtype=torch.bfloat16, device="cuda")
+        ns.W2p = torch.empty(w.EL, w.H, w.I, dtype=torch.bfloat16, device="cuda")
+        W1, W2 = bf16_dev(d["W1"]), bf16_dev(d["W2"])
+        moe.pack_weights(shape, W1, W2, ns.W1p, ns.W2p)
+        del W1, W2
+    ns.ws = moe.alloc_workspace(shape)
+    ns.y = torch.full((w.T, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    return ns
+
+
+def tables(ns):
+    t = {n: moe.ws_region(ns.ws, ns.shape, n).cpu().numpy() for n in TABLES}
+    meta = moe.ws_region(ns.ws, ns.shape, "meta").cpu().numpy()
+    t["num_rows"], t["dropped"] = int(meta[0]), int(meta[1])
+    return t
+
+
+def assert_tables_equal(got, ref):
+    for n in TABLES:
+        assert np.array_equal(got[n], ref[n]), "table %s differs" % n
+    assert got["num_rows"] == ref["num_rows"] and got["dropped"] == ref["dropped"]
+
+
+def sample_tokens(tok_nloc, n, seed=0):
+    """Tokens to compare at full size: some with no, one and several local pairs, plus the
+    first and last token."""
+    rng = np.random.default_rng(seed)
+    T = len(tok_nloc)
+    pick = {0, T - 1}
+    for cls in (tok_nloc == 0, tok_nloc == 1, tok_nloc >= 2):
+        ids = np.nonzero(cls)[0]
+        if len(ids):
+            pick.update(rng.choice(ids, size=min(len(ids), n // 3), replace=False).tolist())
+    return np.array(sorted(pick), np.int64)

@@ -1,0 +1,239 @@
+"""MoE expert layer (one GPU's share of the experts) on MI355X / gfx950.
+
+A thin binding over the C ABI of ``libmoe_gfx950.so`` (declared in ``include/moe.h``): every
+function here only checks tensor dtypes/devices and passes ``data_ptr()`` values and the HIP
+stream to the function of the same name (``moe_`` prefix) in the library.  All arithmetic runs
+in the library's HIP kernels; there is no fallback.  PyTorch is used for device memory and
+streams only.
+
+Pipeline ("Mega MoE" page, Pipeline): route_prologue -> dispatch_gemm1 (gather + L1 NT +
+SwiGLU) -> gemm2_combine (L2 NT + top-k weighted scatter-add), or ``forward`` for all of it;
+the backward entry points follow the page's backward (L2 dgrad NN, SwiGLU transpose, dW2 and
+dW1 with a variable K).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that the library then shares (same soname)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
+_lib = None
+
+ENTRY_POINTS = (
+    "moe_status_string", "moe_workspace_bytes", "moe_workspace_layout", "moe_preferred_block_m",
+    "moe_pack_weights", "moe_route_prologue", "moe_dispatch_gemm1", "moe_swiglu",
+    "moe_gemm2_combine", "moe_forward", "moe_bwd_gemm2_dgrad", "moe_swiglu_bwd", "moe_wgrad2",
+    "moe_wgrad1", "moe_backward",
+)
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "I", "E", "e_lo", "EL", "k", "block_m", "train")]
+
+    def __repr__(self):
+        return "Shape(%s)" % ", ".join("%s=%d" % (n, getattr(self, n)) for n, _ in self._fields_)
+
+
+_LAYOUT_FIELDS = ("counts", "padded_offsets", "row_pair", "pair_row", "tile_expert", "tok_nloc",
+                  "meta", "act", "stage", "hgu", "dact", "dhgu", "scratch")
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = ([("total_bytes", ctypes.c_size_t), ("rows_capacity", ctypes.c_int64),
+                 ("num_blocks", ctypes.c_int64)] + [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS])
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError("HIP library %s is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, i32 = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_int32
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [i32]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_bytes.argtypes = [S]
+        L.moe_workspace_layout.argtypes = [S, ctypes.POINTER(WsLayout)]
+        L.moe_preferred_block_m.argtypes = [S]
+        L.moe_pack_weights.argtypes = [S, P, P, P, P, P]
+        L.moe_route_prologue.argtypes = [S, P, P, ctypes.c_size_t, P]
+        L.moe_dispatch_gemm1.argtypes = [S, P, P, P, ctypes.c_size_t, P, P, P]
+        L.moe_swiglu.argtypes = [S, P, P, ctypes.c_size_t, P, P]
+        L.moe_gemm2_combine.argtypes = [S, P, P, P, P, ctypes.c_size_t, P, P]
+        L.moe_forward.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P, P]
+        L.moe_bwd_gemm2_dgrad.argtypes = [S, P, P, P, P, ctypes.c_size_t, i32, P]
+        L.moe_swiglu_bwd.argtypes = [S, P, ctypes.c_size_t, P]
+        L.moe_wgrad2.argtypes = [S, P, P, P, ctypes.c_size_t, P, P]
+        L.moe_wgrad1.argtypes = [S, P, P, ctypes.c_size_t, P, P]
+        L.moe_backward.argtypes = [S, P, P, P, P, P, ctypes.c_size_t, P, P, P]
+        for n in ENTRY_POINTS[2:]:
+            if n != "moe_workspace_bytes":
+                getattr(L, n).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MoeError("%s: %s (%d)" % (what, lib().moe_status_string(status).decode(), status))
+
+
+def _ptr(t, dtype, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise MoeError("%s must be a contiguous %s tensor on a GPU" % (name, dtype))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ws(ws):
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise MoeError("ws must be a contiguous GPU tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def make_shape(T, H, I, E, EL, k, block_m=None, e_lo=0, train=False) -> Shape:
+    s = Shape(T, H, I, E, e_lo, EL, k, 0, int(bool(train)))
+    s.block_m = block_m if block_m is not None else preferred_block_m(s)
+    return s
+
+
+def preferred_block_m(shape: Shape) -> int:
+    return int(lib().moe_preferred_block_m(ctypes.byref(shape)))
+
+
+def workspace_bytes(shape: Shape) -> int:
+    n = int(lib().moe_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        raise MoeError("invalid shape %r" % (shape,))
+    return n
+
+
+def workspace_layout(shape: Shape) -> dict:
+    L = WsLayout()
+    _check(lib().moe_workspace_layout(ctypes.byref(shape), ctypes.byref(L)), "moe_workspace_layout")
+    return {n: getattr(L, n) for n, _ in WsLayout._fields_}
+
+
+def alloc_workspace(shape: Shape, device="cuda") -> torch.Tensor:
+    """A workspace tensor for the shape (torch's allocator returns 512-byte aligned blocks)."""
+    return torch.empty(workspace_bytes(shape), dtype=torch.uint8, device=device)
+
+
+_REGION = {  # name -> (dtype, row width in elements or None)
+    "counts": (torch.int32, None), "padded_offsets": (torch.int32, None),
+    "row_pair": (torch.int32, None), "pair_row": (torch.int32, None),
+    "tile_expert": (torch.int32, None), "tok_nloc": (torch.int32, None), "meta": (torch.int32, None),
+    "act": (torch.bfloat16, "I"), "stage": (torch.float32, "H"), "hgu": (torch.bfloat16, "2I"),
+    "dact": (torch.bfloat16, "I"), "dhgu": (torch.bfloat16, "2I"),
+}
+
+
+def ws_region(ws: torch.Tensor, shape: Shape, name: str) -> torch.Tensor:
+    """A typed view of one workspace region (no copy)."""
+    L = workspace_layout(shape)
+    R = L["rows_capacity"]
+    sizes = {"counts": shape.EL, "padded_offsets": shape.EL + 1, "row_pair": R,
+             "pair_row": shape.T * shape.k, "tile_expert": L["num_blocks"], "tok_nloc": shape.T,
+             "meta": 4}
+    dtype, width = _REGION[name]
+    if width is None:
+        n, view = sizes[name], None
+    else:
+        if name in ("hgu", "dact", "dhgu") and not shape.train:
+            raise MoeError("region %s exists only for train shapes" % name)
+        cols = {"I": shape.I, "H": shape.H, "2I": 2 * shape.I}[width]
+        n, view = R * cols, (R, cols)
+    esz = torch.tensor([], dtype=dtype).element_size()
+    t = ws[L[name]:L[name] + n * esz].view(dtype)
+    return t.view(*view) if view else t
+
+
+def pack_weights(shape, w1=None, w2=None, w1p=None, w2p=None, stream=None):
+    _check(lib().moe_pack_weights(ctypes.byref(shape), _ptr(w1, torch.bfloat16, "w1"),
+                                  _ptr(w2, torch.bfloat16, "w2"), _ptr(w1p, torch.bfloat16, "w1p"),
+                                  _ptr(w2p, torch.bfloat16, "w2p"), _stream(stream)), "moe_pack_weights")
+
+
+def route_prologue(shape, topk_idx, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_route_prologue(ctypes.byref(shape), _ptr(topk_idx, torch.int32, "topk_idx"), p, n,
+                                    _stream(stream)), "moe_route_prologue")
+
+
+def dispatch_gemm1(shape, x, w1p, ws, act_out=None, hgu_out=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_dispatch_gemm1(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"),
+                                    _ptr(w1p, torch.bfloat16, "w1p"), p, n,
+                                    _ptr(act_out, torch.bfloat16, "act_out"),
+                                    _ptr(hgu_out, torch.bfloat16, "hgu_out"), _stream(stream)),
+           "moe_dispatch_gemm1")
+
+
+def swiglu(shape, hgu, ws, act, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_swiglu(ctypes.byref(shape), _ptr(hgu, torch.bfloat16, "hgu"), p, n,
+                            _ptr(act, torch.bfloat16, "act"), _stream(stream)), "moe_swiglu")
+
+
+def gemm2_combine(shape, act, w2p, topk_w, ws, y, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_gemm2_combine(ctypes.byref(shape), _ptr(act, torch.bfloat16, "act"),
+                                   _ptr(w2p, torch.bfloat16, "w2p"), _ptr(topk_w, torch.float32, "topk_w"),
+                                   p, n, _ptr(y, torch.bfloat16, "y"), _stream(stream)), "moe_gemm2_combine")
+
+
+def forward(shape, x, topk_idx, topk_w, w1p, w2p, ws, y, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_forward(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"),
+                             _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_w, torch.float32, "topk_w"),
+                             _ptr(w1p, torch.bfloat16, "w1p"), _ptr(w2p, torch.bfloat16, "w2p"), p, n,
+                             _ptr(y, torch.bfloat16, "y"), _stream(stream)), "moe_forward")
+
+
+def bwd_gemm2_dgrad(shape, dy, topk_w, w2p, ws, fuse_swiglu_bwd=True, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_bwd_gemm2_dgrad(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy"),
+                                     _ptr(topk_w, torch.float32, "topk_w"), _ptr(w2p, torch.bfloat16, "w2p"),
+                                     p, n, int(bool(fuse_swiglu_bwd)), _stream(stream)), "moe_bwd_gemm2_dgrad")
+
+
+def swiglu_bwd(shape, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_swiglu_bwd(ctypes.byref(shape), p, n, _stream(stream)), "moe_swiglu_bwd")
+
+
+def wgrad2(shape, dy, topk_w, ws, dw2p, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_wgrad2(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy"),
+                            _ptr(topk_w, torch.float32, "topk_w"), p, n, _ptr(dw2p, torch.bfloat16, "dw2p"),
+                            _stream(stream)), "moe_wgrad2")
+
+
+def wgrad1(shape, x, ws, dw1p, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_wgrad1(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"), p, n,
+                            _ptr(dw1p, torch.bfloat16, "dw1p"), _stream(stream)), "moe_wgrad1")
+
+
+def backward(shape, x, dy, topk_w, w2p, ws, dw1p, dw2p, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_backward(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"), _ptr(dy, torch.bfloat16, "dy"),
+                              _ptr(topk_w, torch.float32, "topk_w"), _ptr(w2p, torch.bfloat16, "w2p"), p, n,
+                              _ptr(dw1p, torch.bfloat16, "dw1p"), _ptr(dw2p, torch.bfloat16, "dw2p"),
+                              _stream(stream)), "moe_backward")

@@ -1,0 +1,302 @@
+// C ABI of the gfx950 MoE expert-layer library: argument checks, workspace layout and stage
+// launches on the caller's stream.  Declarations and the meaning of every argument are in
+// include/moe.h.  No entry point allocates, frees, copies to or from the host, or waits.
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int32_t check_shape(const moe_shape* s) {
+    if (!s) return MOE_ERR_NULL;
+    if (s->block_m != 32 && s->block_m != 64 && s->block_m != 128 && s->block_m != 256) return MOE_ERR_BLOCK_M;
+    if (s->T < 0 || s->H <= 0 || s->I <= 0 || s->E <= 0 || s->EL < 1 || s->EL > 1024 || s->e_lo < 0 ||
+        s->k < 1 || s->k > 32)
+        return MOE_ERR_SHAPE;
+    if (static_cast<int64_t>(s->e_lo) + s->EL > s->E) return MOE_ERR_SHAPE;
+    if (s->H % 128 != 0 || s->I % 64 != 0) return MOE_ERR_SHAPE;
+    if (s->train && s->I % 128 != 0) return MOE_ERR_SHAPE;
+    // row and element indices stay far inside int32 / int64 ranges
+    const int64_t rows = static_cast<int64_t>(s->T) * s->k + static_cast<int64_t>(s->EL) * s->block_m;
+    if (rows > (int64_t(1) << 28) || s->H > (1 << 20) || s->I > (1 << 20)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int32_t layout_of(const moe_shape* s, moe_ws_layout* L) {
+    const int32_t st = check_shape(s);
+    if (st != MOE_OK) return st;
+    memset(L, 0, sizeof(*L));
+    const int64_t BM = s->block_m;
+    const int64_t pairs = static_cast<int64_t>(s->T) * s->k;
+    const int64_t R = (pairs + static_cast<int64_t>(s->EL) * (BM - 1) + BM - 1) / BM * BM;
+    const int64_t chunks = pairs > 0 ? (pairs + kRouteChunk - 1) / kRouteChunk : 1;
+    const size_t H = s->H, I = s->I, EL = s->EL;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L->rows_capacity = R;
+    L->num_blocks = R / BM;
+    L->counts = take(4 * EL);
+    L->padded_offsets = take(4 * (EL + 1));
+    L->row_pair = take(4 * static_cast<size_t>(R));
+    L->pair_row = take(4 * static_cast<size_t>(pairs));
+    L->tile_expert = take(4 * static_cast<size_t>(R / BM));
+    L->tok_nloc = take(4 * static_cast<size_t>(s->T));
+    L->meta = take(16);
+    L->act = take(2 * static_cast<size_t>(R) * I);
+    L->stage = take(4 * static_cast<size_t>(R) * H);
+    if (s->train) {
+        L->hgu = take(2 * static_cast<size_t>(R) * 2 * I);
+        L->dact = take(2 * static_cast<size_t>(R) * I);
+        L->dhgu = take(2 * static_cast<size_t>(R) * 2 * I);
+    }
+    L->scratch = take(4 * static_cast<size_t>(chunks) * (EL + 1));
+    L->total_bytes = off;
+    return MOE_OK;
+}
+
+bool is_gfx950() {
+    static int cached[64] = {0};   // 0 unknown, 1 yes, 2 no
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    if (!cached[dev]) {
+        hipDeviceProp_t prop;
+        bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                  strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        cached[dev] = ok ? 1 : 2;
+    }
+    return cached[dev] == 1;
+}
+
+// Shared preamble of every device entry point: shape, workspace size/alignment, device.
+int32_t prepare(const moe_shape* s, const void* ws, size_t ws_bytes, bool need_train, Dims* d, Ws* w,
+                moe_ws_layout* L) {
+    const int32_t st = layout_of(s, L);
+    if (st != MOE_OK) return st;
+    if (!ws) return MOE_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kWsAlign - 1)) != 0) return MOE_ERR_ALIGN;
+    if (ws_bytes < L->total_bytes) return MOE_ERR_WORKSPACE;
+    if (need_train && !s->train) return MOE_ERR_WORKSPACE;
+    if (!is_gfx950()) return MOE_ERR_DEVICE;
+    *d = Dims{s->T, s->H, s->I, s->E, s->e_lo, s->EL, s->k, s->block_m};
+    char* b = static_cast<char*>(const_cast<void*>(ws));
+    w->counts = reinterpret_cast<int32_t*>(b + L->counts);
+    w->offsets = reinterpret_cast<int32_t*>(b + L->padded_offsets);
+    w->row_pair = reinterpret_cast<int32_t*>(b + L->row_pair);
+    w->pair_row = reinterpret_cast<int32_t*>(b + L->pair_row);
+    w->tile_expert = reinterpret_cast<int32_t*>(b + L->tile_expert);
+    w->tok_nloc = reinterpret_cast<int32_t*>(b + L->tok_nloc);
+    w->meta = reinterpret_cast<int32_t*>(b + L->meta);
+    w->act = reinterpret_cast<uint16_t*>(b + L->act);
+    w->stage = reinterpret_cast<float*>(b + L->stage);
+    w->hgu = s->train ? reinterpret_cast<uint16_t*>(b + L->hgu) : nullptr;
+    w->dact = s->train ? reinterpret_cast<uint16_t*>(b + L->dact) : nullptr;
+    w->dhgu = s->train ? reinterpret_cast<uint16_t*>(b + L->dhgu) : nullptr;
+    const int64_t pairs = static_cast<int64_t>(s->T) * s->k;
+    w->num_chunks = static_cast<int32_t>(pairs > 0 ? (pairs + kRouteChunk - 1) / kRouteChunk : 1);
+    w->chunk_hist = reinterpret_cast<int32_t*>(b + L->scratch);
+    w->chunk_dropped = w->chunk_hist + static_cast<int64_t>(w->num_chunks) * s->EL;
+    w->rows_cap = L->rows_capacity;
+    w->num_blocks = static_cast<int32_t>(L->num_blocks);
+    return MOE_OK;
+}
+
+int32_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "a size is out of the supported range";
+        case MOE_ERR_BLOCK_M: return "block_m must be 32, 64, 128 or 256";
+        case MOE_ERR_WORKSPACE: return "workspace too small or without the train buffers";
+        case MOE_ERR_ALIGN: return "misaligned pointer (16 bytes; workspace 256 bytes)";
+        case MOE_ERR_LAUNCH: return "kernel launch failed";
+        case MOE_ERR_DEVICE: return "current device is not gfx950 or HIP failed";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+    moe_ws_layout L;
+    return layout_of(shape, &L) == MOE_OK ? L.total_bytes : 0;
+}
+
+int32_t moe_workspace_layout(const moe_shape* shape, moe_ws_layout* out) {
+    if (!out) return MOE_ERR_NULL;
+    return layout_of(shape, out);
+}
+
+int32_t moe_preferred_block_m(const moe_shape* s) {
+    if (!s || s->E <= 0 || s->T < 0 || s->k < 1) return 64;
+    // mean rows per expert under uniform routing; a block at most half that keeps the expected
+    // padding of each segment (half a block) under about a quarter of its rows
+    const double mean = static_cast<double>(s->T) * s->k / s->E;
+    if (mean >= 512) return 256;
+    if (mean >= 256) return 128;
+    return 64;
+}
+
+int32_t moe_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2, uint16_t* w1p,
+                         uint16_t* w2p, void* stream) {
+    const int32_t st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if ((w1 == nullptr) != (w1p == nullptr) || (w2 == nullptr) != (w2p == nullptr)) return MOE_ERR_NULL;
+    if ((w1 && w1 == w1p) || (w2 && w2 == w2p)) return MOE_ERR_SHAPE;   // no in-place transpose
+    if (!is_gfx950()) return MOE_ERR_DEVICE;
+    const Dims d{shape->T, shape->H, shape->I, shape->E, shape->e_lo, shape->EL, shape->k, shape->block_m};
+    return launched(launch_pack(d, w1, w2, w1p, w2p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_route_prologue(const moe_shape* shape, const int32_t* topk_idx, void* ws, size_t ws_bytes,
+                           void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!topk_idx && shape->T > 0) return MOE_ERR_NULL;
+    if (!aligned4(topk_idx)) return MOE_ERR_ALIGN;
+    return launched(launch_route(d, topk_idx, w, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_dispatch_gemm1(const moe_shape* shape, const uint16_t* x, const uint16_t* w1p, void* ws,
+                           size_t ws_bytes, uint16_t* act_out, uint16_t* hgu_out, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if ((!x && shape->T > 0) || !w1p || (!act_out && !hgu_out)) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w1p) || !aligned16(act_out) || !aligned16(hgu_out)) return MOE_ERR_ALIGN;
+    return launched(launch_gemm1(d, x, w1p, w, act_out, hgu_out, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_swiglu(const moe_shape* shape, const uint16_t* hgu, const void* ws, size_t ws_bytes, uint16_t* act,
+                   void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!hgu || !act) return MOE_ERR_NULL;
+    if (!aligned16(hgu) || !aligned16(act)) return MOE_ERR_ALIGN;
+    return launched(launch_swiglu(d, hgu, w, act, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_gemm2_combine(const moe_shape* shape, const uint16_t* act, const uint16_t* w2p, const float* topk_w,
+                          void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!act || !w2p || ((!topk_w || !y) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(act) || !aligned16(w2p) || !aligned4(topk_w) || !aligned16(y)) return MOE_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_gemm2_combine(d, act, w2p, topk_w, w, y, s);
+    if (e == hipSuccess) e = launch_combine_finish(d, w, y, s);
+    return launched(e);
+}
+
+int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* topk_idx, const float* topk_w,
+                    const uint16_t* w1p, const uint16_t* w2p, void* ws, size_t ws_bytes, uint16_t* y,
+                    void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!w1p || !w2p || ((!x || !topk_idx || !topk_w || !y) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned16(w1p) || !aligned16(w2p) ||
+        !aligned16(y))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_route(d, topk_idx, w, s);
+    if (e == hipSuccess) e = launch_gemm1(d, x, w1p, w, w.act, w.hgu, s);
+    if (e == hipSuccess) e = launch_gemm2_combine(d, w.act, w2p, topk_w, w, y, s);
+    if (e == hipSuccess) e = launch_combine_finish(d, w, y, s);
+    return launched(e);
+}
+
+int32_t moe_bwd_gemm2_dgrad(const moe_shape* shape, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
+                            void* ws, size_t ws_bytes, int32_t fuse_swiglu_bwd, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!w2p || ((!dy || !topk_w) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(dy) || !aligned4(topk_w) || !aligned16(w2p)) return MOE_ERR_ALIGN;
+    return launched(launch_dgrad(d, dy, topk_w, w2p, w, fuse_swiglu_bwd != 0, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_swiglu_bwd(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    return launched(launch_swiglu_bwd(d, w, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, const float* topk_w, void* ws, size_t ws_bytes,
+                   uint16_t* dw2p, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!dw2p || ((!dy || !topk_w) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(dy) || !aligned4(topk_w) || !aligned16(dw2p)) return MOE_ERR_ALIGN;
+    return launched(launch_wgrad2(d, dy, topk_w, w, dw2p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_wgrad1(const moe_shape* shape, const uint16_t* x, void* ws, size_t ws_bytes, uint16_t* dw1p,
+                   void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!dw1p || (!x && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(dw1p)) return MOE_ERR_ALIGN;
+    return launched(launch_wgrad1(d, x, w, dw1p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* dy, const float* topk_w,
+                     const uint16_t* w2p, void* ws, size_t ws_bytes, uint16_t* dw1p, uint16_t* dw2p,
+                     void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!w2p || !dw1p || !dw2p || ((!x || !dy || !topk_w) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(dy) || !aligned4(topk_w) || !aligned16(w2p) || !aligned16(dw1p) ||
+        !aligned16(dw2p))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_dgrad(d, dy, topk_w, w2p, w, 1, s);
+    if (e == hipSuccess) e = launch_wgrad2(d, dy, topk_w, w, dw2p, s);
+    if (e == hipSuccess) e = launch_wgrad1(d, x, w, dw1p, s);
+    return launched(e);
+}
+
+}  // extern "C"

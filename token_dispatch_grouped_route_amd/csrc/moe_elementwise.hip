@@ -1,0 +1,162 @@
+// Memory-bound kernels of the MoE expert layer: the one-time weight transform, the standalone
+// SwiGLU forward and backward ("Mega MoE" page, Implementation Map: SwiGLU fwd/bwd), and the
+// last step of the combine (top-k reduce, "Mega MoE" page, Pipeline).  All use 16-byte
+// vector accesses on contiguous rows; row counts that depend on the routing are read from the
+// workspace on the device.
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// Weight transform: [EL, R, C] -> [EL, C, R] (bf16), 64 x 64 tiles through LDS.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in,
+                                                        uint16_t* __restrict__ out, int R, int C) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int e = blockIdx.z;
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const uint16_t* src = in + static_cast<int64_t>(e) * R * C;
+    uint16_t* dst = out + static_cast<int64_t>(e) * R * C;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4)
+        if (r0 + r < R && c0 + tx < C) tile[r][tx] = src[static_cast<int64_t>(r0 + r) * C + c0 + tx];
+    __syncthreads();
+    for (int c = ty; c < 64; c += 4)
+        if (c0 + c < C && r0 + tx < R) dst[static_cast<int64_t>(c0 + c) * R + r0 + tx] = tile[tx][c];
+}
+
+hipError_t launch_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, uint16_t* w1p,
+                       uint16_t* w2p, hipStream_t s) {
+    if (w1 && w1p) {   // [EL, H, 2I] -> [EL, 2I, H]
+        dim3 g((2 * d.I + 63) / 64, (d.H + 63) / 64, d.EL);
+        transpose_kernel<<<g, 256, 0, s>>>(w1, w1p, d.H, 2 * d.I);
+    }
+    if (w2 && w2p) {   // [EL, I, H] -> [EL, H, I]
+        dim3 g((d.H + 63) / 64, (d.I + 63) / 64, d.EL);
+        transpose_kernel<<<g, 256, 0, s>>>(w2, w2p, d.I, d.H);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// SwiGLU forward / backward over rows [0, R)
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+constexpr int kEwThreads = 256;
+
+__global__ __launch_bounds__(kEwThreads) void swiglu_kernel(const uint16_t* __restrict__ hgu, Dims d, Ws ws,
+                                                            uint16_t* __restrict__ act) {
+    const int64_t R = ws.meta[0];
+    const int v8 = d.I / 8;
+    const int64_t n = R * v8;
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < n;
+         q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t r = q / v8;
+        const int c = static_cast<int>(q - r * v8) * 8;
+        float g[8], u[8], a[8];
+        unpack8(*reinterpret_cast<const uint4*>(hgu + r * 2 * d.I + c), g);
+        unpack8(*reinterpret_cast<const uint4*>(hgu + r * 2 * d.I + d.I + c), u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = silu_f32(g[i]) * u[i];
+        *reinterpret_cast<uint4*>(act + r * d.I + c) = pack8(a);
+    }
+}
+
+__global__ __launch_bounds__(kEwThreads) void swiglu_bwd_kernel(Dims d, Ws ws) {
+    const int64_t R = ws.meta[0];
+    const int v8 = d.I / 8;
+    const int64_t n = R * v8;
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < n;
+         q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t r = q / v8;
+        const int c = static_cast<int>(q - r * v8) * 8;
+        float g[8], u[8], da[8], dg[8], du[8];
+        unpack8(*reinterpret_cast<const uint4*>(ws.hgu + r * 2 * d.I + c), g);
+        unpack8(*reinterpret_cast<const uint4*>(ws.hgu + r * 2 * d.I + d.I + c), u);
+        unpack8(*reinterpret_cast<const uint4*>(ws.dact + r * d.I + c), da);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float sg = 1.0f / (1.0f + __expf(-g[i]));
+            dg[i] = da[i] * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
+            du[i] = da[i] * g[i] * sg;
+        }
+        *reinterpret_cast<uint4*>(ws.dhgu + r * 2 * d.I + c) = pack8(dg);
+        *reinterpret_cast<uint4*>(ws.dhgu + r * 2 * d.I + d.I + c) = pack8(du);
+    }
+}
+
+static int ew_grid(int64_t rows_cap, int per_row_vectors) {
+    const int64_t want = (rows_cap * per_row_vectors + kEwThreads - 1) / kEwThreads;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+    return static_cast<int>(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+hipError_t launch_swiglu(const Dims& d, const uint16_t* hgu, const Ws& ws, uint16_t* act, hipStream_t s) {
+    swiglu_kernel<<<ew_grid(ws.rows_cap, d.I / 8), kEwThreads, 0, s>>>(hgu, d, ws, act);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s) {
+    swiglu_bwd_kernel<<<ew_grid(ws.rows_cap, d.I / 8), kEwThreads, 0, s>>>(d, ws);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Combine finish: y rows of tokens with no local pair are zero; tokens with several local pairs
+// sum their weighted fp32 L2 rows from ws.stage in slot order and store bf16.  Tokens with one
+// local pair were written by the L2 epilogue and are left alone.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws ws, uint16_t* __restrict__ y) {
+    __shared__ int s_rows[32];
+    __shared__ int s_n;
+    const int v8 = d.H / 8;
+    for (int t = blockIdx.x; t < d.T; t += gridDim.x) {
+        const int nloc = ws.tok_nloc[t];   // uniform per block
+        if (nloc == 1) continue;
+        __syncthreads();   // the previous token's s_rows are no longer read
+        if (threadIdx.x == 0) {
+            int n = 0;
+            for (int j = 0; j < d.k; ++j) {
+                const int r = ws.pair_row[static_cast<int64_t>(t) * d.k + j];
+                if (r >= 0) s_rows[n++] = r;
+            }
+            s_n = n;
+        }
+        __syncthreads();
+        const int n = s_n;
+        for (int c = threadIdx.x; c < v8; c += blockDim.x) {
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int i = 0; i < n; ++i) {
+                const float4* src = reinterpret_cast<const float4*>(ws.stage + static_cast<int64_t>(s_rows[i]) * d.H + 8 * c);
+                const float4 lo = src[0], hi = src[1];
+                acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+                acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+            }
+            *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * d.H + 8 * c) = pack8(acc);
+        }
+    }
+}
+
+hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s) {
+    if (d.T <= 0) return hipSuccess;
+    const int cap = device_cu_count() * 8;
+    combine_finish_kernel<<<d.T < cap ? d.T : cap, kEwThreads, 0, s>>>(d, ws, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,74 @@
+// Internal declarations of the gfx950 MoE expert-layer library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Layer sizes as the kernels see them.
+struct Dims {
+    int32_t T, H, I, E, e_lo, EL, k, BM;
+};
+
+// Device addresses of the workspace regions (host-computed from moe_ws_layout).
+struct Ws {
+    int32_t* counts;
+    int32_t* offsets;       // padded_offsets [EL + 1]
+    int32_t* row_pair;      // [R_max]
+    int32_t* pair_row;      // [T * k]
+    int32_t* tile_expert;   // [R_max / BM]
+    int32_t* tok_nloc;      // [T]
+    int32_t* meta;          // [0] R (padded rows), [1] dropped ids
+    int32_t* chunk_hist;    // [num_chunks, EL] per-chunk expert counts, then exclusive bases
+    int32_t* chunk_dropped; // [num_chunks]
+    uint16_t* act;          // bf16 [R_max, I]
+    float* stage;           // fp32 [R_max, H]
+    uint16_t* hgu;          // bf16 [R_max, 2I] (train)
+    uint16_t* dact;         // bf16 [R_max, I]  (train)
+    uint16_t* dhgu;         // bf16 [R_max, 2I] (train)
+    int64_t rows_cap;
+    int32_t num_blocks;     // R_max / BM
+    int32_t num_chunks;     // prologue chunks of kRouteChunk pairs
+};
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteChunk = 2048;   // pairs per prologue block
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {   // round to nearest even
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+// Host launchers (each returns a hipError_t from the launch).
+hipError_t launch_route(const Dims& d, const int32_t* topk_idx, const Ws& ws, hipStream_t s);
+hipError_t launch_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, uint16_t* w1p,
+                       uint16_t* w2p, hipStream_t s);
+hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
+                        uint16_t* act_out, uint16_t* hgu_out, hipStream_t s);
+hipError_t launch_swiglu(const Dims& d, const uint16_t* hgu, const Ws& ws, uint16_t* act,
+                         hipStream_t s);
+hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16_t* w2p,
+                                const float* topk_w, const Ws& ws, uint16_t* y, hipStream_t s);
+hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s);
+hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w,
+                        const uint16_t* w2p, const Ws& ws, int fuse_swiglu_bwd, hipStream_t s);
+hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s);
+hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
+                         uint16_t* dw2p, hipStream_t s);
+hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p,
+                         hipStream_t s);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,193 @@
+// Dispatch prologue: routing tables from external top-k routing ("Mega MoE" page,
+// Implementation Map: dispatch prologue (routing tables); block-M padding from the
+// "How Mega MoE Overlaps ..." page, Block-M Alignment).
+//
+// Three launches, all with fixed grids, none waiting on the host:
+//   1. count: each block histograms the experts of one chunk of kRouteChunk pairs (LDS
+//      counters) and counts the local pairs of a slice of tokens.
+//   2. scan (one block): per expert, an exclusive scan over chunks gives each chunk's base
+//      inside the expert; a block-wide scan of the padded counts gives the segment offsets;
+//      then the block -> expert map and the meta counters.
+//   3. place: each block re-reads its chunk in pair order, 256 pairs at a time.  Inside a
+//      wavefront, pairs with the same expert are grouped with ballots (the wave-level
+//      histogram), giving each pair its rank among earlier lanes; the per-wave counts are
+//      prefix-summed across the block's waves in LDS.  So a pair's row is
+//      offset[e] + (pairs of e in earlier chunks) + (in earlier sub-steps) + (in earlier
+//      waves) + (in earlier lanes): ascending pair order inside every segment, no atomics on
+//      the row positions, the same tables on every run.
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ int local_slot(int32_t id, const Dims& d) {
+    if (id < 0 || id >= d.E) return -1;
+    const int e = id - d.e_lo;
+    return (e >= 0 && e < d.EL) ? e : -1;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ idx,
+                                                                     Dims d, Ws ws) {
+    extern __shared__ int32_t hist[];   // [EL]
+    __shared__ int32_t s_drop;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < d.EL; e += blockDim.x) hist[e] = 0;
+    if (tid == 0) s_drop = 0;
+    __syncthreads();
+
+    const int64_t npairs = static_cast<int64_t>(d.T) * d.k;
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kRouteChunk;
+    const int64_t p1 = min(npairs, p0 + kRouteChunk);
+    int drop = 0;
+    for (int64_t p = p0 + tid; p < p1; p += blockDim.x) {
+        const int32_t id = idx[p];
+        drop += (id < 0 || id >= d.E);
+        const int e = local_slot(id, d);
+        if (e >= 0) atomicAdd(&hist[e], 1);
+    }
+    if (drop) atomicAdd(&s_drop, drop);
+    __syncthreads();
+    for (int e = tid; e < d.EL; e += blockDim.x)
+        ws.chunk_hist[static_cast<int64_t>(blockIdx.x) * d.EL + e] = hist[e];
+    if (tid == 0) ws.chunk_dropped[blockIdx.x] = s_drop;
+
+    // local pairs per token, over an even slice of the tokens
+    const int per = (d.T + gridDim.x - 1) / gridDim.x;
+    const int t0 = blockIdx.x * per, t1 = min(d.T, t0 + per);
+    for (int t = t0 + tid; t < t1; t += blockDim.x) {
+        int n = 0;
+        for (int j = 0; j < d.k; ++j) n += local_slot(idx[static_cast<int64_t>(t) * d.k + j], d) >= 0;
+        ws.tok_nloc[t] = n;
+    }
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(Dims d, Ws ws) {
+    __shared__ int32_t s_val[kScanThreads];
+    __shared__ int32_t s_off[kScanThreads + 1];
+    __shared__ int32_t s_drop;
+    const int tid = threadIdx.x;
+    const int nch = ws.num_chunks;
+
+    // per-expert exclusive scan over chunks (in place), total count and padded count
+    int padded = 0;
+    if (tid < d.EL) {
+        int run = 0;
+        for (int c = 0; c < nch; ++c) {
+            int32_t* h = ws.chunk_hist + static_cast<int64_t>(c) * d.EL + tid;
+            const int v = *h;
+            *h = run;
+            run += v;
+        }
+        ws.counts[tid] = run;
+        padded = (run + d.BM - 1) / d.BM * d.BM;
+    }
+    // inclusive Hillis-Steele scan of the padded counts
+    s_val[tid] = padded;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+        const int v = tid >= off ? s_val[tid - off] : 0;
+        __syncthreads();
+        s_val[tid] += v;
+        __syncthreads();
+    }
+    s_off[tid + 1] = s_val[tid];
+    if (tid == 0) {
+        s_off[0] = 0;
+        int dr = 0;
+        for (int c = 0; c < nch; ++c) dr += ws.chunk_dropped[c];
+        s_drop = dr;
+    }
+    __syncthreads();
+    if (tid < d.EL) ws.offsets[tid] = s_off[tid];
+    if (tid == 0) ws.offsets[d.EL] = s_off[d.EL];
+    const int R = s_off[d.EL];
+    if (tid == 0) {
+        ws.meta[0] = R;
+        ws.meta[1] = s_drop;
+    }
+    // block -> expert map: the last expert whose segment starts at or before the block
+    for (int m = tid; m < ws.num_blocks; m += blockDim.x) {
+        const int r0 = m * d.BM;
+        int e = -1;
+        if (r0 < R) {
+            int lo = 0, hi = d.EL - 1;   // largest e with s_off[e] <= r0
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= r0) lo = mid; else hi = mid - 1;
+            }
+            e = lo;
+        }
+        ws.tile_expert[m] = e;
+    }
+}
+
+constexpr int kPlaceWaves = kRouteThreads / 64;
+
+__global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_t* __restrict__ idx,
+                                                                     Dims d, Ws ws) {
+    extern __shared__ int32_t sm[];
+    int32_t* base = sm;                   // [EL]
+    int32_t* wcnt = sm + d.EL;            // [kPlaceWaves][EL]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t npairs = static_cast<int64_t>(d.T) * d.k;
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kRouteChunk;
+    const int64_t p1 = min(npairs, p0 + kRouteChunk);
+
+    for (int e = tid; e < d.EL; e += blockDim.x)
+        base[e] = ws.offsets[e] + ws.chunk_hist[static_cast<int64_t>(blockIdx.x) * d.EL + e];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int64_t s0 = p0; s0 < p1; s0 += kRouteThreads) {
+        for (int e = lane; e < d.EL; e += 64) wcnt[wave * d.EL + e] = 0;
+        __syncthreads();
+        const int64_t p = s0 + tid;
+        const int e = (p < p1) ? local_slot(idx[p], d) : -1;
+        // group the lanes of this wave by expert; each lane learns its rank in its group
+        int rank = 0;
+        uint64_t todo = __ballot(e >= 0);
+        while (todo) {
+            const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+            const int le = __shfl(e, leader);
+            const uint64_t grp = __ballot(e == le);
+            if (e == le) rank = __popcll(grp & lt_mask);
+            if (lane == leader) wcnt[wave * d.EL + le] = __popcll(grp);
+            todo &= ~grp;
+        }
+        __syncthreads();
+        if (e >= 0) {
+            int row = base[e] + rank;
+            for (int w = 0; w < wave; ++w) row += wcnt[w * d.EL + e];
+            ws.row_pair[row] = static_cast<int32_t>(p);
+            ws.pair_row[p] = row;
+        } else if (p < p1) {
+            ws.pair_row[p] = -1;
+        }
+        __syncthreads();
+        for (int x = tid; x < d.EL; x += blockDim.x) {
+            int add = 0;
+            for (int w = 0; w < kPlaceWaves; ++w) add += wcnt[w * d.EL + x];
+            base[x] += add;
+        }
+        // the next sub-step's zeroing of wcnt is ordered after these reads by its barrier
+        __syncthreads();
+    }
+
+    // -1 in every row that no pair fills: padding inside segments and rows past R
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid; r < ws.rows_cap; r += stride) {
+        const int e = ws.tile_expert[r / d.BM];
+        if (e < 0 || r >= ws.offsets[e] + ws.counts[e]) ws.row_pair[r] = -1;
+    }
+}
+
+hipError_t launch_route(const Dims& d, const int32_t* topk_idx, const Ws& ws, hipStream_t s) {
+    const int nch = ws.num_chunks;
+    route_count_kernel<<<nch, kRouteThreads, sizeof(int32_t) * d.EL, s>>>(topk_idx, d, ws);
+    route_scan_kernel<<<1, kScanThreads, 0, s>>>(d, ws);
+    route_place_kernel<<<nch, kRouteThreads, sizeof(int32_t) * d.EL * (1 + kPlaceWaves), s>>>(
+        topk_idx, d, ws);
+    return hipGetLastError();
+}
+
+}  // namespace moe
