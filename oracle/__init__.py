@@ -149,9 +149,10 @@ def swiglu(hgu_bits) -> np.ndarray:
     return a
 
 
-def swiglu_bwd(hgu_bits, da_bits) -> np.ndarray:
-    """Gradient of silu(gate) * up w.r.t. [gate | up] for an upstream gradient da (bf16)."""
-    hgu, da = _c(hgu_bits, np.uint16), _c(da_bits, np.uint16)
+def swiglu_bwd(hgu_bits, da) -> np.ndarray:
+    """Gradient of silu(gate) * up w.r.t. [gate | up] (bf16 rows) for an upstream gradient da
+    (fp64 values, [n, I])."""
+    hgu, da = _c(hgu_bits, np.uint16), _c(da, np.float64)
     n, N = hgu.shape
     assert da.shape == (n, N // 2)
     d = np.zeros((n, N), np.float64)

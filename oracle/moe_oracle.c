@@ -228,16 +228,16 @@ int oracle_swiglu(int64_t nrows, int I, const uint16_t* hgu, double* a) {
     return 0;
 }
 
-/* SwiGLU backward on given bf16 [gate | up] rows and an upstream gradient da [nrows, I]:
+/* SwiGLU backward on given bf16 [gate | up] rows and an upstream gradient da [nrows, I] (fp64):
  * with s = sigmoid(g): dgate = da * up * s * (1 + g * (1 - s)), dup = da * g * s. */
-int oracle_swiglu_bwd(int64_t nrows, int I, const uint16_t* hgu, const uint16_t* da,
+int oracle_swiglu_bwd(int64_t nrows, int I, const uint16_t* hgu, const double* da,
                       double* dhgu) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nrows; ++r)
         for (int c = 0; c < I; ++c) {
             const double g = bf16_value(hgu[r * 2 * I + c]);
             const double u = bf16_value(hgu[r * 2 * I + I + c]);
-            const double d = bf16_value(da[r * I + c]);
+            const double d = da[r * I + c];
             const double s = 1.0 / (1.0 + exp(-g));
             dhgu[r * 2 * I + c] = d * u * s * (1.0 + g * (1.0 - s));
             dhgu[r * 2 * I + I + c] = d * g * s;

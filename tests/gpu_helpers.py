@@ -23,12 +23,56 @@ def f64_host(t):
 
 
 def rel_max_err(got, ref):
-    """max |got - ref| / rms(ref) over the whole array (the acceptance measure)."""
+    """max |got - ref| / rms(ref) over the whole array."""
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(ref * ref))
     if rms == 0:
         return float(np.max(np.abs(got))) if got.size else 0.0
     return float(np.max(np.abs(got - ref)) / rms)
+
+
+def bf16_half_ulp(v):
+    """Largest error of rounding a value of magnitude |v| to bf16 (half an ulp of its binade)."""
+    v = np.abs(np.asarray(v, np.float64))
+    _, e = np.frexp(v)   # v = m * 2**e with m in [0.5, 1): the ulp is 2**(e - 8)
+    return np.where(v > 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def bf16_out_err(got, ref):
+    """Acceptance measure for a bf16 output: max over elements of |got - ref| minus the element's
+    own rounding to bf16 (half an ulp at max(|got|, |ref|)), over rms(ref).  The bound 2e-2
+    applies to this: the error of the computation, with the output dtype's rounding on top."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    excess = np.abs(got - ref) - bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref)))
+    m = float(np.max(excess)) if got.size else 0.0
+    return max(m, 0.0) / rms if rms > 0 else max(m, 0.0)
+
+
+def check_bf16(got, ref, tol, what=""):
+    e, raw = bf16_out_err(got, ref), rel_max_err(got, ref)
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    print("[parity] %-28s err beyond bf16 rounding %.3e  raw max|err|/rms %.3e" % (what, e, raw))
+    assert e <= tol, "%s: error beyond bf16 rounding %.4g > %.3g (raw max|err|/rms %.4g)" % (what, e, tol, raw)
+    return e, raw
+
+
+BF16_U = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits)
+
+
+def check_sum_bound(got, ref, S, c, tol, what=""):
+    """Acceptance for a bf16 output that is a sum of products of bf16-rounded MFMA operands:
+    |got - ref| <= tol * rms(ref) + (own rounding to bf16) + c * u_bf16 * S per element, where
+    S = sum of |terms| of that element (the dot-product error bound for operands that each carry
+    a relative rounding error of at most u_bf16)."""
+    got, ref, S = (np.asarray(a, np.float64) for a in (got, ref, S))
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    rms = np.sqrt(np.mean(ref * ref))
+    allow = tol * rms + bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref))) + c * BF16_U * S
+    ratio = float(np.max(np.abs(got - ref) / allow)) if got.size else 0.0
+    print("[parity] %-28s max |err| / allowed %.3f  (raw max|err|/rms %.3e)" % (what, ratio, rel_max_err(got, ref)))
+    assert ratio <= 1.0, "%s: error exceeds the bound by a factor %.3f" % (what, ratio)
+    return ratio
 
 
 def layer(w, d, block_m, train=False, weights=True):

@@ -1,0 +1,172 @@
+"""GPU parity of the backward stages against the CPU oracle, through the C ABI.
+
+Covers L2 dgrad (NN) with and without the SwiGLU transpose in its epilogue, the standalone
+SwiGLU backward, dW2 and dW1 with a variable K (rows per expert, including experts without
+rows, whose gradients must be exact zeros).
+
+Acceptance:
+  * row intermediates (dact, dhgu) are checked link by link: dact against the oracle's L2
+    dgrad, dhgu against the oracle's SwiGLU transpose evaluated on the GPU's own saved bf16
+    pre-activations; bound 2e-2 * rms on top of each element's own rounding to bf16;
+  * dW1 and dW2 are sums over an expert's rows of products of bf16 MFMA operands; besides
+    2e-2 * rms and the output rounding, each element may carry c * 2^-8 * sum|terms| (the
+    dot-product error bound, 2^-8 = bf16 unit roundoff): c = 2 for dW2 (both operands, the
+    saved activation and w * dy, are rounded once) and c = 3 for dW1 (x is exact; the dhgu
+    operand is rounded and was itself computed from bf16 saved pre-activations).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as mw
+import oracle
+import token_dispatch_grouped_route_amd as moe
+from gpu_helpers import bits_host, check_bf16, check_sum_bound, f64_host, layer, tables
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+C_DW1, C_DW2 = 3.0, 2.0
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+REDUCED = [
+    mw.Workload("wide_reduced", T=64, H=256, I=128, E=48, EL=6, k=6, backward=True),
+    mw.Workload("bwd_ragged_shard", T=301, H=384, I=256, E=10, EL=5, k=3, e_lo=2, backward=True),
+]
+
+
+def with_empty_expert(w, d):
+    """Routing where local expert 1 receives no pair (its ids move to local expert 0)."""
+    idx = d["topk_idx"].copy()
+    idx[idx == w.e_lo + 1] = w.e_lo
+    return dict(d, topk_idx=idx)
+
+
+def run_forward_backward(w, d, bm):
+    ns = layer(w, d, bm, train=True)
+    moe.forward(ns.shape, ns.x, ns.idx, ns.wts, ns.W1p, ns.W2p, ns.ws, ns.y)
+    ns.dW1p = torch.full((w.EL, 2 * w.I, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ns.dW2p = torch.full((w.EL, w.H, w.I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.backward(ns.shape, ns.x, ns.dy, ns.wts, ns.W2p, ns.ws, ns.dW1p, ns.dW2p)
+    torch.cuda.synchronize()
+    return ns
+
+
+def oracle_rows(w, d, pairs):
+    args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    dA, dH = oracle.backward_rows(*args, E=w.E, e_lo=w.e_lo, pairs=pairs)
+    _, a = oracle.l1_rows(d["x"], d["topk_idx"], d["W1"], w.E, w.e_lo, pairs)
+    return dA, dH, a
+
+
+def term_sums(w, d, experts, rows_of):
+    """sum|terms| of every dW1 / dW2 element of the given experts, from the oracle's rows."""
+    X = mw.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    dy = mw.bf16_bits_to_f32(d["dy"]).astype(np.float64)
+    S1 = np.zeros((len(experts), w.H, 2 * w.I))
+    S2 = np.zeros((len(experts), w.I, w.H))
+    for i, e in enumerate(experts):
+        pairs = rows_of(e)
+        if len(pairs) == 0:
+            continue
+        _, dH, a = oracle_rows(w, d, pairs)
+        t = pairs // w.k
+        wd = np.abs(d["topk_weights"].reshape(-1)[pairs])[:, None] * np.abs(dy[t])
+        S1[i] = np.abs(X[t]).T @ np.abs(dH)
+        S2[i] = np.abs(a).T @ wd
+    return S1, S2
+
+
+def pairs_of_expert(tab):
+    def rows_of(e):
+        o, c = tab["padded_offsets"][e], tab["counts"][e]
+        return tab["row_pair"][o:o + c].astype(np.int64)
+    return rows_of
+
+
+@pytest.mark.parametrize("bm", [32, 64, 128])
+@pytest.mark.parametrize("w", REDUCED, ids=[r.name for r in REDUCED])
+def test_backward_reduced_full_compare(w, bm):
+    d = with_empty_expert(w, mw.inputs(w, 9))
+    ns = run_forward_backward(w, d, bm)
+    t = tables(ns)
+    args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
+    S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
+    g1 = f64_host(ns.dW1p).transpose(0, 2, 1)
+    g2 = f64_host(ns.dW2p).transpose(0, 2, 1)
+    check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1")
+    check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2")
+    assert np.all(g1[1] == 0.0) and np.all(g2[1] == 0.0), "expert without rows must get exact zeros"
+    real = np.nonzero(t["row_pair"] >= 0)[0]
+    dA, _, _ = oracle_rows(w, d, t["row_pair"][real])
+    hgu = bits_host(moe.ws_region(ns.ws, ns.shape, "hgu"))[real]
+    dhgu = f64_host(moe.ws_region(ns.ws, ns.shape, "dhgu"))[real]
+    check_bf16(dhgu, oracle.swiglu_bwd(hgu, dA), TOL, "dhgu (fused epilogue)")
+
+
+def test_backward_stages_match_oracle_and_fused():
+    w = REDUCED[1]
+    d = mw.inputs(w, 10)
+    bm = 64
+    ns = run_forward_backward(w, d, bm)
+    s = ns.shape
+    t = tables(ns)
+    real = np.nonzero(t["row_pair"] >= 0)[0]
+    dA, _, _ = oracle_rows(w, d, t["row_pair"][real])
+
+    moe.bwd_gemm2_dgrad(s, ns.dy, ns.wts, ns.W2p, ns.ws, fuse_swiglu_bwd=False)
+    torch.cuda.synchronize()
+    dact = moe.ws_region(ns.ws, s, "dact")
+    check_bf16(f64_host(dact)[real], dA, TOL, "dact (L2 dgrad)")
+    pad = np.setdiff1d(np.arange(t["num_rows"]), real)
+    assert np.all(f64_host(dact)[pad] == 0.0)
+
+    moe.swiglu_bwd(s, ns.ws)
+    torch.cuda.synchronize()
+    hgu = bits_host(moe.ws_region(ns.ws, s, "hgu"))
+    dhgu = f64_host(moe.ws_region(ns.ws, s, "dhgu"))
+    ref_local = oracle.swiglu_bwd(hgu[real], f64_host(dact)[real])
+    check_bf16(dhgu[real], ref_local, TOL, "swiglu_bwd (standalone)")
+    assert np.all(dhgu[pad] == 0.0)
+
+    dW1p = torch.empty_like(ns.dW1p)
+    dW2p = torch.empty_like(ns.dW2p)
+    moe.wgrad2(s, ns.dy, ns.wts, ns.ws, dW2p)
+    moe.wgrad1(s, ns.x, ns.ws, dW1p)
+    torch.cuda.synchronize()
+    assert torch.equal(dW2p, ns.dW2p), "dW2 does not depend on the SwiGLU-transpose path"
+    args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
+    S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
+    check_sum_bound(f64_host(dW1p).transpose(0, 2, 1), dW1, S1, C_DW1, TOL, "dW1 (staged)")
+    check_sum_bound(f64_host(dW2p).transpose(0, 2, 1), dW2, S2, C_DW2, TOL, "dW2 (staged)")
+
+
+def test_backward_full_size_sampled_experts():
+    w = mw.get(4)
+    d = mw.inputs(w, 0)
+    bm = moe.preferred_block_m(moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=64))
+    ns = run_forward_backward(w, d, bm)
+    t = tables(ns)
+    counts = t["counts"]
+    experts = sorted({int(np.argmin(counts)), int(np.argmax(counts)), w.EL // 2})
+    args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo, experts=experts)
+    S1, S2 = term_sums(w, d, experts, pairs_of_expert(t))
+    for i, e in enumerate(experts):
+        check_sum_bound(f64_host(ns.dW1p[e]).T, dW1[i], S1[i], C_DW1, TOL, "dW1[%d] (%d rows)" % (e, counts[e]))
+        check_sum_bound(f64_host(ns.dW2p[e]).T, dW2[i], S2[i], C_DW2, TOL, "dW2[%d] (%d rows)" % (e, counts[e]))
+    rng = np.random.default_rng(4)
+    real = np.nonzero(t["row_pair"] >= 0)[0]
+    rows = rng.choice(real, size=24, replace=False)
+    dA, _, _ = oracle_rows(w, d, t["row_pair"][rows])
+    hgu = bits_host(moe.ws_region(ns.ws, ns.shape, "hgu"))[rows]
+    check_bf16(f64_host(moe.ws_region(ns.ws, ns.shape, "dhgu"))[rows], oracle.swiglu_bwd(hgu, dA), TOL,
+               "dhgu rows")

@@ -351,7 +351,7 @@ def test_swiglu_fwd_bwd_match_torch_autograd():
     a = F.silu(h[:, :I]) * h[:, I:]
     a.backward(f64(da))
     assert rel_err(oracle.swiglu(hgu), a.detach().numpy()) < 1e-13
-    assert rel_err(oracle.swiglu_bwd(hgu, da), h.grad.numpy()) < 1e-13
+    assert rel_err(oracle.swiglu_bwd(hgu, f64(da).numpy()), h.grad.numpy()) < 1e-13
 
 
 # ----------------------------------------------------------------------------------------
