@@ -1,0 +1,203 @@
+"""Benchmark of the MoE expert layer forward on one MI355X (gfx950).
+
+Workload: the DeepSeek-V3 one-GPU expert-parallel share ("Mega MoE" page, Performance / Test
+Configuration shapes: hidden 7168, intermediate 2048, 256 experts, top-8, 8192 tokens), this GPU
+owning experts 0..31 and computing only the pairs that hit them.  Seeded synthetic inputs (no
+dataset is involved: the pages do not state their routing; N(0,1) router logits stand in).
+
+One step = one pass of the whole forward path on inputs already resident in HBM: routing
+prologue, dispatch gather + L1 grouped GEMM + SwiGLU, L2 grouped GEMM + weighted combine.
+value = algorithmic forward FLOPs (2*P*H*2I + 2*P*I*H on the P real local pairs, padding
+excluded) / step time.  Prints one JSON line.
+
+Flags: --gpus N (only 1 is supported: the path is one GPU's share), --steps K, --warmup W,
+--workload NAME, --block-m BM, --no-cpu-baseline, --copy-calibration (also times a plain 1 GiB
+device copy, for reading HBM counters against a kernel of known traffic).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_workloads as mw  # noqa: E402
+import token_dispatch_grouped_route_amd as moe  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_dsv3_share_traffic.json")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def bf16_dev(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch_alg):
+    """HBM bytes per L1 launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, d, budget_s=15.0):
+    """The oracle (test infrastructure) timed on the host cores on a bounded sample of tokens."""
+    import oracle
+    idx = d["topk_idx"]
+    local = (idx >= w.e_lo) & (idx < w.e_lo + w.EL)
+    toks = np.nonzero(local.any(axis=1))[0]
+    rng = np.random.default_rng(0)
+    toks = rng.permutation(toks)
+    args = (d["x"], idx, d["topk_weights"], d["W1"], d["W2"])
+    n = max(1, oracle.num_threads())   # calibrate on one token per thread
+    t0 = time.perf_counter()
+    oracle.forward(*args, E=w.E, e_lo=w.e_lo, tokens=toks[:n])
+    dt = time.perf_counter() - t0
+    n2 = int(min(len(toks), max(n, n * budget_s / max(dt, 1e-3))))
+    sample = toks[:n2]
+    t0 = time.perf_counter()
+    oracle.forward(*args, E=w.E, e_lo=w.e_lo, tokens=sample)
+    dt = time.perf_counter() - t0
+    pairs = int(local[sample].sum())
+    flops = w.flops_fwd(pairs)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d tokens (%d local pairs), fp64 per-token loop, %.1f s" % (len(sample), w.T, pairs, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3_share_fwd")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the experts; runs on more than one GPU are not "
+              "part of this path (cross-GPU dispatch/combine is out of scope). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    torch.cuda.set_device(0)
+    w = mw.get(a.workload)
+    log("generating %s inputs (seed 0)" % w.name)
+    d = mw.inputs(w, 0)
+    P = mw.local_pairs(w, d["topk_idx"])
+    flops = w.flops_fwd(P)
+    bm = a.block_m or moe.preferred_block_m(moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=64))
+    shape = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=bm, e_lo=w.e_lo)
+
+    x, y = bf16_dev(d["x"]), torch.empty(w.T, w.H, dtype=torch.bfloat16, device="cuda")
+    idx = torch.from_numpy(d["topk_idx"]).cuda()
+    wts = torch.from_numpy(d["topk_weights"]).cuda()
+    W1p = torch.empty(w.EL, 2 * w.I, w.H, dtype=torch.bfloat16, device="cuda")
+    W2p = torch.empty(w.EL, w.H, w.I, dtype=torch.bfloat16, device="cuda")
+    W1, W2 = bf16_dev(d["W1"]), bf16_dev(d["W2"])
+    moe.pack_weights(shape, W1, W2, W1p, W2p)
+    del W1, W2
+    ws = moe.alloc_workspace(shape)
+    act = moe.ws_region(ws, shape, "act")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    if a.copy_calibration:   # a plain copy of known size, for HBM counter scaling
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    fwd = lambda: moe.forward(shape, x, idx, wts, W1p, W2p, ws, y)
+    log("warmup %d" % a.warmup)
+    for _ in range(a.warmup):
+        fwd()
+    torch.cuda.synchronize()
+
+    # headline: K fused forwards
+    log("timing %d fused forward steps" % a.steps)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(a.steps):
+        fwd()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+
+    # per stage: the same kernels through the stage entry points, events between stages
+    log("timing %d staged steps" % a.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        ev[i][0].record(s)
+        moe.route_prologue(shape, idx, ws)
+        ev[i][1].record(s)
+        moe.dispatch_gemm1(shape, x, W1p, ws, act_out=act)
+        ev[i][2].record(s)
+        moe.gemm2_combine(shape, act, W2p, wts, ws, y)
+        ev[i][3].record(s)
+    torch.cuda.synchronize()
+    st = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(a.steps)])
+    st_ms = st.mean(axis=0)
+
+    R = int(moe.ws_region(ws, shape, "meta")[0].item())
+    # algorithmic bytes of the L1 launch: each non-empty local expert's W1 once, the x rows of
+    # tokens with a local pair once, the SwiGLU output rows written once, the pair ids of the rows
+    idx_np = d["topk_idx"]
+    local = (idx_np >= w.e_lo) & (idx_np < w.e_lo + w.EL)
+    nonempty = len(np.unique(idx_np[local]))
+    tok_local = int(local.any(axis=1).sum())
+    l1_flops = 2.0 * P * w.H * 2 * w.I
+    l1_bytes = nonempty * 2 * w.I * w.H * 2 + tok_local * w.H * 2 + P * w.I * 2 + P * 4
+    l1_s = st_ms[1] / 1e3
+    traffic = measured_traffic(l1_bytes)
+    roof = {"bound": "hbm", "achieved": l1_bytes / l1_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
+            "kernel": "gemm1 (dispatch gather + L1 NT + SwiGLU)",
+            "alg_bytes_per_launch": l1_bytes, "alg_flops_per_launch": l1_flops,
+            "mfma_frac": l1_flops / l1_s / 1e12 / PEAK_BF16_TFLOPS}
+
+    value = flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": "MoE layer fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak); per-stage ms",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) logits, x, scaled weights)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "EL": w.EL, "k": w.k,
+                   "block_m": bm, "local_pairs": P, "padded_rows": R, "parallelism": "none (1 GPU share)"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {"prologue": round(st_ms[0], 4), "dispatch_gemm1_swiglu": round(st_ms[1], 4),
+                      "gemm2_combine": round(st_ms[2], 4), "staged_total": round(st_ms.sum(), 4)},
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        log("timing the oracle on a CPU sample")
+        out["cpu_baseline"] = cpu_baseline(w, d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
