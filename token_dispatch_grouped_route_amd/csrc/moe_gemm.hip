@@ -33,19 +33,30 @@ namespace moe {
 
 constexpr int BK = 64;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes of staged operand
+
+// 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7): with 64 banks of 4 bytes a row
+// covers half of the banks, so rows r and r + 1 fill the two halves and the 16 rows read by a
+// 16-lane group of a fragment load hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * 128 + ((chunk ^ (row & 7)) << 4);
+    return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int PF_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int PF = PF_;   // K steps of global loads in flight ahead of the MFMAs (1 or 2)
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int MI = TM / 32, NI = TN / 32;
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int OPERAND_BYTES = 2 * STAGE_BYTES;
+    // fp32 C tile for the epilogue, row stride BN + 8 floats: the two half-waves of an
+    // accumulator write (rows 4 apart) then start 32 banks apart
+    static constexpr int C_STRIDE = BN + 8;
+    static constexpr int C_BYTES = BM * C_STRIDE * 4;
+    static constexpr int LDS_BYTES = OPERAND_BYTES > C_BYTES ? OPERAND_BYTES : C_BYTES;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
     static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "K-row chunks must split evenly");
 };
@@ -56,34 +67,40 @@ struct Cfg {
 template <int ROWS, int NT>
 struct KRows {
     static constexpr int PER = ROWS * 8 / NT;   // 16-byte chunks per thread per K step
-    const uint16_t* src[PER];                   // row start + chunk offset, nullptr = zero row
-    uint4 v[PER];
+    const char* base;                           // uniform base of every row of this operand
+    uint32_t off[PER];                          // byte offset of the thread's chunk of each row
+    uint32_t keep;                              // bit i clear: row i is padding and reads as zeros
+    u32x4 v[2][PER];                            // two register slots: steps k+1 and k+2 in flight
 
     // chunk q = tid + i*NT covers row q/8, chunk q%8
     __device__ __forceinline__ static int row_of(int tid, int i) { return (tid + i * NT) >> 3; }
     __device__ __forceinline__ static int chunk_of(int tid, int i) { return (tid + i * NT) & 7; }
 
-    __device__ __forceinline__ void load(int kt) {
+    template <int S>
+    __device__ __forceinline__ void load(int kt, int) {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            v[i] = src[i] ? *reinterpret_cast<const uint4*>(src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
+            v[S][i] = *reinterpret_cast<const u32x4*>(base + off[i] + kt * (BK * 2));
     }
+    template <int S>
     __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            *reinterpret_cast<uint4*>(lds + lds_off(row_of(tid, i), chunk_of(tid, i))) = v[i];
+        for (int i = 0; i < PER; ++i) {
+            const uint32_t m = ((keep >> i) & 1u) ? 0xffffffffu : 0u;
+            *reinterpret_cast<u32x4*>(lds + lds_off(row_of(tid, i), chunk_of(tid, i))) = v[S][i] & m;
+        }
     }
 };
 
-__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float s) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float s) {
+    u32x4 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(w[i] << 16) * s;
-        const float hi = __uint_as_float(w[i] & 0xffff0000u) * s;
-        w[i] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+        const float lo = __uint_as_float(v[i] << 16) * s;
+        const float hi = __uint_as_float(v[i] & 0xffff0000u) * s;
+        r[i] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return r;
 }
 
 // Operand tile of ROWS rows (the M or N index) x BK, stored in memory as K-indexed rows with the
@@ -97,8 +114,9 @@ struct TRows {
     static constexpr int PER = (UNITS + NT - 1) / NT;
     Src src;
     int m_base;
-    uint4 v[PER][4];
+    u32x4 v[2][PER][4];
 
+    template <int S>
     __device__ __forceinline__ void load(int kt, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -109,28 +127,26 @@ struct TRows {
                 for (int r = 0; r < 4; ++r) {
                     const int k = kt * BK + 4 * kq + r;
                     const uint16_t* p = src.row(k);
-                    uint4 x = p ? *reinterpret_cast<const uint4*>(p + m_base + 8 * mc) : make_uint4(0, 0, 0, 0);
+                    u32x4 x = 0;
+                    if (p) x = *reinterpret_cast<const u32x4*>(p + m_base + 8 * mc);
                     if (Src::kScaled && p) x = scale_bf16x8(x, src.scale(k));
-                    v[i][r] = x;
+                    v[S][i][r] = x;
                 }
             }
         }
     }
+    template <int S>
     __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int u = tid + i * NT;
             if (u < UNITS) {
                 const int kq = u % (BK / 4), mc = u / (BK / 4);
-                const uint32_t w[4][4] = {{v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w},
-                                          {v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w},
-                                          {v[i][2].x, v[i][2].y, v[i][2].z, v[i][2].w},
-                                          {v[i][3].x, v[i][3].y, v[i][3].z, v[i][3].w}};
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int dw = j >> 1, sh = (j & 1) * 16;
-                    const uint32_t k0 = (w[0][dw] >> sh) & 0xffffu, k1 = (w[1][dw] >> sh) & 0xffffu;
-                    const uint32_t k2 = (w[2][dw] >> sh) & 0xffffu, k3 = (w[3][dw] >> sh) & 0xffffu;
+                    const uint32_t k0 = (v[S][i][0][dw] >> sh) & 0xffffu, k1 = (v[S][i][1][dw] >> sh) & 0xffffu;
+                    const uint32_t k2 = (v[S][i][2][dw] >> sh) & 0xffffu, k3 = (v[S][i][3][dw] >> sh) & 0xffffu;
                     uint2 out = make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
                     *reinterpret_cast<uint2*>(lds + lds_off(8 * mc + j, kq >> 1) + (kq & 1) * 8) = out;
                 }
@@ -143,31 +159,54 @@ struct TRows {
 // MFMA core
 // ---------------------------------------------------------------------------------------------
 template <class C>
+__device__ __forceinline__ void read_frags(const char* lA, const char* lB, bf16x8_t (&a)[C::MI],
+                                           bf16x8_t (&b)[C::NI], int s, int wm0, int wn0, int lane) {
+    const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(lA + lds_off(wm0 + i * 32 + (lane & 31), ch));
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(lB + lds_off(wn0 + j * 32 + (lane & 31), ch));
+}
+
+// The fragments of 16-k substep s+1 are read from LDS before the MFMAs of substep s.
+template <class C>
 __device__ __forceinline__ void mma_step(const char* lA, const char* lB, f32x16_t (&acc)[C::MI][C::NI],
                                          int wm0, int wn0, int lane) {
+    constexpr int KS = BK / 16;
+    bf16x8_t a[2][C::MI], b[2][C::NI];
+    read_frags<C>(lA, lB, a[0], b[0], 0, wm0, wn0, lane);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-        const int ch = 2 * s + (lane >> 5);
-        bf16x8_t a[C::MI], b[C::NI];
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-            a[i] = *reinterpret_cast<const bf16x8_t*>(lA + lds_off(wm0 + i * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-            b[j] = *reinterpret_cast<const bf16x8_t*>(lB + lds_off(wn0 + j * 32 + (lane & 31), ch));
+    for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) read_frags<C>(lA, lB, a[(s + 1) & 1], b[(s + 1) & 1], s + 1, wm0, wn0, lane);
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
 #pragma unroll
             for (int j = 0; j < C::NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
     }
 }
 
-// Loader adapters: KRows loads by step only, TRows needs the thread id.
-template <int R, int NT>
-__device__ __forceinline__ void op_load(KRows<R, NT>& l, int kt, int) { l.load(kt); }
-template <int R, int NT, class S>
-__device__ __forceinline__ void op_load(TRows<R, NT, S>& l, int kt, int tid) { l.load(kt, tid); }
+// One K step of the pipeline.  On entry LDS buffer S holds step kt, register slot S^1 holds step
+// kt+1 (loads in flight) and slot S is free: it receives step kt+2, then the MFMAs consume buffer
+// S, then slot S^1 moves to LDS buffer S^1 (read by nobody since the previous barrier).
+template <class C, int S, class LA, class LB>
+__device__ __forceinline__ void pipe_step(LA& la, LB& lb, int kt, int nk, char* smem,
+                                          f32x16_t (&acc)[C::MI][C::NI], int tid, int wm0, int wn0, int lane) {
+    if (kt + 2 < nk) {
+        la.template load<S>(kt + 2, tid);
+        lb.template load<S>(kt + 2, tid);
+    }
+    const char* cur = smem + S * C::STAGE_BYTES;
+    mma_step<C>(cur, cur + C::A_BYTES, acc, wm0, wn0, lane);
+    if (kt + 1 < nk) {
+        char* nxt = smem + (S ^ 1) * C::STAGE_BYTES;
+        la.template store<S ^ 1>(nxt, tid);
+        lb.template store<S ^ 1>(nxt + C::A_BYTES, tid);
+    }
+    __syncthreads();
+}
 
 template <class C, class LA, class LB>
 __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f32x16_t (&acc)[C::MI][C::NI],
@@ -179,31 +218,72 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f3
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     if (nk <= 0) return;
-    op_load(la, 0, tid);
-    op_load(lb, 0, tid);
-    la.store(smem, tid);
-    lb.store(smem + C::A_BYTES, tid);
+    la.template load<0>(0, tid);
+    lb.template load<0>(0, tid);
+    if constexpr (C::PF == 2) {
+        if (nk > 1) {
+            la.template load<1>(1, tid);
+            lb.template load<1>(1, tid);
+        }
+    }
+    la.template store<0>(smem, tid);
+    lb.template store<0>(smem + C::A_BYTES, tid);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        char* cur = smem + (kt & 1) * C::STAGE_BYTES;
-        char* nxt = smem + ((kt + 1) & 1) * C::STAGE_BYTES;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            op_load(la, kt + 1, tid);
-            op_load(lb, kt + 1, tid);
+    if constexpr (C::PF == 2) {
+        for (int kt = 0; kt < nk; kt += 2) {
+            pipe_step<C, 0>(la, lb, kt, nk, smem, acc, tid, wm0, wn0, lane);
+            if (kt + 1 < nk) pipe_step<C, 1>(la, lb, kt + 1, nk, smem, acc, tid, wm0, wn0, lane);
         }
-        mma_step<C>(cur, cur + C::A_BYTES, acc, wm0, wn0, lane);
-        if (more) {
-            la.store(nxt, tid);
-            lb.store(nxt + C::A_BYTES, tid);
+    } else {
+        // one register slot: step kt+1 loads while step kt computes, then goes to the other buffer
+        for (int kt = 0; kt < nk; ++kt) {
+            const bool more = kt + 1 < nk;
+            if (more) {
+                la.template load<0>(kt + 1, tid);
+                lb.template load<0>(kt + 1, tid);
+            }
+            const char* cur = smem + (kt & 1) * C::STAGE_BYTES;
+            mma_step<C>(cur, cur + C::A_BYTES, acc, wm0, wn0, lane);
+            if (more) {
+                char* nxt = smem + ((kt + 1) & 1) * C::STAGE_BYTES;
+                la.template store<0>(nxt, tid);
+                lb.template store<0>(nxt + C::A_BYTES, tid);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
 // Row (within the tile) and column (within the wave's N range) of accumulator element r of
 // the 32x32 block: 4 groups of 8 rows, the lane's half picks 4 of them, lane%32 is the column.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Accumulators to the fp32 C tile in LDS; col_of(ni) gives the tile column of block ni's lane 0.
+// The caller has passed a barrier after the last MFMA reads of the operand buffers.
+template <class C, class ColOf>
+__device__ __forceinline__ void acc_to_lds(float* ct, const f32x16_t (&acc)[C::MI][C::NI], int wm0, int lane,
+                                           ColOf col_of) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni) {
+            const int col = col_of(ni) + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ct[(wm0 + mi * 32 + acc_row(r, lane)) * C::C_STRIDE + col] = acc[mi][ni][r];
+        }
+}
+
+__device__ __forceinline__ void ld8(const float* p, float (&f)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ u32x4 bf16x8_of(const float (&f)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
+    return r;
+}
 
 // ---------------------------------------------------------------------------------------------
 // gemm1: dispatch gather + L1 (NT) + SwiGLU
@@ -233,39 +313,53 @@ __global__ __launch_bounds__(C::NT) void gemm1_kernel(const uint16_t* __restrict
         const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
 
         KRows<C::BM, C::NT> la;
+        la.base = reinterpret_cast<const char*>(x);
+        la.keep = 0;
 #pragma unroll
         for (int i = 0; i < la.PER; ++i) {
             const int p = ws.row_pair[row0 + la.row_of(tid, i)];
-            la.src[i] = (p >= 0 && p < npairs) ? x + static_cast<int64_t>(p / d.k) * H + 8 * la.chunk_of(tid, i) : nullptr;
+            const bool ok = p >= 0 && p < npairs;
+            la.keep |= static_cast<uint32_t>(ok) << i;
+            la.off[i] = 2u * (static_cast<uint32_t>(ok ? p / d.k : 0) * H + 8 * la.chunk_of(tid, i));
         }
         KRows<C::BN, C::NT> lb;
+        lb.base = reinterpret_cast<const char*>(w1p + static_cast<int64_t>(e) * 2 * I * H);
+        lb.keep = ~0u;
 #pragma unroll
         for (int i = 0; i < lb.PER; ++i) {
             const int nl = lb.row_of(tid, i);
             const int w = nl / C::TN, j = nl % C::TN;
             const int grow = (j / HALF) * I + nt * (C::BN / 2) + w * HALF + (j % HALF);
-            lb.src[i] = w1p + (static_cast<int64_t>(e) * 2 * I + grow) * H + 8 * lb.chunk_of(tid, i);
+            lb.off[i] = 2u * (static_cast<uint32_t>(grow) * H + 8 * lb.chunk_of(tid, i));
         }
         f32x16_t acc[C::MI][C::NI];
         __syncthreads();   // the previous tile's LDS reads are done
         gemm_tile<C>(la, lb, H / BK, smem, acc, tid, wm0, wn0, lane);
 
-#pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-            for (int nh = 0; nh < C::NI / 2; ++nh) {
-                const int c = nt * (C::BN / 2) + wn * HALF + nh * 32 + (lane & 31);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = row0 + wm0 + mi * 32 + acc_row(r, lane);
-                    const float g = acc[mi][nh][r], u = acc[mi][nh + C::NI / 2][r];
-                    if (hgu_out) {
-                        hgu_out[row * 2 * I + c] = f32_to_bf16(g);
-                        hgu_out[row * 2 * I + I + c] = f32_to_bf16(u);
-                    }
-                    if (act_out) act_out[row * I + c] = f32_to_bf16(silu_f32(g) * u);
-                }
+        // C tile columns: [0, BN/2) gate, [BN/2, BN) up, both in intermediate-column order
+        float* ct = reinterpret_cast<float*>(smem);
+        acc_to_lds<C>(ct, acc, wm0, lane, [&](int ni) {
+            return ni < C::NI / 2 ? wn * HALF + ni * 32 : C::BN / 2 + wn * HALF + (ni - C::NI / 2) * 32;
+        });
+        __syncthreads();
+        constexpr int CH = C::BN / 16;   // 8-column chunks of the tile's intermediate columns
+        const int c0 = nt * (C::BN / 2);
+        for (int u = tid; u < C::BM * CH; u += C::NT) {
+            const int rl = u / CH, c8 = (u % CH) * 8;
+            const int64_t row = row0 + rl;
+            float g[8], up[8], a[8];
+            ld8(ct + rl * C::C_STRIDE + c8, g);
+            ld8(ct + rl * C::C_STRIDE + C::BN / 2 + c8, up);
+            if (hgu_out) {
+                *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + c0 + c8) = bf16x8_of(g);
+                *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + I + c0 + c8) = bf16x8_of(up);
             }
+            if (act_out) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) a[q] = silu_f32(g[q]) * up[q];
+                *reinterpret_cast<u32x4*>(act_out + row * I + c0 + c8) = bf16x8_of(a);
+            }
+        }
     }
 }
 
@@ -299,14 +393,17 @@ __global__ __launch_bounds__(C::NT) void gemm2_kernel(const uint16_t* __restrict
         const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
 
         KRows<C::BM, C::NT> la;
+        la.base = reinterpret_cast<const char*>(act + row0 * I);
+        la.keep = ~0u;
 #pragma unroll
         for (int i = 0; i < la.PER; ++i)
-            la.src[i] = act + (row0 + la.row_of(tid, i)) * I + 8 * la.chunk_of(tid, i);
+            la.off[i] = 2u * (static_cast<uint32_t>(la.row_of(tid, i)) * I + 8 * la.chunk_of(tid, i));
         KRows<C::BN, C::NT> lb;
+        lb.base = reinterpret_cast<const char*>(w2p + (static_cast<int64_t>(e) * H + nt * C::BN) * I);
+        lb.keep = ~0u;
 #pragma unroll
         for (int i = 0; i < lb.PER; ++i)
-            lb.src[i] = w2p + (static_cast<int64_t>(e) * H + nt * C::BN + lb.row_of(tid, i)) * I +
-                        8 * lb.chunk_of(tid, i);
+            lb.off[i] = 2u * (static_cast<uint32_t>(lb.row_of(tid, i)) * I + 8 * lb.chunk_of(tid, i));
         f32x16_t acc[C::MI][C::NI];
         __syncthreads();   // previous tile's LDS (operands and row info) no longer read
         for (int r = tid; r < C::BM; r += C::NT) {
@@ -324,24 +421,28 @@ __global__ __launch_bounds__(C::NT) void gemm2_kernel(const uint16_t* __restrict
         }
         gemm_tile<C>(la, lb, I / BK, smem, acc, tid, wm0, wn0, lane);   // its barriers publish row info
 
+        float* ct = reinterpret_cast<float*>(smem);
+        acc_to_lds<C>(ct, acc, wm0, lane, [&](int ni) { return wn0 + ni * 32; });
+        __syncthreads();
+        constexpr int CH = C::BN / 8;
+        const int col0 = nt * C::BN;
+        for (int u = tid; u < C::BM * CH; u += C::NT) {
+            const int rl = u / CH, c8 = (u % CH) * 8;
+            const int t = s_tok[rl];
+            if (t < 0) continue;
+            const float w = s_w[rl];
+            float o[8];
+            ld8(ct + rl * C::C_STRIDE + c8, o);
 #pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = wm0 + mi * 32 + acc_row(r, lane);
-                const int t = s_tok[rl];
-                if (t < 0) continue;
-                const float w = s_w[rl];
-                if (s_direct[rl]) {
-                    uint16_t* yr = y + static_cast<int64_t>(t) * H + nt * C::BN + wn0 + (lane & 31);
-#pragma unroll
-                    for (int ni = 0; ni < C::NI; ++ni) yr[ni * 32] = f32_to_bf16(w * acc[mi][ni][r]);
-                } else {
-                    float* sr = ws.stage + (row0 + rl) * H + nt * C::BN + wn0 + (lane & 31);
-#pragma unroll
-                    for (int ni = 0; ni < C::NI; ++ni) sr[ni * 32] = w * acc[mi][ni][r];
-                }
+            for (int q = 0; q < 8; ++q) o[q] *= w;
+            if (s_direct[rl]) {
+                *reinterpret_cast<u32x4*>(y + static_cast<int64_t>(t) * H + col0 + c8) = bf16x8_of(o);
+            } else {
+                float* sr = ws.stage + (row0 + rl) * H + col0 + c8;
+                *reinterpret_cast<float4*>(sr) = make_float4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<float4*>(sr + 4) = make_float4(o[4], o[5], o[6], o[7]);
             }
+        }
     }
 }
 
@@ -378,10 +479,14 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const uint16_t* __restrict
         const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
 
         KRows<C::BM, C::NT> la;
+        la.base = reinterpret_cast<const char*>(dy);
+        la.keep = 0;
 #pragma unroll
         for (int i = 0; i < la.PER; ++i) {
             const int p = ws.row_pair[row0 + la.row_of(tid, i)];
-            la.src[i] = (p >= 0 && p < npairs) ? dy + static_cast<int64_t>(p / d.k) * H + 8 * la.chunk_of(tid, i) : nullptr;
+            const bool ok = p >= 0 && p < npairs;
+            la.keep |= static_cast<uint32_t>(ok) << i;
+            la.off[i] = 2u * (static_cast<uint32_t>(ok ? p / d.k : 0) * H + 8 * la.chunk_of(tid, i));
         }
         TRows<C::BN, C::NT, W2ColSrc> lb;
         lb.src.base = w2p + static_cast<int64_t>(e) * H * I;
