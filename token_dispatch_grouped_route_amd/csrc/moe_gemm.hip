@@ -46,6 +46,8 @@ template <int BM_, int BN_, int WM_, int WN_, int PF_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int PF = PF_;   // K steps of global loads in flight ahead of the MFMAs (1 or 2)
+    // workgroups per CU the register allocation must allow (the LDS of two fits in 160 KB)
+    static constexpr int MIN_WG = (BM * BN <= 128 * 128) ? 2 : 1;
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int MI = TM / 32, NI = TN / 32;
@@ -191,13 +193,15 @@ __device__ __forceinline__ void mma_step(const char* lA, const char* lB, f32x16_
 // One K step of the pipeline.  On entry LDS buffer S holds step kt, register slot S^1 holds step
 // kt+1 (loads in flight) and slot S is free: it receives step kt+2, then the MFMAs consume buffer
 // S, then slot S^1 moves to LDS buffer S^1 (read by nobody since the previous barrier).
+// The loads are unconditional (past the end they re-read the last step, which is never stored):
+// a load under a branch would make the compiler's wait counts conservative on the merged path and
+// wait for the loads just issued, serialising the pipeline.
 template <class C, int S, class LA, class LB>
 __device__ __forceinline__ void pipe_step(LA& la, LB& lb, int kt, int nk, char* smem,
                                           f32x16_t (&acc)[C::MI][C::NI], int tid, int wm0, int wn0, int lane) {
-    if (kt + 2 < nk) {
-        la.template load<S>(kt + 2, tid);
-        lb.template load<S>(kt + 2, tid);
-    }
+    const int kl = min(kt + 2, nk - 1);
+    la.template load<S>(kl, tid);
+    lb.template load<S>(kl, tid);
     const char* cur = smem + S * C::STAGE_BYTES;
     mma_step<C>(cur, cur + C::A_BYTES, acc, wm0, wn0, lane);
     if (kt + 1 < nk) {
@@ -221,19 +225,19 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f3
     la.template load<0>(0, tid);
     lb.template load<0>(0, tid);
     if constexpr (C::PF == 2) {
-        if (nk > 1) {
-            la.template load<1>(1, tid);
-            lb.template load<1>(1, tid);
-        }
+        la.template load<1>(min(1, nk - 1), tid);
+        lb.template load<1>(min(1, nk - 1), tid);
     }
     la.template store<0>(smem, tid);
     lb.template store<0>(smem + C::A_BYTES, tid);
     __syncthreads();
     if constexpr (C::PF == 2) {
-        for (int kt = 0; kt < nk; kt += 2) {
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
             pipe_step<C, 0>(la, lb, kt, nk, smem, acc, tid, wm0, wn0, lane);
-            if (kt + 1 < nk) pipe_step<C, 1>(la, lb, kt + 1, nk, smem, acc, tid, wm0, wn0, lane);
+            pipe_step<C, 1>(la, lb, kt + 1, nk, smem, acc, tid, wm0, wn0, lane);
         }
+        if (kt < nk) pipe_step<C, 0>(la, lb, kt, nk, smem, acc, tid, wm0, wn0, lane);
     } else {
         // one register slot: step kt+1 loads while step kt computes, then goes to the other buffer
         for (int kt = 0; kt < nk; ++kt) {
@@ -292,7 +296,7 @@ __device__ __forceinline__ u32x4 bf16x8_of(const float (&f)[8]) {
 // B tile are [gate cols | up cols] of the same BN/(2*WN) intermediate columns, so the lane that
 // holds gate(r, c) in block j also holds up(r, c) in block j + NI/2.
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm1_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_kernel(const uint16_t* __restrict__ x,
                                                       const uint16_t* __restrict__ w1p, Dims d, Ws ws,
                                                       uint16_t* __restrict__ act_out,
                                                       uint16_t* __restrict__ hgu_out) {
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(C::NT) void gemm1_kernel(const uint16_t* __restrict
 // pair owns its y row: the epilogue stores bf16(w * o) there.  A token with several local pairs
 // gets fp32 rows in ws.stage, summed in slot order by combine_finish (deterministic, no atomics).
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm2_kernel(const uint16_t* __restrict__ act,
+__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm2_kernel(const uint16_t* __restrict__ act,
                                                       const uint16_t* __restrict__ w2p,
                                                       const float* __restrict__ topk_w, Dims d, Ws ws,
                                                       uint16_t* __restrict__ y) {
@@ -686,6 +690,7 @@ static int persistent_grid(K kernel, int threads, size_t lds, int n_tiles, int64
         if (4 * r >= 3 * g) g = r;
     }
     if (g > max_tiles) g = max_tiles;
+    if (g >= 8) g &= ~int64_t(7);   // whole groups of 8 (one workgroup per XCD in each group)
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
@@ -726,9 +731,10 @@ static hipError_t gemm2_launch(const Dims& d, const uint16_t* act, const uint16_
     return hipGetLastError();
 }
 
-template <class C>
+template <class C0>
 static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
                                const Ws& ws, int fuse, hipStream_t s) {
+    using C = Cfg<C0::BM, C0::BN, C0::WM, C0::WN, 1>;   // one staging slot: the transposing loader is register-heavy
     const size_t lds = C::LDS_BYTES + sizeof(float) * C::BM;
     auto k = dgrad_kernel<C>;
     allow_lds(k, lds);
