@@ -111,8 +111,7 @@ def main():
     x, y = bf16_dev(d["x"]), torch.empty(w.T, w.H, dtype=torch.bfloat16, device="cuda")
     idx = torch.from_numpy(d["topk_idx"]).cuda()
     wts = torch.from_numpy(d["topk_weights"]).cuda()
-    W1p = torch.empty(w.EL, 2 * w.I, w.H, dtype=torch.bfloat16, device="cuda")
-    W2p = torch.empty(w.EL, w.H, w.I, dtype=torch.bfloat16, device="cuda")
+    W1p, W2p = moe.alloc_packed(shape)
     W1, W2 = bf16_dev(d["W1"]), bf16_dev(d["W2"])
     moe.pack_weights(shape, W1, W2, W1p, W2p)
     del W1, W2

@@ -2,7 +2,7 @@
  * moe.h — C ABI of the MI355X (gfx950) MoE expert-layer library, one GPU's share of the
  * experts.
  *
- * The layer follows the "Mega MoE" page (Primus-Turbo, docs/README_Mega_MoE.md), section
+ * The layer follows the "Mega MoE" page (Primus-Turbo documentation), section
  * Pipeline: a dispatch prologue builds routing tables from external top-k routing; the
  * dispatched token rows go through an L1 grouped GEMM (NT) into a [gate | up] projection;
  * SwiGLU; an L2 grouped GEMM (NT); and a combine that weights each row by its top-k weight
@@ -88,6 +88,8 @@ typedef struct moe_shape {
  *   hgu            bf16  [R_max, 2I]    pre-activation rows (train only, else 0)
  *   dact           bf16  [R_max, I]     L2 dgrad rows (train only, else 0)
  *   dhgu           bf16  [R_max, 2I]    [gate | up] gradient rows (train only, else 0)
+ *   zeros          bf16  [max(H, 2I)]   a zero row (written by moe_route_prologue), read in place
+ *                                       of the token row of a padding row
  *   scratch        prologue scratch (per-chunk expert histograms)
  */
 typedef struct moe_ws_layout {
@@ -95,7 +97,7 @@ typedef struct moe_ws_layout {
     int64_t rows_capacity;
     int64_t num_blocks;
     size_t counts, padded_offsets, row_pair, pair_row, tile_expert, tok_nloc, meta;
-    size_t act, stage, hgu, dact, dhgu, scratch;
+    size_t act, stage, hgu, dact, dhgu, zeros, scratch;
 } moe_ws_layout;
 
 /* Message for a status code (static string). */

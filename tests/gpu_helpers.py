@@ -85,8 +85,7 @@ def layer(w, d, block_m, train=False, weights=True):
     if "dy" in d:
         ns.dy = bf16_dev(d["dy"])
     if weights:
-        ns.W1p = torch.empty(w.EL, 2 * w.I, w.H, dtype=torch.bfloat16, device="cuda")
-        ns.W2p = torch.empty(w.EL, w.H, w.I, dtype=torch.bfloat16, device="cuda")
+        ns.W1p, ns.W2p = moe.alloc_packed(shape)
         W1, W2 = bf16_dev(d["W1"]), bf16_dev(d["W2"])
         moe.pack_weights(shape, W1, W2, ns.W1p, ns.W2p)
         del W1, W2

@@ -59,6 +59,7 @@ def test_workspace_layout(cfg, bm, train):
         assert L[n] % 256 == 0
     assert L["total_bytes"] >= spans[-1][1] and L["scratch"] + 4 <= L["total_bytes"]
     assert moe.workspace_bytes(s) == L["total_bytes"]
+    assert moe.packed_sizes(s) == ((EL, 2 * I, H), (EL, H, I))
 
 
 @pytest.mark.parametrize("field,value,code", [

@@ -51,8 +51,9 @@ def with_empty_expert(w, d):
 def run_forward_backward(w, d, bm):
     ns = layer(w, d, bm, train=True)
     moe.forward(ns.shape, ns.x, ns.idx, ns.wts, ns.W1p, ns.W2p, ns.ws, ns.y)
-    ns.dW1p = torch.full((w.EL, 2 * w.I, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ns.dW2p = torch.full((w.EL, w.H, w.I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    s1, s2 = moe.packed_sizes(ns.shape)
+    ns.dW1p = torch.full(s1, float("nan"), dtype=torch.bfloat16, device="cuda")
+    ns.dW2p = torch.full(s2, float("nan"), dtype=torch.bfloat16, device="cuda")
     moe.backward(ns.shape, ns.x, ns.dy, ns.wts, ns.W2p, ns.ws, ns.dW1p, ns.dW2p)
     torch.cuda.synchronize()
     return ns

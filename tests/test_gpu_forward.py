@@ -132,6 +132,7 @@ def test_pack_weights_is_an_exact_transpose():
     w = REDUCED[0]
     d = mw.inputs(w, 4)
     ns = layer(w, d, 64)
+    assert tuple(ns.W1p.shape) == (w.EL, 2 * w.I, w.H) and tuple(ns.W2p.shape) == (w.EL, w.H, w.I)
     assert np.array_equal(bits_host(ns.W1p), np.ascontiguousarray(d["W1"].transpose(0, 2, 1)))
     assert np.array_equal(bits_host(ns.W2p), np.ascontiguousarray(d["W2"].transpose(0, 2, 1)))
 

@@ -42,7 +42,7 @@ class Shape(ctypes.Structure):
 
 
 _LAYOUT_FIELDS = ("counts", "padded_offsets", "row_pair", "pair_row", "tile_expert", "tok_nloc",
-                  "meta", "act", "stage", "hgu", "dact", "dhgu", "scratch")
+                  "meta", "act", "stage", "hgu", "dact", "dhgu", "zeros", "scratch")
 
 
 class WsLayout(ctypes.Structure):
@@ -145,7 +145,7 @@ _REGION = {  # name -> (dtype, row width in elements or None)
 
 
 def ws_region(ws: torch.Tensor, shape: Shape, name: str) -> torch.Tensor:
-    """A typed view of one workspace region (no copy)."""
+    """A typed view of one workspace region (no copy); row regions are [rows_capacity, width]."""
     L = workspace_layout(shape)
     R = L["rows_capacity"]
     sizes = {"counts": shape.EL, "padded_offsets": shape.EL + 1, "row_pair": R,
@@ -162,6 +162,18 @@ def ws_region(ws: torch.Tensor, shape: Shape, name: str) -> torch.Tensor:
     esz = torch.tensor([], dtype=dtype).element_size()
     t = ws[L[name]:L[name] + n * esz].view(dtype)
     return t.view(*view) if view else t
+
+
+def packed_sizes(shape: Shape):
+    """Tensor sizes of the packed weights: W1p (and dW1p) [EL, 2I, H], W2p (and dW2p) [EL, H, I]."""
+    return ((shape.EL, 2 * shape.I, shape.H), (shape.EL, shape.H, shape.I))
+
+
+def alloc_packed(shape: Shape, device="cuda"):
+    """Uninitialised (W1p, W2p) tensors of the packed sizes."""
+    s1, s2 = packed_sizes(shape)
+    return (torch.empty(s1, dtype=torch.bfloat16, device=device),
+            torch.empty(s2, dtype=torch.bfloat16, device=device))
 
 
 def pack_weights(shape, w1=None, w2=None, w1p=None, w2p=None, stream=None):

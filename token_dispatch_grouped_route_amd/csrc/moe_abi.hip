@@ -28,6 +28,8 @@ int32_t check_shape(const moe_shape* s) {
     // row and element indices stay far inside int32 / int64 ranges
     const int64_t rows = static_cast<int64_t>(s->T) * s->k + static_cast<int64_t>(s->EL) * s->block_m;
     if (rows > (int64_t(1) << 28) || s->H > (1 << 20) || s->I > (1 << 20)) return MOE_ERR_SHAPE;
+    // byte offsets inside one expert's packed weights are 32-bit in the GEMM tile loaders
+    if (4 * static_cast<int64_t>(s->I) * s->H >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -62,6 +64,7 @@ int32_t layout_of(const moe_shape* s, moe_ws_layout* L) {
         L->dact = take(2 * static_cast<size_t>(R) * I);
         L->dhgu = take(2 * static_cast<size_t>(R) * 2 * I);
     }
+    L->zeros = take(2 * (H > 2 * I ? H : 2 * I));
     L->scratch = take(4 * static_cast<size_t>(chunks) * (EL + 1));
     L->total_bytes = off;
     return MOE_OK;
@@ -108,6 +111,8 @@ int32_t prepare(const moe_shape* s, const void* ws, size_t ws_bytes, bool need_t
     w->num_chunks = static_cast<int32_t>(pairs > 0 ? (pairs + kRouteChunk - 1) / kRouteChunk : 1);
     w->chunk_hist = reinterpret_cast<int32_t*>(b + L->scratch);
     w->chunk_dropped = w->chunk_hist + static_cast<int64_t>(w->num_chunks) * s->EL;
+    w->zeros = reinterpret_cast<uint16_t*>(b + L->zeros);
+    w->zero_len = s->H > 2 * s->I ? s->H : 2 * s->I;
     w->rows_cap = L->rows_capacity;
     w->num_blocks = static_cast<int32_t>(L->num_blocks);
     return MOE_OK;

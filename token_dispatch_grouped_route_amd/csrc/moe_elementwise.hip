@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
     const int e = blockIdx.z;
     const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     const uint16_t* src = in + static_cast<int64_t>(e) * R * C;
-    uint16_t* dst = out + static_cast<int64_t>(e) * R * C;
+    uint16_t* dst = out + static_cast<int64_t>(e) * C * R;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int r = ty; r < 64; r += 4)
         if (r0 + r < R && c0 + tx < C) tile[r][tx] = src[static_cast<int64_t>(r0 + r) * C + c0 + tx];

@@ -660,6 +660,223 @@ __global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------------------------
+// L1 GEMM with a direct-to-LDS operand ring
+// ---------------------------------------------------------------------------------------------
+// The L1 GEMM is bound by moving operands into the CUs, so this kernel keeps more bytes in
+// flight per CU for the same LDS: K advances 32 per stage (64-byte LDS rows), operands go straight
+// from global memory into a 3-stage LDS ring with global_load_lds_dwordx4 (no staging registers,
+// no LDS store instructions), two stages stay in flight while the MFMAs consume the third, and the
+// epilogue goes through LDS one band of wave rows at a time so two workgroups still fit per CU.
+typedef __attribute__((address_space(1))) void g_void;
+typedef __attribute__((address_space(3))) void l_void;
+
+constexpr int BKD = 32;   // K per ring stage
+
+// 16-byte chunk c (0..3) of 64-byte row r sits at position c ^ ((r >> 2) & 3): four rows fill the
+// 64 banks, and the 16 rows of a 16-lane fragment read land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int lds_off32(int row, int chunk) {
+    return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct DCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int MI = TM / 32, NI = TN / 32;
+    static constexpr int STAGES = 3;
+    static constexpr int A_BYTES = BM * BKD * 2, B_BYTES = BN * BKD * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int C_STRIDE = BN + 8;             // see Cfg::C_STRIDE
+    static constexpr int C_BYTES = TM * C_STRIDE * 4;   // one band of TM rows
+    static constexpr int LDS_BYTES = RING_BYTES > C_BYTES ? RING_BYTES : C_BYTES;
+    static constexpr int MIN_WG = 2;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+};
+
+// One instruction fills 16 rows x 64 bytes of a stage: lane L lands at position L & 3 of row
+// 16g + L/4 and fetches the logical chunk the swizzle keeps there.
+template <int ROWS, int NT>
+struct Ring {
+    static constexpr int GROUPS = ROWS / 16;
+    static constexpr int WAVES = NT / 64;
+    static constexpr int PER = GROUPS / WAVES;   // instructions per wave per stage
+    static_assert(GROUPS % WAVES == 0, "row groups must split evenly over the waves");
+    const char* src[PER];   // the lane's chunk in its row at K step 0
+    int wave;
+
+    __device__ __forceinline__ static int row_of(int wave, int i, int lane) { return 16 * (wave + WAVES * i) + (lane >> 2); }
+    __device__ __forceinline__ static int chunk_of(int wave, int i, int lane) {
+        return (lane & 3) ^ ((row_of(wave, i, lane) >> 2) & 3);
+    }
+    __device__ __forceinline__ void issue(int kt, char* stage) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            __builtin_amdgcn_global_load_lds((g_void*)(src[i] + kt * (BKD * 2)),
+                                             (l_void*)(stage + 1024 * (wave + WAVES * i)), 16, 0, 0);
+    }
+};
+
+// s_waitcnt vmcnt(n) alone (gfx9 encoding: expcnt and lgkmcnt fields at their "no wait" maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <class C>
+__device__ __forceinline__ void mma_step32(const char* lA, const char* lB, f32x16_t (&acc)[C::MI][C::NI],
+                                           int wm0, int wn0, int lane) {
+    bf16x8_t a[2][C::MI], b[2][C::NI];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+            a[s][i] = *reinterpret_cast<const bf16x8_t*>(lA + lds_off32(wm0 + i * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+            b[s][j] = *reinterpret_cast<const bf16x8_t*>(lB + lds_off32(wn0 + j * 32 + (lane & 31), ch));
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][i], b[s][j], acc[i][j], 0, 0, 0);
+}
+
+// K loop over the ring.  Every iteration issues one stage (past the end it re-reads the last step
+// into a free stage, never read), so exactly one stage of this wave's loads is still allowed in
+// flight when a stage is consumed.  Ends with no load in flight, so the caller may reuse the LDS.
+template <class C, class LA, class LB>
+__device__ __forceinline__ void gemm_tile_ring(const LA& la, const LB& lb, int nk, char* smem,
+                                               f32x16_t (&acc)[C::MI][C::NI], int wm0, int wn0, int lane) {
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    if (nk <= 0) return;
+    constexpr int PER_STEP = LA::PER + LB::PER;
+    la.issue(0, smem);
+    lb.issue(0, smem + C::A_BYTES);
+    char* s1 = smem + C::STAGE_BYTES;
+    la.issue(min(1, nk - 1), s1);
+    lb.issue(min(1, nk - 1), s1 + C::A_BYTES);
+    int cur = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<PER_STEP>();   // this wave's loads of step kt have landed
+        __syncthreads();          // everyone's have, and stage (kt+2)%3 = (kt-1)%3 is no longer read
+        const int nxt2 = cur == 0 ? 2 : cur - 1;   // (kt + 2) % 3
+        char* st = smem + nxt2 * C::STAGE_BYTES;
+        const int kl = min(kt + 2, nk - 1);
+        la.issue(kl, st);
+        lb.issue(kl, st + C::A_BYTES);
+        const char* sc = smem + cur * C::STAGE_BYTES;
+        mma_step32<C>(sc, sc + C::A_BYTES, acc, wm0, wn0, lane);
+        cur = cur == 2 ? 0 : cur + 1;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+}
+
+// Accumulators of the waves in row band `band` to the C tile (band-local rows).
+template <class C, class ColOf>
+__device__ __forceinline__ void band_to_lds(float* ct, const f32x16_t (&acc)[C::MI][C::NI], int lane, ColOf col_of) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni) {
+            const int col = col_of(ni) + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ct[(mi * 32 + acc_row(r, lane)) * C::C_STRIDE + col] = acc[mi][ni][r];
+        }
+}
+
+// gemm1 on the ring: dispatch gather + L1 (NT) + SwiGLU, same tile order and column mapping as
+// gemm1_kernel (each wave's TN weight rows are [gate | up] of TN/2 intermediate columns).
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_ring_kernel(const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ w1p, Dims d,
+                                                                       Ws ws, uint16_t* __restrict__ act_out,
+                                                                       uint16_t* __restrict__ hgu_out) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int wm0 = wm * C::TM, wn0 = wn * C::TN;
+    const int H = d.H, I = d.I;
+    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);
+    const int n_tiles = (2 * I) / C::BN;
+    const int total = m_tiles * n_tiles;
+    const int npairs = d.T * d.k;
+    constexpr int HALF = C::TN / 2;
+    const char* zrow = reinterpret_cast<const char*>(ws.zeros);
+
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        const int mt = tile / n_tiles, nt = tile - mt * n_tiles;
+        const int e = ws.tile_expert[mt];
+        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
+        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
+
+        Ring<C::BM, C::NT> la;   // token rows through row_pair; padding rows read the zero row
+        la.wave = wave;
+#pragma unroll
+        for (int i = 0; i < la.PER; ++i) {
+            const int p = ws.row_pair[row0 + la.row_of(wave, i, lane)];
+            const int c16 = 16 * la.chunk_of(wave, i, lane);
+            la.src[i] = (p >= 0 && p < npairs)
+                            ? reinterpret_cast<const char*>(x + static_cast<int64_t>(p / d.k) * H) + c16
+                            : zrow + c16;
+        }
+        Ring<C::BN, C::NT> lb;
+        const char* wbase = reinterpret_cast<const char*>(w1p + static_cast<int64_t>(e) * 2 * I * H);
+        lb.wave = wave;
+#pragma unroll
+        for (int i = 0; i < lb.PER; ++i) {
+            const int nl = lb.row_of(wave, i, lane);
+            const int w = nl / C::TN, j = nl % C::TN;
+            const int grow = (j / HALF) * I + nt * (C::BN / 2) + w * HALF + (j % HALF);
+            lb.src[i] = wbase + static_cast<int64_t>(grow) * H * 2 + 16 * lb.chunk_of(wave, i, lane);
+        }
+        f32x16_t acc[C::MI][C::NI];
+        __syncthreads();   // the previous tile's epilogue reads of LDS are done
+        gemm_tile_ring<C>(la, lb, H / BKD, smem, acc, wm0, wn0, lane);
+
+        float* ct = reinterpret_cast<float*>(smem);
+        constexpr int CH = C::BN / 16;
+        const int c0 = nt * (C::BN / 2);
+        for (int band = 0; band < C::WM; ++band) {
+            if (wm == band)
+                band_to_lds<C>(ct, acc, lane, [&](int ni) {
+                    return ni < C::NI / 2 ? wn * HALF + ni * 32 : C::BN / 2 + wn * HALF + (ni - C::NI / 2) * 32;
+                });
+            __syncthreads();
+            for (int u = tid; u < C::TM * CH; u += C::NT) {
+                const int rl = u / CH, c8 = (u % CH) * 8;
+                const int64_t row = row0 + band * C::TM + rl;
+                float g[8], up[8], a[8];
+                ld8(ct + rl * C::C_STRIDE + c8, g);
+                ld8(ct + rl * C::C_STRIDE + C::BN / 2 + c8, up);
+                if (hgu_out) {
+                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + c0 + c8) = bf16x8_of(g);
+                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + I + c0 + c8) = bf16x8_of(up);
+                }
+                if (act_out) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) a[q] = silu_f32(g[q]) * up[q];
+                    *reinterpret_cast<u32x4*>(act_out + row * I + c0 + c8) = bf16x8_of(a);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------------------------
 int device_cu_count() {
@@ -744,8 +961,24 @@ static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* t
     return hipGetLastError();
 }
 
+using R128 = DCfg<128, 256, 2, 2>;   // ring kernel for block_m 128
+
+template <class C>
+static hipError_t gemm1_ring_launch(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
+                                    uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
+    const size_t lds = C::LDS_BYTES;
+    auto k = gemm1_ring_kernel<C>;
+    allow_lds(k, lds);
+    const int n_tiles = 2 * d.I / C::BN;
+    const int grid = persistent_grid(k, C::NT, lds, n_tiles, static_cast<int64_t>(ws.num_blocks) * n_tiles);
+    k<<<grid, C::NT, lds, s>>>(x, w1p, d, ws, act_out, hgu_out);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
                         uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
+    if (d.BM == 128 && (2 * d.I) % R128::BN == 0 && d.H % BKD == 0)
+        return gemm1_ring_launch<R128>(d, x, w1p, ws, act_out, hgu_out, s);
     switch (d.BM) {
         case 32: return gemm1_launch<G32>(d, x, w1p, ws, act_out, hgu_out, s);
         case 64: return gemm1_launch<G64>(d, x, w1p, ws, act_out, hgu_out, s);

@@ -33,9 +33,11 @@ struct Ws {
     uint16_t* hgu;          // bf16 [R_max, 2I] (train)
     uint16_t* dact;         // bf16 [R_max, I]  (train)
     uint16_t* dhgu;         // bf16 [R_max, 2I] (train)
+    uint16_t* zeros;        // a zero row of max(H, 2I) bf16 (written by the prologue)
     int64_t rows_cap;
     int32_t num_blocks;     // R_max / BM
     int32_t num_chunks;     // prologue chunks of kRouteChunk pairs
+    int32_t zero_len;       // elements of the zero row
 };
 
 constexpr int kRouteThreads = 256;
