@@ -22,11 +22,13 @@
 //   wgrad2  dW2 = dO^T A, K = rows of the expert (variable K), TN
 //   wgrad1  dW1 = dHgu^T X with X re-gathered from x, TN
 //
-// Forward launches are persistent: a fixed grid (CUs x occupancy) walks the tile list whose
-// length R / BM * n_tiles is read from the workspace on the device, so the host never needs R.
-// Tiles are numbered M-major with N fastest and the grid is a multiple of the N-tile count
-// when possible, so a workgroup keeps its weight panel (N tile) and the M tiles of one expert
-// that share a panel run at the same time on the same XCD (workgroup ids congruent mod 8).
+// Row-tiled launches (gemm1, gemm2, dgrad) are persistent: a fixed grid (CUs x occupancy) walks
+// the tile list whose length R / BM * n_tiles is read from the workspace on the device, so the
+// host never needs R.  The list is ordered expert by expert, and inside an expert N-panel by
+// N-panel with the expert's M tiles adjacent; it is cut into one contiguous chunk per XCD (the
+// hardware places workgroup b on XCD b mod 8, each XCD with its own L2).  So one XCD fetches a
+// given weight panel and a given expert's token rows, and the workgroups that read the same
+// panel run side by side.
 #include "moe_internal.h"
 
 namespace moe {
@@ -290,6 +292,48 @@ __device__ __forceinline__ u32x4 bf16x8_of(const float (&f)[8]) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Tile schedule of the row-tiled launches
+// ---------------------------------------------------------------------------------------------
+constexpr int kXcds = 8;
+
+// The positions [begin, end) (stride step) of the tile list that this workgroup runs: one
+// contiguous chunk per XCD when the grid covers the XCDs evenly, else a plain round robin.
+struct TileRange {
+    int begin, end, step;
+    __device__ explicit TileRange(int total) {
+        const int G = gridDim.x;
+        if (G % kXcds == 0) {
+            const int x = blockIdx.x % kXcds;
+            const int chunk = (total + kXcds - 1) / kXcds;
+            begin = x * chunk + blockIdx.x / kXcds;
+            end = min(total, (x + 1) * chunk);
+            step = G / kXcds;
+        } else {
+            begin = blockIdx.x;
+            end = total;
+            step = G;
+        }
+    }
+};
+
+// Position t of the tile list -> (M tile, N tile).  Expert e owns positions
+// [m0 * n_tiles, (m0 + mc) * n_tiles) where its segment is M tiles [m0, m0 + mc), so the expert
+// is found from the M tile at t / n_tiles; inside its run the M index varies fastest.
+__device__ __forceinline__ void tile_at(const Ws& ws, const Dims& d, int n_tiles, int t, int& mt, int& nt) {
+    const int m = t / n_tiles;
+    mt = m;
+    nt = t - m * n_tiles;
+    const int e = ws.tile_expert[m];
+    if (e < 0 || e >= d.EL) return;   // the caller skips this tile
+    const int m0 = ws.offsets[e] / d.BM;
+    const int mc = (ws.offsets[e + 1] - ws.offsets[e]) / d.BM;
+    if (mc < 1 || m < m0 || m >= m0 + mc) return;   // tables not from one prologue: keep M-major
+    const int local = t - m0 * n_tiles;
+    nt = local / mc;
+    mt = m0 + (local - nt * mc);
+}
+
+// ---------------------------------------------------------------------------------------------
 // gemm1: dispatch gather + L1 (NT) + SwiGLU
 // ---------------------------------------------------------------------------------------------
 // Each N tile holds BN/2 gate columns and the BN/2 matching up columns: wave wn's TN rows of the
@@ -310,8 +354,10 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_kernel(const uint16_t*
     const int npairs = d.T * d.k;
     constexpr int HALF = C::TN / 2;   // intermediate columns per wave
 
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const int mt = tile / n_tiles, nt = tile - mt * n_tiles;
+    const TileRange tr(total);
+    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
+        int mt, nt;
+        tile_at(ws, d, n_tiles, tile, mt, nt);
         const int e = ws.tile_expert[mt];
         if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
         const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
@@ -390,8 +436,10 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm2_kernel(const uint16_t*
     const int total = m_tiles * n_tiles;
     const int npairs = d.T * d.k;
 
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const int mt = tile / n_tiles, nt = tile - mt * n_tiles;
+    const TileRange tr(total);
+    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
+        int mt, nt;
+        tile_at(ws, d, n_tiles, tile, mt, nt);
         const int e = ws.tile_expert[mt];
         if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
         const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
@@ -476,8 +524,10 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const uint16_t* __restrict
     const int total = m_tiles * n_tiles;
     const int npairs = d.T * d.k;
 
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const int mt = tile / n_tiles, nt = tile - mt * n_tiles;
+    const TileRange tr(total);
+    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
+        int mt, nt;
+        tile_at(ws, d, n_tiles, tile, mt, nt);
         const int e = ws.tile_expert[mt];
         if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
         const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
@@ -662,15 +712,16 @@ __global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restric
 // ---------------------------------------------------------------------------------------------
 // L1 GEMM with a direct-to-LDS operand ring
 // ---------------------------------------------------------------------------------------------
-// The L1 GEMM is bound by moving operands into the CUs, so this kernel keeps more bytes in
-// flight per CU for the same LDS: K advances 32 per stage (64-byte LDS rows), operands go straight
-// from global memory into a 3-stage LDS ring with global_load_lds_dwordx4 (no staging registers,
-// no LDS store instructions), two stages stay in flight while the MFMAs consume the third, and the
-// epilogue goes through LDS one band of wave rows at a time so two workgroups still fit per CU.
+// The L1 GEMM is bound by moving operands into the CUs.  Here operands go straight from global
+// memory into a multi-stage LDS ring with global_load_lds_dwordx4 (no staging registers, no LDS
+// store instructions) and STAGES - 1 stages stay in flight while the MFMAs consume one.  Each
+// load instruction should cover whole 128-byte lines: one that reads 64 bytes from each of 16
+// rows moves half as many bytes per cycle, from L2 and from HBM, as one that reads 128 bytes
+// from each of 8 rows.  So K advances 64 per stage (128-byte LDS rows, the same swizzled layout
+// as the register-staged kernels); a 32-per-stage form (64-byte rows) is kept for small tiles.
+// The epilogue goes through LDS one band of wave rows at a time, inside the ring's memory.
 typedef __attribute__((address_space(1))) void g_void;
 typedef __attribute__((address_space(3))) void l_void;
-
-constexpr int BKD = 32;   // K per ring stage
 
 // 16-byte chunk c (0..3) of 64-byte row r sits at position c ^ ((r >> 2) & 3): four rows fill the
 // 64 banks, and the 16 rows of a 16-lane fragment read land on 16 distinct 16-byte bank groups.
@@ -678,42 +729,48 @@ __device__ __forceinline__ int lds_off32(int row, int chunk) {
     return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int KS_, int STAGES_, int MIN_WG_>
 struct DCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int KS = KS_;           // K per ring stage: 32 or 64
+    static constexpr int STAGES = STAGES_;   // 3: two stages in flight
+    static constexpr int MIN_WG = MIN_WG_;   // workgroups per CU the registers must allow
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int MI = TM / 32, NI = TN / 32;
-    static constexpr int STAGES = 3;
-    static constexpr int A_BYTES = BM * BKD * 2, B_BYTES = BN * BKD * 2;
+    static constexpr int A_BYTES = BM * KS * 2, B_BYTES = BN * KS * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
     static constexpr int C_STRIDE = BN + 8;             // see Cfg::C_STRIDE
     static constexpr int C_BYTES = TM * C_STRIDE * 4;   // one band of TM rows
     static constexpr int LDS_BYTES = RING_BYTES > C_BYTES ? RING_BYTES : C_BYTES;
-    static constexpr int MIN_WG = 2;
+    static_assert(KS == 32 || KS == 64, "ring stage depth");
+    static_assert(STAGES == 3, "the K loop keeps two stages in flight");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
 };
 
-// One instruction fills 16 rows x 64 bytes of a stage: lane L lands at position L & 3 of row
-// 16g + L/4 and fetches the logical chunk the swizzle keeps there.
-template <int ROWS, int NT>
+// One instruction fills 1 KB of a stage, RPI rows of KS * 2 bytes: lane L lands at position
+// L % LPR of row RPI * g + L / LPR and fetches the logical chunk the swizzle keeps there.
+template <int ROWS, int NT, int KS>
 struct Ring {
-    static constexpr int GROUPS = ROWS / 16;
+    static constexpr int LPR = KS / 8;    // lanes per row (16 bytes each)
+    static constexpr int RPI = 64 / LPR;  // rows per instruction
+    static constexpr int GROUPS = ROWS / RPI;
     static constexpr int WAVES = NT / 64;
     static constexpr int PER = GROUPS / WAVES;   // instructions per wave per stage
     static_assert(GROUPS % WAVES == 0, "row groups must split evenly over the waves");
     const char* src[PER];   // the lane's chunk in its row at K step 0
     int wave;
 
-    __device__ __forceinline__ static int row_of(int wave, int i, int lane) { return 16 * (wave + WAVES * i) + (lane >> 2); }
+    __device__ __forceinline__ static int row_of(int wave, int i, int lane) { return RPI * (wave + WAVES * i) + lane / LPR; }
     __device__ __forceinline__ static int chunk_of(int wave, int i, int lane) {
-        return (lane & 3) ^ ((row_of(wave, i, lane) >> 2) & 3);
+        const int r = row_of(wave, i, lane);
+        return KS == 64 ? (lane & 7) ^ ((r >> 1) & 7) : (lane & 3) ^ ((r >> 2) & 3);
     }
     __device__ __forceinline__ void issue(int kt, char* stage) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            __builtin_amdgcn_global_load_lds((g_void*)(src[i] + kt * (BKD * 2)),
+            __builtin_amdgcn_global_load_lds((g_void*)(src[i] + kt * (KS * 2)),
                                              (l_void*)(stage + 1024 * (wave + WAVES * i)), 16, 0, 0);
     }
 };
@@ -777,7 +834,10 @@ __device__ __forceinline__ void gemm_tile_ring(const LA& la, const LB& lb, int n
         la.issue(kl, st);
         lb.issue(kl, st + C::A_BYTES);
         const char* sc = smem + cur * C::STAGE_BYTES;
-        mma_step32<C>(sc, sc + C::A_BYTES, acc, wm0, wn0, lane);
+        if constexpr (C::KS == 64)
+            mma_step<C>(sc, sc + C::A_BYTES, acc, wm0, wn0, lane);
+        else
+            mma_step32<C>(sc, sc + C::A_BYTES, acc, wm0, wn0, lane);
         cur = cur == 2 ? 0 : cur + 1;
     }
     wait_vmcnt<0>();
@@ -816,13 +876,15 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_ring_kernel(const uint
     constexpr int HALF = C::TN / 2;
     const char* zrow = reinterpret_cast<const char*>(ws.zeros);
 
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const int mt = tile / n_tiles, nt = tile - mt * n_tiles;
+    const TileRange tr(total);
+    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
+        int mt, nt;
+        tile_at(ws, d, n_tiles, tile, mt, nt);
         const int e = ws.tile_expert[mt];
         if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
         const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
 
-        Ring<C::BM, C::NT> la;   // token rows through row_pair; padding rows read the zero row
+        Ring<C::BM, C::NT, C::KS> la;   // token rows through row_pair; padding rows read the zero row
         la.wave = wave;
 #pragma unroll
         for (int i = 0; i < la.PER; ++i) {
@@ -832,7 +894,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_ring_kernel(const uint
                             ? reinterpret_cast<const char*>(x + static_cast<int64_t>(p / d.k) * H) + c16
                             : zrow + c16;
         }
-        Ring<C::BN, C::NT> lb;
+        Ring<C::BN, C::NT, C::KS> lb;
         const char* wbase = reinterpret_cast<const char*>(w1p + static_cast<int64_t>(e) * 2 * I * H);
         lb.wave = wave;
 #pragma unroll
@@ -844,7 +906,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_ring_kernel(const uint
         }
         f32x16_t acc[C::MI][C::NI];
         __syncthreads();   // the previous tile's epilogue reads of LDS are done
-        gemm_tile_ring<C>(la, lb, H / BKD, smem, acc, wm0, wn0, lane);
+        gemm_tile_ring<C>(la, lb, H / C::KS, smem, acc, wm0, wn0, lane);
 
         float* ct = reinterpret_cast<float*>(smem);
         constexpr int CH = C::BN / 16;
@@ -876,6 +938,98 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_ring_kernel(const uint
     }
 }
 
+// gemm1 with one row band of waves (WM = 1): each wave holds whole rows of TN/2 gate columns and
+// the matching up columns, so SwiGLU runs on the accumulators; the bf16 results go through a
+// wave-private LDS slab (TM rows x TN/2 columns) and leave as 16-byte row segments.
+template <class C>
+struct WideEpi {
+    static constexpr int HALF = C::TN / 2;         // intermediate columns per wave
+    static constexpr int LD = HALF + 8;            // slab row stride (elements): the two half-waves
+                                                   // of an accumulator write land 64 banks apart
+    static constexpr int SLAB = C::TM * LD;        // elements per wave
+    static constexpr int LDS_BYTES = (C::NT / 64) * SLAB * 2;
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_wide_kernel(const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ w1p, Dims d,
+                                                                       Ws ws, uint16_t* __restrict__ act_out,
+                                                                       uint16_t* __restrict__ hgu_out) {
+    static_assert(C::WM == 1, "one row band of waves");
+    using Epi = WideEpi<C>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave, wn0 = wn * C::TN;
+    const int H = d.H, I = d.I;
+    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);
+    const int n_tiles = (2 * I) / C::BN;
+    const int total = m_tiles * n_tiles;
+    const int npairs = d.T * d.k;
+    constexpr int HALF = Epi::HALF, NH = C::NI / 2;
+    const char* zrow = reinterpret_cast<const char*>(ws.zeros);
+    uint16_t* slab = reinterpret_cast<uint16_t*>(smem) + wave * Epi::SLAB;
+
+    const TileRange tr(total);
+    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
+        int mt, nt;
+        tile_at(ws, d, n_tiles, tile, mt, nt);
+        const int e = ws.tile_expert[mt];
+        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
+        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
+
+        Ring<C::BM, C::NT, C::KS> la;   // token rows through row_pair; padding rows read the zero row
+        la.wave = wave;
+#pragma unroll
+        for (int i = 0; i < la.PER; ++i) {
+            const int p = ws.row_pair[row0 + la.row_of(wave, i, lane)];
+            const int c16 = 16 * la.chunk_of(wave, i, lane);
+            la.src[i] = (p >= 0 && p < npairs)
+                            ? reinterpret_cast<const char*>(x + static_cast<int64_t>(p / d.k) * H) + c16
+                            : zrow + c16;
+        }
+        Ring<C::BN, C::NT, C::KS> lb;
+        const char* wbase = reinterpret_cast<const char*>(w1p + static_cast<int64_t>(e) * 2 * I * H);
+        lb.wave = wave;
+#pragma unroll
+        for (int i = 0; i < lb.PER; ++i) {
+            const int nl = lb.row_of(wave, i, lane);
+            const int w = nl / C::TN, j = nl % C::TN;
+            const int grow = (j / HALF) * I + nt * (C::BN / 2) + w * HALF + (j % HALF);
+            lb.src[i] = wbase + static_cast<int64_t>(grow) * H * 2 + 16 * lb.chunk_of(wave, i, lane);
+        }
+        f32x16_t acc[C::MI][C::NI];
+        __syncthreads();   // the previous tile's epilogue reads of LDS are done
+        gemm_tile_ring<C>(la, lb, H / C::KS, smem, acc, 0, wn0, lane);
+
+        // passes: gate and up pre-activations (when hgu_out), then SwiGLU (when act_out)
+        const int c0 = nt * (C::BN / 2) + wn * HALF;
+        for (int pass = 0; pass < 3; ++pass) {
+            uint16_t* out = pass < 2 ? hgu_out : act_out;
+            if (!out) continue;   // uniform
+            const int64_t ld = pass < 2 ? 2 * static_cast<int64_t>(I) : I;
+            const int col0 = (pass == 1 ? I : 0) + c0;
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int jj = 0; jj < NH; ++jj)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float g = acc[mi][jj][r], u = acc[mi][jj + NH][r];
+                        const float v = pass == 0 ? g : pass == 1 ? u : silu_f32(g) * u;
+                        slab[(mi * 32 + acc_row(r, lane)) * Epi::LD + jj * 32 + (lane & 31)] = f32_to_bf16(v);
+                    }
+            __syncthreads();
+            constexpr int CPR = HALF / 8;   // 16-byte chunks per row
+            for (int u = lane; u < C::TM * CPR; u += 64) {
+                const int rl = u / CPR, ch = u - rl * CPR;
+                *reinterpret_cast<u32x4*>(out + (row0 + rl) * ld + col0 + ch * 8) =
+                    *reinterpret_cast<const u32x4*>(slab + rl * Epi::LD + ch * 8);
+            }
+            __syncthreads();   // the slab is rewritten by the next pass
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------------------------
@@ -892,22 +1046,17 @@ int device_cu_count() {
     return cached[dev];
 }
 
-// Persistent grid for a kernel: resident workgroups on the whole device, rounded down to a
-// multiple of the N-tile count when that keeps at least 3/4 of them (so a workgroup keeps one
-// N tile), capped by the most tiles the launch can have.
+// Persistent grid for a kernel: resident workgroups on the whole device, capped by the most
+// tiles the launch can have, rounded down to a multiple of the XCD count.
 template <class K>
-static int persistent_grid(K kernel, int threads, size_t lds, int n_tiles, int64_t max_tiles) {
+static int persistent_grid(K kernel, int threads, size_t lds, int64_t max_tiles) {
     static_assert(sizeof(K) > 0, "");
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
         per_cu = 1;
     int64_t g = static_cast<int64_t>(per_cu) * device_cu_count();
-    if (n_tiles > 0 && g >= n_tiles) {
-        const int64_t r = g / n_tiles * n_tiles;
-        if (4 * r >= 3 * g) g = r;
-    }
     if (g > max_tiles) g = max_tiles;
-    if (g >= 8) g &= ~int64_t(7);   // whole groups of 8 (one workgroup per XCD in each group)
+    if (g >= kXcds) g -= g % kXcds;   // the same number of workgroups on every XCD
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
@@ -931,7 +1080,7 @@ static hipError_t gemm1_launch(const Dims& d, const uint16_t* x, const uint16_t*
     auto k = gemm1_kernel<C>;
     allow_lds(k, lds);
     const int n_tiles = 2 * d.I / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, n_tiles, static_cast<int64_t>(ws.num_blocks) * n_tiles);
+    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
     k<<<grid, C::NT, lds, s>>>(x, w1p, d, ws, act_out, hgu_out);
     return hipGetLastError();
 }
@@ -943,7 +1092,7 @@ static hipError_t gemm2_launch(const Dims& d, const uint16_t* act, const uint16_
     auto k = gemm2_kernel<C>;
     allow_lds(k, lds);
     const int n_tiles = d.H / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, n_tiles, static_cast<int64_t>(ws.num_blocks) * n_tiles);
+    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
     k<<<grid, C::NT, lds, s>>>(act, w2p, topk_w, d, ws, y);
     return hipGetLastError();
 }
@@ -956,12 +1105,12 @@ static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* t
     auto k = dgrad_kernel<C>;
     allow_lds(k, lds);
     const int n_tiles = d.I / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, n_tiles, static_cast<int64_t>(ws.num_blocks) * n_tiles);
+    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
     k<<<grid, C::NT, lds, s>>>(dy, topk_w, w2p, d, ws, fuse);
     return hipGetLastError();
 }
 
-using R128 = DCfg<128, 256, 2, 2>;   // ring kernel for block_m 128
+using R128 = DCfg<128, 256, 2, 2, 32, 3, 2>;   // ring kernel for block_m 128
 
 template <class C>
 static hipError_t gemm1_ring_launch(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
@@ -970,14 +1119,32 @@ static hipError_t gemm1_ring_launch(const Dims& d, const uint16_t* x, const uint
     auto k = gemm1_ring_kernel<C>;
     allow_lds(k, lds);
     const int n_tiles = 2 * d.I / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, n_tiles, static_cast<int64_t>(ws.num_blocks) * n_tiles);
+    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
+    k<<<grid, C::NT, lds, s>>>(x, w1p, d, ws, act_out, hgu_out);
+    return hipGetLastError();
+}
+
+using W128 = DCfg<128, 512, 1, 4, 32, 3, 1>;   // wide ring kernel for block_m 128
+
+template <class C>
+static hipError_t gemm1_wide_launch(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
+                                    uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
+    const size_t lds = C::RING_BYTES > WideEpi<C>::LDS_BYTES ? C::RING_BYTES : WideEpi<C>::LDS_BYTES;
+    auto k = gemm1_wide_kernel<C>;
+    allow_lds(k, lds);
+    const int n_tiles = 2 * d.I / C::BN;
+    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
     k<<<grid, C::NT, lds, s>>>(x, w1p, d, ws, act_out, hgu_out);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
                         uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
-    if (d.BM == 128 && (2 * d.I) % R128::BN == 0 && d.H % BKD == 0)
+#ifdef MOE_WIDE_L1
+    if (d.BM == 128 && (2 * d.I) % W128::BN == 0 && d.H % W128::KS == 0)
+        return gemm1_wide_launch<W128>(d, x, w1p, ws, act_out, hgu_out, s);
+#endif
+    if (d.BM == 128 && (2 * d.I) % R128::BN == 0 && d.H % R128::KS == 0)
         return gemm1_ring_launch<R128>(d, x, w1p, ws, act_out, hgu_out, s);
     switch (d.BM) {
         case 32: return gemm1_launch<G32>(d, x, w1p, ws, act_out, hgu_out, s);
