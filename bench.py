@@ -32,7 +32,7 @@ import token_dispatch_grouped_route_amd as moe  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-GEMM_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_gemm.hip")
+GEMM_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_grouped.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_dsv3_share_traffic.json")
 
 

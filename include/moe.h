@@ -58,8 +58,7 @@ typedef enum moe_status {
  * Layer shape (host struct).
  *   T        tokens on this GPU (>= 0)
  *   H        hidden size (multiple of 128)
- *   I        intermediate size; the L1 output is [gate | up], 2*I wide (multiple of 64;
- *            multiple of 128 for the backward entry points)
+ *   I        intermediate size; the L1 output is [gate | up], 2*I wide (multiple of 128)
  *   E        experts in routing; ids in [0, E) are valid
  *   e_lo     first expert owned by this GPU; it owns ids [e_lo, e_lo + EL), e_lo + EL <= E
  *   EL       experts owned by this GPU (1 .. 1024)
@@ -91,13 +90,15 @@ typedef struct moe_shape {
  *   zeros          bf16  [max(H, 2I)]   a zero row (written by moe_route_prologue), read in place
  *                                       of the token row of a padding row
  *   scratch        prologue scratch (per-chunk expert histograms)
+ *   tile_sync      int32 [512]          tile-scheduler counters of the forward GEMMs (zeroed by
+ *                                       moe_route_prologue; zero again after each GEMM launch)
  */
 typedef struct moe_ws_layout {
     size_t total_bytes;
     int64_t rows_capacity;
     int64_t num_blocks;
     size_t counts, padded_offsets, row_pair, pair_row, tile_expert, tok_nloc, meta;
-    size_t act, stage, hgu, dact, dhgu, zeros, scratch;
+    size_t act, stage, hgu, dact, dhgu, zeros, scratch, tile_sync;
 } moe_ws_layout;
 
 /* Message for a status code (static string). */
@@ -113,15 +114,29 @@ int32_t moe_workspace_layout(const moe_shape* shape, moe_ws_layout* out /* [host
 int32_t moe_preferred_block_m(const moe_shape* shape);
 
 /*
- * One-time weight transform (untimed): the logical x @ W layouts become K-major ("NT")
- * layouts, as in the weight transform step of the "How Mega MoE Overlaps ..." page's
- * example.
- *   w1  [device] bf16 [EL, H, 2I]  ->  w1p [device] bf16 [EL, 2I, H]
- *   w2  [device] bf16 [EL, I, H]   ->  w2p [device] bf16 [EL, H, I]
- * Either pair may be NULL/NULL to skip it.
+ * One-time weight transform (untimed), as in the weight transform step that precedes the fused
+ * call in the "How Mega MoE Overlaps ..." page's example: the logical x @ W weights become
+ * fragment-major packed weights that the GEMMs stream straight into MFMA operand registers.
+ *   w1  [device] bf16 [EL, H, 2I]  ->  w1p [device] bf16, EL * 2I * H elements
+ *   w2  [device] bf16 [EL, I, H]   ->  w2p [device] bf16, EL * H * I elements
+ * Packed layout.  Expert e's block starts at element e * N * K.  View the expert's matrix as
+ * B[n][k] with n an output column (N = 2I for W1, H for W2) and k the reduction index (K = H
+ * for W1, I for W2); element (n, k) sits at
+ *     ((n / 32) * (K / 16) + k / 16) * 512 + ((k / 8) % 2 * 32 + n % 32) * 8 + k % 8
+ * i.e. 1 KB blocks of 32 columns x 16 k, column-group major, each block the B operand of one
+ * 32x32x16 MFMA.  For W2, n = h and k = i.  For W1, n is a packed column: L1 output column c
+ * (c < I: gate column c; c >= I: up column c - I) is packed column
+ *     ((c mod I) / 32) * 64 + (c >= I) * 32 + c mod 32,
+ * so gate and up groups of the same 32 intermediate columns alternate.
+ * Either pair may be NULL/NULL to skip it.  Inputs and outputs must not overlap.
  */
 int32_t moe_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2,
                          uint16_t* w1p, uint16_t* w2p, void* stream);
+
+/* Inverse of moe_pack_weights: packed w1p / w2p (or weight gradients dw1p / dw2p, which share
+ * the packed layout) -> logical w1 [EL, H, 2I] / w2 [EL, I, H].  Either pair may be NULL/NULL. */
+int32_t moe_unpack_weights(const moe_shape* shape, const uint16_t* w1p, const uint16_t* w2p,
+                           uint16_t* w1, uint16_t* w2, void* stream);
 
 /*
  * Dispatch prologue ("Mega MoE" page, Implementation Map: routing tables): from topk_idx
@@ -134,8 +149,8 @@ int32_t moe_route_prologue(const moe_shape* shape, const int32_t* topk_idx, void
 
 /*
  * Dispatch + L1 grouped GEMM, NT ("Mega MoE" page, Pipeline, dispatch_grouped_gemm): for every
- * row r of a real block, h[r] = x[row_pair[r] / k] @ W1[e]^T over w1p [device] bf16
- * [EL, 2I, H], with x [device] bf16 [T, H] gathered through row_pair inside the tile load
+ * row r of a real block, h[r] = x[row_pair[r] / k] @ W1[e] over the packed w1p [device]
+ * (moe_pack_weights), with x [device] bf16 [T, H] gathered through row_pair inside the tile load
  * (padding rows are zero).  Writes, for rows [0, R):
  *   act_out [device] bf16 [R_max, I]  = silu(h[:, :I]) * h[:, I:]   (SwiGLU in the epilogue)
  *   hgu_out [device] bf16 [R_max, 2I] = h                            (pre-activation)
@@ -156,8 +171,8 @@ int32_t moe_swiglu(const moe_shape* shape, const uint16_t* hgu, const void* ws,
 
 /*
  * L2 grouped GEMM, NT + combine ("Mega MoE" page, Pipeline, grouped_gemm_combine, top-k
- * reduce as a weighted scatter-add): o[r] = act[r] @ W2[e]^T over w2p [device] bf16
- * [EL, H, I], then y[t] = sum over the local pairs (t, j) of topk_w[t, j] * o[row of (t, j)],
+ * reduce as a weighted scatter-add): o[r] = act[r] @ W2[e] over the packed w2p [device],
+ * then y[t] = sum over the local pairs (t, j) of topk_w[t, j] * o[row of (t, j)],
  * accumulated in fp32 and written as bf16; tokens with no local pair get y[t] = 0.
  *   act [device] bf16 [R_max, I]; topk_w [device] fp32 [T, k]; y [device] bf16 [T, H]
  */
@@ -170,7 +185,7 @@ int32_t moe_gemm2_combine(const moe_shape* shape, const uint16_t* act, const uin
  * With shape->train nonzero the pre-activation rows are also kept in ws (layout hgu) for the
  * backward entry points.
  *   x [device] bf16 [T, H]; topk_idx [device] int32 [T, k]; topk_w [device] fp32 [T, k];
- *   w1p [device] bf16 [EL, 2I, H]; w2p [device] bf16 [EL, H, I]; y [device] bf16 [T, H]
+ *   w1p, w2p [device] packed weights (moe_pack_weights); y [device] bf16 [T, H]
  */
 int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* topk_idx,
                     const float* topk_w, const uint16_t* w1p, const uint16_t* w2p, void* ws,
@@ -180,8 +195,8 @@ int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* to
  * Backward entry points ("Mega MoE" page, Pipeline, backward).  They need a workspace with
  * shape->train nonzero that a moe_forward of the same inputs filled (tables, act, hgu).
  *
- * L2 dgrad, NN: dact[r] = topk_w[p] * (dy[t] @ W2[e]) with p = row_pair[r], t = p / k, read
- * through w2p [EL, H, I] as the [K = H, N = I] operand.  With fuse_swiglu_bwd nonzero the
+ * L2 dgrad, NN: dact[r] = topk_w[p] * (dy[t] @ W2[e]^T) with p = row_pair[r], t = p / k, read
+ * from the packed w2p as the [K = H, N = I] operand.  With fuse_swiglu_bwd nonzero the
  * epilogue applies the SwiGLU transpose and writes ws dhgu directly; else it writes ws dact.
  *   dy [device] bf16 [T, H]; topk_w [device] fp32 [T, k]
  */
@@ -194,14 +209,16 @@ int32_t moe_bwd_gemm2_dgrad(const moe_shape* shape, const uint16_t* dy, const fl
 int32_t moe_swiglu_bwd(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream);
 
 /* dW2 with variable K ("Mega MoE" page, backward: dW2 (variable-K)):
- * dw2p[e] [H, I] = sum over rows r of e of (topk_w[p] * dy[t])^T (x) act[r]; K = count of e.
- * An expert without rows gets exact zeros.  dw2p [device] bf16 [EL, H, I]. */
+ * dW2[e] [I, H] = sum over rows r of e of act[r]^T (x) (topk_w[p] * dy[t]); K = count of e.
+ * An expert without rows gets exact zeros.  dw2p [device] bf16, EL * H * I elements, in the
+ * packed layout of w2p (moe_unpack_weights gives the logical [EL, I, H]). */
 int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, const float* topk_w, void* ws,
                    size_t ws_bytes, uint16_t* dw2p, void* stream);
 
 /* dW1, TN with variable K ("Mega MoE" page, backward: dW1 (TN); Core Design section 2):
- * dw1p[e] [2I, H] = sum over rows r of e of dhgu[r]^T (x) x[row_pair[r] / k], re-gathering
- * the token rows instead of saving them.  dw1p [device] bf16 [EL, 2I, H]. */
+ * dW1[e] [H, 2I] = sum over rows r of e of x[row_pair[r] / k]^T (x) dhgu[r], re-gathering
+ * the token rows instead of saving them.  dw1p [device] bf16, EL * 2I * H elements, in the
+ * packed layout of w1p (moe_unpack_weights gives the logical [EL, H, 2I]). */
 int32_t moe_wgrad1(const moe_shape* shape, const uint16_t* x, void* ws, size_t ws_bytes,
                    uint16_t* dw1p, void* stream);
 

@@ -94,6 +94,16 @@ def layer(w, d, block_m, train=False, weights=True):
     return ns
 
 
+def unpacked(ns, dw1p, dw2p):
+    """Logical [EL, H, 2I] / [EL, I, H] copies (f64, host) of packed weight gradients."""
+    s = ns.shape
+    W1 = torch.empty(s.EL, s.H, 2 * s.I, dtype=torch.bfloat16, device="cuda")
+    W2 = torch.empty(s.EL, s.I, s.H, dtype=torch.bfloat16, device="cuda")
+    moe.unpack_weights(s, dw1p, dw2p, W1, W2)
+    torch.cuda.synchronize()
+    return f64_host(W1), f64_host(W2)
+
+
 def tables(ns):
     t = {n: moe.ws_region(ns.ws, ns.shape, n).cpu().numpy() for n in TABLES}
     meta = moe.ws_region(ns.ws, ns.shape, "meta").cpu().numpy()

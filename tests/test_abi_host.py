@@ -52,6 +52,7 @@ def test_workspace_layout(cfg, bm, train):
              "tile_expert": 4 * (R // bm), "tok_nloc": 4 * T, "meta": 16, "act": 2 * R * I, "stage": 4 * R * H}
     if train:
         sizes.update(hgu=4 * R * I, dact=2 * R * I, dhgu=4 * R * I)
+    sizes["tile_sync"] = 4 * 512
     spans = sorted((L[n], L[n] + sz, n) for n, sz in sizes.items())
     for (a0, a1, na), (b0, b1, nb) in zip(spans, spans[1:]):
         assert a1 <= b0, (na, nb)
@@ -59,11 +60,11 @@ def test_workspace_layout(cfg, bm, train):
         assert L[n] % 256 == 0
     assert L["total_bytes"] >= spans[-1][1] and L["scratch"] + 4 <= L["total_bytes"]
     assert moe.workspace_bytes(s) == L["total_bytes"]
-    assert moe.packed_sizes(s) == ((EL, 2 * I, H), (EL, H, I))
+    assert moe.packed_sizes(s) == ((EL, 2 * I * H), (EL, H * I))
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("block_m", 48, -3), ("block_m", 0, -3), ("H", 100, -2), ("I", 96, -2), ("EL", 0, -2),
+    ("block_m", 48, -3), ("block_m", 0, -3), ("H", 100, -2), ("I", 96, -2), ("I", 192, -2), ("EL", 0, -2),
     ("EL", 1025, -2), ("k", 0, -2), ("k", 33, -2), ("T", -1, -2), ("e_lo", 250, -2), ("E", 0, -2),
 ])
 def test_shape_validation(field, value, code):
@@ -74,11 +75,12 @@ def test_shape_validation(field, value, code):
     assert moe.lib().moe_workspace_bytes(ctypes.byref(s)) == 0
 
 
-def test_train_requires_backward_tile_multiple():
-    s = moe.make_shape(64, 256, 192, 8, 8, 2, block_m=64, train=True)
-    assert moe.lib().moe_workspace_bytes(ctypes.byref(s)) == 0
-    s.train = 0
-    assert moe.lib().moe_workspace_bytes(ctypes.byref(s)) > 0
+def test_intermediate_size_is_a_multiple_of_128():
+    for train in (0, 1):
+        s = moe.make_shape(64, 256, 192, 8, 8, 2, block_m=64, train=train)
+        assert moe.lib().moe_workspace_bytes(ctypes.byref(s)) == 0
+        s.I = 256
+        assert moe.lib().moe_workspace_bytes(ctypes.byref(s)) > 0
 
 
 def test_null_arguments_are_rejected_before_any_launch():

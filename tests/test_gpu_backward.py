@@ -21,7 +21,7 @@ import torch
 import moe_workloads as mw
 import oracle
 import token_dispatch_grouped_route_amd as moe
-from gpu_helpers import bits_host, check_bf16, check_sum_bound, f64_host, layer, tables
+from gpu_helpers import bits_host, check_bf16, check_sum_bound, f64_host, layer, tables, unpacked
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -100,8 +100,7 @@ def test_backward_reduced_full_compare(w, bm):
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
     S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
-    g1 = f64_host(ns.dW1p).transpose(0, 2, 1)
-    g2 = f64_host(ns.dW2p).transpose(0, 2, 1)
+    g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
     check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1")
     check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2")
     assert np.all(g1[1] == 0.0) and np.all(g2[1] == 0.0), "expert without rows must get exact zeros"
@@ -146,8 +145,9 @@ def test_backward_stages_match_oracle_and_fused():
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
     S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
-    check_sum_bound(f64_host(dW1p).transpose(0, 2, 1), dW1, S1, C_DW1, TOL, "dW1 (staged)")
-    check_sum_bound(f64_host(dW2p).transpose(0, 2, 1), dW2, S2, C_DW2, TOL, "dW2 (staged)")
+    g1, g2 = unpacked(ns, dW1p, dW2p)
+    check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1 (staged)")
+    check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2 (staged)")
 
 
 def test_backward_full_size_sampled_experts():
@@ -161,9 +161,10 @@ def test_backward_full_size_sampled_experts():
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo, experts=experts)
     S1, S2 = term_sums(w, d, experts, pairs_of_expert(t))
+    g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
     for i, e in enumerate(experts):
-        check_sum_bound(f64_host(ns.dW1p[e]).T, dW1[i], S1[i], C_DW1, TOL, "dW1[%d] (%d rows)" % (e, counts[e]))
-        check_sum_bound(f64_host(ns.dW2p[e]).T, dW2[i], S2[i], C_DW2, TOL, "dW2[%d] (%d rows)" % (e, counts[e]))
+        check_sum_bound(g1[e], dW1[i], S1[i], C_DW1, TOL, "dW1[%d] (%d rows)" % (e, counts[e]))
+        check_sum_bound(g2[e], dW2[i], S2[i], C_DW2, TOL, "dW2[%d] (%d rows)" % (e, counts[e]))
     rng = np.random.default_rng(4)
     real = np.nonzero(t["row_pair"] >= 0)[0]
     rows = rng.choice(real, size=24, replace=False)

@@ -76,7 +76,7 @@ def test_route_edge_cases(case):
     elif case == "dups":
         idx[:, 1] = idx[:, 0] % EL
         idx[:, 2] = idx[:, 0] % EL
-    w = mw.Workload("edge", T=T, H=128, I=64, E=E, EL=EL, k=k, e_lo=e_lo)
+    w = mw.Workload("edge", T=T, H=128, I=128, E=E, EL=EL, k=k, e_lo=e_lo)
     for bm in (32, 64, 256):
         got = route_only(w, idx, bm)
         assert_tables_equal(got, oracle.route(idx, E, e_lo, EL, bm))
@@ -94,10 +94,12 @@ def test_route_is_deterministic():
 # Forward on reduced shapes, compared in full
 # ------------------------------------------------------------------------------------------
 REDUCED = [
-    # several M tiles per expert, ragged tails, a shard with e_lo > 0 and non-local pairs
-    mw.Workload("reduced_shard", T=333, H=384, I=192, E=12, EL=6, k=3, e_lo=3),
+    # several M tiles per expert, ragged tails, a shard with e_lo > 0 and non-local pairs; the
+    # N sizes select every forward tile width (L1 2I % 512 or only % 256, L2 H % 512, % 256, % 128)
+    mw.Workload("reduced_shard", T=333, H=384, I=384, E=12, EL=6, k=3, e_lo=3),
     mw.Workload("reduced_all_local", T=500, H=256, I=128, E=8, EL=8, k=4),
-    mw.Workload("reduced_k1", T=200, H=128, I=64, E=4, EL=4, k=1),
+    mw.Workload("reduced_k1", T=200, H=128, I=128, E=4, EL=4, k=1),
+    mw.Workload("reduced_wide", T=700, H=512, I=256, E=10, EL=5, k=2),
 ]
 
 
@@ -128,13 +130,34 @@ def test_forward_tiny_workload_full_compare():
         check_bf16(f64_host(ns.y), ref, TOL)
 
 
-def test_pack_weights_is_an_exact_transpose():
-    w = REDUCED[0]
+def packed_reference(W, I=None):
+    """The packed layout as include/moe.h states it: logical [EL, K, N] -> [EL, N * K] with
+    element (n, k) at ((n / 32) * (K / 16) + k / 16) * 512 + ((k / 8) % 2 * 32 + n % 32) * 8
+    + k % 8, where for W1 (I given) logical column c becomes packed column
+    ((c mod I) / 32) * 64 + (c >= I) * 32 + c mod 32."""
+    EL, K, N = W.shape
+    c = np.arange(N)
+    n = (c % I) // 32 * 64 + (c >= I) * 32 + c % 32 if I is not None else c
+    k = np.arange(K)[:, None]
+    pos = ((n[None, :] // 32) * (K // 16) + k // 16) * 512 + ((k // 8) % 2 * 32 + n[None, :] % 32) * 8 + k % 8
+    assert np.array_equal(np.sort(pos.reshape(-1)), np.arange(N * K))
+    out = np.empty((EL, N * K), np.uint16)
+    out[:, pos.reshape(-1)] = W.reshape(EL, -1)
+    return out
+
+
+@pytest.mark.parametrize("w", [REDUCED[0], REDUCED[3]], ids=["shard", "wide"])
+def test_pack_weights_follows_the_documented_layout(w):
     d = mw.inputs(w, 4)
     ns = layer(w, d, 64)
-    assert tuple(ns.W1p.shape) == (w.EL, 2 * w.I, w.H) and tuple(ns.W2p.shape) == (w.EL, w.H, w.I)
-    assert np.array_equal(bits_host(ns.W1p), np.ascontiguousarray(d["W1"].transpose(0, 2, 1)))
-    assert np.array_equal(bits_host(ns.W2p), np.ascontiguousarray(d["W2"].transpose(0, 2, 1)))
+    assert tuple(ns.W1p.shape) == (w.EL, 2 * w.I * w.H) and tuple(ns.W2p.shape) == (w.EL, w.H * w.I)
+    assert np.array_equal(bits_host(ns.W1p), packed_reference(d["W1"], w.I))
+    assert np.array_equal(bits_host(ns.W2p), packed_reference(d["W2"]))
+    W1, W2 = torch.empty(w.EL, w.H, 2 * w.I, dtype=torch.bfloat16, device="cuda"), \
+        torch.empty(w.EL, w.I, w.H, dtype=torch.bfloat16, device="cuda")
+    moe.unpack_weights(ns.shape, ns.W1p, ns.W2p, W1, W2)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_host(W1), d["W1"]) and np.array_equal(bits_host(W2), d["W2"])
 
 
 def test_stages_match_oracle_and_fused_forward():

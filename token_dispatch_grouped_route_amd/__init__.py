@@ -24,7 +24,7 @@ _lib = None
 
 ENTRY_POINTS = (
     "moe_status_string", "moe_workspace_bytes", "moe_workspace_layout", "moe_preferred_block_m",
-    "moe_pack_weights", "moe_route_prologue", "moe_dispatch_gemm1", "moe_swiglu",
+    "moe_pack_weights", "moe_unpack_weights", "moe_route_prologue", "moe_dispatch_gemm1", "moe_swiglu",
     "moe_gemm2_combine", "moe_forward", "moe_bwd_gemm2_dgrad", "moe_swiglu_bwd", "moe_wgrad2",
     "moe_wgrad1", "moe_backward",
 )
@@ -42,7 +42,7 @@ class Shape(ctypes.Structure):
 
 
 _LAYOUT_FIELDS = ("counts", "padded_offsets", "row_pair", "pair_row", "tile_expert", "tok_nloc",
-                  "meta", "act", "stage", "hgu", "dact", "dhgu", "zeros", "scratch")
+                  "meta", "act", "stage", "hgu", "dact", "dhgu", "zeros", "scratch", "tile_sync")
 
 
 class WsLayout(ctypes.Structure):
@@ -66,6 +66,7 @@ def lib():
         L.moe_workspace_layout.argtypes = [S, ctypes.POINTER(WsLayout)]
         L.moe_preferred_block_m.argtypes = [S]
         L.moe_pack_weights.argtypes = [S, P, P, P, P, P]
+        L.moe_unpack_weights.argtypes = [S, P, P, P, P, P]
         L.moe_route_prologue.argtypes = [S, P, P, ctypes.c_size_t, P]
         L.moe_dispatch_gemm1.argtypes = [S, P, P, P, ctypes.c_size_t, P, P, P]
         L.moe_swiglu.argtypes = [S, P, P, ctypes.c_size_t, P, P]
@@ -165,8 +166,9 @@ def ws_region(ws: torch.Tensor, shape: Shape, name: str) -> torch.Tensor:
 
 
 def packed_sizes(shape: Shape):
-    """Tensor sizes of the packed weights: W1p (and dW1p) [EL, 2I, H], W2p (and dW2p) [EL, H, I]."""
-    return ((shape.EL, 2 * shape.I, shape.H), (shape.EL, shape.H, shape.I))
+    """Tensor sizes of the packed weights W1p (and dW1p) and W2p (and dW2p): one flat row of
+    2I*H resp. H*I elements per expert, in the fragment-major order of moe_pack_weights."""
+    return ((shape.EL, 2 * shape.I * shape.H), (shape.EL, shape.H * shape.I))
 
 
 def alloc_packed(shape: Shape, device="cuda"):
@@ -186,6 +188,13 @@ def route_prologue(shape, topk_idx, ws, stream=None):
     p, n = _ws(ws)
     _check(lib().moe_route_prologue(ctypes.byref(shape), _ptr(topk_idx, torch.int32, "topk_idx"), p, n,
                                     _stream(stream)), "moe_route_prologue")
+
+
+def unpack_weights(shape, w1p=None, w2p=None, w1=None, w2=None, stream=None):
+    """Packed (w1p, w2p) or weight gradients (dw1p, dw2p) -> logical [EL, H, 2I], [EL, I, H]."""
+    _check(lib().moe_unpack_weights(ctypes.byref(shape), _ptr(w1p, torch.bfloat16, "w1p"),
+                                    _ptr(w2p, torch.bfloat16, "w2p"), _ptr(w1, torch.bfloat16, "w1"),
+                                    _ptr(w2, torch.bfloat16, "w2"), _stream(stream)), "moe_unpack_weights")
 
 
 def dispatch_gemm1(shape, x, w1p, ws, act_out=None, hgu_out=None, stream=None):

@@ -23,8 +23,7 @@ int32_t check_shape(const moe_shape* s) {
         s->k < 1 || s->k > 32)
         return MOE_ERR_SHAPE;
     if (static_cast<int64_t>(s->e_lo) + s->EL > s->E) return MOE_ERR_SHAPE;
-    if (s->H % 128 != 0 || s->I % 64 != 0) return MOE_ERR_SHAPE;
-    if (s->train && s->I % 128 != 0) return MOE_ERR_SHAPE;
+    if (s->H % 128 != 0 || s->I % 128 != 0) return MOE_ERR_SHAPE;
     // row and element indices stay far inside int32 / int64 ranges
     const int64_t rows = static_cast<int64_t>(s->T) * s->k + static_cast<int64_t>(s->EL) * s->block_m;
     if (rows > (int64_t(1) << 28) || s->H > (1 << 20) || s->I > (1 << 20)) return MOE_ERR_SHAPE;
@@ -65,6 +64,7 @@ int32_t layout_of(const moe_shape* s, moe_ws_layout* L) {
         L->dhgu = take(2 * static_cast<size_t>(R) * 2 * I);
     }
     L->zeros = take(2 * (H > 2 * I ? H : 2 * I));
+    L->tile_sync = take(4 * static_cast<size_t>(kMaxGrid));
     L->scratch = take(4 * static_cast<size_t>(chunks) * (EL + 1));
     L->total_bytes = off;
     return MOE_OK;
@@ -112,6 +112,7 @@ int32_t prepare(const moe_shape* s, const void* ws, size_t ws_bytes, bool need_t
     w->chunk_hist = reinterpret_cast<int32_t*>(b + L->scratch);
     w->chunk_dropped = w->chunk_hist + static_cast<int64_t>(w->num_chunks) * s->EL;
     w->zeros = reinterpret_cast<uint16_t*>(b + L->zeros);
+    w->tile_sync = reinterpret_cast<int32_t*>(b + L->tile_sync);
     w->zero_len = s->H > 2 * s->I ? s->H : 2 * s->I;
     w->rows_cap = L->rows_capacity;
     w->num_blocks = static_cast<int32_t>(L->num_blocks);
@@ -163,10 +164,23 @@ int32_t moe_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint1
     const int32_t st = check_shape(shape);
     if (st != MOE_OK) return st;
     if ((w1 == nullptr) != (w1p == nullptr) || (w2 == nullptr) != (w2p == nullptr)) return MOE_ERR_NULL;
-    if ((w1 && w1 == w1p) || (w2 && w2 == w2p)) return MOE_ERR_SHAPE;   // no in-place transpose
+    if ((w1 && w1 == w1p) || (w2 && w2 == w2p)) return MOE_ERR_SHAPE;   // not in place
+    if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1p) || !aligned16(w2p)) return MOE_ERR_ALIGN;
     if (!is_gfx950()) return MOE_ERR_DEVICE;
     const Dims d{shape->T, shape->H, shape->I, shape->E, shape->e_lo, shape->EL, shape->k, shape->block_m};
     return launched(launch_pack(d, w1, w2, w1p, w2p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_unpack_weights(const moe_shape* shape, const uint16_t* w1p, const uint16_t* w2p, uint16_t* w1,
+                           uint16_t* w2, void* stream) {
+    const int32_t st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if ((w1 == nullptr) != (w1p == nullptr) || (w2 == nullptr) != (w2p == nullptr)) return MOE_ERR_NULL;
+    if ((w1 && w1 == w1p) || (w2 && w2 == w2p)) return MOE_ERR_SHAPE;   // not in place
+    if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1p) || !aligned16(w2p)) return MOE_ERR_ALIGN;
+    if (!is_gfx950()) return MOE_ERR_DEVICE;
+    const Dims d{shape->T, shape->H, shape->I, shape->E, shape->e_lo, shape->EL, shape->k, shape->block_m};
+    return launched(launch_unpack(d, w1p, w2p, w1, w2, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_route_prologue(const moe_shape* shape, const int32_t* topk_idx, void* ws, size_t ws_bytes,

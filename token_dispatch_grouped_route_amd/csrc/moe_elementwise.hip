@@ -1,5 +1,5 @@
-// Memory-bound kernels of the MoE expert layer: the one-time weight transform, the standalone
-// SwiGLU forward and backward ("Mega MoE" page, Implementation Map: SwiGLU fwd/bwd), and the
+// Memory-bound kernels of the MoE expert layer: the one-time weight transform (and its inverse),
+// the standalone SwiGLU forward and backward ("Mega MoE" page, Implementation Map: SwiGLU fwd/bwd), and the
 // last step of the combine (top-k reduce, "Mega MoE" page, Pipeline).  All use 16-byte
 // vector accesses on contiguous rows; row counts that depend on the routing are read from the
 // workspace on the device.
@@ -8,32 +8,87 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------------------------
-// Weight transform: [EL, R, C] -> [EL, C, R] (bf16), 64 x 64 tiles through LDS.
+// Weight transform: logical [EL, K, N] (x @ W layout) <-> fragment-major packed layout
+// (frag_index).  One block moves one 32-column group x 128 K of one expert through LDS.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in,
-                                                        uint16_t* __restrict__ out, int R, int C) {
-    __shared__ uint16_t tile[64][64 + 2];
-    const int e = blockIdx.z;
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-    const uint16_t* src = in + static_cast<int64_t>(e) * R * C;
-    uint16_t* dst = out + static_cast<int64_t>(e) * C * R;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int r = ty; r < 64; r += 4)
-        if (r0 + r < R && c0 + tx < C) tile[r][tx] = src[static_cast<int64_t>(r0 + r) * C + c0 + tx];
-    __syncthreads();
-    for (int c = ty; c < 64; c += 4)
-        if (c0 + c < C && r0 + tx < R) dst[static_cast<int64_t>(c0 + c) * R + r0 + tx] = tile[tx][c];
+// First logical column of packed column group nb (L1: gate and up groups alternate).
+__device__ __forceinline__ int64_t group_col0(int nb, int I, bool l1) {
+    return l1 ? static_cast<int64_t>(nb & 1) * I + 32 * (nb >> 1) : 32 * static_cast<int64_t>(nb);
 }
 
+template <bool PACK>
+__global__ __launch_bounds__(256) void repack_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                     int K, int N, int I, int l1) {
+    __shared__ uint16_t tile[128][32 + 2];
+    const int nb = blockIdx.x, k0 = blockIdx.y * 128, e = blockIdx.z, tid = threadIdx.x;
+    const int64_t ebase = static_cast<int64_t>(e) * K * N;
+    const int64_t n0 = group_col0(nb, I, l1 != 0);
+    const uint16_t* logical_in = in + ebase;
+    uint16_t* logical_out = out + ebase;
+    if (PACK) {
+        for (int q = tid; q < 128 * 16; q += 256) {   // 128 rows x 16 pairs of columns
+            const int r = q >> 4, c2 = q & 15;
+            if (k0 + r < K) {
+                const uint32_t v = *reinterpret_cast<const uint32_t*>(logical_in + static_cast<int64_t>(k0 + r) * N + n0 + 2 * c2);
+                tile[r][2 * c2] = static_cast<uint16_t>(v & 0xffffu);
+                tile[r][2 * c2 + 1] = static_cast<uint16_t>(v >> 16);
+            }
+        }
+        __syncthreads();
+        for (int q = tid; q < 8 * 64; q += 256) {   // 8 K steps x 64 lanes of 16 bytes
+            const int kb = q >> 6, L = q & 63, c = L & 31, kk = kb * 16 + 8 * (L >> 5);
+            if (k0 + kk >= K) continue;
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = static_cast<uint32_t>(tile[kk + 2 * j][c]) | (static_cast<uint32_t>(tile[kk + 2 * j + 1][c]) << 16);
+            *reinterpret_cast<uint4*>(out + ebase + frag_index(32 * nb + c, k0 + kk, K)) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        for (int q = tid; q < 8 * 64; q += 256) {
+            const int kb = q >> 6, L = q & 63, c = L & 31, kk = kb * 16 + 8 * (L >> 5);
+            if (k0 + kk >= K) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(in + ebase + frag_index(32 * nb + c, k0 + kk, K));
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tile[kk + 2 * j][c] = static_cast<uint16_t>(w[j] & 0xffffu);
+                tile[kk + 2 * j + 1][c] = static_cast<uint16_t>(w[j] >> 16);
+            }
+        }
+        __syncthreads();
+        for (int q = tid; q < 128 * 16; q += 256) {
+            const int r = q >> 4, c2 = q & 15;
+            if (k0 + r < K)
+                *reinterpret_cast<uint32_t*>(logical_out + static_cast<int64_t>(k0 + r) * N + n0 + 2 * c2) =
+                    static_cast<uint32_t>(tile[r][2 * c2]) | (static_cast<uint32_t>(tile[r][2 * c2 + 1]) << 16);
+        }
+    }
+}
+
+// W1 [EL, H, 2I] (K = H, N = 2I, gate/up groups interleaved) and W2 [EL, I, H] (K = I, N = H).
 hipError_t launch_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, uint16_t* w1p,
                        uint16_t* w2p, hipStream_t s) {
-    if (w1 && w1p) {   // [EL, H, 2I] -> [EL, 2I, H]
-        dim3 g((2 * d.I + 63) / 64, (d.H + 63) / 64, d.EL);
-        transpose_kernel<<<g, 256, 0, s>>>(w1, w1p, d.H, 2 * d.I);
+    if (w1 && w1p) {
+        dim3 g(2 * d.I / 32, (d.H + 127) / 128, d.EL);
+        repack_kernel<true><<<g, 256, 0, s>>>(w1, w1p, d.H, 2 * d.I, d.I, 1);
     }
-    if (w2 && w2p) {   // [EL, I, H] -> [EL, H, I]
-        dim3 g((d.H + 63) / 64, (d.I + 63) / 64, d.EL);
-        transpose_kernel<<<g, 256, 0, s>>>(w2, w2p, d.I, d.H);
+    if (w2 && w2p) {
+        dim3 g(d.H / 32, (d.I + 127) / 128, d.EL);
+        repack_kernel<true><<<g, 256, 0, s>>>(w2, w2p, d.I, d.H, d.I, 0);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const Dims& d, const uint16_t* w1p, const uint16_t* w2p, uint16_t* w1,
+                         uint16_t* w2, hipStream_t s) {
+    if (w1 && w1p) {
+        dim3 g(2 * d.I / 32, (d.H + 127) / 128, d.EL);
+        repack_kernel<false><<<g, 256, 0, s>>>(w1p, w1, d.H, 2 * d.I, d.I, 1);
+    }
+    if (w2 && w2p) {
+        dim3 g(d.H / 32, (d.I + 127) / 128, d.EL);
+        repack_kernel<false><<<g, 256, 0, s>>>(w2p, w2, d.I, d.H, d.I, 0);
     }
     return hipGetLastError();
 }

@@ -1,34 +1,32 @@
-// Grouped GEMMs of the MoE expert layer on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
-// accumulation).
+// Backward grouped GEMMs of the MoE expert layer on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation); the forward GEMMs are in moe_grouped.hip.
 //
-// One core serves every GEMM: a workgroup computes a BM x BN tile with WM x WN wavefronts, each
+// One core serves these GEMMs: a workgroup computes a BM x BN tile with WM x WN wavefronts, each
 // wave a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.  K advances 64 elements per step.  Both
 // operand tiles live in LDS K-contiguous (128 bytes per row, 16-byte chunks XOR-swizzled by
 // row so a wave's fragment reads spread over the banks), double-buffered so the global loads
 // of step k+1 are in flight while the MFMAs of step k run; one barrier per step.
 //
 // Loaders differ per operand:
-//   KRows  rows that are K-contiguous in memory (token rows, packed weights, activations);
-//          16-byte vector loads, 8 lanes per 128-byte row segment.  A row may come from a
-//          gather (the dispatch: x or dy rows through row_pair) or be absent (zeros).
-//   TRows  operands stored with M (or N) contiguous and K strided (the NN/TN products of the
-//          backward): each thread loads 4 K-rows x 8 elements and transposes them in registers
-//          into 8 rows x 4 K before the LDS store.
+//   KRows  rows that are K-contiguous in memory (token rows, activations); 16-byte vector
+//          loads, 8 lanes per 128-byte row segment.  A row may come from a gather (dy rows
+//          through row_pair) or be absent (zeros).
+//   TRows  operands stored with M (or N) contiguous in runs of 8 and K strided (the NN/TN
+//          products of the backward, and the packed W2 read transposed): each thread loads 4
+//          K-rows x 8 elements and transposes them in registers into 8 rows x 4 K before the
+//          LDS store.
 //
-// Kernels ("Mega MoE" page, Pipeline):
-//   gemm1   dispatch gather fused into the A load + L1 NT + SwiGLU epilogue (dispatch_grouped_gemm)
-//   gemm2   L2 NT + top-k weighted combine epilogue                     (grouped_gemm_combine)
+// Kernels ("Mega MoE" page, Pipeline, backward):
 //   dgrad   L2 dgrad NN, row weight and optional SwiGLU transpose in the epilogue
 //   wgrad2  dW2 = dO^T A, K = rows of the expert (variable K), TN
 //   wgrad1  dW1 = dHgu^T X with X re-gathered from x, TN
+// Weight gradients are written in the packed layout of the weights they belong to.
 //
-// Row-tiled launches (gemm1, gemm2, dgrad) are persistent: a fixed grid (CUs x occupancy) walks
-// the tile list whose length R / BM * n_tiles is read from the workspace on the device, so the
-// host never needs R.  The list is ordered expert by expert, and inside an expert N-panel by
-// N-panel with the expert's M tiles adjacent; it is cut into one contiguous chunk per XCD (the
-// hardware places workgroup b on XCD b mod 8, each XCD with its own L2).  So one XCD fetches a
-// given weight panel and a given expert's token rows, and the workgroups that read the same
-// panel run side by side.
+// The dgrad launch is persistent: a fixed grid (CUs x occupancy) walks the tile list whose
+// length R / BM * n_tiles is read from the workspace on the device, so the host never needs R.
+// The list is ordered expert by expert, and inside an expert N-panel by N-panel with the
+// expert's M tiles adjacent; it is cut into one contiguous chunk per XCD (the hardware places
+// workgroup b on XCD b mod 8, each XCD with its own L2).
 #include "moe_internal.h"
 
 namespace moe {
@@ -107,8 +105,9 @@ __device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float s) {
     return r;
 }
 
-// Operand tile of ROWS rows (the M or N index) x BK, stored in memory as K-indexed rows with the
-// tile's index contiguous: element (m, k) = Src::row(k)[m_base + m] (times Src::scale(k)).
+// Operand tile of ROWS rows (the M or N index) x BK, stored in memory with the tile's index
+// contiguous in runs of 8: elements (m .. m+7, k) = Src::chunk(k, m_base + m) for m a multiple of
+// 8 (times Src::scale(k)); a null chunk reads as zeros.
 // Unit u moves K rows 4*kq..4*kq+3 of the 16-byte column mc; kq varies fastest across lanes so
 // the transposed 8-byte LDS writes of a wave fill whole rows without bank conflicts.
 template <int ROWS, int NT, class Src>
@@ -130,9 +129,9 @@ struct TRows {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int k = kt * BK + 4 * kq + r;
-                    const uint16_t* p = src.row(k);
+                    const uint16_t* p = src.chunk(k, m_base + 8 * mc);
                     u32x4 x = 0;
-                    if (p) x = *reinterpret_cast<const u32x4*>(p + m_base + 8 * mc);
+                    if (p) x = *reinterpret_cast<const u32x4*>(p);
                     if (Src::kScaled && p) x = scale_bf16x8(x, src.scale(k));
                     v[S][i][r] = x;
                 }
@@ -211,7 +210,7 @@ __device__ __forceinline__ void pipe_step(LA& la, LB& lb, int kt, int nk, char* 
         la.template store<S ^ 1>(nxt, tid);
         lb.template store<S ^ 1>(nxt + C::A_BYTES, tid);
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 template <class C, class LA, class LB>
@@ -232,7 +231,7 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f3
     }
     la.template store<0>(smem, tid);
     lb.template store<0>(smem + C::A_BYTES, tid);
-    __syncthreads();
+    lds_barrier();
     if constexpr (C::PF == 2) {
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
@@ -255,7 +254,7 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f3
                 la.template store<0>(nxt, tid);
                 lb.template store<0>(nxt + C::A_BYTES, tid);
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 }
@@ -334,178 +333,13 @@ __device__ __forceinline__ void tile_at(const Ws& ws, const Dims& d, int n_tiles
 }
 
 // ---------------------------------------------------------------------------------------------
-// gemm1: dispatch gather + L1 (NT) + SwiGLU
-// ---------------------------------------------------------------------------------------------
-// Each N tile holds BN/2 gate columns and the BN/2 matching up columns: wave wn's TN rows of the
-// B tile are [gate cols | up cols] of the same BN/(2*WN) intermediate columns, so the lane that
-// holds gate(r, c) in block j also holds up(r, c) in block j + NI/2.
-template <class C>
-__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_kernel(const uint16_t* __restrict__ x,
-                                                      const uint16_t* __restrict__ w1p, Dims d, Ws ws,
-                                                      uint16_t* __restrict__ act_out,
-                                                      uint16_t* __restrict__ hgu_out) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / C::WN) * C::TM, wn = wave % C::WN, wn0 = wn * C::TN;
-    const int H = d.H, I = d.I;
-    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);   // R / BM, clamped to the tables
-    const int n_tiles = (2 * I) / C::BN;
-    const int total = m_tiles * n_tiles;
-    const int npairs = d.T * d.k;
-    constexpr int HALF = C::TN / 2;   // intermediate columns per wave
-
-    const TileRange tr(total);
-    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
-        int mt, nt;
-        tile_at(ws, d, n_tiles, tile, mt, nt);
-        const int e = ws.tile_expert[mt];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
-        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
-
-        KRows<C::BM, C::NT> la;
-        la.base = reinterpret_cast<const char*>(x);
-        la.keep = 0;
-#pragma unroll
-        for (int i = 0; i < la.PER; ++i) {
-            const int p = ws.row_pair[row0 + la.row_of(tid, i)];
-            const bool ok = p >= 0 && p < npairs;
-            la.keep |= static_cast<uint32_t>(ok) << i;
-            la.off[i] = 2u * (static_cast<uint32_t>(ok ? p / d.k : 0) * H + 8 * la.chunk_of(tid, i));
-        }
-        KRows<C::BN, C::NT> lb;
-        lb.base = reinterpret_cast<const char*>(w1p + static_cast<int64_t>(e) * 2 * I * H);
-        lb.keep = ~0u;
-#pragma unroll
-        for (int i = 0; i < lb.PER; ++i) {
-            const int nl = lb.row_of(tid, i);
-            const int w = nl / C::TN, j = nl % C::TN;
-            const int grow = (j / HALF) * I + nt * (C::BN / 2) + w * HALF + (j % HALF);
-            lb.off[i] = 2u * (static_cast<uint32_t>(grow) * H + 8 * lb.chunk_of(tid, i));
-        }
-        f32x16_t acc[C::MI][C::NI];
-        __syncthreads();   // the previous tile's LDS reads are done
-        gemm_tile<C>(la, lb, H / BK, smem, acc, tid, wm0, wn0, lane);
-
-        // C tile columns: [0, BN/2) gate, [BN/2, BN) up, both in intermediate-column order
-        float* ct = reinterpret_cast<float*>(smem);
-        acc_to_lds<C>(ct, acc, wm0, lane, [&](int ni) {
-            return ni < C::NI / 2 ? wn * HALF + ni * 32 : C::BN / 2 + wn * HALF + (ni - C::NI / 2) * 32;
-        });
-        __syncthreads();
-        constexpr int CH = C::BN / 16;   // 8-column chunks of the tile's intermediate columns
-        const int c0 = nt * (C::BN / 2);
-        for (int u = tid; u < C::BM * CH; u += C::NT) {
-            const int rl = u / CH, c8 = (u % CH) * 8;
-            const int64_t row = row0 + rl;
-            float g[8], up[8], a[8];
-            ld8(ct + rl * C::C_STRIDE + c8, g);
-            ld8(ct + rl * C::C_STRIDE + C::BN / 2 + c8, up);
-            if (hgu_out) {
-                *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + c0 + c8) = bf16x8_of(g);
-                *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + I + c0 + c8) = bf16x8_of(up);
-            }
-            if (act_out) {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) a[q] = silu_f32(g[q]) * up[q];
-                *reinterpret_cast<u32x4*>(act_out + row * I + c0 + c8) = bf16x8_of(a);
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
-// gemm2: L2 (NT) + top-k weighted combine
-// ---------------------------------------------------------------------------------------------
-// Row r of pair p = (t, j): o = act[r] @ W2[e]^T, scaled by topk_w[p].  A token with one local
-// pair owns its y row: the epilogue stores bf16(w * o) there.  A token with several local pairs
-// gets fp32 rows in ws.stage, summed in slot order by combine_finish (deterministic, no atomics).
-template <class C>
-__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm2_kernel(const uint16_t* __restrict__ act,
-                                                      const uint16_t* __restrict__ w2p,
-                                                      const float* __restrict__ topk_w, Dims d, Ws ws,
-                                                      uint16_t* __restrict__ y) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    int* s_tok = reinterpret_cast<int*>(smem + C::LDS_BYTES);   // token, or -1 (padding)
-    float* s_w = reinterpret_cast<float*>(s_tok + C::BM);
-    int* s_direct = reinterpret_cast<int*>(s_w + C::BM);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
-    const int H = d.H, I = d.I;
-    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);   // R / BM, clamped to the tables
-    const int n_tiles = H / C::BN;
-    const int total = m_tiles * n_tiles;
-    const int npairs = d.T * d.k;
-
-    const TileRange tr(total);
-    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
-        int mt, nt;
-        tile_at(ws, d, n_tiles, tile, mt, nt);
-        const int e = ws.tile_expert[mt];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
-        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
-
-        KRows<C::BM, C::NT> la;
-        la.base = reinterpret_cast<const char*>(act + row0 * I);
-        la.keep = ~0u;
-#pragma unroll
-        for (int i = 0; i < la.PER; ++i)
-            la.off[i] = 2u * (static_cast<uint32_t>(la.row_of(tid, i)) * I + 8 * la.chunk_of(tid, i));
-        KRows<C::BN, C::NT> lb;
-        lb.base = reinterpret_cast<const char*>(w2p + (static_cast<int64_t>(e) * H + nt * C::BN) * I);
-        lb.keep = ~0u;
-#pragma unroll
-        for (int i = 0; i < lb.PER; ++i)
-            lb.off[i] = 2u * (static_cast<uint32_t>(lb.row_of(tid, i)) * I + 8 * lb.chunk_of(tid, i));
-        f32x16_t acc[C::MI][C::NI];
-        __syncthreads();   // previous tile's LDS (operands and row info) no longer read
-        for (int r = tid; r < C::BM; r += C::NT) {
-            const int p = ws.row_pair[row0 + r];
-            int t = -1, direct = 0;
-            float w = 0.0f;
-            if (p >= 0 && p < npairs) {
-                t = p / d.k;
-                w = topk_w[p];
-                direct = ws.tok_nloc[t] == 1;
-            }
-            s_tok[r] = t;
-            s_w[r] = w;
-            s_direct[r] = direct;
-        }
-        gemm_tile<C>(la, lb, I / BK, smem, acc, tid, wm0, wn0, lane);   // its barriers publish row info
-
-        float* ct = reinterpret_cast<float*>(smem);
-        acc_to_lds<C>(ct, acc, wm0, lane, [&](int ni) { return wn0 + ni * 32; });
-        __syncthreads();
-        constexpr int CH = C::BN / 8;
-        const int col0 = nt * C::BN;
-        for (int u = tid; u < C::BM * CH; u += C::NT) {
-            const int rl = u / CH, c8 = (u % CH) * 8;
-            const int t = s_tok[rl];
-            if (t < 0) continue;
-            const float w = s_w[rl];
-            float o[8];
-            ld8(ct + rl * C::C_STRIDE + c8, o);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) o[q] *= w;
-            if (s_direct[rl]) {
-                *reinterpret_cast<u32x4*>(y + static_cast<int64_t>(t) * H + col0 + c8) = bf16x8_of(o);
-            } else {
-                float* sr = ws.stage + (row0 + rl) * H + col0 + c8;
-                *reinterpret_cast<float4*>(sr) = make_float4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<float4*>(sr + 4) = make_float4(o[4], o[5], o[6], o[7]);
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
 // dgrad: L2 dgrad (NN) with the row weight and optional SwiGLU transpose in the epilogue
 // ---------------------------------------------------------------------------------------------
-struct W2ColSrc {   // B operand of the dgrad: row k = h of W2[e] in its packed [H, I] layout
+struct W2ColSrc {   // B operand of the dgrad: (K = h, N = i) of expert e's packed W2
     static constexpr bool kScaled = false;
     const uint16_t* base;   // w2p + e*H*I
     int I;
-    __device__ __forceinline__ const uint16_t* row(int k) const { return base + static_cast<int64_t>(k) * I; }
+    __device__ __forceinline__ const uint16_t* chunk(int k, int m) const { return base + frag_index(k, m, I); }
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
@@ -547,7 +381,7 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const uint16_t* __restrict
         lb.src.I = I;
         lb.m_base = nt * C::BN;
         f32x16_t acc[C::MI][C::NI];
-        __syncthreads();
+        lds_barrier();
         for (int r = tid; r < C::BM; r += C::NT) {
             const int p = ws.row_pair[row0 + r];
             s_w[r] = (p >= 0 && p < npairs) ? topk_w[p] : 0.0f;
@@ -590,10 +424,10 @@ struct GatherTokenSrc {   // row k -> token row of x or dy through row_pair, opt
     const int32_t* row_pair;
     int64_t seg0;
     int count, k, H, npairs;
-    __device__ __forceinline__ const uint16_t* row(int kk) const {
+    __device__ __forceinline__ const uint16_t* chunk(int kk, int m) const {
         if (kk >= count) return nullptr;
         const int p = row_pair[seg0 + kk];
-        return (p >= 0 && p < npairs) ? base + static_cast<int64_t>(p / k) * H : nullptr;
+        return (p >= 0 && p < npairs) ? base + static_cast<int64_t>(p / k) * H + m : nullptr;
     }
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
@@ -607,13 +441,14 @@ struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
     const uint16_t* base;
     int64_t seg0;
     int count, width;
-    __device__ __forceinline__ const uint16_t* row(int kk) const {
-        return kk < count ? base + (seg0 + kk) * width : nullptr;
+    __device__ __forceinline__ const uint16_t* chunk(int kk, int m) const {
+        return kk < count ? base + (seg0 + kk) * width + m : nullptr;
     }
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
-// dW2p[e][h][i] = sum_k (w dy)[k][h] * act[k][i]: M = H, N = I.
+// dW2[e] (packed like W2: column h, reduction index i) = sum_k (w dy)[k][h] * act[k][i]:
+// M = H, N = I.
 template <class C>
 __global__ __launch_bounds__(C::NT) void wgrad2_kernel(const uint16_t* __restrict__ dy,
                                                        const float* __restrict__ topk_w, Dims d, Ws ws,
@@ -658,11 +493,12 @@ __global__ __launch_bounds__(C::NT) void wgrad2_kernel(const uint16_t* __restric
             const int64_t h = mt * C::BM + wm0 + mi * 32 + acc_row(r, lane);
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                out[h * I + nt * C::BN + wn0 + ni * 32 + (lane & 31)] = f32_to_bf16(acc[mi][ni][r]);
+                out[frag_index(h, nt * C::BN + wn0 + ni * 32 + (lane & 31), I)] = f32_to_bf16(acc[mi][ni][r]);
         }
 }
 
-// dW1p[e][n][h] = sum_k dhgu[k][n] * x[t_k][h]: M = 2I, N = H.
+// dW1[e] (packed like W1: L1 column n, reduction index h) = sum_k dhgu[k][n] * x[t_k][h]:
+// M = 2I, N = H.
 template <class C>
 __global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
                                                        uint16_t* __restrict__ dw1p) {
@@ -705,329 +541,9 @@ __global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restric
             const int64_t n = mt * C::BM + wm0 + mi * 32 + acc_row(r, lane);
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                out[n * H + nt * C::BN + wn0 + ni * 32 + (lane & 31)] = f32_to_bf16(acc[mi][ni][r]);
+                out[frag_index(l1_packed_col(n, d.I), nt * C::BN + wn0 + ni * 32 + (lane & 31), H)] =
+                    f32_to_bf16(acc[mi][ni][r]);
         }
-}
-
-// ---------------------------------------------------------------------------------------------
-// L1 GEMM with a direct-to-LDS operand ring
-// ---------------------------------------------------------------------------------------------
-// The L1 GEMM is bound by moving operands into the CUs.  Here operands go straight from global
-// memory into a multi-stage LDS ring with global_load_lds_dwordx4 (no staging registers, no LDS
-// store instructions) and STAGES - 1 stages stay in flight while the MFMAs consume one.  Each
-// load instruction should cover whole 128-byte lines: one that reads 64 bytes from each of 16
-// rows moves half as many bytes per cycle, from L2 and from HBM, as one that reads 128 bytes
-// from each of 8 rows.  So K advances 64 per stage (128-byte LDS rows, the same swizzled layout
-// as the register-staged kernels); a 32-per-stage form (64-byte rows) is kept for small tiles.
-// The epilogue goes through LDS one band of wave rows at a time, inside the ring's memory.
-typedef __attribute__((address_space(1))) void g_void;
-typedef __attribute__((address_space(3))) void l_void;
-
-// 16-byte chunk c (0..3) of 64-byte row r sits at position c ^ ((r >> 2) & 3): four rows fill the
-// 64 banks, and the 16 rows of a 16-lane fragment read land on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int lds_off32(int row, int chunk) {
-    return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
-
-template <int BM_, int BN_, int WM_, int WN_, int KS_, int STAGES_, int MIN_WG_>
-struct DCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int KS = KS_;           // K per ring stage: 32 or 64
-    static constexpr int STAGES = STAGES_;   // 3: two stages in flight
-    static constexpr int MIN_WG = MIN_WG_;   // workgroups per CU the registers must allow
-    static constexpr int NT = 64 * WM * WN;
-    static constexpr int TM = BM / WM, TN = BN / WN;
-    static constexpr int MI = TM / 32, NI = TN / 32;
-    static constexpr int A_BYTES = BM * KS * 2, B_BYTES = BN * KS * 2;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int C_STRIDE = BN + 8;             // see Cfg::C_STRIDE
-    static constexpr int C_BYTES = TM * C_STRIDE * 4;   // one band of TM rows
-    static constexpr int LDS_BYTES = RING_BYTES > C_BYTES ? RING_BYTES : C_BYTES;
-    static_assert(KS == 32 || KS == 64, "ring stage depth");
-    static_assert(STAGES == 3, "the K loop keeps two stages in flight");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
-};
-
-// One instruction fills 1 KB of a stage, RPI rows of KS * 2 bytes: lane L lands at position
-// L % LPR of row RPI * g + L / LPR and fetches the logical chunk the swizzle keeps there.
-template <int ROWS, int NT, int KS>
-struct Ring {
-    static constexpr int LPR = KS / 8;    // lanes per row (16 bytes each)
-    static constexpr int RPI = 64 / LPR;  // rows per instruction
-    static constexpr int GROUPS = ROWS / RPI;
-    static constexpr int WAVES = NT / 64;
-    static constexpr int PER = GROUPS / WAVES;   // instructions per wave per stage
-    static_assert(GROUPS % WAVES == 0, "row groups must split evenly over the waves");
-    const char* src[PER];   // the lane's chunk in its row at K step 0
-    int wave;
-
-    __device__ __forceinline__ static int row_of(int wave, int i, int lane) { return RPI * (wave + WAVES * i) + lane / LPR; }
-    __device__ __forceinline__ static int chunk_of(int wave, int i, int lane) {
-        const int r = row_of(wave, i, lane);
-        return KS == 64 ? (lane & 7) ^ ((r >> 1) & 7) : (lane & 3) ^ ((r >> 2) & 3);
-    }
-    __device__ __forceinline__ void issue(int kt, char* stage) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            __builtin_amdgcn_global_load_lds((g_void*)(src[i] + kt * (KS * 2)),
-                                             (l_void*)(stage + 1024 * (wave + WAVES * i)), 16, 0, 0);
-    }
-};
-
-// s_waitcnt vmcnt(n) alone (gfx9 encoding: expcnt and lgkmcnt fields at their "no wait" maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <class C>
-__device__ __forceinline__ void mma_step32(const char* lA, const char* lB, f32x16_t (&acc)[C::MI][C::NI],
-                                           int wm0, int wn0, int lane) {
-    bf16x8_t a[2][C::MI], b[2][C::NI];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-            a[s][i] = *reinterpret_cast<const bf16x8_t*>(lA + lds_off32(wm0 + i * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-            b[s][j] = *reinterpret_cast<const bf16x8_t*>(lB + lds_off32(wn0 + j * 32 + (lane & 31), ch));
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][i], b[s][j], acc[i][j], 0, 0, 0);
-}
-
-// K loop over the ring.  Every iteration issues one stage (past the end it re-reads the last step
-// into a free stage, never read), so exactly one stage of this wave's loads is still allowed in
-// flight when a stage is consumed.  Ends with no load in flight, so the caller may reuse the LDS.
-template <class C, class LA, class LB>
-__device__ __forceinline__ void gemm_tile_ring(const LA& la, const LB& lb, int nk, char* smem,
-                                               f32x16_t (&acc)[C::MI][C::NI], int wm0, int wn0, int lane) {
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    if (nk <= 0) return;
-    constexpr int PER_STEP = LA::PER + LB::PER;
-    la.issue(0, smem);
-    lb.issue(0, smem + C::A_BYTES);
-    char* s1 = smem + C::STAGE_BYTES;
-    la.issue(min(1, nk - 1), s1);
-    lb.issue(min(1, nk - 1), s1 + C::A_BYTES);
-    int cur = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-        wait_vmcnt<PER_STEP>();   // this wave's loads of step kt have landed
-        __syncthreads();          // everyone's have, and stage (kt+2)%3 = (kt-1)%3 is no longer read
-        const int nxt2 = cur == 0 ? 2 : cur - 1;   // (kt + 2) % 3
-        char* st = smem + nxt2 * C::STAGE_BYTES;
-        const int kl = min(kt + 2, nk - 1);
-        la.issue(kl, st);
-        lb.issue(kl, st + C::A_BYTES);
-        const char* sc = smem + cur * C::STAGE_BYTES;
-        if constexpr (C::KS == 64)
-            mma_step<C>(sc, sc + C::A_BYTES, acc, wm0, wn0, lane);
-        else
-            mma_step32<C>(sc, sc + C::A_BYTES, acc, wm0, wn0, lane);
-        cur = cur == 2 ? 0 : cur + 1;
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-}
-
-// Accumulators of the waves in row band `band` to the C tile (band-local rows).
-template <class C, class ColOf>
-__device__ __forceinline__ void band_to_lds(float* ct, const f32x16_t (&acc)[C::MI][C::NI], int lane, ColOf col_of) {
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-            const int col = col_of(ni) + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ct[(mi * 32 + acc_row(r, lane)) * C::C_STRIDE + col] = acc[mi][ni][r];
-        }
-}
-
-// gemm1 on the ring: dispatch gather + L1 (NT) + SwiGLU, same tile order and column mapping as
-// gemm1_kernel (each wave's TN weight rows are [gate | up] of TN/2 intermediate columns).
-template <class C>
-__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_ring_kernel(const uint16_t* __restrict__ x,
-                                                                       const uint16_t* __restrict__ w1p, Dims d,
-                                                                       Ws ws, uint16_t* __restrict__ act_out,
-                                                                       uint16_t* __restrict__ hgu_out) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WN, wn = wave % C::WN;
-    const int wm0 = wm * C::TM, wn0 = wn * C::TN;
-    const int H = d.H, I = d.I;
-    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);
-    const int n_tiles = (2 * I) / C::BN;
-    const int total = m_tiles * n_tiles;
-    const int npairs = d.T * d.k;
-    constexpr int HALF = C::TN / 2;
-    const char* zrow = reinterpret_cast<const char*>(ws.zeros);
-
-    const TileRange tr(total);
-    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
-        int mt, nt;
-        tile_at(ws, d, n_tiles, tile, mt, nt);
-        const int e = ws.tile_expert[mt];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
-        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
-
-        Ring<C::BM, C::NT, C::KS> la;   // token rows through row_pair; padding rows read the zero row
-        la.wave = wave;
-#pragma unroll
-        for (int i = 0; i < la.PER; ++i) {
-            const int p = ws.row_pair[row0 + la.row_of(wave, i, lane)];
-            const int c16 = 16 * la.chunk_of(wave, i, lane);
-            la.src[i] = (p >= 0 && p < npairs)
-                            ? reinterpret_cast<const char*>(x + static_cast<int64_t>(p / d.k) * H) + c16
-                            : zrow + c16;
-        }
-        Ring<C::BN, C::NT, C::KS> lb;
-        const char* wbase = reinterpret_cast<const char*>(w1p + static_cast<int64_t>(e) * 2 * I * H);
-        lb.wave = wave;
-#pragma unroll
-        for (int i = 0; i < lb.PER; ++i) {
-            const int nl = lb.row_of(wave, i, lane);
-            const int w = nl / C::TN, j = nl % C::TN;
-            const int grow = (j / HALF) * I + nt * (C::BN / 2) + w * HALF + (j % HALF);
-            lb.src[i] = wbase + static_cast<int64_t>(grow) * H * 2 + 16 * lb.chunk_of(wave, i, lane);
-        }
-        f32x16_t acc[C::MI][C::NI];
-        __syncthreads();   // the previous tile's epilogue reads of LDS are done
-        gemm_tile_ring<C>(la, lb, H / C::KS, smem, acc, wm0, wn0, lane);
-
-        float* ct = reinterpret_cast<float*>(smem);
-        constexpr int CH = C::BN / 16;
-        const int c0 = nt * (C::BN / 2);
-        for (int band = 0; band < C::WM; ++band) {
-            if (wm == band)
-                band_to_lds<C>(ct, acc, lane, [&](int ni) {
-                    return ni < C::NI / 2 ? wn * HALF + ni * 32 : C::BN / 2 + wn * HALF + (ni - C::NI / 2) * 32;
-                });
-            __syncthreads();
-            for (int u = tid; u < C::TM * CH; u += C::NT) {
-                const int rl = u / CH, c8 = (u % CH) * 8;
-                const int64_t row = row0 + band * C::TM + rl;
-                float g[8], up[8], a[8];
-                ld8(ct + rl * C::C_STRIDE + c8, g);
-                ld8(ct + rl * C::C_STRIDE + C::BN / 2 + c8, up);
-                if (hgu_out) {
-                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + c0 + c8) = bf16x8_of(g);
-                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + I + c0 + c8) = bf16x8_of(up);
-                }
-                if (act_out) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) a[q] = silu_f32(g[q]) * up[q];
-                    *reinterpret_cast<u32x4*>(act_out + row * I + c0 + c8) = bf16x8_of(a);
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// gemm1 with one row band of waves (WM = 1): each wave holds whole rows of TN/2 gate columns and
-// the matching up columns, so SwiGLU runs on the accumulators; the bf16 results go through a
-// wave-private LDS slab (TM rows x TN/2 columns) and leave as 16-byte row segments.
-template <class C>
-struct WideEpi {
-    static constexpr int HALF = C::TN / 2;         // intermediate columns per wave
-    static constexpr int LD = HALF + 8;            // slab row stride (elements): the two half-waves
-                                                   // of an accumulator write land 64 banks apart
-    static constexpr int SLAB = C::TM * LD;        // elements per wave
-    static constexpr int LDS_BYTES = (C::NT / 64) * SLAB * 2;
-};
-
-template <class C>
-__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm1_wide_kernel(const uint16_t* __restrict__ x,
-                                                                       const uint16_t* __restrict__ w1p, Dims d,
-                                                                       Ws ws, uint16_t* __restrict__ act_out,
-                                                                       uint16_t* __restrict__ hgu_out) {
-    static_assert(C::WM == 1, "one row band of waves");
-    using Epi = WideEpi<C>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave, wn0 = wn * C::TN;
-    const int H = d.H, I = d.I;
-    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);
-    const int n_tiles = (2 * I) / C::BN;
-    const int total = m_tiles * n_tiles;
-    const int npairs = d.T * d.k;
-    constexpr int HALF = Epi::HALF, NH = C::NI / 2;
-    const char* zrow = reinterpret_cast<const char*>(ws.zeros);
-    uint16_t* slab = reinterpret_cast<uint16_t*>(smem) + wave * Epi::SLAB;
-
-    const TileRange tr(total);
-    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
-        int mt, nt;
-        tile_at(ws, d, n_tiles, tile, mt, nt);
-        const int e = ws.tile_expert[mt];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
-        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
-
-        Ring<C::BM, C::NT, C::KS> la;   // token rows through row_pair; padding rows read the zero row
-        la.wave = wave;
-#pragma unroll
-        for (int i = 0; i < la.PER; ++i) {
-            const int p = ws.row_pair[row0 + la.row_of(wave, i, lane)];
-            const int c16 = 16 * la.chunk_of(wave, i, lane);
-            la.src[i] = (p >= 0 && p < npairs)
-                            ? reinterpret_cast<const char*>(x + static_cast<int64_t>(p / d.k) * H) + c16
-                            : zrow + c16;
-        }
-        Ring<C::BN, C::NT, C::KS> lb;
-        const char* wbase = reinterpret_cast<const char*>(w1p + static_cast<int64_t>(e) * 2 * I * H);
-        lb.wave = wave;
-#pragma unroll
-        for (int i = 0; i < lb.PER; ++i) {
-            const int nl = lb.row_of(wave, i, lane);
-            const int w = nl / C::TN, j = nl % C::TN;
-            const int grow = (j / HALF) * I + nt * (C::BN / 2) + w * HALF + (j % HALF);
-            lb.src[i] = wbase + static_cast<int64_t>(grow) * H * 2 + 16 * lb.chunk_of(wave, i, lane);
-        }
-        f32x16_t acc[C::MI][C::NI];
-        __syncthreads();   // the previous tile's epilogue reads of LDS are done
-        gemm_tile_ring<C>(la, lb, H / C::KS, smem, acc, 0, wn0, lane);
-
-        // passes: gate and up pre-activations (when hgu_out), then SwiGLU (when act_out)
-        const int c0 = nt * (C::BN / 2) + wn * HALF;
-        for (int pass = 0; pass < 3; ++pass) {
-            uint16_t* out = pass < 2 ? hgu_out : act_out;
-            if (!out) continue;   // uniform
-            const int64_t ld = pass < 2 ? 2 * static_cast<int64_t>(I) : I;
-            const int col0 = (pass == 1 ? I : 0) + c0;
-#pragma unroll
-            for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-                for (int jj = 0; jj < NH; ++jj)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float g = acc[mi][jj][r], u = acc[mi][jj + NH][r];
-                        const float v = pass == 0 ? g : pass == 1 ? u : silu_f32(g) * u;
-                        slab[(mi * 32 + acc_row(r, lane)) * Epi::LD + jj * 32 + (lane & 31)] = f32_to_bf16(v);
-                    }
-            __syncthreads();
-            constexpr int CPR = HALF / 8;   // 16-byte chunks per row
-            for (int u = lane; u < C::TM * CPR; u += 64) {
-                const int rl = u / CPR, ch = u - rl * CPR;
-                *reinterpret_cast<u32x4*>(out + (row0 + rl) * ld + col0 + ch * 8) =
-                    *reinterpret_cast<const u32x4*>(slab + rl * Epi::LD + ch * 8);
-            }
-            __syncthreads();   // the slab is rewritten by the next pass
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1073,30 +589,6 @@ using G128 = Cfg<128, 128, 2, 2>;
 using G256 = Cfg<256, 128, 4, 1>;
 using WG = Cfg<128, 128, 2, 2>;   // weight-gradient tiles
 
-template <class C>
-static hipError_t gemm1_launch(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
-                               uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
-    const size_t lds = C::LDS_BYTES;
-    auto k = gemm1_kernel<C>;
-    allow_lds(k, lds);
-    const int n_tiles = 2 * d.I / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
-    k<<<grid, C::NT, lds, s>>>(x, w1p, d, ws, act_out, hgu_out);
-    return hipGetLastError();
-}
-
-template <class C>
-static hipError_t gemm2_launch(const Dims& d, const uint16_t* act, const uint16_t* w2p, const float* topk_w,
-                               const Ws& ws, uint16_t* y, hipStream_t s) {
-    const size_t lds = C::LDS_BYTES + 3 * sizeof(int) * C::BM;
-    auto k = gemm2_kernel<C>;
-    allow_lds(k, lds);
-    const int n_tiles = d.H / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
-    k<<<grid, C::NT, lds, s>>>(act, w2p, topk_w, d, ws, y);
-    return hipGetLastError();
-}
-
 template <class C0>
 static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
                                const Ws& ws, int fuse, hipStream_t s) {
@@ -1108,62 +600,6 @@ static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* t
     const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
     k<<<grid, C::NT, lds, s>>>(dy, topk_w, w2p, d, ws, fuse);
     return hipGetLastError();
-}
-
-using R128 = DCfg<128, 256, 2, 2, 32, 3, 2>;   // ring kernel for block_m 128
-
-template <class C>
-static hipError_t gemm1_ring_launch(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
-                                    uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
-    const size_t lds = C::LDS_BYTES;
-    auto k = gemm1_ring_kernel<C>;
-    allow_lds(k, lds);
-    const int n_tiles = 2 * d.I / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
-    k<<<grid, C::NT, lds, s>>>(x, w1p, d, ws, act_out, hgu_out);
-    return hipGetLastError();
-}
-
-using W128 = DCfg<128, 512, 1, 4, 32, 3, 1>;   // wide ring kernel for block_m 128
-
-template <class C>
-static hipError_t gemm1_wide_launch(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
-                                    uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
-    const size_t lds = C::RING_BYTES > WideEpi<C>::LDS_BYTES ? C::RING_BYTES : WideEpi<C>::LDS_BYTES;
-    auto k = gemm1_wide_kernel<C>;
-    allow_lds(k, lds);
-    const int n_tiles = 2 * d.I / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
-    k<<<grid, C::NT, lds, s>>>(x, w1p, d, ws, act_out, hgu_out);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
-                        uint16_t* act_out, uint16_t* hgu_out, hipStream_t s) {
-#ifdef MOE_WIDE_L1
-    if (d.BM == 128 && (2 * d.I) % W128::BN == 0 && d.H % W128::KS == 0)
-        return gemm1_wide_launch<W128>(d, x, w1p, ws, act_out, hgu_out, s);
-#endif
-    if (d.BM == 128 && (2 * d.I) % R128::BN == 0 && d.H % R128::KS == 0)
-        return gemm1_ring_launch<R128>(d, x, w1p, ws, act_out, hgu_out, s);
-    switch (d.BM) {
-        case 32: return gemm1_launch<G32>(d, x, w1p, ws, act_out, hgu_out, s);
-        case 64: return gemm1_launch<G64>(d, x, w1p, ws, act_out, hgu_out, s);
-        case 128: return gemm1_launch<G128>(d, x, w1p, ws, act_out, hgu_out, s);
-        case 256: return gemm1_launch<G256>(d, x, w1p, ws, act_out, hgu_out, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16_t* w2p, const float* topk_w,
-                                const Ws& ws, uint16_t* y, hipStream_t s) {
-    switch (d.BM) {
-        case 32: return gemm2_launch<G32>(d, act, w2p, topk_w, ws, y, s);
-        case 64: return gemm2_launch<G64>(d, act, w2p, topk_w, ws, y, s);
-        case 128: return gemm2_launch<G128>(d, act, w2p, topk_w, ws, y, s);
-        case 256: return gemm2_launch<G256>(d, act, w2p, topk_w, ws, y, s);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,

@@ -1,0 +1,564 @@
+// Forward grouped GEMMs of the MoE expert layer on gfx950 (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation), reading fragment-packed weights ("Mega MoE" page, Pipeline: the L1 grouped
+// GEMM with the dispatch gather and SwiGLU, and the L2 grouped GEMM with the top-k combine).
+//
+// Tiles.  An M tile is up to eight 32-row groups of one expert's segment (256 rows), covering only
+// the groups that hold real rows: rows past the last real group are padding and get no MFMA work.
+// An expert with more than eight groups is cut into M tiles of equal size (the last one padded
+// with zero rows), so the workgroups that stream the same weight panel progress at the same rate
+// and the later reads of the panel hit L2.  An N tile is BN = 4 waves
+// x 32*NI columns; every wave (one per SIMD) computes all rows of its own 32*NI columns.  So a
+// weight panel (expert, N tile) is streamed by one workgroup per M tile, and an expert's token
+// rows are read by the workgroups of all its N tiles at the same time, from L2.
+//
+// Operands
+//   A  token rows (L1: x rows gathered through row_pair; L2: act rows), K-contiguous.  Shared by
+//      the waves, so it goes through LDS, straight from memory (global_load_lds_dwordx4: no
+//      staging registers, no LDS store instructions) into a ring of three 64-deep K slots; each
+//      load instruction fills 8 rows x 128 bytes, chunks XOR-swizzled so fragment reads spread
+//      over the banks.
+//   B  packed expert weights (moe_pack_weights): every 1 KB block is one MFMA B operand of a
+//      32-column group and a 16-deep K step.  Each wave owns its column groups, so B never
+//      touches LDS: a wave streams its blocks straight into registers, one contiguous 1 KB load
+//      per block, through a ring of three 64-deep K stages.
+// Both are loaded two slots ahead of their MFMAs.  Per slot: wait for this wave's loads of the
+// slot, one barrier, then the slot's four 16-deep MFMA steps, each issuing a quarter of the loads
+// of slot + 2 and reading the next step's fragments between its MFMAs.  The LDS slots
+// are distinct noalias pointers of the K loop, so the compiler does not make fragment reads wait
+// for the DMA loads into other slots.
+//
+// Schedule: a persistent grid of one workgroup per CU.  The tile list is ordered expert by
+// expert, then N tile by N tile with the M tiles of that panel adjacent, and cut into one
+// contiguous chunk per XCD (workgroup b runs on XCD b mod 8).  Workgroups take the next tile of
+// their XCD's chunk from an atomic counter, and help other XCDs once their own is done.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void g_void;
+typedef __attribute__((address_space(3))) void l_void;
+
+constexpr int kWaves = 4;
+constexpr int kXcds = 8;
+constexpr int kSlots = 3;   // LDS slots of A and register stages of B, 64-deep K each
+constexpr int kMaxEL = 1024;
+
+// NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most; OCC: workgroups per CU.
+template <int NI_, int MAXMI_, int OCC_>
+struct Tile {
+    static constexpr int NI = NI_, MAXMI = MAXMI_, OCC = OCC_;
+    static_assert(MAXMI >= 1 && MAXMI <= 8, "M tile of 1..8 groups");
+    static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
+    static constexpr int NT = 64 * kWaves;
+    static constexpr int SLOT = BM * 128;   // bytes of one A slot: BM rows x 64 bf16
+    static constexpr int RING_BYTES = kSlots * SLOT;
+    static constexpr int ROWINFO_BYTES = 3 * 4 * BM;
+    static constexpr int LDS_BYTES = RING_BYTES + ROWINFO_BYTES;
+};
+
+// 16-byte chunk c of LDS row r sits at position c ^ ((r >> 1) & 7): rows r and r + 1 fill the
+// two halves of the 64 banks, so the 16 rows of a fragment read hit 16 distinct bank groups.
+__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
+    return static_cast<uint32_t>(row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4));
+}
+
+// Row of accumulator element r of a 32x32 MFMA block (lane % 32 is the column).
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// s_waitcnt vmcnt(n) alone (gfx9 encoding: expcnt and lgkmcnt fields at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Loads of one tile with MA active 32-row groups.  DMA instruction i of wave w fills rows
+// 32 i + 8 w .. 32 i + 8 w + 7 of a slot: lane L lands at position L % 8 of row 32 i + 8 w + L / 8
+// and fetches the logical chunk the swizzle keeps there.
+template <class C, int MA>
+struct Pipe {
+    const char* a_src[MA];       // the lane's chunk of its row in group i, at K 0
+    const char* b_src[C::NI];    // the lane's 16 bytes of block (column group, K step 0)
+    bf16x8_t b[kSlots][C::NI][4];
+    int nslot;                   // K / 64 (loads past the end re-read the last slot)
+    int wave;
+
+    // part q (0..3) of the loads of slot j: A rows of groups i = q, q + 4, ...; B K step q
+    __device__ __forceinline__ void a_issue(int j, char* __restrict__ slot, int q) const {
+        const int jj = min(j, nslot - 1);
+#pragma unroll
+        for (int i = 0; i < MA; ++i)
+            if (i % 4 == q)
+                __builtin_amdgcn_global_load_lds((g_void*)(a_src[i] + jj * 128),
+                                                 (l_void*)(slot + 1024 * (wave + kWaves * i)), 16, 0, 0);
+    }
+    __device__ __forceinline__ void b_issue(int j, int buf, int q) {
+        const int jj = min(j, nslot - 1);
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+            b[buf][ni][q] = *reinterpret_cast<const bf16x8_t*>(b_src[ni] + (4 * jj + q) * 1024);
+    }
+    static constexpr int a_loads(int q) { return (MA + 3 - q) / 4; }
+    static constexpr int kBLoads = 4 * C::NI;
+    static constexpr int kLoadsPerSlot = MA + kBLoads;
+};
+
+template <class C, int MA>
+__device__ __forceinline__ void read_frags(bf16x8_t (&a)[MA], const char* __restrict__ slot, int kb, int lane) {
+#pragma unroll
+    for (int mi = 0; mi < MA; ++mi)
+        a[mi] = *reinterpret_cast<const bf16x8_t*>(slot + lds_off(mi * 32 + (lane & 31), 2 * kb + (lane >> 5)));
+}
+
+// One slot of the unrolled loop (U = j % 3 static: LDS slot and B stage U).  The loads of slot
+// j + 2 go out a quarter per 16-deep step, between the MFMAs (a burst would stall the waves on the
+// CU's shared address unit); each step reads the next step's fragments between its MFMAs.
+//
+// ISSUE false (the last two slots, past the loop) issues nothing: those loads would only fetch
+// past the end, the compiler drops the register ones as dead, and the wait counts below count
+// loads in issue order, so they must match what really went out.  WAIT is the number of this
+// wave's loads issued after slot j's that may still be in flight.
+template <class C, int MA, int U, bool ISSUE, int WAIT>
+__device__ __forceinline__ void slot_step(Pipe<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+                                          char* __restrict__ s2, f32x16_t (&acc)[MA][C::NI], int lane) {
+    char* const slots[3] = {s0, s1, s2};
+    constexpr int FAR = U == 0 ? 2 : U - 1;   // (j+2)%3
+    // this wave's loads of slot j landed (those of slot j+1 may still be in flight), then
+    // everyone's have, and slot (j+2)%3 = (j-1)%3 is no longer read
+    wait_vmcnt<WAIT>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's fragment reads are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t a[2][MA];
+    read_frags<C, MA>(a[0], slots[U], 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        if (ISSUE) {
+            p.a_issue(j + 2, slots[FAR], kb);
+            p.b_issue(j + 2, FAR, kb);
+        }
+        if (kb < 3) read_frags<C, MA>(a[(kb + 1) & 1], slots[U], kb + 1, lane);
+#pragma unroll
+        for (int mi = 0; mi < MA; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb & 1][mi], p.b[U][ni][kb], acc[mi][ni], 0, 0, 0);
+        // order: MFMA, fragment read, global load alternating
+        constexpr int NM = MA * C::NI;
+        const int nv = ISSUE ? Pipe<C, MA>::a_loads(kb) + C::NI : 0;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
+            if (kb < 3 && i < MA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // global load
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// acc = A[rows, 0:K] . B[0:K, cols] (K a multiple of 128).  Ends with no load in flight and all
+// waves past their last fragment read, so the caller may reuse the LDS.
+template <class C, int MA>
+__device__ __forceinline__ void k_loop(Pipe<C, MA>& p, char* __restrict__ s0, char* __restrict__ s1,
+                                       char* __restrict__ s2, f32x16_t (&acc)[MA][C::NI], int lane) {
+#pragma unroll
+    for (int mi = 0; mi < MA; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    // all loads of slot 0 go out before any of slot 1: the waits count loads in issue order
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        p.a_issue(0, s0, q);
+        p.b_issue(0, 0, q);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        p.a_issue(1, s1, q);
+        p.b_issue(1, 1, q);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int j = 0;
+    constexpr int kL = Pipe<C, MA>::kLoadsPerSlot;
+    for (; j + 3 <= p.nslot; j += 3) {
+        slot_step<C, MA, 0, true, kL>(p, j, s0, s1, s2, acc, lane);
+        slot_step<C, MA, 1, true, kL>(p, j + 1, s0, s1, s2, acc, lane);
+        slot_step<C, MA, 2, true, kL>(p, j + 2, s0, s1, s2, acc, lane);
+    }
+    // one or two slots remain: their loads went out in the prologue or the loop, and one more
+    // slot's worth (slot j + 1, or a re-read past the end) follows slot j's
+    if (j < p.nslot) slot_step<C, MA, 0, false, kL>(p, j, s0, s1, s2, acc, lane);
+    if (j + 1 < p.nslot) slot_step<C, MA, 1, false, 0>(p, j + 1, s0, s1, s2, acc, lane);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Tile list and schedule
+// ---------------------------------------------------------------------------------------------
+// Groups of real rows of expert e and its number of M tiles.
+__device__ __forceinline__ int real_groups(const Ws& ws, int e) {
+    const int c = ws.counts[e];
+    return c > 0 ? (c + 31) >> 5 : 0;
+}
+template <int MAXMI>
+__device__ __forceinline__ int m_tiles_of(int groups) { return (groups + MAXMI - 1) / MAXMI; }
+
+// s_pref[e] = M tiles of experts [0, e), e in [0, EL]; returns the total.
+template <int NT, int MAXMI>
+__device__ int m_tile_prefix(const Ws& ws, int EL, int* s_pref, int* s_part) {
+    static_assert(4 * NT >= kMaxEL, "four experts per thread");
+    const int tid = threadIdx.x;
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        v[q] = e < EL ? m_tiles_of<MAXMI>(real_groups(ws, e)) : 0;
+        sum += v[q];
+    }
+    s_part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+        const int t = tid >= off ? s_part[tid - off] : 0;
+        __syncthreads();
+        s_part[tid] += t;
+        __syncthreads();
+    }
+    int run = s_part[tid] - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        if (e <= EL) s_pref[e] = run;
+        run += v[q];
+    }
+    __syncthreads();
+    return s_part[NT - 1];
+}
+
+struct TileRef {
+    int e, nt, row0, groups, real_rows, last;   // groups computed (some may be zero rows); rows that
+                                                // belong to the tile; last: holds the expert's last group
+};
+
+// List position -> tile: expert e owns positions [n_tiles * s_pref[e], n_tiles * s_pref[e+1]),
+// N tile major, its M tiles adjacent.
+__device__ __forceinline__ TileRef decode(const Ws& ws, int EL, int n_tiles, int pos, const int* s_pref) {
+    int lo = 0, hi = EL;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] * n_tiles <= pos) lo = mid;
+        else hi = mid;
+    }
+    TileRef t;
+    t.e = lo;
+    const int mt_e = s_pref[lo + 1] - s_pref[lo];
+    const int local = pos - s_pref[lo] * n_tiles;
+    t.nt = local / mt_e;
+    const int mt = local - t.nt * mt_e;
+    const int g = real_groups(ws, lo), q = (g + mt_e - 1) / mt_e;   // groups per M tile
+    const int g0 = mt * q;
+    t.groups = q;
+    t.row0 = ws.offsets[lo] + 32 * g0;
+    t.real_rows = 32 * max(0, min(q, g - g0));
+    t.last = mt == mt_e - 1;
+    return t;
+}
+
+// Next list position for this workgroup, or -1.  Counters in ws.tile_sync: [0, 8) one per XCD
+// chunk, [8] finished workgroups; all zero between launches (the last workgroup resets them).
+__device__ int grab(int32_t* cnt, int total) {
+    const int nx = gridDim.x % kXcds == 0 ? kXcds : 1;
+    const int x = nx == kXcds ? blockIdx.x % kXcds : 0;
+    const int chunk = (total + nx - 1) / nx;
+    for (int k = 0; k < nx; ++k) {
+        const int xx = x + k < nx ? x + k : x + k - nx;
+        const int lo = xx * chunk, hi = min(total, lo + chunk);
+        if (lo >= hi) continue;
+        const int p = atomicAdd(&cnt[xx], 1);
+        if (lo + p < hi) return lo + p;
+    }
+    return -1;
+}
+
+__device__ void finish_schedule(int32_t* cnt) {
+    if (threadIdx.x == 0 && atomicAdd(&cnt[kXcds], 1) == static_cast<int>(gridDim.x) - 1)
+        for (int k = 0; k <= kXcds; ++k) atomicExch(&cnt[k], 0);
+}
+
+// Runs the tile list: body.run<MA>(tile) for each tile this workgroup takes.
+template <class C, class Body>
+__device__ __forceinline__ void run_tiles(const Dims& d, const Ws& ws, int n_tiles, Body& body) {
+    __shared__ int s_pref[kMaxEL + 1];
+    __shared__ int s_part[C::NT];
+    __shared__ int s_pos;
+    const int EL = d.EL;
+    const int total = m_tile_prefix<C::NT, C::MAXMI>(ws, EL, s_pref, s_part) * n_tiles;
+    for (;;) {
+        if (threadIdx.x == 0) s_pos = grab(ws.tile_sync, total);
+        lds_barrier();   // publishes s_pos; the previous tile's LDS reads are done
+        const int pos = s_pos;
+        if (pos < 0) break;
+        const TileRef t = decode(ws, EL, n_tiles, pos, s_pref);
+        if (t.row0 < 0 || t.row0 + t.real_rows > ws.rows_cap) continue;   // tables not from one prologue
+        switch (t.groups) {
+            case 1: body.template run<1>(t); break;
+            case 2: if constexpr (C::MAXMI >= 2) body.template run<2>(t); break;
+            case 3: if constexpr (C::MAXMI >= 3) body.template run<3>(t); break;
+            case 4: if constexpr (C::MAXMI >= 4) body.template run<4>(t); break;
+            case 5: if constexpr (C::MAXMI >= 5) body.template run<5>(t); break;
+            case 6: if constexpr (C::MAXMI >= 6) body.template run<6>(t); break;
+            case 7: if constexpr (C::MAXMI >= 7) body.template run<7>(t); break;
+            case 8: if constexpr (C::MAXMI >= 8) body.template run<8>(t); break;
+            default: break;
+        }
+    }
+    finish_schedule(ws.tile_sync);
+}
+
+// ---------------------------------------------------------------------------------------------
+// L1: dispatch gather + grouped GEMM (NT) + SwiGLU
+// ---------------------------------------------------------------------------------------------
+// Packed W1 column group nb holds gate columns (nb even) or the matching up columns (nb odd) of
+// intermediate columns [32 (nb/2), 32 (nb/2) + 32), so a wave's blocks 2q and 2q + 1 are the gate
+// and up of the same columns, lane by lane.
+template <class C>
+struct L1Body {
+    const uint16_t* x;
+    const uint16_t* w1f;
+    Dims d;
+    Ws ws;
+    uint16_t* act_out;
+    uint16_t* hgu_out;
+    char* smem;
+
+    template <int MA>
+    __device__ __forceinline__ void run(const TileRef& t) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int H = d.H, I = d.I, npairs = d.T * d.k;
+        Pipe<C, MA> p;
+        p.nslot = H / 64;
+        p.wave = __builtin_amdgcn_readfirstlane(wave);
+        const char* zrow = reinterpret_cast<const char*>(ws.zeros);
+#pragma unroll
+        for (int i = 0; i < MA; ++i) {
+            const int row = 32 * i + 8 * wave + (lane >> 3);
+            const int pr = row < t.real_rows ? ws.row_pair[t.row0 + row] : -1;
+            const int c16 = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+            p.a_src[i] = (pr >= 0 && pr < npairs)
+                             ? reinterpret_cast<const char*>(x + static_cast<int64_t>(pr / d.k) * H) + c16
+                             : zrow + c16;
+        }
+        const char* wb = reinterpret_cast<const char*>(w1f) + static_cast<int64_t>(t.e) * (2 * I) * H * 2;
+        const int nb0 = t.nt * (C::BN / 32) + wave * C::NI;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+            p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (H / 16) * 1024 + lane * 16;
+        f32x16_t acc[MA][C::NI];
+        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, acc, lane);
+
+        const int g0 = nb0 / 2;   // first intermediate column group of the wave
+#pragma unroll
+        for (int q = 0; q < C::NI / 2; ++q) {
+            const int col = 32 * (g0 + q) + (lane & 31);
+#pragma unroll
+            for (int mi = 0; mi < MA; ++mi) {
+                if (32 * mi >= t.real_rows) break;   // zero rows that belong to no output
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = t.row0 + mi * 32 + acc_row(r, lane);
+                    const float g = acc[mi][2 * q][r], u = acc[mi][2 * q + 1][r];
+                    if (hgu_out) {
+                        hgu_out[row * 2 * I + col] = f32_to_bf16(g);
+                        hgu_out[row * 2 * I + I + col] = f32_to_bf16(u);
+                    }
+                    if (act_out) act_out[row * I + col] = f32_to_bf16(silu_f32(g) * u);
+                }
+            }
+        }
+        if (t.last) {   // padding rows after the last real group read as zero rows downstream
+            const int64_t r0 = t.row0 + t.real_rows, r1 = min(static_cast<int64_t>(ws.offsets[t.e + 1]), ws.rows_cap);
+            const int c0 = t.nt * (C::BN / 2);
+            constexpr int CH = C::BN / 16;   // 8-column chunks of the tile's intermediate columns
+            for (int64_t u = tid; u < (r1 - r0) * CH; u += C::NT) {
+                const int64_t row = r0 + u / CH;
+                const int c = c0 + static_cast<int>(u % CH) * 8;
+                const u32x4 z = 0;
+                if (act_out) *reinterpret_cast<u32x4*>(act_out + row * I + c) = z;
+                if (hgu_out) {
+                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + c) = z;
+                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + I + c) = z;
+                }
+            }
+        }
+    }
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::OCC) void l1_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1f,
+                                                     Dims d, Ws ws, uint16_t* __restrict__ act_out,
+                                                     uint16_t* __restrict__ hgu_out) {
+    static_assert(C::NI % 2 == 0, "a wave holds whole gate/up pairs");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    L1Body<C> body{x, w1f, d, ws, act_out, hgu_out, smem};
+    run_tiles<C>(d, ws, 2 * d.I / C::BN, body);
+}
+
+// ---------------------------------------------------------------------------------------------
+// L2: grouped GEMM (NT) + top-k weighted combine
+// ---------------------------------------------------------------------------------------------
+// Row r of pair p = (t, j): o = act[r] @ W2[e]^T scaled by topk_w[p].  A token with one local
+// pair owns its y row, so the epilogue stores bf16(w * o) there; a token with several local
+// pairs gets fp32 rows in ws.stage that combine_finish sums in slot order.
+template <class C>
+struct L2Body {
+    const uint16_t* act;
+    const uint16_t* w2f;
+    const float* topk_w;
+    Dims d;
+    Ws ws;
+    uint16_t* y;
+    char* smem;
+
+    template <int MA>
+    __device__ __forceinline__ void run(const TileRef& t) {
+        int* s_tok = reinterpret_cast<int*>(smem + C::RING_BYTES);   // token, or -1 (padding)
+        float* s_w = reinterpret_cast<float*>(s_tok + C::BM);
+        int* s_direct = reinterpret_cast<int*>(s_w + C::BM);
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int H = d.H, I = d.I, npairs = d.T * d.k;
+        for (int r = tid; r < 32 * MA; r += C::NT) {   // read in the epilogue, after the K loop's barriers
+            const int pr = r < t.real_rows ? ws.row_pair[t.row0 + r] : -1;
+            int tok = -1, direct = 0;
+            float w = 0.0f;
+            if (pr >= 0 && pr < npairs) {
+                tok = pr / d.k;
+                w = topk_w[pr];
+                direct = ws.tok_nloc[tok] == 1;
+            }
+            s_tok[r] = tok;
+            s_w[r] = w;
+            s_direct[r] = direct;
+        }
+        Pipe<C, MA> p;
+        p.nslot = I / 64;
+        p.wave = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int i = 0; i < MA; ++i) {
+            const int row = 32 * i + 8 * wave + (lane >> 3);
+            const int c16 = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+            p.a_src[i] = row < t.real_rows
+                             ? reinterpret_cast<const char*>(act + (t.row0 + row) * static_cast<int64_t>(I)) + c16
+                             : reinterpret_cast<const char*>(ws.zeros) + c16;
+        }
+        const char* wb = reinterpret_cast<const char*>(w2f) + static_cast<int64_t>(t.e) * H * I * 2;
+        const int nb0 = t.nt * (C::BN / 32) + wave * C::NI;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+            p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (I / 16) * 1024 + lane * 16;
+        f32x16_t acc[MA][C::NI];
+        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, acc, lane);
+
+        // one row at a time (scheduling barriers keep the row information from being hoisted)
+        const int col0 = nb0 * 32 + (lane & 31);
+#pragma unroll
+        for (int mi = 0; mi < MA; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = mi * 32 + acc_row(r, lane);
+                const int tok = s_tok[rl];
+                const float w = s_w[rl];
+                if (tok >= 0) {
+                    if (s_direct[rl]) {
+                        uint16_t* yr = y + static_cast<int64_t>(tok) * H + col0;
+#pragma unroll
+                        for (int ni = 0; ni < C::NI; ++ni) yr[ni * 32] = f32_to_bf16(w * acc[mi][ni][r]);
+                    } else {
+                        float* sr = ws.stage + (t.row0 + rl) * static_cast<int64_t>(H) + col0;
+#pragma unroll
+                        for (int ni = 0; ni < C::NI; ++ni) sr[ni * 32] = w * acc[mi][ni][r];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::OCC) void l2_kernel(const uint16_t* __restrict__ act,
+                                                     const uint16_t* __restrict__ w2f,
+                                                     const float* __restrict__ topk_w, Dims d, Ws ws,
+                                                     uint16_t* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    L2Body<C> body{act, w2f, topk_w, d, ws, y, smem};
+    run_tiles<C>(d, ws, d.H / C::BN, body);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------------------------
+template <class K>
+int persistent_grid(K kernel, int threads, size_t lds) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    int64_t g = static_cast<int64_t>(per_cu) * device_cu_count();
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (g >= kXcds) g -= g % kXcds;   // the same number of workgroups on every XCD
+    return static_cast<int>(g < 1 ? 1 : g);
+}
+
+template <class K>
+void allow_lds(K kernel, size_t bytes) {
+    static bool done = false;   // per instantiation
+    if (!done && bytes > 64 * 1024) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+        done = true;
+    }
+}
+
+template <class C>
+hipError_t l1_launch(const Dims& d, const uint16_t* x, const uint16_t* w1f, const Ws& ws, uint16_t* act_out,
+                     uint16_t* hgu_out, hipStream_t s) {
+    auto k = l1_kernel<C>;
+    allow_lds(k, C::LDS_BYTES);
+    k<<<persistent_grid(k, C::NT, C::LDS_BYTES), C::NT, C::LDS_BYTES, s>>>(x, w1f, d, ws, act_out, hgu_out);
+    return hipGetLastError();
+}
+
+template <class C>
+hipError_t l2_launch(const Dims& d, const uint16_t* act, const uint16_t* w2f, const float* topk_w, const Ws& ws,
+                     uint16_t* y, hipStream_t s) {
+    auto k = l2_kernel<C>;
+    allow_lds(k, C::LDS_BYTES);
+    k<<<persistent_grid(k, C::NT, C::LDS_BYTES), C::NT, C::LDS_BYTES, s>>>(act, w2f, topk_w, d, ws, y);
+    return hipGetLastError();
+}
+
+using L1Tile = Tile<2, 8, 1>;
+using L2Tile = Tile<1, 4, 2>;
+
+}  // namespace
+
+// L1 N tiles are 256 columns (2I is a multiple of 256); L2 N tiles 128 columns (H is a multiple of 128).
+hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1f, const Ws& ws, uint16_t* act_out,
+                        uint16_t* hgu_out, hipStream_t s) {
+    if (d.EL > kMaxEL) return hipErrorInvalidValue;
+    return l1_launch<L1Tile>(d, x, w1f, ws, act_out, hgu_out, s);
+}
+
+hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16_t* w2f, const float* topk_w,
+                                const Ws& ws, uint16_t* y, hipStream_t s) {
+    if (d.EL > kMaxEL) return hipErrorInvalidValue;
+    return l2_launch<L2Tile>(d, act, w2f, topk_w, ws, y, s);
+}
+
+}  // namespace moe

@@ -34,6 +34,7 @@ struct Ws {
     uint16_t* dact;         // bf16 [R_max, I]  (train)
     uint16_t* dhgu;         // bf16 [R_max, 2I] (train)
     uint16_t* zeros;        // a zero row of max(H, 2I) bf16 (written by the prologue)
+    int32_t* tile_sync;     // [kMaxGrid] tile-scheduler counters of the forward GEMMs (zero between launches)
     int64_t rows_cap;
     int32_t num_blocks;     // R_max / BM
     int32_t num_chunks;     // prologue chunks of kRouteChunk pairs
@@ -41,6 +42,7 @@ struct Ws {
 };
 
 constexpr int kRouteThreads = 256;
+constexpr int kMaxGrid = 512;   // workgroups of a persistent GEMM launch, at most
 constexpr int kRouteChunk = 2048;   // pairs per prologue block
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -51,10 +53,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {   // round to nearest
 }
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then s_barrier.
+// __syncthreads() also fences global memory, which waits for every global load in flight
+// (s_waitcnt vmcnt(0)) and so drains a software pipeline at each step.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Fragment-major packed weights.  An expert's matrix B[n][k] (n output column, k reduction index,
+// K = reduction length) is stored as 1 KB blocks, one per (32-column group, 16-deep K step),
+// column group major; inside a block lane L holds the 8 consecutive k of column 32*nb + L%32
+// starting at 16*kb + 8*(L/32): the B operand of v_mfma_f32_32x32x16_bf16, one 16-byte load per
+// lane.  Eight consecutive k (from a multiple of 8) of one column are 16 contiguous bytes.
+__host__ __device__ __forceinline__ int64_t frag_index(int64_t n, int64_t k, int64_t K) {
+    return (((n >> 5) * (K >> 4) + (k >> 4)) * 64 + ((k >> 3) & 1) * 32 + (n & 31)) * 8 + (k & 7);
+}
+// Packed column of L1 output column n ([gate | up], 2I wide): column groups alternate gate and
+// up of the same 32 intermediate columns, so a wave holding groups 2g and 2g+1 holds both halves
+// of SwiGLU's input for intermediate columns [32g, 32g + 32).
+__host__ __device__ __forceinline__ int64_t l1_packed_col(int64_t n, int64_t I) {
+    const int64_t t = n >= I ? 1 : 0, m = n - t * I;
+    return (m >> 5) * 64 + t * 32 + (m & 31);
+}
+
 // Host launchers (each returns a hipError_t from the launch).
 hipError_t launch_route(const Dims& d, const int32_t* topk_idx, const Ws& ws, hipStream_t s);
 hipError_t launch_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, uint16_t* w1p,
                        uint16_t* w2p, hipStream_t s);
+hipError_t launch_unpack(const Dims& d, const uint16_t* w1p, const uint16_t* w2p, uint16_t* w1,
+                         uint16_t* w2, hipStream_t s);
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
                         uint16_t* act_out, uint16_t* hgu_out, hipStream_t s);
 hipError_t launch_swiglu(const Dims& d, const uint16_t* hgu, const Ws& ws, uint16_t* act,

@@ -45,9 +45,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_
         if (e >= 0) atomicAdd(&hist[e], 1);
     }
     if (drop) atomicAdd(&s_drop, drop);
-    if (blockIdx.x == 0)   // the zero row read by the GEMMs for padding rows
+    if (blockIdx.x == 0) {   // the zero row read by the GEMMs for padding rows; K-split counters
         for (int i = tid; i < ws.zero_len / 8; i += blockDim.x)
             reinterpret_cast<uint4*>(ws.zeros)[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < kMaxGrid; i += blockDim.x) ws.tile_sync[i] = 0;
+    }
     __syncthreads();
     for (int e = tid; e < d.EL; e += blockDim.x)
         ws.chunk_hist[static_cast<int64_t>(blockIdx.x) * d.EL + e] = hist[e];
