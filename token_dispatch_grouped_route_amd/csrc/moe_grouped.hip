@@ -30,7 +30,8 @@
 // Schedule: a persistent grid of one workgroup per CU.  The tile list is ordered expert by
 // expert, then N tile by N tile with the M tiles of that panel adjacent, and cut into one
 // contiguous chunk per XCD (workgroup b runs on XCD b mod 8).  Workgroups take the next tile of
-// their XCD's chunk from an atomic counter, and help other XCDs once their own is done.
+// their XCD's chunk from an atomic counter, largest tiles first, and help other XCDs once their
+// own is done.
 #include "moe_internal.h"
 
 namespace moe {
@@ -212,16 +213,19 @@ __device__ __forceinline__ int real_groups(const Ws& ws, int e) {
 template <int MAXMI>
 __device__ __forceinline__ int m_tiles_of(int groups) { return (groups + MAXMI - 1) / MAXMI; }
 
-// s_pref[e] = M tiles of experts [0, e), e in [0, EL]; returns the total.
+// s_pref[e] = M tiles of experts [0, e), e in [0, EL]; s_q[e] = groups per M tile of expert e
+// (0: no rows); returns the total.
 template <int NT, int MAXMI>
-__device__ int m_tile_prefix(const Ws& ws, int EL, int* s_pref, int* s_part) {
+__device__ int m_tile_prefix(const Ws& ws, int EL, int* s_pref, int* s_q, int* s_part) {
     static_assert(4 * NT >= kMaxEL, "four experts per thread");
     const int tid = threadIdx.x;
     int v[4], sum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = 4 * tid + q;
-        v[q] = e < EL ? m_tiles_of<MAXMI>(real_groups(ws, e)) : 0;
+        const int g = e < EL ? real_groups(ws, e) : 0;
+        v[q] = m_tiles_of<MAXMI>(g);
+        if (e < EL) s_q[e] = v[q] > 0 ? (g + v[q] - 1) / v[q] : 0;
         sum += v[q];
     }
     s_part[tid] = sum;
@@ -248,15 +252,21 @@ struct TileRef {
                                                 // belong to the tile; last: holds the expert's last group
 };
 
-// List position -> tile: expert e owns positions [n_tiles * s_pref[e], n_tiles * s_pref[e+1]),
-// N tile major, its M tiles adjacent.
-__device__ __forceinline__ TileRef decode(const Ws& ws, int EL, int n_tiles, int pos, const int* s_pref) {
+// Expert owning list position pos: expert e owns positions [n_tiles * s_pref[e],
+// n_tiles * s_pref[e+1]), N tile major, its M tiles adjacent.
+__device__ __forceinline__ int expert_of(int EL, int n_tiles, int pos, const int* s_pref) {
     int lo = 0, hi = EL;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (s_pref[mid] * n_tiles <= pos) lo = mid;
         else hi = mid;
     }
+    return lo;
+}
+
+// List position -> tile.
+__device__ __forceinline__ TileRef decode(const Ws& ws, int EL, int n_tiles, int pos, const int* s_pref) {
+    const int lo = expert_of(EL, n_tiles, pos, s_pref);
     TileRef t;
     t.e = lo;
     const int mt_e = s_pref[lo + 1] - s_pref[lo];
@@ -272,10 +282,14 @@ __device__ __forceinline__ TileRef decode(const Ws& ws, int EL, int n_tiles, int
     return t;
 }
 
-// Next list position for this workgroup, or -1.  Counters in ws.tile_sync: [0, 8) one per XCD
-// chunk, [8] finished workgroups; all zero between launches (the last workgroup resets them).
+// The list is cut into one contiguous chunk per XCD (workgroup b runs on XCD b mod 8).
+__device__ __forceinline__ int schedule_chunks() { return gridDim.x % kXcds == 0 ? kXcds : 1; }
+
+// Next (chunk, rank in chunk) for this workgroup as lo + rank, or -1: its own XCD's chunk first,
+// then the others'.  Counters in ws.tile_sync: [0, 8) one per chunk, [8] finished workgroups; all
+// zero between launches (the last workgroup resets them).
 __device__ int grab(int32_t* cnt, int total) {
-    const int nx = gridDim.x % kXcds == 0 ? kXcds : 1;
+    const int nx = schedule_chunks();
     const int x = nx == kXcds ? blockIdx.x % kXcds : 0;
     const int chunk = (total + nx - 1) / nx;
     for (int k = 0; k < nx; ++k) {
@@ -288,6 +302,29 @@ __device__ int grab(int32_t* cnt, int total) {
     return -1;
 }
 
+// Inside a chunk, tiles are handed out largest first (longest-processing-time order, so the last
+// tiles to start are the short ones and the workgroups finish close together): the chunk's
+// experts by decreasing groups per M tile, each expert's positions in list order.  Maps rank r of
+// a chunk (as lo + r) to its list position.  Chunks spanning many experts keep list order.
+constexpr int kLptMaxExperts = 64;
+template <int MAXMI>
+__device__ int lpt_position(int EL, int n_tiles, int total, int slot, const int* s_pref, const int* s_q) {
+    const int nx = schedule_chunks();
+    const int chunk = (total + nx - 1) / nx;
+    const int lo = (slot / chunk) * chunk, hi = min(total, lo + chunk);
+    const int e0 = expert_of(EL, n_tiles, lo, s_pref), e1 = expert_of(EL, n_tiles, hi - 1, s_pref);
+    if (e1 - e0 >= kLptMaxExperts) return slot;
+    int p = slot - lo;
+    for (int q = MAXMI; q >= 1; --q)
+        for (int e = e0; e <= e1; ++e) {
+            if (s_q[e] != q) continue;
+            const int a = max(lo, s_pref[e] * n_tiles), b = min(hi, s_pref[e + 1] * n_tiles);
+            if (p < b - a) return a + p;
+            p -= b - a;
+        }
+    return slot;   // not reached: the classes cover the chunk
+}
+
 __device__ void finish_schedule(int32_t* cnt) {
     if (threadIdx.x == 0 && atomicAdd(&cnt[kXcds], 1) == static_cast<int>(gridDim.x) - 1)
         for (int k = 0; k <= kXcds; ++k) atomicExch(&cnt[k], 0);
@@ -297,12 +334,16 @@ __device__ void finish_schedule(int32_t* cnt) {
 template <class C, class Body>
 __device__ __forceinline__ void run_tiles(const Dims& d, const Ws& ws, int n_tiles, Body& body) {
     __shared__ int s_pref[kMaxEL + 1];
+    __shared__ int s_q[kMaxEL];
     __shared__ int s_part[C::NT];
     __shared__ int s_pos;
     const int EL = d.EL;
-    const int total = m_tile_prefix<C::NT, C::MAXMI>(ws, EL, s_pref, s_part) * n_tiles;
+    const int total = m_tile_prefix<C::NT, C::MAXMI>(ws, EL, s_pref, s_q, s_part) * n_tiles;
     for (;;) {
-        if (threadIdx.x == 0) s_pos = grab(ws.tile_sync, total);
+        if (threadIdx.x == 0) {
+            const int slot = grab(ws.tile_sync, total);
+            s_pos = slot < 0 ? -1 : lpt_position<C::MAXMI>(EL, n_tiles, total, slot, s_pref, s_q);
+        }
         lds_barrier();   // publishes s_pos; the previous tile's LDS reads are done
         const int pos = s_pos;
         if (pos < 0) break;
@@ -466,28 +507,47 @@ struct L2Body {
         f32x16_t acc[MA][C::NI];
         k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, acc, lane);
 
-        // one row at a time (scheduling barriers keep the row information from being hoisted)
-        const int col0 = nb0 * 32 + (lane & 31);
+        // Epilogue through LDS (the ring is free after the K loop), two 32-row groups per pass:
+        // the waves drop their accumulators into a row-major fp32 tile, then each wave takes whole
+        // rows, scales them by the pair's weight and stores 4-column chunks (bf16 into y for a
+        // token's only local pair, fp32 into the stage row otherwise), so every store instruction
+        // covers a contiguous row segment.
+        constexpr int LD = C::BN + 8;   // floats per LDS row: rows r and r + 4 fall in opposite bank halves
+        constexpr int CH = C::BN / 4;   // 4-column chunks per row
+        static_assert(2 * 32 * LD * 4 <= C::RING_BYTES, "two groups fit in the ring");
+        float* tile = reinterpret_cast<float*>(smem);
+        const int colw = wave * 32 * C::NI + (lane & 31);
 #pragma unroll
-        for (int mi = 0; mi < MA; ++mi)
+        for (int m0 = 0; m0 < MA; m0 += 2) {
+            if (m0 > 0) lds_barrier();   // the previous pass's reads are done
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = mi * 32 + acc_row(r, lane);
+            for (int mm = 0; mm < 2; ++mm)
+                if (m0 + mm < MA)
+#pragma unroll
+                    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            tile[(mm * 32 + acc_row(r, lane)) * LD + colw + ni * 32] = acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
+            lds_barrier();
+            const int rows = (m0 + 2 <= MA ? 2 : 1) * 32;
+            for (int u = tid; u < rows * CH; u += C::NT) {
+                const int rr = u / CH, c4 = (u % CH) * 4;
+                const int rl = m0 * 32 + rr;
                 const int tok = s_tok[rl];
+                if (tok < 0) continue;
                 const float w = s_w[rl];
-                if (tok >= 0) {
-                    if (s_direct[rl]) {
-                        uint16_t* yr = y + static_cast<int64_t>(tok) * H + col0;
-#pragma unroll
-                        for (int ni = 0; ni < C::NI; ++ni) yr[ni * 32] = f32_to_bf16(w * acc[mi][ni][r]);
-                    } else {
-                        float* sr = ws.stage + (t.row0 + rl) * static_cast<int64_t>(H) + col0;
-#pragma unroll
-                        for (int ni = 0; ni < C::NI; ++ni) sr[ni * 32] = w * acc[mi][ni][r];
-                    }
+                const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + c4);
+                const int64_t col = static_cast<int64_t>(t.nt) * C::BN + c4;
+                if (s_direct[rl]) {
+                    const uint32_t lo = f32_to_bf16(w * v.x) | (static_cast<uint32_t>(f32_to_bf16(w * v.y)) << 16);
+                    const uint32_t hi = f32_to_bf16(w * v.z) | (static_cast<uint32_t>(f32_to_bf16(w * v.w)) << 16);
+                    *reinterpret_cast<uint2*>(y + static_cast<int64_t>(tok) * H + col) = make_uint2(lo, hi);
+                } else {
+                    *reinterpret_cast<float4*>(ws.stage + (t.row0 + rl) * static_cast<int64_t>(H) + col) =
+                        make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
+        }
     }
 };
 
@@ -544,11 +604,12 @@ hipError_t l2_launch(const Dims& d, const uint16_t* act, const uint16_t* w2f, co
 }
 
 using L1Tile = Tile<2, 8, 1>;
-using L2Tile = Tile<1, 4, 2>;
+using L2Tile = Tile<2, 8, 1>;
+using L2TileNarrow = Tile<1, 8, 1>;
 
 }  // namespace
 
-// L1 N tiles are 256 columns (2I is a multiple of 256); L2 N tiles 128 columns (H is a multiple of 128).
+// L1 N tiles are 256 columns (2I is a multiple of 256); L2 N tiles 256 columns when H allows, else 128.
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1f, const Ws& ws, uint16_t* act_out,
                         uint16_t* hgu_out, hipStream_t s) {
     if (d.EL > kMaxEL) return hipErrorInvalidValue;
@@ -558,7 +619,8 @@ hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1f, c
 hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16_t* w2f, const float* topk_w,
                                 const Ws& ws, uint16_t* y, hipStream_t s) {
     if (d.EL > kMaxEL) return hipErrorInvalidValue;
-    return l2_launch<L2Tile>(d, act, w2f, topk_w, ws, y, s);
+    return d.H % L2Tile::BN == 0 ? l2_launch<L2Tile>(d, act, w2f, topk_w, ws, y, s)
+                                 : l2_launch<L2TileNarrow>(d, act, w2f, topk_w, ws, y, s);
 }
 
 }  // namespace moe
