@@ -43,19 +43,21 @@ typedef __attribute__((address_space(3))) void l_void;
 
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;
-constexpr int kSlots = 3;   // LDS slots of A and register stages of B, 64-deep K each
 constexpr int kMaxEL = 1024;
+constexpr int kEpiBatch = 4;   // L2 epilogue: LDS chunks read before their stores go out
 
-// NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most; OCC: workgroups per CU.
-template <int NI_, int MAXMI_, int OCC_>
+// NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most; OCC: workgroups per CU;
+// SLOTS: LDS slots of A and register stages of B (64-deep K each), loaded SLOTS - 1 slots ahead.
+template <int NI_, int MAXMI_, int OCC_, int SLOTS_>
 struct Tile {
-    static constexpr int NI = NI_, MAXMI = MAXMI_, OCC = OCC_;
+    static constexpr int NI = NI_, MAXMI = MAXMI_, OCC = OCC_, SLOTS = SLOTS_;
     static_assert(MAXMI >= 1 && MAXMI <= 8, "M tile of 1..8 groups");
+    static_assert(SLOTS == 3 || SLOTS == 4, "ring of three or four slots");
     static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
     static constexpr int NT = 64 * kWaves;
     static constexpr int SLOT = BM * 128;   // bytes of one A slot: BM rows x 64 bf16
-    static constexpr int RING_BYTES = kSlots * SLOT;
-    static constexpr int ROWINFO_BYTES = 3 * 4 * BM;
+    static constexpr int RING_BYTES = SLOTS * SLOT;
+    static constexpr int ROWINFO_BYTES = 16 * BM;   // L2: per row (token, weight, direct)
     static constexpr int LDS_BYTES = RING_BYTES + ROWINFO_BYTES;
 };
 
@@ -82,7 +84,7 @@ template <class C, int MA>
 struct Pipe {
     const char* a_src[MA];       // the lane's chunk of its row in group i, at K 0
     const char* b_src[C::NI];    // the lane's 16 bytes of block (column group, K step 0)
-    bf16x8_t b[kSlots][C::NI][4];
+    bf16x8_t b[C::SLOTS][C::NI][4];
     int nslot;                   // K / 64 (loads past the end re-read the last slot)
     int wave;
 
@@ -113,21 +115,22 @@ __device__ __forceinline__ void read_frags(bf16x8_t (&a)[MA], const char* __rest
         a[mi] = *reinterpret_cast<const bf16x8_t*>(slot + lds_off(mi * 32 + (lane & 31), 2 * kb + (lane >> 5)));
 }
 
-// One slot of the unrolled loop (U = j % 3 static: LDS slot and B stage U).  The loads of slot
-// j + 2 go out a quarter per 16-deep step, between the MFMAs (a burst would stall the waves on the
-// CU's shared address unit); each step reads the next step's fragments between its MFMAs.
+// One slot of the unrolled loop (U = j % SLOTS static: LDS slot and B stage U).  The loads of
+// slot j + SLOTS - 1 go out a quarter per 16-deep step, between the MFMAs (a burst would stall
+// the waves on the CU's shared address unit); each step reads the next step's fragments between
+// its MFMAs.
 //
-// ISSUE false (the last two slots, past the loop) issues nothing: those loads would only fetch
-// past the end, the compiler drops the register ones as dead, and the wait counts below count
-// loads in issue order, so they must match what really went out.  WAIT is the number of this
-// wave's loads issued after slot j's that may still be in flight.
+// ISSUE false (the slots past the unrolled loop) issues nothing: those loads would only fetch
+// past the end, the compiler drops the register ones as dead, and the wait counts count loads in
+// issue order, so they must match what really went out.  WAIT is the number of this wave's loads
+// issued after slot j's, which may still be in flight.
 template <class C, int MA, int U, bool ISSUE, int WAIT>
 __device__ __forceinline__ void slot_step(Pipe<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
-                                          char* __restrict__ s2, f32x16_t (&acc)[MA][C::NI], int lane) {
-    char* const slots[3] = {s0, s1, s2};
-    constexpr int FAR = U == 0 ? 2 : U - 1;   // (j+2)%3
-    // this wave's loads of slot j landed (those of slot j+1 may still be in flight), then
-    // everyone's have, and slot (j+2)%3 = (j-1)%3 is no longer read
+                                          char* __restrict__ s2, char* __restrict__ s3,
+                                          f32x16_t (&acc)[MA][C::NI], int lane) {
+    char* const slots[4] = {s0, s1, s2, s3};
+    constexpr int FAR = (U + C::SLOTS - 1) % C::SLOTS;   // slot of j + SLOTS - 1 = slot of j - 1
+    // this wave's loads of slot j landed, then everyone's have, and slot FAR is no longer read
     wait_vmcnt<WAIT>();
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's fragment reads are done
     __builtin_amdgcn_s_barrier();
@@ -138,8 +141,8 @@ __device__ __forceinline__ void slot_step(Pipe<C, MA>& p, int j, char* __restric
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         if (ISSUE) {
-            p.a_issue(j + 2, slots[FAR], kb);
-            p.b_issue(j + 2, FAR, kb);
+            p.a_issue(j + C::SLOTS - 1, slots[FAR], kb);
+            p.b_issue(j + C::SLOTS - 1, FAR, kb);
         }
         if (kb < 3) read_frags<C, MA>(a[(kb + 1) & 1], slots[U], kb + 1, lane);
 #pragma unroll
@@ -160,42 +163,67 @@ __device__ __forceinline__ void slot_step(Pipe<C, MA>& p, int j, char* __restric
     }
 }
 
+// Slots j + I .. j + SLOTS - 1 of one turn of the unrolled loop.
+template <class C, int MA, int I>
+__device__ __forceinline__ void loop_turn(Pipe<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+                                          char* __restrict__ s2, char* __restrict__ s3,
+                                          f32x16_t (&acc)[MA][C::NI], int lane) {
+    if constexpr (I < C::SLOTS) {
+        slot_step<C, MA, I, true, (C::SLOTS - 2) * Pipe<C, MA>::kLoadsPerSlot>(p, j + I, s0, s1, s2, s3, acc, lane);
+        loop_turn<C, MA, I + 1>(p, j, s0, s1, s2, s3, acc, lane);
+    }
+}
+
+// The last nslot % SLOTS slots (j is a multiple of SLOTS): all their loads went out in the
+// prologue or the loop, which issued through slot j + SLOTS - 2 (re-reading the last slot past
+// the end), so SLOTS - 2 - I slots' loads follow those of slot j + I.
+template <class C, int MA, int I>
+__device__ __forceinline__ void loop_tail(Pipe<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+                                          char* __restrict__ s2, char* __restrict__ s3,
+                                          f32x16_t (&acc)[MA][C::NI], int lane) {
+    if constexpr (I < C::SLOTS - 1) {
+        if (j + I < p.nslot) {
+            slot_step<C, MA, I, false, (C::SLOTS - 2 - I) * Pipe<C, MA>::kLoadsPerSlot>(p, j + I, s0, s1, s2, s3, acc, lane);
+            loop_tail<C, MA, I + 1>(p, j, s0, s1, s2, s3, acc, lane);
+        }
+    }
+}
+
+// Issues the loads of slots I .. SLOTS - 2 (prologue), all of one slot before any of the next: the
+// waits count loads in issue order.
+template <class C, int MA, int I>
+__device__ __forceinline__ void prologue_issue(Pipe<C, MA>& p, char* __restrict__ s0, char* __restrict__ s1,
+                                               char* __restrict__ s2) {
+    if constexpr (I < C::SLOTS - 1) {
+        char* const slots[3] = {s0, s1, s2};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            p.a_issue(I, slots[I], q);
+            p.b_issue(I, I, q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        prologue_issue<C, MA, I + 1>(p, s0, s1, s2);
+    }
+}
+
 // acc = A[rows, 0:K] . B[0:K, cols] (K a multiple of 128).  Ends with no load in flight and all
-// waves past their last fragment read, so the caller may reuse the LDS.
+// waves past their last fragment read, so the caller may reuse the LDS.  s3 is unused with three
+// slots.
 template <class C, int MA>
 __device__ __forceinline__ void k_loop(Pipe<C, MA>& p, char* __restrict__ s0, char* __restrict__ s1,
-                                       char* __restrict__ s2, f32x16_t (&acc)[MA][C::NI], int lane) {
+                                       char* __restrict__ s2, char* __restrict__ s3,
+                                       f32x16_t (&acc)[MA][C::NI], int lane) {
 #pragma unroll
     for (int mi = 0; mi < MA; ++mi)
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-    // all loads of slot 0 go out before any of slot 1: the waits count loads in issue order
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        p.a_issue(0, s0, q);
-        p.b_issue(0, 0, q);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        p.a_issue(1, s1, q);
-        p.b_issue(1, 1, q);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    prologue_issue<C, MA, 0>(p, s0, s1, s2);
     int j = 0;
-    constexpr int kL = Pipe<C, MA>::kLoadsPerSlot;
-    for (; j + 3 <= p.nslot; j += 3) {
-        slot_step<C, MA, 0, true, kL>(p, j, s0, s1, s2, acc, lane);
-        slot_step<C, MA, 1, true, kL>(p, j + 1, s0, s1, s2, acc, lane);
-        slot_step<C, MA, 2, true, kL>(p, j + 2, s0, s1, s2, acc, lane);
-    }
-    // one or two slots remain: their loads went out in the prologue or the loop, and one more
-    // slot's worth (slot j + 1, or a re-read past the end) follows slot j's
-    if (j < p.nslot) slot_step<C, MA, 0, false, kL>(p, j, s0, s1, s2, acc, lane);
-    if (j + 1 < p.nslot) slot_step<C, MA, 1, false, 0>(p, j + 1, s0, s1, s2, acc, lane);
+    for (; j + C::SLOTS <= p.nslot; j += C::SLOTS) loop_turn<C, MA, 0>(p, j, s0, s1, s2, s3, acc, lane);
+    loop_tail<C, MA, 0>(p, j, s0, s1, s2, s3, acc, lane);
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
@@ -284,45 +312,30 @@ __device__ __forceinline__ TileRef decode(const Ws& ws, int EL, int n_tiles, int
 
 // The list is cut into one contiguous chunk per XCD (workgroup b runs on XCD b mod 8).
 __device__ __forceinline__ int schedule_chunks() { return gridDim.x % kXcds == 0 ? kXcds : 1; }
-
-// Next (chunk, rank in chunk) for this workgroup as lo + rank, or -1: its own XCD's chunk first,
-// then the others'.  Counters in ws.tile_sync: [0, 8) one per chunk, [8] finished workgroups; all
-// zero between launches (the last workgroup resets them).
-__device__ int grab(int32_t* cnt, int total) {
+__device__ __forceinline__ int chunk_size(int total) {
     const int nx = schedule_chunks();
-    const int x = nx == kXcds ? blockIdx.x % kXcds : 0;
-    const int chunk = (total + nx - 1) / nx;
-    for (int k = 0; k < nx; ++k) {
-        const int xx = x + k < nx ? x + k : x + k - nx;
-        const int lo = xx * chunk, hi = min(total, lo + chunk);
-        if (lo >= hi) continue;
-        const int p = atomicAdd(&cnt[xx], 1);
-        if (lo + p < hi) return lo + p;
-    }
-    return -1;
+    return (total + nx - 1) / nx;
 }
 
-// Inside a chunk, tiles are handed out largest first (longest-processing-time order, so the last
-// tiles to start are the short ones and the workgroups finish close together): the chunk's
-// experts by decreasing groups per M tile, each expert's positions in list order.  Maps rank r of
-// a chunk (as lo + r) to its list position.  Chunks spanning many experts keep list order.
-constexpr int kLptMaxExperts = 64;
-template <int MAXMI>
-__device__ int lpt_position(int EL, int n_tiles, int total, int slot, const int* s_pref, const int* s_q) {
-    const int nx = schedule_chunks();
-    const int chunk = (total + nx - 1) / nx;
-    const int lo = (slot / chunk) * chunk, hi = min(total, lo + chunk);
-    const int e0 = expert_of(EL, n_tiles, lo, s_pref), e1 = expert_of(EL, n_tiles, hi - 1, s_pref);
-    if (e1 - e0 >= kLptMaxExperts) return slot;
-    int p = slot - lo;
-    for (int q = MAXMI; q >= 1; --q)
-        for (int e = e0; e <= e1; ++e) {
-            if (s_q[e] != q) continue;
-            const int a = max(lo, s_pref[e] * n_tiles), b = min(hi, s_pref[e + 1] * n_tiles);
-            if (p < b - a) return a + p;
-            p -= b - a;
-        }
-    return slot;   // not reached: the classes cover the chunk
+// Counters in ws.tile_sync: [0, 8) one per chunk, [8] finished workgroups; all zero between
+// launches (the last workgroup resets them).  A workgroup first takes ranks of its own XCD's
+// chunk, then helps the others.
+__device__ __forceinline__ int own_chunk() { return schedule_chunks() == kXcds ? blockIdx.x % kXcds : 0; }
+
+// Rank p (returned by the atomic on the own chunk's counter) -> slot lo + p, or, once the own chunk
+// is used up, a slot taken from another chunk, or -1.
+__device__ int settle_grab(int32_t* cnt, int total, int p) {
+    const int nx = schedule_chunks(), x = own_chunk(), chunk = chunk_size(total);
+    const int lo = x * chunk, hi = min(total, lo + chunk);
+    if (lo + p < hi) return lo + p;
+    for (int k = 1; k < nx; ++k) {
+        const int xx = x + k < nx ? x + k : x + k - nx;
+        const int l2 = xx * chunk, h2 = min(total, l2 + chunk);
+        if (l2 >= h2) continue;
+        const int q = atomicAdd(&cnt[xx], 1);
+        if (l2 + q < h2) return l2 + q;
+    }
+    return -1;
 }
 
 __device__ void finish_schedule(int32_t* cnt) {
@@ -330,38 +343,99 @@ __device__ void finish_schedule(int32_t* cnt) {
         for (int k = 0; k <= kXcds; ++k) atomicExch(&cnt[k], 0);
 }
 
-// Runs the tile list: body.run<MA>(tile) for each tile this workgroup takes.
+// Inside a chunk, tiles are handed out largest first (longest-processing-time order, so the last
+// tiles to start are the short ones and the workgroups finish close together): the chunk's
+// experts by decreasing groups per M tile, each expert's positions in list order.  The table
+// holds, per chunk, the segments of that order (first rank, first list position); a chunk that
+// spans more experts than the table holds keeps list order.
+constexpr int kLptMaxSeg = 64;
+struct LptTable {
+    int start[kXcds][kLptMaxSeg];
+    int pos[kXcds][kLptMaxSeg];
+    int n[kXcds];   // segments, or 0: list order
+};
+
+template <int MAXMI>
+__device__ void build_lpt(int EL, int n_tiles, int total, const int* s_pref, const int* s_q, LptTable& tb) {
+    const int nx = schedule_chunks(), x = threadIdx.x;
+    if (x < nx) {
+        const int chunk = chunk_size(total);
+        const int lo = x * chunk, hi = min(total, lo + chunk);
+        int n = 0;
+        if (lo < hi) {
+            const int e0 = expert_of(EL, n_tiles, lo, s_pref), e1 = expert_of(EL, n_tiles, hi - 1, s_pref);
+            if (e1 - e0 < kLptMaxSeg) {
+                int rank = 0;
+                for (int q = MAXMI; q >= 1; --q)
+                    for (int e = e0; e <= e1; ++e) {
+                        if (s_q[e] != q) continue;
+                        const int a = max(lo, s_pref[e] * n_tiles), b = min(hi, s_pref[e + 1] * n_tiles);
+                        if (b <= a) continue;
+                        tb.start[x][n] = rank;
+                        tb.pos[x][n] = a;
+                        ++n;
+                        rank += b - a;
+                    }
+            }
+        }
+        tb.n[x] = n;
+    }
+    __syncthreads();
+}
+
+// Slot (chunk lo + rank) -> list position.
+__device__ __forceinline__ int lpt_position(int total, int slot, const LptTable& tb) {
+    const int chunk = chunk_size(total);
+    const int x = slot / chunk, p = slot - x * chunk;
+    const int n = tb.n[x];
+    if (n == 0) return slot;
+    int i = 0;
+    while (i + 1 < n && tb.start[x][i + 1] <= p) ++i;
+    return tb.pos[x][i] + (p - tb.start[x][i]);
+}
+
+// Runs the tile list: body.run<MA>(tile) for each tile this workgroup takes.  (The next tile is
+// claimed only once the current one is done: a claim made earlier would hold a tile that an idle
+// workgroup could start, which at the end of the list lengthens the tail.)
 template <class C, class Body>
 __device__ __forceinline__ void run_tiles(const Dims& d, const Ws& ws, int n_tiles, Body& body) {
     __shared__ int s_pref[kMaxEL + 1];
     __shared__ int s_q[kMaxEL];
     __shared__ int s_part[C::NT];
-    __shared__ int s_pos;
+    __shared__ LptTable s_lpt;
+    __shared__ int s_pos[2];   // alternate per tile: written for tile i + 1 while tile i's is read
     const int EL = d.EL;
     const int total = m_tile_prefix<C::NT, C::MAXMI>(ws, EL, s_pref, s_q, s_part) * n_tiles;
-    for (;;) {
-        if (threadIdx.x == 0) {
-            const int slot = grab(ws.tile_sync, total);
-            s_pos = slot < 0 ? -1 : lpt_position<C::MAXMI>(EL, n_tiles, total, slot, s_pref, s_q);
-        }
-        lds_barrier();   // publishes s_pos; the previous tile's LDS reads are done
-        const int pos = s_pos;
+    build_lpt<C::MAXMI>(EL, n_tiles, total, s_pref, s_q, s_lpt);
+    int32_t* const cnt = ws.tile_sync;
+    if (threadIdx.x == 0) {
+        const int slot = settle_grab(cnt, total, atomicAdd(&cnt[own_chunk()], 1));
+        s_pos[0] = slot < 0 ? -1 : lpt_position(total, slot, s_lpt);
+    }
+    for (int it = 0;; ++it) {
+        lds_barrier();   // publishes s_pos[it & 1]; the previous tile's LDS reads are done
+        const int pos = s_pos[it & 1];
         if (pos < 0) break;
         const TileRef t = decode(ws, EL, n_tiles, pos, s_pref);
-        if (t.row0 < 0 || t.row0 + t.real_rows > ws.rows_cap) continue;   // tables not from one prologue
-        switch (t.groups) {
-            case 1: body.template run<1>(t); break;
-            case 2: if constexpr (C::MAXMI >= 2) body.template run<2>(t); break;
-            case 3: if constexpr (C::MAXMI >= 3) body.template run<3>(t); break;
-            case 4: if constexpr (C::MAXMI >= 4) body.template run<4>(t); break;
-            case 5: if constexpr (C::MAXMI >= 5) body.template run<5>(t); break;
-            case 6: if constexpr (C::MAXMI >= 6) body.template run<6>(t); break;
-            case 7: if constexpr (C::MAXMI >= 7) body.template run<7>(t); break;
-            case 8: if constexpr (C::MAXMI >= 8) body.template run<8>(t); break;
-            default: break;
+        if (t.row0 >= 0 && t.row0 + t.real_rows <= ws.rows_cap) {   // else tables not from one prologue
+            switch (t.groups) {
+                case 1: body.template run<1>(t); break;
+                case 2: if constexpr (C::MAXMI >= 2) body.template run<2>(t); break;
+                case 3: if constexpr (C::MAXMI >= 3) body.template run<3>(t); break;
+                case 4: if constexpr (C::MAXMI >= 4) body.template run<4>(t); break;
+                case 5: if constexpr (C::MAXMI >= 5) body.template run<5>(t); break;
+                case 6: if constexpr (C::MAXMI >= 6) body.template run<6>(t); break;
+                case 7: if constexpr (C::MAXMI >= 7) body.template run<7>(t); break;
+                case 8: if constexpr (C::MAXMI >= 8) body.template run<8>(t); break;
+                default: break;
+            }
+        }
+        if (threadIdx.x == 0) {
+            const int slot = settle_grab(cnt, total, atomicAdd(&cnt[own_chunk()], 1));
+            s_pos[(it + 1) & 1] = slot < 0 ? -1 : lpt_position(total, slot, s_lpt);
         }
     }
-    finish_schedule(ws.tile_sync);
+    finish_schedule(cnt);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -403,7 +477,7 @@ struct L1Body {
         for (int ni = 0; ni < C::NI; ++ni)
             p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (H / 16) * 1024 + lane * 16;
         f32x16_t acc[MA][C::NI];
-        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, acc, lane);
+        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, smem + (C::SLOTS - 1) * C::SLOT, acc, lane);
 
         const int g0 = nb0 / 2;   // first intermediate column group of the wave
 #pragma unroll
@@ -470,24 +544,13 @@ struct L2Body {
 
     template <int MA>
     __device__ __forceinline__ void run(const TileRef& t) {
-        int* s_tok = reinterpret_cast<int*>(smem + C::RING_BYTES);   // token, or -1 (padding)
-        float* s_w = reinterpret_cast<float*>(s_tok + C::BM);
-        int* s_direct = reinterpret_cast<int*>(s_w + C::BM);
+        int4* s_row = reinterpret_cast<int4*>(smem + C::RING_BYTES);   // token (-1: none), weight, direct
+        static_assert(C::BM <= C::NT, "one row per thread");
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int H = d.H, I = d.I, npairs = d.T * d.k;
-        for (int r = tid; r < 32 * MA; r += C::NT) {   // read in the epilogue, after the K loop's barriers
-            const int pr = r < t.real_rows ? ws.row_pair[t.row0 + r] : -1;
-            int tok = -1, direct = 0;
-            float w = 0.0f;
-            if (pr >= 0 && pr < npairs) {
-                tok = pr / d.k;
-                w = topk_w[pr];
-                direct = ws.tok_nloc[tok] == 1;
-            }
-            s_tok[r] = tok;
-            s_w[r] = w;
-            s_direct[r] = direct;
-        }
+        // the row's pair now; what depends on it is loaded after the K loop, so the loop does not
+        // start behind a chain of dependent loads
+        const int pr = tid < t.real_rows ? ws.row_pair[t.row0 + tid] : -1;
         Pipe<C, MA> p;
         p.nslot = I / 64;
         p.wave = __builtin_amdgcn_readfirstlane(wave);
@@ -505,46 +568,79 @@ struct L2Body {
         for (int ni = 0; ni < C::NI; ++ni)
             p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (I / 16) * 1024 + lane * 16;
         f32x16_t acc[MA][C::NI];
-        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, acc, lane);
+        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, smem + (C::SLOTS - 1) * C::SLOT, acc, lane);
 
-        // Epilogue through LDS (the ring is free after the K loop), two 32-row groups per pass:
-        // the waves drop their accumulators into a row-major fp32 tile, then each wave takes whole
+        if (tid < 32 * MA) {
+            int tok = -1, direct = 0;
+            float w = 0.0f;
+            if (pr >= 0 && pr < npairs) {
+                tok = pr / d.k;
+                w = topk_w[pr];
+                direct = ws.tok_nloc[tok] == 1;
+            }
+            s_row[tid] = make_int4(tok, __float_as_int(w), direct, 0);
+        }
+
+        // Epilogue through LDS (the ring is free after the K loop), GP 32-row groups per pass: the
+        // waves drop their accumulators into a row-major fp32 tile, then each wave takes whole
         // rows, scales them by the pair's weight and stores 4-column chunks (bf16 into y for a
         // token's only local pair, fp32 into the stage row otherwise), so every store instruction
-        // covers a contiguous row segment.
+        // covers a contiguous row segment.  A pass first reads all its chunks, then stores them.
         constexpr int LD = C::BN + 8;   // floats per LDS row: rows r and r + 4 fall in opposite bank halves
         constexpr int CH = C::BN / 4;   // 4-column chunks per row
-        static_assert(2 * 32 * LD * 4 <= C::RING_BYTES, "two groups fit in the ring");
+        constexpr int GP = 2;
+        constexpr int ITER = GP * 32 * CH / C::NT;
+        static_assert(ITER % kEpiBatch == 0, "whole batches");
+        static_assert(GP * 32 * LD * 4 <= C::RING_BYTES, "a pass fits in the ring");
+        static_assert(C::NT % CH == 0, "a thread's chunks share their column");
+        constexpr int RSTEP = C::NT / CH;   // rows between a thread's consecutive chunks
         float* tile = reinterpret_cast<float*>(smem);
-        const int colw = wave * 32 * C::NI + (lane & 31);
+        // Per-lane bases, re-derived in every tile (the empty asm hides their value), so that the
+        // element addresses are a base plus a constant offset instead of dozens of precomputed
+        // addresses held across the tile loop.
+        int wbase = 4 * (lane >> 5) * LD + wave * 32 * C::NI + (lane & 31);   // accumulator row 0 of a group
+        int rrow = tid / CH, rcol = (tid % CH) * 4;                             // first chunk of a pass
+        asm volatile("" : "+v"(wbase), "+v"(rrow), "+v"(rcol));
 #pragma unroll
-        for (int m0 = 0; m0 < MA; m0 += 2) {
+        for (int m0 = 0; m0 < MA; m0 += GP) {
             if (m0 > 0) lds_barrier();   // the previous pass's reads are done
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm)
+            for (int mm = 0; mm < GP; ++mm)
                 if (m0 + mm < MA)
 #pragma unroll
                     for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            tile[(mm * 32 + acc_row(r, lane)) * LD + colw + ni * 32] = acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
-            lds_barrier();
-            const int rows = (m0 + 2 <= MA ? 2 : 1) * 32;
-            for (int u = tid; u < rows * CH; u += C::NT) {
-                const int rr = u / CH, c4 = (u % CH) * 4;
-                const int rl = m0 * 32 + rr;
-                const int tok = s_tok[rl];
-                if (tok < 0) continue;
-                const float w = s_w[rl];
-                const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + c4);
-                const int64_t col = static_cast<int64_t>(t.nt) * C::BN + c4;
-                if (s_direct[rl]) {
-                    const uint32_t lo = f32_to_bf16(w * v.x) | (static_cast<uint32_t>(f32_to_bf16(w * v.y)) << 16);
-                    const uint32_t hi = f32_to_bf16(w * v.z) | (static_cast<uint32_t>(f32_to_bf16(w * v.w)) << 16);
-                    *reinterpret_cast<uint2*>(y + static_cast<int64_t>(tok) * H + col) = make_uint2(lo, hi);
-                } else {
-                    *reinterpret_cast<float4*>(ws.stage + (t.row0 + rl) * static_cast<int64_t>(H) + col) =
-                        make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+                            tile[wbase + (mm * 32 + 8 * (r >> 2) + (r & 3)) * LD + ni * 32] =
+                                acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
+            lds_barrier();   // also publishes s_row (first pass)
+            const int rows = (m0 + GP <= MA ? GP : MA - m0) * 32;
+#pragma unroll
+            for (int k0 = 0; k0 < ITER; k0 += kEpiBatch) {
+                float4 v[kEpiBatch];
+                int4 ri[kEpiBatch];
+#pragma unroll
+                for (int k = 0; k < kEpiBatch; ++k) {
+                    const int rr = rrow + (k0 + k) * RSTEP;
+                    if ((k0 + k) * RSTEP < rows) {   // rows is a multiple of 32 >= RSTEP
+                        v[k] = *reinterpret_cast<const float4*>(tile + rr * LD + rcol);
+                        ri[k] = s_row[m0 * 32 + rr];
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < kEpiBatch; ++k) {
+                    const int rr = rrow + (k0 + k) * RSTEP;
+                    if ((k0 + k) * RSTEP >= rows || ri[k].x < 0) continue;
+                    const float w = __int_as_float(ri[k].y);
+                    const int64_t col = static_cast<int64_t>(t.nt) * C::BN + rcol;
+                    if (ri[k].z) {
+                        const uint32_t lo = f32_to_bf16(w * v[k].x) | (static_cast<uint32_t>(f32_to_bf16(w * v[k].y)) << 16);
+                        const uint32_t hi = f32_to_bf16(w * v[k].z) | (static_cast<uint32_t>(f32_to_bf16(w * v[k].w)) << 16);
+                        *reinterpret_cast<uint2*>(y + static_cast<int64_t>(ri[k].x) * H + col) = make_uint2(lo, hi);
+                    } else {
+                        *reinterpret_cast<float4*>(ws.stage + (t.row0 + m0 * 32 + rr) * static_cast<int64_t>(H) + col) =
+                            make_float4(w * v[k].x, w * v[k].y, w * v[k].z, w * v[k].w);
+                    }
                 }
             }
         }
@@ -603,9 +699,9 @@ hipError_t l2_launch(const Dims& d, const uint16_t* act, const uint16_t* w2f, co
     return hipGetLastError();
 }
 
-using L1Tile = Tile<2, 8, 1>;
-using L2Tile = Tile<2, 8, 1>;
-using L2TileNarrow = Tile<1, 8, 1>;
+using L1Tile = Tile<2, 8, 1, 4>;
+using L2Tile = Tile<2, 8, 1, 4>;
+using L2TileNarrow = Tile<1, 8, 1, 4>;
 
 }  // namespace
 
