@@ -1,0 +1,119 @@
+"""Summarise rocprofv3 counter passes over bench.py into per-kernel HBM traffic and MFMA use.
+
+Each pass is its own `rocprofv3 --pmc ...` run of `bench.py --copy-calibration` (the counter
+blocks cannot all be sampled in one run).  The plain 1 GiB device copy that --copy-calibration
+adds reads and writes a known number of bytes; FETCH_SIZE / WRITE_SIZE of every kernel are scaled by
+known / measured on that copy, so the figures are in true HBM bytes whatever unit the counters use.
+
+    python profile_counters.py --trace TRACE_DIR --out-json profiles/gemm1_dsv3_share_traffic.json \
+        PASS_DIR [PASS_DIR ...] > profiles/forward_dsv3_share_counters.md
+
+Writes the L1 launch's HBM bytes (read + write) with the hash of the kernel source they were taken
+on (bench.py reports them only while that source is unchanged) and prints a markdown table.
+"""
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_grouped.hip")
+COPY_BYTES = 1 << 30   # bench.py --copy-calibration: one 1 GiB buffer copied to another
+KINDS = (("l1_kernel", "L1: dispatch gather + grouped GEMM + SwiGLU"),
+         ("l2_kernel", "L2: grouped GEMM + weighted combine"),
+         ("combine_finish", "combine finish (multi-pair tokens)"),
+         ("route_count", "prologue: count"), ("route_scan", "prologue: scan"),
+         ("route_place", "prologue: place"))
+
+
+def kind_of(name):
+    for key, _ in KINDS:
+        if key in name:
+            return key
+    if "copyBuffer" in name or ("copy" in name.lower() and "repack" not in name):
+        return "copy"
+    return None
+
+
+def read_counters(dirs):
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    copies = collections.defaultdict(list)   # counter -> (grid size, value): other copies may run too
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            k = kind_of(r["Kernel_Name"])
+            if k == "copy":
+                copies[r["Counter_Name"]].append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+            elif k:
+                agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+    if copies:   # the calibration copy is the largest one
+        out["copy"] = {}
+        for cname, vals in copies.items():
+            g = max(v[0] for v in vals)
+            sel = [v[1] for v in vals if v[0] == g]
+            out["copy"][cname] = sum(sel) / len(sel)
+    return out
+
+
+def read_durations(trace_dir):
+    dur = {}
+    for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))):
+        k = kind_of(r["Name"])
+        if k and k not in dur:
+            dur[k] = float(r["AverageNs"]) * 1e-9
+    return dur
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--out-json", required=True)
+    ap.add_argument("--command", default="", help="the command lines that made the passes, for the record")
+    ap.add_argument("passes", nargs="+")
+    a = ap.parse_args()
+    c = read_counters(a.passes)
+    dur = read_durations(a.trace)
+    cp = c.get("copy", {})
+    if "FETCH_SIZE" not in cp or "WRITE_SIZE" not in cp:
+        sys.exit("no copy-calibration kernel with FETCH_SIZE and WRITE_SIZE in the passes")
+    # counters are in KiB; scale each to the copy's known bytes
+    fr = COPY_BYTES / (cp["FETCH_SIZE"] * 1024.0)
+    fw = COPY_BYTES / (cp["WRITE_SIZE"] * 1024.0)
+    print("# rocprofv3 counters per kernel (DeepSeek-V3 share forward)\n")
+    if a.command:
+        print("Commands (run from /tmp with TMPDIR=/tmp, repository at $R):\n\n```\n%s\n```\n" % a.command)
+    print("FETCH_SIZE and WRITE_SIZE are scaled by what they read on a plain 1 GiB device copy: "
+          "read x %.3f, write x %.3f.  Durations are the kernel-trace averages of the same workload; "
+          "MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs.\n" % (fr, fw))
+    print("| kernel | avg us | HBM read MB | HBM write MB | HBM GB/s | MFMA busy % | bf16 MFMA TFLOP/s |")
+    print("|---|---|---|---|---|---|---|")
+    rec = {}
+    for key, label in KINDS:
+        if key not in c:
+            continue
+        v = c[key]
+        rd = v.get("FETCH_SIZE", float("nan")) * 1024.0 * fr
+        wr = v.get("WRITE_SIZE", float("nan")) * 1024.0 * fw
+        t = dur.get(key)
+        bw = (rd + wr) / t / 1e9 if t else float("nan")
+        busy = v.get("MfmaUtil", float("nan"))
+        fl = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512
+        tf = fl / t / 1e12 if t else float("nan")
+        print("| %s | %.1f | %.1f | %.1f | %.0f | %.1f | %.0f |" % (label, (t or 0) * 1e6, rd / 1e6, wr / 1e6, bw, busy, tf))
+        rec[key] = {"read_bytes": rd, "write_bytes": wr, "avg_s": t, "mfma_busy_pct": busy, "mfma_bf16_flops": fl}
+    l1 = rec.get("l1_kernel")
+    if l1:
+        out = {"kernel_source_sha256_16": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16],
+               "hbm_bytes_per_launch": l1["read_bytes"] + l1["write_bytes"],
+               "hbm_read_bytes_per_launch": l1["read_bytes"], "hbm_write_bytes_per_launch": l1["write_bytes"],
+               "copy_scale_read": fr, "copy_scale_write": fw, "kernels": rec, "command": a.command}
+        with open(a.out_json, "w") as f:
+            json.dump(out, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()
