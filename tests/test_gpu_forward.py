@@ -50,7 +50,7 @@ def test_route_tables_bit_exact(cfg, bm):
 
 
 @pytest.mark.parametrize("case", ["empty", "none_local", "all_dropped", "k1", "dups", "shard",
-                                  "one_expert", "many_experts", "ragged_chunks"])
+                                  "one_expert", "many_experts", "ragged_chunks", "many_chunks"])
 def test_route_edge_cases(case):
     rng = np.random.default_rng(21)
     T, E, EL, e_lo, k = 300, 16, 4, 0, 3
@@ -64,6 +64,8 @@ def test_route_edge_cases(case):
         T, E, EL, k = 700, 2048, 1024, 8
     elif case == "ragged_chunks":
         T, E, EL, k = 5000, 64, 48, 7      # pair chunks of 2048 split tokens
+    elif case == "many_chunks":
+        T, E, EL, k = 40000, 256, 64, 8    # chunk histograms too large for one block's LDS
     idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
     if case == "none_local":
         idx = rng.integers(EL, E, size=(T, k)).astype(np.int32)

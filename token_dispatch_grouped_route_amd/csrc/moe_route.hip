@@ -2,19 +2,22 @@
 // Implementation Map: dispatch prologue (routing tables); block-M padding from the
 // "How Mega MoE Overlaps ..." page, Block-M Alignment).
 //
-// Three launches, all with fixed grids, none waiting on the host:
+// Two launches with fixed grids, none waiting on the host:
 //   1. count: each block histograms the experts of one chunk of kRouteChunk pairs (LDS
 //      counters) and counts the local pairs of a slice of tokens.
-//   2. scan (one block): per expert, an exclusive scan over chunks gives each chunk's base
-//      inside the expert; a block-wide scan of the padded counts gives the segment offsets;
-//      then the block -> expert map and the meta counters.
-//   3. place: each block re-reads its chunk in pair order, 256 pairs at a time.  Inside a
-//      wavefront, pairs with the same expert are grouped with ballots (the wave-level
-//      histogram), giving each pair its rank among earlier lanes; the per-wave counts are
-//      prefix-summed across the block's waves in LDS.  So a pair's row is
-//      offset[e] + (pairs of e in earlier chunks) + (in earlier sub-steps) + (in earlier
-//      waves) + (in earlier lanes): ascending pair order inside every segment, no atomics on
-//      the row positions, the same tables on every run.
+//   2. scan + place: every block stages all chunk histograms in LDS and derives what it needs
+//      itself: per expert the total, the padded segment offsets (a block-wide scan) and its own
+//      chunk's base inside each segment (the sum over earlier chunks).  Block 0 also writes the
+//      counts, offsets and meta counters, and the blocks share the block -> expert map and the
+//      -1 fill of rows no pair takes.  Then each block re-reads its chunk in pair order, 256
+//      pairs at a time.  Inside a wavefront, pairs with the same expert are grouped with ballots
+//      (the wave-level histogram), giving each pair its rank among earlier lanes; the per-wave
+//      counts are prefix-summed across the block's waves in LDS.  So a pair's row is
+//      offset[e] + (pairs of e in earlier chunks) + (in earlier sub-steps) + (in earlier waves)
+//      + (in earlier lanes): ascending pair order inside every segment, no atomics on the row
+//      positions, the same tables on every run.
+// Shapes whose histograms do not fit in LDS (chunks x local experts > kFusedHist) run the scan
+// as a one-block launch of its own between the two.
 #include "moe_internal.h"
 
 namespace moe {
@@ -186,12 +189,151 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_
     }
 }
 
+constexpr int kFusedHist = 8192;   // chunks x local experts staged in LDS by the fused launch
+
+// Scan + place in one launch (see the top of the file).  LDS: hist [nch * EL], tot, mine, off
+// [EL + 1], base, wcnt [kPlaceWaves * EL], scan [kRouteThreads].
+__global__ __launch_bounds__(kRouteThreads) void route_scan_place_kernel(const int32_t* __restrict__ idx,
+                                                                         Dims d, Ws ws) {
+    extern __shared__ int32_t sm[];
+    const int EL = d.EL, nch = ws.num_chunks;
+    int32_t* hist = sm;
+    int32_t* tot = hist + nch * EL;
+    int32_t* mine = tot + EL;
+    int32_t* off = mine + EL;   // [EL + 1]
+    int32_t* base = off + EL + 1;
+    int32_t* wcnt = base + EL;
+    int32_t* scan = wcnt + kPlaceWaves * EL;
+    __shared__ int32_t s_drop;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int i = tid; i < nch * EL; i += blockDim.x) hist[i] = ws.chunk_hist[i];
+    if (tid == 0) s_drop = 0;
+    __syncthreads();
+    for (int e = tid; e < EL; e += blockDim.x) {
+        int t = 0, m = 0;
+        for (int c = 0; c < nch; ++c) {
+            const int v = hist[c * EL + e];
+            m += c < static_cast<int>(blockIdx.x) ? v : 0;
+            t += v;
+        }
+        tot[e] = t;
+        mine[e] = m;
+    }
+    __syncthreads();
+    // offsets: exclusive scan of the padded counts, kRouteThreads experts per round
+    int carry = 0;
+    for (int e0 = 0; e0 < EL; e0 += kRouteThreads) {
+        const int e = e0 + tid;
+        const int v = e < EL ? (tot[e] + d.BM - 1) / d.BM * d.BM : 0;
+        scan[tid] = v;
+        __syncthreads();
+        for (int o = 1; o < kRouteThreads; o <<= 1) {
+            const int u = tid >= o ? scan[tid - o] : 0;
+            __syncthreads();
+            scan[tid] += u;
+            __syncthreads();
+        }
+        if (e < EL) off[e] = carry + scan[tid] - v;
+        carry += scan[kRouteThreads - 1];
+        __syncthreads();
+    }
+    if (tid == 0) off[EL] = carry;
+    if (blockIdx.x == 0) {
+        int dr = 0;
+        for (int c = tid; c < nch; c += blockDim.x) dr += ws.chunk_dropped[c];
+        if (dr) atomicAdd(&s_drop, dr);
+    }
+    __syncthreads();
+    const int R = off[EL];
+    if (blockIdx.x == 0) {
+        for (int e = tid; e < EL; e += blockDim.x) {
+            ws.counts[e] = tot[e];
+            ws.offsets[e] = off[e];
+        }
+        if (tid == 0) {
+            ws.offsets[EL] = R;
+            ws.meta[0] = R;
+            ws.meta[1] = s_drop;
+        }
+    }
+    // block -> expert map (the last expert whose segment starts at or before the block), and -1 in
+    // every row no pair takes: padding inside segments and rows past R; a slice per block
+    const int64_t gstride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid;
+    auto expert_at = [&](int64_t r) {   // largest e with off[e] <= r < R
+        int lo = 0, hi = EL - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    };
+    for (int64_t m = gtid; m < ws.num_blocks; m += gstride) {
+        const int64_t r0 = m * d.BM;
+        ws.tile_expert[m] = r0 < R ? expert_at(r0) : -1;
+    }
+    for (int64_t r = gtid; r < ws.rows_cap; r += gstride) {
+        if (r >= R) {
+            ws.row_pair[r] = -1;
+        } else {
+            const int e = expert_at(r);
+            if (r >= off[e] + tot[e]) ws.row_pair[r] = -1;
+        }
+    }
+
+    // placement
+    const int64_t npairs = static_cast<int64_t>(d.T) * d.k;
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kRouteChunk;
+    const int64_t p1 = min(npairs, p0 + kRouteChunk);
+    for (int e = tid; e < EL; e += blockDim.x) base[e] = off[e] + mine[e];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int64_t s0 = p0; s0 < p1; s0 += kRouteThreads) {
+        for (int e = lane; e < EL; e += 64) wcnt[wave * EL + e] = 0;
+        __syncthreads();
+        const int64_t p = s0 + tid;
+        const int e = (p < p1) ? local_slot(idx[p], d) : -1;
+        int rank = 0;
+        uint64_t todo = __ballot(e >= 0);
+        while (todo) {
+            const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+            const int le = __shfl(e, leader);
+            const uint64_t grp = __ballot(e == le);
+            if (e == le) rank = __popcll(grp & lt_mask);
+            if (lane == leader) wcnt[wave * EL + le] = __popcll(grp);
+            todo &= ~grp;
+        }
+        __syncthreads();
+        if (e >= 0) {
+            int row = base[e] + rank;
+            for (int w = 0; w < wave; ++w) row += wcnt[w * EL + e];
+            ws.row_pair[row] = static_cast<int32_t>(p);
+            ws.pair_row[p] = row;
+        } else if (p < p1) {
+            ws.pair_row[p] = -1;
+        }
+        __syncthreads();
+        for (int x = tid; x < EL; x += blockDim.x) {
+            int add = 0;
+            for (int w = 0; w < kPlaceWaves; ++w) add += wcnt[w * EL + x];
+            base[x] += add;
+        }
+        __syncthreads();
+    }
+}
+
 hipError_t launch_route(const Dims& d, const int32_t* topk_idx, const Ws& ws, hipStream_t s) {
     const int nch = ws.num_chunks;
     route_count_kernel<<<nch, kRouteThreads, sizeof(int32_t) * d.EL, s>>>(topk_idx, d, ws);
-    route_scan_kernel<<<1, kScanThreads, 0, s>>>(d, ws);
-    route_place_kernel<<<nch, kRouteThreads, sizeof(int32_t) * d.EL * (1 + kPlaceWaves), s>>>(
-        topk_idx, d, ws);
+    const size_t lds = sizeof(int32_t) * (static_cast<size_t>(nch) * d.EL + (4 + kPlaceWaves) * d.EL + 1 +
+                                          kRouteThreads);
+    if (static_cast<int64_t>(nch) * d.EL <= kFusedHist && lds <= 64 * 1024) {
+        route_scan_place_kernel<<<nch, kRouteThreads, lds, s>>>(topk_idx, d, ws);
+    } else {
+        route_scan_kernel<<<1, kScanThreads, 0, s>>>(d, ws);
+        route_place_kernel<<<nch, kRouteThreads, sizeof(int32_t) * d.EL * (1 + kPlaceWaves), s>>>(
+            topk_idx, d, ws);
+    }
     return hipGetLastError();
 }
 
