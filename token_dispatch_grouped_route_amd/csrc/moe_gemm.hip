@@ -5,7 +5,9 @@
 // wave a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.  K advances 64 elements per step.  Both
 // operand tiles live in LDS K-contiguous (128 bytes per row, 16-byte chunks XOR-swizzled by
 // row so a wave's fragment reads spread over the banks), double-buffered so the global loads
-// of step k+1 are in flight while the MFMAs of step k run; one barrier per step.
+// of step k+1 are in flight while the MFMAs of step k run; one barrier per step.  The weight
+// gradients, whose K is one expert's rows (often a single step), use one LDS buffer instead, for
+// more resident workgroups per CU.
 //
 // Loaders differ per operand:
 //   KRows  rows that are K-contiguous in memory (token rows, activations); 16-byte vector
@@ -20,7 +22,8 @@
 //   dgrad   L2 dgrad NN, row weight and optional SwiGLU transpose in the epilogue
 //   wgrad2  dW2 = dO^T A, K = rows of the expert (variable K), TN
 //   wgrad1  dW1 = dHgu^T X with X re-gathered from x, TN
-// Weight gradients are written in the packed layout of the weights they belong to.
+// Weight gradients are written in the packed layout of the weights they belong to, whole 1 KB
+// blocks per store instruction (the tile's M index runs along the packed reduction index).
 //
 // The dgrad launch is persistent: a fixed grid (CUs x occupancy) walks the tile list whose
 // length R / BM * n_tiles is read from the workspace on the device, so the host never needs R.
@@ -45,7 +48,9 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 template <int BM_, int BN_, int WM_, int WN_, int PF_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int PF = PF_;   // K steps of global loads in flight ahead of the MFMAs (1 or 2)
+    // K steps of global loads in flight ahead of the MFMAs (1 or 2; 0: one step, one LDS buffer,
+    // for launches of many short-K tiles where occupancy matters more than overlap)
+    static constexpr int PF = PF_;
     // workgroups per CU the register allocation must allow (the LDS of two fits in 160 KB)
     static constexpr int MIN_WG = (BM * BN <= 128 * 128) ? 2 : 1;
     static constexpr int NT = 64 * WM * WN;
@@ -53,12 +58,7 @@ struct Cfg {
     static constexpr int MI = TM / 32, NI = TN / 32;
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int OPERAND_BYTES = 2 * STAGE_BYTES;
-    // fp32 C tile for the epilogue, row stride BN + 8 floats: the two half-waves of an
-    // accumulator write (rows 4 apart) then start 32 banks apart
-    static constexpr int C_STRIDE = BN + 8;
-    static constexpr int C_BYTES = BM * C_STRIDE * 4;
-    static constexpr int LDS_BYTES = OPERAND_BYTES > C_BYTES ? OPERAND_BYTES : C_BYTES;
+    static constexpr int LDS_BYTES = (PF == 0 ? 1 : 2) * STAGE_BYTES;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
     static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "K-row chunks must split evenly");
 };
@@ -232,7 +232,22 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f3
     la.template store<0>(smem, tid);
     lb.template store<0>(smem + C::A_BYTES, tid);
     lds_barrier();
-    if constexpr (C::PF == 2) {
+    if constexpr (C::PF == 0) {
+        for (int kt = 0; kt < nk; ++kt) {
+            const bool more = kt + 1 < nk;
+            if (more) {
+                la.template load<0>(kt + 1, tid);
+                lb.template load<0>(kt + 1, tid);
+            }
+            mma_step<C>(smem, smem + C::A_BYTES, acc, wm0, wn0, lane);
+            if (more) {
+                lds_barrier();   // every wave's fragment reads of step kt are done
+                la.template store<0>(smem, tid);
+                lb.template store<0>(smem + C::A_BYTES, tid);
+                lds_barrier();
+            }
+        }
+    } else if constexpr (C::PF == 2) {
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
             pipe_step<C, 0>(la, lb, kt, nk, smem, acc, tid, wm0, wn0, lane);
@@ -262,33 +277,6 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f3
 // Row (within the tile) and column (within the wave's N range) of accumulator element r of
 // the 32x32 block: 4 groups of 8 rows, the lane's half picks 4 of them, lane%32 is the column.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// Accumulators to the fp32 C tile in LDS; col_of(ni) gives the tile column of block ni's lane 0.
-// The caller has passed a barrier after the last MFMA reads of the operand buffers.
-template <class C, class ColOf>
-__device__ __forceinline__ void acc_to_lds(float* ct, const f32x16_t (&acc)[C::MI][C::NI], int wm0, int lane,
-                                           ColOf col_of) {
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-            const int col = col_of(ni) + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ct[(wm0 + mi * 32 + acc_row(r, lane)) * C::C_STRIDE + col] = acc[mi][ni][r];
-        }
-}
-
-__device__ __forceinline__ void ld8(const float* p, float (&f)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-__device__ __forceinline__ u32x4 bf16x8_of(const float (&f)[8]) {
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
-    return r;
-}
 
 // ---------------------------------------------------------------------------------------------
 // Tile schedule of the row-tiled launches
@@ -447,8 +435,37 @@ struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
-// dW2[e] (packed like W2: column h, reduction index i) = sum_k (w dy)[k][h] * act[k][i]:
-// M = H, N = I.
+// A wave's 32x32 accumulator block as whole 1 KB blocks of a fragment-packed weight gradient
+// (moe_pack_weights layout, reduction length K): the tile's M index is the packed reduction index
+// k (a 32-row block spans two 16-deep K steps) and its N index the packed column n (a 32-column
+// block is one packed column group).  Lane L holds column n0 + L%32 and k = k0 + 8*(r/4) +
+// 4*(L/32) + r%4 for r = 0..15, while a packed block wants lane L to hold the 8 consecutive k from
+// 8*(L/32) of each 16-deep step; so lanes L and L^32 trade four values per step, and every lane
+// then stores 16 bytes: one store instruction writes a whole 1 KB block.
+__device__ __forceinline__ void store_grad_block(uint16_t* out, int64_t K, int64_t n0, int64_t k0,
+                                                 const f32x16_t& acc, int lane) {
+    const bool lo = lane < 32;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = acc[8 * st + q], b = acc[8 * st + 4 + q];
+            const float got = __shfl_xor(lo ? b : a, 32);
+            v[q] = lo ? a : got;
+            v[4 + q] = lo ? got : b;
+        }
+        u32x4 pk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            pk[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
+        const int64_t blk = (n0 >> 5) * (K >> 4) + ((k0 >> 4) + st);
+        *reinterpret_cast<u32x4*>(out + (blk * 64 + lane) * 8) = pk;
+    }
+}
+
+// dW2[e] (packed like W2: column h, reduction index i) = sum_k act[k][i] * (w dy)[k][h]:
+// M = I (the packed reduction index), N = H (the packed column).
 template <class C>
 __global__ __launch_bounds__(C::NT) void wgrad2_kernel(const uint16_t* __restrict__ dy,
                                                        const float* __restrict__ topk_w, Dims d, Ws ws,
@@ -457,56 +474,7 @@ __global__ __launch_bounds__(C::NT) void wgrad2_kernel(const uint16_t* __restric
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
     const int H = d.H, I = d.I;
-    const int n_tiles = I / C::BN, m_tiles = H / C::BM;
-    const int e = blockIdx.x / (m_tiles * n_tiles);
-    const int rem = blockIdx.x - e * (m_tiles * n_tiles);
-    const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
-    const int64_t seg0 = ws.offsets[e];
-    int count = ws.counts[e];   // K of this expert; kept inside the row tables
-    if (seg0 < 0 || seg0 > ws.rows_cap || count < 0) count = 0;
-    if (count > ws.rows_cap - seg0) count = static_cast<int>(ws.rows_cap - seg0);
-
-    TRows<C::BM, C::NT, WeightedGatherSrc> la;
-    la.src.base = dy;
-    la.src.row_pair = ws.row_pair;
-    la.src.seg0 = seg0;
-    la.src.count = count;
-    la.src.k = d.k;
-    la.src.H = H;
-    la.src.npairs = d.T * d.k;
-    la.src.topk_w = topk_w;
-    la.m_base = mt * C::BM;
-    TRows<C::BN, C::NT, DirectRowSrc> lb;
-    lb.src.base = ws.act;
-    lb.src.seg0 = seg0;
-    lb.src.count = count;
-    lb.src.width = I;
-    lb.m_base = nt * C::BN;
-    f32x16_t acc[C::MI][C::NI];
-    gemm_tile<C>(la, lb, (count + BK - 1) / BK, smem, acc, tid, wm0, wn0, lane);
-
-    uint16_t* out = dw2p + static_cast<int64_t>(e) * H * I;
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t h = mt * C::BM + wm0 + mi * 32 + acc_row(r, lane);
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-                out[frag_index(h, nt * C::BN + wn0 + ni * 32 + (lane & 31), I)] = f32_to_bf16(acc[mi][ni][r]);
-        }
-}
-
-// dW1[e] (packed like W1: L1 column n, reduction index h) = sum_k dhgu[k][n] * x[t_k][h]:
-// M = 2I, N = H.
-template <class C>
-__global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
-                                                       uint16_t* __restrict__ dw1p) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
-    const int H = d.H, N2 = 2 * d.I;
-    const int n_tiles = H / C::BN, m_tiles = N2 / C::BM;
+    const int m_tiles = I / C::BM, n_tiles = H / C::BN;
     const int e = blockIdx.x / (m_tiles * n_tiles);
     const int rem = blockIdx.x - e * (m_tiles * n_tiles);
     const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
@@ -516,19 +484,65 @@ __global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restric
     if (count > ws.rows_cap - seg0) count = static_cast<int>(ws.rows_cap - seg0);
 
     TRows<C::BM, C::NT, DirectRowSrc> la;
-    la.src.base = ws.dhgu;
+    la.src.base = ws.act;
     la.src.seg0 = seg0;
     la.src.count = count;
-    la.src.width = N2;
+    la.src.width = I;
     la.m_base = mt * C::BM;
-    TRows<C::BN, C::NT, GatherTokenSrc> lb;
-    lb.src.base = x;
+    TRows<C::BN, C::NT, WeightedGatherSrc> lb;
+    lb.src.base = dy;
     lb.src.row_pair = ws.row_pair;
     lb.src.seg0 = seg0;
     lb.src.count = count;
     lb.src.k = d.k;
     lb.src.H = H;
     lb.src.npairs = d.T * d.k;
+    lb.src.topk_w = topk_w;
+    lb.m_base = nt * C::BN;
+    f32x16_t acc[C::MI][C::NI];
+    gemm_tile<C>(la, lb, (count + BK - 1) / BK, smem, acc, tid, wm0, wn0, lane);
+
+    uint16_t* out = dw2p + static_cast<int64_t>(e) * H * I;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+            store_grad_block(out, I, nt * C::BN + wn0 + ni * 32, mt * C::BM + wm0 + mi * 32, acc[mi][ni], lane);
+}
+
+// dW1[e] (packed like W1: L1 column n, reduction index h) = sum_k x[t_k][h] * dhgu[k][n]:
+// M = H (the packed reduction index), N = 2I (logical L1 columns; 32-column groups map to packed
+// column groups whole).
+template <class C>
+__global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
+                                                       uint16_t* __restrict__ dw1p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
+    const int H = d.H, N2 = 2 * d.I;
+    const int m_tiles = H / C::BM, n_tiles = N2 / C::BN;
+    const int e = blockIdx.x / (m_tiles * n_tiles);
+    const int rem = blockIdx.x - e * (m_tiles * n_tiles);
+    const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
+    const int64_t seg0 = ws.offsets[e];
+    int count = ws.counts[e];   // K of this expert; kept inside the row tables
+    if (seg0 < 0 || seg0 > ws.rows_cap || count < 0) count = 0;
+    if (count > ws.rows_cap - seg0) count = static_cast<int>(ws.rows_cap - seg0);
+
+    TRows<C::BM, C::NT, GatherTokenSrc> la;
+    la.src.base = x;
+    la.src.row_pair = ws.row_pair;
+    la.src.seg0 = seg0;
+    la.src.count = count;
+    la.src.k = d.k;
+    la.src.H = H;
+    la.src.npairs = d.T * d.k;
+    la.m_base = mt * C::BM;
+    TRows<C::BN, C::NT, DirectRowSrc> lb;
+    lb.src.base = ws.dhgu;
+    lb.src.seg0 = seg0;
+    lb.src.count = count;
+    lb.src.width = N2;
     lb.m_base = nt * C::BN;
     f32x16_t acc[C::MI][C::NI];
     gemm_tile<C>(la, lb, (count + BK - 1) / BK, smem, acc, tid, wm0, wn0, lane);
@@ -537,13 +551,9 @@ __global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restric
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t n = mt * C::BM + wm0 + mi * 32 + acc_row(r, lane);
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-                out[frag_index(l1_packed_col(n, d.I), nt * C::BN + wn0 + ni * 32 + (lane & 31), H)] =
-                    f32_to_bf16(acc[mi][ni][r]);
-        }
+        for (int ni = 0; ni < C::NI; ++ni)
+            store_grad_block(out, H, l1_packed_col(nt * C::BN + wn0 + ni * 32, d.I), mt * C::BM + wm0 + mi * 32,
+                             acc[mi][ni], lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -587,7 +597,7 @@ using G32 = Cfg<32, 128, 1, 2>;
 using G64 = Cfg<64, 128, 2, 2>;
 using G128 = Cfg<128, 128, 2, 2>;
 using G256 = Cfg<256, 128, 4, 1>;
-using WG = Cfg<128, 128, 2, 2>;   // weight-gradient tiles
+using WG = Cfg<128, 128, 2, 2, 0>;   // weight-gradient tiles: K is an expert's rows, often one step
 
 template <class C0>
 static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
@@ -615,14 +625,14 @@ hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w, 
 
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
                          uint16_t* dw2p, hipStream_t s) {
-    const int blocks = d.EL * (d.H / WG::BM) * (d.I / WG::BN);
+    const int blocks = d.EL * (d.I / WG::BM) * (d.H / WG::BN);
     if (blocks <= 0) return hipSuccess;
     wgrad2_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES, s>>>(dy, topk_w, d, ws, dw2p);
     return hipGetLastError();
 }
 
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
-    const int blocks = d.EL * (2 * d.I / WG::BM) * (d.H / WG::BN);
+    const int blocks = d.EL * (d.H / WG::BM) * (2 * d.I / WG::BN);
     if (blocks <= 0) return hipSuccess;
     wgrad1_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES, s>>>(x, d, ws, dw1p);
     return hipGetLastError();
