@@ -13,6 +13,11 @@ excluded) / step time.  Prints one JSON line.
 Flags: --gpus N (only 1 is supported: the path is one GPU's share), --steps K, --warmup W,
 --workload NAME, --block-m BM, --no-cpu-baseline, --copy-calibration (also times a plain 1 GiB
 device copy, for reading HBM counters against a kernel of known traffic).
+
+--backward measures the training step of the wide-expert share instead (T 4096, H 7168, I 3072,
+384 experts, 48 local, top-6): forward with the activations saved, L2 dgrad with the SwiGLU
+transpose, dW2 and dW1; one JSON line with per-stage times and each backward kernel against the
+HBM roofline (its algorithmic bytes per launch / its time).  The default run is the forward.
 """
 import argparse
 import hashlib
@@ -84,6 +89,84 @@ def cpu_baseline(w, d, budget_s=15.0):
             "sample": "%d of %d tokens (%d local pairs), fp64 per-token loop, %.1f s" % (len(sample), w.T, pairs, dt)}
 
 
+def bench_backward(a):
+    """Training step of the wide-expert share: forward (activations saved) + backward stages."""
+    w = mw.get("wide_share_fwd_bwd" if a.workload == "dsv3_share_fwd" else a.workload)
+    log("generating %s inputs (seed 0)" % w.name)
+    d = mw.inputs(w, 0)
+    P = mw.local_pairs(w, d["topk_idx"])
+    bm = a.block_m or moe.preferred_block_m(moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=64))
+    shape = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=bm, e_lo=w.e_lo, train=True)
+    x, dy = bf16_dev(d["x"]), bf16_dev(d["dy"])
+    y = torch.empty(w.T, w.H, dtype=torch.bfloat16, device="cuda")
+    idx = torch.from_numpy(d["topk_idx"]).cuda()
+    wts = torch.from_numpy(d["topk_weights"]).cuda()
+    W1p, W2p = moe.alloc_packed(shape)
+    W1, W2 = bf16_dev(d["W1"]), bf16_dev(d["W2"])
+    moe.pack_weights(shape, W1, W2, W1p, W2p)
+    del W1, W2
+    ws = moe.alloc_workspace(shape)
+    dW1p, dW2p = torch.empty_like(W1p), torch.empty_like(W2p)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    stages = (("forward_train", lambda: moe.forward(shape, x, idx, wts, W1p, W2p, ws, y)),
+              ("dgrad_swiglu_bwd", lambda: moe.bwd_gemm2_dgrad(shape, dy, wts, W2p, ws, fuse_swiglu_bwd=True)),
+              ("wgrad2", lambda: moe.wgrad2(shape, dy, wts, ws, dW2p)),
+              ("wgrad1", lambda: moe.wgrad1(shape, x, ws, dW1p)))
+    log("warmup %d" % a.warmup)
+    for _ in range(a.warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    log("timing %d training steps" % a.steps)
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        ev[i][0].record(s)
+        for j, (_, fn) in enumerate(stages):
+            fn()
+            ev[i][j + 1].record(s)
+    torch.cuda.synchronize()
+    st = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(stages))] for i in range(a.steps)])
+    st_ms = st.mean(axis=0)
+    ms = st.sum(axis=1).mean()
+
+    idx_np = d["topk_idx"]
+    local = (idx_np >= w.e_lo) & (idx_np < w.e_lo + w.EL)
+    nonempty = len(np.unique(idx_np[local]))
+    tok_local = int(local.any(axis=1).sum())
+    H, I, EL = w.H, w.I, w.EL
+    # algorithmic HBM bytes and FLOPs per launch of each backward kernel (real rows only)
+    alg = {
+        "dgrad_swiglu_bwd": (nonempty * H * I * 2 + tok_local * H * 2 + P * 2 * I * 2 * 2, 2.0 * P * H * I),
+        "wgrad2": (EL * H * I * 2 + P * I * 2 + tok_local * H * 2, 2.0 * P * H * I),
+        "wgrad1": (EL * 2 * I * H * 2 + P * 2 * I * 2 + tok_local * H * 2, 2.0 * P * H * 2 * I),
+    }
+    roof = {}
+    for j, (name, _) in enumerate(stages):
+        if name not in alg:
+            continue
+        b, f = alg[name]
+        t = st_ms[j] / 1e3
+        roof[name] = {"bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": b / t / 1e9 / PEAK_HBM_GBS, "traffic": None, "alg_bytes_per_launch": b,
+                      "alg_flops_per_launch": f, "mfma_frac": f / t / 1e12 / PEAK_BF16_TFLOPS}
+    flops = w.flops_fwd(P) + sum(v[1] for v in alg.values())
+    value = flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": "MoE layer training step (fwd + L2 dgrad + SwiGLU bwd + dW2 + dW1) TFLOP/s on 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) logits, x, dy, scaled weights)",
+        "config": {"workload": w.name, "T": w.T, "H": H, "I": I, "E": w.E, "EL": EL, "k": w.k,
+                   "block_m": bm, "local_pairs": P, "parallelism": "none (1 GPU share)"},
+        "stages_ms": {name: round(st_ms[j], 4) for j, (name, _) in enumerate(stages)},
+        "roofline": roof,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +176,7 @@ def main():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--backward", action="store_true")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the experts; runs on more than one GPU are not "
@@ -100,6 +184,8 @@ def main():
         sys.exit(2)
 
     torch.cuda.set_device(0)
+    if a.backward:
+        return bench_backward(a)
     w = mw.get(a.workload)
     log("generating %s inputs (seed 0)" % w.name)
     d = mw.inputs(w, 0)
