@@ -464,96 +464,159 @@ __device__ __forceinline__ void store_grad_block(uint16_t* out, int64_t K, int64
     }
 }
 
+constexpr int kWgradChunk = 8;   // output tiles per weight-gradient workgroup
+
+// A run of output tiles of one expert's weight gradient that share one operand tile: with
+// STREAM_A the M tiles [t0, t1) of N tile `fixed` (the N operand lb is shared), else the N tiles
+// [t0, t1) of M tile `fixed` (la is shared); the streamed operand is the cheaper one to load.  When
+// the expert has at most one K step of rows (the common case: K is the expert's row count), the
+// shared tile is loaded into LDS once and the streamed one's loads for tile t + 1 go out before
+// the MFMAs and stores of tile t, so the launch streams its output.  With more rows every tile
+// runs the full K loop.  n_col(nt, ni) gives the packed column of block ni of the wave in N tile nt;
+// K_out is the packed reduction length.
+template <class C, bool STREAM_A, class LA, class LB, class NCol>
+__device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed, int t0, int t1, uint16_t* out,
+                                            int64_t K_out, NCol n_col, char* smem, int tid, int wm0, int wn0,
+                                            int lane) {
+    const int nk = (count + BK - 1) / BK;
+    f32x16_t acc[C::MI][C::NI];
+    auto store = [&](int t) {
+        const int mt = STREAM_A ? t : fixed, nt = STREAM_A ? fixed : t;
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                store_grad_block(out, K_out, n_col(nt, ni), mt * C::BM + wm0 + mi * 32, acc[mi][ni], lane);
+    };
+    auto aim = [&](int t) {   // point the streamed operand at tile t
+        if constexpr (STREAM_A) la.m_base = t * C::BM;
+        else lb.m_base = t * C::BN;
+    };
+    if constexpr (STREAM_A) lb.m_base = fixed * C::BN;
+    else la.m_base = fixed * C::BM;
+    if (nk <= 1) {
+        char* lA = smem;
+        char* lB = smem + C::A_BYTES;
+        aim(t0);
+        la.template load<0>(0, tid);
+        lb.template load<0>(0, tid);
+        la.template store<0>(lA, tid);
+        lb.template store<0>(lB, tid);
+        lds_barrier();
+        for (int t = t0; t < t1; ++t) {
+            const bool more = t + 1 < t1;
+            if (more) {
+                aim(t + 1);
+                if constexpr (STREAM_A) la.template load<0>(0, tid);
+                else lb.template load<0>(0, tid);
+            }
+#pragma unroll
+            for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            if (nk == 1) mma_step<C>(lA, lB, acc, wm0, wn0, lane);
+            store(t);
+            if (more) {
+                lds_barrier();   // every wave's fragment reads of tile t are done
+                if constexpr (STREAM_A) la.template store<0>(lA, tid);
+                else lb.template store<0>(lB, tid);
+                lds_barrier();
+            }
+        }
+    } else {
+        for (int t = t0; t < t1; ++t) {
+            aim(t);
+            gemm_tile<C>(la, lb, nk, smem, acc, tid, wm0, wn0, lane);
+            store(t);
+            lds_barrier();   // the next tile's first LDS stores follow every wave's last reads
+        }
+    }
+}
+
+// Workgroup b of a weight-gradient launch: expert, the fixed tile index and its chunk [t0, t1) of
+// streamed tiles; the row count of the expert, kept inside the row tables.
+struct WgradWork {
+    int e, fixed, t0, t1, count;
+    int64_t seg0;
+    __device__ WgradWork(const Ws& ws, int n_fixed, int n_stream) {
+        const int chunks = (n_stream + kWgradChunk - 1) / kWgradChunk;
+        e = blockIdx.x / (n_fixed * chunks);
+        const int rem = blockIdx.x - e * (n_fixed * chunks);
+        fixed = rem / chunks;
+        t0 = (rem - fixed * chunks) * kWgradChunk;
+        t1 = min(n_stream, t0 + kWgradChunk);
+        seg0 = ws.offsets[e];
+        count = ws.counts[e];
+        if (seg0 < 0 || seg0 > ws.rows_cap || count < 0) count = 0;
+        if (count > ws.rows_cap - seg0) count = static_cast<int>(ws.rows_cap - seg0);
+    }
+};
+
 // dW2[e] (packed like W2: column h, reduction index i) = sum_k act[k][i] * (w dy)[k][h]:
-// M = I (the packed reduction index), N = H (the packed column).
+// M = I (the packed reduction index), N = H (the packed column).  The weighted dy gather is the
+// shared operand; act tiles stream.
 template <class C>
-__global__ __launch_bounds__(C::NT) void wgrad2_kernel(const uint16_t* __restrict__ dy,
-                                                       const float* __restrict__ topk_w, Dims d, Ws ws,
-                                                       uint16_t* __restrict__ dw2p) {
+__global__ __launch_bounds__(C::NT, 2) void wgrad2_kernel(const uint16_t* __restrict__ dy,
+                                                          const float* __restrict__ topk_w, Dims d, Ws ws,
+                                                          uint16_t* __restrict__ dw2p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
     const int H = d.H, I = d.I;
-    const int m_tiles = I / C::BM, n_tiles = H / C::BN;
-    const int e = blockIdx.x / (m_tiles * n_tiles);
-    const int rem = blockIdx.x - e * (m_tiles * n_tiles);
-    const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
-    const int64_t seg0 = ws.offsets[e];
-    int count = ws.counts[e];   // K of this expert; kept inside the row tables
-    if (seg0 < 0 || seg0 > ws.rows_cap || count < 0) count = 0;
-    if (count > ws.rows_cap - seg0) count = static_cast<int>(ws.rows_cap - seg0);
+    const WgradWork wk(ws, H / C::BN, I / C::BM);
 
     TRows<C::BM, C::NT, DirectRowSrc> la;
     la.src.base = ws.act;
-    la.src.seg0 = seg0;
-    la.src.count = count;
+    la.src.seg0 = wk.seg0;
+    la.src.count = wk.count;
     la.src.width = I;
-    la.m_base = mt * C::BM;
     TRows<C::BN, C::NT, WeightedGatherSrc> lb;
     lb.src.base = dy;
     lb.src.row_pair = ws.row_pair;
-    lb.src.seg0 = seg0;
-    lb.src.count = count;
+    lb.src.seg0 = wk.seg0;
+    lb.src.count = wk.count;
     lb.src.k = d.k;
     lb.src.H = H;
     lb.src.npairs = d.T * d.k;
     lb.src.topk_w = topk_w;
-    lb.m_base = nt * C::BN;
-    f32x16_t acc[C::MI][C::NI];
-    gemm_tile<C>(la, lb, (count + BK - 1) / BK, smem, acc, tid, wm0, wn0, lane);
-
-    uint16_t* out = dw2p + static_cast<int64_t>(e) * H * I;
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
-            store_grad_block(out, I, nt * C::BN + wn0 + ni * 32, mt * C::BM + wm0 + mi * 32, acc[mi][ni], lane);
+    uint16_t* out = dw2p + static_cast<int64_t>(wk.e) * H * I;
+    wgrad_tiles<C, true>(la, lb, wk.count, wk.fixed, wk.t0, wk.t1, out, I,
+                         [&](int nt, int ni) { return static_cast<int64_t>(nt * C::BN + wn0 + ni * 32); }, smem,
+                         tid, wm0, wn0, lane);
 }
 
 // dW1[e] (packed like W1: L1 column n, reduction index h) = sum_k x[t_k][h] * dhgu[k][n]:
 // M = H (the packed reduction index), N = 2I (logical L1 columns; 32-column groups map to packed
-// column groups whole).
+// column groups whole).  The x gather is the shared operand; dhgu tiles stream.
 template <class C>
-__global__ __launch_bounds__(C::NT) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
-                                                       uint16_t* __restrict__ dw1p) {
+__global__ __launch_bounds__(C::NT, 2) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
+                                                          uint16_t* __restrict__ dw1p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
     const int H = d.H, N2 = 2 * d.I;
-    const int m_tiles = H / C::BM, n_tiles = N2 / C::BN;
-    const int e = blockIdx.x / (m_tiles * n_tiles);
-    const int rem = blockIdx.x - e * (m_tiles * n_tiles);
-    const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
-    const int64_t seg0 = ws.offsets[e];
-    int count = ws.counts[e];   // K of this expert; kept inside the row tables
-    if (seg0 < 0 || seg0 > ws.rows_cap || count < 0) count = 0;
-    if (count > ws.rows_cap - seg0) count = static_cast<int>(ws.rows_cap - seg0);
+    const WgradWork wk(ws, H / C::BM, N2 / C::BN);
 
     TRows<C::BM, C::NT, GatherTokenSrc> la;
     la.src.base = x;
     la.src.row_pair = ws.row_pair;
-    la.src.seg0 = seg0;
-    la.src.count = count;
+    la.src.seg0 = wk.seg0;
+    la.src.count = wk.count;
     la.src.k = d.k;
     la.src.H = H;
     la.src.npairs = d.T * d.k;
-    la.m_base = mt * C::BM;
     TRows<C::BN, C::NT, DirectRowSrc> lb;
     lb.src.base = ws.dhgu;
-    lb.src.seg0 = seg0;
-    lb.src.count = count;
+    lb.src.seg0 = wk.seg0;
+    lb.src.count = wk.count;
     lb.src.width = N2;
-    lb.m_base = nt * C::BN;
-    f32x16_t acc[C::MI][C::NI];
-    gemm_tile<C>(la, lb, (count + BK - 1) / BK, smem, acc, tid, wm0, wn0, lane);
-
-    uint16_t* out = dw1p + static_cast<int64_t>(e) * N2 * H;
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
-            store_grad_block(out, H, l1_packed_col(nt * C::BN + wn0 + ni * 32, d.I), mt * C::BM + wm0 + mi * 32,
-                             acc[mi][ni], lane);
+    uint16_t* out = dw1p + static_cast<int64_t>(wk.e) * N2 * H;
+    const int I = d.I;
+    wgrad_tiles<C, false>(la, lb, wk.count, wk.fixed, wk.t0, wk.t1, out, H,
+                          [&](int nt, int ni) { return l1_packed_col(nt * C::BN + wn0 + ni * 32, I); }, smem, tid,
+                          wm0, wn0, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -625,14 +688,14 @@ hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w, 
 
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
                          uint16_t* dw2p, hipStream_t s) {
-    const int blocks = d.EL * (d.I / WG::BM) * (d.H / WG::BN);
+    const int blocks = d.EL * (d.H / WG::BN) * ((d.I / WG::BM + kWgradChunk - 1) / kWgradChunk);
     if (blocks <= 0) return hipSuccess;
     wgrad2_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES, s>>>(dy, topk_w, d, ws, dw2p);
     return hipGetLastError();
 }
 
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
-    const int blocks = d.EL * (d.H / WG::BM) * (2 * d.I / WG::BN);
+    const int blocks = d.EL * (d.H / WG::BM) * ((2 * d.I / WG::BN + kWgradChunk - 1) / kWgradChunk);
     if (blocks <= 0) return hipSuccess;
     wgrad1_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES, s>>>(x, d, ws, dw1p);
     return hipGetLastError();
