@@ -51,8 +51,10 @@ def configure(lib):
     lib.oracle_swiglu_bwd.argtypes = [i64, i32, P, P, P]
     lib.oracle_backward_rows.argtypes = [i32] * 7 + [P] * 6 + [P, i32, P, P]
     lib.oracle_backward.argtypes = [i32] * 7 + [P] * 6 + [P, i32, P, P]
+    lib.oracle_backward_tokens.argtypes = [i32] * 7 + [P] * 6 + [P, i32, P, P]
     for f in ("oracle_route", "oracle_forward", "oracle_l1_rows", "oracle_swiglu",
-              "oracle_swiglu_bwd", "oracle_backward_rows", "oracle_backward"):
+              "oracle_swiglu_bwd", "oracle_backward_rows", "oracle_backward",
+              "oracle_backward_tokens"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -188,3 +190,20 @@ def backward(x, topk_idx, topk_w, W1, W2, dy, E: int, e_lo: int = 0, experts=Non
     if rc != 0:
         raise MemoryError("oracle_backward failed: %d" % rc)
     return dW1, dW2
+
+
+def backward_tokens(x, topk_idx, topk_w, W1, W2, dy, E: int, e_lo: int = 0, tokens=None):
+    """Token-side gradients for the given tokens (default: all): dx [n, H] (the L1 dgrad rows
+    summed back to token order) and dtopk_w [n, k] (<dy[t], o_p> for each local pair, else 0),
+    fp64."""
+    x, idx, w = _c(x, np.uint16), _c(topk_idx, np.int32), _c(topk_w, np.float32)
+    W1, W2, dy = _c(W1, np.uint16), _c(W2, np.uint16), _c(dy, np.uint16)
+    T, H, I, EL, k = _shape(x, W1, W2, idx)
+    tok = _c(np.arange(T) if tokens is None else tokens, np.int32)
+    dx = np.zeros((len(tok), H), np.float64)
+    dw = np.zeros((len(tok), k), np.float64)
+    rc = _load().oracle_backward_tokens(T, H, I, E, e_lo, EL, k, _p(x), _p(idx), _p(w), _p(W1),
+                                        _p(W2), _p(dy), _p(tok), len(tok), _p(dx), _p(dw))
+    if rc != 0:
+        raise MemoryError("oracle_backward_tokens failed: %d" % rc)
+    return dx, dw

@@ -367,3 +367,81 @@ int oracle_backward(int T, int H, int I, int E, int e_lo, int EL, int k, const u
     }
     return err;
 }
+
+/*
+ * Token-side gradients of a list of tokens ("Mega MoE" page, Pipeline, backward: the
+ * conjugate of dispatch + L1 is an L1 dgrad whose rows are summed back to token order; the
+ * routing weights get the gradient of the weighted scatter-add).  For token t:
+ *   dx[t, q]      = sum over local pairs p = (t, j) of sum_n W1[e, q, n] * dHgu_p[n]
+ *   dtopk_w[t, j] = sum_m dy[t, m] * o_p[m]      for a local pair, where o_p is the L2 output
+ *                   row SwiGLU(x[t] @ W1[e]) @ W2[e] before weighting; 0 for a pair that is not
+ *                   local (this GPU's partial of the gradient, like y).
+ * dHgu_p is the per-pair gradient of pair_backward (w_p * dy[t] through L2 and SwiGLU).
+ * dx is [ntok, H] and dtopk_w [ntok, k], fp64.
+ */
+int oracle_backward_tokens(int T, int H, int I, int E, int e_lo, int EL, int k,
+                           const uint16_t* x, const int32_t* topk_idx, const float* topk_w,
+                           const uint16_t* W1, const uint16_t* W2, const uint16_t* dy,
+                           const int32_t* tokens, int ntok, double* dx, double* dtopk_w) {
+    if (H <= 0 || I <= 0 || k <= 0) return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        double* o = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dO = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dA = (double*)malloc(sizeof(double) * (size_t)I);
+        double* dhgu = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+        const int ok = h && a && o && dO && dA && dhgu;
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < ntok; ++i) {
+            if (!ok) continue;
+            {
+                const int t = tokens[i];
+                double* gx = dx + (size_t)i * H;
+                double* gw = dtopk_w + (size_t)i * k;
+                for (int q = 0; q < H; ++q) gx[q] = 0.0;
+                for (int j = 0; j < k; ++j) gw[j] = 0.0;
+                if (t < 0 || t >= T) continue;
+                const uint16_t* xrow = x + (size_t)t * H;
+                const uint16_t* dyrow = dy + (size_t)t * H;
+                for (int j = 0; j < k; ++j) {
+                    const int e = local_expert(topk_idx[(int64_t)t * k + j], E, e_lo, EL);
+                    if (e < 0) continue;
+                    const uint16_t* W1e = W1 + (size_t)e * H * 2 * I;
+                    const uint16_t* W2e = W2 + (size_t)e * I * H;
+                    l1_row(xrow, W1e, H, I, h);
+                    for (int c = 0; c < I; ++c) a[c] = silu(h[c]) * h[I + c];
+                    for (int m = 0; m < H; ++m) o[m] = 0.0;
+                    for (int c = 0; c < I; ++c) {
+                        const uint16_t* wrow = W2e + (size_t)c * H;
+                        for (int m = 0; m < H; ++m) o[m] += a[c] * bf16_value(wrow[m]);
+                    }
+                    double s = 0.0;
+                    for (int m = 0; m < H; ++m) s += bf16_value(dyrow[m]) * o[m];
+                    gw[j] = s;
+                    pair_backward(dyrow, (double)topk_w[(int64_t)t * k + j], W2e, H, I, h, dO,
+                                  dA, dhgu);
+                    for (int q = 0; q < H; ++q) {
+                        const uint16_t* wrow = W1e + (size_t)q * 2 * I;
+                        double d = 0.0;
+                        for (int n = 0; n < 2 * I; ++n) d += bf16_value(wrow[n]) * dhgu[n];
+                        gx[q] += d;
+                    }
+                }
+            }
+        }
+        free(h);
+        free(a);
+        free(o);
+        free(dO);
+        free(dA);
+        free(dhgu);
+    }
+    return err;
+}

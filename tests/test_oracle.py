@@ -357,12 +357,15 @@ def test_swiglu_fwd_bwd_match_torch_autograd():
 # ----------------------------------------------------------------------------------------
 # Backward (weight gradients and per-pair intermediates) against torch autograd
 # ----------------------------------------------------------------------------------------
-def autograd_backward(x, idx, wts, W1b, W2b, dyb, E, e_lo):
+def autograd_backward(x, idx, wts, W1b, W2b, dyb, E, e_lo, token_grads=None):
     X, dy = f64(x), f64(dyb)
     W1 = f64(W1b).requires_grad_(True)
     W2 = f64(W2b).requires_grad_(True)
     idx_t = torch.from_numpy(idx.astype(np.int64))
     wt = torch.from_numpy(wts.astype(np.float64))
+    if token_grads is not None:
+        X.requires_grad_(True)
+        wt.requires_grad_(True)
     EL, _, N = W1b.shape
     I = N // 2
     y = torch.zeros(X.shape, dtype=torch.float64)
@@ -379,6 +382,9 @@ def autograd_backward(x, idx, wts, W1b, W2b, dyb, E, e_lo):
             y = y + coef[:, None] * (a @ W2[e])
             per_slot[(j, e)] = (h, a)
     (y * dy).sum().backward()
+    if token_grads is not None:
+        token_grads["x"] = X.grad.numpy()
+        token_grads["w"] = wt.grad.numpy()
     return W1.grad.numpy(), W2.grad.numpy(), per_slot
 
 
@@ -411,6 +417,47 @@ def test_backward_matches_torch_autograd(shape):
             assert rel_err(dH[p], h.grad[t].numpy()) < 1e-12
 
 
+@pytest.mark.parametrize("shape", ["tiny", "wide_reduced", "shard"])
+def test_backward_tokens_match_torch_autograd(shape):
+    """dx and d(topk_weights) of the oracle against torch autograd of the layer in fp64: the
+    gradient of sum(y * dy) with respect to x and to the routing weights (pairs that are not
+    local get 0, since y is this GPU's partial sum)."""
+    if shape == "tiny":
+        w = mw.scaled(mw.get(0), backward=True)
+    elif shape == "wide_reduced":
+        w = mw.scaled(mw.get(4), T=64, H=256, I=128, E=48, EL=6)
+    else:
+        w = mw.scaled(mw.get(4), T=40, H=128, I=64, E=16, EL=4, e_lo=8)
+    d = mw.inputs(w, 0)
+    idx = d["topk_idx"].copy()
+    if shape != "tiny":
+        idx[3, 0] = w.E + 5           # dropped id
+        idx[5, 1] = idx[5, 0]         # duplicated expert in one token
+    args = (d["x"], idx, d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    dx, dw = oracle.backward_tokens(*args, E=w.E, e_lo=w.e_lo)
+    g = {}
+    autograd_backward(*args, w.E, w.e_lo, token_grads=g)
+    assert rel_err(dx, g["x"]) < 1e-12 and rel_err(dw, g["w"]) < 1e-12
+    local = (idx >= w.e_lo) & (idx < w.e_lo + w.EL)
+    assert np.all(dw[~local] == 0)
+    assert np.all(dx[~local.any(axis=1)] == 0)
+    sub = np.array([7, 2, 5])
+    dx2, dw2 = oracle.backward_tokens(*args, E=w.E, e_lo=w.e_lo, tokens=sub)
+    assert np.array_equal(dx2, dx[sub]) and np.array_equal(dw2, dw[sub])
+
+
+def test_backward_tokens_weight_gradient_is_forward_row_dot():
+    """With k = 1 and weight 1, d(topk_weights)[t] = <dy[t], y[t]>: the forward output row
+    is the unweighted L2 row of the token's only pair."""
+    w = mw.Workload("t", T=24, H=64, I=32, E=4, EL=4, k=1, backward=True)
+    d = mw.inputs(w, 3)
+    wts = np.ones((w.T, 1), np.float32)
+    args = (d["x"], d["topk_idx"], wts, d["W1"], d["W2"])
+    y = oracle.forward(*args, E=w.E)
+    _, dw = oracle.backward_tokens(*args, d["dy"], E=w.E)
+    assert rel_err(dw[:, 0], np.sum(f64(d["dy"]).numpy() * y, axis=1)) < 1e-12
+
+
 def test_backward_expert_without_rows_is_exact_zero():
     w = mw.Workload("t", T=16, H=32, I=16, E=4, EL=4, k=1, backward=True)
     d = mw.inputs(w, 2)
@@ -424,6 +471,10 @@ def test_backward_expert_without_rows_is_exact_zero():
 # ----------------------------------------------------------------------------------------
 def _backward_pin():
     test_backward_matches_torch_autograd("tiny")
+
+
+def _backward_tokens_pin():
+    test_backward_tokens_match_torch_autograd("wide_reduced")
 
 
 MUTATIONS = [
@@ -442,6 +493,12 @@ MUTATIONS = [
      "dhgu[c] = dA[c] * u * sg * (1.0 - g * (1.0 - sg));", _backward_pin),
     ("dW2 uses pre-activation", "row[m] += a[c] * dO[m];", "row[m] += h[c] * dO[m];",
      _backward_pin),
+    ("dx through the transposed W1 index", "for (int n = 0; n < 2 * I; ++n) d += bf16_value(wrow[n]) * dhgu[n];",
+     "for (int n = 0; n < 2 * I; ++n) d += bf16_value(W1e[(size_t)n * H + q]) * dhgu[n];",
+     _backward_tokens_pin),
+    ("dtopk_w from the weighted row", "for (int m = 0; m < H; ++m) s += bf16_value(dyrow[m]) * o[m];",
+     "for (int m = 0; m < H; ++m) s += bf16_value(dyrow[m]) * o[m] * topk_w[(int64_t)t * k + j];",
+     _backward_tokens_pin),
     ("slot weight index", "const double w = (double)topk_w[(int64_t)t * k + j];",
      "const double w = (double)topk_w[(int64_t)t * k];", pin_forward_masked_dense),
 ]
