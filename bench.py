@@ -16,8 +16,9 @@ device copy, for reading HBM counters against a kernel of known traffic).
 
 --backward measures the training step of the wide-expert share instead (T 4096, H 7168, I 3072,
 384 experts, 48 local, top-6): forward with the activations saved, L2 dgrad with the SwiGLU
-transpose, dW2 and dW1; one JSON line with per-stage times and each backward kernel against the
-HBM roofline (its algorithmic bytes per launch / its time).  The default run is the forward.
+transpose and the routing-weight gradient, dW2, dW1, and the L1 dgrad with its combine into dx;
+one JSON line with per-stage times and each backward kernel against the HBM roofline (its
+algorithmic bytes per launch / its time).  The default run is the forward.
 """
 import argparse
 import hashlib
@@ -107,12 +108,16 @@ def bench_backward(a):
     del W1, W2
     ws = moe.alloc_workspace(shape)
     dW1p, dW2p = torch.empty_like(W1p), torch.empty_like(W2p)
+    dx = torch.empty_like(x)
+    dtw = torch.empty_like(wts)
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     stages = (("forward_train", lambda: moe.forward(shape, x, idx, wts, W1p, W2p, ws, y)),
-              ("dgrad_swiglu_bwd", lambda: moe.bwd_gemm2_dgrad(shape, dy, wts, W2p, ws, fuse_swiglu_bwd=True)),
+              ("dgrad_swiglu_bwd", lambda: moe.bwd_gemm2_dgrad(shape, dy, wts, W2p, ws, fuse_swiglu_bwd=True,
+                                                               dtopk_w=dtw)),
               ("wgrad2", lambda: moe.wgrad2(shape, dy, wts, ws, dW2p)),
-              ("wgrad1", lambda: moe.wgrad1(shape, x, ws, dW1p)))
+              ("wgrad1", lambda: moe.wgrad1(shape, x, ws, dW1p)),
+              ("dgrad1_combine", lambda: moe.bwd_gemm1_dgrad_combine(shape, W1p, ws, dx)))
     log("warmup %d" % a.warmup)
     for _ in range(a.warmup):
         for _, fn in stages:
@@ -138,10 +143,14 @@ def bench_backward(a):
     tok_local = int(local.any(axis=1).sum())
     H, I, EL = w.H, w.I, w.EL
     # algorithmic HBM bytes and FLOPs per launch of each backward kernel (real rows only)
+    # dgrad: W2 once, dy rows of tokens with a local pair, hgu read and dhgu written, act read for
+    # d(topk_w); dgrad1: W1 once, dhgu rows read, dx rows of tokens with a local pair written
     alg = {
-        "dgrad_swiglu_bwd": (nonempty * H * I * 2 + tok_local * H * 2 + P * 2 * I * 2 * 2, 2.0 * P * H * I),
+        "dgrad_swiglu_bwd": (nonempty * H * I * 2 + tok_local * H * 2 + P * 2 * I * 2 * 2 + P * I * 2,
+                             2.0 * P * H * I),
         "wgrad2": (EL * H * I * 2 + P * I * 2 + tok_local * H * 2, 2.0 * P * H * I),
         "wgrad1": (EL * 2 * I * H * 2 + P * 2 * I * 2 + tok_local * H * 2, 2.0 * P * H * 2 * I),
+        "dgrad1_combine": (nonempty * 2 * I * H * 2 + P * 2 * I * 2 + tok_local * H * 2, 2.0 * P * 2 * I * H),
     }
     roof = {}
     for j, (name, _) in enumerate(stages):
@@ -155,7 +164,8 @@ def bench_backward(a):
     flops = w.flops_fwd(P) + sum(v[1] for v in alg.values())
     value = flops / (ms / 1e3) / 1e12
     out = {
-        "metric": "MoE layer training step (fwd + L2 dgrad + SwiGLU bwd + dW2 + dW1) TFLOP/s on 1 MI355X",
+        "metric": "MoE layer training step (fwd + L2 dgrad + SwiGLU bwd + d topk_w + dW2 + dW1 + L1 dgrad + "
+                  "combine) TFLOP/s on 1 MI355X",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) logits, x, dy, scaled weights)",

@@ -7,9 +7,10 @@
  * dispatched token rows go through an L1 grouped GEMM (NT) into a [gate | up] projection;
  * SwiGLU; an L2 grouped GEMM (NT); and a combine that weights each row by its top-k weight
  * and sums the contributions of each token (a weighted scatter-add).  The backward entry
- * points follow the same section's backward: L2 dgrad (NN), the SwiGLU transpose, dW2 with a
- * variable K (the row count of each expert) and dW1 (TN) on re-gathered token rows, as in
- * the page's Core Design section 2 (recompute the dispatched x instead of saving it).
+ * points follow the same section's backward: L2 dgrad (NN) with the gradient of the routing
+ * weights, the SwiGLU transpose, dW2 with a variable K (the row count of each expert), dW1 (TN)
+ * on re-gathered token rows, as in the page's Core Design section 2 (recompute the dispatched
+ * x instead of saving it), and the L1 dgrad (NN) whose rows are summed back to token order.
  * Per-expert row counts are padded to the GEMM block (block-M alignment, "How Mega MoE
  * Overlaps Expert Parallelism Communication with Computation in DeepGEMM" page, section
  * Block-M Alignment), so every launch has a shape fixed on the host and nothing waits on the
@@ -92,13 +93,15 @@ typedef struct moe_shape {
  *   scratch        prologue scratch (per-chunk expert histograms)
  *   tile_sync      int32 [512]          tile-scheduler counters of the forward GEMMs (zeroed by
  *                                       moe_route_prologue; zero again after each GEMM launch)
+ *   dtw_part       fp32  [R_max, I/128] per-row partial sums of the routing-weight gradient, one
+ *                                       per 128-column tile of the L2 dgrad (train only, else 0)
  */
 typedef struct moe_ws_layout {
     size_t total_bytes;
     int64_t rows_capacity;
     int64_t num_blocks;
     size_t counts, padded_offsets, row_pair, pair_row, tile_expert, tok_nloc, meta;
-    size_t act, stage, hgu, dact, dhgu, zeros, scratch, tile_sync;
+    size_t act, stage, hgu, dact, dhgu, zeros, scratch, tile_sync, dtw_part;
 } moe_ws_layout;
 
 /* Message for a status code (static string). */
@@ -198,15 +201,31 @@ int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* to
  * L2 dgrad, NN: dact[r] = topk_w[p] * (dy[t] @ W2[e]^T) with p = row_pair[r], t = p / k, read
  * from the packed w2p as the [K = H, N = I] operand.  With fuse_swiglu_bwd nonzero the
  * epilogue applies the SwiGLU transpose and writes ws dhgu directly; else it writes ws dact.
+ * With dtopk_w non-NULL it also writes the gradient of the routing weights, the derivative of
+ * the weighted scatter-add y[t] = sum_j topk_w[t, j] * o_p:
+ *   dtopk_w [device] fp32 [T, k]: dtopk_w[t, j] = <dy[t], o_p> for a local pair p = t*k + j,
+ *   computed as <dy[t] @ W2[e]^T, act[r]> on the saved activation row (the same value, since
+ *   o_p = act[r] @ W2[e]); 0 for a pair this GPU does not handle (its partial of the gradient).
  *   dy [device] bf16 [T, H]; topk_w [device] fp32 [T, k]
  */
 int32_t moe_bwd_gemm2_dgrad(const moe_shape* shape, const uint16_t* dy, const float* topk_w,
                             const uint16_t* w2p, void* ws, size_t ws_bytes,
-                            int32_t fuse_swiglu_bwd, void* stream);
+                            int32_t fuse_swiglu_bwd, float* dtopk_w, void* stream);
 
 /* SwiGLU transpose ("Mega MoE" page, SwiGLU bwd): from ws dact and ws hgu, with
  * s = sigmoid(g): dgate = dact * u * s * (1 + g * (1 - s)), dup = dact * g * s -> ws dhgu. */
 int32_t moe_swiglu_bwd(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * L1 dgrad, NN, and its combine ("Mega MoE" page, Pipeline, backward: the conjugate of dispatch +
+ * L1 sends each row's gradient back to its token): for every real row r of pair p = (t, j),
+ * dX[r] = dhgu[r] @ W1[e]^T, read from the packed w1p as the [K = 2I, N = H] operand, then
+ *   dx [device] bf16 [T, H]: dx[t] = sum over the local pairs of t of dX[row of the pair],
+ *   summed in fp32 in slot order (deterministic); 0 for a token with no local pair.
+ * Reads ws dhgu (moe_bwd_gemm2_dgrad with fuse_swiglu_bwd, or moe_swiglu_bwd); uses ws stage.
+ */
+int32_t moe_bwd_gemm1_dgrad_combine(const moe_shape* shape, const uint16_t* w1p, void* ws,
+                                    size_t ws_bytes, uint16_t* dx, void* stream);
 
 /* dW2 with variable K ("Mega MoE" page, backward: dW2 (variable-K)):
  * dW2[e] [I, H] = sum over rows r of e of act[r]^T (x) (topk_w[p] * dy[t]); K = count of e.
@@ -222,10 +241,14 @@ int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, const float* topk
 int32_t moe_wgrad1(const moe_shape* shape, const uint16_t* x, void* ws, size_t ws_bytes,
                    uint16_t* dw1p, void* stream);
 
-/* Fused backward: L2 dgrad with the SwiGLU transpose in its epilogue, dW2, dW1. */
+/* Fused backward: L2 dgrad with the SwiGLU transpose in its epilogue (and the routing-weight
+ * gradient when dtopk_w is non-NULL), dW2, dW1, then the L1 dgrad with its combine when dx is
+ * non-NULL (w1p is then required; it may be NULL otherwise).  Outputs as in the stage entry
+ * points above: dw1p, dw2p packed bf16; dx bf16 [T, H]; dtopk_w fp32 [T, k]. */
 int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* dy,
-                     const float* topk_w, const uint16_t* w2p, void* ws, size_t ws_bytes,
-                     uint16_t* dw1p, uint16_t* dw2p, void* stream);
+                     const float* topk_w, const uint16_t* w1p, const uint16_t* w2p, void* ws,
+                     size_t ws_bytes, uint16_t* dw1p, uint16_t* dw2p, uint16_t* dx,
+                     float* dtopk_w, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,8 +1,9 @@
 """GPU parity of the backward stages against the CPU oracle, through the C ABI.
 
-Covers L2 dgrad (NN) with and without the SwiGLU transpose in its epilogue, the standalone
-SwiGLU backward, dW2 and dW1 with a variable K (rows per expert, including experts without
-rows, whose gradients must be exact zeros).
+Covers L2 dgrad (NN) with and without the SwiGLU transpose in its epilogue, the gradient of
+the routing weights, the standalone SwiGLU backward, dW2 and dW1 with a variable K (rows per
+expert, including experts without rows, whose gradients must be exact zeros) and the L1 dgrad
+(NN) with its combine back to token order (dx).
 
 Acceptance:
   * row intermediates (dact, dhgu) are checked link by link: dact against the oracle's L2
@@ -13,6 +14,10 @@ Acceptance:
     dot-product error bound, 2^-8 = bf16 unit roundoff): c = 2 for dW2 (both operands, the
     saved activation and w * dy, are rounded once) and c = 3 for dW1 (x is exact; the dhgu
     operand is rounded and was itself computed from bf16 saved pre-activations).
+  * dx is a sum over a token's local pairs of dhgu rows times W1[e]^T: like dW1, c = 3 on
+    sum_p |W1[e]| |dhgu_p|.  d(topk_w)[t, j] = <dy[t] @ W2[e]^T, act_p> with the saved bf16
+    activation: c = 2 on sum_c |(dy W2^T)_c act_c|.  Tokens with no local pair (dx) and pairs
+    this GPU does not handle (d(topk_w)) must be exact zeros.
 """
 import numpy as np
 import pytest
@@ -26,6 +31,7 @@ from gpu_helpers import bits_host, check_bf16, check_sum_bound, f64_host, layer,
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
 C_DW1, C_DW2 = 3.0, 2.0
+C_DX, C_DTW = 3.0, 2.0
 
 
 @pytest.fixture(autouse=True)
@@ -54,9 +60,47 @@ def run_forward_backward(w, d, bm):
     s1, s2 = moe.packed_sizes(ns.shape)
     ns.dW1p = torch.full(s1, float("nan"), dtype=torch.bfloat16, device="cuda")
     ns.dW2p = torch.full(s2, float("nan"), dtype=torch.bfloat16, device="cuda")
-    moe.backward(ns.shape, ns.x, ns.dy, ns.wts, ns.W2p, ns.ws, ns.dW1p, ns.dW2p)
+    ns.dx = torch.full((w.T, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ns.dtw = torch.full((w.T, w.k), float("nan"), dtype=torch.float32, device="cuda")
+    moe.backward(ns.shape, ns.x, ns.dy, ns.wts, ns.W2p, ns.ws, ns.dW1p, ns.dW2p, w1p=ns.W1p, dx=ns.dx,
+                 dtopk_w=ns.dtw)
     torch.cuda.synchronize()
     return ns
+
+
+def token_term_sums(w, d, tokens):
+    """sum|terms| of the dx rows and d(topk_w) entries of the given tokens, from the oracle's
+    per-pair rows: sum_p |W1[e]| |dhgu_p| and sum_c |(dy W2^T)_c act_c|."""
+    idx = d["topk_idx"]
+    Sx = np.zeros((len(tokens), w.H))
+    Sw = np.zeros((len(tokens), w.k))
+    pairs = [int(t) * w.k + j for t in tokens for j in range(w.k)
+             if w.e_lo <= idx[t, j] < w.e_lo + w.EL]
+    if not pairs:
+        return Sx, Sw
+    dA, dH, a = oracle_rows(w, d, np.array(pairs))
+    wts = d["topk_weights"].reshape(-1)[pairs].astype(np.float64)
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    for n, p in enumerate(pairs):
+        t, j = divmod(p, w.k)
+        e = int(idx[t, j]) - w.e_lo
+        W1e = np.abs(mw.bf16_bits_to_f32(d["W1"][e]).astype(np.float64))
+        Sx[pos[t]] += W1e @ np.abs(dH[n])
+        Sw[pos[t], j] = np.sum(np.abs(dA[n] / wts[n]) * np.abs(a[n]))
+    return Sx, Sw
+
+
+def check_token_grads(w, d, ns, tokens, what):
+    args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    dx_ref, dw_ref = oracle.backward_tokens(*args, E=w.E, e_lo=w.e_lo, tokens=tokens)
+    Sx, Sw = token_term_sums(w, d, tokens)
+    dx = f64_host(ns.dx)[tokens]
+    dw = ns.dtw.cpu().double().numpy()[tokens]
+    check_sum_bound(dx, dx_ref, Sx, C_DX, TOL, "dx " + what)
+    check_sum_bound(dw, dw_ref, Sw, C_DTW, TOL, "d(topk_w) " + what)
+    local = (d["topk_idx"] >= w.e_lo) & (d["topk_idx"] < w.e_lo + w.EL)
+    assert np.all(dw[~local[tokens]] == 0.0), "pairs this GPU does not handle must get exact zeros"
+    assert np.all(dx[~local[tokens].any(axis=1)] == 0.0), "tokens with no local pair must get exact zeros"
 
 
 def oracle_rows(w, d, pairs):
@@ -109,6 +153,35 @@ def test_backward_reduced_full_compare(w, bm):
     hgu = bits_host(moe.ws_region(ns.ws, ns.shape, "hgu"))[real]
     dhgu = f64_host(moe.ws_region(ns.ws, ns.shape, "dhgu"))[real]
     check_bf16(dhgu, oracle.swiglu_bwd(hgu, dA), TOL, "dhgu (fused epilogue)")
+    check_token_grads(w, d, ns, np.arange(w.T), "(all tokens)")
+
+
+def test_backward_token_grads_edge_routing():
+    """Dropped ids, a duplicated expert in one token, tokens with no local pair and tokens whose
+    only local pair is the single one (direct store) next to multi-pair tokens (staged sum)."""
+    w = REDUCED[1]
+    d = mw.inputs(w, 12)
+    idx = d["topk_idx"].copy()
+    idx[0] = [w.E + 3, -1, w.E]                  # all dropped
+    idx[1] = [w.e_lo, w.e_lo, w.e_lo]            # one expert three times
+    idx[2] = [0, 1, w.e_lo + w.EL]               # none local (shard starts at e_lo = 2)
+    idx[3] = [w.e_lo + 1, w.E + 1, w.E - 1]      # one local pair, one dropped, one remote
+    d = dict(d, topk_idx=idx)
+    ns = run_forward_backward(w, d, 64)
+    check_token_grads(w, d, ns, np.arange(w.T), "(edge routing)")
+    assert np.all(f64_host(ns.dx)[[0, 2]] == 0.0)
+
+
+def test_backward_is_deterministic():
+    w = REDUCED[1]
+    d = mw.inputs(w, 13)
+    a = run_forward_backward(w, d, 64)
+    b = run_forward_backward(w, d, 64)
+    for n in ("dx", "dtw", "dW1p", "dW2p"):
+        assert torch.equal(getattr(a, n).view(torch.int16) if getattr(a, n).dtype == torch.bfloat16
+                           else getattr(a, n).view(torch.int32),
+                           getattr(b, n).view(torch.int16) if getattr(b, n).dtype == torch.bfloat16
+                           else getattr(b, n).view(torch.int32)), n
 
 
 def test_backward_stages_match_oracle_and_fused():
@@ -121,8 +194,10 @@ def test_backward_stages_match_oracle_and_fused():
     real = np.nonzero(t["row_pair"] >= 0)[0]
     dA, _, _ = oracle_rows(w, d, t["row_pair"][real])
 
-    moe.bwd_gemm2_dgrad(s, ns.dy, ns.wts, ns.W2p, ns.ws, fuse_swiglu_bwd=False)
+    dtw = torch.full_like(ns.dtw, float("nan"))
+    moe.bwd_gemm2_dgrad(s, ns.dy, ns.wts, ns.W2p, ns.ws, fuse_swiglu_bwd=False, dtopk_w=dtw)
     torch.cuda.synchronize()
+    assert torch.equal(dtw, ns.dtw), "d(topk_w) does not depend on the SwiGLU-transpose path"
     dact = moe.ws_region(ns.ws, s, "dact")
     check_bf16(f64_host(dact)[real], dA, TOL, "dact (L2 dgrad)")
     pad = np.setdiff1d(np.arange(t["num_rows"]), real)
@@ -149,6 +224,13 @@ def test_backward_stages_match_oracle_and_fused():
     check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1 (staged)")
     check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2 (staged)")
 
+    # L1 dgrad + combine on the standalone SwiGLU transpose's dhgu
+    ns.dx = torch.full_like(ns.dx, float("nan"))
+    ns.dtw = dtw
+    moe.bwd_gemm1_dgrad_combine(s, ns.W1p, ns.ws, ns.dx)
+    torch.cuda.synchronize()
+    check_token_grads(w, d, ns, np.arange(w.T), "(staged)")
+
 
 def test_backward_full_size_sampled_experts():
     w = mw.get(4)
@@ -172,3 +254,6 @@ def test_backward_full_size_sampled_experts():
     hgu = bits_host(moe.ws_region(ns.ws, ns.shape, "hgu"))[rows]
     check_bf16(f64_host(moe.ws_region(ns.ws, ns.shape, "dhgu"))[rows], oracle.swiglu_bwd(hgu, dA), TOL,
                "dhgu rows")
+    from gpu_helpers import sample_tokens
+    tokens = sample_tokens(t["tok_nloc"], 18, seed=5)
+    check_token_grads(w, d, ns, tokens, "(sampled tokens)")

@@ -8,8 +8,8 @@ streams only.
 
 Pipeline ("Mega MoE" page, Pipeline): route_prologue -> dispatch_gemm1 (gather + L1 NT +
 SwiGLU) -> gemm2_combine (L2 NT + top-k weighted scatter-add), or ``forward`` for all of it;
-the backward entry points follow the page's backward (L2 dgrad NN, SwiGLU transpose, dW2 and
-dW1 with a variable K).
+the backward entry points follow the page's backward (L2 dgrad NN with the routing-weight
+gradient, SwiGLU transpose, dW2 and dW1 with a variable K, L1 dgrad NN with its combine to dx).
 """
 from __future__ import annotations
 
@@ -25,8 +25,8 @@ _lib = None
 ENTRY_POINTS = (
     "moe_status_string", "moe_workspace_bytes", "moe_workspace_layout", "moe_preferred_block_m",
     "moe_pack_weights", "moe_unpack_weights", "moe_route_prologue", "moe_dispatch_gemm1", "moe_swiglu",
-    "moe_gemm2_combine", "moe_forward", "moe_bwd_gemm2_dgrad", "moe_swiglu_bwd", "moe_wgrad2",
-    "moe_wgrad1", "moe_backward",
+    "moe_gemm2_combine", "moe_forward", "moe_bwd_gemm2_dgrad", "moe_swiglu_bwd",
+    "moe_bwd_gemm1_dgrad_combine", "moe_wgrad2", "moe_wgrad1", "moe_backward",
 )
 
 
@@ -42,7 +42,8 @@ class Shape(ctypes.Structure):
 
 
 _LAYOUT_FIELDS = ("counts", "padded_offsets", "row_pair", "pair_row", "tile_expert", "tok_nloc",
-                  "meta", "act", "stage", "hgu", "dact", "dhgu", "zeros", "scratch", "tile_sync")
+                  "meta", "act", "stage", "hgu", "dact", "dhgu", "zeros", "scratch", "tile_sync",
+                  "dtw_part")
 
 
 class WsLayout(ctypes.Structure):
@@ -72,11 +73,12 @@ def lib():
         L.moe_swiglu.argtypes = [S, P, P, ctypes.c_size_t, P, P]
         L.moe_gemm2_combine.argtypes = [S, P, P, P, P, ctypes.c_size_t, P, P]
         L.moe_forward.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P, P]
-        L.moe_bwd_gemm2_dgrad.argtypes = [S, P, P, P, P, ctypes.c_size_t, i32, P]
+        L.moe_bwd_gemm2_dgrad.argtypes = [S, P, P, P, P, ctypes.c_size_t, i32, P, P]
         L.moe_swiglu_bwd.argtypes = [S, P, ctypes.c_size_t, P]
+        L.moe_bwd_gemm1_dgrad_combine.argtypes = [S, P, P, ctypes.c_size_t, P, P]
         L.moe_wgrad2.argtypes = [S, P, P, P, ctypes.c_size_t, P, P]
         L.moe_wgrad1.argtypes = [S, P, P, ctypes.c_size_t, P, P]
-        L.moe_backward.argtypes = [S, P, P, P, P, P, ctypes.c_size_t, P, P, P]
+        L.moe_backward.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P, P, P, P, P]
         for n in ENTRY_POINTS[2:]:
             if n != "moe_workspace_bytes":
                 getattr(L, n).restype = i32
@@ -142,6 +144,7 @@ _REGION = {  # name -> (dtype, row width in elements or None)
     "tile_expert": (torch.int32, None), "tok_nloc": (torch.int32, None), "meta": (torch.int32, None),
     "act": (torch.bfloat16, "I"), "stage": (torch.float32, "H"), "hgu": (torch.bfloat16, "2I"),
     "dact": (torch.bfloat16, "I"), "dhgu": (torch.bfloat16, "2I"),
+    "dtw_part": (torch.float32, "I/128"),
 }
 
 
@@ -156,9 +159,9 @@ def ws_region(ws: torch.Tensor, shape: Shape, name: str) -> torch.Tensor:
     if width is None:
         n, view = sizes[name], None
     else:
-        if name in ("hgu", "dact", "dhgu") and not shape.train:
+        if name in ("hgu", "dact", "dhgu", "dtw_part") and not shape.train:
             raise MoeError("region %s exists only for train shapes" % name)
-        cols = {"I": shape.I, "H": shape.H, "2I": 2 * shape.I}[width]
+        cols = {"I": shape.I, "H": shape.H, "2I": 2 * shape.I, "I/128": shape.I // 128}[width]
         n, view = R * cols, (R, cols)
     esz = torch.tensor([], dtype=dtype).element_size()
     t = ws[L[name]:L[name] + n * esz].view(dtype)
@@ -227,11 +230,19 @@ def forward(shape, x, topk_idx, topk_w, w1p, w2p, ws, y, stream=None):
                              _ptr(y, torch.bfloat16, "y"), _stream(stream)), "moe_forward")
 
 
-def bwd_gemm2_dgrad(shape, dy, topk_w, w2p, ws, fuse_swiglu_bwd=True, stream=None):
+def bwd_gemm2_dgrad(shape, dy, topk_w, w2p, ws, fuse_swiglu_bwd=True, dtopk_w=None, stream=None):
     p, n = _ws(ws)
     _check(lib().moe_bwd_gemm2_dgrad(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy"),
                                      _ptr(topk_w, torch.float32, "topk_w"), _ptr(w2p, torch.bfloat16, "w2p"),
-                                     p, n, int(bool(fuse_swiglu_bwd)), _stream(stream)), "moe_bwd_gemm2_dgrad")
+                                     p, n, int(bool(fuse_swiglu_bwd)), _ptr(dtopk_w, torch.float32, "dtopk_w"),
+                                     _stream(stream)), "moe_bwd_gemm2_dgrad")
+
+
+def bwd_gemm1_dgrad_combine(shape, w1p, ws, dx, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_bwd_gemm1_dgrad_combine(ctypes.byref(shape), _ptr(w1p, torch.bfloat16, "w1p"), p, n,
+                                             _ptr(dx, torch.bfloat16, "dx"), _stream(stream)),
+           "moe_bwd_gemm1_dgrad_combine")
 
 
 def swiglu_bwd(shape, ws, stream=None):
@@ -252,9 +263,11 @@ def wgrad1(shape, x, ws, dw1p, stream=None):
                             _ptr(dw1p, torch.bfloat16, "dw1p"), _stream(stream)), "moe_wgrad1")
 
 
-def backward(shape, x, dy, topk_w, w2p, ws, dw1p, dw2p, stream=None):
+def backward(shape, x, dy, topk_w, w2p, ws, dw1p, dw2p, w1p=None, dx=None, dtopk_w=None, stream=None):
     p, n = _ws(ws)
     _check(lib().moe_backward(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"), _ptr(dy, torch.bfloat16, "dy"),
-                              _ptr(topk_w, torch.float32, "topk_w"), _ptr(w2p, torch.bfloat16, "w2p"), p, n,
+                              _ptr(topk_w, torch.float32, "topk_w"), _ptr(w1p, torch.bfloat16, "w1p"),
+                              _ptr(w2p, torch.bfloat16, "w2p"), p, n,
                               _ptr(dw1p, torch.bfloat16, "dw1p"), _ptr(dw2p, torch.bfloat16, "dw2p"),
+                              _ptr(dx, torch.bfloat16, "dx"), _ptr(dtopk_w, torch.float32, "dtopk_w"),
                               _stream(stream)), "moe_backward")

@@ -66,6 +66,7 @@ int32_t layout_of(const moe_shape* s, moe_ws_layout* L) {
     L->zeros = take(2 * (H > 2 * I ? H : 2 * I));
     L->tile_sync = take(4 * static_cast<size_t>(kMaxGrid));
     L->scratch = take(4 * static_cast<size_t>(chunks) * (EL + 1));
+    if (s->train) L->dtw_part = take(4 * static_cast<size_t>(R) * (I / 128));
     L->total_bytes = off;
     return MOE_OK;
 }
@@ -107,6 +108,8 @@ int32_t prepare(const moe_shape* s, const void* ws, size_t ws_bytes, bool need_t
     w->hgu = s->train ? reinterpret_cast<uint16_t*>(b + L->hgu) : nullptr;
     w->dact = s->train ? reinterpret_cast<uint16_t*>(b + L->dact) : nullptr;
     w->dhgu = s->train ? reinterpret_cast<uint16_t*>(b + L->dhgu) : nullptr;
+    w->dtw_part = s->train ? reinterpret_cast<float*>(b + L->dtw_part) : nullptr;
+    w->dtw_cols = s->I / 128;
     const int64_t pairs = static_cast<int64_t>(s->T) * s->k;
     w->num_chunks = static_cast<int32_t>(pairs > 0 ? (pairs + kRouteChunk - 1) / kRouteChunk : 1);
     w->chunk_hist = reinterpret_cast<int32_t*>(b + L->scratch);
@@ -255,15 +258,30 @@ int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* to
 }
 
 int32_t moe_bwd_gemm2_dgrad(const moe_shape* shape, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
-                            void* ws, size_t ws_bytes, int32_t fuse_swiglu_bwd, void* stream) {
+                            void* ws, size_t ws_bytes, int32_t fuse_swiglu_bwd, float* dtopk_w, void* stream) {
     Dims d;
     Ws w;
     moe_ws_layout L;
     int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
     if (st != MOE_OK) return st;
     if (!w2p || ((!dy || !topk_w) && shape->T > 0)) return MOE_ERR_NULL;
-    if (!aligned16(dy) || !aligned4(topk_w) || !aligned16(w2p)) return MOE_ERR_ALIGN;
-    return launched(launch_dgrad(d, dy, topk_w, w2p, w, fuse_swiglu_bwd != 0, static_cast<hipStream_t>(stream)));
+    if (!aligned16(dy) || !aligned4(topk_w) || !aligned16(w2p) || !aligned4(dtopk_w)) return MOE_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_dgrad(d, dy, topk_w, w2p, w, fuse_swiglu_bwd != 0, dtopk_w != nullptr, s);
+    if (e == hipSuccess && dtopk_w) e = launch_dtopk_w_finish(d, w, dtopk_w, s);
+    return launched(e);
+}
+
+int32_t moe_bwd_gemm1_dgrad_combine(const moe_shape* shape, const uint16_t* w1p, void* ws, size_t ws_bytes,
+                                    uint16_t* dx, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!w1p || (!dx && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(w1p) || !aligned16(dx)) return MOE_ERR_ALIGN;
+    return launched(launch_dgrad1(d, w1p, w, dx, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_swiglu_bwd(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream) {
@@ -300,21 +318,24 @@ int32_t moe_wgrad1(const moe_shape* shape, const uint16_t* x, void* ws, size_t w
 }
 
 int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* dy, const float* topk_w,
-                     const uint16_t* w2p, void* ws, size_t ws_bytes, uint16_t* dw1p, uint16_t* dw2p,
-                     void* stream) {
+                     const uint16_t* w1p, const uint16_t* w2p, void* ws, size_t ws_bytes, uint16_t* dw1p,
+                     uint16_t* dw2p, uint16_t* dx, float* dtopk_w, void* stream) {
     Dims d;
     Ws w;
     moe_ws_layout L;
     int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
     if (st != MOE_OK) return st;
     if (!w2p || !dw1p || !dw2p || ((!x || !dy || !topk_w) && shape->T > 0)) return MOE_ERR_NULL;
-    if (!aligned16(x) || !aligned16(dy) || !aligned4(topk_w) || !aligned16(w2p) || !aligned16(dw1p) ||
-        !aligned16(dw2p))
+    if (dx && !w1p) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(dy) || !aligned4(topk_w) || !aligned16(w1p) || !aligned16(w2p) ||
+        !aligned16(dw1p) || !aligned16(dw2p) || !aligned16(dx) || !aligned4(dtopk_w))
         return MOE_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_dgrad(d, dy, topk_w, w2p, w, 1, s);
+    hipError_t e = launch_dgrad(d, dy, topk_w, w2p, w, 1, dtopk_w != nullptr, s);
+    if (e == hipSuccess && dtopk_w) e = launch_dtopk_w_finish(d, w, dtopk_w, s);
     if (e == hipSuccess) e = launch_wgrad2(d, dy, topk_w, w, dw2p, s);
     if (e == hipSuccess) e = launch_wgrad1(d, x, w, dw1p, s);
+    if (e == hipSuccess && dx) e = launch_dgrad1(d, w1p, w, dx, s);
     return launched(e);
 }
 

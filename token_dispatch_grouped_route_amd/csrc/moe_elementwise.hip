@@ -214,4 +214,27 @@ hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipSt
     return hipGetLastError();
 }
 
+// d(topk_w)[p] = sum over the N tiles of the L2 dgrad of its per-row partial, in tile order, for
+// the row of a local pair; 0 for a pair this GPU does not handle.
+__global__ __launch_bounds__(kEwThreads) void dtopk_w_finish_kernel(Dims d, Ws ws, float* __restrict__ dtopk_w) {
+    const int64_t np = static_cast<int64_t>(d.T) * d.k;
+    const int cols = ws.dtw_cols;
+    for (int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; p < np;
+         p += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int r = ws.pair_row[p];
+        float sum = 0.0f;
+        if (r >= 0 && r < ws.rows_cap)
+            for (int j = 0; j < cols; ++j) sum += ws.dtw_part[static_cast<int64_t>(r) * cols + j];
+        dtopk_w[p] = sum;
+    }
+}
+
+hipError_t launch_dtopk_w_finish(const Dims& d, const Ws& ws, float* dtopk_w, hipStream_t s) {
+    const int64_t np = static_cast<int64_t>(d.T) * d.k;
+    if (np <= 0) return hipSuccess;
+    const int64_t want = (np + kEwThreads - 1) / kEwThreads, cap = device_cu_count() * 8;
+    dtopk_w_finish_kernel<<<static_cast<int>(want < cap ? want : cap), kEwThreads, 0, s>>>(d, ws, dtopk_w);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -19,7 +19,9 @@
 //          LDS store.
 //
 // Kernels ("Mega MoE" page, Pipeline, backward):
-//   dgrad   L2 dgrad NN, row weight and optional SwiGLU transpose in the epilogue
+//   dgrad   L2 dgrad NN, row weight and optional SwiGLU transpose in the epilogue; optionally
+//           the per-row partials of d(topk_w) = <dy[t], o_p> = <dy[t] W2^T, act_p>
+//   dgrad1  L1 dgrad NN over the packed W1, rows summed back to token order (the combine)
 //   wgrad2  dW2 = dO^T A, K = rows of the expert (variable K), TN
 //   wgrad1  dW1 = dHgu^T X with X re-gathered from x, TN
 // Weight gradients are written in the packed layout of the weights they belong to, whole 1 KB
@@ -331,13 +333,19 @@ struct W2ColSrc {   // B operand of the dgrad: (K = h, N = i) of expert e's pack
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
+// The GEMM runs on the plain dy rows, so the accumulator is dA'[r] = dy[t] @ W2[e]^T and the
+// row weight enters in the epilogue (dA = w * dA').  With topk_w_grad the epilogue also forms
+// sum over the tile's columns of dA'[r, c] * act[r, c]: summed over the N tiles (in tile order,
+// by the finish kernel) that is <dy[t], o_p>, the gradient of the routing weight, because
+// o_p = act_p @ W2[e].
 template <class C>
 __global__ __launch_bounds__(C::NT) void dgrad_kernel(const uint16_t* __restrict__ dy,
                                                       const float* __restrict__ topk_w,
                                                       const uint16_t* __restrict__ w2p, Dims d, Ws ws,
-                                                      int fuse) {
+                                                      int fuse, int topk_w_grad) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float* s_w = reinterpret_cast<float*>(smem + C::LDS_BYTES);
+    float* s_part = s_w + C::BM;   // [WN][BM] row sums of dA' * act over each wave's columns
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
     const int H = d.H, I = d.I;
@@ -383,10 +391,12 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const uint16_t* __restrict
                 const int rl = wm0 + mi * 32 + acc_row(r, lane);
                 const int64_t row = row0 + rl;
                 const float w = s_w[rl];
+                float part = 0.0f;
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
                     const int c = nt * C::BN + wn0 + ni * 32 + (lane & 31);
                     const float da = w * acc[mi][ni][r];
+                    if (topk_w_grad) part += acc[mi][ni][r] * bf16_to_f32(ws.act[row * I + c]);
                     if (fuse) {
                         const float g = bf16_to_f32(ws.hgu[row * 2 * I + c]);
                         const float u = bf16_to_f32(ws.hgu[row * 2 * I + I + c]);
@@ -396,6 +406,106 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const uint16_t* __restrict
                     } else {
                         ws.dact[row * I + c] = f32_to_bf16(da);
                     }
+                }
+                if (topk_w_grad) {   // uniform: every lane takes part in the shuffles
+                    // lanes 0-31 hold row rl of 32 columns, lanes 32-63 row rl + 4: sum each half
+#pragma unroll
+                    for (int o = 16; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+                    if ((lane & 31) == 0) s_part[(wave % C::WN) * C::BM + rl] = part;
+                }
+            }
+        if (topk_w_grad) {
+            lds_barrier();
+            for (int r = tid; r < C::BM; r += C::NT) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int wn = 0; wn < C::WN; ++wn) sum += s_part[wn * C::BM + r];
+                ws.dtw_part[(row0 + r) * n_tiles + nt] = sum;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dgrad1: L1 dgrad (NN) and the combine of its rows back to token order
+// ---------------------------------------------------------------------------------------------
+struct W1ColSrc {   // B operand of the L1 dgrad: (K = L1 output column, N = h) of expert e's packed W1
+    static constexpr bool kScaled = false;
+    const uint16_t* base;   // w1p + e*2I*H
+    int H, I;
+    __device__ __forceinline__ const uint16_t* chunk(int k, int m) const {
+        return base + frag_index(l1_packed_col(k, I), m, H);
+    }
+    __device__ __forceinline__ float scale(int) const { return 1.0f; }
+};
+
+// dX[r] = dhgu[r] @ W1[e]^T (K = 2I in the logical [gate | up] order of dhgu, N = H).  The row
+// of a token's only local pair is stored as bf16 straight into dx[t]; rows of tokens with several
+// local pairs go to their fp32 stage rows, which combine_finish sums in slot order (and it zeroes
+// tokens with no local pair), so dx is deterministic.
+template <class C>
+__global__ __launch_bounds__(C::NT) void dgrad1_kernel(const uint16_t* __restrict__ w1p, Dims d, Ws ws,
+                                                       uint16_t* __restrict__ dx) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    int* s_tok = reinterpret_cast<int*>(smem + C::LDS_BYTES);   // token of each tile row, -1 padding
+    int* s_one = s_tok + C::BM;                                  // 1: the row is its token's only local pair
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
+    const int H = d.H, I = d.I, N2 = 2 * d.I;
+    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);
+    const int n_tiles = H / C::BN;
+    const int total = m_tiles * n_tiles;
+    const int npairs = d.T * d.k;
+
+    const TileRange tr(total);
+    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
+        int mt, nt;
+        tile_at(ws, d, n_tiles, tile, mt, nt);
+        const int e = ws.tile_expert[mt];
+        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
+        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
+
+        KRows<C::BM, C::NT> la;
+        la.base = reinterpret_cast<const char*>(ws.dhgu + row0 * N2);
+        la.keep = 0;
+#pragma unroll
+        for (int i = 0; i < la.PER; ++i) {
+            const int rl = la.row_of(tid, i);
+            const int p = ws.row_pair[row0 + rl];
+            la.keep |= static_cast<uint32_t>(p >= 0 && p < npairs) << i;
+            la.off[i] = 2u * (static_cast<uint32_t>(rl) * N2 + 8 * la.chunk_of(tid, i));
+        }
+        TRows<C::BN, C::NT, W1ColSrc> lb;
+        lb.src.base = w1p + static_cast<int64_t>(e) * N2 * H;
+        lb.src.H = H;
+        lb.src.I = I;
+        lb.m_base = nt * C::BN;
+        f32x16_t acc[C::MI][C::NI];
+        lds_barrier();
+        for (int r = tid; r < C::BM; r += C::NT) {
+            const int p = ws.row_pair[row0 + r];
+            const bool ok = p >= 0 && p < npairs;
+            const int t = ok ? p / d.k : -1;
+            s_tok[r] = t;
+            s_one[r] = ok && ws.tok_nloc[t] == 1;
+        }
+        gemm_tile<C>(la, lb, N2 / BK, smem, acc, tid, wm0, wn0, lane);
+
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = wm0 + mi * 32 + acc_row(r, lane);
+                const int t = s_tok[rl];
+                if (t < 0) continue;
+                const int64_t row = row0 + rl;
+                const bool one = s_one[rl] != 0;
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni) {
+                    const int c = nt * C::BN + wn0 + ni * 32 + (lane & 31);
+                    const float v = acc[mi][ni][r];
+                    if (one) dx[static_cast<int64_t>(t) * H + c] = f32_to_bf16(v);
+                    else ws.stage[row * H + c] = v;
                 }
             }
     }
@@ -664,26 +774,53 @@ using WG = Cfg<128, 128, 2, 2, 0>;   // weight-gradient tiles: K is an expert's 
 
 template <class C0>
 static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
-                               const Ws& ws, int fuse, hipStream_t s) {
+                               const Ws& ws, int fuse, bool topk_w_grad, hipStream_t s) {
     using C = Cfg<C0::BM, C0::BN, C0::WM, C0::WN, 1>;   // one staging slot: the transposing loader is register-heavy
-    const size_t lds = C::LDS_BYTES + sizeof(float) * C::BM;
+    static_assert(C::BN == 128, "d(topk_w) partials are laid out per 128-column N tile");
+    const size_t lds = C::LDS_BYTES + sizeof(float) * C::BM * (1 + C::WN);
     auto k = dgrad_kernel<C>;
     allow_lds(k, lds);
     const int n_tiles = d.I / C::BN;
     const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
-    k<<<grid, C::NT, lds, s>>>(dy, topk_w, w2p, d, ws, fuse);
+    k<<<grid, C::NT, lds, s>>>(dy, topk_w, w2p, d, ws, fuse, topk_w_grad ? 1 : 0);
     return hipGetLastError();
 }
 
 hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
-                        const Ws& ws, int fuse, hipStream_t s) {
+                        const Ws& ws, int fuse, bool topk_w_grad, hipStream_t s) {
+    if (topk_w_grad && (!ws.dtw_part || ws.dtw_cols != d.I / 128)) return hipErrorInvalidValue;
     switch (d.BM) {
-        case 32: return dgrad_launch<G32>(d, dy, topk_w, w2p, ws, fuse, s);
-        case 64: return dgrad_launch<G64>(d, dy, topk_w, w2p, ws, fuse, s);
-        case 128: return dgrad_launch<G128>(d, dy, topk_w, w2p, ws, fuse, s);
-        case 256: return dgrad_launch<G256>(d, dy, topk_w, w2p, ws, fuse, s);
+        case 32: return dgrad_launch<G32>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
+        case 64: return dgrad_launch<G64>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
+        case 128: return dgrad_launch<G128>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
+        case 256: return dgrad_launch<G256>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <class C0>
+static hipError_t dgrad1_launch(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s) {
+    using C = Cfg<C0::BM, C0::BN, C0::WM, C0::WN, 1>;
+    const size_t lds = C::LDS_BYTES + 2 * sizeof(int) * C::BM;
+    auto k = dgrad1_kernel<C>;
+    allow_lds(k, lds);
+    const int n_tiles = d.H / C::BN;
+    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
+    k<<<grid, C::NT, lds, s>>>(w1p, d, ws, dx);
+    return hipGetLastError();
+}
+
+hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s) {
+    hipError_t e;
+    switch (d.BM) {
+        case 32: e = dgrad1_launch<G32>(d, w1p, ws, dx, s); break;
+        case 64: e = dgrad1_launch<G64>(d, w1p, ws, dx, s); break;
+        case 128: e = dgrad1_launch<G128>(d, w1p, ws, dx, s); break;
+        case 256: e = dgrad1_launch<G256>(d, w1p, ws, dx, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    return launch_combine_finish(d, ws, dx, s);
 }
 
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,

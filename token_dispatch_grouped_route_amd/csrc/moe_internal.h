@@ -33,12 +33,14 @@ struct Ws {
     uint16_t* hgu;          // bf16 [R_max, 2I] (train)
     uint16_t* dact;         // bf16 [R_max, I]  (train)
     uint16_t* dhgu;         // bf16 [R_max, 2I] (train)
+    float* dtw_part;        // fp32 [R_max, I / 128] per-row partials of d(topk_w) (train)
     uint16_t* zeros;        // a zero row of max(H, 2I) bf16 (written by the prologue)
     int32_t* tile_sync;     // [kMaxGrid] tile-scheduler counters of the forward GEMMs (zero between launches)
     int64_t rows_cap;
     int32_t num_blocks;     // R_max / BM
     int32_t num_chunks;     // prologue chunks of kRouteChunk pairs
     int32_t zero_len;       // elements of the zero row
+    int32_t dtw_cols;       // I / 128: partials per row in dtw_part
 };
 
 constexpr int kRouteThreads = 256;
@@ -92,7 +94,10 @@ hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16
                                 const float* topk_w, const Ws& ws, uint16_t* y, hipStream_t s);
 hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s);
 hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w,
-                        const uint16_t* w2p, const Ws& ws, int fuse_swiglu_bwd, hipStream_t s);
+                        const uint16_t* w2p, const Ws& ws, int fuse_swiglu_bwd, bool topk_w_grad,
+                        hipStream_t s);
+hipError_t launch_dtopk_w_finish(const Dims& d, const Ws& ws, float* dtopk_w, hipStream_t s);
+hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s);
 hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s);
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
                          uint16_t* dw2p, hipStream_t s);
