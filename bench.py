@@ -54,14 +54,16 @@ def kernel_source_hash():
     return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(bytes_per_launch_alg):
+def measured_traffic(workload):
     """HBM bytes per L1 launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source; else None."""
+    the current kernel source and on this workload; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if rec.get("workload", "dsv3_share_fwd") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -268,7 +270,7 @@ def main():
     l1_flops = 2.0 * P * w.H * 2 * w.I
     l1_bytes = nonempty * 2 * w.I * w.H * 2 + tok_local * w.H * 2 + P * w.I * 2 + P * 4
     l1_s = st_ms[1] / 1e3
-    traffic = measured_traffic(l1_bytes)
+    traffic = measured_traffic(w.name)
     roof = {"bound": "hbm", "achieved": l1_bytes / l1_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
             "kernel": "gemm1 (dispatch gather + L1 NT + SwiGLU)",

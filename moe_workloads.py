@@ -8,7 +8,8 @@ can consume the same arrays without sharing any code of the method.
 
 Workloads follow the shapes of the pages' test models:
   * DeepSeek-V3 expert shapes (hidden 7168, intermediate 2048, 256 experts, top-8, 8192 tokens
-    per rank): "Mega MoE" page, Performance / Test Configuration.
+    per rank): "Mega MoE" page, Performance / Test Configuration; the page-scale share stands in
+    for the rows one of its 8 ranks receives from all of them (65 536 tokens' worth).
   * DeepSeek-V2-Lite and DeepSeek-V3 as MoE model presets: "MoE training deep-dive" page,
     section 2 (Representative model configs).
   * 384 experts, top-6, hidden 7168, intermediate 3072, 4096 tokens: the "How Mega MoE Overlaps
@@ -64,6 +65,9 @@ WORKLOADS = [
     Workload("dsv3_share_fwd", T=8192, H=7168, I=2048, E=256, EL=32, k=8),
     Workload("dsv3_share_skewed_fwd", T=8192, H=7168, I=2048, E=256, EL=32, k=8, zipf_s=1.2),
     Workload("wide_share_fwd_bwd", T=4096, H=7168, I=3072, E=384, EL=48, k=6, backward=True),
+    # the rows one GPU of the pages' 8-GPU DeepSeek-V3 run receives: 8 x 8192 tokens routed
+    # top-8 over 256 experts, 32 of them local (about 65 536 local rows), all resident here
+    Workload("dsv3_page_share_fwd", T=65536, H=7168, I=2048, E=256, EL=32, k=8),
 ]
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))

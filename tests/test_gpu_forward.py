@@ -40,7 +40,7 @@ def route_only(w, idx, bm):
 # ------------------------------------------------------------------------------------------
 # Routing prologue
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("bm", [32, 64, 128, 256])
 def test_route_tables_bit_exact(cfg, bm):
     w = mw.get(cfg)
@@ -291,7 +291,7 @@ def full_inputs(cfg):
     return _FULL[cfg]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_forward_full_size_sampled(cfg):
     w, d = full_inputs(cfg)
     bm = moe.preferred_block_m(moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=64))

@@ -167,7 +167,7 @@ def test_route_brute_force_golden():
     pin_route_golden()
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("BM", [32, 64, 128, 256])
 def test_route_matches_stable_sort_on_workloads(cfg, BM):
     w = mw.get(cfg)
@@ -175,7 +175,7 @@ def test_route_matches_stable_sort_on_workloads(cfg, BM):
     pin_route_sort(idx, w.E, w.e_lo, w.EL, BM)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 def test_route_invariants(cfg):
     w = mw.get(cfg)
     idx, _ = mw.routing(w, 0)
