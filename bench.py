@@ -12,7 +12,10 @@ excluded) / step time.  Prints one JSON line.
 
 Flags: --gpus N (only 1 is supported: the path is one GPU's share), --steps K, --warmup W,
 --workload NAME, --block-m BM, --no-cpu-baseline, --copy-calibration (also times a plain 1 GiB
-device copy, for reading HBM counters against a kernel of known traffic).
+device copy, for reading HBM counters against a kernel of known traffic), --replays N (the forward
+captured into a HIP graph and replayed N times, each timed: median and min), --no-references
+(skip the measured ceilings: 1 GiB copy bandwidth, the vendor library's dense bf16 GEMM rate and
+its batched GEMM on a uniform stand-in of each forward GEMM).
 
 --backward measures the training step of the wide-expert share instead (T 4096, H 7168, I 3072,
 384 experts, 48 local, top-6): forward with the activations saved, L2 dgrad with the SwiGLU
@@ -90,6 +93,84 @@ def cpu_baseline(w, d, budget_s=15.0):
     flops = w.flops_fwd(pairs)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d of %d tokens (%d local pairs), fp64 per-token loop, %.1f s" % (len(sample), w.T, pairs, dt)}
+
+
+def stage_rates(ms, flops, nbytes):
+    t = ms / 1e3
+    return {"ms": round(ms, 4), "tflops": round(flops / t / 1e12, 1),
+            "pct_bf16_peak": round(100 * flops / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "alg_gbs": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 2),
+            "alg_flops": flops, "alg_bytes": nbytes}
+
+
+def graph_replay_stats(fn, replays):
+    """The forward captured once into a HIP graph; 10 warm-up replays, then `replays` replays each
+    bracketed by events: median and min per replay."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for e0, e1 in ev:
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    return {"replays": replays, "median_ms": round(float(np.median(t)), 4), "min_ms": round(float(t.min()), 4)}
+
+
+def references(w):
+    """Measured ceilings on this GPU: a plain 1 GiB device copy (HBM read + write), a dense bf16
+    GEMM of the vendor library (8192^3 through torch.matmul), and the vendor batched GEMM on a
+    uniform stand-in of each forward GEMM (EL experts x round(P/EL) rows, no gather, no SwiGLU,
+    no combine)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+    out = {}
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 10)
+    out["copy_1gib_gbs"] = round(2 * src.numel() * 2 / t / 1e9, 1)
+    del src, dst
+    n = 8192
+    A = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    B = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    t = timed(lambda: torch.matmul(A, B), 10)
+    out["vendor_gemm_8192_tflops"] = round(2.0 * n ** 3 / t / 1e12, 1)
+    del A, B
+    rows = 256 if w.name == "dsv3_share_fwd" else max(32, int(round(w.T * w.k * w.EL / w.E / w.EL)))
+    X = torch.randn(w.EL, rows, w.H, device="cuda").to(torch.bfloat16)
+    W1 = torch.randn(w.EL, w.H, 2 * w.I, device="cuda").to(torch.bfloat16)
+    t1 = timed(lambda: torch.bmm(X, W1), 10)
+    del W1
+    A2 = torch.randn(w.EL, rows, w.I, device="cuda").to(torch.bfloat16)
+    W2 = torch.randn(w.EL, w.I, w.H, device="cuda").to(torch.bfloat16)
+    t2 = timed(lambda: torch.bmm(A2, W2), 10)
+    del X, A2, W2
+    torch.cuda.empty_cache()
+    out["vendor_bmm_l1_standin_ms"] = round(t1 * 1e3, 4)
+    out["vendor_bmm_l2_standin_ms"] = round(t2 * 1e3, 4)
+    out["standin_rows_per_expert"] = rows
+    return out
 
 
 def bench_backward(a):
@@ -189,6 +270,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--replays", type=int, default=100, help="graph replays timed one by one (0: skip)")
+    ap.add_argument("--no-references", action="store_true", help="skip the copy / vendor-GEMM references")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the experts; runs on more than one GPU are not "
@@ -260,6 +343,8 @@ def main():
     st = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(a.steps)])
     st_ms = st.mean(axis=0)
 
+    graph = graph_replay_stats(fwd, a.replays) if a.replays > 0 else None
+
     R = int(moe.ws_region(ws, shape, "meta")[0].item())
     # algorithmic bytes of the L1 launch: each non-empty local expert's W1 once, the x rows of
     # tokens with a local pair once, the SwiGLU output rows written once, the pair ids of the rows
@@ -277,6 +362,15 @@ def main():
             "alg_bytes_per_launch": l1_bytes, "alg_flops_per_launch": l1_flops,
             "mfma_frac": l1_flops / l1_s / 1e12 / PEAK_BF16_TFLOPS}
 
+    # per stage: algorithmic FLOPs and bytes (real rows only) over the event-timed stage; L2 +
+    # combine must read each non-empty expert's W2 and the act rows once and write y once (the fp32
+    # staging of multi-pair tokens is this design's, not the method's, so it is not counted)
+    l2_flops = 2.0 * P * w.I * w.H
+    l2_bytes = nonempty * w.H * w.I * 2 + P * w.I * 2 + w.T * w.H * 2
+    stages = {"prologue": {"ms": round(st_ms[0], 4), "alg_bytes": w.T * w.k * 4},
+              "dispatch_gemm1_swiglu": stage_rates(st_ms[1], l1_flops, l1_bytes),
+              "gemm2_combine": stage_rates(st_ms[2], l2_flops, l2_bytes)}
+
     value = flops / (ms / 1e3) / 1e12
     out = {
         "metric": "MoE layer fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak); per-stage ms",
@@ -288,8 +382,14 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {"prologue": round(st_ms[0], 4), "dispatch_gemm1_swiglu": round(st_ms[1], 4),
                       "gemm2_combine": round(st_ms[2], 4), "staged_total": round(st_ms.sum(), 4)},
+        "stages": stages,
         "roofline": roof,
     }
+    if graph:
+        out["graph_replay"] = graph
+    if not a.no_references:
+        log("measuring the copy and vendor-GEMM references")
+        out["references"] = references(w)
     if not a.no_cpu_baseline:
         log("timing the oracle on a CPU sample")
         out["cpu_baseline"] = cpu_baseline(w, d)
