@@ -356,11 +356,19 @@ def main():
     l1_bytes = nonempty * 2 * w.I * w.H * 2 + tok_local * w.H * 2 + P * w.I * 2 + P * 4
     l1_s = st_ms[1] / 1e3
     traffic = measured_traffic(w.name)
-    roof = {"bound": "hbm", "achieved": l1_bytes / l1_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
-            "kernel": "gemm1 (dispatch gather + L1 NT + SwiGLU)",
-            "alg_bytes_per_launch": l1_bytes, "alg_flops_per_launch": l1_flops,
-            "mfma_frac": l1_flops / l1_s / 1e12 / PEAK_BF16_TFLOPS}
+    # the bound is the roof the kernel's arithmetic intensity (algorithmic FLOP per algorithmic
+    # byte) meets first: HBM below the ridge (peak FLOP/s / peak B/s), MFMA above it
+    if l1_flops / l1_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": l1_bytes / l1_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": l1_flops / l1_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": l1_flops / l1_s / 1e12 / PEAK_BF16_TFLOPS}
+    roof.update({"traffic": traffic, "kernel": "gemm1 (dispatch gather + L1 NT + SwiGLU)",
+                 "alg_bytes_per_launch": l1_bytes, "alg_flops_per_launch": l1_flops,
+                 "intensity_flop_per_byte": round(l1_flops / l1_bytes, 1),
+                 "hbm_frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS,
+                 "mfma_frac": l1_flops / l1_s / 1e12 / PEAK_BF16_TFLOPS})
 
     # per stage: algorithmic FLOPs and bytes (real rows only) over the event-timed stage; L2 +
     # combine must read each non-empty expert's W2 and the act rows once and write y once (the fp32
