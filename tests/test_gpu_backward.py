@@ -257,3 +257,43 @@ def test_backward_full_size_sampled_experts():
     from gpu_helpers import sample_tokens
     tokens = sample_tokens(t["tok_nloc"], 18, seed=5)
     check_token_grads(w, d, ns, tokens, "(sampled tokens)")
+
+
+@pytest.mark.parametrize("case", ["empty_batch", "none_local", "one_expert_takes_all"])
+def test_degenerate_routing_forward_and_backward(case):
+    """The method's degenerate cases end to end: no tokens at all; tokens none of whose pairs
+    this GPU handles (y, dx, d(topk_w) and every dW exactly zero); every pair on one expert (the
+    other experts' weight gradients exactly zero)."""
+    w = mw.Workload("degenerate", T=96, H=256, I=128, E=12, EL=4, k=2, e_lo=4, backward=True)
+    if case == "empty_batch":
+        w = mw.scaled(w, T=0)
+    d = mw.inputs(w, 14)
+    idx = d["topk_idx"].copy()
+    if case == "none_local":
+        idx = np.where((idx >= w.e_lo) & (idx < w.e_lo + w.EL), idx + w.EL, idx) % w.E
+        idx = np.where((idx >= w.e_lo) & (idx < w.e_lo + w.EL), 0, idx).astype(np.int32)
+    elif case == "one_expert_takes_all":
+        idx[:] = w.e_lo + 2
+    d = dict(d, topk_idx=idx)
+    ns = run_forward_backward(w, d, 64)
+    t = tables(ns)
+    local = (idx >= w.e_lo) & (idx < w.e_lo + w.EL)
+    assert int(t["counts"].sum()) == int(local.sum())
+    g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
+    empty = np.nonzero(t["counts"] == 0)[0]
+    assert np.all(g1[empty] == 0.0) and np.all(g2[empty] == 0.0)
+    if w.T == 0:
+        return
+    y = f64_host(ns.y)
+    ref = oracle.forward(d["x"], idx, d["topk_weights"], d["W1"], d["W2"], E=w.E, e_lo=w.e_lo)
+    if case == "none_local":
+        assert np.all(y == 0.0) and np.all(f64_host(ns.dx) == 0.0) and torch.all(ns.dtw == 0)
+        assert np.all(g1 == 0.0) and np.all(g2 == 0.0)
+    else:
+        check_bf16(y, ref, TOL, "y (%s)" % case)
+        check_token_grads(w, d, ns, np.arange(w.T), "(%s)" % case)
+        args = (d["x"], idx, d["topk_weights"], d["W1"], d["W2"], d["dy"])
+        dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
+        S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
+        check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1 (%s)" % case)
+        check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2 (%s)" % case)
