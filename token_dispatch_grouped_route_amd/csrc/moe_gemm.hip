@@ -32,6 +32,8 @@
 // The list is ordered expert by expert, and inside an expert N-panel by N-panel with the
 // expert's M tiles adjacent; it is cut into one contiguous chunk per XCD (the hardware places
 // workgroup b on XCD b mod 8, each XCD with its own L2).
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -109,7 +111,9 @@ __device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float s) {
 
 // Operand tile of ROWS rows (the M or N index) x BK, stored in memory with the tile's index
 // contiguous in runs of 8: elements (m .. m+7, k) = Src::chunk(k, m_base + m) for m a multiple of
-// 8 (times Src::scale(k)); a null chunk reads as zeros.
+// 8 (times Src::scale(k)).  Every chunk is a valid address (absent rows point at the workspace's
+// zero row), so the loads carry no branch and the compiler's wait counts stay exact: a load under
+// a branch makes it wait for every load in flight before the next one.
 // Unit u moves K rows 4*kq..4*kq+3 of the 16-byte column mc; kq varies fastest across lanes so
 // the transposed 8-byte LDS writes of a wave fill whole rows without bank conflicts.
 template <int ROWS, int NT, class Src>
@@ -128,14 +132,14 @@ struct TRows {
             const int u = tid + i * NT;
             if (u < UNITS) {
                 const int kq = u % (BK / 4), mc = u / (BK / 4);
+                const uint16_t* p[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int k = kt * BK + 4 * kq + r;
-                    const uint16_t* p = src.chunk(k, m_base + 8 * mc);
-                    u32x4 x = 0;
-                    if (p) x = *reinterpret_cast<const u32x4*>(p);
-                    if (Src::kScaled && p) x = scale_bf16x8(x, src.scale(k));
-                    v[S][i][r] = x;
+                for (int r = 0; r < 4; ++r) p[r] = src.chunk(kt * BK + 4 * kq + r, m_base + 8 * mc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[S][i][r] = *reinterpret_cast<const u32x4*>(p[r]);
+                if constexpr (Src::kScaled) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[S][i][r] = scale_bf16x8(v[S][i][r], src.scale(kt * BK + 4 * kq + r));
                 }
             }
         }
@@ -514,33 +518,38 @@ __global__ __launch_bounds__(C::NT) void dgrad1_kernel(const uint16_t* __restric
 // ---------------------------------------------------------------------------------------------
 // Weight gradients (TN, variable K = rows of the expert)
 // ---------------------------------------------------------------------------------------------
-// K index k is row seg0 + k of the expert's segment; k >= count reads as zero, so the K tail and
-// an expert without rows contribute nothing (an empty expert's tile stores exact zeros).
+// K index k is row seg0 + k of the expert's segment; k >= count reads the zero row, so the K tail
+// and an expert without rows contribute nothing (an empty expert's tile stores exact zeros).
 struct GatherTokenSrc {   // row k -> token row of x or dy through row_pair, optionally weighted
     static constexpr bool kScaled = false;
     const uint16_t* base;
+    const uint16_t* zeros;   // ws.zeros: a zero row at least H long
     const int32_t* row_pair;
     int64_t seg0;
     int count, k, H, npairs;
+    __device__ __forceinline__ int pair(int kk) const { return kk < count ? row_pair[seg0 + kk] : -1; }
     __device__ __forceinline__ const uint16_t* chunk(int kk, int m) const {
-        if (kk >= count) return nullptr;
-        const int p = row_pair[seg0 + kk];
-        return (p >= 0 && p < npairs) ? base + static_cast<int64_t>(p / k) * H + m : nullptr;
+        const int p = pair(kk);
+        return (p >= 0 && p < npairs) ? base + static_cast<int64_t>(p / k) * H + m : zeros + m;
     }
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 struct WeightedGatherSrc : GatherTokenSrc {   // dO rows: topk_w[p] * dy[t]
     static constexpr bool kScaled = true;
     const float* topk_w;
-    __device__ __forceinline__ float scale(int kk) const { return topk_w[row_pair[seg0 + kk]]; }
+    __device__ __forceinline__ float scale(int kk) const {
+        const int p = pair(kk);
+        return (p >= 0 && p < npairs) ? topk_w[p] : 0.0f;
+    }
 };
 struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
     static constexpr bool kScaled = false;
     const uint16_t* base;
+    const uint16_t* zeros;   // ws.zeros: a zero row at least width long
     int64_t seg0;
     int count, width;
     __device__ __forceinline__ const uint16_t* chunk(int kk, int m) const {
-        return kk < count ? base + (seg0 + kk) * width + m : nullptr;
+        return kk < count ? base + (seg0 + kk) * width + m : zeros + m;
     }
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
@@ -605,21 +614,24 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed
     if constexpr (STREAM_A) lb.m_base = fixed * C::BN;
     else la.m_base = fixed * C::BM;
     if (nk <= 1) {
+        // Two tiles of the streamed operand are in flight (register slots 0 and 1) while tile t
+        // multiplies and stores: with one, every tile waited a whole memory latency for its
+        // operand.  The loads are unconditional (past the end they re-read the last tile, never
+        // stored to LDS), so the compiler's wait counts stay exact.
         char* lA = smem;
         char* lB = smem + C::A_BYTES;
-        aim(t0);
-        la.template load<0>(0, tid);
-        lb.template load<0>(0, tid);
-        la.template store<0>(lA, tid);
-        lb.template store<0>(lB, tid);
-        lds_barrier();
-        for (int t = t0; t < t1; ++t) {
-            const bool more = t + 1 < t1;
-            if (more) {
-                aim(t + 1);
-                if constexpr (STREAM_A) la.template load<0>(0, tid);
-                else lb.template load<0>(0, tid);
-            }
+        auto stream_load = [&](int t, auto slot) {
+            aim(min(t, t1 - 1));
+            if constexpr (STREAM_A) la.template load<decltype(slot)::value>(0, tid);
+            else lb.template load<decltype(slot)::value>(0, tid);
+        };
+        auto stream_store = [&](auto slot) {
+            lds_barrier();   // every wave's fragment reads of the previous tile are done
+            if constexpr (STREAM_A) la.template store<decltype(slot)::value>(lA, tid);
+            else lb.template store<decltype(slot)::value>(lB, tid);
+            lds_barrier();
+        };
+        auto compute = [&](int t) {
 #pragma unroll
             for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -628,12 +640,27 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed
                     for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
             if (nk == 1) mma_step<C>(lA, lB, acc, wm0, wn0, lane);
             store(t);
-            if (more) {
-                lds_barrier();   // every wave's fragment reads of tile t are done
-                if constexpr (STREAM_A) la.template store<0>(lA, tid);
-                else lb.template store<0>(lB, tid);
-                lds_barrier();
-            }
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        aim(t0);
+        la.template load<0>(0, tid);
+        lb.template load<0>(0, tid);
+        stream_load(t0 + 1, S1{});
+        la.template store<0>(lA, tid);
+        lb.template store<0>(lB, tid);
+        lds_barrier();
+        for (int t = t0; t < t1; t += 2) {
+            // slot 1 holds tile t + 1, slot 0 is free
+            stream_load(t + 2, S0{});
+            compute(t);
+            if (t + 1 >= t1) break;
+            stream_store(S1{});
+            // slot 0 holds tile t + 2, slot 1 is free
+            stream_load(t + 3, S1{});
+            compute(t + 1);
+            if (t + 2 >= t1) break;
+            stream_store(S0{});
         }
     } else {
         for (int t = t0; t < t1; ++t) {
@@ -679,11 +706,13 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad2_kernel(const uint16_t* __rest
 
     TRows<C::BM, C::NT, DirectRowSrc> la;
     la.src.base = ws.act;
+    la.src.zeros = ws.zeros;
     la.src.seg0 = wk.seg0;
     la.src.count = wk.count;
     la.src.width = I;
     TRows<C::BN, C::NT, WeightedGatherSrc> lb;
     lb.src.base = dy;
+    lb.src.zeros = ws.zeros;
     lb.src.row_pair = ws.row_pair;
     lb.src.seg0 = wk.seg0;
     lb.src.count = wk.count;
@@ -711,6 +740,7 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad1_kernel(const uint16_t* __rest
 
     TRows<C::BM, C::NT, GatherTokenSrc> la;
     la.src.base = x;
+    la.src.zeros = ws.zeros;
     la.src.row_pair = ws.row_pair;
     la.src.seg0 = wk.seg0;
     la.src.count = wk.count;
@@ -719,6 +749,7 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad1_kernel(const uint16_t* __rest
     la.src.npairs = d.T * d.k;
     TRows<C::BN, C::NT, DirectRowSrc> lb;
     lb.src.base = ws.dhgu;
+    lb.src.zeros = ws.zeros;
     lb.src.seg0 = wk.seg0;
     lb.src.count = wk.count;
     lb.src.width = N2;
