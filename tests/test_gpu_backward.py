@@ -297,3 +297,36 @@ def test_degenerate_routing_forward_and_backward(case):
         S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
         check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1 (%s)" % case)
         check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2 (%s)" % case)
+
+
+def test_backward_is_graph_capturable():
+    """The fused backward (dgrad with d(topk_w), dW2, dW1, dx) captured into a HIP graph replays
+    bit-identically to the eager call, with eager work and a stale workspace between replays."""
+    w = REDUCED[1]
+    d = mw.inputs(w, 15)
+    ns = run_forward_backward(w, d, 64)
+    ref = {n: getattr(ns, n).clone() for n in ("dx", "dtw", "dW1p", "dW2p")}
+    out = {n: torch.full_like(t, float("nan")) for n, t in ref.items()}
+    args = (ns.shape, ns.x, ns.dy, ns.wts, ns.W2p, ns.ws)
+    kw = dict(w1p=ns.W1p, dx=out["dx"], dtopk_w=out["dtw"])
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        moe.backward(*args, out["dW1p"], out["dW2p"], **kw)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            moe.backward(*args, out["dW1p"], out["dW2p"], **kw)
+    torch.cuda.current_stream().wait_stream(stream)
+    for i in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        stage = moe.ws_region(ns.ws, ns.shape, "stage")
+        stage.fill_(float("nan"))    # stale staging rows between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in ref:
+            assert torch.equal(out[n], ref[n]), "replay %d: %s differs" % (i, n)
+        moe.forward(ns.shape, ns.x, ns.idx, ns.wts, ns.W1p, ns.W2p, ns.ws, ns.y)   # eager work between
+        torch.cuda.synchronize()
