@@ -176,28 +176,22 @@ hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s) {
 // sum their weighted fp32 L2 rows from ws.stage in slot order and store bf16.  Tokens with one
 // local pair were written by the L2 epilogue and are left alone.
 // ---------------------------------------------------------------------------------------------
+// One wave per token: lanes [0, k) read the token's pair rows at once and a ballot lists its local
+// pairs in slot order, so a token costs one dependent load before its stage rows stream.
 __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws ws, uint16_t* __restrict__ y) {
-    __shared__ int s_rows[32];
-    __shared__ int s_n;
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * (kEwThreads / 64);
     const int v8 = d.H / 8;
-    for (int t = blockIdx.x; t < d.T; t += gridDim.x) {
-        const int nloc = ws.tok_nloc[t];   // uniform per block
-        if (nloc == 1) continue;
-        __syncthreads();   // the previous token's s_rows are no longer read
-        if (threadIdx.x == 0) {
-            int n = 0;
-            for (int j = 0; j < d.k; ++j) {
-                const int r = ws.pair_row[static_cast<int64_t>(t) * d.k + j];
-                if (r >= 0) s_rows[n++] = r;
-            }
-            s_n = n;
-        }
-        __syncthreads();
-        const int n = s_n;
-        for (int c = threadIdx.x; c < v8; c += blockDim.x) {
+    for (int t = blockIdx.x * (kEwThreads / 64) + (threadIdx.x >> 6); t < d.T; t += waves) {
+        int r = -1;
+        if (lane < d.k) r = ws.pair_row[static_cast<int64_t>(t) * d.k + lane];
+        const uint64_t local = __ballot(r >= 0 && r < ws.rows_cap);
+        if (__popcll(local) == 1) continue;   // the GEMM epilogue stored this token's only row
+        for (int c = lane; c < v8; c += 64) {
             float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            for (int i = 0; i < n; ++i) {
-                const float4* src = reinterpret_cast<const float4*>(ws.stage + static_cast<int64_t>(s_rows[i]) * d.H + 8 * c);
+            for (uint64_t m = local; m; m &= m - 1) {   // local pairs in slot order
+                const int row = __shfl(r, __ffsll(static_cast<unsigned long long>(m)) - 1);
+                const float4* src = reinterpret_cast<const float4*>(ws.stage + static_cast<int64_t>(row) * d.H + 8 * c);
                 const float4 lo = src[0], hi = src[1];
                 acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
                 acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
@@ -209,8 +203,8 @@ __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws w
 
 hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s) {
     if (d.T <= 0) return hipSuccess;
-    const int cap = device_cu_count() * 8;
-    combine_finish_kernel<<<d.T < cap ? d.T : cap, kEwThreads, 0, s>>>(d, ws, y);
+    const int cap = device_cu_count() * 8, want = (d.T + kEwThreads / 64 - 1) / (kEwThreads / 64);
+    combine_finish_kernel<<<want < cap ? want : cap, kEwThreads, 0, s>>>(d, ws, y);
     return hipGetLastError();
 }
 
