@@ -52,9 +52,13 @@ def configure(lib):
     lib.oracle_backward_rows.argtypes = [i32] * 7 + [P] * 6 + [P, i32, P, P]
     lib.oracle_backward.argtypes = [i32] * 7 + [P] * 6 + [P, i32, P, P]
     lib.oracle_backward_tokens.argtypes = [i32] * 7 + [P] * 6 + [P, i32, P, P]
+    lib.oracle_mx_quantize.argtypes = [i32, i64, P, P, P]
+    lib.oracle_mx_dequantize.argtypes = [i32, i64, P, P, P]
+    lib.oracle_forward_mx.argtypes = [i32] * 7 + [P] * 8 + [ctypes.c_double, i32, P, i32, P]
     for f in ("oracle_route", "oracle_forward", "oracle_l1_rows", "oracle_swiglu",
               "oracle_swiglu_bwd", "oracle_backward_rows", "oracle_backward",
-              "oracle_backward_tokens"):
+              "oracle_backward_tokens", "oracle_mx_quantize", "oracle_mx_dequantize",
+              "oracle_forward_mx"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -207,3 +211,48 @@ def backward_tokens(x, topk_idx, topk_w, W1, W2, dy, E: int, e_lo: int = 0, toke
     if rc != 0:
         raise MemoryError("oracle_backward_tokens failed: %d" % rc)
     return dx, dw
+
+
+MX_FP8, MX_FP4 = 0, 1
+
+
+def mx_quantize(fmt: int, values):
+    """Cast values (last axis a multiple of 32) in blocks of 32 along the last axis: codes (uint8,
+    one code per byte, same shape) and UE8M0 scale bytes (shape [..., n / 32]).  fmt: MX_FP8
+    (E4M3) or MX_FP4 (E2M1)."""
+    v = _c(values, np.float64)
+    codes = np.zeros(v.shape, np.uint8)
+    scales = np.zeros(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    if _load().oracle_mx_quantize(fmt, v.size, _p(v), _p(codes), _p(scales)) != 0:
+        raise ValueError("mx_quantize: the last axis must be a multiple of 32")
+    return codes, scales
+
+
+def mx_dequantize(fmt: int, codes, scales) -> np.ndarray:
+    c, sc = _c(codes, np.uint8), _c(scales, np.uint8)
+    v = np.zeros(c.shape, np.float64)
+    if _load().oracle_mx_dequantize(fmt, c.size, _p(c), _p(sc), _p(v)) != 0:
+        raise ValueError("mx_dequantize: the last axis must be a multiple of 32")
+    return v
+
+
+def forward_mx(x_codes, x_scales, topk_idx, topk_w, w1_codes, w1_scales, w2_codes, w2_scales, E: int,
+               e_lo: int = 0, clamp: float = 10.0, quant_act: bool = True, tokens=None) -> np.ndarray:
+    """MX forward (fp64) for the given tokens on quantized inputs: x [T, H] FP8 codes + [T, H/32]
+    scales; W1 as [EL, 2I, H] FP4 codes + [EL, 2I, H/32] scales (column-major: blocks along H);
+    W2 as [EL, H, I] codes + [EL, H, I/32] scales.  clamp <= 0 disables the SwiGLU clamp."""
+    xc, xs = _c(x_codes, np.uint8), _c(x_scales, np.uint8)
+    idx, w = _c(topk_idx, np.int32), _c(topk_w, np.float32)
+    w1c, w1s, w2c, w2s = (_c(a, np.uint8) for a in (w1_codes, w1_scales, w2_codes, w2_scales))
+    T, H = xc.shape
+    EL, N, _ = w1c.shape
+    I, k = N // 2, idx.shape[1]
+    assert w2c.shape == (EL, H, I) and xs.shape == (T, H // 32)
+    tok = _c(np.arange(T) if tokens is None else tokens, np.int32)
+    y = np.zeros((len(tok), H), np.float64)
+    rc = _load().oracle_forward_mx(T, H, I, E, e_lo, EL, k, _p(xc), _p(xs), _p(idx), _p(w), _p(w1c), _p(w1s),
+                                   _p(w2c), _p(w2s), float(clamp), int(bool(quant_act)), _p(tok), len(tok),
+                                   _p(y))
+    if rc != 0:
+        raise MemoryError("oracle_forward_mx failed: %d" % rc)
+    return y

@@ -445,3 +445,180 @@ int oracle_backward_tokens(int T, int H, int I, int E, int e_lo, int EL, int k,
     }
     return err;
 }
+
+/*
+ * ---------------------------------------------------------------------------------------------
+ * MX variant: FP8 activations and FP4 weights with power-of-two block scales ("How Mega MoE
+ * Overlaps ..." page, Code Example: activations cast per token to FP8 with UE8M0 scale factors
+ * over groups of 32 along K; weights transformed to FP4; the fused call takes an activation clamp
+ * of 10).  Readings where the page only names the calls:
+ *   - A block of 32 consecutive values along K shares one scale 2^E, E an integer in [-127, 127]
+ *     (the UE8M0 byte is E + 127).  E is the smallest integer with amax <= fmax * 2^E, where amax is
+ *     the block's largest magnitude and fmax the element format's largest value (448 for FP8 E4M3,
+ *     6 for FP4 E2M1), so no element saturates; a block of zeros takes E = 0.
+ *   - Elements are v / 2^E rounded to the nearest value of the format, ties to the even mantissa
+ *     (OCP FP8 E4M3: 1 sign, 4 exponent bits of bias 7, 3 mantissa bits, subnormals, largest 448;
+ *     OCP FP4 E2M1: 1 sign, 2 exponent bits of bias 1, 1 mantissa bit, values 0, 0.5, 1, 1.5, 2,
+ *     3, 4, 6).  A value that rounds to zero keeps its sign.
+ *   - The SwiGLU inputs are clamped: gate to at most `clamp`, up to [-clamp, clamp].
+ *   - The SwiGLU output is cast again, per row and group of 32 along I, to FP8 for L2.
+ * ---------------------------------------------------------------------------------------------
+ */
+static double pow2i(int e) { return ldexp(1.0, e); }
+
+/* Value of exponent field e_field and mantissa field m of a format with `mbits` mantissa bits and
+ * exponent bias `bias` (e_field 0: subnormal). */
+static double fmt_value(int e_field, int m, int mbits, int bias) {
+    const double frac = (double)m / (double)(1 << mbits);
+    return e_field == 0 ? frac * pow2i(1 - bias) : (1.0 + frac) * pow2i(e_field - bias);
+}
+
+/* Nearest code (sign-magnitude: sign << (ebits + mbits) | e << mbits | m) of a finite value v whose
+ * magnitude does not exceed the format's largest value; ties to the even mantissa. */
+static int fmt_encode(double v, int ebits, int mbits, int bias, double vmax) {
+    const int sign = v < 0 || (v == 0 && signbit(v));
+    const double a = fabs(v) > vmax ? vmax : fabs(v);
+    int best = 0;
+    double best_err = INFINITY;
+    const int ncode = 1 << (ebits + mbits);
+    for (int c = 0; c < ncode; ++c) {
+        const int e = c >> mbits, m = c & ((1 << mbits) - 1);
+        const double x = fmt_value(e, m, mbits, bias);
+        if (x > vmax) continue;
+        const double err = fabs(x - a);
+        /* codes are scanned in increasing value, so an equal error is the upper neighbour: it wins
+         * the tie only when its mantissa is even */
+        if (err < best_err || (err == best_err && (m & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (sign << (ebits + mbits)) | best;
+}
+
+static double fmt_decode(int code, int ebits, int mbits, int bias) {
+    const int mag = code & ((1 << (ebits + mbits)) - 1);
+    const double x = fmt_value(mag >> mbits, mag & ((1 << mbits) - 1), mbits, bias);
+    return (code >> (ebits + mbits)) & 1 ? -x : x;
+}
+
+/* Block exponent: the smallest E with amax <= vmax * 2^E, in [-127, 127]; 0 for amax == 0. */
+static int block_exponent(double amax, double vmax) {
+    if (!(amax > 0)) return 0;
+    int E = (int)ceil(log2(amax / vmax));
+    while (E > -127 && amax <= vmax * pow2i(E - 1)) --E;   /* exact correction of log2 rounding */
+    while (E < 127 && amax > vmax * pow2i(E)) ++E;
+    return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+/* fmt: 0 = FP8 E4M3, 1 = FP4 E2M1.  Quantizes n values (n a multiple of 32) in blocks of 32:
+ * codes[n] (one code per byte), scales[n / 32] (UE8M0 bytes, E + 127). */
+int oracle_mx_quantize(int fmt, int64_t n, const double* v, uint8_t* codes, uint8_t* scales) {
+    const int ebits = fmt == 0 ? 4 : 2, mbits = fmt == 0 ? 3 : 1, bias = fmt == 0 ? 7 : 1;
+    const double vmax = fmt == 0 ? 448.0 : 6.0;
+    if (n % 32) return -1;
+    for (int64_t b = 0; b < n / 32; ++b) {
+        double amax = 0;
+        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[b * 32 + i]));
+        const int E = block_exponent(amax, vmax);
+        scales[b] = (uint8_t)(E + 127);
+        for (int i = 0; i < 32; ++i)
+            codes[b * 32 + i] = (uint8_t)fmt_encode(v[b * 32 + i] / pow2i(E), ebits, mbits, bias, vmax);
+    }
+    return 0;
+}
+
+/* Value of a code times its block scale. */
+int oracle_mx_dequantize(int fmt, int64_t n, const uint8_t* codes, const uint8_t* scales, double* v) {
+    const int ebits = fmt == 0 ? 4 : 2, mbits = fmt == 0 ? 3 : 1, bias = fmt == 0 ? 7 : 1;
+    if (n % 32) return -1;
+    for (int64_t i = 0; i < n; ++i)
+        v[i] = fmt_decode(codes[i], ebits, mbits, bias) * pow2i((int)scales[i / 32] - 127);
+    return 0;
+}
+
+/*
+ * MX forward for a list of tokens, on already quantized inputs:
+ *   x_codes [T, H] FP8 codes with x_scales [T, H/32] (blocks along H);
+ *   w1_codes [EL, 2I, H] FP4 codes (one per byte) with w1_scales [EL, 2I, H/32]: column n of the
+ *     [gate | up] output, blocks along the reduction index H;
+ *   w2_codes [EL, H, I] with w2_scales [EL, H, I/32]: output column m, blocks along I.
+ *   h = x . W1 on the dequantized values; a = silu(min(g, clamp)) * clamp(u, -clamp, clamp);
+ *   a cast to FP8 per group of 32 along I when quant_act is nonzero; o = a . W2;
+ *   y[t] = sum over local pairs of w * o.  clamp <= 0 disables the clamp.  y is [ntok, H] fp64.
+ */
+int oracle_forward_mx(int T, int H, int I, int E, int e_lo, int EL, int k, const uint8_t* x_codes,
+                      const uint8_t* x_scales, const int32_t* topk_idx, const float* topk_w,
+                      const uint8_t* w1_codes, const uint8_t* w1_scales, const uint8_t* w2_codes,
+                      const uint8_t* w2_scales, double clamp, int quant_act, const int32_t* tokens,
+                      int ntok, double* y) {
+    if (H % 32 || I % 32 || k <= 0) return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+        double* wr = (double*)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+        double* h = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        uint8_t* ac = (uint8_t*)malloc((size_t)I);
+        uint8_t* as = (uint8_t*)malloc((size_t)I / 32);
+        double* o = (double*)malloc(sizeof(double) * (size_t)H);
+        const int ok = xr && wr && h && a && ac && as && o;
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < ntok; ++i) {
+            if (!ok) continue;
+            {
+                const int t = tokens[i];
+                double* acc = y + (size_t)i * H;
+                for (int m = 0; m < H; ++m) acc[m] = 0.0;
+                if (t < 0 || t >= T) continue;
+                oracle_mx_dequantize(0, H, x_codes + (size_t)t * H, x_scales + (size_t)t * (H / 32), xr);
+                for (int j = 0; j < k; ++j) {
+                    const int e = local_expert(topk_idx[(int64_t)t * k + j], E, e_lo, EL);
+                    if (e < 0) continue;
+                    for (int n = 0; n < 2 * I; ++n) {
+                        const size_t row = ((size_t)e * 2 * I + n);
+                        oracle_mx_dequantize(1, H, w1_codes + row * H, w1_scales + row * (H / 32), wr);
+                        double s = 0.0;
+                        for (int q = 0; q < H; ++q) s += xr[q] * wr[q];
+                        h[n] = s;
+                    }
+                    for (int c = 0; c < I; ++c) {
+                        double g = h[c], u = h[I + c];
+                        if (clamp > 0) {
+                            if (g > clamp) g = clamp;
+                            if (u > clamp) u = clamp;
+                            if (u < -clamp) u = -clamp;
+                        }
+                        a[c] = silu(g) * u;
+                    }
+                    if (quant_act) {
+                        oracle_mx_quantize(0, I, a, ac, as);
+                        oracle_mx_dequantize(0, I, ac, as, a);
+                    }
+                    for (int m = 0; m < H; ++m) {
+                        const size_t row = ((size_t)e * H + m);
+                        oracle_mx_dequantize(1, I, w2_codes + row * I, w2_scales + row * (I / 32), wr);
+                        double s = 0.0;
+                        for (int c = 0; c < I; ++c) s += a[c] * wr[c];
+                        o[m] = s;
+                    }
+                    const double w = (double)topk_w[(int64_t)t * k + j];
+                    for (int m = 0; m < H; ++m) acc[m] += w * o[m];
+                }
+            }
+        }
+        free(xr);
+        free(wr);
+        free(h);
+        free(a);
+        free(ac);
+        free(as);
+        free(o);
+    }
+    return err;
+}
