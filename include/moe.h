@@ -250,6 +250,38 @@ int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* 
                      size_t ws_bytes, uint16_t* dw1p, uint16_t* dw2p, uint16_t* dx,
                      float* dtopk_w, void* stream);
 
+/*
+ * MX variant ("How Mega MoE Overlaps ..." page, Code Example: FP8 activations cast per token with
+ * UE8M0 scale factors over groups of 32 along K, weights transformed to FP4, a fused forward with
+ * an activation clamp).  Formats (OCP microscaling): FP8 E4M3 (largest 448), FP4 E2M1 (values 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6); every 32 consecutive values along K share a scale 2^E stored as the
+ * byte E + 127, E the smallest integer with max|v| <= (largest value) * 2^E (0 for a block of
+ * zeros); values are v / 2^E rounded to nearest, ties to the even mantissa.
+ *
+ * FP8 cast of bf16 rows (the per-token cast):
+ *   x      [device] bf16 [rows, cols], cols a multiple of 32
+ *   codes  [device] uint8 [rows, cols]       FP8 E4M3 codes
+ *   scales [device] uint8 [rows, cols / 32]  UE8M0 bytes
+ */
+int32_t moe_mx_cast_fp8(int64_t rows, int32_t cols, const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                        void* stream);
+
+/*
+ * One-time FP4 transform of the weights (the weight transform of the page's example), from the
+ * logical w1 [EL, H, 2I] / w2 [EL, I, H] bf16 (each output column quantized in blocks of 32 along
+ * its reduction index) into the operand layout of the block-scaled MFMA:
+ *   w1q [device] uint8, EL * 2I * H / 2 bytes;  w1s [device] uint8, EL * 2I * H / 32 bytes
+ *   w2q [device] uint8, EL * H * I / 2 bytes;   w2s [device] uint8, EL * H * I / 32 bytes
+ * Per expert (N output columns, reduction length K; N = 2I, K = H for W1 and N = H, K = I for W2;
+ * the expert's data starts at e * N * K / 2, its scales at e * N * K / 32), the data of column n and
+ * reduction index k is nibble k % 32 (low nibble first) of the 16 bytes at
+ *     (((n / 32) * (K / 64) + k / 64) * 64 + n % 32 + 32 * ((k % 64) / 32)) * 16
+ * and its block's scale the byte at ((n / 32) * (K / 64) + k / 64) * 64 + n % 32 + 32 * ((k % 64) / 32).
+ * For W1, n is the packed L1 column (moe_pack_weights).  Either triple may be NULL.
+ */
+int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2, uint8_t* w1q,
+                            uint8_t* w1s, uint8_t* w2q, uint8_t* w2s, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

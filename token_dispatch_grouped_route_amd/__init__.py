@@ -27,6 +27,7 @@ ENTRY_POINTS = (
     "moe_pack_weights", "moe_unpack_weights", "moe_route_prologue", "moe_dispatch_gemm1", "moe_swiglu",
     "moe_gemm2_combine", "moe_forward", "moe_bwd_gemm2_dgrad", "moe_swiglu_bwd",
     "moe_bwd_gemm1_dgrad_combine", "moe_wgrad2", "moe_wgrad1", "moe_backward",
+    "moe_mx_cast_fp8", "moe_mx_pack_weights",
 )
 
 
@@ -79,6 +80,8 @@ def lib():
         L.moe_wgrad2.argtypes = [S, P, P, P, ctypes.c_size_t, P, P]
         L.moe_wgrad1.argtypes = [S, P, P, ctypes.c_size_t, P, P]
         L.moe_backward.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P, P, P, P, P]
+        L.moe_mx_cast_fp8.argtypes = [ctypes.c_int64, i32, P, P, P, P]
+        L.moe_mx_pack_weights.argtypes = [S, P, P, P, P, P, P, P]
         for n in ENTRY_POINTS[2:]:
             if n != "moe_workspace_bytes":
                 getattr(L, n).restype = i32
@@ -271,3 +274,36 @@ def backward(shape, x, dy, topk_w, w2p, ws, dw1p, dw2p, w1p=None, dx=None, dtopk
                               _ptr(dw1p, torch.bfloat16, "dw1p"), _ptr(dw2p, torch.bfloat16, "dw2p"),
                               _ptr(dx, torch.bfloat16, "dx"), _ptr(dtopk_w, torch.float32, "dtopk_w"),
                               _stream(stream)), "moe_backward")
+
+
+# ------------------------------------------------------------------------------------------------
+# MX variant: FP8 activations, FP4 weights, power-of-two scales per 32 values along K
+# ------------------------------------------------------------------------------------------------
+def mx_cast_fp8(x, codes=None, scales=None, stream=None):
+    """FP8 E4M3 codes (uint8, x's shape) and UE8M0 scale bytes (uint8, [rows, cols / 32]) of bf16 x."""
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)
+    _check(lib().moe_mx_cast_fp8(rows, cols, _ptr(x, torch.bfloat16, "x"), _ptr(codes, torch.uint8, "codes"),
+                                 _ptr(scales, torch.uint8, "scales"), _stream(stream)), "moe_mx_cast_fp8")
+    return codes, scales
+
+
+def mx_packed_sizes(shape: Shape):
+    """Byte sizes of (w1q, w1s, w2q, w2s) of moe_mx_pack_weights."""
+    n1 = shape.EL * 2 * shape.I * shape.H
+    n2 = shape.EL * shape.H * shape.I
+    return n1 // 2, n1 // 32, n2 // 2, n2 // 32
+
+
+def mx_alloc_packed(shape: Shape, device="cuda"):
+    return tuple(torch.empty(n, dtype=torch.uint8, device=device) for n in mx_packed_sizes(shape))
+
+
+def mx_pack_weights(shape, w1, w2, w1q, w1s, w2q, w2s, stream=None):
+    _check(lib().moe_mx_pack_weights(ctypes.byref(shape), _ptr(w1, torch.bfloat16, "w1"),
+                                     _ptr(w2, torch.bfloat16, "w2"), _ptr(w1q, torch.uint8, "w1q"),
+                                     _ptr(w1s, torch.uint8, "w1s"), _ptr(w2q, torch.uint8, "w2q"),
+                                     _ptr(w2s, torch.uint8, "w2s"), _stream(stream)), "moe_mx_pack_weights")

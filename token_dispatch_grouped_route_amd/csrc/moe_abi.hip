@@ -339,4 +339,26 @@ int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* 
     return launched(e);
 }
 
+int32_t moe_mx_cast_fp8(int64_t rows, int32_t cols, const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                        void* stream) {
+    if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_SHAPE;
+    if (rows > 0 && (!x || !codes || !scales)) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes)) return MOE_ERR_ALIGN;
+    if (!is_gfx950()) return MOE_ERR_DEVICE;
+    return launched(launch_mx_cast_fp8(rows, cols, x, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2, uint8_t* w1q,
+                            uint8_t* w1s, uint8_t* w2q, uint8_t* w2s, void* stream) {
+    const int32_t st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if ((w1 == nullptr) != (w1q == nullptr) || (w1 == nullptr) != (w1s == nullptr) ||
+        (w2 == nullptr) != (w2q == nullptr) || (w2 == nullptr) != (w2s == nullptr))
+        return MOE_ERR_NULL;
+    if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1q) || !aligned16(w2q)) return MOE_ERR_ALIGN;
+    if (!is_gfx950()) return MOE_ERR_DEVICE;
+    const Dims d{shape->T, shape->H, shape->I, shape->E, shape->e_lo, shape->EL, shape->k, shape->block_m};
+    return launched(launch_mx_pack(d, w1, w2, w1q, w1s, w2q, w2s, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -104,6 +104,11 @@ hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w,
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p,
                          hipStream_t s);
 
+hipError_t launch_mx_cast_fp8(int64_t rows, int cols, const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+hipError_t launch_mx_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, uint8_t* w1q, uint8_t* w1s,
+                          uint8_t* w2q, uint8_t* w2s, hipStream_t s);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
