@@ -282,6 +282,21 @@ int32_t moe_mx_cast_fp8(int64_t rows, int32_t cols, const uint16_t* x, uint8_t* 
 int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2, uint8_t* w1q,
                             uint8_t* w1s, uint8_t* w2q, uint8_t* w2s, void* stream);
 
+/*
+ * Fused MX forward: the routing prologue, the dispatch gather of FP8 x rows with L1 on the
+ * block-scaled MFMA (FP8 x FP4, fp32 accumulation), SwiGLU with its inputs clamped (gate to at
+ * most clamp, up to [-clamp, clamp]; clamp <= 0: no clamp), the activation rows cast to FP8 per
+ * group of 32, L2 on the block-scaled MFMA, and the combine of moe_gemm2_combine (y bf16).
+ *   xq [device] uint8 [T, H], xs [device] uint8 [T, H / 32]  (moe_mx_cast_fp8 of x)
+ *   w1q, w1s, w2q, w2s [device]                              (moe_mx_pack_weights)
+ *   topk_idx, topk_w, ws, y as for moe_forward.  The act region of ws holds the FP8 activation
+ *   codes [R_max, I] followed by their scale bytes [R_max, I / 32].
+ * H and I must be multiples of 256 and 128.
+ */
+int32_t moe_forward_mx(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs, const int32_t* topk_idx,
+                       const float* topk_w, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
+                       const uint8_t* w2s, float clamp, void* ws, size_t ws_bytes, uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,9 @@ WORKLOADS = [
     # the rows one GPU of the pages' 8-GPU DeepSeek-V3 run receives: 8 x 8192 tokens routed
     # top-8 over 256 experts, 32 of them local (about 65 536 local rows), all resident here
     Workload("dsv3_page_share_fwd", T=65536, H=7168, I=2048, E=256, EL=32, k=8),
+    # the pages' low-precision run (FP8 activations, FP4 weights): 384 experts, top-6, 4096 tokens
+    # per GPU, the 48 experts of one GPU of eight
+    Workload("wide_share_mx_fwd", T=4096, H=7168, I=3072, E=384, EL=48, k=6),
 ]
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))

@@ -55,10 +55,12 @@ def configure(lib):
     lib.oracle_mx_quantize.argtypes = [i32, i64, P, P, P]
     lib.oracle_mx_dequantize.argtypes = [i32, i64, P, P, P]
     lib.oracle_forward_mx.argtypes = [i32] * 7 + [P] * 8 + [ctypes.c_double, i32, P, i32, P]
+    lib.oracle_mx_l1_rows.argtypes = [i32] * 7 + [P] * 5 + [ctypes.c_double, P, i32, P]
+    lib.oracle_mx_l2_rows.argtypes = [i32] * 3 + [P] * 3 + [i32, P, P, P]
     for f in ("oracle_route", "oracle_forward", "oracle_l1_rows", "oracle_swiglu",
               "oracle_swiglu_bwd", "oracle_backward_rows", "oracle_backward",
               "oracle_backward_tokens", "oracle_mx_quantize", "oracle_mx_dequantize",
-              "oracle_forward_mx"):
+              "oracle_forward_mx", "oracle_mx_l1_rows", "oracle_mx_l2_rows"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -256,3 +258,30 @@ def forward_mx(x_codes, x_scales, topk_idx, topk_w, w1_codes, w1_scales, w2_code
     if rc != 0:
         raise MemoryError("oracle_forward_mx failed: %d" % rc)
     return y
+
+
+def mx_l1_rows(x_codes, x_scales, topk_idx, w1_codes, w1_scales, E: int, e_lo: int, pairs, clamp=10.0):
+    """MX L1 rows a [n, I] (fp64, before the FP8 cast of the activation) for given pair ids."""
+    xc, xs, idx = _c(x_codes, np.uint8), _c(x_scales, np.uint8), _c(topk_idx, np.int32)
+    w1c, w1s = _c(w1_codes, np.uint8), _c(w1_scales, np.uint8)
+    T, H = xc.shape
+    EL, N, _ = w1c.shape
+    pr = _c(pairs, np.int32)
+    a = np.zeros((len(pr), N // 2), np.float64)
+    rc = _load().oracle_mx_l1_rows(T, H, N // 2, E, e_lo, EL, idx.shape[1], _p(xc), _p(xs), _p(idx), _p(w1c),
+                                   _p(w1s), float(clamp), _p(pr), len(pr), _p(a))
+    if rc != 0:
+        raise MemoryError("oracle_mx_l1_rows failed: %d" % rc)
+    return a
+
+
+def mx_l2_rows(w2_codes, w2_scales, experts, act_codes, act_scales):
+    """MX L2 rows o [n, H] (fp64, unweighted) of given FP8 activation rows and their local experts."""
+    w2c, w2s = _c(w2_codes, np.uint8), _c(w2_scales, np.uint8)
+    EL, H, I = w2c.shape
+    ex, ac, as_ = _c(experts, np.int32), _c(act_codes, np.uint8), _c(act_scales, np.uint8)
+    o = np.zeros((len(ex), H), np.float64)
+    rc = _load().oracle_mx_l2_rows(H, I, EL, _p(w2c), _p(w2s), _p(ex), len(ex), _p(ac), _p(as_), _p(o))
+    if rc != 0:
+        raise MemoryError("oracle_mx_l2_rows failed: %d" % rc)
+    return o

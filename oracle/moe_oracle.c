@@ -517,6 +517,7 @@ int oracle_mx_quantize(int fmt, int64_t n, const double* v, uint8_t* codes, uint
     const int ebits = fmt == 0 ? 4 : 2, mbits = fmt == 0 ? 3 : 1, bias = fmt == 0 ? 7 : 1;
     const double vmax = fmt == 0 ? 448.0 : 6.0;
     if (n % 32) return -1;
+#pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < n / 32; ++b) {
         double amax = 0;
         for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[b * 32 + i]));
@@ -532,6 +533,7 @@ int oracle_mx_quantize(int fmt, int64_t n, const double* v, uint8_t* codes, uint
 int oracle_mx_dequantize(int fmt, int64_t n, const uint8_t* codes, const uint8_t* scales, double* v) {
     const int ebits = fmt == 0 ? 4 : 2, mbits = fmt == 0 ? 3 : 1, bias = fmt == 0 ? 7 : 1;
     if (n % 32) return -1;
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i)
         v[i] = fmt_decode(codes[i], ebits, mbits, bias) * pow2i((int)scales[i / 32] - 127);
     return 0;
@@ -619,6 +621,100 @@ int oracle_forward_mx(int T, int H, int I, int E, int e_lo, int EL, int k, const
         free(ac);
         free(as);
         free(o);
+    }
+    return err;
+}
+
+/* MX L1 rows for a list of pair ids: a = silu(min(g, clamp)) * clamp(u, -clamp, clamp) of the
+ * dequantized x row times the dequantized W1 (before the FP8 cast of the activation); [np, I] fp64,
+ * zero for a pair that is not local.  Layouts as in oracle_forward_mx. */
+int oracle_mx_l1_rows(int T, int H, int I, int E, int e_lo, int EL, int k, const uint8_t* x_codes,
+                      const uint8_t* x_scales, const int32_t* topk_idx, const uint8_t* w1_codes,
+                      const uint8_t* w1_scales, double clamp, const int32_t* pairs, int np, double* a_out) {
+    if (H % 32 || I % 32 || k <= 0) return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+        double* wr = (double*)malloc(sizeof(double) * (size_t)H);
+        const int ok = xr && wr;
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < np; ++i) {
+            if (!ok) continue;
+            {
+                double* a = a_out + (size_t)i * I;
+                for (int c = 0; c < I; ++c) a[c] = 0.0;
+                const int64_t p = pairs[i];
+                const int e = (p >= 0 && p < (int64_t)T * k) ? local_expert(topk_idx[p], E, e_lo, EL) : -1;
+                if (e < 0) continue;
+                const int64_t t = p / k;
+                oracle_mx_dequantize(0, H, x_codes + (size_t)t * H, x_scales + (size_t)t * (H / 32), xr);
+                for (int c = 0; c < I; ++c) {
+                    double h2[2];
+                    for (int half = 0; half < 2; ++half) {
+                        const size_t row = (size_t)e * 2 * I + (size_t)half * I + c;
+                        oracle_mx_dequantize(1, H, w1_codes + row * H, w1_scales + row * (H / 32), wr);
+                        double s = 0.0;
+                        for (int q = 0; q < H; ++q) s += xr[q] * wr[q];
+                        h2[half] = s;
+                    }
+                    double g = h2[0], u = h2[1];
+                    if (clamp > 0) {
+                        if (g > clamp) g = clamp;
+                        if (u > clamp) u = clamp;
+                        if (u < -clamp) u = -clamp;
+                    }
+                    a[c] = silu(g) * u;
+                }
+            }
+        }
+        free(xr);
+        free(wr);
+    }
+    return err;
+}
+
+/* MX L2 rows: o = (dequantized FP8 activation row) . (dequantized W2 of expert experts[i]) for np
+ * given activation rows (codes [np, I], scales [np, I/32]); [np, H] fp64, unweighted; a row whose
+ * expert is outside [0, EL) is zero. */
+int oracle_mx_l2_rows(int H, int I, int EL, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                      const int32_t* experts, int np, const uint8_t* act_codes, const uint8_t* act_scales,
+                      double* o_out) {
+    if (H % 32 || I % 32) return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* ar = (double*)malloc(sizeof(double) * (size_t)I);
+        double* wr = (double*)malloc(sizeof(double) * (size_t)I);
+        const int ok = ar && wr;
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < np; ++i) {
+            if (!ok) continue;
+            {
+                double* o = o_out + (size_t)i * H;
+                for (int m = 0; m < H; ++m) o[m] = 0.0;
+                const int e = experts[i];
+                if (e < 0 || e >= EL) continue;
+                oracle_mx_dequantize(0, I, act_codes + (size_t)i * I, act_scales + (size_t)i * (I / 32), ar);
+                for (int m = 0; m < H; ++m) {
+                    const size_t row = (size_t)e * H + m;
+                    oracle_mx_dequantize(1, I, w2_codes + row * I, w2_scales + row * (I / 32), wr);
+                    double s = 0.0;
+                    for (int c = 0; c < I; ++c) s += ar[c] * wr[c];
+                    o[m] = s;
+                }
+            }
+        }
+        free(ar);
+        free(wr);
     }
     return err;
 }

@@ -8,7 +8,7 @@ import torch
 import moe_workloads as mw
 import oracle
 import token_dispatch_grouped_route_amd as moe
-from gpu_helpers import bf16_dev
+from gpu_helpers import bf16_dev, check_bf16, f64_host, rel_max_err
 
 pytestmark = pytest.mark.gpu
 FP8, FP4 = oracle.MX_FP8, oracle.MX_FP4
@@ -80,3 +80,196 @@ def test_fp4_pack_bit_exact_in_documented_layout(shape):
         rc, rs = oracle.mx_quantize(FP4, Wt)
         assert np.array_equal(scales, rs)
         assert np.array_equal(codes, rc)
+
+
+REDUCED = [
+    mw.Workload("mx_shard", T=333, H=256, I=256, E=12, EL=6, k=3, e_lo=3),
+    mw.Workload("mx_all_local", T=500, H=512, I=128, E=8, EL=8, k=4),
+]
+U32 = 2.0 ** -24          # unit roundoff of fp32
+FP8_MAX = 448.0
+
+
+def oracle_weight_codes(W, experts):
+    """The oracle's FP4 codes and scales of bf16 weights W [EL, K, N] in [EL, N, K] order, for the
+    listed experts only (zero elsewhere)."""
+    EL, K, N = W.shape
+    codes, scales = np.zeros((EL, N, K), np.uint8), np.zeros((EL, N, K // 32), np.uint8)
+    for e in experts:
+        Wt = np.ascontiguousarray(mw.bf16_bits_to_f32(W[e]).astype(np.float64).T)
+        codes[e], scales[e] = oracle.mx_quantize(FP4, Wt)
+    return codes, scales
+
+
+def mx_layer(w, d, bm, x_scale=1.0, experts=None):
+    """Device inputs of the MX forward: x cast on the GPU, weights packed on the GPU; the oracle's
+    codes of the same inputs (bit-identical, by the tests above), for the given local experts
+    (all by default)."""
+    s = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=bm, e_lo=w.e_lo)
+    xbits = d["x"] if x_scale == 1.0 else mw.f32_to_bf16_bits(mw.bf16_bits_to_f32(d["x"]) * x_scale)
+    xq, xs = moe.mx_cast_fp8(bf16_dev(xbits))
+    w1q, w1s, w2q, w2s = moe.mx_alloc_packed(s)
+    moe.mx_pack_weights(s, bf16_dev(d["W1"]), bf16_dev(d["W2"]), w1q, w1s, w2q, w2s)
+    ws = moe.alloc_workspace(s)
+    y = torch.full((w.T, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    idx = torch.from_numpy(np.ascontiguousarray(d["topk_idx"], np.int32)).cuda()
+    wts = torch.from_numpy(np.ascontiguousarray(d["topk_weights"], np.float32)).cuda()
+    oc = oracle.mx_quantize(FP8, mw.bf16_bits_to_f32(xbits).astype(np.float64))
+    experts = range(w.EL) if experts is None else experts
+    ref_codes = oc + oracle_weight_codes(d["W1"], experts) + oracle_weight_codes(d["W2"], experts)
+    return s, (xq, xs, idx, wts, w1q, w1s, w2q, w2s, ws, y), ref_codes
+
+
+def gpu_act(ws, s, w):
+    """The FP8 activation rows the MX forward leaves in the workspace's act region (codes
+    [R_max, I], then scales [R_max, I / 32]) and the pair id of each row."""
+    L = moe.workspace_layout(s)
+    R, off = L["rows_capacity"], L["act"]
+    codes = ws[off:off + R * w.I].cpu().numpy().reshape(R, w.I)
+    scales = ws[off + R * w.I:off + R * w.I + R * (w.I // 32)].cpu().numpy().reshape(R, w.I // 32)
+    return codes, scales, moe.ws_region(ws, s, "row_pair").cpu().numpy()
+
+
+def fp8_half_step(v, scale_codes):
+    """Half the spacing of FP8 E4M3 values (times the block's scale) at the magnitude of each v."""
+    sc = np.exp2(np.repeat(scale_codes.astype(np.float64) - 127, 32, axis=-1))
+    mag = np.abs(v) / sc
+    e = np.maximum(np.floor(np.log2(np.maximum(mag, 2.0 ** -30))), -6)   # subnormals share 2**-9
+    return 0.5 * np.exp2(e - 3) * sc
+
+
+# Accuracy of one gfx950 scaled MFMA (32x32x64, FP8 x FP4): the result differs from the exact
+# C + sum of its 64 products by up to EPS_MMA * (sum |products| + |C|), measured over 5e5 random
+# results with a spread of block scales (largest 4096 u, mean about 260 u).  The K loop chains the
+# instructions through C, so a dot product of K terms errs by up to
+# EPS_MMA * sum over 64-deep steps s of (S_s + |C_s|), C_s being the partial sum before step s.
+EPS_MMA = 2.0 ** -12
+
+
+def chained_mma_bound(x, w):
+    """Error bound of the chained scaled MFMA for the dot products of rows x[i] and w[i]."""
+    p = (x * w).reshape(len(x), -1, 64)
+    steps = p.sum(axis=2)
+    c = np.cumsum(steps, axis=1) - steps        # partial sum entering each step
+    return EPS_MMA * (np.abs(p).sum(axis=2) + np.abs(c)).sum(axis=1)
+
+
+def check_act_link(w, d, ref_codes, pairs, gc, gs, clamp=10.0):
+    """L1 link: the GPU's FP8 activation rows for the given pair ids against the oracle's fp64 L1.
+    The GPU decides each code on a value its matrix core computed with the error bound above, the
+    oracle on an exact one, so a code may differ where the two values straddle a rounding
+    boundary.  Every GPU value must be the FP8 rounding, at the GPU's block scale, of a value within
+    delta of the oracle's: the bounds of gate and up carried through the derivatives of the clamped
+    SwiGLU, plus a few fp32 ulps for the activation itself.  Block scales must agree unless the
+    block maximum lies within its delta of a boundary 448 * 2**E."""
+    xc, xs, w1c, w1s = ref_codes[:4]
+    a = oracle.mx_l1_rows(xc, xs, d["topk_idx"], w1c, w1s, w.E, w.e_lo, pairs, clamp)
+    rc, rs = oracle.mx_quantize(FP8, a)
+    smis = gs != rs
+    check = (gc != rc) | np.repeat(smis, 32, axis=1)
+    print("[parity] act codes: %d of %d differ, %d of %d block scales" % (np.sum(gc != rc), gc.size,
+                                                                        smis.sum(), smis.size))
+    assert check.mean() <= 5e-3, "too many activation codes differ"
+    ri, ci = np.nonzero(check)
+    if len(ri):
+        p = pairs[ri]
+        t, e = p // w.k, d["topk_idx"].reshape(-1)[p] - w.e_lo
+        xr = oracle.mx_dequantize(FP8, xc[t], xs[t])
+        wg = oracle.mx_dequantize(FP4, w1c[e, ci], w1s[e, ci])
+        wu = oracle.mx_dequantize(FP4, w1c[e, w.I + ci], w1s[e, w.I + ci])
+        g, u = np.sum(xr * wg, axis=1), np.sum(xr * wu, axis=1)
+        bg, bu = chained_mma_bound(xr, wg), chained_mma_bound(xr, wu)
+        if clamp > 0:
+            g, u = np.minimum(g, clamp), np.clip(u, -clamp, clamp)
+        sg = 1.0 / (1.0 + np.exp(-g))
+        delta = bg * np.abs(u * sg * (1 + g * (1 - sg))) + bu * np.abs(g * sg) + 16 * U32 * np.abs(a[ri, ci])
+        gv = oracle.mx_dequantize(FP8, gc, gs)[ri, ci]
+        over = np.abs(a[ri, ci] - gv) - fp8_half_step(gv[:, None], gs[ri, ci // 32][:, None])[:, 0] - delta
+        print("[parity] act codes outside their rounding interval by at most %.3f of delta" % np.max(
+            (np.abs(a[ri, ci] - gv) - fp8_half_step(gv[:, None], gs[ri, ci // 32][:, None])[:, 0]) / delta))
+        assert np.all(over <= 0), "activation code outside its rounding interval by %.3g" % over.max()
+        if smis.any():
+            bi, bj = np.nonzero(smis)
+            amax = np.abs(a).reshape(len(a), -1, 32).max(axis=2)[bi, bj]
+            edge = FP8_MAX * np.exp2(np.minimum(gs, rs)[bi, bj].astype(np.float64) - 127)
+            dmax = np.zeros(smis.shape)
+            np.maximum.at(dmax, (ri, ci // 32), delta)
+            assert np.all(np.abs(amax - edge) <= dmax[bi, bj]), "block scale differs away from a boundary"
+
+
+def check_l2_link(w, d, ref_codes, y, tokens, pair_row, gc, gs):
+    """L2 + combine link: y of the given tokens against the oracle's L2 evaluated on the GPU's own
+    FP8 activation rows, weighted and summed per token, to the same bar as the bf16 forward
+    (2e-2 of rms beyond y's own rounding to bf16)."""
+    w2c, w2s = ref_codes[4:]
+    ref = np.zeros((len(tokens), w.H))
+    for j in range(w.k):
+        p = tokens * w.k + j
+        r = pair_row[p]
+        e = np.where(r >= 0, d["topk_idx"][tokens, j] - w.e_lo, -1).astype(np.int32)
+        rr = np.maximum(r, 0)
+        o = oracle.mx_l2_rows(w2c, w2s, e, gc[rr], gs[rr])
+        ref += d["topk_weights"][tokens, j].astype(np.float64)[:, None] * o
+    return check_bf16(y[tokens], ref, 2e-2, "y (MX, on the GPU's act)")
+
+
+def run_mx_forward(w, d, bm, x_scale=1.0, clamp=10.0, experts=None):
+    s, args, ref_codes = mx_layer(w, d, bm, x_scale, experts)
+    moe.forward_mx(s, *args, clamp=clamp)
+    torch.cuda.synchronize()
+    gc, gs, row_pair = gpu_act(args[8], s, w)
+    pair_row = moe.ws_region(args[8], s, "pair_row").cpu().numpy()
+    return f64_host(args[-1]), ref_codes, gc, gs, row_pair, pair_row
+
+
+@pytest.mark.parametrize("bm", [32, 64, 128, 256])
+@pytest.mark.parametrize("w", REDUCED, ids=[r.name for r in REDUCED])
+def test_mx_forward_reduced_link_by_link(w, bm):
+    d = mw.inputs(w, 21)
+    y, ref_codes, gc, gs, row_pair, pair_row = run_mx_forward(w, d, bm)
+    assert np.all(np.isfinite(y))
+    rows = np.nonzero(row_pair >= 0)[0]
+    local = (d["topk_idx"] >= w.e_lo) & (d["topk_idx"] < w.e_lo + w.EL)
+    assert len(rows) == local.sum()
+    check_act_link(w, d, ref_codes, row_pair[rows], gc[rows], gs[rows])
+    check_l2_link(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs)
+    assert np.all(y[~local.any(axis=1)] == 0.0)
+    full = oracle.forward_mx(*ref_codes[:2], d["topk_idx"], d["topk_weights"], *ref_codes[2:], E=w.E, e_lo=w.e_lo)
+    print("[parity] y (MX) against the oracle end to end: raw max|err|/rms %.3e" % rel_max_err(y, full))
+
+
+def test_mx_forward_clamp_active():
+    w = REDUCED[1]
+    d = mw.inputs(w, 22)
+    y, ref_codes, gc, gs, row_pair, pair_row = run_mx_forward(w, d, 64, x_scale=12.0)
+    rows = np.nonzero(row_pair >= 0)[0]
+    check_act_link(w, d, ref_codes, row_pair[rows], gc[rows], gs[rows], clamp=10.0)
+    check_l2_link(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs)
+    xc, xs, w1c, w1s = ref_codes[:4]
+    a10 = oracle.mx_l1_rows(xc, xs, d["topk_idx"], w1c, w1s, w.E, w.e_lo, row_pair[rows], 10.0)
+    a0 = oracle.mx_l1_rows(xc, xs, d["topk_idx"], w1c, w1s, w.E, w.e_lo, row_pair[rows], 0.0)
+    assert np.mean(a10 != a0) > 0.05, "the case must exercise the clamp"
+
+
+def test_mx_forward_full_size_sampled():
+    """The pages' low-precision workload on one GPU's share (384 experts, top-6, H 7168, I 3072,
+    4096 tokens, 48 experts local), sampled tokens checked link by link."""
+    w = mw.get("wide_share_mx_fwd")
+    d = mw.inputs(w, 0)
+    print("[mx full] inputs ready", flush=True)
+    nloc = ((d["topk_idx"] >= w.e_lo) & (d["topk_idx"] < w.e_lo + w.EL)).sum(axis=1)
+    tok = np.sort(np.random.default_rng(5).choice(np.nonzero(nloc)[0], 16, replace=False))
+    sel = d["topk_idx"][tok]
+    experts = sorted(set((sel[(sel >= w.e_lo) & (sel < w.e_lo + w.EL)] - w.e_lo).tolist()))
+    bm = moe.preferred_block_m(moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=64, e_lo=w.e_lo))
+    y, ref_codes, gc, gs, row_pair, pair_row = run_mx_forward(w, d, bm, experts=experts)
+    print("[mx full] forward done, oracle codes of %d experts ready" % len(experts), flush=True)
+    assert np.all(np.isfinite(y))
+    assert np.all(y[nloc == 0] == 0.0)
+    pairs = (tok[:, None] * w.k + np.arange(w.k)[None, :]).reshape(-1)
+    pairs = pairs[pair_row[pairs] >= 0]
+    r = pair_row[pairs]
+    assert np.array_equal(row_pair[r], pairs)
+    check_act_link(w, d, ref_codes, pairs, gc[r], gs[r])
+    print("[mx full] act link done", flush=True)
+    check_l2_link(w, d, ref_codes, y, tok, pair_row, gc, gs)

@@ -131,6 +131,24 @@ def pin_clamp_and_act_cast_dense(seed=5):
     assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+def test_mx_rows_compose_to_the_mx_forward():
+    """L1 rows, the FP8 cast of each row, L2 rows and the weighted sum per token reproduce the MX
+    forward (the row functions the GPU parity tests use link by link)."""
+    w = mw.Workload("mxr", T=36, H=128, I=64, E=9, EL=3, k=3, e_lo=2)
+    d = mw.inputs(w, 7)
+    xc, xs, w1c, w1s, w2c, w2s = quantized_layer(w, d)
+    y = oracle.forward_mx(xc, xs, d["topk_idx"], d["topk_weights"], w1c, w1s, w2c, w2s, E=w.E, e_lo=w.e_lo)
+    pairs = np.arange(w.T * w.k)
+    a = oracle.mx_l1_rows(xc, xs, d["topk_idx"], w1c, w1s, w.E, w.e_lo, pairs)
+    ac, as_ = oracle.mx_quantize(FP8, a)
+    ids = d["topk_idx"].reshape(-1) - w.e_lo
+    ex = np.where((ids >= 0) & (ids < w.EL), ids, -1)
+    o = oracle.mx_l2_rows(w2c, w2s, ex, ac, as_)
+    ref = (o * d["topk_weights"].reshape(-1, 1).astype(np.float64)).reshape(w.T, w.k, w.H).sum(axis=1)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(y))
+    assert np.all(a[ex < 0] == 0) and np.all(o[ex < 0] == 0)
+
+
 def test_fp8_cast_matches_torch_float8_e4m3fn():
     pin_fp8_matches_torch()
 
