@@ -21,7 +21,10 @@ its batched GEMM on a uniform stand-in of each forward GEMM).
 384 experts, 48 local, top-6): forward with the activations saved, L2 dgrad with the SwiGLU
 transpose and the routing-weight gradient, dW2, dW1, and the L1 dgrad with its combine into dx;
 one JSON line with per-stage times and each backward kernel against the HBM roofline (its
-algorithmic bytes per launch / its time).  The default run is the forward.
+algorithmic bytes per launch / its time).  --mx measures the low-precision variant's forward (FP8
+activations, FP4 weights, one power-of-two scale per 32 values along K; the "Mega MoE" page's FP8 x
+FP4 example shapes: 384 experts, top-6, hidden 7168, intermediate 3072, 4096 tokens, this GPU
+owning 48 experts).  The default run is the bf16 forward.
 """
 import argparse
 import hashlib
@@ -260,6 +263,148 @@ def bench_backward(a):
     print(json.dumps(out), flush=True)
 
 
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA (the FP8 x FP4 instruction is priced at the rate of its FP8 operand)
+
+
+def cpu_baseline_mx(w, d, budget_s=15.0):
+    """The MX oracle timed on the host cores on a bounded sample of tokens (the oracle's FP8 / FP4
+    casts of the inputs are made beforehand for the experts the sample touches, untimed)."""
+    import oracle
+    idx = d["topk_idx"]
+    local = (idx >= w.e_lo) & (idx < w.e_lo + w.EL)
+    toks = np.random.default_rng(0).permutation(np.nonzero(local.any(axis=1))[0])[:64]
+    sel = idx[toks]
+    experts = sorted(set((sel[(sel >= w.e_lo) & (sel < w.e_lo + w.EL)] - w.e_lo).tolist()))
+    xc, xs = oracle.mx_quantize(oracle.MX_FP8, mw.bf16_bits_to_f32(d["x"]).astype(np.float64))
+    codes = []
+    for W in (d["W1"], d["W2"]):
+        EL, K, N = W.shape
+        c, sc = np.zeros((EL, N, K), np.uint8), np.zeros((EL, N, K // 32), np.uint8)
+        for e in experts:
+            c[e], sc[e] = oracle.mx_quantize(oracle.MX_FP4, np.ascontiguousarray(
+                mw.bf16_bits_to_f32(W[e]).astype(np.float64).T))
+        codes += [c, sc]
+    run = lambda tk: oracle.forward_mx(xc, xs, idx, d["topk_weights"], *codes, E=w.E, e_lo=w.e_lo, tokens=tk)
+    n = max(1, oracle.num_threads())
+    t0 = time.perf_counter()
+    run(toks[:n])
+    dt = time.perf_counter() - t0
+    n2 = int(min(len(toks), max(n, n * budget_s / max(dt, 1e-3))))
+    sample = toks[:n2]
+    t0 = time.perf_counter()
+    run(sample)
+    dt = time.perf_counter() - t0
+    pairs = int(local[sample].sum())
+    return {"value": w.flops_fwd(pairs) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d tokens (%d local pairs), fp64 per-token loop on decoded FP8 / FP4 values, %.1f s"
+                      % (len(sample), w.T, pairs, dt)}
+
+
+def bench_mx(a):
+    """Forward of the low-precision variant: FP8 activations, FP4 weights, block scales per 32."""
+    w = mw.get("wide_share_mx_fwd" if a.workload == "dsv3_share_fwd" else a.workload)
+    log("generating %s inputs (seed 0)" % w.name)
+    d = mw.inputs(w, 0)
+    P = mw.local_pairs(w, d["topk_idx"])
+    bm = a.block_m or 32
+    shape = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=bm, e_lo=w.e_lo)
+    x = bf16_dev(d["x"])
+    idx = torch.from_numpy(d["topk_idx"]).cuda()
+    wts = torch.from_numpy(d["topk_weights"]).cuda()
+    xq, xs = moe.mx_cast_fp8(x)
+    w1q, w1s, w2q, w2s = moe.mx_alloc_packed(shape)
+    W1, W2 = bf16_dev(d["W1"]), bf16_dev(d["W2"])
+    moe.mx_pack_weights(shape, W1, W2, w1q, w1s, w2q, w2s)
+    del W1, W2
+    ws = moe.alloc_workspace(shape)
+    y = torch.empty(w.T, w.H, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    fwd = lambda: moe.forward_mx(shape, xq, xs, idx, wts, w1q, w1s, w2q, w2s, ws, y)
+    log("warmup %d" % a.warmup)
+    for _ in range(a.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    log("timing %d MX forward steps" % a.steps)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(a.steps):
+        fwd()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    log("timing %d staged MX steps" % a.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    for i in range(a.steps):
+        ev[i][0].record(s)
+        moe.route_prologue(shape, idx, ws)
+        ev[i][1].record(s)
+        moe.mx_dispatch_gemm1(shape, xq, xs, w1q, w1s, ws)
+        ev[i][2].record(s)
+        moe.mx_gemm2_combine(shape, w2q, w2s, wts, ws, y)
+        ev[i][3].record(s)
+        moe.mx_cast_fp8(x, xq, xs)   # not part of the step: the caller's cast of bf16 x, for reference
+        ev[i][4].record(s)
+    torch.cuda.synchronize()
+    st = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(a.steps)])
+    st_ms = st.mean(axis=0)
+    graph = graph_replay_stats(fwd, a.replays) if a.replays > 0 else None
+
+    idx_np = d["topk_idx"]
+    local = (idx_np >= w.e_lo) & (idx_np < w.e_lo + w.EL)
+    nonempty = len(np.unique(idx_np[local]))
+    tok_local = int(local.any(axis=1).sum())
+    H, I = w.H, w.I
+    fp4 = lambda n, kk: n * kk // 2 + n * kk // 32          # FP4 codes + one scale byte per 32
+    fp8 = lambda r, kk: r * kk + r * kk // 32
+    # L1: each non-empty expert's W1 once, the FP8 x rows of tokens with a local pair once, the FP8
+    # activation rows written once, the pair id of each row; L2: W2 once, the activation rows once,
+    # y written once
+    l1_bytes = nonempty * fp4(2 * I, H) + fp8(tok_local, H) + fp8(P, I) + P * 4
+    l1_flops = 2.0 * P * H * 2 * I
+    l2_bytes = nonempty * fp4(H, I) + fp8(P, I) + w.T * H * 2
+    l2_flops = 2.0 * P * I * H
+    l1_s = st_ms[1] / 1e3
+    ridge = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if l1_flops / l1_bytes < ridge:
+        roof = {"bound": "hbm", "achieved": l1_bytes / l1_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": l1_flops / l1_s / 1e12, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": l1_flops / l1_s / 1e12 / PEAK_FP8_TFLOPS}
+    roof.update({"traffic": None, "kernel": "MX gemm1 (dispatch gather of FP8 x + L1 + clamped SwiGLU + FP8 cast)",
+                 "alg_bytes_per_launch": l1_bytes, "alg_flops_per_launch": l1_flops,
+                 "intensity_flop_per_byte": round(l1_flops / l1_bytes, 1),
+                 "hbm_frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS,
+                 "mfma_frac": l1_flops / l1_s / 1e12 / PEAK_FP8_TFLOPS})
+    rates = lambda ms_, f, b: {"ms": round(ms_, 4), "tflops": round(f / (ms_ / 1e3) / 1e12, 1),
+                               "alg_gbs": round(b / (ms_ / 1e3) / 1e9, 1),
+                               "pct_hbm_peak": round(100 * b / (ms_ / 1e3) / 1e9 / PEAK_HBM_GBS, 2),
+                               "alg_flops": f, "alg_bytes": b}
+    value = w.flops_fwd(P) / (ms / 1e3) / 1e12
+    out = {
+        "metric": "MoE layer fwd, FP8 activations x FP4 weights (block scales per 32), TFLOP/s on 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1 -> fp32", "data": "synthetic (seeded N(0,1) logits, x, scaled weights)",
+        "config": {"workload": w.name, "T": w.T, "H": H, "I": I, "E": w.E, "EL": w.EL, "k": w.k,
+                   "block_m": bm, "local_pairs": P, "clamp": 10.0, "parallelism": "none (1 GPU share)"},
+        "stages_ms": {"prologue": round(st_ms[0], 4), "mx_dispatch_gemm1": round(st_ms[1], 4),
+                      "mx_gemm2_combine": round(st_ms[2], 4), "staged_total": round(st_ms[:3].sum(), 4),
+                      "x_cast_fp8_not_in_step": round(st_ms[3], 4)},
+        "stages": {"mx_dispatch_gemm1": rates(st_ms[1], l1_flops, l1_bytes),
+                   "mx_gemm2_combine": rates(st_ms[2], l2_flops, l2_bytes)},
+        "roofline": roof,
+    }
+    if graph:
+        out["graph_replay"] = graph
+    if not a.no_cpu_baseline:
+        log("timing the MX oracle on a CPU sample")
+        out["cpu_baseline"] = cpu_baseline_mx(w, d)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +415,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--mx", action="store_true", help="the FP8 x FP4 variant's forward")
     ap.add_argument("--replays", type=int, default=100, help="graph replays timed one by one (0: skip)")
     ap.add_argument("--no-references", action="store_true", help="skip the copy / vendor-GEMM references")
     a = ap.parse_args()
@@ -281,6 +427,8 @@ def main():
     torch.cuda.set_device(0)
     if a.backward:
         return bench_backward(a)
+    if a.mx:
+        return bench_mx(a)
     w = mw.get(a.workload)
     log("generating %s inputs (seed 0)" % w.name)
     d = mw.inputs(w, 0)

@@ -273,3 +273,28 @@ def test_mx_forward_full_size_sampled():
     check_act_link(w, d, ref_codes, pairs, gc[r], gs[r])
     print("[mx full] act link done", flush=True)
     check_l2_link(w, d, ref_codes, y, tok, pair_row, gc, gs)
+
+
+def test_mx_stage_entry_points_match_the_fused_forward():
+    """route_prologue + mx_dispatch_gemm1 + mx_gemm2_combine give the fused MX forward's y bit for bit."""
+    w = REDUCED[0]
+    d = mw.inputs(w, 23)
+    s, args, _ = mx_layer(w, d, 32, experts=[])
+    xq, xs, idx, wts, w1q, w1s, w2q, w2s, ws, y = args
+    moe.forward_mx(s, *args)
+    y2 = torch.full_like(y, float("nan"))
+    moe.route_prologue(s, idx, ws)
+    moe.mx_dispatch_gemm1(s, xq, xs, w1q, w1s, ws)
+    moe.mx_gemm2_combine(s, w2q, w2s, wts, ws, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_mx_rejects_unsupported_shapes():
+    w = mw.Workload("mx_bad", T=16, H=128, I=128, E=4, EL=4, k=2)
+    d = mw.inputs(w, 1)
+    s, args, _ = mx_layer(w, d, 32, experts=[])
+    with pytest.raises(moe.MoeError, match="size"):
+        moe.forward_mx(s, *args)
+    with pytest.raises(moe.MoeError, match="size"):
+        moe.mx_dispatch_gemm1(s, args[0], args[1], args[4], args[5], args[8])

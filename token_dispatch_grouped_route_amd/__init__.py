@@ -27,7 +27,8 @@ ENTRY_POINTS = (
     "moe_pack_weights", "moe_unpack_weights", "moe_route_prologue", "moe_dispatch_gemm1", "moe_swiglu",
     "moe_gemm2_combine", "moe_forward", "moe_bwd_gemm2_dgrad", "moe_swiglu_bwd",
     "moe_bwd_gemm1_dgrad_combine", "moe_wgrad2", "moe_wgrad1", "moe_backward",
-    "moe_mx_cast_fp8", "moe_mx_pack_weights", "moe_forward_mx",
+    "moe_mx_cast_fp8", "moe_mx_pack_weights", "moe_forward_mx", "moe_mx_dispatch_gemm1",
+    "moe_mx_gemm2_combine",
 )
 
 
@@ -83,6 +84,8 @@ def lib():
         L.moe_mx_cast_fp8.argtypes = [ctypes.c_int64, i32, P, P, P, P]
         L.moe_mx_pack_weights.argtypes = [S, P, P, P, P, P, P, P]
         L.moe_forward_mx.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P, P]
+        L.moe_mx_dispatch_gemm1.argtypes = [S, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
+        L.moe_mx_gemm2_combine.argtypes = [S, P, P, P, P, ctypes.c_size_t, P, P]
         for n in ENTRY_POINTS[2:]:
             if n != "moe_workspace_bytes":
                 getattr(L, n).restype = i32
@@ -317,3 +320,17 @@ def forward_mx(shape, xq, xs, topk_idx, topk_w, w1q, w1s, w2q, w2s, ws, y, clamp
                                 _ptr(w1q, torch.uint8, "w1q"), _ptr(w1s, torch.uint8, "w1s"),
                                 _ptr(w2q, torch.uint8, "w2q"), _ptr(w2s, torch.uint8, "w2s"), float(clamp), p, n,
                                 _ptr(y, torch.bfloat16, "y"), _stream(stream)), "moe_forward_mx")
+
+
+def mx_dispatch_gemm1(shape, xq, xs, w1q, w1s, ws, clamp=10.0, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_mx_dispatch_gemm1(ctypes.byref(shape), _ptr(xq, torch.uint8, "xq"), _ptr(xs, torch.uint8, "xs"),
+                                       _ptr(w1q, torch.uint8, "w1q"), _ptr(w1s, torch.uint8, "w1s"), float(clamp), p,
+                                       n, _stream(stream)), "moe_mx_dispatch_gemm1")
+
+
+def mx_gemm2_combine(shape, w2q, w2s, topk_w, ws, y, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_mx_gemm2_combine(ctypes.byref(shape), _ptr(w2q, torch.uint8, "w2q"), _ptr(w2s, torch.uint8, "w2s"),
+                                      _ptr(topk_w, torch.float32, "topk_w"), p, n, _ptr(y, torch.bfloat16, "y"),
+                                      _stream(stream)), "moe_mx_gemm2_combine")

@@ -362,6 +362,39 @@ int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const ui
     return launched(launch_mx_pack(d, w1, w2, w1q, w1s, w2q, w2s, static_cast<hipStream_t>(stream)));
 }
 
+static bool mx_shape_ok(const moe_shape* shape) {
+    return shape->H % 256 == 0 && shape->I % kMxBlockK == 0 && (2 * shape->I) % 256 == 0;
+}
+
+int32_t moe_mx_dispatch_gemm1(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,
+                              const uint8_t* w1s, float clamp, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!mx_shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (!w1q || !w1s || ((!xq || !xs) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(xq) || !aligned4(xs) || !aligned16(w1q)) return MOE_ERR_ALIGN;
+    return launched(launch_mx_gemm1(d, xq, xs, w1q, w1s, w, clamp, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_mx_gemm2_combine(const moe_shape* shape, const uint8_t* w2q, const uint8_t* w2s, const float* topk_w,
+                             void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
+    Dims d;
+    Ws w;
+    moe_ws_layout L;
+    int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    if (!mx_shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (!w2q || !w2s || ((!topk_w || !y) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(w2q) || !aligned4(topk_w) || !aligned16(y)) return MOE_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_mx_gemm2(d, w2q, w2s, topk_w, w, y, s);
+    if (e == hipSuccess) e = launch_combine_finish(d, w, y, s);
+    return launched(e);
+}
+
 int32_t moe_forward_mx(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs, const int32_t* topk_idx,
                        const float* topk_w, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
                        const uint8_t* w2s, float clamp, void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
@@ -370,15 +403,15 @@ int32_t moe_forward_mx(const moe_shape* shape, const uint8_t* xq, const uint8_t*
     moe_ws_layout L;
     int32_t st = prepare(shape, ws, ws_bytes, false, &d, &w, &L);
     if (st != MOE_OK) return st;
-    if (shape->H % kMxBlockK != 0 || shape->I % kMxBlockK != 0 || (2 * shape->I) % 256 != 0 || shape->H % 256 != 0)
-        return MOE_ERR_SHAPE;
+    if (!mx_shape_ok(shape)) return MOE_ERR_SHAPE;
     if (!w1q || !w1s || !w2q || !w2s || ((!xq || !xs || !topk_idx || !topk_w || !y) && shape->T > 0)) return MOE_ERR_NULL;
     if (!aligned16(xq) || !aligned4(xs) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned16(w1q) ||
         !aligned16(w2q) || !aligned16(y))
         return MOE_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_route(d, topk_idx, w, s);
-    if (e == hipSuccess) e = launch_mx_forward_gemms(d, xq, xs, w1q, w1s, w2q, w2s, topk_w, w, clamp, y, s);
+    if (e == hipSuccess) e = launch_mx_gemm1(d, xq, xs, w1q, w1s, w, clamp, s);
+    if (e == hipSuccess) e = launch_mx_gemm2(d, w2q, w2s, topk_w, w, y, s);
     if (e == hipSuccess) e = launch_combine_finish(d, w, y, s);
     return launched(e);
 }

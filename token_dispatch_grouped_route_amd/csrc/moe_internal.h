@@ -106,9 +106,10 @@ hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_
 
 hipError_t launch_mx_cast_fp8(int64_t rows, int cols, const uint16_t* x, uint8_t* codes, uint8_t* scales,
                               hipStream_t s);
-hipError_t launch_mx_forward_gemms(const Dims& d, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,
-                                   const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const float* topk_w,
-                                   const Ws& ws, float clamp, uint16_t* y, hipStream_t s);
+hipError_t launch_mx_gemm1(const Dims& d, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q, const uint8_t* w1s,
+                           const Ws& ws, float clamp, hipStream_t s);
+hipError_t launch_mx_gemm2(const Dims& d, const uint8_t* w2q, const uint8_t* w2s, const float* topk_w, const Ws& ws,
+                           uint16_t* y, hipStream_t s);
 hipError_t launch_mx_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, uint8_t* w1q, uint8_t* w1s,
                           uint8_t* w2q, uint8_t* w2s, hipStream_t s);
 

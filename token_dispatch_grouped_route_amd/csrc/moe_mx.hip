@@ -440,11 +440,13 @@ hipError_t launch_mx_cast_fp8(int64_t rows, int cols, const uint16_t* x, uint8_t
     return hipGetLastError();
 }
 
-hipError_t launch_mx_forward_gemms(const Dims& d, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,
-                                   const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s, const float* topk_w,
-                                   const Ws& ws, float clamp, uint16_t* y, hipStream_t s) {
-    hipError_t e = mx_gemm<true>(d, xq, xs, w1q, w1s, nullptr, ws, clamp, nullptr, s);
-    if (e != hipSuccess) return e;
+hipError_t launch_mx_gemm1(const Dims& d, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q, const uint8_t* w1s,
+                           const Ws& ws, float clamp, hipStream_t s) {
+    return mx_gemm<true>(d, xq, xs, w1q, w1s, nullptr, ws, clamp, nullptr, s);
+}
+
+hipError_t launch_mx_gemm2(const Dims& d, const uint8_t* w2q, const uint8_t* w2s, const float* topk_w, const Ws& ws,
+                           uint16_t* y, hipStream_t s) {
     const uint8_t* act_codes = reinterpret_cast<const uint8_t*>(ws.act);
     return mx_gemm<false>(d, act_codes, act_codes + ws.rows_cap * d.I, w2q, w2s, topk_w, ws, 0.0f, y, s);
 }
