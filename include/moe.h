@@ -273,11 +273,12 @@ int32_t moe_mx_cast_fp8(int64_t rows, int32_t cols, const uint16_t* x, uint8_t* 
  *   w1q [device] uint8, EL * 2I * H / 2 bytes;  w1s [device] uint8, EL * 2I * H / 32 bytes
  *   w2q [device] uint8, EL * H * I / 2 bytes;   w2s [device] uint8, EL * H * I / 32 bytes
  * Per expert (N output columns, reduction length K; N = 2I, K = H for W1 and N = H, K = I for W2;
- * the expert's data starts at e * N * K / 2, its scales at e * N * K / 32), the data of column n and
- * reduction index k is nibble k % 32 (low nibble first) of the 16 bytes at
- *     (((n / 32) * (K / 64) + k / 64) * 64 + n % 32 + 32 * ((k % 64) / 32)) * 16
- * and its block's scale the byte at ((n / 32) * (K / 64) + k / 64) * 64 + n % 32 + 32 * ((k % 64) / 32).
- * For W1, n is the packed L1 column (moe_pack_weights).  Either triple may be NULL.
+ * the expert's data starts at e * N * K / 2, its scales at e * N * K / 32), with j = k / 64 and
+ * l = n % 32 + 32 * ((k % 64) / 32), the data of column n and reduction index k is nibble k % 32
+ * (low nibble first) of the 16 bytes at (((n / 32) * (K / 64) + j) * 64 + l) * 16, and its block's
+ * scale the byte at (n / 32) * (K / 64) * 64 + (j / 4) * 256 + l * 4 + j % 4 (one dword per lane
+ * holds the scales of four K steps).  For W1, n is the packed L1 column (moe_pack_weights).
+ * H and I must be multiples of 256 (MOE_ERR_SHAPE otherwise).  Either triple may be NULL.
  */
 int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2, uint8_t* w1q,
                             uint8_t* w1s, uint8_t* w2q, uint8_t* w2s, void* stream);
@@ -292,7 +293,7 @@ int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const ui
  *   w1q, w1s, w2q, w2s [device]                              (moe_mx_pack_weights)
  *   topk_idx, topk_w, ws, y as for moe_forward.  The act region of ws holds the FP8 activation
  *   codes [R_max, I] followed by their scale bytes [R_max, I / 32].
- * H and I must be multiples of 256 and 128.
+ * H and I must be multiples of 256.
  */
 int32_t moe_forward_mx(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs, const int32_t* topk_idx,
                        const float* topk_w, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,

@@ -45,15 +45,17 @@ def test_fp8_cast_bit_exact(T, H):
 def unpack_fp4(wq, ws, EL, N, K, I=None):
     """Codes [EL, N, K] and scales [EL, N, K / 32] in logical column order, read through the layout
     documented for moe_mx_pack_weights (I given: W1, whose column n is packed column
-    ((n mod I) / 32) * 64 + (n >= I) * 32 + n mod 32)."""
+    ((n mod I) / 32) * 64 + (n >= I) * 32 + n mod 32; the scales of a column group hold four
+    64-deep K steps per lane dword)."""
     n = np.arange(N)[:, None]
     k = np.arange(K)[None, :]
     pc = ((n % I) // 32) * 64 + (n >= I) * 32 + n % 32 if I is not None else n
-    blk = (pc // 32) * (K // 64) + k // 64
+    j = k // 64
+    blk = (pc // 32) * (K // 64) + j
     lane = pc % 32 + 32 * ((k % 64) // 32)
     byte = (blk * 64 + lane) * 16 + (k % 32) // 2
     shift = 4 * ((k % 32) % 2)
-    sidx = (blk * 64 + lane)[:, ::32]
+    sidx = ((pc // 32) * (K // 64) * 64 + (j // 4) * 256 + lane * 4 + j % 4)[:, ::32]
     codes = np.zeros((EL, N, K), np.uint8)
     scales = np.zeros((EL, N, K // 32), np.uint8)
     for e in range(EL):
@@ -63,7 +65,7 @@ def unpack_fp4(wq, ws, EL, N, K, I=None):
     return codes, scales
 
 
-@pytest.mark.parametrize("shape", [(3, 256, 128), (2, 384, 256)])
+@pytest.mark.parametrize("shape", [(3, 256, 256), (2, 768, 512)])
 def test_fp4_pack_bit_exact_in_documented_layout(shape):
     EL, H, I = shape
     w = mw.Workload("mxpack", T=8, H=H, I=I, E=EL, EL=EL, k=1)
@@ -84,7 +86,7 @@ def test_fp4_pack_bit_exact_in_documented_layout(shape):
 
 REDUCED = [
     mw.Workload("mx_shard", T=333, H=256, I=256, E=12, EL=6, k=3, e_lo=3),
-    mw.Workload("mx_all_local", T=500, H=512, I=128, E=8, EL=8, k=4),
+    mw.Workload("mx_all_local", T=500, H=512, I=256, E=8, EL=8, k=4),
 ]
 U32 = 2.0 ** -24          # unit roundoff of fp32
 FP8_MAX = 448.0
@@ -291,10 +293,22 @@ def test_mx_stage_entry_points_match_the_fused_forward():
 
 
 def test_mx_rejects_unsupported_shapes():
-    w = mw.Workload("mx_bad", T=16, H=128, I=128, E=4, EL=4, k=2)
+    """H and I must be multiples of 256 for the pack and every MX GEMM entry point."""
+    w = mw.Workload("mx_bad", T=16, H=128, I=256, E=4, EL=4, k=2)
     d = mw.inputs(w, 1)
-    s, args, _ = mx_layer(w, d, 32, experts=[])
+    s = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=32)
+    w1q, w1s, w2q, w2s = moe.mx_alloc_packed(s)
     with pytest.raises(moe.MoeError, match="size"):
-        moe.forward_mx(s, *args)
+        moe.mx_pack_weights(s, bf16_dev(d["W1"]), bf16_dev(d["W2"]), w1q, w1s, w2q, w2s)
+    xq, xs = moe.mx_cast_fp8(bf16_dev(d["x"]))
+    idx = torch.from_numpy(np.ascontiguousarray(d["topk_idx"], np.int32)).cuda()
+    wts = torch.from_numpy(np.ascontiguousarray(d["topk_weights"], np.float32)).cuda()
+    ws = moe.alloc_workspace(s)
+    y = torch.empty(w.T, w.H, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(moe.MoeError, match="size"):
-        moe.mx_dispatch_gemm1(s, args[0], args[1], args[4], args[5], args[8])
+        moe.forward_mx(s, xq, xs, idx, wts, w1q, w1s, w2q, w2s, ws, y)
+    with pytest.raises(moe.MoeError, match="size"):
+        moe.mx_dispatch_gemm1(s, xq, xs, w1q, w1s, ws)
+    with pytest.raises(moe.MoeError, match="size"):
+        moe.mx_gemm2_combine(s, w2q, w2s, wts, ws, y)
+    torch.cuda.synchronize()

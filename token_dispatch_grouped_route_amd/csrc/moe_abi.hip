@@ -10,7 +10,7 @@ using namespace moe;
 namespace {
 
 constexpr size_t kWsAlign = 256;
-constexpr int kMxBlockK = 128;   // K advances 128 per slot in the MX GEMMs
+constexpr int kMxSlotK = 256;   // K advances 256 per slot in the MX GEMMs (and the FP4 scale layout groups four 64-deep steps)
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
@@ -349,10 +349,15 @@ int32_t moe_mx_cast_fp8(int64_t rows, int32_t cols, const uint16_t* x, uint8_t* 
     return launched(launch_mx_cast_fp8(rows, cols, x, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
+static bool mx_shape_ok(const moe_shape* shape) {
+    return shape->H % kMxSlotK == 0 && shape->I % kMxSlotK == 0;
+}
+
 int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const uint16_t* w2, uint8_t* w1q,
                             uint8_t* w1s, uint8_t* w2q, uint8_t* w2s, void* stream) {
     const int32_t st = check_shape(shape);
     if (st != MOE_OK) return st;
+    if (!mx_shape_ok(shape)) return MOE_ERR_SHAPE;
     if ((w1 == nullptr) != (w1q == nullptr) || (w1 == nullptr) != (w1s == nullptr) ||
         (w2 == nullptr) != (w2q == nullptr) || (w2 == nullptr) != (w2s == nullptr))
         return MOE_ERR_NULL;
@@ -360,10 +365,6 @@ int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const ui
     if (!is_gfx950()) return MOE_ERR_DEVICE;
     const Dims d{shape->T, shape->H, shape->I, shape->E, shape->e_lo, shape->EL, shape->k, shape->block_m};
     return launched(launch_mx_pack(d, w1, w2, w1q, w1s, w2q, w2s, static_cast<hipStream_t>(stream)));
-}
-
-static bool mx_shape_ok(const moe_shape* shape) {
-    return shape->H % 256 == 0 && shape->I % kMxBlockK == 0 && (2 * shape->I) % 256 == 0;
 }
 
 int32_t moe_mx_dispatch_gemm1(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,

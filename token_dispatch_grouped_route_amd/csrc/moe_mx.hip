@@ -118,11 +118,12 @@ __global__ __launch_bounds__(256) void cast_fp8_kernel(int64_t nblocks, const ui
 // ---------------------------------------------------------------------------------------------
 // FP4 pack of the weights: one (expert, output column, 32-block along K) per thread
 // ---------------------------------------------------------------------------------------------
-// Packed layout (per expert, N output columns, reduction length K): the data of (column group
-// n / 32, K step k / 64) is a 1 KB block at ((n / 32) * (K / 64) + k / 64) * 1024 whose lane
-// l = n % 32 + 32 * ((k % 64) / 32) holds the 16 bytes at l * 16, nibble q = k % 32 (low nibble
-// first); the scale bytes of the same (group, step) are a 64-byte block at the same block index *
-// 64, byte l.  For W1 the column is the packed L1 column (gate and up groups interleaved).
+// Packed layout (per expert, N output columns, reduction length K, K a multiple of 256): the data
+// of (column group n / 32, K step j = k / 64) is a 1 KB block at ((n / 32) * (K / 64) + j) * 1024
+// whose lane l = n % 32 + 32 * ((k % 64) / 32) holds the 16 bytes at l * 16, nibble q = k % 32 (low
+// nibble first); the scale bytes of a column group are (K / 64) * 64 bytes at (n / 32) * (K / 64) *
+// 64, the scale of lane l in step j at (j / 4) * 256 + l * 4 + j % 4, so that one dword per lane
+// holds four steps.  For W1 the column is the packed L1 column (gate and up groups interleaved).
 template <bool W1>
 __global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restrict__ w, int EL, int N, int K, int I,
                                                        uint8_t* __restrict__ wq, uint8_t* __restrict__ ws) {
@@ -148,113 +149,206 @@ __global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restric
 #pragma unroll
         for (int i = 0; i < 32; ++i) out[i / 8] |= fp4_code(v[i] * inv) << (4 * (i % 8));
         const int64_t pc = W1 ? l1_packed_col(n, I) : n;
-        const int64_t blk = static_cast<int64_t>(e) * (static_cast<int64_t>(N) / 32) * (K / 64) + (pc / 32) * (K / 64) + kb / 2;
+        const int64_t grp = static_cast<int64_t>(e) * (static_cast<int64_t>(N) / 32) + pc / 32;
+        const int j = kb / 2;   // K step of 64 within the column group
         const int lane = static_cast<int>(pc % 32) + 32 * (kb % 2);
-        *reinterpret_cast<uint4*>(wq + blk * 1024 + lane * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-        ws[blk * 64 + lane] = static_cast<uint8_t>(E + 127);
+        *reinterpret_cast<uint4*>(wq + (grp * (K / 64) + j) * 1024 + lane * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+        ws[grp * (K / 64) * 64 + (j / 4) * 256 + lane * 4 + j % 4] = static_cast<uint8_t>(E + 127);
     }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Grouped GEMMs on the block-scaled MFMA
 // ---------------------------------------------------------------------------------------------
-// A workgroup computes a BM x 256 tile (BM = 32 * MG = the workspace's block_m, so a tile is one
-// row block of one expert) with four waves, each holding MG row groups x two 32-column groups.
-// K advances 128 per slot (two 64-deep MFMA steps).  A (FP8 rows, 128 bytes per row per slot) and
-// its scale bytes (4 per row per slot) go through a double-buffered LDS stage, 16-byte chunks
-// XOR-swizzled by row; B (FP4, one 1 KB fragment and 64 scale bytes per column group and step) is
-// private to a wave and loaded straight into registers one slot ahead.
-constexpr int kMxThreads = 256;
-constexpr int kMxBN = 256;
+// A workgroup computes a BM x 256 tile (BM = 32 * MG rows of one expert) with four waves, one per
+// SIMD, each holding MG row groups x two 32-column groups; K advances 256 per slot (four 64-deep
+// MFMA steps).  B, the FP4 weights, is the stream that sets the pace (a weight byte serves only
+// BM rows): each wave streams its two column groups straight into registers (per slot and lane
+// eight 16-byte loads and one scale dword per group).  A, the FP8 rows, is shared by the waves and
+// goes through LDS, straight from memory (global_load_lds_dwordx4: each instruction fills four
+// 256-byte rows, chunks XOR-swizzled so fragment reads spread over the banks); each lane loads its
+// own rows' eight scale bytes per slot into registers.  All of it runs through a ring of three
+// slots loaded two slots ahead, a quarter per MFMA step; per slot: wait for this wave's loads of
+// the slot, one barrier, four steps.
+typedef __attribute__((address_space(1))) void g_void;
+typedef __attribute__((address_space(3))) void l_void;
 
-__device__ __forceinline__ int mx_lds_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+constexpr int kMxThreads = 256;
+constexpr int kMxWaves = 4;
+constexpr int kMxBN = 256;
+constexpr int kMxSK = 256;   // K per slot
+constexpr int kMxSlots = 3;
+
+// 16-byte chunk c of LDS row r (256 bytes) sits at position c ^ (r % 16).
+__device__ __forceinline__ int mx_lds_off(int row, int chunk) { return row * kMxSK + ((chunk ^ (row & 15)) << 4); }
 __device__ __forceinline__ int mx_acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// s_waitcnt vmcnt(n) alone (gfx9 encoding: expcnt and lgkmcnt fields at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void mx_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int MG>
-struct MxStage {   // one slot of A (codes + scales) in registers on its way into LDS
-    static constexpr int PER = MG;   // 16-byte chunks per thread: BM * 8 / 256
-    uint4 v[PER];
-    uint32_t sc;
-};
-
-struct MxB {   // one slot of a wave's B: two column groups x two K steps
-    uint4 d[2][2];
-    uint32_t s[2][2];
-};
-
-template <int MG, bool L1>
 struct MxGemm {
     static constexpr int BM = 32 * MG;
-    static constexpr int A_BYTES = BM * 128, S_BYTES = BM * 4;
-    static constexpr int BUF = A_BYTES + S_BYTES;
-    static constexpr int LDS = 2 * BUF + 16 * BM;   // two buffers + row info
+    static constexpr int SLOT = BM * kMxSK;                 // bytes of one A slot
+    static constexpr int LDS = kMxSlots * SLOT + 16 * BM;   // ring + row info
+    static constexpr int A_DMA = BM / 16;                   // DMA loads per wave per slot (4 rows each)
+    static constexpr int LOADS = A_DMA + 8 + 2 + MG;        // this wave's loads of one slot
 };
 
-// Row sources of a tile: for every row the byte address of its codes and its scale bytes (padding
-// rows read the zero row).
 template <int MG>
-__device__ __forceinline__ void mx_load_a(MxStage<MG>& st, const uint8_t* const* rows, const uint8_t* const* srows,
-                                          int kt, int tid) {
-#pragma unroll
-    for (int i = 0; i < MG; ++i) {
-        const int q = tid + i * kMxThreads;
-        st.v[i] = *reinterpret_cast<const uint4*>(rows[i] + kt * 128 + (q & 7) * 16);
-    }
-    if (tid < 32 * MG) st.sc = *reinterpret_cast<const uint32_t*>(srows[0] + kt * 4);
-}
+struct MxPipe {
+    const char* a_src[MxGemm<MG>::A_DMA];   // the lane's chunk of its row of DMA load i, at K 0
+    const uint8_t* as_src[MG];              // scale bytes of row 32 mi + lane % 32, at K 0
+    const uint8_t* b_src[2];                // the lane's 16 bytes of group g's block, K step 0
+    const uint8_t* bs_src[2];               // the lane's scale dword of group g, slot 0
+    uint4 b[kMxSlots][2][4];
+    uint32_t bs[kMxSlots][2];
+    uint2 as[kMxSlots][MG];
+    int nslot;                              // K / 256 (loads past the end re-read the last slot)
+    int wave;
 
-template <int MG>
-__device__ __forceinline__ void mx_store_a(const MxStage<MG>& st, char* buf, int tid) {
+    // part q (0..3) of the loads of slot j into ring entry buf: DMA loads i = q, q + 4, ...; B K step q
+    // of both groups; the B scale dwords with part 0 and the A scales with part 1
+    __device__ __forceinline__ void issue(int j, char* __restrict__ slot, int buf, int q) {
+        const int jj = min(j, nslot - 1);
 #pragma unroll
-    for (int i = 0; i < MG; ++i) {
-        const int q = tid + i * kMxThreads;
-        *reinterpret_cast<uint4*>(buf + mx_lds_off(q >> 3, q & 7)) = st.v[i];
-    }
-    if (tid < 32 * MG) *reinterpret_cast<uint32_t*>(buf + 32 * MG * 128 + tid * 4) = st.sc;
-}
-
-__device__ __forceinline__ void mx_load_b(MxB& b, const uint8_t* const (&blk)[2], const uint8_t* const (&sblk)[2], int kt,
-                                          int lane) {
+        for (int i = 0; i < MxGemm<MG>::A_DMA; ++i)
+            if (i % 4 == q)
+                __builtin_amdgcn_global_load_lds((g_void*)(a_src[i] + jj * kMxSK),
+                                                 (l_void*)(slot + 1024 * (wave + kMxWaves * i)), 16, 0, 0);
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < 2; ++g) b[buf][g][q] = *reinterpret_cast<const uint4*>(b_src[g] + (4 * jj + q) * 1024);
+        if (q == 0) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            b.d[g][s] = *reinterpret_cast<const uint4*>(blk[g] + (2 * kt + s) * 1024 + lane * 16);
-            b.s[g][s] = sblk[g][(2 * kt + s) * 64 + lane];
+            for (int g = 0; g < 2; ++g) bs[buf][g] = *reinterpret_cast<const uint32_t*>(bs_src[g] + jj * 256);
         }
-}
-
-template <int MG>
-__device__ __forceinline__ void mx_mma(const char* buf, const MxB& b, f32x16_t (&acc)[MG][2], int lane) {
-    const char* sc = buf + 32 * MG * 128;
+        if (q == 1) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        v8i bv[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            bv[g] = v8i{static_cast<int>(b.d[g][s].x), static_cast<int>(b.d[g][s].y), static_cast<int>(b.d[g][s].z),
-                        static_cast<int>(b.d[g][s].w), 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int mi = 0; mi < MG; ++mi) {
-            const int row = 32 * mi + (lane & 31), h = lane >> 5;
-            const uint4 lo = *reinterpret_cast<const uint4*>(buf + mx_lds_off(row, 4 * s + h));
-            const uint4 hi = *reinterpret_cast<const uint4*>(buf + mx_lds_off(row, 4 * s + 2 + h));
-            const v8i av = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                            static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-            const int as = static_cast<int>(static_cast<const uint8_t*>(static_cast<const void*>(sc))[row * 4 + 2 * s + h]);
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
-                acc[mi][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[g], acc[mi][g], 0, 4, 0, as, 0,
-                                                                             static_cast<int>(b.s[g][s]));
+            for (int mi = 0; mi < MG; ++mi) as[buf][mi] = *reinterpret_cast<const uint2*>(as_src[mi] + jj * 8);
         }
     }
+    static constexpr int loads(int q) {
+        return (MxGemm<MG>::A_DMA + 3 - q) / 4 + 2 + (q == 0 ? 2 : 0) + (q == 1 ? MG : 0);
+    }
+};
+
+template <int MG>
+__device__ __forceinline__ void mx_read_a(v8i (&a)[MG], const char* __restrict__ slot, int J, int lane) {
+#pragma unroll
+    for (int mi = 0; mi < MG; ++mi) {
+        const int row = 32 * mi + (lane & 31), h = lane >> 5;
+        const uint4 lo = *reinterpret_cast<const uint4*>(slot + mx_lds_off(row, 4 * J + h));
+        const uint4 hi = *reinterpret_cast<const uint4*>(slot + mx_lds_off(row, 4 * J + 2 + h));
+        a[mi] = v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                    static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    }
+}
+
+// MFMA step J (0..3) of slot ring entry U: byte J of a scale dword is this step's scale (the
+// instruction's scale byte select); the loads of part J of slot j + 2 go out between the MFMAs.
+template <int MG, int U, int J, bool ISSUE>
+__device__ __forceinline__ void mx_step(MxPipe<MG>& p, int j, char* __restrict__ far, v8i (&a)[2][MG],
+                                        const uint32_t (&asel)[MG], const char* __restrict__ cur,
+                                        f32x16_t (&acc)[MG][2], int lane) {
+    constexpr int FAR = (U + kMxSlots - 1) % kMxSlots;
+    if (ISSUE) p.issue(j + kMxSlots - 1, far, FAR, J);
+    if (J < 3) mx_read_a<MG>(a[(J + 1) & 1], cur, J + 1, lane);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const uint4 bd = p.b[U][g][J];
+        const v8i bv = {static_cast<int>(bd.x), static_cast<int>(bd.y), static_cast<int>(bd.z), static_cast<int>(bd.w),
+                        0, 0, 0, 0};
+#pragma unroll
+        for (int mi = 0; mi < MG; ++mi)
+            acc[mi][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[J & 1][mi], bv, acc[mi][g], 0, 4, J,
+                                                                         static_cast<int>(asel[mi]), J,
+                                                                         static_cast<int>(p.bs[U][g]));
+    }
+    const int nv = ISSUE ? MxPipe<MG>::loads(J) : 0;
+#pragma unroll
+    for (int i = 0; i < 2 * MG; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+        if (J < 3 && i < 2 * MG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);               // global load
+    }
+    if (2 * MG < nv)
+        for (int i = 2 * MG; i < nv; ++i) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Slot j held in ring entry U.  WAIT: this wave's loads issued after slot j's, which may still be
+// in flight.
+template <int MG, int U, bool ISSUE, int WAIT>
+__device__ __forceinline__ void mx_slot(MxPipe<MG>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+                                        char* __restrict__ s2, f32x16_t (&acc)[MG][2], int lane) {
+    char* const slots[3] = {s0, s1, s2};
+    char* const cur = slots[U];
+    char* const far = slots[(U + kMxSlots - 1) % kMxSlots];
+    mx_wait_vmcnt<WAIT>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's fragment reads are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // A scale of (row, step J, 32-block h = lane / 32) is the row's slot byte 2 J + h: this lane's
+    // four, byte J for step J
+    uint32_t asel[MG];
+#pragma unroll
+    for (int mi = 0; mi < MG; ++mi)
+        asel[mi] = __builtin_amdgcn_perm(p.as[U][mi].y, p.as[U][mi].x, (lane >> 5) ? 0x07050301u : 0x06040200u);
+    v8i a[2][MG];
+    mx_read_a<MG>(a[0], cur, 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_step<MG, U, 0, ISSUE>(p, j, far, a, asel, cur, acc, lane);
+    mx_step<MG, U, 1, ISSUE>(p, j, far, a, asel, cur, acc, lane);
+    mx_step<MG, U, 2, ISSUE>(p, j, far, a, asel, cur, acc, lane);
+    mx_step<MG, U, 3, ISSUE>(p, j, far, a, asel, cur, acc, lane);
+}
+
+// acc = A[rows, 0:K] . B[0:K, cols].  Ends with no load in flight and all waves past their last
+// fragment read, so the caller may reuse the LDS.
+template <int MG>
+__device__ __forceinline__ void mx_k_loop(MxPipe<MG>& p, char* __restrict__ s0, char* __restrict__ s1,
+                                          char* __restrict__ s2, f32x16_t (&acc)[MG][2], int lane) {
+    constexpr int L = MxGemm<MG>::LOADS;
+#pragma unroll
+    for (int mi = 0; mi < MG; ++mi)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][g][r] = 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
+    // prologue: slots 0 and 1, all of one slot before any of the next (the waits count in issue order)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p.issue(0, s0, 0, q);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p.issue(1, s1, 1, q);
+    __builtin_amdgcn_sched_barrier(0);
+    int j = 0;
+    for (; j + kMxSlots <= p.nslot; j += kMxSlots) {
+        mx_slot<MG, 0, true, L>(p, j, s0, s1, s2, acc, lane);
+        mx_slot<MG, 1, true, L>(p, j + 1, s0, s1, s2, acc, lane);
+        mx_slot<MG, 2, true, L>(p, j + 2, s0, s1, s2, acc, lane);
+    }
+    // the last nslot % 3 slots: the loop (or the prologue) issued through slot j + 1
+    if (j < p.nslot) {
+        mx_slot<MG, 0, false, L>(p, j, s0, s1, s2, acc, lane);
+        if (j + 1 < p.nslot) mx_slot<MG, 1, false, 0>(p, j + 1, s0, s1, s2, acc, lane);
+    }
+    mx_wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // L1: gather the FP8 x rows through row_pair, GEMM against the FP4 W1, clamped SwiGLU, FP8 cast of
 // the activation rows (codes [R_max, I] and scale bytes [R_max, I / 32] in ws.act).
 // L2: GEMM of the FP8 activation rows against the FP4 W2, then the combine of the bf16 path
 // (bf16(w * o) into y for a token's only local pair, fp32 w * o into its stage row otherwise).
+// A tile is BM = 32 MG rows; block_m (d.BM) is a multiple of it, so a tile lies in one expert's block.
 template <int MG, bool L1>
 __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __restrict__ a_codes,
                                                              const uint8_t* __restrict__ a_scales,
@@ -262,88 +356,64 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __re
                                                              const uint8_t* __restrict__ wsc,
                                                              const float* __restrict__ topk_w, Dims d, Ws ws,
                                                              float clamp, uint16_t* __restrict__ y) {
-    using G = MxGemm<MG, L1>;
+    using G = MxGemm<MG>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    int4* s_row = reinterpret_cast<int4*>(smem + 2 * G::BUF);   // token (-1 padding), weight, single
+    char* const s0 = smem;
+    char* const s1 = smem + G::SLOT;
+    char* const s2 = smem + 2 * G::SLOT;
+    int4* s_row = reinterpret_cast<int4*>(smem + kMxSlots * G::SLOT);   // token (-1 padding), weight, single
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = L1 ? d.H : d.I, N = L1 ? 2 * d.I : d.H;
-    const int nk = K / 128, n_tiles = N / kMxBN;
+    const int n_tiles = N / kMxBN;
     const int npairs = d.T * d.k;
-    const int m_tiles = min(ws.meta[0] / G::BM, ws.num_blocks);
-    const int total = m_tiles * n_tiles;
+    const int64_t R = min(static_cast<int64_t>(ws.meta[0]), ws.rows_cap);
+    const int total = static_cast<int>(R / G::BM) * n_tiles;
     uint8_t* act_codes = reinterpret_cast<uint8_t*>(ws.act);
     uint8_t* act_scales = act_codes + ws.rows_cap * d.I;
     const uint8_t* zrow = reinterpret_cast<const uint8_t*>(ws.zeros);
+    MxPipe<MG> p;
+    p.nslot = K / kMxSK;
+    p.wave = wave;
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int mt = tile / n_tiles, nt = tile - mt * n_tiles;   // N tiles of an M tile adjacent: its rows stay in L2
-        const int e = ws.tile_expert[mt];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
         const int64_t row0 = static_cast<int64_t>(mt) * G::BM;
-        // row sources of this thread's A chunks and scale row
-        const uint8_t* rows[MG];
-        const uint8_t* srows[1];
+        const int e = ws.tile_expert[row0 / d.BM];
+        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
+        // sources (padding rows read the zero row)
 #pragma unroll
-        for (int i = 0; i < MG; ++i) {
-            const int r = (tid + i * kMxThreads) >> 3;
-            const int p = ws.row_pair[row0 + r];
-            const bool ok = p >= 0 && p < npairs;
-            rows[i] = !ok ? zrow : (L1 ? a_codes + static_cast<int64_t>(p / d.k) * K : a_codes + (row0 + r) * K);
+        for (int i = 0; i < G::A_DMA; ++i) {
+            const int r = 4 * (wave + kMxWaves * i) + (lane >> 4);
+            const int pr = ws.row_pair[row0 + r];
+            const bool ok = pr >= 0 && pr < npairs;
+            const uint8_t* src = !ok ? zrow : (L1 ? a_codes + static_cast<int64_t>(pr / d.k) * K : a_codes + (row0 + r) * K);
+            p.a_src[i] = reinterpret_cast<const char*>(src) + 16 * ((lane & 15) ^ (r & 15));
         }
-        {
-            const int r = tid < G::BM ? tid : 0;
-            const int p = ws.row_pair[row0 + r];
-            const bool ok = p >= 0 && p < npairs;
-            srows[0] = !ok ? zrow
-                           : (L1 ? a_scales + static_cast<int64_t>(p / d.k) * (K / 32) : a_scales + (row0 + r) * (K / 32));
+#pragma unroll
+        for (int mi = 0; mi < MG; ++mi) {
+            const int r = 32 * mi + (lane & 31);
+            const int pr = ws.row_pair[row0 + r];
+            const bool ok = pr >= 0 && pr < npairs;
+            p.as_src[mi] = !ok ? zrow
+                               : (L1 ? a_scales + static_cast<int64_t>(pr / d.k) * (K / 32) : a_scales + (row0 + r) * (K / 32));
         }
-        // this wave's two column groups of the packed weights
         const int64_t ebase = static_cast<int64_t>(e) * (N / 32) * (K / 64);
-        const uint8_t* blk[2];
-        const uint8_t* sblk[2];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const int64_t grp = ebase + static_cast<int64_t>(nt * 8 + wave * 2 + g) * (K / 64);
-            blk[g] = wq + grp * 1024;
-            sblk[g] = wsc + grp * 64;
+            p.b_src[g] = wq + grp * 1024 + lane * 16;
+            p.bs_src[g] = wsc + grp * 64 + lane * 4;
         }
-        f32x16_t acc[MG][2];
-#pragma unroll
-        for (int mi = 0; mi < MG; ++mi)
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mi][g][r] = 0.0f;
-
-        lds_barrier();   // the previous tile's LDS reads are done
-        if (tid < G::BM) {
-            const int p = ws.row_pair[row0 + tid];
-            const bool ok = p >= 0 && p < npairs;
-            const int t = ok ? p / d.k : -1;
-            const float w = ok && !L1 ? topk_w[p] : 0.0f;
+        __syncthreads();   // the previous tile's epilogue is done with s_row
+        if (tid < G::BM) {   // read in the epilogue, after the K loop's barriers
+            const int pr = ws.row_pair[row0 + tid];
+            const bool ok = pr >= 0 && pr < npairs;
+            const int t = ok ? pr / d.k : -1;
+            const float w = ok && !L1 ? topk_w[pr] : 0.0f;
             const int single = ok && !L1 ? (ws.tok_nloc[t] == 1) : 0;
             s_row[tid] = make_int4(t, __float_as_int(w), single, 0);
         }
-        MxStage<MG> st;
-        MxB b[2];
-        mx_load_a<MG>(st, rows, srows, 0, tid);
-        mx_load_b(b[0], blk, sblk, 0, lane);
-        mx_store_a<MG>(st, smem, tid);
-        lds_barrier();
-        for (int kt = 0; kt < nk; kt += 2) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int k = kt + u;
-                if (k >= nk) break;
-                const bool more = k + 1 < nk;
-                if (more) {
-                    mx_load_a<MG>(st, rows, srows, k + 1, tid);
-                    mx_load_b(b[u ^ 1], blk, sblk, k + 1, lane);
-                }
-                mx_mma<MG>(smem + u * G::BUF, b[u], acc, lane);
-                if (more) mx_store_a<MG>(st, smem + (u ^ 1) * G::BUF, tid);
-                lds_barrier();
-            }
-        }
+        f32x16_t acc[MG][2];
+        mx_k_loop<MG>(p, s0, s1, s2, acc, lane);
 
         if constexpr (L1) {
             // SwiGLU on (gate, up) = column groups (0, 1); the wave's 32 intermediate columns are one
@@ -397,7 +467,7 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __re
 template <int MG, bool L1>
 hipError_t mx_gemm_launch(const Dims& d, const uint8_t* ac, const uint8_t* as, const uint8_t* wq, const uint8_t* wsc,
                           const float* topk_w, const Ws& ws, float clamp, uint16_t* y, hipStream_t s) {
-    using G = MxGemm<MG, L1>;
+    using G = MxGemm<MG>;
     auto k = mx_gemm_kernel<MG, L1>;
     if (G::LDS > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
@@ -406,7 +476,7 @@ hipError_t mx_gemm_launch(const Dims& d, const uint8_t* ac, const uint8_t* as, c
         per_cu = 1;
     const int n_tiles = (L1 ? 2 * d.I : d.H) / kMxBN;
     int64_t grid = static_cast<int64_t>(per_cu) * device_cu_count();
-    const int64_t tiles = static_cast<int64_t>(ws.num_blocks) * n_tiles;
+    const int64_t tiles = ws.rows_cap / G::BM * n_tiles;
     if (grid > tiles) grid = tiles;
     if (grid < 1) grid = 1;
     k<<<static_cast<int>(grid), kMxThreads, G::LDS, s>>>(ac, as, wq, wsc, topk_w, d, ws, clamp, y);
@@ -416,13 +486,10 @@ hipError_t mx_gemm_launch(const Dims& d, const uint8_t* ac, const uint8_t* as, c
 template <bool L1>
 hipError_t mx_gemm(const Dims& d, const uint8_t* ac, const uint8_t* as, const uint8_t* wq, const uint8_t* wsc,
                    const float* topk_w, const Ws& ws, float clamp, uint16_t* y, hipStream_t s) {
-    switch (d.BM) {
-        case 32: return mx_gemm_launch<1, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
-        case 64: return mx_gemm_launch<2, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
-        case 128: return mx_gemm_launch<4, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
-        case 256: return mx_gemm_launch<8, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
-        default: return hipErrorInvalidValue;
-    }
+    // 32-row tiles for block_m 32; 64-row tiles otherwise (block_m is 64, 128 or 256)
+    if (d.BM == 32) return mx_gemm_launch<1, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
+    if (d.BM % 64 == 0) return mx_gemm_launch<2, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
+    return hipErrorInvalidValue;
 }
 
 int grid_for(int64_t items) {
