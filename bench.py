@@ -306,7 +306,7 @@ def bench_mx(a):
     log("generating %s inputs (seed 0)" % w.name)
     d = mw.inputs(w, 0)
     P = mw.local_pairs(w, d["topk_idx"])
-    bm = a.block_m or 32
+    bm = a.block_m or 64   # 64-row MX tiles: an expert's ~62 rows of this share in one tile, its weights streamed once
     shape = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=bm, e_lo=w.e_lo)
     x = bf16_dev(d["x"])
     idx = torch.from_numpy(d["topk_idx"]).cuda()

@@ -177,7 +177,7 @@ constexpr int kMxThreads = 256;
 constexpr int kMxWaves = 4;
 constexpr int kMxBN = 256;
 constexpr int kMxSK = 256;   // K per slot
-constexpr int kMxSlots = 3;
+constexpr int kMxSlots = 3;   // ring slots: loads go out kMxSlots - 1 slots ahead (four measured no faster)
 
 // 16-byte chunk c of LDS row r (256 bytes) sits at position c ^ (r % 16).
 __device__ __forceinline__ int mx_lds_off(int row, int chunk) { return row * kMxSK + ((chunk ^ (row & 15)) << 4); }
@@ -192,6 +192,7 @@ __device__ __forceinline__ void mx_wait_vmcnt() {
 
 template <int MG>
 struct MxGemm {
+    static_assert(kMxSlots == 3 || kMxSlots == 4, "ring of three or four slots");
     static constexpr int BM = 32 * MG;
     static constexpr int SLOT = BM * kMxSK;                 // bytes of one A slot
     static constexpr int LDS = kMxSlots * SLOT + 16 * BM;   // ring + row info
@@ -284,8 +285,9 @@ __device__ __forceinline__ void mx_step(MxPipe<MG>& p, int j, char* __restrict__
 // in flight.
 template <int MG, int U, bool ISSUE, int WAIT>
 __device__ __forceinline__ void mx_slot(MxPipe<MG>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
-                                        char* __restrict__ s2, f32x16_t (&acc)[MG][2], int lane) {
-    char* const slots[3] = {s0, s1, s2};
+                                        char* __restrict__ s2, char* __restrict__ s3, f32x16_t (&acc)[MG][2],
+                                        int lane) {
+    char* const slots[4] = {s0, s1, s2, s3};
     char* const cur = slots[U];
     char* const far = slots[(U + kMxSlots - 1) % kMxSlots];
     mx_wait_vmcnt<WAIT>();
@@ -307,12 +309,51 @@ __device__ __forceinline__ void mx_slot(MxPipe<MG>& p, int j, char* __restrict__
     mx_step<MG, U, 3, ISSUE>(p, j, far, a, asel, cur, acc, lane);
 }
 
+// Slots j + I .. j + kMxSlots - 1 of one turn of the unrolled loop.
+template <int MG, int I>
+__device__ __forceinline__ void mx_turn(MxPipe<MG>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+                                        char* __restrict__ s2, char* __restrict__ s3, f32x16_t (&acc)[MG][2],
+                                        int lane) {
+    if constexpr (I < kMxSlots) {
+        mx_slot<MG, I, true, (kMxSlots - 2) * MxGemm<MG>::LOADS>(p, j + I, s0, s1, s2, s3, acc, lane);
+        mx_turn<MG, I + 1>(p, j, s0, s1, s2, s3, acc, lane);
+    }
+}
+
+// The last nslot % kMxSlots slots (j a multiple of kMxSlots): the loop (or the prologue) issued
+// through slot j + kMxSlots - 2, so kMxSlots - 2 - I slots' loads follow those of slot j + I.
+template <int MG, int I>
+__device__ __forceinline__ void mx_tail(MxPipe<MG>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+                                        char* __restrict__ s2, char* __restrict__ s3, f32x16_t (&acc)[MG][2],
+                                        int lane) {
+    if constexpr (I < kMxSlots - 1) {
+        if (j + I < p.nslot) {
+            mx_slot<MG, I, false, (kMxSlots - 2 - I) * MxGemm<MG>::LOADS>(p, j + I, s0, s1, s2, s3, acc, lane);
+            mx_tail<MG, I + 1>(p, j, s0, s1, s2, s3, acc, lane);
+        }
+    }
+}
+
+// Prologue: the loads of slots I .. kMxSlots - 2, all of one slot before any of the next (the
+// waits count in issue order).
+template <int MG, int I>
+__device__ __forceinline__ void mx_prologue(MxPipe<MG>& p, char* __restrict__ s0, char* __restrict__ s1,
+                                            char* __restrict__ s2) {
+    if constexpr (I < kMxSlots - 1) {
+        char* const slots[3] = {s0, s1, s2};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p.issue(I, slots[I], I, q);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_prologue<MG, I + 1>(p, s0, s1, s2);
+    }
+}
+
 // acc = A[rows, 0:K] . B[0:K, cols].  Ends with no load in flight and all waves past their last
-// fragment read, so the caller may reuse the LDS.
+// fragment read, so the caller may reuse the LDS.  s3 is unused with three slots.
 template <int MG>
 __device__ __forceinline__ void mx_k_loop(MxPipe<MG>& p, char* __restrict__ s0, char* __restrict__ s1,
-                                          char* __restrict__ s2, f32x16_t (&acc)[MG][2], int lane) {
-    constexpr int L = MxGemm<MG>::LOADS;
+                                          char* __restrict__ s2, char* __restrict__ s3, f32x16_t (&acc)[MG][2],
+                                          int lane) {
 #pragma unroll
     for (int mi = 0; mi < MG; ++mi)
 #pragma unroll
@@ -320,24 +361,10 @@ __device__ __forceinline__ void mx_k_loop(MxPipe<MG>& p, char* __restrict__ s0, 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][g][r] = 0.0f;
     __builtin_amdgcn_sched_barrier(0);
-    // prologue: slots 0 and 1, all of one slot before any of the next (the waits count in issue order)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) p.issue(0, s0, 0, q);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) p.issue(1, s1, 1, q);
-    __builtin_amdgcn_sched_barrier(0);
+    mx_prologue<MG, 0>(p, s0, s1, s2);
     int j = 0;
-    for (; j + kMxSlots <= p.nslot; j += kMxSlots) {
-        mx_slot<MG, 0, true, L>(p, j, s0, s1, s2, acc, lane);
-        mx_slot<MG, 1, true, L>(p, j + 1, s0, s1, s2, acc, lane);
-        mx_slot<MG, 2, true, L>(p, j + 2, s0, s1, s2, acc, lane);
-    }
-    // the last nslot % 3 slots: the loop (or the prologue) issued through slot j + 1
-    if (j < p.nslot) {
-        mx_slot<MG, 0, false, L>(p, j, s0, s1, s2, acc, lane);
-        if (j + 1 < p.nslot) mx_slot<MG, 1, false, 0>(p, j + 1, s0, s1, s2, acc, lane);
-    }
+    for (; j + kMxSlots <= p.nslot; j += kMxSlots) mx_turn<MG, 0>(p, j, s0, s1, s2, s3, acc, lane);
+    mx_tail<MG, 0>(p, j, s0, s1, s2, s3, acc, lane);
     mx_wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
@@ -361,6 +388,7 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __re
     char* const s0 = smem;
     char* const s1 = smem + G::SLOT;
     char* const s2 = smem + 2 * G::SLOT;
+    char* const s3 = smem + (kMxSlots - 1) * G::SLOT;   // the fourth slot (unused with three)
     int4* s_row = reinterpret_cast<int4*>(smem + kMxSlots * G::SLOT);   // token (-1 padding), weight, single
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = L1 ? d.H : d.I, N = L1 ? 2 * d.I : d.H;
@@ -413,7 +441,7 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __re
             s_row[tid] = make_int4(t, __float_as_int(w), single, 0);
         }
         f32x16_t acc[MG][2];
-        mx_k_loop<MG>(p, s0, s1, s2, acc, lane);
+        mx_k_loop<MG>(p, s0, s1, s2, s3, acc, lane);
 
         if constexpr (L1) {
             // SwiGLU on (gate, up) = column groups (0, 1); the wave's 32 intermediate columns are one
