@@ -266,13 +266,13 @@ def bench_backward(a):
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA (the FP8 x FP4 instruction is priced at the rate of its FP8 operand)
 
 
-def cpu_baseline_mx(w, d, budget_s=15.0):
+def cpu_baseline_mx(w, d, budget_s=12.0):
     """The MX oracle timed on the host cores on a bounded sample of tokens (the oracle's FP8 / FP4
     casts of the inputs are made beforehand for the experts the sample touches, untimed)."""
     import oracle
     idx = d["topk_idx"]
     local = (idx >= w.e_lo) & (idx < w.e_lo + w.EL)
-    toks = np.random.default_rng(0).permutation(np.nonzero(local.any(axis=1))[0])[:64]
+    toks = np.random.default_rng(0).permutation(np.nonzero(local.any(axis=1))[0])[:192]
     sel = idx[toks]
     experts = sorted(set((sel[(sel >= w.e_lo) & (sel < w.e_lo + w.EL)] - w.e_lo).tolist()))
     xc, xs = oracle.mx_quantize(oracle.MX_FP8, mw.bf16_bits_to_f32(d["x"]).astype(np.float64))
