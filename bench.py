@@ -46,6 +46,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_grouped.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_dsv3_share_traffic.json")
+MX_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_mx.hip")
+MX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mx_gemm1_wide_share_traffic.json")
 
 
 def log(msg):
@@ -56,22 +58,32 @@ def bf16_dev(u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def kernel_source_hash():
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(src=GEMM_SRC):
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, path=TRAFFIC_FILE, src=GEMM_SRC):
     """HBM bytes per L1 launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel source and on this workload; else None."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     if rec.get("workload", "dsv3_share_fwd") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain copy of known size (1 GiB read, 1 GiB written), for HBM counter scaling."""
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(w, d, budget_s=15.0):
@@ -320,6 +332,8 @@ def bench_mx(a):
     y = torch.empty(w.T, w.H, dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    if a.copy_calibration:
+        copy_calibration()
     fwd = lambda: moe.forward_mx(shape, xq, xs, idx, wts, w1q, w1s, w2q, w2s, ws, y)
     log("warmup %d" % a.warmup)
     for _ in range(a.warmup):
@@ -373,7 +387,8 @@ def bench_mx(a):
     else:
         roof = {"bound": "mfma", "achieved": l1_flops / l1_s / 1e12, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": l1_flops / l1_s / 1e12 / PEAK_FP8_TFLOPS}
-    roof.update({"traffic": None, "kernel": "MX gemm1 (dispatch gather of FP8 x + L1 + clamped SwiGLU + FP8 cast)",
+    roof.update({"traffic": measured_traffic(w.name, MX_TRAFFIC_FILE, MX_SRC),
+                 "kernel": "MX gemm1 (dispatch gather of FP8 x + L1 + clamped SwiGLU + FP8 cast)",
                  "alg_bytes_per_launch": l1_bytes, "alg_flops_per_launch": l1_flops,
                  "intensity_flop_per_byte": round(l1_flops / l1_bytes, 1),
                  "hbm_frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS,
@@ -449,13 +464,8 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
-    if a.copy_calibration:   # a plain copy of known size, for HBM counter scaling
-        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    if a.copy_calibration:
+        copy_calibration()
 
     fwd = lambda: moe.forward(shape, x, idx, wts, W1p, W2p, ws, y)
     log("warmup %d" % a.warmup)

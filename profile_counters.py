@@ -7,9 +7,12 @@ known / measured on that copy, so the figures are in true HBM bytes whatever uni
 
     python profile_counters.py --trace TRACE_DIR --out-json profiles/gemm1_dsv3_share_traffic.json \
         PASS_DIR [PASS_DIR ...] > profiles/forward_dsv3_share_counters.md
+    python profile_counters.py --variant mx --trace TRACE_DIR \
+        --out-json profiles/mx_gemm1_wide_share_traffic.json PASS_DIR [...] > profiles/forward_mx_wide_share_counters.md
 
 Writes the L1 launch's HBM bytes (read + write) with the hash of the kernel source they were taken
-on (bench.py reports them only while that source is unchanged) and prints a markdown table.
+on (bench.py reports them only while that source is unchanged) and prints a markdown table.  With
+--variant mx the kernels are those of bench.py --mx (the FP8 x FP4 forward).
 """
 import argparse
 import collections
@@ -22,16 +25,27 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_grouped.hip")
+MX_SRC = os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", "moe_mx.hip")
 COPY_BYTES = 1 << 30   # bench.py --copy-calibration: one 1 GiB buffer copied to another
-KINDS = (("l1_kernel", "L1: dispatch gather + grouped GEMM + SwiGLU"),
-         ("l2_kernel", "L2: grouped GEMM + weighted combine"),
-         ("combine_finish", "combine finish (multi-pair tokens)"),
-         ("route_count", "prologue: count"), ("route_scan", "prologue: scan"),
-         ("route_place", "prologue: place"))
+COMMON = (("combine_finish", "combine finish (multi-pair tokens)"),
+          ("route_count", "prologue: count"), ("route_scan", "prologue: scan"),
+          ("route_place", "prologue: place"))
+VARIANTS = {
+    "bf16": {"title": "DeepSeek-V3 share forward", "src": GEMM_SRC, "l1": "l1_kernel", "workload": "dsv3_share_fwd",
+             "kinds": (("l1_kernel", "L1: dispatch gather + grouped GEMM + SwiGLU"),
+                       ("l2_kernel", "L2: grouped GEMM + weighted combine")) + COMMON},
+    "mx": {"title": "MX (FP8 x FP4) forward, wide-expert share", "src": MX_SRC, "l1": "mx_l1",
+           "workload": "wide_share_mx_fwd",
+           "kinds": (("mx_l1", "MX L1: dispatch gather + FP8 x FP4 GEMM + clamped SwiGLU + FP8 cast"),
+                     ("mx_l2", "MX L2: FP8 x FP4 GEMM + weighted combine")) + COMMON},
+}
+KINDS = VARIANTS["bf16"]["kinds"]
 
 
 def kind_of(name):
-    for key, _ in KINDS:
+    if "mx_gemm_kernel" in name:
+        return "mx_l1" if ", true>" in name else "mx_l2"
+    for key, _ in KINDS + VARIANTS["mx"]["kinds"]:
         if key in name:
             return key
     if "copyBuffer" in name or ("copy" in name.lower() and "repack" not in name):
@@ -73,8 +87,10 @@ def main():
     ap.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--out-json", required=True)
     ap.add_argument("--command", default="", help="the command lines that made the passes, for the record")
+    ap.add_argument("--variant", choices=sorted(VARIANTS), default="bf16")
     ap.add_argument("passes", nargs="+")
     a = ap.parse_args()
+    var = VARIANTS[a.variant]
     c = read_counters(a.passes)
     dur = read_durations(a.trace)
     cp = c.get("copy", {})
@@ -83,16 +99,17 @@ def main():
     # counters are in KiB; scale each to the copy's known bytes
     fr = COPY_BYTES / (cp["FETCH_SIZE"] * 1024.0)
     fw = COPY_BYTES / (cp["WRITE_SIZE"] * 1024.0)
-    print("# rocprofv3 counters per kernel (DeepSeek-V3 share forward)\n")
+    print("# rocprofv3 counters per kernel (%s)\n" % var["title"])
     if a.command:
         print("Commands (run from /tmp with TMPDIR=/tmp, repository at $R):\n\n```\n%s\n```\n" % a.command)
     print("FETCH_SIZE and WRITE_SIZE are scaled by what they read on a plain 1 GiB device copy: "
           "read x %.3f, write x %.3f.  Durations are the kernel-trace averages of the same workload; "
           "MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs.\n" % (fr, fw))
-    print("| kernel | avg us | HBM read MB | HBM write MB | HBM GB/s | MFMA busy % | bf16 MFMA TFLOP/s |")
+    print("| kernel | avg us | HBM read MB | HBM write MB | HBM GB/s | MFMA busy %% | %s |"
+          % ("bf16 MFMA TFLOP/s" if a.variant == "bf16" else "MFMA TFLOP/s (not counted)"))
     print("|---|---|---|---|---|---|---|")
     rec = {}
-    for key, label in KINDS:
+    for key, label in var["kinds"]:
         if key not in c:
             continue
         v = c[key]
@@ -105,9 +122,10 @@ def main():
         tf = fl / t / 1e12 if t else float("nan")
         print("| %s | %.1f | %.1f | %.1f | %.0f | %.1f | %.0f |" % (label, (t or 0) * 1e6, rd / 1e6, wr / 1e6, bw, busy, tf))
         rec[key] = {"read_bytes": rd, "write_bytes": wr, "avg_s": t, "mfma_busy_pct": busy, "mfma_bf16_flops": fl}
-    l1 = rec.get("l1_kernel")
+    l1 = rec.get(var["l1"])
     if l1:
-        out = {"kernel_source_sha256_16": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16],
+        out = {"kernel_source_sha256_16": hashlib.sha256(open(var["src"], "rb").read()).hexdigest()[:16],
+               "workload": var["workload"],
                "hbm_bytes_per_launch": l1["read_bytes"] + l1["write_bytes"],
                "hbm_read_bytes_per_launch": l1["read_bytes"], "hbm_write_bytes_per_launch": l1["write_bytes"],
                "copy_scale_read": fr, "copy_scale_write": fw, "kernels": rec, "command": a.command}
