@@ -312,3 +312,64 @@ def test_mx_rejects_unsupported_shapes():
     with pytest.raises(moe.MoeError, match="size"):
         moe.mx_gemm2_combine(s, w2q, w2s, wts, ws, y)
     torch.cuda.synchronize()
+
+
+def test_mx_forward_is_deterministic_and_graph_capturable():
+    """Two eager MX forwards give the same y bit for bit; the MX forward captured into a HIP graph
+    replays it bit for bit over a stale workspace, with eager work between the replays."""
+    w = REDUCED[0]
+    d = mw.inputs(w, 24)
+    s, args, _ = mx_layer(w, d, 64, experts=[])
+    *inputs, ws, y = args
+    y0 = torch.empty_like(y)
+    moe.forward_mx(s, *inputs, ws, y0)
+    moe.forward_mx(s, *inputs, ws, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y.view(torch.int16))
+    yg = torch.full_like(y, float("nan"))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        moe.forward_mx(s, *inputs, ws, yg)   # warm up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            moe.forward_mx(s, *inputs, ws, yg)
+    torch.cuda.current_stream().wait_stream(stream)
+    for i in range(3):
+        yg.fill_(float("nan"))
+        ws.fill_(0x7f)   # stale workspace between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg.view(torch.int16), y0.view(torch.int16)), "replay %d differs" % i
+        moe.forward_mx(s, *inputs, ws, y)   # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", ["empty_batch", "none_local", "one_expert_takes_all"])
+def test_mx_degenerate_routing(case):
+    """No tokens at all; tokens none of whose pairs this GPU handles (y exactly zero); every pair on
+    one expert (several M tiles of one expert, checked link by link)."""
+    w = mw.Workload("mx_degenerate", T=96, H=256, I=256, E=12, EL=4, k=2, e_lo=4)
+    if case == "empty_batch":
+        w = mw.scaled(w, T=0)
+    d = mw.inputs(w, 15)
+    idx = d["topk_idx"].copy()
+    if case == "none_local":
+        idx = np.where((idx >= w.e_lo) & (idx < w.e_lo + w.EL), idx + w.EL, idx) % w.E
+        idx = np.where((idx >= w.e_lo) & (idx < w.e_lo + w.EL), 0, idx).astype(np.int32)
+    elif case == "one_expert_takes_all":
+        idx[:] = w.e_lo + 2
+    d = dict(d, topk_idx=idx)
+    y, ref_codes, gc, gs, row_pair, pair_row = run_mx_forward(w, d, 64)
+    local = (idx >= w.e_lo) & (idx < w.e_lo + w.EL)
+    rows = np.nonzero(row_pair >= 0)[0]
+    assert len(rows) == int(local.sum())
+    if w.T == 0:
+        return
+    if case == "none_local":
+        assert np.all(y == 0.0)
+        return
+    check_act_link(w, d, ref_codes, row_pair[rows], gc[rows], gs[rows])
+    check_l2_link(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs)
