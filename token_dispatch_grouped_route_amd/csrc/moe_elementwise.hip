@@ -177,7 +177,12 @@ hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s) {
 // local pair were written by the L2 epilogue and are left alone.
 // ---------------------------------------------------------------------------------------------
 // One wave per token: lanes [0, k) read the token's pair rows at once and a ballot lists its local
-// pairs in slot order, so a token costs one dependent load before its stage rows stream.
+// pairs in slot order, so a token costs one dependent load before its stage rows stream.  A pass
+// covers up to kFinishChunks 32-byte chunks per lane: all of one pair row's chunks are loaded
+// before they are added, so a pass waits once per local pair, not once per chunk; each element is
+// still summed in slot order.
+constexpr int kFinishChunks = 4;
+
 __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws ws, uint16_t* __restrict__ y) {
     const int lane = threadIdx.x & 63;
     const int waves = gridDim.x * (kEwThreads / 64);
@@ -187,16 +192,37 @@ __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws w
         if (lane < d.k) r = ws.pair_row[static_cast<int64_t>(t) * d.k + lane];
         const uint64_t local = __ballot(r >= 0 && r < ws.rows_cap);
         if (__popcll(local) == 1) continue;   // the GEMM epilogue stored this token's only row
-        for (int c = lane; c < v8; c += 64) {
-            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int c0 = lane; c0 < v8; c0 += 64 * kFinishChunks) {
+            float acc[kFinishChunks][8];
+#pragma unroll
+            for (int i = 0; i < kFinishChunks; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
             for (uint64_t m = local; m; m &= m - 1) {   // local pairs in slot order
                 const int row = __shfl(r, __ffsll(static_cast<unsigned long long>(m)) - 1);
-                const float4* src = reinterpret_cast<const float4*>(ws.stage + static_cast<int64_t>(row) * d.H + 8 * c);
-                const float4 lo = src[0], hi = src[1];
-                acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
-                acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+                const float4* src = reinterpret_cast<const float4*>(ws.stage + static_cast<int64_t>(row) * d.H);
+                float4 lo[kFinishChunks], hi[kFinishChunks];
+#pragma unroll
+                for (int i = 0; i < kFinishChunks; ++i) {
+                    const int c = c0 + 64 * i;
+                    if (c < v8) {
+                        lo[i] = src[2 * c];
+                        hi[i] = src[2 * c + 1];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kFinishChunks; ++i) {
+                    if (c0 + 64 * i < v8) {
+                        acc[i][0] += lo[i].x; acc[i][1] += lo[i].y; acc[i][2] += lo[i].z; acc[i][3] += lo[i].w;
+                        acc[i][4] += hi[i].x; acc[i][5] += hi[i].y; acc[i][6] += hi[i].z; acc[i][7] += hi[i].w;
+                    }
+                }
             }
-            *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * d.H + 8 * c) = pack8(acc);
+#pragma unroll
+            for (int i = 0; i < kFinishChunks; ++i) {
+                const int c = c0 + 64 * i;
+                if (c < v8) *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * d.H + 8 * c) = pack8(acc[i]);
+            }
         }
     }
 }
