@@ -40,7 +40,8 @@ int32_t layout_of(const moe_shape* s, moe_ws_layout* L) {
     const int64_t BM = s->block_m;
     const int64_t pairs = static_cast<int64_t>(s->T) * s->k;
     const int64_t R = (pairs + static_cast<int64_t>(s->EL) * (BM - 1) + BM - 1) / BM * BM;
-    const int64_t chunks = pairs > 0 ? (pairs + kRouteChunk - 1) / kRouteChunk : 1;
+    const int64_t rc = route_chunk_for(pairs, s->EL);
+    const int64_t chunks = pairs > 0 ? (pairs + rc - 1) / rc : 1;
     const size_t H = s->H, I = s->I, EL = s->EL;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -112,7 +113,8 @@ int32_t prepare(const moe_shape* s, const void* ws, size_t ws_bytes, bool need_t
     w->dtw_part = s->train ? reinterpret_cast<float*>(b + L->dtw_part) : nullptr;
     w->dtw_cols = s->I / 128;
     const int64_t pairs = static_cast<int64_t>(s->T) * s->k;
-    w->num_chunks = static_cast<int32_t>(pairs > 0 ? (pairs + kRouteChunk - 1) / kRouteChunk : 1);
+    w->route_chunk = route_chunk_for(pairs, s->EL);
+    w->num_chunks = static_cast<int32_t>(pairs > 0 ? (pairs + w->route_chunk - 1) / w->route_chunk : 1);
     w->chunk_hist = reinterpret_cast<int32_t*>(b + L->scratch);
     w->chunk_dropped = w->chunk_hist + static_cast<int64_t>(w->num_chunks) * s->EL;
     w->zeros = reinterpret_cast<uint16_t*>(b + L->zeros);

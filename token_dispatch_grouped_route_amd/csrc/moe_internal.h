@@ -38,14 +38,25 @@ struct Ws {
     int32_t* tile_sync;     // [kMaxGrid] tile-scheduler counters of the forward GEMMs (zero between launches)
     int64_t rows_cap;
     int32_t num_blocks;     // R_max / BM
-    int32_t num_chunks;     // prologue chunks of kRouteChunk pairs
+    int32_t num_chunks;     // prologue chunks of route_chunk pairs
+    int32_t route_chunk;    // pairs per prologue block (route_chunk_for)
     int32_t zero_len;       // elements of the zero row
     int32_t dtw_cols;       // I / 128: partials per row in dtw_part
 };
 
 constexpr int kRouteThreads = 256;
 constexpr int kMaxGrid = 512;   // workgroups of a persistent GEMM launch, at most
-constexpr int kRouteChunk = 2048;   // pairs per prologue block
+constexpr int kRouteChunkMin = 512;   // pairs per prologue block, at least
+constexpr int kFusedHist = 8192;      // chunks x local experts staged in LDS by the fused scan + place launch
+
+// Pairs per prologue block: the smallest power of two >= kRouteChunkMin that cuts the pairs into at
+// most 256 chunks (one block per CU) and keeps chunks x local experts within the fused launch's
+// LDS staging when it can.  Small batches then get more, shorter blocks.
+inline int32_t route_chunk_for(int64_t pairs, int EL) {
+    int64_t c = kRouteChunkMin;
+    while (c < (int64_t(1) << 30) && ((pairs + c - 1) / c > 256 || (pairs + c - 1) / c * EL > kFusedHist)) c <<= 1;
+    return static_cast<int32_t>(c);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -3,7 +3,7 @@
 // "How Mega MoE Overlaps ..." page, Block-M Alignment).
 //
 // Two launches with fixed grids, none waiting on the host:
-//   1. count: each block histograms the experts of one chunk of kRouteChunk pairs (LDS
+//   1. count: each block histograms the experts of one chunk of pairs (LDS
 //      counters) and counts the local pairs of a slice of tokens.
 //   2. scan + place: every block stages all chunk histograms in LDS and derives what it needs
 //      itself: per expert the total, the padded segment offsets (a block-wide scan) and its own
@@ -38,8 +38,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_
     __syncthreads();
 
     const int64_t npairs = static_cast<int64_t>(d.T) * d.k;
-    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kRouteChunk;
-    const int64_t p1 = min(npairs, p0 + kRouteChunk);
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * ws.route_chunk;
+    const int64_t p1 = min(npairs, p0 + ws.route_chunk);
     int drop = 0;
     for (int64_t p = p0 + tid; p < p1; p += blockDim.x) {
         const int32_t id = idx[p];
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_
     int32_t* wcnt = sm + d.EL;            // [kPlaceWaves][EL]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t npairs = static_cast<int64_t>(d.T) * d.k;
-    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kRouteChunk;
-    const int64_t p1 = min(npairs, p0 + kRouteChunk);
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * ws.route_chunk;
+    const int64_t p1 = min(npairs, p0 + ws.route_chunk);
 
     for (int e = tid; e < d.EL; e += blockDim.x)
         base[e] = ws.offsets[e] + ws.chunk_hist[static_cast<int64_t>(blockIdx.x) * d.EL + e];
@@ -189,7 +189,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_
     }
 }
 
-constexpr int kFusedHist = 8192;   // chunks x local experts staged in LDS by the fused launch
 
 // Scan + place in one launch (see the top of the file).  LDS: hist [nch * EL], tot, mine, off
 // [EL + 1], base, wcnt [kPlaceWaves * EL], scan [kRouteThreads].
@@ -284,8 +283,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_place_kernel(const i
 
     // placement
     const int64_t npairs = static_cast<int64_t>(d.T) * d.k;
-    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kRouteChunk;
-    const int64_t p1 = min(npairs, p0 + kRouteChunk);
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * ws.route_chunk;
+    const int64_t p1 = min(npairs, p0 + ws.route_chunk);
     for (int e = tid; e < EL; e += blockDim.x) base[e] = off[e] + mine[e];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int64_t s0 = p0; s0 < p1; s0 += kRouteThreads) {
