@@ -559,20 +559,21 @@ struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
 // k (a 32-row block spans two 16-deep K steps) and its N index the packed column n (a 32-column
 // block is one packed column group).  Lane L holds column n0 + L%32 and k = k0 + 8*(r/4) +
 // 4*(L/32) + r%4 for r = 0..15, while a packed block wants lane L to hold the 8 consecutive k from
-// 8*(L/32) of each 16-deep step; so lanes L and L^32 trade four values per step, and every lane
-// then stores 16 bytes: one store instruction writes a whole 1 KB block.
+// 8*(L/32) of each 16-deep step; so lanes L and L^32 trade four values per step (one
+// v_permlane32_swap each, a VALU exchange of the two half-waves: lane L < 32 keeps a and gets the a
+// of lane L + 32, lane L >= 32 gets the b of lane L - 32 and keeps b), and every lane then stores
+// 16 bytes: one store instruction writes a whole 1 KB block.
 __device__ __forceinline__ void store_grad_block(uint16_t* out, int64_t K, int64_t n0, int64_t k0,
                                                  const f32x16_t& acc, int lane) {
-    const bool lo = lane < 32;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         float v[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float a = acc[8 * st + q], b = acc[8 * st + 4 + q];
-            const float got = __shfl_xor(lo ? b : a, 32);
-            v[q] = lo ? a : got;
-            v[4 + q] = lo ? got : b;
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[8 * st + q]),
+                                                            __float_as_uint(acc[8 * st + 4 + q]), false, false);
+            v[q] = __uint_as_float(r[0]);
+            v[4 + q] = __uint_as_float(r[1]);
         }
         u32x4 pk;
 #pragma unroll
@@ -802,6 +803,7 @@ using G64 = Cfg<64, 128, 2, 2>;
 using G128 = Cfg<128, 128, 2, 2>;
 using G256 = Cfg<256, 128, 4, 1>;
 using WG = Cfg<128, 128, 2, 2, 0>;   // weight-gradient tiles: K is an expert's rows, often one step
+using WG1 = Cfg<256, 128, 4, 1, 0>;  // dW1 with H a multiple of 256: fewer, taller tiles measured faster
 
 template <class C0>
 static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
@@ -862,11 +864,17 @@ hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w,
     return hipGetLastError();
 }
 
-hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
-    const int blocks = d.EL * (d.H / WG::BM) * ((2 * d.I / WG::BN + kWgradChunk - 1) / kWgradChunk);
+template <class C>
+static hipError_t wgrad1_launch(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
+    const int blocks = d.EL * (d.H / C::BM) * ((2 * d.I / C::BN + kWgradChunk - 1) / kWgradChunk);
     if (blocks <= 0) return hipSuccess;
-    wgrad1_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES, s>>>(x, d, ws, dw1p);
+    wgrad1_kernel<C><<<blocks, C::NT, C::LDS_BYTES, s>>>(x, d, ws, dw1p);
     return hipGetLastError();
+}
+
+hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
+    if (d.H % WG1::BM == 0) return wgrad1_launch<WG1>(d, x, ws, dw1p, s);
+    return wgrad1_launch<WG>(d, x, ws, dw1p, s);
 }
 
 }  // namespace moe
