@@ -48,7 +48,7 @@ def kind_of(name):
     for key, _ in KINDS + VARIANTS["mx"]["kinds"]:
         if key in name:
             return key
-    if "copyBuffer" in name or ("copy" in name.lower() and "repack" not in name):
+    if "copyBuffer" in name:   # the runtime's plain device copy (--copy-calibration); conversion copies do not count
         return "copy"
     return None
 
