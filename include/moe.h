@@ -23,8 +23,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).
  *   - Ownership: the caller owns every buffer (inputs, weights, outputs, workspace) and must
  *     keep it alive until the enqueued work completes.  The library allocates nothing, frees
- *     nothing, copies nothing between host and device and keeps no state between calls, so
- *     calls with distinct workspaces may run concurrently on different streams.
+ *     nothing, copies nothing between host and device and keeps no state between calls (beyond
+ *     cached device properties and kernel attributes), so calls with distinct workspaces may run
+ *     concurrently on different streams.
  *   - Workspace: `ws` is a device buffer of at least moe_workspace_bytes(shape) bytes, 256-B
  *     aligned.  The stages of one layer communicate through it and rely on stream order:
  *     moe_route_prologue, then moe_dispatch_gemm1, then moe_gemm2_combine, on one stream.
@@ -262,6 +263,7 @@ int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* 
  *   x      [device] bf16 [rows, cols], cols a multiple of 32
  *   codes  [device] uint8 [rows, cols]       FP8 E4M3 codes
  *   scales [device] uint8 [rows, cols / 32]  UE8M0 bytes
+ * MOE_ERR_SHAPE for rows < 0 or cols not a positive multiple of 32; x and codes 16-byte aligned.
  */
 int32_t moe_mx_cast_fp8(int64_t rows, int32_t cols, const uint16_t* x, uint8_t* codes, uint8_t* scales,
                         void* stream);

@@ -673,11 +673,13 @@ int persistent_grid(K kernel, int threads, size_t lds) {
 
 template <class K>
 void allow_lds(K kernel, size_t bytes) {
-    static bool done = false;   // per instantiation
-    if (!done && bytes > 64 * 1024) {
+    static bool done[64] = {};   // per instantiation and device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+    if (bytes > 64 * 1024 && (dev < 0 || !done[dev])) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
-        done = true;
+        if (dev >= 0) done[dev] = true;
     }
 }
 
