@@ -71,6 +71,8 @@ WORKLOADS = [
     # the pages' low-precision run (FP8 activations, FP4 weights): 384 experts, top-6, 4096 tokens
     # per GPU, the 48 experts of one GPU of eight
     Workload("wide_share_mx_fwd", T=4096, H=7168, I=3072, E=384, EL=48, k=6),
+    # the page-scale share's training step (the pages time its backward legs at this scale)
+    Workload("dsv3_page_share_fwd_bwd", T=65536, H=7168, I=2048, E=256, EL=32, k=8, backward=True),
 ]
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))

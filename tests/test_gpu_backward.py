@@ -44,6 +44,8 @@ def _free_memory():
 REDUCED = [
     mw.Workload("wide_reduced", T=64, H=256, I=128, E=48, EL=6, k=6, backward=True),
     mw.Workload("bwd_ragged_shard", T=301, H=384, I=256, E=10, EL=5, k=3, e_lo=2, backward=True),
+    # about 256 rows per expert: the weight gradients run on the forward pipeline (block_m >= 64)
+    mw.Workload("bwd_many_rows", T=1024, H=512, I=256, E=8, EL=4, k=2, e_lo=2, backward=True),
 ]
 
 
@@ -135,7 +137,7 @@ def pairs_of_expert(tab):
     return rows_of
 
 
-@pytest.mark.parametrize("bm", [32, 64, 128])
+@pytest.mark.parametrize("bm", [32, 64, 128, 256])
 @pytest.mark.parametrize("w", REDUCED, ids=[r.name for r in REDUCED])
 def test_backward_reduced_full_compare(w, bm):
     d = with_empty_expert(w, mw.inputs(w, 9))

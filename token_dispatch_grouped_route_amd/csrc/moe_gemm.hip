@@ -554,34 +554,11 @@ struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
     __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
-// A wave's 32x32 accumulator block as whole 1 KB blocks of a fragment-packed weight gradient
-// (moe_pack_weights layout, reduction length K): the tile's M index is the packed reduction index
-// k (a 32-row block spans two 16-deep K steps) and its N index the packed column n (a 32-column
-// block is one packed column group).  Lane L holds column n0 + L%32 and k = k0 + 8*(r/4) +
-// 4*(L/32) + r%4 for r = 0..15, while a packed block wants lane L to hold the 8 consecutive k from
-// 8*(L/32) of each 16-deep step; so lanes L and L^32 trade four values per step (one
-// v_permlane32_swap each, a VALU exchange of the two half-waves: lane L < 32 keeps a and gets the a
-// of lane L + 32, lane L >= 32 gets the b of lane L - 32 and keeps b), and every lane then stores
-// 16 bytes: one store instruction writes a whole 1 KB block.
+// The accumulator of a 32x32 MFMA block stored as one packed 1 KB block: store_packed_block in
+// moe_internal.h.
 __device__ __forceinline__ void store_grad_block(uint16_t* out, int64_t K, int64_t n0, int64_t k0,
                                                  const f32x16_t& acc, int lane) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[8 * st + q]),
-                                                            __float_as_uint(acc[8 * st + 4 + q]), false, false);
-            v[q] = __uint_as_float(r[0]);
-            v[4 + q] = __uint_as_float(r[1]);
-        }
-        u32x4 pk;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            pk[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
-        const int64_t blk = (n0 >> 5) * (K >> 4) + ((k0 >> 4) + st);
-        *reinterpret_cast<u32x4*>(out + (blk * 64 + lane) * 8) = pk;
-    }
+    store_packed_block(out, K, n0, k0, acc, lane);
 }
 
 constexpr int kWgradChunk = 8;   // output tiles per weight-gradient workgroup
@@ -856,8 +833,99 @@ hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint1
     return launch_combine_finish(d, ws, dx, s);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Operands of the weight gradients on the forward pipeline (experts with many rows)
+// ---------------------------------------------------------------------------------------------
+// A tile of 64 ws rows x 64 columns goes through LDS: read row by row (16 bytes per thread; zero
+// for a row no pair holds), written column by column, either into At [W, R_max] (row c holds
+// column c of every ws row; PACKED false) or into MFMA fragments along the rows (PACKED true:
+// block (n / 32, r / 16) at (n / 32 * (R_max / 16) + r / 16) * 1 KB, lane n % 32 + 32 * ((r / 8) % 2)
+// holding the 8 rows of r's octet, n the packed column of c).  Sources: ws act rows, the token
+// rows of x or dy through row_pair (dy scaled by the routing weight and rounded to bf16, as the
+// streaming kernels do), or ws dhgu rows (packed by L1 column).
+enum RowsSrc { kActRows, kTokenRows, kWeightedTokenRows, kDhguRows };
+
+template <int SRC, bool PACKED>
+__global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __restrict__ tok,
+                                                              const float* __restrict__ topk_w, Dims d, Ws ws, int W,
+                                                              uint16_t* __restrict__ dst) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+    const int tid = threadIdx.x;
+    const int64_t Rcap = ws.rows_cap;
+    const int64_t R = min(static_cast<int64_t>(ws.meta[0]), Rcap);
+    const int npairs = d.T * d.k;
+    const int col_tiles = W / 64;
+    const int64_t total = (R + 63) / 64 * col_tiles;
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+        const int64_t r0 = t / col_tiles * 64;
+        const int c0 = static_cast<int>(t % col_tiles) * 64;
+        __syncthreads();   // the previous tile's LDS reads are done
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = tid + 256 * h, row = q >> 3, ch = q & 7;
+            const int64_t r = r0 + row;
+            u32x4 v = {0, 0, 0, 0};
+            const int p = r < R ? ws.row_pair[r] : -1;
+            if (p >= 0 && p < npairs) {
+                const uint16_t* src;
+                if constexpr (SRC == kActRows) src = ws.act + r * W;
+                else if constexpr (SRC == kDhguRows) src = ws.dhgu + r * W;
+                else src = tok + static_cast<int64_t>(p / d.k) * W;
+                v = *reinterpret_cast<const u32x4*>(src + c0 + 8 * ch);
+                if constexpr (SRC == kWeightedTokenRows) v = scale_bf16x8(v, topk_w[p]);
+            }
+            *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = tid + 256 * h;
+            const int m = PACKED ? (q & 63) : (q >> 3), o = PACKED ? (q >> 6) : (q & 7);
+            u32x4 w4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w4[j] = static_cast<uint32_t>(tile[8 * o + 2 * j][m]) | (static_cast<uint32_t>(tile[8 * o + 2 * j + 1][m]) << 16);
+            const int64_t r = r0 + 8 * o;
+            uint16_t* dp;
+            if constexpr (!PACKED) {
+                dp = dst + static_cast<int64_t>(c0 + m) * Rcap + r;
+            } else {
+                const int64_t n = SRC == kDhguRows ? l1_packed_col(c0 + m, d.I) : static_cast<int64_t>(c0 + m);
+                const int64_t blk = (n >> 5) * (Rcap / 16) + (r >> 4);
+                dp = dst + (blk * 64 + (n & 31) + 32 * ((r >> 3) & 1)) * 8;
+            }
+            *reinterpret_cast<u32x4*>(dp) = w4;
+        }
+    }
+}
+
+template <int SRC, bool PACKED>
+static hipError_t rows_to_k_major(const Dims& d, const Ws& ws, const uint16_t* tok, const float* topk_w, int W,
+                                  uint16_t* dst, hipStream_t s) {
+    rows_to_k_major_kernel<SRC, PACKED><<<device_cu_count() * 8, 256, 0, s>>>(tok, topk_w, d, ws, W, dst);
+    return hipGetLastError();
+}
+
+// The forward-pipeline weight gradients pay off once an expert has several 64-row K slots
+// (expected rows per expert T*k/E at least kWgradNtRows); they need segments in whole 64-row slots
+// (block_m a multiple of 64) and both transformed operands inside ws stage (4 * H * R_max bytes).
+constexpr int64_t kWgradNtRows = 256;
+
+static bool wgrad_nt_use(const Dims& d, int M, int N) {
+    return d.BM % 64 == 0 && static_cast<int64_t>(d.T) * d.k >= kWgradNtRows * d.E && wgrad_nt_fits(M, N) &&
+           static_cast<int64_t>(M) + N <= 2 * static_cast<int64_t>(d.H);
+}
+
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
                          uint16_t* dw2p, hipStream_t s) {
+    if (wgrad_nt_use(d, d.I, d.H)) {   // dW2 packed like W2: reduction index i (M = I), column h (N = H)
+        uint16_t* at = reinterpret_cast<uint16_t*>(ws.stage);
+        uint16_t* bp = at + static_cast<int64_t>(d.I) * ws.rows_cap;
+        hipError_t e = rows_to_k_major<kActRows, false>(d, ws, nullptr, nullptr, d.I, at, s);
+        if (e == hipSuccess) e = rows_to_k_major<kWeightedTokenRows, true>(d, ws, dy, topk_w, d.H, bp, s);
+        if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.I, d.H, ws, dw2p, s);
+        return e;
+    }
     const int blocks = d.EL * (d.H / WG::BN) * ((d.I / WG::BM + kWgradChunk - 1) / kWgradChunk);
     if (blocks <= 0) return hipSuccess;
     wgrad2_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES, s>>>(dy, topk_w, d, ws, dw2p);
@@ -873,6 +941,14 @@ static hipError_t wgrad1_launch(const Dims& d, const uint16_t* x, const Ws& ws, 
 }
 
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
+    if (wgrad_nt_use(d, d.H, 2 * d.I)) {   // dW1 packed like W1: reduction index h (M = H), packed column (N = 2I)
+        uint16_t* at = reinterpret_cast<uint16_t*>(ws.stage);
+        uint16_t* bp = at + static_cast<int64_t>(d.H) * ws.rows_cap;
+        hipError_t e = rows_to_k_major<kTokenRows, false>(d, ws, x, nullptr, d.H, at, s);
+        if (e == hipSuccess) e = rows_to_k_major<kDhguRows, true>(d, ws, nullptr, nullptr, 2 * d.I, bp, s);
+        if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.H, 2 * d.I, ws, dw1p, s);
+        return e;
+    }
     if (d.H % WG1::BM == 0) return wgrad1_launch<WG1>(d, x, ws, dw1p, s);
     return wgrad1_launch<WG>(d, x, ws, dw1p, s);
 }

@@ -701,11 +701,88 @@ hipError_t l2_launch(const Dims& d, const uint16_t* act, const uint16_t* w2f, co
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Weight gradients of experts with many rows, on the forward's pipeline
+// ---------------------------------------------------------------------------------------------
+// dW[e] (packed: reduction index m, packed column n) = sum over the expert's rows r of
+// At[m][r] * B[r][n].  At is the row operand transposed to K-contiguous rows ([M, R_max]: row m
+// holds column m of every ws row), B the column operand packed into MFMA fragments along the rows
+// (a 1 KB block per (32-column group, 16 rows) at (group * (R_max / 16) + r / 16) * 1 KB); the
+// transforms of moe_gemm.hip build both, with zeros in rows no pair holds.  A 256 x 256 tile (an
+// M tile and an N tile of one expert) runs the forward's K loop over the expert's rows rounded
+// up to 64 (inside its segment: block_m is a multiple of 64, and the padding rows are zero) and
+// stores whole packed blocks; an expert without rows gets exact zeros.
+template <class C>
+__global__ __launch_bounds__(C::NT, C::OCC) void wgrad_nt_kernel(const uint16_t* __restrict__ at,
+                                                                 const uint16_t* __restrict__ bp, int M, int N,
+                                                                 Dims d, Ws ws, uint16_t* __restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    constexpr int MA = C::MAXMI;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m_tiles = M / C::BM, n_tiles = N / C::BN;
+    const int total = d.EL * m_tiles * n_tiles;
+    const int64_t R = ws.rows_cap;   // row stride of At, K extent of B
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        const int e = tile / (m_tiles * n_tiles);
+        const int rem = tile - e * (m_tiles * n_tiles);
+        const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
+        const int64_t seg0 = ws.offsets[e], seg1 = ws.offsets[e + 1];
+        int64_t len = (static_cast<int64_t>(ws.counts[e]) + 63) / 64 * 64;
+        if (seg0 < 0 || seg1 > R || seg1 < seg0 || (seg0 & 63)) len = 0;   // tables not from one prologue
+        else if (len > seg1 - seg0) len = (seg1 - seg0) / 64 * 64;
+        uint16_t* o = out + static_cast<int64_t>(e) * M * N;
+        if (len < 64) {   // no rows: exact zeros, tile (mt, nt) of the packed gradient
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            for (int mi = 0; mi < MA; ++mi)
+                for (int ni = 0; ni < C::NI; ++ni)
+                    for (int st = 0; st < 2; ++st) {
+                        const int64_t n0 = static_cast<int64_t>(nt) * C::BN + wave * 32 * C::NI + ni * 32;
+                        const int64_t blk = (n0 >> 5) * (M >> 4) + ((static_cast<int64_t>(mt) * C::BM + mi * 32) >> 4) + st;
+                        *reinterpret_cast<uint4*>(o + (blk * 64 + lane) * 8) = z;
+                    }
+            continue;
+        }
+        f32x16_t acc[MA][C::NI];
+        Pipe<C, MA> p;
+        p.nslot = static_cast<int>(len / 64);
+        p.wave = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int i = 0; i < MA; ++i) {
+            const int row = 32 * i + 8 * wave + (lane >> 3);   // M row of the tile
+            const int c16 = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+            p.a_src[i] = reinterpret_cast<const char*>(at + (static_cast<int64_t>(mt) * C::BM + row) * R + seg0) + c16;
+        }
+        const int64_t g0 = static_cast<int64_t>(nt) * (C::BN / 32) + wave * C::NI;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+            p.b_src[ni] = reinterpret_cast<const char*>(bp) + ((g0 + ni) * (R / 16) + seg0 / 16) * 1024 + lane * 16;
+        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, smem + (C::SLOTS - 1) * C::SLOT, acc, lane);
+#pragma unroll
+        for (int mi = 0; mi < MA; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                store_packed_block(o, M, static_cast<int64_t>(nt) * C::BN + wave * 32 * C::NI + ni * 32,
+                                   static_cast<int64_t>(mt) * C::BM + mi * 32, acc[mi][ni], lane);
+    }
+}
+
 using L1Tile = Tile<2, 8, 1, 4>;
 using L2Tile = Tile<2, 8, 1, 4>;
 using L2TileNarrow = Tile<1, 8, 1, 4>;
+using WgTile = Tile<2, 8, 1, 3>;   // three ring slots: the packed-block epilogue needs the registers of a fourth
 
 }  // namespace
+
+bool wgrad_nt_fits(int M, int N) { return M % WgTile::BM == 0 && N % WgTile::BN == 0; }
+
+hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp, int M, int N, const Ws& ws,
+                           uint16_t* out, hipStream_t s) {
+    if (!wgrad_nt_fits(M, N) || d.EL > kMaxEL) return hipErrorInvalidValue;
+    auto k = wgrad_nt_kernel<WgTile>;
+    allow_lds(k, WgTile::LDS_BYTES);
+    k<<<persistent_grid(k, WgTile::NT, WgTile::LDS_BYTES), WgTile::NT, WgTile::LDS_BYTES, s>>>(at, bp, M, N, d, ws, out);
+    return hipGetLastError();
+}
 
 // L1 N tiles are 256 columns (2I is a multiple of 256); L2 N tiles 256 columns when H allows, else 128.
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1f, const Ws& ws, uint16_t* act_out,

@@ -92,6 +92,37 @@ __host__ __device__ __forceinline__ int64_t l1_packed_col(int64_t n, int64_t I) 
 }
 
 // Host launchers (each returns a hipError_t from the launch).
+// A wave's 32x32 accumulator block as whole 1 KB blocks of a fragment-packed weight gradient
+// (moe_pack_weights layout, reduction length K): the tile's M index is the packed reduction index
+// k (a 32-row block spans two 16-deep K steps) and its N index the packed column n (a 32-column
+// block is one packed column group).  Lane L holds column n0 + L%32 and k = k0 + 8*(r/4) +
+// 4*(L/32) + r%4 for r = 0..15, while a packed block wants lane L to hold the 8 consecutive k from
+// 8*(L/32) of each 16-deep step; so lanes L and L^32 trade four values per step (one
+// v_permlane32_swap each, a VALU exchange of the two half-waves: lane L < 32 keeps a and gets the a
+// of lane L + 32, lane L >= 32 gets the b of lane L - 32 and keeps b), and every lane then stores
+// 16 bytes: one store instruction writes a whole 1 KB block.
+__device__ __forceinline__ void store_packed_block(uint16_t* out, int64_t K, int64_t n0, int64_t k0,
+                                                 const f32x16_t& acc, int lane) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[8 * st + q]),
+                                                            __float_as_uint(acc[8 * st + 4 + q]), false, false);
+            v[q] = __uint_as_float(r[0]);
+            v[4 + q] = __uint_as_float(r[1]);
+        }
+        uint32_t pk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            pk[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
+        const int64_t blk = (n0 >> 5) * (K >> 4) + ((k0 >> 4) + st);
+        *reinterpret_cast<uint4*>(out + (blk * 64 + lane) * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
+}
+
+
 hipError_t launch_route(const Dims& d, const int32_t* topk_idx, const Ws& ws, hipStream_t s);
 hipError_t launch_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, uint16_t* w1p,
                        uint16_t* w2p, hipStream_t s);
@@ -112,6 +143,9 @@ hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint1
 hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s);
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
                          uint16_t* dw2p, hipStream_t s);
+bool wgrad_nt_fits(int M, int N);
+hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp, int M, int N, const Ws& ws,
+                           uint16_t* out, hipStream_t s);
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p,
                          hipStream_t s);
 
