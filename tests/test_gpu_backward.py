@@ -46,6 +46,8 @@ REDUCED = [
     mw.Workload("bwd_ragged_shard", T=301, H=384, I=256, E=10, EL=5, k=3, e_lo=2, backward=True),
     # about 256 rows per expert: the weight gradients run on the forward pipeline (block_m >= 64)
     mw.Workload("bwd_many_rows", T=1024, H=512, I=256, E=8, EL=4, k=2, e_lo=2, backward=True),
+    # about 512 rows per expert and 2 * EL * H <= R_max: the L1 dgrad also runs as the forward's L2
+    mw.Workload("bwd_many_rows_narrow", T=2048, H=256, I=128, E=8, EL=4, k=2, e_lo=2, backward=True),
 ]
 
 

@@ -820,7 +820,64 @@ static hipError_t dgrad1_launch(const Dims& d, const uint16_t* w1p, const Ws& ws
     return hipGetLastError();
 }
 
+// Expected rows per local expert (T * k / E, uniform routing) from which the backward GEMMs of an
+// expert run on the forward's pipeline instead of the streaming kernels above.
+constexpr int64_t kWgradNtRows = 256;
+
+// W1p (packed: column = packed L1 column, reduction index h) -> W1 as the B operand of an NT GEMM
+// with N = h and K = the logical L1 column c ([gate | up] order, as in dhgu): element (h, c) moves
+// from frag_index(l1_packed_col(c), h, H) to frag_index(h, c, 2I) of the same expert.  A 64 x 64
+// tile goes through LDS; both sides read and write whole 16-byte chunks.
+__global__ __launch_bounds__(256) void repack_w1_t_kernel(const uint16_t* __restrict__ w1p, Dims d,
+                                                          uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // [c][h]
+    const int H = d.H, N2 = 2 * d.I, tid = threadIdx.x;
+    const int h_tiles = H / 64, c_tiles = N2 / 64;
+    const int64_t per_e = static_cast<int64_t>(h_tiles) * c_tiles;
+    const int64_t total = per_e * d.EL;
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+        const int64_t e = t / per_e, rem = t - e * per_e;
+        const int hb = static_cast<int>(rem / c_tiles) * 64, cb = static_cast<int>(rem % c_tiles) * 64;
+        const uint16_t* in = w1p + e * H * N2;
+        uint16_t* o = out + e * H * N2;
+        __syncthreads();   // the previous tile's LDS reads are done
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + 256 * i, c = q & 63, oc = q >> 6;   // 8 consecutive h of column cb + c
+            const int64_t pc = l1_packed_col(cb + c, d.I);
+            *reinterpret_cast<u32x4*>(&tile[c][8 * oc]) = *reinterpret_cast<const u32x4*>(in + frag_index(pc, hb + 8 * oc, H));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + 256 * i, h = q & 63, oc = q >> 6;   // 8 consecutive c of row hb + h
+            u32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = static_cast<uint32_t>(tile[8 * oc + 2 * j][h]) | (static_cast<uint32_t>(tile[8 * oc + 2 * j + 1][h]) << 16);
+            *reinterpret_cast<u32x4*>(o + frag_index(hb + h, cb + 8 * oc, N2)) = v;
+        }
+    }
+}
+
+// The L1 dgrad of experts with many rows runs as the forward's L2 (NT, with its combine into
+// token order, weight 1): K = 2I over the dhgu rows, B = W1 repacked by repack_w1_t_kernel into
+// ws dact (dead once dhgu exists; it holds EL * H * 2I elements when 2 * EL * H <= R_max).
+static bool dgrad1_nt_use(const Dims& d, const Ws& ws) {
+    return ws.dact && ws.dhgu && static_cast<int64_t>(d.T) * d.k >= kWgradNtRows * d.E && d.H % 256 == 0 &&
+           (2 * d.I) % 64 == 0 && 2 * static_cast<int64_t>(d.EL) * d.H <= ws.rows_cap;
+}
+
 hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s) {
+    if (dgrad1_nt_use(d, ws)) {
+        repack_w1_t_kernel<<<device_cu_count() * 8, 256, 0, s>>>(w1p, d, ws.dact);
+        hipError_t e = hipGetLastError();
+        Dims d2 = d;
+        d2.I = 2 * d.I;   // the GEMM's K: dhgu rows are 2I wide
+        if (e == hipSuccess) e = launch_gemm2_combine(d2, ws.dhgu, ws.dact, nullptr, ws, dx, s);
+        if (e == hipSuccess) e = launch_combine_finish(d, ws, dx, s);
+        return e;
+    }
     hipError_t e;
     switch (d.BM) {
         case 32: e = dgrad1_launch<G32>(d, w1p, ws, dx, s); break;
@@ -909,7 +966,6 @@ static hipError_t rows_to_k_major(const Dims& d, const Ws& ws, const uint16_t* t
 // The forward-pipeline weight gradients pay off once an expert has several 64-row K slots
 // (expected rows per expert T*k/E at least kWgradNtRows); they need segments in whole 64-row slots
 // (block_m a multiple of 64) and both transformed operands inside ws stage (4 * H * R_max bytes).
-constexpr int64_t kWgradNtRows = 256;
 
 static bool wgrad_nt_use(const Dims& d, int M, int N) {
     return d.BM % 64 == 0 && static_cast<int64_t>(d.T) * d.k >= kWgradNtRows * d.E && wgrad_nt_fits(M, N) &&

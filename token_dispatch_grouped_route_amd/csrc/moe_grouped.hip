@@ -575,7 +575,7 @@ struct L2Body {
             float w = 0.0f;
             if (pr >= 0 && pr < npairs) {
                 tok = pr / d.k;
-                w = topk_w[pr];
+                w = topk_w ? topk_w[pr] : 1.0f;   // no weights: the L1 dgrad's combine into dx
                 direct = ws.tok_nloc[tok] == 1;
             }
             s_row[tid] = make_int4(tok, __float_as_int(w), direct, 0);
