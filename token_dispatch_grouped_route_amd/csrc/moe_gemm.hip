@@ -796,9 +796,67 @@ static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* t
     return hipGetLastError();
 }
 
+// Expected rows per local expert (T * k / E, uniform routing) from which the backward GEMMs of an
+// expert run on the forward's pipeline instead of the streaming kernels above.
+constexpr int64_t kWgradNtRows = 256;
+
+// A packed weight read as the B operand of the other GEMM direction: element (a, b) of each expert
+// (a < A, the output column; b < B, the reduction index) moves from the source's packed position
+// (column src_col(b), reduction index a, reduction length A) to frag_index(a, b, B).  W1 -> (N = h,
+// K = L1 column in [gate | up] order; A = H, B = 2I, src_col = l1_packed_col) for the L1 dgrad;
+// W2 -> (N = i, K = h; A = I, B = H) for the L2 dgrad.  A 64 x 64 tile goes through LDS; both
+// sides move whole 16-byte chunks.
+template <bool L1COL>
+__global__ __launch_bounds__(256) void repack_t_kernel(const uint16_t* __restrict__ src, int A, int B, int I, int EL,
+                                                       uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // [b][a]
+    const int tid = threadIdx.x;
+    const int a_tiles = A / 64, b_tiles = B / 64;
+    const int64_t per_e = static_cast<int64_t>(a_tiles) * b_tiles;
+    const int64_t total = per_e * EL;
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+        const int64_t e = t / per_e, rem = t - e * per_e;
+        const int ab = static_cast<int>(rem / b_tiles) * 64, bb = static_cast<int>(rem % b_tiles) * 64;
+        const uint16_t* in = src + e * A * B;
+        uint16_t* o = out + e * A * B;
+        __syncthreads();   // the previous tile's LDS reads are done
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + 256 * i, b = q & 63, oa = q >> 6;   // 8 consecutive a of source column b
+            const int64_t col = L1COL ? l1_packed_col(bb + b, I) : static_cast<int64_t>(bb + b);
+            *reinterpret_cast<u32x4*>(&tile[b][8 * oa]) = *reinterpret_cast<const u32x4*>(in + frag_index(col, ab + 8 * oa, A));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + 256 * i, a = q & 63, ob = q >> 6;   // 8 consecutive b of output column a
+            u32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = static_cast<uint32_t>(tile[8 * ob + 2 * j][a]) | (static_cast<uint32_t>(tile[8 * ob + 2 * j + 1][a]) << 16);
+            *reinterpret_cast<u32x4*>(o + frag_index(ab + a, bb + 8 * ob, B)) = v;
+        }
+    }
+}
+
+// The L2 dgrad of experts with many rows runs on the forward's L1 tile loop (dgrad_nt_kernel) with W2
+// repacked to an (N = i, K = h) operand in ws stage (free during the backward's first GEMM; it
+// holds EL * I * H elements when EL * I <= 2 * R_max).
+static bool dgrad_nt_use(const Dims& d, const Ws& ws, int fuse, bool topk_w_grad) {
+    return static_cast<int64_t>(d.T) * d.k >= kWgradNtRows * d.E && dgrad_nt_fits(d) && ws.stage &&
+           static_cast<int64_t>(d.EL) * d.I <= 2 * ws.rows_cap && (!fuse || (ws.hgu && ws.dhgu)) &&
+           (fuse || ws.dact) && (!topk_w_grad || ws.act);
+}
+
 hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
                         const Ws& ws, int fuse, bool topk_w_grad, hipStream_t s) {
     if (topk_w_grad && (!ws.dtw_part || ws.dtw_cols != d.I / 128)) return hipErrorInvalidValue;
+    if (dgrad_nt_use(d, ws, fuse, topk_w_grad)) {
+        uint16_t* w2t = reinterpret_cast<uint16_t*>(ws.stage);
+        repack_t_kernel<false><<<device_cu_count() * 8, 256, 0, s>>>(w2p, d.I, d.H, d.I, d.EL, w2t);
+        const hipError_t e = hipGetLastError();
+        return e == hipSuccess ? launch_dgrad_nt(d, dy, w2t, topk_w, ws, fuse, topk_w_grad, s) : e;
+    }
     switch (d.BM) {
         case 32: return dgrad_launch<G32>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
         case 64: return dgrad_launch<G64>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
@@ -820,46 +878,6 @@ static hipError_t dgrad1_launch(const Dims& d, const uint16_t* w1p, const Ws& ws
     return hipGetLastError();
 }
 
-// Expected rows per local expert (T * k / E, uniform routing) from which the backward GEMMs of an
-// expert run on the forward's pipeline instead of the streaming kernels above.
-constexpr int64_t kWgradNtRows = 256;
-
-// W1p (packed: column = packed L1 column, reduction index h) -> W1 as the B operand of an NT GEMM
-// with N = h and K = the logical L1 column c ([gate | up] order, as in dhgu): element (h, c) moves
-// from frag_index(l1_packed_col(c), h, H) to frag_index(h, c, 2I) of the same expert.  A 64 x 64
-// tile goes through LDS; both sides read and write whole 16-byte chunks.
-__global__ __launch_bounds__(256) void repack_w1_t_kernel(const uint16_t* __restrict__ w1p, Dims d,
-                                                          uint16_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // [c][h]
-    const int H = d.H, N2 = 2 * d.I, tid = threadIdx.x;
-    const int h_tiles = H / 64, c_tiles = N2 / 64;
-    const int64_t per_e = static_cast<int64_t>(h_tiles) * c_tiles;
-    const int64_t total = per_e * d.EL;
-    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-        const int64_t e = t / per_e, rem = t - e * per_e;
-        const int hb = static_cast<int>(rem / c_tiles) * 64, cb = static_cast<int>(rem % c_tiles) * 64;
-        const uint16_t* in = w1p + e * H * N2;
-        uint16_t* o = out + e * H * N2;
-        __syncthreads();   // the previous tile's LDS reads are done
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = tid + 256 * i, c = q & 63, oc = q >> 6;   // 8 consecutive h of column cb + c
-            const int64_t pc = l1_packed_col(cb + c, d.I);
-            *reinterpret_cast<u32x4*>(&tile[c][8 * oc]) = *reinterpret_cast<const u32x4*>(in + frag_index(pc, hb + 8 * oc, H));
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = tid + 256 * i, h = q & 63, oc = q >> 6;   // 8 consecutive c of row hb + h
-            u32x4 v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[j] = static_cast<uint32_t>(tile[8 * oc + 2 * j][h]) | (static_cast<uint32_t>(tile[8 * oc + 2 * j + 1][h]) << 16);
-            *reinterpret_cast<u32x4*>(o + frag_index(hb + h, cb + 8 * oc, N2)) = v;
-        }
-    }
-}
-
 // The L1 dgrad of experts with many rows runs as the forward's L2 (NT, with its combine into
 // token order, weight 1): K = 2I over the dhgu rows, B = W1 repacked by repack_w1_t_kernel into
 // ws dact (dead once dhgu exists; it holds EL * H * 2I elements when 2 * EL * H <= R_max).
@@ -870,7 +888,7 @@ static bool dgrad1_nt_use(const Dims& d, const Ws& ws) {
 
 hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s) {
     if (dgrad1_nt_use(d, ws)) {
-        repack_w1_t_kernel<<<device_cu_count() * 8, 256, 0, s>>>(w1p, d, ws.dact);
+        repack_t_kernel<true><<<device_cu_count() * 8, 256, 0, s>>>(w1p, d.H, 2 * d.I, d.I, d.EL, ws.dact);
         hipError_t e = hipGetLastError();
         Dims d2 = d;
         d2.I = 2 * d.I;   // the GEMM's K: dhgu rows are 2I wide

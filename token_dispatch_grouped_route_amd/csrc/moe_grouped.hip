@@ -766,6 +766,134 @@ __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_nt_kernel(const uint16_t*
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// L2 dgrad of experts with many rows, on the forward's pipeline
+// ---------------------------------------------------------------------------------------------
+// dA'[r] = dy[t] @ W2[e]^T (t the row's token) on the L1 tile loop: the dy rows gathered through
+// row_pair into the A ring, W2 repacked to an (N = i, K = h) operand streaming into B registers.
+// The epilogue is the streaming dgrad's: the row weight (dA = w * dA'), the SwiGLU transpose from
+// the saved pre-activation (fuse) or plain dA rows, and the routing-weight partials: for each
+// 128-column half of the 256-column tile (waves 2h and 2h + 1) the sum over its columns of
+// dA' * act, in the [R_max, I / 128] layout of ws dtw_part.
+template <class C>
+struct DgradBody {
+    const uint16_t* dy;
+    const uint16_t* w2t;
+    const float* topk_w;
+    Dims d;
+    Ws ws;
+    int fuse, tw;
+    char* smem;
+
+    template <int MA>
+    __device__ __forceinline__ void run(const TileRef& t) {
+        static_assert(C::BN == 256 && C::NI == 2, "two 128-column halves of two waves each");
+        float* s_w = reinterpret_cast<float*>(smem + C::RING_BYTES);   // row weight (0: no pair)
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int H = d.H, I = d.I, npairs = d.T * d.k;
+        const int pr_own = tid < t.real_rows ? ws.row_pair[t.row0 + tid] : -1;
+        Pipe<C, MA> p;
+        p.nslot = H / 64;
+        p.wave = __builtin_amdgcn_readfirstlane(wave);
+        const char* zrow = reinterpret_cast<const char*>(ws.zeros);
+#pragma unroll
+        for (int i = 0; i < MA; ++i) {
+            const int row = 32 * i + 8 * wave + (lane >> 3);
+            const int pr = row < t.real_rows ? ws.row_pair[t.row0 + row] : -1;
+            const int c16 = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+            p.a_src[i] = (pr >= 0 && pr < npairs)
+                             ? reinterpret_cast<const char*>(dy + static_cast<int64_t>(pr / d.k) * H) + c16
+                             : zrow + c16;
+        }
+        const char* wb = reinterpret_cast<const char*>(w2t) + static_cast<int64_t>(t.e) * I * H * 2;
+        const int nb0 = t.nt * (C::BN / 32) + wave * C::NI;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+            p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (H / 16) * 1024 + lane * 16;
+        f32x16_t acc[MA][C::NI];
+        k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, smem + (C::SLOTS - 1) * C::SLOT, acc, lane);
+
+        if (tid < 32 * MA) s_w[tid] = (pr_own >= 0 && pr_own < npairs) ? topk_w[pr_own] : 0.0f;
+        // Epilogue through LDS, GP 32-row groups per pass: the waves drop dA' into a row-major fp32
+        // tile, then each wave takes whole rows (64 lanes x 4 columns = the tile's 256 columns), so
+        // the act / hgu reads and the dhgu (or dact) writes are contiguous row segments, and a row's
+        // two 128-column routing-weight partials are the sums over lanes 0-31 and 32-63.
+        constexpr int LD = C::BN + 4;   // floats per LDS row: rows r and r + 4 fall on different banks
+        constexpr int GP = 2;
+        static_assert(GP * 32 * LD * 4 <= C::RING_BYTES, "a pass fits in the ring");
+        float* tile = reinterpret_cast<float*>(smem);
+        const int cols_tw = I / 128;
+#pragma unroll
+        for (int m0 = 0; m0 < MA; m0 += GP) {
+            if (32 * m0 >= t.real_rows) break;   // groups that belong to no row
+            lds_barrier();   // the previous pass's reads are done; publishes s_w on the first pass
+#pragma unroll
+            for (int mm = 0; mm < GP; ++mm)
+                if (m0 + mm < MA)
+#pragma unroll
+                    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            tile[(mm * 32 + acc_row(r, lane)) * LD + wave * 32 * C::NI + ni * 32 + (lane & 31)] =
+                                acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
+            lds_barrier();
+            const int rows = min(GP * 32, t.real_rows - 32 * m0);
+            for (int rr = wave; rr < rows; rr += C::NT / 64) {
+                const int rl = 32 * m0 + rr;
+                const int64_t row = t.row0 + rl;
+                const float w = s_w[rl];
+                const int c = t.nt * C::BN + lane * 4;
+                const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + lane * 4);
+                const float va[4] = {v.x, v.y, v.z, v.w};
+                float part = 0.0f;
+                if (tw) {
+                    const uint2 a = *reinterpret_cast<const uint2*>(ws.act + row * I + c);
+                    const uint32_t aw[2] = {a.x, a.y};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) part += va[q] * bf16_to_f32(static_cast<uint16_t>(aw[q >> 1] >> (16 * (q & 1))));
+                }
+                if (fuse) {
+                    const uint2 gp = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + c);
+                    const uint2 up = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + I + c);
+                    const uint32_t gw[2] = {gp.x, gp.y}, uw[2] = {up.x, up.y};
+                    uint32_t dg[2] = {0, 0}, du[2] = {0, 0};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float g = bf16_to_f32(static_cast<uint16_t>(gw[q >> 1] >> (16 * (q & 1))));
+                        const float u = bf16_to_f32(static_cast<uint16_t>(uw[q >> 1] >> (16 * (q & 1))));
+                        const float da = w * va[q];
+                        const float sg = 1.0f / (1.0f + __expf(-g));
+                        dg[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)))) << (16 * (q & 1));
+                        du[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * g * sg)) << (16 * (q & 1));
+                    }
+                    *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + c) = make_uint2(dg[0], dg[1]);
+                    *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + I + c) = make_uint2(du[0], du[1]);
+                } else {
+                    uint32_t o[2] = {0, 0};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) o[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(w * va[q])) << (16 * (q & 1));
+                    *reinterpret_cast<uint2*>(ws.dact + row * I + c) = make_uint2(o[0], o[1]);
+                }
+                if (tw) {   // uniform over the wave: its lanes hold one row
+#pragma unroll
+                    for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+                    if ((lane & 31) == 0) ws.dtw_part[row * cols_tw + 2 * t.nt + (lane >> 5)] = part;
+                }
+            }
+        }
+    }
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::OCC) void dgrad_nt_kernel(const uint16_t* __restrict__ dy,
+                                                                 const uint16_t* __restrict__ w2t,
+                                                                 const float* __restrict__ topk_w, Dims d, Ws ws,
+                                                                 int fuse, int tw) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    DgradBody<C> body{dy, w2t, topk_w, d, ws, fuse, tw, smem};
+    run_tiles<C>(d, ws, d.I / C::BN, body);
+}
+
 using L1Tile = Tile<2, 8, 1, 4>;
 using L2Tile = Tile<2, 8, 1, 4>;
 using L2TileNarrow = Tile<1, 8, 1, 4>;
@@ -774,6 +902,18 @@ using WgTile = Tile<2, 8, 1, 3>;   // three ring slots: the packed-block epilogu
 }  // namespace
 
 bool wgrad_nt_fits(int M, int N) { return M % WgTile::BM == 0 && N % WgTile::BN == 0; }
+
+bool dgrad_nt_fits(const Dims& d) { return d.I % L1Tile::BN == 0 && d.H % 64 == 0 && d.EL <= kMaxEL; }
+
+hipError_t launch_dgrad_nt(const Dims& d, const uint16_t* dy, const uint16_t* w2t, const float* topk_w, const Ws& ws,
+                           int fuse, bool topk_w_grad, hipStream_t s) {
+    if (!dgrad_nt_fits(d)) return hipErrorInvalidValue;
+    auto k = dgrad_nt_kernel<L1Tile>;
+    allow_lds(k, L1Tile::LDS_BYTES);
+    k<<<persistent_grid(k, L1Tile::NT, L1Tile::LDS_BYTES), L1Tile::NT, L1Tile::LDS_BYTES, s>>>(
+        dy, w2t, topk_w, d, ws, fuse, topk_w_grad ? 1 : 0);
+    return hipGetLastError();
+}
 
 hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp, int M, int N, const Ws& ws,
                            uint16_t* out, hipStream_t s) {

@@ -144,6 +144,9 @@ hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s);
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
                          uint16_t* dw2p, hipStream_t s);
 bool wgrad_nt_fits(int M, int N);
+bool dgrad_nt_fits(const Dims& d);
+hipError_t launch_dgrad_nt(const Dims& d, const uint16_t* dy, const uint16_t* w2t, const float* topk_w, const Ws& ws,
+                           int fuse, bool topk_w_grad, hipStream_t s);
 hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp, int M, int N, const Ws& ws,
                            uint16_t* out, hipStream_t s);
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p,
