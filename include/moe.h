@@ -198,6 +198,10 @@ int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* to
 /*
  * Backward entry points ("Mega MoE" page, Pipeline, backward).  They need a workspace with
  * shape->train nonzero that a moe_forward of the same inputs filled (tables, act, hgu).
+ * When the expected rows per local expert (T * k / E) are at least 256 (and the shape allows),
+ * they run on the forward GEMM's pipeline and use ws regions that are dead at that point as
+ * scratch: moe_bwd_gemm2_dgrad, moe_wgrad2 and moe_wgrad1 overwrite ws stage (after the forward's
+ * combine has consumed it), moe_bwd_gemm1_dgrad_combine overwrites ws dact (after dhgu exists).
  *
  * L2 dgrad, NN: dact[r] = topk_w[p] * (dy[t] @ W2[e]^T) with p = row_pair[r], t = p / k, read
  * from the packed w2p as the [K = H, N = I] operand.  With fuse_swiglu_bwd nonzero the
