@@ -838,46 +838,66 @@ struct DgradBody {
                                 acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
             lds_barrier();
             const int rows = min(GP * 32, t.real_rows - 32 * m0);
-            for (int rr = wave; rr < rows; rr += C::NT / 64) {
-                const int rl = 32 * m0 + rr;
-                const int64_t row = t.row0 + rl;
-                const float w = s_w[rl];
-                const int c = t.nt * C::BN + lane * 4;
-                const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + lane * 4);
-                const float va[4] = {v.x, v.y, v.z, v.w};
-                float part = 0.0f;
-                if (tw) {
-                    const uint2 a = *reinterpret_cast<const uint2*>(ws.act + row * I + c);
-                    const uint32_t aw[2] = {a.x, a.y};
+            // four rows per wave at a time: their act / hgu loads all go out before any is used
+            constexpr int RB = 4, WS = C::NT / 64;
+            for (int rb = wave; rb < rows; rb += RB * WS) {
+                uint2 av[RB], gv[RB], uv[RB];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) part += va[q] * bf16_to_f32(static_cast<uint16_t>(aw[q >> 1] >> (16 * (q & 1))));
-                }
-                if (fuse) {
-                    const uint2 gp = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + c);
-                    const uint2 up = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + I + c);
-                    const uint32_t gw[2] = {gp.x, gp.y}, uw[2] = {up.x, up.y};
-                    uint32_t dg[2] = {0, 0}, du[2] = {0, 0};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float g = bf16_to_f32(static_cast<uint16_t>(gw[q >> 1] >> (16 * (q & 1))));
-                        const float u = bf16_to_f32(static_cast<uint16_t>(uw[q >> 1] >> (16 * (q & 1))));
-                        const float da = w * va[q];
-                        const float sg = 1.0f / (1.0f + __expf(-g));
-                        dg[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)))) << (16 * (q & 1));
-                        du[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * g * sg)) << (16 * (q & 1));
+                for (int b = 0; b < RB; ++b) {
+                    const int rr = rb + b * WS;
+                    av[b] = gv[b] = uv[b] = make_uint2(0, 0);
+                    if (rr < rows) {
+                        const int64_t row = t.row0 + 32 * m0 + rr;
+                        const int c = t.nt * C::BN + lane * 4;
+                        if (tw) av[b] = *reinterpret_cast<const uint2*>(ws.act + row * I + c);
+                        if (fuse) {
+                            gv[b] = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + c);
+                            uv[b] = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + I + c);
+                        }
                     }
-                    *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + c) = make_uint2(dg[0], dg[1]);
-                    *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + I + c) = make_uint2(du[0], du[1]);
-                } else {
-                    uint32_t o[2] = {0, 0};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) o[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(w * va[q])) << (16 * (q & 1));
-                    *reinterpret_cast<uint2*>(ws.dact + row * I + c) = make_uint2(o[0], o[1]);
                 }
-                if (tw) {   // uniform over the wave: its lanes hold one row
 #pragma unroll
-                    for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-                    if ((lane & 31) == 0) ws.dtw_part[row * cols_tw + 2 * t.nt + (lane >> 5)] = part;
+                for (int b = 0; b < RB; ++b) {
+                    const int rr = rb + b * WS;
+                    if (rr >= rows) break;   // uniform over the wave
+                    const int rl = 32 * m0 + rr;
+                    const int64_t row = t.row0 + rl;
+                    const float w = s_w[rl];
+                    const int c = t.nt * C::BN + lane * 4;
+                    const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + lane * 4);
+                    const float va[4] = {v.x, v.y, v.z, v.w};
+                    float part = 0.0f;
+                    if (tw) {
+                        const uint32_t aw[2] = {av[b].x, av[b].y};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            part += va[q] * bf16_to_f32(static_cast<uint16_t>(aw[q >> 1] >> (16 * (q & 1))));
+                    }
+                    if (fuse) {
+                        const uint32_t gw[2] = {gv[b].x, gv[b].y}, uw[2] = {uv[b].x, uv[b].y};
+                        uint32_t dg[2] = {0, 0}, du[2] = {0, 0};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float g = bf16_to_f32(static_cast<uint16_t>(gw[q >> 1] >> (16 * (q & 1))));
+                            const float u = bf16_to_f32(static_cast<uint16_t>(uw[q >> 1] >> (16 * (q & 1))));
+                            const float da = w * va[q];
+                            const float sg = 1.0f / (1.0f + __expf(-g));
+                            dg[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)))) << (16 * (q & 1));
+                            du[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * g * sg)) << (16 * (q & 1));
+                        }
+                        *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + c) = make_uint2(dg[0], dg[1]);
+                        *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + I + c) = make_uint2(du[0], du[1]);
+                    } else {
+                        uint32_t o[2] = {0, 0};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) o[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(w * va[q])) << (16 * (q & 1));
+                        *reinterpret_cast<uint2*>(ws.dact + row * I + c) = make_uint2(o[0], o[1]);
+                    }
+                    if (tw) {   // uniform over the wave: its lanes hold one row
+#pragma unroll
+                        for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+                        if ((lane & 31) == 0) ws.dtw_part[row * cols_tw + 2 * t.nt + (lane >> 5)] = part;
+                    }
                 }
             }
         }
