@@ -256,9 +256,15 @@ def bench_backward(a):
             continue
         b, f = alg[name]
         t = st_ms[j] / 1e3
-        roof[name] = {"bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                      "frac": b / t / 1e9 / PEAK_HBM_GBS, "traffic": None, "alg_bytes_per_launch": b,
-                      "alg_flops_per_launch": f, "mfma_frac": f / t / 1e12 / PEAK_BF16_TFLOPS}
+        # the roof the kernel's arithmetic intensity meets first (HBM below the ridge, MFMA above)
+        if f / b < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+            r = {"bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        else:
+            r = {"bound": "mfma", "achieved": f / t / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        r.update({"frac": r["achieved"] / r["peak"], "traffic": None, "alg_bytes_per_launch": b,
+                  "alg_flops_per_launch": f, "intensity_flop_per_byte": round(f / b, 1),
+                  "hbm_frac": b / t / 1e9 / PEAK_HBM_GBS, "mfma_frac": f / t / 1e12 / PEAK_BF16_TFLOPS})
+        roof[name] = r
     flops = w.flops_fwd(P) + sum(v[1] for v in alg.values())
     value = flops / (ms / 1e3) / 1e12
     out = {
