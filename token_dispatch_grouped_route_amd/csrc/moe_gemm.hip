@@ -341,9 +341,10 @@ struct W2ColSrc {   // B operand of the dgrad: (K = h, N = i) of expert e's pack
 // row weight enters in the epilogue (dA = w * dA').  With topk_w_grad the epilogue also forms
 // sum over the tile's columns of dA'[r, c] * act[r, c]: summed over the N tiles (in tile order,
 // by the finish kernel) that is <dy[t], o_p>, the gradient of the routing weight, because
-// o_p = act_p @ W2[e].
+// o_p = act_p @ W2[e].  64-row tiles fit three waves per SIMD (at most 168 registers), which
+// keeps more weight loads in flight per CU.
 template <class C>
-__global__ __launch_bounds__(C::NT) void dgrad_kernel(const uint16_t* __restrict__ dy,
+__global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad_kernel(const uint16_t* __restrict__ dy,
                                                       const float* __restrict__ topk_w,
                                                       const uint16_t* __restrict__ w2p, Dims d, Ws ws,
                                                       int fuse, int topk_w_grad) {
@@ -448,7 +449,7 @@ struct W1ColSrc {   // B operand of the L1 dgrad: (K = L1 output column, N = h) 
 // local pairs go to their fp32 stage rows, which combine_finish sums in slot order (and it zeroes
 // tokens with no local pair), so dx is deterministic.
 template <class C>
-__global__ __launch_bounds__(C::NT) void dgrad1_kernel(const uint16_t* __restrict__ w1p, Dims d, Ws ws,
+__global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad1_kernel(const uint16_t* __restrict__ w1p, Dims d, Ws ws,
                                                        uint16_t* __restrict__ dx) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     int* s_tok = reinterpret_cast<int*>(smem + C::LDS_BYTES);   // token of each tile row, -1 padding
@@ -673,7 +674,7 @@ struct WgradWork {
 // M = I (the packed reduction index), N = H (the packed column).  The weighted dy gather is the
 // shared operand; act tiles stream.
 template <class C>
-__global__ __launch_bounds__(C::NT, 2) void wgrad2_kernel(const uint16_t* __restrict__ dy,
+__global__ __launch_bounds__(C::NT, 3) void wgrad2_kernel(const uint16_t* __restrict__ dy,
                                                           const float* __restrict__ topk_w, Dims d, Ws ws,
                                                           uint16_t* __restrict__ dw2p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -708,7 +709,7 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad2_kernel(const uint16_t* __rest
 // M = H (the packed reduction index), N = 2I (logical L1 columns; 32-column groups map to packed
 // column groups whole).  The x gather is the shared operand; dhgu tiles stream.
 template <class C>
-__global__ __launch_bounds__(C::NT, 2) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
+__global__ __launch_bounds__(C::NT, C::BM == 128 ? 3 : 2) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
                                                           uint16_t* __restrict__ dw1p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
