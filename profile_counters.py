@@ -118,9 +118,10 @@ def main():
         t = dur.get(key)
         bw = (rd + wr) / t / 1e9 if t else float("nan")
         busy = v.get("MfmaUtil", float("nan"))
-        fl = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512
-        tf = fl / t / 1e12 if t else float("nan")
-        print("| %s | %.1f | %.1f | %.1f | %.0f | %.1f | %.0f |" % (label, (t or 0) * 1e6, rd / 1e6, wr / 1e6, bw, busy, tf))
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        fl = mops * 512 if mops is not None else None   # None: the pass set holds no MFMA op counter
+        tf = "%.0f" % (fl / t / 1e12) if (fl is not None and t) else "-"
+        print("| %s | %.1f | %.1f | %.1f | %.0f | %.1f | %s |" % (label, (t or 0) * 1e6, rd / 1e6, wr / 1e6, bw, busy, tf))
         rec[key] = {"read_bytes": rd, "write_bytes": wr, "avg_s": t, "mfma_busy_pct": busy, "mfma_bf16_flops": fl}
     l1 = rec.get(var["l1"])
     if l1:

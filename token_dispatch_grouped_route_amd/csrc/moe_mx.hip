@@ -376,8 +376,10 @@ __device__ __forceinline__ void mx_k_loop(MxPipe<MG>& p, char* __restrict__ s0, 
 // L2: GEMM of the FP8 activation rows against the FP4 W2, then the combine of the bf16 path
 // (bf16(w * o) into y for a token's only local pair, fp32 w * o into its stage row otherwise).
 // A tile is BM = 32 MG rows; block_m (d.BM) is a multiple of it, so a tile lies in one expert's block.
+// L2 runs two waves per SIMD (at most 256 registers; its 64-row tiles then spill a few values
+// outside the K loop), which measured faster than one; L1 measured slower with two.
 template <int MG, bool L1>
-__global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __restrict__ a_codes,
+__global__ __launch_bounds__(kMxThreads, L1 ? 1 : 2) void mx_gemm_kernel(const uint8_t* __restrict__ a_codes,
                                                              const uint8_t* __restrict__ a_scales,
                                                              const uint8_t* __restrict__ wq,
                                                              const uint8_t* __restrict__ wsc,
