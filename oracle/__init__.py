@@ -148,19 +148,28 @@ def l1_rows(x, topk_idx, W1, E: int, e_lo: int, pairs):
     return h, a
 
 
-def swiglu(hgu_bits) -> np.ndarray:
-    """silu(gate) * up on bf16 [gate | up] rows; returns fp64 [n, I]."""
-    hgu = _c(hgu_bits, np.uint16)
+def _rows_values(hgu):
+    """[gate | up] rows as fp64 values: uint16 arrays are bf16 bit patterns, anything else is
+    taken as real values (e.g. fp32 rows)."""
+    a = np.asarray(hgu)
+    if a.dtype == np.uint16:
+        return (np.ascontiguousarray(a).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return _c(a, np.float64)
+
+
+def swiglu(hgu) -> np.ndarray:
+    """silu(gate) * up on [gate | up] rows (bf16 bits or real values); returns fp64 [n, I]."""
+    hgu = _rows_values(hgu)
     n, N = hgu.shape
     a = np.zeros((n, N // 2), np.float64)
     _load().oracle_swiglu(n, N // 2, _p(hgu), _p(a))
     return a
 
 
-def swiglu_bwd(hgu_bits, da) -> np.ndarray:
-    """Gradient of silu(gate) * up w.r.t. [gate | up] (bf16 rows) for an upstream gradient da
-    (fp64 values, [n, I])."""
-    hgu, da = _c(hgu_bits, np.uint16), _c(da, np.float64)
+def swiglu_bwd(hgu, da) -> np.ndarray:
+    """Gradient of silu(gate) * up w.r.t. [gate | up] (rows as bf16 bits or real values) for an
+    upstream gradient da (fp64 values, [n, I])."""
+    hgu, da = _rows_values(hgu), _c(da, np.float64)
     n, N = hgu.shape
     assert da.shape == (n, N // 2)
     d = np.zeros((n, N), np.float64)

@@ -219,24 +219,25 @@ int oracle_l1_rows(int T, int H, int I, int E, int e_lo, int EL, int k, const ui
     return 0;
 }
 
-/* SwiGLU on given bf16 [gate | up] rows: a[r, c] = silu(hgu[r, c]) * hgu[r, I + c]. */
-int oracle_swiglu(int64_t nrows, int I, const uint16_t* hgu, double* a) {
+/* SwiGLU on given [gate | up] rows (real values, fp64): a[r, c] = silu(hgu[r, c]) * hgu[r, I + c]. */
+int oracle_swiglu(int64_t nrows, int I, const double* hgu, double* a) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nrows; ++r)
         for (int c = 0; c < I; ++c)
-            a[r * I + c] = silu(bf16_value(hgu[r * 2 * I + c])) * bf16_value(hgu[r * 2 * I + I + c]);
+            a[r * I + c] = silu(hgu[r * 2 * I + c]) * hgu[r * 2 * I + I + c];
     return 0;
 }
 
-/* SwiGLU backward on given bf16 [gate | up] rows and an upstream gradient da [nrows, I] (fp64):
- * with s = sigmoid(g): dgate = da * up * s * (1 + g * (1 - s)), dup = da * g * s. */
-int oracle_swiglu_bwd(int64_t nrows, int I, const uint16_t* hgu, const double* da,
+/* SwiGLU backward on given [gate | up] rows (real values, fp64) and an upstream gradient
+ * da [nrows, I] (fp64): with s = sigmoid(g): dgate = da * up * s * (1 + g * (1 - s)),
+ * dup = da * g * s. */
+int oracle_swiglu_bwd(int64_t nrows, int I, const double* hgu, const double* da,
                       double* dhgu) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nrows; ++r)
         for (int c = 0; c < I; ++c) {
-            const double g = bf16_value(hgu[r * 2 * I + c]);
-            const double u = bf16_value(hgu[r * 2 * I + I + c]);
+            const double g = hgu[r * 2 * I + c];
+            const double u = hgu[r * 2 * I + I + c];
             const double d = da[r * I + c];
             const double s = 1.0 / (1.0 + exp(-g));
             dhgu[r * 2 * I + c] = d * u * s * (1.0 + g * (1.0 - s));

@@ -354,6 +354,25 @@ def test_swiglu_fwd_bwd_match_torch_autograd():
     assert rel_err(oracle.swiglu_bwd(hgu, f64(da).numpy()), h.grad.numpy()) < 1e-13
 
 
+def test_swiglu_on_real_valued_rows_matches_torch_autograd():
+    """The SwiGLU functions also take the [gate | up] rows as real values (the saved fp32
+    pre-activation of a training forward): fp64 rows that no bf16 or fp32 pattern holds."""
+    rng = np.random.default_rng(16)
+    n, I = 29, 40
+    hv = 4 * rng.standard_normal((n, 2 * I))
+    da = rng.standard_normal((n, I))
+    h = torch.from_numpy(hv.copy()).requires_grad_(True)
+    a = F.silu(h[:, :I]) * h[:, I:]
+    a.backward(torch.from_numpy(da))
+    assert rel_err(oracle.swiglu(hv), a.detach().numpy()) < 1e-13
+    assert rel_err(oracle.swiglu_bwd(hv, da), h.grad.numpy()) < 1e-13
+    # bf16 bit patterns and the same values given as reals agree exactly
+    bits = mw.f32_to_bf16_bits(hv.astype(np.float32))
+    vals = mw.bf16_bits_to_f32(bits).astype(np.float64)
+    assert np.array_equal(oracle.swiglu(bits), oracle.swiglu(vals))
+    assert np.array_equal(oracle.swiglu_bwd(bits, da), oracle.swiglu_bwd(vals, da))
+
+
 # ----------------------------------------------------------------------------------------
 # Backward (weight gradients and per-pair intermediates) against torch autograd
 # ----------------------------------------------------------------------------------------
