@@ -334,3 +334,29 @@ def test_backward_is_graph_capturable():
             assert torch.equal(out[n], ref[n]), "replay %d: %s differs" % (i, n)
         moe.forward(ns.shape, ns.x, ns.idx, ns.wts, ns.W1p, ns.W2p, ns.ws, ns.y)   # eager work between
         torch.cuda.synchronize()
+
+
+def test_max_local_experts_forward_and_backward():
+    """EL = 1024 (the largest the ABI accepts, four experts per thread of the forward's tile-prefix
+    scan): the last expert's prefix entry must be written, so every expert's rows reach the GEMMs.
+    Forward and backward against the oracle on a small batch spread over 1024 local experts."""
+    w = mw.Workload("max_experts", T=256, H=128, I=128, E=1024, EL=1024, k=4, backward=True)
+    d = mw.inputs(w, 16)
+    idx = d["topk_idx"].copy()
+    idx[0, 0] = w.EL - 1          # the last local expert holds rows
+    idx[1, :] = [w.EL - 1, w.EL - 2, 0, 5]
+    d = dict(d, topk_idx=idx)
+    ns = run_forward_backward(w, d, 64)
+    t = tables(ns)
+    assert t["counts"][w.EL - 1] >= 2
+    ref = oracle.forward(d["x"], idx, d["topk_weights"], d["W1"], d["W2"], E=w.E, e_lo=w.e_lo)
+    check_bf16(f64_host(ns.y), ref, TOL, "y (EL = 1024)")
+    args = (d["x"], idx, d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    experts = [0, 5, w.EL - 2, w.EL - 1]
+    dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo, experts=experts)
+    g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
+    S1, S2 = term_sums(w, d, experts, pairs_of_expert(t))
+    for i, e in enumerate(experts):
+        check_sum_bound(g1[e], dW1[i], S1[i], C_DW1, TOL, "dW1[%d] (EL = 1024)" % e)
+        check_sum_bound(g2[e], dW2[i], S2[i], C_DW2, TOL, "dW2[%d] (EL = 1024)" % e)
+    check_token_grads(w, d, ns, np.arange(w.T), "(EL = 1024)")

@@ -98,12 +98,40 @@ def _check(status: int, what: str):
         raise MoeError("%s: %s (%d)" % (what, lib().moe_status_string(status).decode(), status))
 
 
-def _ptr(t, dtype, name):
+def _ptr(t, dtype, name, numel=None):
+    """Device address of t after checking dtype, device, contiguity and (when given) that it
+    holds at least ``numel`` elements: an undersized buffer becomes an error here instead of an
+    out-of-bounds access in a kernel."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
         raise MoeError("%s must be a contiguous %s tensor on a GPU" % (name, dtype))
+    if numel is not None and t.numel() < numel:
+        raise MoeError("%s holds %d elements; the shape needs %d" % (name, t.numel(), numel))
     return t.data_ptr()
+
+
+def _n(shape: Shape):
+    """Element counts of every caller buffer of a shape (rows regions use the static bound)."""
+    R = _rows_capacity(shape)
+    th, tk, w1n, w2n = shape.T * shape.H, shape.T * shape.k, shape.EL * 2 * shape.I * shape.H, \
+        shape.EL * shape.H * shape.I
+    return {"x": th, "y": th, "dy": th, "dx": th, "topk_idx": tk, "topk_w": tk, "dtopk_w": tk,
+            "w1": w1n, "w2": w2n, "w1p": w1n, "w2p": w2n, "dw1p": w1n, "dw2p": w2n,
+            "act": R * shape.I, "act_out": R * shape.I, "hgu": R * 2 * shape.I, "hgu_out": R * 2 * shape.I,
+            "xq": th, "xs": th // 32, "w1q": w1n // 2, "w1s": w1n // 32, "w2q": w2n // 2, "w2s": w2n // 32}
+
+
+_ROWS_CAP = {}
+
+
+def _rows_capacity(shape: Shape) -> int:
+    key = tuple(getattr(shape, n) for n, _ in Shape._fields_)
+    if key not in _ROWS_CAP:
+        L = WsLayout()
+        _check(lib().moe_workspace_layout(ctypes.byref(shape), ctypes.byref(L)), "moe_workspace_layout")
+        _ROWS_CAP[key] = int(L.rows_capacity)
+    return _ROWS_CAP[key]
 
 
 def _stream(stream):
@@ -189,66 +217,75 @@ def alloc_packed(shape: Shape, device="cuda"):
 
 
 def pack_weights(shape, w1=None, w2=None, w1p=None, w2p=None, stream=None):
-    _check(lib().moe_pack_weights(ctypes.byref(shape), _ptr(w1, torch.bfloat16, "w1"),
-                                  _ptr(w2, torch.bfloat16, "w2"), _ptr(w1p, torch.bfloat16, "w1p"),
-                                  _ptr(w2p, torch.bfloat16, "w2p"), _stream(stream)), "moe_pack_weights")
+    nn = _n(shape)
+    _check(lib().moe_pack_weights(ctypes.byref(shape), _ptr(w1, torch.bfloat16, "w1", nn["w1"]),
+                                  _ptr(w2, torch.bfloat16, "w2", nn["w2"]), _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]),
+                                  _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]), _stream(stream)), "moe_pack_weights")
 
 
 def route_prologue(shape, topk_idx, ws, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_route_prologue(ctypes.byref(shape), _ptr(topk_idx, torch.int32, "topk_idx"), p, n,
+    _check(lib().moe_route_prologue(ctypes.byref(shape), _ptr(topk_idx, torch.int32, "topk_idx", nn["topk_idx"]), p, n,
                                     _stream(stream)), "moe_route_prologue")
 
 
 def unpack_weights(shape, w1p=None, w2p=None, w1=None, w2=None, stream=None):
     """Packed (w1p, w2p) or weight gradients (dw1p, dw2p) -> logical [EL, H, 2I], [EL, I, H]."""
-    _check(lib().moe_unpack_weights(ctypes.byref(shape), _ptr(w1p, torch.bfloat16, "w1p"),
-                                    _ptr(w2p, torch.bfloat16, "w2p"), _ptr(w1, torch.bfloat16, "w1"),
-                                    _ptr(w2, torch.bfloat16, "w2"), _stream(stream)), "moe_unpack_weights")
+    nn = _n(shape)
+    _check(lib().moe_unpack_weights(ctypes.byref(shape), _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]),
+                                    _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]), _ptr(w1, torch.bfloat16, "w1", nn["w1"]),
+                                    _ptr(w2, torch.bfloat16, "w2", nn["w2"]), _stream(stream)), "moe_unpack_weights")
 
 
 def dispatch_gemm1(shape, x, w1p, ws, act_out=None, hgu_out=None, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_dispatch_gemm1(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"),
-                                    _ptr(w1p, torch.bfloat16, "w1p"), p, n,
-                                    _ptr(act_out, torch.bfloat16, "act_out"),
-                                    _ptr(hgu_out, torch.bfloat16, "hgu_out"), _stream(stream)),
+    _check(lib().moe_dispatch_gemm1(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x", nn["x"]),
+                                    _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]), p, n,
+                                    _ptr(act_out, torch.bfloat16, "act_out", nn["act_out"]),
+                                    _ptr(hgu_out, torch.bfloat16, "hgu_out", nn["hgu_out"]), _stream(stream)),
            "moe_dispatch_gemm1")
 
 
 def swiglu(shape, hgu, ws, act, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_swiglu(ctypes.byref(shape), _ptr(hgu, torch.bfloat16, "hgu"), p, n,
-                            _ptr(act, torch.bfloat16, "act"), _stream(stream)), "moe_swiglu")
+    _check(lib().moe_swiglu(ctypes.byref(shape), _ptr(hgu, torch.bfloat16, "hgu", nn["hgu"]), p, n,
+                            _ptr(act, torch.bfloat16, "act", nn["act"]), _stream(stream)), "moe_swiglu")
 
 
 def gemm2_combine(shape, act, w2p, topk_w, ws, y, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_gemm2_combine(ctypes.byref(shape), _ptr(act, torch.bfloat16, "act"),
-                                   _ptr(w2p, torch.bfloat16, "w2p"), _ptr(topk_w, torch.float32, "topk_w"),
-                                   p, n, _ptr(y, torch.bfloat16, "y"), _stream(stream)), "moe_gemm2_combine")
+    _check(lib().moe_gemm2_combine(ctypes.byref(shape), _ptr(act, torch.bfloat16, "act", nn["act"]),
+                                   _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]), _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]),
+                                   p, n, _ptr(y, torch.bfloat16, "y", nn["y"]), _stream(stream)), "moe_gemm2_combine")
 
 
 def forward(shape, x, topk_idx, topk_w, w1p, w2p, ws, y, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_forward(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"),
-                             _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_w, torch.float32, "topk_w"),
-                             _ptr(w1p, torch.bfloat16, "w1p"), _ptr(w2p, torch.bfloat16, "w2p"), p, n,
-                             _ptr(y, torch.bfloat16, "y"), _stream(stream)), "moe_forward")
+    _check(lib().moe_forward(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x", nn["x"]),
+                             _ptr(topk_idx, torch.int32, "topk_idx", nn["topk_idx"]), _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]),
+                             _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]), _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]), p, n,
+                             _ptr(y, torch.bfloat16, "y", nn["y"]), _stream(stream)), "moe_forward")
 
 
 def bwd_gemm2_dgrad(shape, dy, topk_w, w2p, ws, fuse_swiglu_bwd=True, dtopk_w=None, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_bwd_gemm2_dgrad(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy"),
-                                     _ptr(topk_w, torch.float32, "topk_w"), _ptr(w2p, torch.bfloat16, "w2p"),
-                                     p, n, int(bool(fuse_swiglu_bwd)), _ptr(dtopk_w, torch.float32, "dtopk_w"),
+    _check(lib().moe_bwd_gemm2_dgrad(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy", nn["dy"]),
+                                     _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]), _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]),
+                                     p, n, int(bool(fuse_swiglu_bwd)), _ptr(dtopk_w, torch.float32, "dtopk_w", nn["dtopk_w"]),
                                      _stream(stream)), "moe_bwd_gemm2_dgrad")
 
 
 def bwd_gemm1_dgrad_combine(shape, w1p, ws, dx, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_bwd_gemm1_dgrad_combine(ctypes.byref(shape), _ptr(w1p, torch.bfloat16, "w1p"), p, n,
-                                             _ptr(dx, torch.bfloat16, "dx"), _stream(stream)),
+    _check(lib().moe_bwd_gemm1_dgrad_combine(ctypes.byref(shape), _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]), p, n,
+                                             _ptr(dx, torch.bfloat16, "dx", nn["dx"]), _stream(stream)),
            "moe_bwd_gemm1_dgrad_combine")
 
 
@@ -258,25 +295,28 @@ def swiglu_bwd(shape, ws, stream=None):
 
 
 def wgrad2(shape, dy, topk_w, ws, dw2p, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_wgrad2(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy"),
-                            _ptr(topk_w, torch.float32, "topk_w"), p, n, _ptr(dw2p, torch.bfloat16, "dw2p"),
+    _check(lib().moe_wgrad2(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy", nn["dy"]),
+                            _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]), p, n, _ptr(dw2p, torch.bfloat16, "dw2p", nn["dw2p"]),
                             _stream(stream)), "moe_wgrad2")
 
 
 def wgrad1(shape, x, ws, dw1p, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_wgrad1(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"), p, n,
-                            _ptr(dw1p, torch.bfloat16, "dw1p"), _stream(stream)), "moe_wgrad1")
+    _check(lib().moe_wgrad1(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x", nn["x"]), p, n,
+                            _ptr(dw1p, torch.bfloat16, "dw1p", nn["dw1p"]), _stream(stream)), "moe_wgrad1")
 
 
 def backward(shape, x, dy, topk_w, w2p, ws, dw1p, dw2p, w1p=None, dx=None, dtopk_w=None, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_backward(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x"), _ptr(dy, torch.bfloat16, "dy"),
-                              _ptr(topk_w, torch.float32, "topk_w"), _ptr(w1p, torch.bfloat16, "w1p"),
-                              _ptr(w2p, torch.bfloat16, "w2p"), p, n,
-                              _ptr(dw1p, torch.bfloat16, "dw1p"), _ptr(dw2p, torch.bfloat16, "dw2p"),
-                              _ptr(dx, torch.bfloat16, "dx"), _ptr(dtopk_w, torch.float32, "dtopk_w"),
+    _check(lib().moe_backward(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x", nn["x"]), _ptr(dy, torch.bfloat16, "dy", nn["dy"]),
+                              _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]), _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]),
+                              _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]), p, n,
+                              _ptr(dw1p, torch.bfloat16, "dw1p", nn["dw1p"]), _ptr(dw2p, torch.bfloat16, "dw2p", nn["dw2p"]),
+                              _ptr(dx, torch.bfloat16, "dx", nn["dx"]), _ptr(dtopk_w, torch.float32, "dtopk_w", nn["dtopk_w"]),
                               _stream(stream)), "moe_backward")
 
 
@@ -290,8 +330,10 @@ def mx_cast_fp8(x, codes=None, scales=None, stream=None):
         codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)
-    _check(lib().moe_mx_cast_fp8(rows, cols, _ptr(x, torch.bfloat16, "x"), _ptr(codes, torch.uint8, "codes"),
-                                 _ptr(scales, torch.uint8, "scales"), _stream(stream)), "moe_mx_cast_fp8")
+    _check(lib().moe_mx_cast_fp8(rows, cols, _ptr(x, torch.bfloat16, "x"),
+                                 _ptr(codes, torch.uint8, "codes", rows * cols),
+                                 _ptr(scales, torch.uint8, "scales", rows * (cols // 32)), _stream(stream)),
+           "moe_mx_cast_fp8")
     return codes, scales
 
 
@@ -307,30 +349,34 @@ def mx_alloc_packed(shape: Shape, device="cuda"):
 
 
 def mx_pack_weights(shape, w1, w2, w1q, w1s, w2q, w2s, stream=None):
-    _check(lib().moe_mx_pack_weights(ctypes.byref(shape), _ptr(w1, torch.bfloat16, "w1"),
-                                     _ptr(w2, torch.bfloat16, "w2"), _ptr(w1q, torch.uint8, "w1q"),
-                                     _ptr(w1s, torch.uint8, "w1s"), _ptr(w2q, torch.uint8, "w2q"),
-                                     _ptr(w2s, torch.uint8, "w2s"), _stream(stream)), "moe_mx_pack_weights")
+    nn = _n(shape)
+    _check(lib().moe_mx_pack_weights(ctypes.byref(shape), _ptr(w1, torch.bfloat16, "w1", nn["w1"]),
+                                     _ptr(w2, torch.bfloat16, "w2", nn["w2"]), _ptr(w1q, torch.uint8, "w1q", nn["w1q"]),
+                                     _ptr(w1s, torch.uint8, "w1s", nn["w1s"]), _ptr(w2q, torch.uint8, "w2q", nn["w2q"]),
+                                     _ptr(w2s, torch.uint8, "w2s", nn["w2s"]), _stream(stream)), "moe_mx_pack_weights")
 
 
 def forward_mx(shape, xq, xs, topk_idx, topk_w, w1q, w1s, w2q, w2s, ws, y, clamp=10.0, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_forward_mx(ctypes.byref(shape), _ptr(xq, torch.uint8, "xq"), _ptr(xs, torch.uint8, "xs"),
-                                _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_w, torch.float32, "topk_w"),
-                                _ptr(w1q, torch.uint8, "w1q"), _ptr(w1s, torch.uint8, "w1s"),
-                                _ptr(w2q, torch.uint8, "w2q"), _ptr(w2s, torch.uint8, "w2s"), float(clamp), p, n,
-                                _ptr(y, torch.bfloat16, "y"), _stream(stream)), "moe_forward_mx")
+    _check(lib().moe_forward_mx(ctypes.byref(shape), _ptr(xq, torch.uint8, "xq", nn["xq"]), _ptr(xs, torch.uint8, "xs", nn["xs"]),
+                                _ptr(topk_idx, torch.int32, "topk_idx", nn["topk_idx"]), _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]),
+                                _ptr(w1q, torch.uint8, "w1q", nn["w1q"]), _ptr(w1s, torch.uint8, "w1s", nn["w1s"]),
+                                _ptr(w2q, torch.uint8, "w2q", nn["w2q"]), _ptr(w2s, torch.uint8, "w2s", nn["w2s"]), float(clamp), p, n,
+                                _ptr(y, torch.bfloat16, "y", nn["y"]), _stream(stream)), "moe_forward_mx")
 
 
 def mx_dispatch_gemm1(shape, xq, xs, w1q, w1s, ws, clamp=10.0, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_mx_dispatch_gemm1(ctypes.byref(shape), _ptr(xq, torch.uint8, "xq"), _ptr(xs, torch.uint8, "xs"),
-                                       _ptr(w1q, torch.uint8, "w1q"), _ptr(w1s, torch.uint8, "w1s"), float(clamp), p,
+    _check(lib().moe_mx_dispatch_gemm1(ctypes.byref(shape), _ptr(xq, torch.uint8, "xq", nn["xq"]), _ptr(xs, torch.uint8, "xs", nn["xs"]),
+                                       _ptr(w1q, torch.uint8, "w1q", nn["w1q"]), _ptr(w1s, torch.uint8, "w1s", nn["w1s"]), float(clamp), p,
                                        n, _stream(stream)), "moe_mx_dispatch_gemm1")
 
 
 def mx_gemm2_combine(shape, w2q, w2s, topk_w, ws, y, stream=None):
+    nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_mx_gemm2_combine(ctypes.byref(shape), _ptr(w2q, torch.uint8, "w2q"), _ptr(w2s, torch.uint8, "w2s"),
-                                      _ptr(topk_w, torch.float32, "topk_w"), p, n, _ptr(y, torch.bfloat16, "y"),
+    _check(lib().moe_mx_gemm2_combine(ctypes.byref(shape), _ptr(w2q, torch.uint8, "w2q", nn["w2q"]), _ptr(w2s, torch.uint8, "w2s", nn["w2s"]),
+                                      _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]), p, n, _ptr(y, torch.bfloat16, "y", nn["y"]),
                                       _stream(stream)), "moe_mx_gemm2_combine")

@@ -271,6 +271,8 @@ __device__ int m_tile_prefix(const Ws& ws, int EL, int* s_pref, int* s_q, int* s
         if (e <= EL) s_pref[e] = run;
         run += v[q];
     }
+    // with EL == 4 * NT no thread holds index EL above: the last thread writes the total there
+    if (tid == NT - 1 && EL == 4 * NT) s_pref[EL] = run;
     __syncthreads();
     return s_part[NT - 1];
 }
