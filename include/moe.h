@@ -74,7 +74,10 @@ typedef struct moe_shape {
 } moe_shape;
 
 /*
- * Workspace layout: byte offsets of each region from the start of `ws`.
+ * Workspace layout: byte offsets of each region from the start of `ws`.  A hi / lo pair holds a
+ * value v computed in fp32 as two bf16 arrays, hi = bf16(v) and lo = bf16(v - hi): the bf16
+ * matrix cores take the pair as two operands, so the value enters a GEMM with about 16
+ * significant bits instead of 8.
  *   rows_capacity  R_max = round_up(T*k + EL*(block_m - 1), block_m), the static bound on
  *                  padded rows every row-indexed region and grid is sized from
  *   counts         int32 [EL]           rows of each local expert
@@ -86,9 +89,9 @@ typedef struct moe_shape {
  *   meta           int32 [4]            [0] padded row total R, [1] ids outside [0, E)
  *   act            bf16  [R_max, I]     SwiGLU output rows (L2 input)
  *   stage          fp32  [R_max, H]     weighted L2 rows of tokens with several local pairs
- *   hgu            bf16  [R_max, 2I]    pre-activation rows (train only, else 0)
- *   dact           bf16  [R_max, I]     L2 dgrad rows (train only, else 0)
- *   dhgu           bf16  [R_max, 2I]    [gate | up] gradient rows (train only, else 0)
+ *   hgu            fp32  [R_max, 2I]    pre-activation rows (train only, else 0)
+ *   dact           fp32  [R_max, I]     L2 dgrad rows (train only, else 0)
+ *   dhgu           bf16  [R_max, 2I]    [gate | up] gradient rows, hi part (train only, else 0)
  *   zeros          bf16  [max(H, 2I)]   a zero row (written by moe_route_prologue), read in place
  *                                       of the token row of a padding row
  *   scratch        prologue scratch (per-chunk expert histograms)
@@ -96,6 +99,10 @@ typedef struct moe_shape {
  *                                       moe_route_prologue; zero again after each GEMM launch)
  *   dtw_part       fp32  [R_max, I/128] per-row partial sums of the routing-weight gradient, one
  *                                       per 128-column tile of the L2 dgrad (train only, else 0)
+ *   dhgu_lo        bf16  [R_max, 2I]    lo part of the [gate | up] gradient rows (train only)
+ *   wact           bf16  [R_max, I]     w * act, the activation row times its pair's routing
+ *                                       weight, hi part (train only, else 0)
+ *   wact_lo        bf16  [R_max, I]     its lo part (train only, else 0)
  */
 typedef struct moe_ws_layout {
     size_t total_bytes;
@@ -103,6 +110,7 @@ typedef struct moe_ws_layout {
     int64_t num_blocks;
     size_t counts, padded_offsets, row_pair, pair_row, tile_expert, tok_nloc, meta;
     size_t act, stage, hgu, dact, dhgu, zeros, scratch, tile_sync, dtw_part;
+    size_t dhgu_lo, wact, wact_lo;
 } moe_ws_layout;
 
 /* Message for a status code (static string). */
@@ -157,20 +165,20 @@ int32_t moe_route_prologue(const moe_shape* shape, const int32_t* topk_idx, void
  * (moe_pack_weights), with x [device] bf16 [T, H] gathered through row_pair inside the tile load
  * (padding rows are zero).  Writes, for rows [0, R):
  *   act_out [device] bf16 [R_max, I]  = silu(h[:, :I]) * h[:, I:]   (SwiGLU in the epilogue)
- *   hgu_out [device] bf16 [R_max, 2I] = h                            (pre-activation)
+ *   hgu_out [device] fp32 [R_max, 2I] = h                            (pre-activation)
  * Either output may be NULL, not both.  Pass ws-relative regions (layout act / hgu) to feed
  * moe_gemm2_combine and the backward.
  */
 int32_t moe_dispatch_gemm1(const moe_shape* shape, const uint16_t* x, const uint16_t* w1p,
-                           void* ws, size_t ws_bytes, uint16_t* act_out, uint16_t* hgu_out,
+                           void* ws, size_t ws_bytes, uint16_t* act_out, float* hgu_out,
                            void* stream);
 
 /*
  * SwiGLU ("Mega MoE" page, Pipeline; Implementation Map, SwiGLU fwd): act[r, c] =
  * silu(hgu[r, c]) * hgu[r, I + c] for rows [0, R) (R read from ws on the device).
- *   hgu [device] bf16 [R_max, 2I], act [device] bf16 [R_max, I]
+ *   hgu [device] fp32 [R_max, 2I], act [device] bf16 [R_max, I]
  */
-int32_t moe_swiglu(const moe_shape* shape, const uint16_t* hgu, const void* ws,
+int32_t moe_swiglu(const moe_shape* shape, const float* hgu, const void* ws,
                    size_t ws_bytes, uint16_t* act, void* stream);
 
 /*
@@ -197,7 +205,9 @@ int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* to
 
 /*
  * Backward entry points ("Mega MoE" page, Pipeline, backward).  They need a workspace with
- * shape->train nonzero that a moe_forward of the same inputs filled (tables, act, hgu).
+ * shape->train nonzero that a moe_forward of the same inputs filled (tables, act, hgu), and run
+ * in this order on one stream: moe_bwd_gemm2_dgrad (or it without the SwiGLU transpose, then
+ * moe_swiglu_bwd), then moe_wgrad2, moe_wgrad1 and moe_bwd_gemm1_dgrad_combine in any order.
  * When the expected rows per local expert (T * k / E) are at least 256 (and the shape allows),
  * they run on the forward GEMM's pipeline and use ws regions that are dead at that point as
  * scratch: moe_bwd_gemm2_dgrad, moe_wgrad2 and moe_wgrad1 overwrite ws stage (after the forward's
@@ -205,20 +215,23 @@ int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* to
  *
  * L2 dgrad, NN: dact[r] = topk_w[p] * (dy[t] @ W2[e]^T) with p = row_pair[r], t = p / k, read
  * from the packed w2p as the [K = H, N = I] operand.  With fuse_swiglu_bwd nonzero the
- * epilogue applies the SwiGLU transpose and writes ws dhgu directly; else it writes ws dact.
+ * epilogue applies the SwiGLU transpose and writes ws dhgu / dhgu_lo directly; else it writes
+ * ws dact (fp32).  Either way it recomputes the activation a = silu(g) * u in fp32 from the saved
+ * pre-activation and writes ws wact / wact_lo = topk_w[p] * a (the operand of moe_wgrad2).
  * With dtopk_w non-NULL it also writes the gradient of the routing weights, the derivative of
  * the weighted scatter-add y[t] = sum_j topk_w[t, j] * o_p:
  *   dtopk_w [device] fp32 [T, k]: dtopk_w[t, j] = <dy[t], o_p> for a local pair p = t*k + j,
- *   computed as <dy[t] @ W2[e]^T, act[r]> on the saved activation row (the same value, since
- *   o_p = act[r] @ W2[e]); 0 for a pair this GPU does not handle (its partial of the gradient).
+ *   computed as <dy[t] @ W2[e]^T, a[r]> (the same value, since o_p = a[r] @ W2[e]); 0 for a pair
+ *   this GPU does not handle (its partial of the gradient).
  *   dy [device] bf16 [T, H]; topk_w [device] fp32 [T, k]
  */
 int32_t moe_bwd_gemm2_dgrad(const moe_shape* shape, const uint16_t* dy, const float* topk_w,
                             const uint16_t* w2p, void* ws, size_t ws_bytes,
                             int32_t fuse_swiglu_bwd, float* dtopk_w, void* stream);
 
-/* SwiGLU transpose ("Mega MoE" page, SwiGLU bwd): from ws dact and ws hgu, with
- * s = sigmoid(g): dgate = dact * u * s * (1 + g * (1 - s)), dup = dact * g * s -> ws dhgu. */
+/* SwiGLU transpose ("Mega MoE" page, SwiGLU bwd): from ws dact and ws hgu (both fp32), with
+ * s = sigmoid(g): dgate = dact * u * s * (1 + g * (1 - s)), dup = dact * g * s -> ws dhgu /
+ * dhgu_lo. */
 int32_t moe_swiglu_bwd(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -233,15 +246,17 @@ int32_t moe_bwd_gemm1_dgrad_combine(const moe_shape* shape, const uint16_t* w1p,
                                     size_t ws_bytes, uint16_t* dx, void* stream);
 
 /* dW2 with variable K ("Mega MoE" page, backward: dW2 (variable-K)):
- * dW2[e] [I, H] = sum over rows r of e of act[r]^T (x) (topk_w[p] * dy[t]); K = count of e.
- * An expert without rows gets exact zeros.  dw2p [device] bf16, EL * H * I elements, in the
- * packed layout of w2p (moe_unpack_weights gives the logical [EL, I, H]). */
-int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, const float* topk_w, void* ws,
-                   size_t ws_bytes, uint16_t* dw2p, void* stream);
+ * dW2[e] [I, H] = sum over rows r of e of (topk_w[p] * act[r])^T (x) dy[t]; K = count of e.
+ * Reads the weighted activation rows ws wact / wact_lo that moe_bwd_gemm2_dgrad wrote; dy
+ * [device] bf16 [T, H].  An expert without rows gets exact zeros.  dw2p [device] bf16,
+ * EL * H * I elements, in the packed layout of w2p (moe_unpack_weights gives the logical
+ * [EL, I, H]). */
+int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, void* ws, size_t ws_bytes,
+                   uint16_t* dw2p, void* stream);
 
 /* dW1, TN with variable K ("Mega MoE" page, backward: dW1 (TN); Core Design section 2):
- * dW1[e] [H, 2I] = sum over rows r of e of x[row_pair[r] / k]^T (x) dhgu[r], re-gathering
- * the token rows instead of saving them.  dw1p [device] bf16, EL * 2I * H elements, in the
+ * dW1[e] [H, 2I] = sum over rows r of e of x[row_pair[r] / k]^T (x) dhgu[r] (hi and lo parts),
+ * re-gathering the token rows instead of saving them.  dw1p [device] bf16, EL * 2I * H elements, in the
  * packed layout of w1p (moe_unpack_weights gives the logical [EL, H, 2I]). */
 int32_t moe_wgrad1(const moe_shape* shape, const uint16_t* x, void* ws, size_t ws_bytes,
                    uint16_t* dw1p, void* stream);

@@ -51,7 +51,8 @@ def test_workspace_layout(cfg, bm, train):
     sizes = {"counts": 4 * EL, "padded_offsets": 4 * (EL + 1), "row_pair": 4 * R, "pair_row": 4 * T * k,
              "tile_expert": 4 * (R // bm), "tok_nloc": 4 * T, "meta": 16, "act": 2 * R * I, "stage": 4 * R * H}
     if train:
-        sizes.update(hgu=4 * R * I, dact=2 * R * I, dhgu=4 * R * I, dtw_part=4 * R * (I // 128))
+        sizes.update(hgu=8 * R * I, dact=4 * R * I, dhgu=4 * R * I, dhgu_lo=4 * R * I, wact=2 * R * I,
+                     wact_lo=2 * R * I, dtw_part=4 * R * (I // 128))
     sizes["tile_sync"] = 4 * 512
     spans = sorted((L[n], L[n] + sz, n) for n, sz in sizes.items())
     for (a0, a1, na), (b0, b1, nb) in zip(spans, spans[1:]):

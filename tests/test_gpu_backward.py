@@ -5,19 +5,13 @@ the routing weights, the standalone SwiGLU backward, dW2 and dW1 with a variable
 expert, including experts without rows, whose gradients must be exact zeros) and the L1 dgrad
 (NN) with its combine back to token order (dx).
 
-Acceptance:
-  * row intermediates (dact, dhgu) are checked link by link: dact against the oracle's L2
-    dgrad, dhgu against the oracle's SwiGLU transpose evaluated on the GPU's own saved bf16
-    pre-activations; bound 2e-2 * rms on top of each element's own rounding to bf16;
-  * dW1 and dW2 are sums over an expert's rows of products of bf16 MFMA operands; besides
-    2e-2 * rms and the output rounding, each element may carry c * 2^-8 * sum|terms| (the
-    dot-product error bound, 2^-8 = bf16 unit roundoff): c = 2 for dW2 (both operands, the
-    saved activation and w * dy, are rounded once) and c = 3 for dW1 (x is exact; the dhgu
-    operand is rounded and was itself computed from bf16 saved pre-activations).
-  * dx is a sum over a token's local pairs of dhgu rows times W1[e]^T: like dW1, c = 3 on
-    sum_p |W1[e]| |dhgu_p|.  d(topk_w)[t, j] = <dy[t] @ W2[e]^T, act_p> with the saved bf16
-    activation: c = 2 on sum_c |(dy W2^T)_c act_c|.  Tokens with no local pair (dx) and pairs
-    this GPU does not handle (d(topk_w)) must be exact zeros.
+Acceptance is the forward's: every bf16 output (dW1, dW2, dx, the dhgu rows) within 2e-2 * rms of
+the oracle plus the element's own rounding to bf16 (check_bf16); every fp32 output or hi + lo
+pair (d(topk_w), dact, the saved pre-activation, the weighted activation) within 2e-2 * rms
+(check_f32).  The oracle computes in fp64 from the bf16 inputs.  Row intermediates are also
+checked link by link: dhgu against the oracle's SwiGLU transpose evaluated on the GPU's own saved
+pre-activation and dact.  Tokens with no local pair (dx) and pairs this GPU does not handle
+(d(topk_w)) must be exact zeros.
 """
 import numpy as np
 import pytest
@@ -26,12 +20,10 @@ import torch
 import moe_workloads as mw
 import oracle
 import token_dispatch_grouped_route_amd as moe
-from gpu_helpers import bits_host, check_bf16, check_sum_bound, f64_host, layer, tables, unpacked
+from gpu_helpers import check_bf16, check_f32, f64_host, layer, tables, unpacked
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
-C_DW1, C_DW2 = 3.0, 2.0
-C_DX, C_DTW = 3.0, 2.0
 
 
 @pytest.fixture(autouse=True)
@@ -46,7 +38,7 @@ REDUCED = [
     mw.Workload("bwd_ragged_shard", T=301, H=384, I=256, E=10, EL=5, k=3, e_lo=2, backward=True),
     # about 256 rows per expert: the weight gradients run on the forward pipeline (block_m >= 64)
     mw.Workload("bwd_many_rows", T=1024, H=512, I=256, E=8, EL=4, k=2, e_lo=2, backward=True),
-    # about 512 rows per expert and 2 * EL * H <= R_max: the L1 dgrad also runs as the forward's L2
+    # about 512 rows per expert and EL * H <= R_max: the L1 dgrad also runs as the forward's L2
     mw.Workload("bwd_many_rows_narrow", T=2048, H=256, I=128, E=8, EL=4, k=2, e_lo=2, backward=True),
 ]
 
@@ -72,36 +64,13 @@ def run_forward_backward(w, d, bm):
     return ns
 
 
-def token_term_sums(w, d, tokens):
-    """sum|terms| of the dx rows and d(topk_w) entries of the given tokens, from the oracle's
-    per-pair rows: sum_p |W1[e]| |dhgu_p| and sum_c |(dy W2^T)_c act_c|."""
-    idx = d["topk_idx"]
-    Sx = np.zeros((len(tokens), w.H))
-    Sw = np.zeros((len(tokens), w.k))
-    pairs = [int(t) * w.k + j for t in tokens for j in range(w.k)
-             if w.e_lo <= idx[t, j] < w.e_lo + w.EL]
-    if not pairs:
-        return Sx, Sw
-    dA, dH, a = oracle_rows(w, d, np.array(pairs))
-    wts = d["topk_weights"].reshape(-1)[pairs].astype(np.float64)
-    pos = {int(t): i for i, t in enumerate(tokens)}
-    for n, p in enumerate(pairs):
-        t, j = divmod(p, w.k)
-        e = int(idx[t, j]) - w.e_lo
-        W1e = np.abs(mw.bf16_bits_to_f32(d["W1"][e]).astype(np.float64))
-        Sx[pos[t]] += W1e @ np.abs(dH[n])
-        Sw[pos[t], j] = np.sum(np.abs(dA[n] / wts[n]) * np.abs(a[n]))
-    return Sx, Sw
-
-
 def check_token_grads(w, d, ns, tokens, what):
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dx_ref, dw_ref = oracle.backward_tokens(*args, E=w.E, e_lo=w.e_lo, tokens=tokens)
-    Sx, Sw = token_term_sums(w, d, tokens)
     dx = f64_host(ns.dx)[tokens]
     dw = ns.dtw.cpu().double().numpy()[tokens]
-    check_sum_bound(dx, dx_ref, Sx, C_DX, TOL, "dx " + what)
-    check_sum_bound(dw, dw_ref, Sw, C_DTW, TOL, "d(topk_w) " + what)
+    check_bf16(dx, dx_ref, TOL, "dx " + what)
+    check_f32(dw, dw_ref, TOL, "d(topk_w) " + what)
     local = (d["topk_idx"] >= w.e_lo) & (d["topk_idx"] < w.e_lo + w.EL)
     assert np.all(dw[~local[tokens]] == 0.0), "pairs this GPU does not handle must get exact zeros"
     assert np.all(dx[~local[tokens].any(axis=1)] == 0.0), "tokens with no local pair must get exact zeros"
@@ -110,26 +79,30 @@ def check_token_grads(w, d, ns, tokens, what):
 def oracle_rows(w, d, pairs):
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dA, dH = oracle.backward_rows(*args, E=w.E, e_lo=w.e_lo, pairs=pairs)
-    _, a = oracle.l1_rows(d["x"], d["topk_idx"], d["W1"], w.E, w.e_lo, pairs)
-    return dA, dH, a
+    h, a = oracle.l1_rows(d["x"], d["topk_idx"], d["W1"], w.E, w.e_lo, pairs)
+    return dA, dH, h, a
 
 
-def term_sums(w, d, experts, rows_of):
-    """sum|terms| of every dW1 / dW2 element of the given experts, from the oracle's rows."""
-    X = mw.bf16_bits_to_f32(d["x"]).astype(np.float64)
-    dy = mw.bf16_bits_to_f32(d["dy"]).astype(np.float64)
-    S1 = np.zeros((len(experts), w.H, 2 * w.I))
-    S2 = np.zeros((len(experts), w.I, w.H))
-    for i, e in enumerate(experts):
-        pairs = rows_of(e)
-        if len(pairs) == 0:
-            continue
-        _, dH, a = oracle_rows(w, d, pairs)
-        t = pairs // w.k
-        wd = np.abs(d["topk_weights"].reshape(-1)[pairs])[:, None] * np.abs(dy[t])
-        S1[i] = np.abs(X[t]).T @ np.abs(dH)
-        S2[i] = np.abs(a).T @ wd
-    return S1, S2
+def ws_f64(ns, name, rows=None):
+    v = f64_host(moe.ws_region(ns.ws, ns.shape, name))
+    return v if rows is None else v[rows]
+
+
+def check_row_links(w, d, ns, rows, what):
+    """Row intermediates of the given ws rows: the saved fp32 pre-activation against the oracle's
+    L1 rows; the weighted activation (hi + lo) against w * SwiGLU of that pre-activation; dhgu (hi,
+    and hi + lo) against the oracle's SwiGLU transpose of the oracle's dA on the GPU's own saved
+    pre-activation."""
+    pairs = tables(ns)["row_pair"][rows]
+    dA, _, h_ref, _ = oracle_rows(w, d, pairs)
+    hgu = ws_f64(ns, "hgu", rows)
+    check_f32(hgu, h_ref, TOL, "hgu " + what)
+    wts = d["topk_weights"].reshape(-1)[pairs].astype(np.float64)[:, None]
+    wact = ws_f64(ns, "wact", rows) + ws_f64(ns, "wact_lo", rows)
+    check_f32(wact, wts * oracle.swiglu(hgu), TOL, "w*act (hi+lo) " + what)
+    ref = oracle.swiglu_bwd(hgu, dA)
+    check_bf16(ws_f64(ns, "dhgu", rows), ref, TOL, "dhgu " + what)
+    check_f32(ws_f64(ns, "dhgu", rows) + ws_f64(ns, "dhgu_lo", rows), ref, TOL, "dhgu (hi+lo) " + what)
 
 
 def pairs_of_expert(tab):
@@ -147,17 +120,14 @@ def test_backward_reduced_full_compare(w, bm):
     t = tables(ns)
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
-    S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
     g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
-    check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1")
-    check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2")
+    tag = "(%s, bm %d)" % (w.name, bm)
+    check_bf16(g1, dW1, TOL, "dW1 " + tag)
+    check_bf16(g2, dW2, TOL, "dW2 " + tag)
     assert np.all(g1[1] == 0.0) and np.all(g2[1] == 0.0), "expert without rows must get exact zeros"
     real = np.nonzero(t["row_pair"] >= 0)[0]
-    dA, _, _ = oracle_rows(w, d, t["row_pair"][real])
-    hgu = bits_host(moe.ws_region(ns.ws, ns.shape, "hgu"))[real]
-    dhgu = f64_host(moe.ws_region(ns.ws, ns.shape, "dhgu"))[real]
-    check_bf16(dhgu, oracle.swiglu_bwd(hgu, dA), TOL, "dhgu (fused epilogue)")
-    check_token_grads(w, d, ns, np.arange(w.T), "(all tokens)")
+    check_row_links(w, d, ns, real, tag)
+    check_token_grads(w, d, ns, np.arange(w.T), tag)
 
 
 def test_backward_token_grads_edge_routing():
@@ -196,37 +166,40 @@ def test_backward_stages_match_oracle_and_fused():
     s = ns.shape
     t = tables(ns)
     real = np.nonzero(t["row_pair"] >= 0)[0]
-    dA, _, _ = oracle_rows(w, d, t["row_pair"][real])
+    dA, _, _, _ = oracle_rows(w, d, t["row_pair"][real])
+    wact_fused = moe.ws_region(ns.ws, s, "wact").clone(), moe.ws_region(ns.ws, s, "wact_lo").clone()
 
     dtw = torch.full_like(ns.dtw, float("nan"))
     moe.bwd_gemm2_dgrad(s, ns.dy, ns.wts, ns.W2p, ns.ws, fuse_swiglu_bwd=False, dtopk_w=dtw)
     torch.cuda.synchronize()
     assert torch.equal(dtw, ns.dtw), "d(topk_w) does not depend on the SwiGLU-transpose path"
-    dact = moe.ws_region(ns.ws, s, "dact")
-    check_bf16(f64_host(dact)[real], dA, TOL, "dact (L2 dgrad)")
+    assert torch.equal(moe.ws_region(ns.ws, s, "wact"), wact_fused[0])
+    assert torch.equal(moe.ws_region(ns.ws, s, "wact_lo"), wact_fused[1])
+    dact = ws_f64(ns, "dact")
+    check_f32(dact[real], dA, TOL, "dact (L2 dgrad)")
     pad = np.setdiff1d(np.arange(t["num_rows"]), real)
-    assert np.all(f64_host(dact)[pad] == 0.0)
+    assert np.all(dact[pad] == 0.0)
 
     moe.swiglu_bwd(s, ns.ws)
     torch.cuda.synchronize()
-    hgu = bits_host(moe.ws_region(ns.ws, s, "hgu"))
-    dhgu = f64_host(moe.ws_region(ns.ws, s, "dhgu"))
-    ref_local = oracle.swiglu_bwd(hgu[real], f64_host(dact)[real])
-    check_bf16(dhgu[real], ref_local, TOL, "swiglu_bwd (standalone)")
-    assert np.all(dhgu[pad] == 0.0)
+    hgu = ws_f64(ns, "hgu")
+    ref_local = oracle.swiglu_bwd(hgu[real], dact[real])
+    check_bf16(ws_f64(ns, "dhgu")[real], ref_local, TOL, "swiglu_bwd (standalone)")
+    check_f32(ws_f64(ns, "dhgu")[real] + ws_f64(ns, "dhgu_lo")[real], ref_local, TOL,
+              "swiglu_bwd (standalone, hi+lo)")
+    assert np.all(ws_f64(ns, "dhgu")[pad] == 0.0)
 
     dW1p = torch.empty_like(ns.dW1p)
     dW2p = torch.empty_like(ns.dW2p)
-    moe.wgrad2(s, ns.dy, ns.wts, ns.ws, dW2p)
+    moe.wgrad2(s, ns.dy, ns.ws, dW2p)
     moe.wgrad1(s, ns.x, ns.ws, dW1p)
     torch.cuda.synchronize()
     assert torch.equal(dW2p, ns.dW2p), "dW2 does not depend on the SwiGLU-transpose path"
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
-    S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
     g1, g2 = unpacked(ns, dW1p, dW2p)
-    check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1 (staged)")
-    check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2 (staged)")
+    check_bf16(g1, dW1, TOL, "dW1 (staged)")
+    check_bf16(g2, dW2, TOL, "dW2 (staged)")
 
     # L1 dgrad + combine on the standalone SwiGLU transpose's dhgu
     ns.dx = torch.full_like(ns.dx, float("nan"))
@@ -246,21 +219,17 @@ def test_backward_full_size_sampled_experts():
     experts = sorted({int(np.argmin(counts)), int(np.argmax(counts)), w.EL // 2})
     args = (d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], d["dy"])
     dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo, experts=experts)
-    S1, S2 = term_sums(w, d, experts, pairs_of_expert(t))
     g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
     for i, e in enumerate(experts):
-        check_sum_bound(g1[e], dW1[i], S1[i], C_DW1, TOL, "dW1[%d] (%d rows)" % (e, counts[e]))
-        check_sum_bound(g2[e], dW2[i], S2[i], C_DW2, TOL, "dW2[%d] (%d rows)" % (e, counts[e]))
+        check_bf16(g1[e], dW1[i], TOL, "dW1[%d] (%d rows, %s)" % (e, counts[e], w.name))
+        check_bf16(g2[e], dW2[i], TOL, "dW2[%d] (%d rows, %s)" % (e, counts[e], w.name))
     rng = np.random.default_rng(4)
     real = np.nonzero(t["row_pair"] >= 0)[0]
-    rows = rng.choice(real, size=24, replace=False)
-    dA, _, _ = oracle_rows(w, d, t["row_pair"][rows])
-    hgu = bits_host(moe.ws_region(ns.ws, ns.shape, "hgu"))[rows]
-    check_bf16(f64_host(moe.ws_region(ns.ws, ns.shape, "dhgu"))[rows], oracle.swiglu_bwd(hgu, dA), TOL,
-               "dhgu rows")
+    rows = np.sort(rng.choice(real, size=24, replace=False))
+    check_row_links(w, d, ns, rows, "(sampled rows, %s)" % w.name)
     from gpu_helpers import sample_tokens
     tokens = sample_tokens(t["tok_nloc"], 18, seed=5)
-    check_token_grads(w, d, ns, tokens, "(sampled tokens)")
+    check_token_grads(w, d, ns, tokens, "(sampled tokens, %s)" % w.name)
 
 
 @pytest.mark.parametrize("case", ["empty_batch", "none_local", "one_expert_takes_all"])
@@ -298,11 +267,8 @@ def test_degenerate_routing_forward_and_backward(case):
         check_token_grads(w, d, ns, np.arange(w.T), "(%s)" % case)
         args = (d["x"], idx, d["topk_weights"], d["W1"], d["W2"], d["dy"])
         dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
-        S1, S2 = term_sums(w, d, list(range(w.EL)), pairs_of_expert(t))
-        check_sum_bound(g1, dW1, S1, C_DW1, TOL, "dW1 (%s)" % case)
-        check_sum_bound(g2, dW2, S2, C_DW2, TOL, "dW2 (%s)" % case)
-
-
+        check_bf16(g1, dW1, TOL, "dW1 (%s)" % case)
+        check_bf16(g2, dW2, TOL, "dW2 (%s)" % case)
 def test_backward_is_graph_capturable():
     """The fused backward (dgrad with d(topk_w), dW2, dW1, dx) captured into a HIP graph replays
     bit-identically to the eager call, with eager work and a stale workspace between replays."""
@@ -355,8 +321,7 @@ def test_max_local_experts_forward_and_backward():
     experts = [0, 5, w.EL - 2, w.EL - 1]
     dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo, experts=experts)
     g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
-    S1, S2 = term_sums(w, d, experts, pairs_of_expert(t))
     for i, e in enumerate(experts):
-        check_sum_bound(g1[e], dW1[i], S1[i], C_DW1, TOL, "dW1[%d] (EL = 1024)" % e)
-        check_sum_bound(g2[e], dW2[i], S2[i], C_DW2, TOL, "dW2[%d] (EL = 1024)" % e)
+        check_bf16(g1[e], dW1[i], TOL, "dW1[%d] (EL = 1024)" % e)
+        check_bf16(g2[e], dW2[i], TOL, "dW2[%d] (EL = 1024)" % e)
     check_token_grads(w, d, ns, np.arange(w.T), "(EL = 1024)")

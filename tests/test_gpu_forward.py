@@ -14,8 +14,8 @@ import torch
 import moe_workloads as mw
 import oracle
 import token_dispatch_grouped_route_amd as moe
-from gpu_helpers import (assert_tables_equal, bits_host, check_bf16, check_sum_bound, f64_host,
-                         layer, sample_tokens, tables)
+from gpu_helpers import (assert_tables_equal, bits_host, check_bf16, check_f32, f64_host, layer,
+                         sample_tokens, tables)
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -116,7 +116,7 @@ def test_forward_reduced_full_compare(w, bm):
     ref = oracle.forward(d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], E=w.E, e_lo=w.e_lo)
     got = f64_host(ns.y)
     assert np.all(np.isfinite(got))
-    check_bf16(got, ref, TOL)
+    check_bf16(got, ref, TOL, "y (%s, bm %d)" % (w.name, bm))
     nloc = tables(ns)["tok_nloc"]
     assert np.all(got[nloc == 0] == 0.0)
 
@@ -129,7 +129,7 @@ def test_forward_tiny_workload_full_compare():
         moe.forward(ns.shape, ns.x, ns.idx, ns.wts, ns.W1p, ns.W2p, ns.ws, ns.y)
         torch.cuda.synchronize()
         ref = oracle.forward(d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], E=w.E)
-        check_bf16(f64_host(ns.y), ref, TOL)
+        check_bf16(f64_host(ns.y), ref, TOL, "y (%s, bm %d)" % (w.name, bm))
 
 
 def packed_reference(W, I=None):
@@ -163,7 +163,7 @@ def test_pack_weights_follows_the_documented_layout(w):
 
 
 def test_stages_match_oracle_and_fused_forward():
-    """prologue -> dispatch_gemm1 (pre-activation and SwiGLU outputs) -> standalone SwiGLU ->
+    """prologue -> dispatch_gemm1 (fp32 pre-activation and SwiGLU outputs) -> standalone SwiGLU ->
     gemm2_combine, each compared with the oracle; staging the fused-SwiGLU output through
     gemm2_combine reproduces the fused forward's y bit for bit."""
     w = REDUCED[0]
@@ -172,7 +172,7 @@ def test_stages_match_oracle_and_fused_forward():
     ns = layer(w, d, bm)
     s = ns.shape
     R = moe.workspace_layout(s)["rows_capacity"]
-    hgu = torch.zeros(R, 2 * w.I, dtype=torch.bfloat16, device="cuda")
+    hgu = torch.zeros(R, 2 * w.I, dtype=torch.float32, device="cuda")
     act = torch.zeros(R, w.I, dtype=torch.bfloat16, device="cuda")
     act2 = torch.zeros(R, w.I, dtype=torch.bfloat16, device="cuda")
     moe.route_prologue(s, ns.idx, ns.ws)
@@ -190,30 +190,17 @@ def test_stages_match_oracle_and_fused_forward():
     real = np.nonzero(t["row_pair"] >= 0)[0]
     pairs = t["row_pair"][real]
     h_ref, a_ref = oracle.l1_rows(d["x"], d["topk_idx"], d["W1"], w.E, w.e_lo, pairs)
-    check_bf16(f64_host(hgu)[real], h_ref, TOL)
-    check_bf16(f64_host(act)[real], a_ref, TOL)
-    # the standalone SwiGLU on the GPU's own bf16 pre-activations
-    hb = bits_host(hgu)[:t["num_rows"]]
-    check_bf16(f64_host(act2)[:t["num_rows"]], oracle.swiglu(hb), TOL)
+    check_f32(f64_host(hgu)[real], h_ref, TOL, "hgu (L1, fp32)")
+    check_bf16(f64_host(act)[real], a_ref, TOL, "act (fused SwiGLU)")
+    # the standalone SwiGLU on the GPU's own fp32 pre-activations
+    hv = f64_host(hgu)[:t["num_rows"]]
+    check_bf16(f64_host(act2)[:t["num_rows"]], oracle.swiglu(hv), TOL, "act (standalone SwiGLU)")
     # padding rows inside segments carry zeros
     pad = np.setdiff1d(np.arange(t["num_rows"]), real)
-    assert np.all(f64_host(act)[pad] == 0.0)
+    assert np.all(f64_host(act)[pad] == 0.0) and np.all(f64_host(hgu)[pad] == 0.0)
     ref = oracle.forward(d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], E=w.E, e_lo=w.e_lo)
     check_bf16(f64_host(ns.y), ref, TOL, "y (fused)")
-    # the staged path feeds L2 with SwiGLU of the bf16 pre-activation: its act operand carries two
-    # bf16 roundings, so y gets the dot-product bound with c = 2 (sum|terms| = sum_j |w_j| |a_j| @ |W2_e|)
-    check_sum_bound(f64_host(y_staged), ref, forward_term_sums(w, d, a_ref, pairs), 2.0, TOL, "y (staged)")
-
-
-def forward_term_sums(w, d, a_rows, pairs):
-    """sum over a token's local pairs of |w_j| * (|a_j| @ |W2[e_j]|): the absolute terms of y."""
-    W2 = np.abs(mw.bf16_bits_to_f32(d["W2"]).astype(np.float64))
-    S = np.zeros((w.T, w.H))
-    ids = d["topk_idx"].reshape(-1)
-    wts = np.abs(d["topk_weights"].reshape(-1).astype(np.float64))
-    for a, p in zip(a_rows, pairs):
-        S[p // w.k] += wts[p] * (np.abs(a) @ W2[ids[p] - w.e_lo])
-    return S
+    check_bf16(f64_host(y_staged), ref, TOL, "y (staged)")
 
 
 def test_forward_is_deterministic_and_graph_capturable():
@@ -261,7 +248,7 @@ def test_dropped_ids_are_counted_and_ignored():
     t = tables(ns)
     assert t["dropped"] == int(np.sum((idx < 0) | (idx >= w.E)))
     ref = oracle.forward(d["x"], idx, d["topk_weights"], d["W1"], d["W2"], E=w.E, e_lo=w.e_lo)
-    check_bf16(f64_host(ns.y), ref, TOL)
+    check_bf16(f64_host(ns.y), ref, TOL, "y (dropped ids)")
 
 
 def test_errors_are_reported_before_launch():
@@ -306,4 +293,4 @@ def test_forward_full_size_sampled(cfg):
     tok = sample_tokens(t["tok_nloc"], 48, seed=cfg)
     ref = oracle.forward(d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], E=w.E, e_lo=w.e_lo,
                          tokens=tok)
-    check_bf16(y[tok], ref, TOL)
+    check_bf16(y[tok], ref, TOL, "y (%s, bm %d, %d sampled tokens)" % (w.name, bm, len(tok)))

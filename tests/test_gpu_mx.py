@@ -8,7 +8,7 @@ import torch
 import moe_workloads as mw
 import oracle
 import token_dispatch_grouped_route_amd as moe
-from gpu_helpers import bf16_dev, check_bf16, f64_host, rel_max_err
+from gpu_helpers import RECORDS, bf16_dev, bf16_half_ulp, check_bf16, f64_host, rel_max_err
 
 pytestmark = pytest.mark.gpu
 FP8, FP4 = oracle.MX_FP8, oracle.MX_FP4
@@ -140,11 +140,12 @@ def fp8_half_step(v, scale_codes):
     return 0.5 * np.exp2(e - 3) * sc
 
 
-# Accuracy of one gfx950 scaled MFMA (32x32x64, FP8 x FP4): the result differs from the exact
-# C + sum of its 64 products by up to EPS_MMA * (sum |products| + |C|), measured over 5e5 random
-# results with a spread of block scales (largest 4096 u, mean about 260 u).  The K loop chains the
-# instructions through C, so a dot product of K terms errs by up to
-# EPS_MMA * sum over 64-deep steps s of (S_s + |C_s|), C_s being the partial sum before step s.
+# Accuracy of the gfx950 scaled MFMA (32x32x64, FP8 x FP4): one instruction's result differs from
+# the exact C + sum of its 64 products by up to EPS_MMA * (sum |products| + |C|); the instruction
+# sums well below fp32 precision.  The K loop chains the instructions through C, so a dot product
+# of K terms errs by up to EPS_MMA * sum over 64-deep steps s of (S_s + |C_s|), C_s being the
+# partial sum before step s.  test_mx_chained_mfma_error_within_eps_mma measures the constant on
+# the product path (the MX L2 GEMM's fp32 results) and checks that it holds.
 EPS_MMA = 2.0 ** -12
 
 
@@ -215,6 +216,55 @@ def check_l2_link(w, d, ref_codes, y, tokens, pair_row, gc, gs):
     return check_bf16(y[tokens], ref, 2e-2, "y (MX, on the GPU's act)")
 
 
+def check_end_to_end(w, d, ref_codes, y, tokens, pair_row, gc, gs, clamp=10.0, what=""):
+    """End to end: y of the given tokens against the oracle's own MX forward (its activation codes
+    decided on exact L1 values).  The GPU decides each activation code on a value its matrix core
+    computed within the chained bound above, so a code next to a rounding boundary may land one FP8
+    step away from the oracle's (check_act_link admits only such flips; a block scale may flip only
+    at a boundary 448 * 2**E).  Each element of y may therefore also differ by the effect of the
+    flipped codes of its token's rows: one FP8 step at the code times |w_j| * |W2[e_j][i, m]|, summed
+    over the flipped codes i.  The bar is the forward's (2e-2 * rms beyond y's own rounding to bf16)
+    plus that flip allowance, per element."""
+    xc, xs, w1c, w1s, w2c, w2s = ref_codes
+    ref = oracle.forward_mx(xc, xs, d["topk_idx"], d["topk_weights"], w1c, w1s, w2c, w2s, E=w.E, e_lo=w.e_lo,
+                            clamp=clamp, tokens=tokens)
+    allow = np.zeros((len(tokens), w.H))
+    w2_cache = {}
+    nflip = 0
+    for j in range(w.k):
+        p = tokens * w.k + j
+        r = pair_row[p]
+        sel = np.nonzero(r >= 0)[0]
+        if len(sel) == 0:
+            continue
+        a = oracle.mx_l1_rows(xc, xs, d["topk_idx"], w1c, w1s, w.E, w.e_lo, p[sel], clamp)
+        rc, rs = oracle.mx_quantize(FP8, a)
+        g_c, g_s = gc[r[sel]], gs[r[sel]]
+        flip = (g_c != rc) | np.repeat(g_s != rs, 32, axis=1)
+        if not flip.any():
+            continue
+        ga, ra = oracle.mx_dequantize(FP8, g_c, g_s), oracle.mx_dequantize(FP8, rc, rs)
+        step = 2.0 * np.maximum(fp8_half_step(ga, g_s), fp8_half_step(ra, rs))
+        assert np.all(np.abs(ga - ra)[flip] <= step[flip]), "a flipped activation moved by more than one FP8 step"
+        nflip += int(flip.sum())
+        for n in np.nonzero(flip.any(axis=1))[0]:
+            e = int(d["topk_idx"][tokens[sel[n]], j]) - w.e_lo
+            if e not in w2_cache:
+                w2_cache[e] = np.abs(oracle.mx_dequantize(FP4, w2c[e], w2s[e]))   # [H, I]
+            cols = np.nonzero(flip[n])[0]
+            wj = abs(float(d["topk_weights"][tokens[sel[n]], j]))
+            allow[sel[n]] += wj * (w2_cache[e][:, cols] @ step[n, cols])
+    rms = np.sqrt(np.mean(ref * ref))
+    own = bf16_half_ulp(np.maximum(np.abs(y[tokens]), np.abs(ref)))
+    diff = np.abs(y[tokens] - ref)
+    beyond = max(float(np.max(diff - own - allow)), 0.0) / rms if diff.size else 0.0
+    raw = rel_max_err(y[tokens], ref)
+    print("[parity] y (MX end to end%s): %d flipped codes, error beyond rounding and flips %.3e, raw "
+          "max|err|/rms %.3e" % (what, nflip, beyond, raw))
+    RECORDS.append(("y (MX end to end%s)" % what, beyond, raw))
+    assert beyond <= 2e-2, "MX y differs from the oracle beyond rounding and flips by %.3g of rms" % beyond
+
+
 def run_mx_forward(w, d, bm, x_scale=1.0, clamp=10.0, experts=None):
     s, args, ref_codes = mx_layer(w, d, bm, x_scale, experts)
     moe.forward_mx(s, *args, clamp=clamp)
@@ -236,8 +286,7 @@ def test_mx_forward_reduced_link_by_link(w, bm):
     check_act_link(w, d, ref_codes, row_pair[rows], gc[rows], gs[rows])
     check_l2_link(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs)
     assert np.all(y[~local.any(axis=1)] == 0.0)
-    full = oracle.forward_mx(*ref_codes[:2], d["topk_idx"], d["topk_weights"], *ref_codes[2:], E=w.E, e_lo=w.e_lo)
-    print("[parity] y (MX) against the oracle end to end: raw max|err|/rms %.3e" % rel_max_err(y, full))
+    check_end_to_end(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs, what=", %s, bm %d" % (w.name, bm))
 
 
 def test_mx_forward_clamp_active():
@@ -247,6 +296,7 @@ def test_mx_forward_clamp_active():
     rows = np.nonzero(row_pair >= 0)[0]
     check_act_link(w, d, ref_codes, row_pair[rows], gc[rows], gs[rows], clamp=10.0)
     check_l2_link(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs)
+    check_end_to_end(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs, clamp=10.0, what=", clamp active")
     xc, xs, w1c, w1s = ref_codes[:4]
     a10 = oracle.mx_l1_rows(xc, xs, d["topk_idx"], w1c, w1s, w.E, w.e_lo, row_pair[rows], 10.0)
     a0 = oracle.mx_l1_rows(xc, xs, d["topk_idx"], w1c, w1s, w.E, w.e_lo, row_pair[rows], 0.0)
@@ -275,6 +325,43 @@ def test_mx_forward_full_size_sampled():
     check_act_link(w, d, ref_codes, pairs, gc[r], gs[r])
     print("[mx full] act link done", flush=True)
     check_l2_link(w, d, ref_codes, y, tok, pair_row, gc, gs)
+    check_end_to_end(w, d, ref_codes, y, tok, pair_row, gc, gs, what=", %s, sampled tokens" % w.name)
+
+
+def test_mx_chained_mfma_error_within_eps_mma():
+    """EPS_MMA pinned on the product path.  With every token holding 4 local pairs, the MX L2 GEMM's
+    combine stages every row's fp32 result times the routing weight in ws stage; divided by the
+    weight, that is the chained scaled-MFMA dot product of the GPU's own FP8 activation row with the
+    FP4 W2 column (K = I, 64-deep steps).  Against the exact fp64 value (the oracle's L2 row on the
+    same codes) the error must stay within EPS_MMA * sum over steps of (S_s + |C_s|), plus a few fp32
+    ulps for the weight's multiply and divide.  The largest error / that sum (the effective
+    per-instruction unit) and the mean are printed."""
+    w = REDUCED[1]
+    d = mw.inputs(w, 25)
+    s, args, ref_codes = mx_layer(w, d, 64)
+    moe.forward_mx(s, *args)
+    torch.cuda.synchronize()
+    ws = args[8]
+    gc, gs, row_pair = gpu_act(ws, s, w)
+    stage = moe.ws_region(ws, s, "stage").cpu().numpy()
+    rows = np.nonzero(row_pair >= 0)[0][:192]
+    p = row_pair[rows]
+    wts = d["topk_weights"].reshape(-1)[p].astype(np.float64)
+    assert np.all(((d["topk_idx"] >= w.e_lo) & (d["topk_idx"] < w.e_lo + w.EL)).sum(axis=1) >= 2)
+    got = stage[rows].astype(np.float64) / wts[:, None]
+    e = (d["topk_idx"].reshape(-1)[p] - w.e_lo).astype(np.int32)
+    w2c, w2s = ref_codes[4:]
+    exact = oracle.mx_l2_rows(w2c, w2s, e, gc[rows], gs[rows])
+    a = oracle.mx_dequantize(FP8, gc[rows], gs[rows])
+    W2 = {int(x): oracle.mx_dequantize(FP4, w2c[x], w2s[x]) for x in np.unique(e)}   # [H, I]
+    unit = np.zeros_like(exact)
+    for n in range(len(rows)):
+        unit[n] = chained_mma_bound(np.broadcast_to(a[n], W2[int(e[n])].shape), W2[int(e[n])]) / EPS_MMA
+    err = np.abs(got - exact)
+    eff = err / np.maximum(unit, 1e-300)
+    print("[parity] chained scaled MFMA over %d dot products of K = %d: max error / sum_s(S_s + |C_s|) = "
+          "2^%.2f (mean 2^%.2f); EPS_MMA = 2^-12" % (err.size, w.I, np.log2(eff.max()), np.log2(eff.mean())))
+    assert np.all(err <= EPS_MMA * unit + 4 * U32 * np.abs(exact)), "the chained MFMA error exceeds EPS_MMA"
 
 
 def test_mx_stage_entry_points_match_the_fused_forward():
@@ -373,3 +460,4 @@ def test_mx_degenerate_routing(case):
         return
     check_act_link(w, d, ref_codes, row_pair[rows], gc[rows], gs[rows])
     check_l2_link(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs)
+    check_end_to_end(w, d, ref_codes, y, np.arange(w.T), pair_row, gc, gs, what=", " + case)

@@ -45,7 +45,7 @@ class Shape(ctypes.Structure):
 
 _LAYOUT_FIELDS = ("counts", "padded_offsets", "row_pair", "pair_row", "tile_expert", "tok_nloc",
                   "meta", "act", "stage", "hgu", "dact", "dhgu", "zeros", "scratch", "tile_sync",
-                  "dtw_part")
+                  "dtw_part", "dhgu_lo", "wact", "wact_lo")
 
 
 class WsLayout(ctypes.Structure):
@@ -78,7 +78,7 @@ def lib():
         L.moe_bwd_gemm2_dgrad.argtypes = [S, P, P, P, P, ctypes.c_size_t, i32, P, P]
         L.moe_swiglu_bwd.argtypes = [S, P, ctypes.c_size_t, P]
         L.moe_bwd_gemm1_dgrad_combine.argtypes = [S, P, P, ctypes.c_size_t, P, P]
-        L.moe_wgrad2.argtypes = [S, P, P, P, ctypes.c_size_t, P, P]
+        L.moe_wgrad2.argtypes = [S, P, P, ctypes.c_size_t, P, P]
         L.moe_wgrad1.argtypes = [S, P, P, ctypes.c_size_t, P, P]
         L.moe_backward.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P, P, P, P, P]
         L.moe_mx_cast_fp8.argtypes = [ctypes.c_int64, i32, P, P, P, P]
@@ -177,8 +177,9 @@ _REGION = {  # name -> (dtype, row width in elements or None)
     "counts": (torch.int32, None), "padded_offsets": (torch.int32, None),
     "row_pair": (torch.int32, None), "pair_row": (torch.int32, None),
     "tile_expert": (torch.int32, None), "tok_nloc": (torch.int32, None), "meta": (torch.int32, None),
-    "act": (torch.bfloat16, "I"), "stage": (torch.float32, "H"), "hgu": (torch.bfloat16, "2I"),
-    "dact": (torch.bfloat16, "I"), "dhgu": (torch.bfloat16, "2I"),
+    "act": (torch.bfloat16, "I"), "stage": (torch.float32, "H"), "hgu": (torch.float32, "2I"),
+    "dact": (torch.float32, "I"), "dhgu": (torch.bfloat16, "2I"), "dhgu_lo": (torch.bfloat16, "2I"),
+    "wact": (torch.bfloat16, "I"), "wact_lo": (torch.bfloat16, "I"),
     "dtw_part": (torch.float32, "I/128"),
 }
 
@@ -194,7 +195,7 @@ def ws_region(ws: torch.Tensor, shape: Shape, name: str) -> torch.Tensor:
     if width is None:
         n, view = sizes[name], None
     else:
-        if name in ("hgu", "dact", "dhgu", "dtw_part") and not shape.train:
+        if name in ("hgu", "dact", "dhgu", "dhgu_lo", "wact", "wact_lo", "dtw_part") and not shape.train:
             raise MoeError("region %s exists only for train shapes" % name)
         cols = {"I": shape.I, "H": shape.H, "2I": 2 * shape.I, "I/128": shape.I // 128}[width]
         n, view = R * cols, (R, cols)
@@ -244,14 +245,14 @@ def dispatch_gemm1(shape, x, w1p, ws, act_out=None, hgu_out=None, stream=None):
     _check(lib().moe_dispatch_gemm1(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x", nn["x"]),
                                     _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]), p, n,
                                     _ptr(act_out, torch.bfloat16, "act_out", nn["act_out"]),
-                                    _ptr(hgu_out, torch.bfloat16, "hgu_out", nn["hgu_out"]), _stream(stream)),
+                                    _ptr(hgu_out, torch.float32, "hgu_out", nn["hgu_out"]), _stream(stream)),
            "moe_dispatch_gemm1")
 
 
 def swiglu(shape, hgu, ws, act, stream=None):
     nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_swiglu(ctypes.byref(shape), _ptr(hgu, torch.bfloat16, "hgu", nn["hgu"]), p, n,
+    _check(lib().moe_swiglu(ctypes.byref(shape), _ptr(hgu, torch.float32, "hgu", nn["hgu"]), p, n,
                             _ptr(act, torch.bfloat16, "act", nn["act"]), _stream(stream)), "moe_swiglu")
 
 
@@ -294,12 +295,12 @@ def swiglu_bwd(shape, ws, stream=None):
     _check(lib().moe_swiglu_bwd(ctypes.byref(shape), p, n, _stream(stream)), "moe_swiglu_bwd")
 
 
-def wgrad2(shape, dy, topk_w, ws, dw2p, stream=None):
+def wgrad2(shape, dy, ws, dw2p, stream=None):
+    """dW2 from the weighted activation rows that bwd_gemm2_dgrad wrote into ws."""
     nn = _n(shape)
     p, n = _ws(ws)
-    _check(lib().moe_wgrad2(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy", nn["dy"]),
-                            _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]), p, n, _ptr(dw2p, torch.bfloat16, "dw2p", nn["dw2p"]),
-                            _stream(stream)), "moe_wgrad2")
+    _check(lib().moe_wgrad2(ctypes.byref(shape), _ptr(dy, torch.bfloat16, "dy", nn["dy"]), p, n,
+                            _ptr(dw2p, torch.bfloat16, "dw2p", nn["dw2p"]), _stream(stream)), "moe_wgrad2")
 
 
 def wgrad1(shape, x, ws, dw1p, stream=None):

@@ -61,9 +61,12 @@ int32_t layout_of(const moe_shape* s, moe_ws_layout* L) {
     L->act = take(2 * static_cast<size_t>(R) * I);
     L->stage = take(4 * static_cast<size_t>(R) * H);
     if (s->train) {
-        L->hgu = take(2 * static_cast<size_t>(R) * 2 * I);
-        L->dact = take(2 * static_cast<size_t>(R) * I);
+        L->hgu = take(4 * static_cast<size_t>(R) * 2 * I);
+        L->dact = take(4 * static_cast<size_t>(R) * I);
         L->dhgu = take(2 * static_cast<size_t>(R) * 2 * I);
+        L->dhgu_lo = take(2 * static_cast<size_t>(R) * 2 * I);
+        L->wact = take(2 * static_cast<size_t>(R) * I);
+        L->wact_lo = take(2 * static_cast<size_t>(R) * I);
     }
     L->zeros = take(2 * (H > 2 * I ? H : 2 * I));
     L->tile_sync = take(4 * static_cast<size_t>(kMaxGrid));
@@ -107,9 +110,12 @@ int32_t prepare(const moe_shape* s, const void* ws, size_t ws_bytes, bool need_t
     w->meta = reinterpret_cast<int32_t*>(b + L->meta);
     w->act = reinterpret_cast<uint16_t*>(b + L->act);
     w->stage = reinterpret_cast<float*>(b + L->stage);
-    w->hgu = s->train ? reinterpret_cast<uint16_t*>(b + L->hgu) : nullptr;
-    w->dact = s->train ? reinterpret_cast<uint16_t*>(b + L->dact) : nullptr;
+    w->hgu = s->train ? reinterpret_cast<float*>(b + L->hgu) : nullptr;
+    w->dact = s->train ? reinterpret_cast<float*>(b + L->dact) : nullptr;
     w->dhgu = s->train ? reinterpret_cast<uint16_t*>(b + L->dhgu) : nullptr;
+    w->dhgu_lo = s->train ? reinterpret_cast<uint16_t*>(b + L->dhgu_lo) : nullptr;
+    w->wact = s->train ? reinterpret_cast<uint16_t*>(b + L->wact) : nullptr;
+    w->wact_lo = s->train ? reinterpret_cast<uint16_t*>(b + L->wact_lo) : nullptr;
     w->dtw_part = s->train ? reinterpret_cast<float*>(b + L->dtw_part) : nullptr;
     w->dtw_cols = s->I / 128;
     const int64_t pairs = static_cast<int64_t>(s->T) * s->k;
@@ -202,7 +208,7 @@ int32_t moe_route_prologue(const moe_shape* shape, const int32_t* topk_idx, void
 }
 
 int32_t moe_dispatch_gemm1(const moe_shape* shape, const uint16_t* x, const uint16_t* w1p, void* ws,
-                           size_t ws_bytes, uint16_t* act_out, uint16_t* hgu_out, void* stream) {
+                           size_t ws_bytes, uint16_t* act_out, float* hgu_out, void* stream) {
     Dims d;
     Ws w;
     moe_ws_layout L;
@@ -213,7 +219,7 @@ int32_t moe_dispatch_gemm1(const moe_shape* shape, const uint16_t* x, const uint
     return launched(launch_gemm1(d, x, w1p, w, act_out, hgu_out, static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_swiglu(const moe_shape* shape, const uint16_t* hgu, const void* ws, size_t ws_bytes, uint16_t* act,
+int32_t moe_swiglu(const moe_shape* shape, const float* hgu, const void* ws, size_t ws_bytes, uint16_t* act,
                    void* stream) {
     Dims d;
     Ws w;
@@ -296,16 +302,16 @@ int32_t moe_swiglu_bwd(const moe_shape* shape, void* ws, size_t ws_bytes, void* 
     return launched(launch_swiglu_bwd(d, w, static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, const float* topk_w, void* ws, size_t ws_bytes,
-                   uint16_t* dw2p, void* stream) {
+int32_t moe_wgrad2(const moe_shape* shape, const uint16_t* dy, void* ws, size_t ws_bytes, uint16_t* dw2p,
+                   void* stream) {
     Dims d;
     Ws w;
     moe_ws_layout L;
     int32_t st = prepare(shape, ws, ws_bytes, true, &d, &w, &L);
     if (st != MOE_OK) return st;
-    if (!dw2p || ((!dy || !topk_w) && shape->T > 0)) return MOE_ERR_NULL;
-    if (!aligned16(dy) || !aligned4(topk_w) || !aligned16(dw2p)) return MOE_ERR_ALIGN;
-    return launched(launch_wgrad2(d, dy, topk_w, w, dw2p, static_cast<hipStream_t>(stream)));
+    if (!dw2p || (!dy && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(dy) || !aligned16(dw2p)) return MOE_ERR_ALIGN;
+    return launched(launch_wgrad2(d, dy, w, dw2p, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_wgrad1(const moe_shape* shape, const uint16_t* x, void* ws, size_t ws_bytes, uint16_t* dw1p,
@@ -336,7 +342,7 @@ int32_t moe_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_dgrad(d, dy, topk_w, w2p, w, 1, dtopk_w != nullptr, s);
     if (e == hipSuccess && dtopk_w) e = launch_dtopk_w_finish(d, w, dtopk_w, s);
-    if (e == hipSuccess) e = launch_wgrad2(d, dy, topk_w, w, dw2p, s);
+    if (e == hipSuccess) e = launch_wgrad2(d, dy, w, dw2p, s);
     if (e == hipSuccess) e = launch_wgrad1(d, x, w, dw1p, s);
     if (e == hipSuccess && dx) e = launch_dgrad1(d, w1p, w, dx, s);
     return launched(e);

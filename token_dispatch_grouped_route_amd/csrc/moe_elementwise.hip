@@ -114,7 +114,29 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
 
 constexpr int kEwThreads = 256;
 
-__global__ __launch_bounds__(kEwThreads) void swiglu_kernel(const uint16_t* __restrict__ hgu, Dims d, Ws ws,
+// 8 consecutive fp32 values (two 16-byte loads)
+__device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+// 8 values as bf16 hi parts and lo parts (split_bf16), one 16-byte store each
+__device__ __forceinline__ void store_split8(uint16_t* hi, uint16_t* lo, const float (&f)[8]) {
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16(f[i], h[i], l[i]);
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wh[i] = h[2 * i] | (static_cast<uint32_t>(h[2 * i + 1]) << 16);
+        wl[i] = l[2 * i] | (static_cast<uint32_t>(l[2 * i + 1]) << 16);
+    }
+    *reinterpret_cast<uint4*>(hi) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    *reinterpret_cast<uint4*>(lo) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+}
+
+// act = silu(g) * u over fp32 [gate | up] rows (the forward's SwiGLU, on the saved pre-activation).
+__global__ __launch_bounds__(kEwThreads) void swiglu_kernel(const float* __restrict__ hgu, Dims d, Ws ws,
                                                             uint16_t* __restrict__ act) {
     const int64_t R = ws.meta[0];
     const int v8 = d.I / 8;
@@ -124,14 +146,15 @@ __global__ __launch_bounds__(kEwThreads) void swiglu_kernel(const uint16_t* __re
         const int64_t r = q / v8;
         const int c = static_cast<int>(q - r * v8) * 8;
         float g[8], u[8], a[8];
-        unpack8(*reinterpret_cast<const uint4*>(hgu + r * 2 * d.I + c), g);
-        unpack8(*reinterpret_cast<const uint4*>(hgu + r * 2 * d.I + d.I + c), u);
+        load8(hgu + r * 2 * d.I + c, g);
+        load8(hgu + r * 2 * d.I + d.I + c, u);
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[i] = silu_f32(g[i]) * u[i];
         *reinterpret_cast<uint4*>(act + r * d.I + c) = pack8(a);
     }
 }
 
+// SwiGLU transpose from fp32 dact and the fp32 pre-activation; dhgu as hi and lo bf16 rows.
 __global__ __launch_bounds__(kEwThreads) void swiglu_bwd_kernel(Dims d, Ws ws) {
     const int64_t R = ws.meta[0];
     const int v8 = d.I / 8;
@@ -141,17 +164,17 @@ __global__ __launch_bounds__(kEwThreads) void swiglu_bwd_kernel(Dims d, Ws ws) {
         const int64_t r = q / v8;
         const int c = static_cast<int>(q - r * v8) * 8;
         float g[8], u[8], da[8], dg[8], du[8];
-        unpack8(*reinterpret_cast<const uint4*>(ws.hgu + r * 2 * d.I + c), g);
-        unpack8(*reinterpret_cast<const uint4*>(ws.hgu + r * 2 * d.I + d.I + c), u);
-        unpack8(*reinterpret_cast<const uint4*>(ws.dact + r * d.I + c), da);
+        load8(ws.hgu + r * 2 * d.I + c, g);
+        load8(ws.hgu + r * 2 * d.I + d.I + c, u);
+        load8(ws.dact + r * d.I + c, da);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float sg = 1.0f / (1.0f + __expf(-g[i]));
             dg[i] = da[i] * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
             du[i] = da[i] * g[i] * sg;
         }
-        *reinterpret_cast<uint4*>(ws.dhgu + r * 2 * d.I + c) = pack8(dg);
-        *reinterpret_cast<uint4*>(ws.dhgu + r * 2 * d.I + d.I + c) = pack8(du);
+        store_split8(ws.dhgu + r * 2 * d.I + c, ws.dhgu_lo + r * 2 * d.I + c, dg);
+        store_split8(ws.dhgu + r * 2 * d.I + d.I + c, ws.dhgu_lo + r * 2 * d.I + d.I + c, du);
     }
 }
 
@@ -161,7 +184,7 @@ static int ew_grid(int64_t rows_cap, int per_row_vectors) {
     return static_cast<int>(want < 1 ? 1 : (want > cap ? cap : want));
 }
 
-hipError_t launch_swiglu(const Dims& d, const uint16_t* hgu, const Ws& ws, uint16_t* act, hipStream_t s) {
+hipError_t launch_swiglu(const Dims& d, const float* hgu, const Ws& ws, uint16_t* act, hipStream_t s) {
     swiglu_kernel<<<ew_grid(ws.rows_cap, d.I / 8), kEwThreads, 0, s>>>(hgu, d, ws, act);
     return hipGetLastError();
 }

@@ -19,11 +19,21 @@
 //          LDS store.
 //
 // Kernels ("Mega MoE" page, Pipeline, backward):
-//   dgrad   L2 dgrad NN, row weight and optional SwiGLU transpose in the epilogue; optionally
-//           the per-row partials of d(topk_w) = <dy[t], o_p> = <dy[t] W2^T, act_p>
+//   dgrad   L2 dgrad NN, row weight and optional SwiGLU transpose in the epilogue, which also
+//           writes the weighted activation rows w * act for dW2; optionally the per-row
+//           partials of d(topk_w) = <dy[t], o_p> = <dy[t] W2^T, act_p>
 //   dgrad1  L1 dgrad NN over the packed W1, rows summed back to token order (the combine)
-//   wgrad2  dW2 = dO^T A, K = rows of the expert (variable K), TN
+//   wgrad2  dW2 = (w act)^T dy, K = rows of the expert (variable K), TN
 //   wgrad1  dW1 = dHgu^T X with X re-gathered from x, TN
+//
+// Precision of the intermediate operands.  The saved pre-activation is fp32, so the row gradients
+// (dHgu) and the weighted activation (w * act) are formed in fp32 and stored as two bf16 arrays,
+// hi = bf16(v) and lo = bf16(v - hi), which together carry about 16 significant bits.  The weight
+// gradients of experts with few rows sum few products, so one bf16 rounding of an operand shows in
+// their largest elements; their streamed operand is that split pair, multiplied by the other
+// operand twice (hi, then lo) into the same accumulators.  x and dy enter unrounded (they are
+// bf16 inputs), and the routing weight rides on the activation, so dW1 and dW2 carry only the
+// fp32 accumulation and the output rounding.
 // Weight gradients are written in the packed layout of the weights they belong to, whole 1 KB
 // blocks per store instruction (the tile's M index runs along the packed reduction index).
 //
@@ -98,20 +108,9 @@ struct KRows {
     }
 };
 
-__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float s) {
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(v[i] << 16) * s;
-        const float hi = __uint_as_float(v[i] & 0xffff0000u) * s;
-        r[i] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-    }
-    return r;
-}
-
 // Operand tile of ROWS rows (the M or N index) x BK, stored in memory with the tile's index
 // contiguous in runs of 8: elements (m .. m+7, k) = Src::chunk(k, m_base + m) for m a multiple of
-// 8 (times Src::scale(k)).  Every chunk is a valid address (absent rows point at the workspace's
+// 8.  Every chunk is a valid address (absent rows point at the workspace's
 // zero row), so the loads carry no branch and the compiler's wait counts stay exact: a load under
 // a branch makes it wait for every load in flight before the next one.
 // Unit u moves K rows 4*kq..4*kq+3 of the 16-byte column mc; kq varies fastest across lanes so
@@ -137,10 +136,6 @@ struct TRows {
                 for (int r = 0; r < 4; ++r) p[r] = src.chunk(kt * BK + 4 * kq + r, m_base + 8 * mc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[S][i][r] = *reinterpret_cast<const u32x4*>(p[r]);
-                if constexpr (Src::kScaled) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[S][i][r] = scale_bf16x8(v[S][i][r], src.scale(kt * BK + 4 * kq + r));
-                }
             }
         }
     }
@@ -194,6 +189,42 @@ __device__ __forceinline__ void mma_step(const char* lA, const char* lB, f32x16_
 #pragma unroll
             for (int j = 0; j < C::NI; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// mma_step with one operand given as hi + lo bf16 tiles (the lo tile at lX, laid out like the
+// operand it completes): acc += A * B + X * B (SPLIT_A) or A * B + A * X.
+template <class C, bool SPLIT_A>
+__device__ __forceinline__ void mma_step_split(const char* lA, const char* lB, const char* lX,
+                                               f32x16_t (&acc)[C::MI][C::NI], int wm0, int wn0, int lane) {
+    constexpr int KS = BK / 16;
+    constexpr int NX = SPLIT_A ? C::MI : C::NI;
+    bf16x8_t a[2][C::MI], b[2][C::NI], x[2][NX];
+    auto read_x = [&](bf16x8_t (&xv)[NX], int s) {
+        const int ch = 2 * s + (lane >> 5);
+        const int w0 = SPLIT_A ? wm0 : wn0;
+#pragma unroll
+        for (int i = 0; i < NX; ++i)
+            xv[i] = *reinterpret_cast<const bf16x8_t*>(lX + lds_off(w0 + i * 32 + (lane & 31), ch));
+    };
+    read_frags<C>(lA, lB, a[0], b[0], 0, wm0, wn0, lane);
+    read_x(x[0], 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+            read_frags<C>(lA, lB, a[(s + 1) & 1], b[(s + 1) & 1], s + 1, wm0, wn0, lane);
+            read_x(x[(s + 1) & 1], s + 1);
+        }
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+                if constexpr (SPLIT_A)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], x[s & 1][j], acc[i][j], 0, 0, 0);
+            }
     }
 }
 
@@ -330,19 +361,18 @@ __device__ __forceinline__ void tile_at(const Ws& ws, const Dims& d, int n_tiles
 // dgrad: L2 dgrad (NN) with the row weight and optional SwiGLU transpose in the epilogue
 // ---------------------------------------------------------------------------------------------
 struct W2ColSrc {   // B operand of the dgrad: (K = h, N = i) of expert e's packed W2
-    static constexpr bool kScaled = false;
     const uint16_t* base;   // w2p + e*H*I
     int I;
     __device__ __forceinline__ const uint16_t* chunk(int k, int m) const { return base + frag_index(k, m, I); }
-    __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
 // The GEMM runs on the plain dy rows, so the accumulator is dA'[r] = dy[t] @ W2[e]^T and the
-// row weight enters in the epilogue (dA = w * dA').  With topk_w_grad the epilogue also forms
-// sum over the tile's columns of dA'[r, c] * act[r, c]: summed over the N tiles (in tile order,
-// by the finish kernel) that is <dy[t], o_p>, the gradient of the routing weight, because
-// o_p = act_p @ W2[e].  64-row tiles fit three waves per SIMD (at most 168 registers), which
-// keeps more weight loads in flight per CU.
+// row weight enters in the epilogue (dA = w * dA').  The epilogue recomputes the activation
+// a = silu(g) * u in fp32 from the saved fp32 pre-activation and writes w * a as a hi/lo bf16
+// pair (the dW2 operand).  With topk_w_grad it also forms the sum over the tile's columns of
+// dA'[r, c] * a[r, c]: summed over the N tiles (in tile order, by the finish kernel) that is
+// <dy[t], o_p>, the gradient of the routing weight, because o_p = a_p @ W2[e].  64-row tiles fit
+// three waves per SIMD, which keeps more weight loads in flight per CU.
 template <class C>
 __global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad_kernel(const uint16_t* __restrict__ dy,
                                                       const float* __restrict__ topk_w,
@@ -401,15 +431,18 @@ __global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad_kernel(const
                 for (int ni = 0; ni < C::NI; ++ni) {
                     const int c = nt * C::BN + wn0 + ni * 32 + (lane & 31);
                     const float da = w * acc[mi][ni][r];
-                    if (topk_w_grad) part += acc[mi][ni][r] * bf16_to_f32(ws.act[row * I + c]);
+                    const float g = ws.hgu[row * 2 * I + c];
+                    const float u = ws.hgu[row * 2 * I + I + c];
+                    const float sg = 1.0f / (1.0f + __expf(-g));
+                    const float a = g * sg * u;
+                    if (topk_w_grad) part += acc[mi][ni][r] * a;
+                    split_bf16(w * a, ws.wact[row * I + c], ws.wact_lo[row * I + c]);
                     if (fuse) {
-                        const float g = bf16_to_f32(ws.hgu[row * 2 * I + c]);
-                        const float u = bf16_to_f32(ws.hgu[row * 2 * I + I + c]);
-                        const float sg = 1.0f / (1.0f + __expf(-g));
-                        ws.dhgu[row * 2 * I + c] = f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)));
-                        ws.dhgu[row * 2 * I + I + c] = f32_to_bf16(da * g * sg);
+                        split_bf16(da * u * sg * (1.0f + g * (1.0f - sg)), ws.dhgu[row * 2 * I + c],
+                                   ws.dhgu_lo[row * 2 * I + c]);
+                        split_bf16(da * g * sg, ws.dhgu[row * 2 * I + I + c], ws.dhgu_lo[row * 2 * I + I + c]);
                     } else {
-                        ws.dact[row * I + c] = f32_to_bf16(da);
+                        ws.dact[row * I + c] = da;
                     }
                 }
                 if (topk_w_grad) {   // uniform: every lane takes part in the shuffles
@@ -435,13 +468,11 @@ __global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad_kernel(const
 // dgrad1: L1 dgrad (NN) and the combine of its rows back to token order
 // ---------------------------------------------------------------------------------------------
 struct W1ColSrc {   // B operand of the L1 dgrad: (K = L1 output column, N = h) of expert e's packed W1
-    static constexpr bool kScaled = false;
     const uint16_t* base;   // w1p + e*2I*H
     int H, I;
     __device__ __forceinline__ const uint16_t* chunk(int k, int m) const {
         return base + frag_index(l1_packed_col(k, I), m, H);
     }
-    __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
 // dX[r] = dhgu[r] @ W1[e]^T (K = 2I in the logical [gate | up] order of dhgu, N = H).  The row
@@ -522,7 +553,6 @@ __global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad1_kernel(cons
 // K index k is row seg0 + k of the expert's segment; k >= count reads the zero row, so the K tail
 // and an expert without rows contribute nothing (an empty expert's tile stores exact zeros).
 struct GatherTokenSrc {   // row k -> token row of x or dy through row_pair, optionally weighted
-    static constexpr bool kScaled = false;
     const uint16_t* base;
     const uint16_t* zeros;   // ws.zeros: a zero row at least H long
     const int32_t* row_pair;
@@ -533,18 +563,8 @@ struct GatherTokenSrc {   // row k -> token row of x or dy through row_pair, opt
         const int p = pair(kk);
         return (p >= 0 && p < npairs) ? base + static_cast<int64_t>(p / k) * H + m : zeros + m;
     }
-    __device__ __forceinline__ float scale(int) const { return 1.0f; }
-};
-struct WeightedGatherSrc : GatherTokenSrc {   // dO rows: topk_w[p] * dy[t]
-    static constexpr bool kScaled = true;
-    const float* topk_w;
-    __device__ __forceinline__ float scale(int kk) const {
-        const int p = pair(kk);
-        return (p >= 0 && p < npairs) ? topk_w[p] : 0.0f;
-    }
 };
 struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
-    static constexpr bool kScaled = false;
     const uint16_t* base;
     const uint16_t* zeros;   // ws.zeros: a zero row at least width long
     int64_t seg0;
@@ -552,7 +572,6 @@ struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
     __device__ __forceinline__ const uint16_t* chunk(int kk, int m) const {
         return kk < count ? base + (seg0 + kk) * width + m : zeros + m;
     }
-    __device__ __forceinline__ float scale(int) const { return 1.0f; }
 };
 
 // The accumulator of a 32x32 MFMA block stored as one packed 1 KB block: store_packed_block in
@@ -564,18 +583,58 @@ __device__ __forceinline__ void store_grad_block(uint16_t* out, int64_t K, int64
 
 constexpr int kWgradChunk = 8;   // output tiles per weight-gradient workgroup
 
+// Full K loop of one weight-gradient tile whose operand A (SPLIT_A) or B comes as hi (la / lb)
+// plus lo (lx) tiles; one LDS buffer: A | B | X.
+template <class C, bool SPLIT_A, class LA, class LB, class LX>
+__device__ __forceinline__ void gemm_tile_split(LA& la, LB& lb, LX& lx, int nk, char* smem,
+                                                f32x16_t (&acc)[C::MI][C::NI], int tid, int wm0, int wn0, int lane) {
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    if (nk <= 0) return;
+    char* lA = smem;
+    char* lB = smem + C::A_BYTES;
+    char* lX = lB + C::B_BYTES;
+    la.template load<0>(0, tid);
+    lb.template load<0>(0, tid);
+    lx.template load<0>(0, tid);
+    la.template store<0>(lA, tid);
+    lb.template store<0>(lB, tid);
+    lx.template store<0>(lX, tid);
+    lds_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        if (more) {
+            la.template load<0>(kt + 1, tid);
+            lb.template load<0>(kt + 1, tid);
+            lx.template load<0>(kt + 1, tid);
+        }
+        mma_step_split<C, SPLIT_A>(lA, lB, lX, acc, wm0, wn0, lane);
+        if (more) {
+            lds_barrier();   // every wave's fragment reads of step kt are done
+            la.template store<0>(lA, tid);
+            lb.template store<0>(lB, tid);
+            lx.template store<0>(lX, tid);
+            lds_barrier();
+        }
+    }
+}
+
 // A run of output tiles of one expert's weight gradient that share one operand tile: with
 // STREAM_A the M tiles [t0, t1) of N tile `fixed` (the N operand lb is shared), else the N tiles
-// [t0, t1) of M tile `fixed` (la is shared); the streamed operand is the cheaper one to load.  When
-// the expert has at most one K step of rows (the common case: K is the expert's row count), the
-// shared tile is loaded into LDS once and the streamed one's loads for tile t + 1 go out before
-// the MFMAs and stores of tile t, so the launch streams its output.  With more rows every tile
-// runs the full K loop.  n_col(nt, ni) gives the packed column of block ni of the wave in N tile nt;
-// K_out is the packed reduction length.
-template <class C, bool STREAM_A, class LA, class LB, class NCol>
-__device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed, int t0, int t1, uint16_t* out,
-                                            int64_t K_out, NCol n_col, char* smem, int tid, int wm0, int wn0,
-                                            int lane) {
+// [t0, t1) of M tile `fixed` (la is shared).  The streamed operand is the one given as a hi/lo
+// pair (lx loads its lo part into the third LDS tile).  When the expert has at most one K step of
+// rows (the common case: K is the expert's row count), the shared tile is loaded into LDS once and
+// the streamed one's loads for tile t + 1 go out before the MFMAs and stores of tile t, so the
+// launch streams its output.  With more rows every tile runs the full K loop.  n_col(nt, ni) gives
+// the packed column of block ni of the wave in N tile nt; K_out is the packed reduction length.
+template <class C, bool STREAM_A, class LA, class LB, class LX, class NCol>
+__device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, LX& lx, int count, int fixed, int t0, int t1,
+                                            uint16_t* out, int64_t K_out, NCol n_col, char* smem, int tid, int wm0,
+                                            int wn0, int lane) {
     const int nk = (count + BK - 1) / BK;
     f32x16_t acc[C::MI][C::NI];
     auto store = [&](int t) {
@@ -586,9 +645,10 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed
             for (int ni = 0; ni < C::NI; ++ni)
                 store_grad_block(out, K_out, n_col(nt, ni), mt * C::BM + wm0 + mi * 32, acc[mi][ni], lane);
     };
-    auto aim = [&](int t) {   // point the streamed operand at tile t
+    auto aim = [&](int t) {   // point the streamed operand (both parts) at tile t
         if constexpr (STREAM_A) la.m_base = t * C::BM;
         else lb.m_base = t * C::BN;
+        lx.m_base = t * (STREAM_A ? C::BM : C::BN);
     };
     if constexpr (STREAM_A) lb.m_base = fixed * C::BN;
     else la.m_base = fixed * C::BM;
@@ -599,15 +659,18 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed
         // stored to LDS), so the compiler's wait counts stay exact.
         char* lA = smem;
         char* lB = smem + C::A_BYTES;
+        char* lX = lB + C::B_BYTES;
         auto stream_load = [&](int t, auto slot) {
             aim(min(t, t1 - 1));
             if constexpr (STREAM_A) la.template load<decltype(slot)::value>(0, tid);
             else lb.template load<decltype(slot)::value>(0, tid);
+            lx.template load<decltype(slot)::value>(0, tid);
         };
         auto stream_store = [&](auto slot) {
             lds_barrier();   // every wave's fragment reads of the previous tile are done
             if constexpr (STREAM_A) la.template store<decltype(slot)::value>(lA, tid);
             else lb.template store<decltype(slot)::value>(lB, tid);
+            lx.template store<decltype(slot)::value>(lX, tid);
             lds_barrier();
         };
         auto compute = [&](int t) {
@@ -617,7 +680,7 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed
                 for (int j = 0; j < C::NI; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-            if (nk == 1) mma_step<C>(lA, lB, acc, wm0, wn0, lane);
+            if (nk == 1) mma_step_split<C, STREAM_A>(lA, lB, lX, acc, wm0, wn0, lane);
             store(t);
         };
         using S0 = std::integral_constant<int, 0>;
@@ -625,9 +688,11 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed
         aim(t0);
         la.template load<0>(0, tid);
         lb.template load<0>(0, tid);
+        lx.template load<0>(0, tid);
         stream_load(t0 + 1, S1{});
         la.template store<0>(lA, tid);
         lb.template store<0>(lB, tid);
+        lx.template store<0>(lX, tid);
         lds_barrier();
         for (int t = t0; t < t1; t += 2) {
             // slot 1 holds tile t + 1, slot 0 is free
@@ -644,7 +709,7 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, int count, int fixed
     } else {
         for (int t = t0; t < t1; ++t) {
             aim(t);
-            gemm_tile<C>(la, lb, nk, smem, acc, tid, wm0, wn0, lane);
+            gemm_tile_split<C, STREAM_A>(la, lb, lx, nk, smem, acc, tid, wm0, wn0, lane);
             store(t);
             lds_barrier();   // the next tile's first LDS stores follow every wave's last reads
         }
@@ -670,12 +735,12 @@ struct WgradWork {
     }
 };
 
-// dW2[e] (packed like W2: column h, reduction index i) = sum_k act[k][i] * (w dy)[k][h]:
-// M = I (the packed reduction index), N = H (the packed column).  The weighted dy gather is the
-// shared operand; act tiles stream.
+// dW2[e] (packed like W2: column h, reduction index i) = sum_k (w act)[k][i] * dy[t_k][h]:
+// M = I (the packed reduction index), N = H (the packed column).  The dy gather is the shared
+// operand; the weighted activation tiles (hi and lo, from the dgrad's epilogue) stream.
+// Two waves per SIMD: the lo tile's loads and fragments need more than the 168 registers of three.
 template <class C>
-__global__ __launch_bounds__(C::NT, 3) void wgrad2_kernel(const uint16_t* __restrict__ dy,
-                                                          const float* __restrict__ topk_w, Dims d, Ws ws,
+__global__ __launch_bounds__(C::NT, 2) void wgrad2_kernel(const uint16_t* __restrict__ dy, Dims d, Ws ws,
                                                           uint16_t* __restrict__ dw2p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -683,13 +748,15 @@ __global__ __launch_bounds__(C::NT, 3) void wgrad2_kernel(const uint16_t* __rest
     const int H = d.H, I = d.I;
     const WgradWork wk(ws, H / C::BN, I / C::BM);
 
-    TRows<C::BM, C::NT, DirectRowSrc> la;
-    la.src.base = ws.act;
+    TRows<C::BM, C::NT, DirectRowSrc> la, lx;
+    la.src.base = ws.wact;
     la.src.zeros = ws.zeros;
     la.src.seg0 = wk.seg0;
     la.src.count = wk.count;
     la.src.width = I;
-    TRows<C::BN, C::NT, WeightedGatherSrc> lb;
+    lx.src = la.src;
+    lx.src.base = ws.wact_lo;
+    TRows<C::BN, C::NT, GatherTokenSrc> lb;
     lb.src.base = dy;
     lb.src.zeros = ws.zeros;
     lb.src.row_pair = ws.row_pair;
@@ -698,18 +765,17 @@ __global__ __launch_bounds__(C::NT, 3) void wgrad2_kernel(const uint16_t* __rest
     lb.src.k = d.k;
     lb.src.H = H;
     lb.src.npairs = d.T * d.k;
-    lb.src.topk_w = topk_w;
     uint16_t* out = dw2p + static_cast<int64_t>(wk.e) * H * I;
-    wgrad_tiles<C, true>(la, lb, wk.count, wk.fixed, wk.t0, wk.t1, out, I,
+    wgrad_tiles<C, true>(la, lb, lx, wk.count, wk.fixed, wk.t0, wk.t1, out, I,
                          [&](int nt, int ni) { return static_cast<int64_t>(nt * C::BN + wn0 + ni * 32); }, smem,
                          tid, wm0, wn0, lane);
 }
 
 // dW1[e] (packed like W1: L1 column n, reduction index h) = sum_k x[t_k][h] * dhgu[k][n]:
 // M = H (the packed reduction index), N = 2I (logical L1 columns; 32-column groups map to packed
-// column groups whole).  The x gather is the shared operand; dhgu tiles stream.
+// column groups whole).  The x gather is the shared operand; dhgu tiles (hi and lo) stream.
 template <class C>
-__global__ __launch_bounds__(C::NT, C::BM == 128 ? 3 : 2) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
+__global__ __launch_bounds__(C::NT, 2) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
                                                           uint16_t* __restrict__ dw1p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -726,15 +792,17 @@ __global__ __launch_bounds__(C::NT, C::BM == 128 ? 3 : 2) void wgrad1_kernel(con
     la.src.k = d.k;
     la.src.H = H;
     la.src.npairs = d.T * d.k;
-    TRows<C::BN, C::NT, DirectRowSrc> lb;
+    TRows<C::BN, C::NT, DirectRowSrc> lb, lx;
     lb.src.base = ws.dhgu;
     lb.src.zeros = ws.zeros;
     lb.src.seg0 = wk.seg0;
     lb.src.count = wk.count;
     lb.src.width = N2;
+    lx.src = lb.src;
+    lx.src.base = ws.dhgu_lo;
     uint16_t* out = dw1p + static_cast<int64_t>(wk.e) * N2 * H;
     const int I = d.I;
-    wgrad_tiles<C, false>(la, lb, wk.count, wk.fixed, wk.t0, wk.t1, out, H,
+    wgrad_tiles<C, false>(la, lb, lx, wk.count, wk.fixed, wk.t0, wk.t1, out, H,
                           [&](int nt, int ni) { return l1_packed_col(nt * C::BN + wn0 + ni * 32, I); }, smem, tid,
                           wm0, wn0, lane);
 }
@@ -781,7 +849,6 @@ using G64 = Cfg<64, 128, 2, 2>;
 using G128 = Cfg<128, 128, 2, 2>;
 using G256 = Cfg<256, 128, 4, 1>;
 using WG = Cfg<128, 128, 2, 2, 0>;   // weight-gradient tiles: K is an expert's rows, often one step
-using WG1 = Cfg<256, 128, 4, 1, 0>;  // dW1 with H a multiple of 256: fewer, taller tiles measured faster
 
 template <class C0>
 static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
@@ -843,16 +910,16 @@ __global__ __launch_bounds__(256) void repack_t_kernel(const uint16_t* __restric
 // The L2 dgrad of experts with many rows runs on the forward's L1 tile loop (dgrad_nt_kernel) with W2
 // repacked to an (N = i, K = h) operand in ws stage (free during the backward's first GEMM; it
 // holds EL * I * H elements when EL * I <= 2 * R_max).
-static bool dgrad_nt_use(const Dims& d, const Ws& ws, int fuse, bool topk_w_grad) {
+static bool dgrad_nt_use(const Dims& d, const Ws& ws) {
     return static_cast<int64_t>(d.T) * d.k >= kWgradNtRows * d.E && dgrad_nt_fits(d) && ws.stage &&
-           static_cast<int64_t>(d.EL) * d.I <= 2 * ws.rows_cap && (!fuse || (ws.hgu && ws.dhgu)) &&
-           (fuse || ws.dact) && (!topk_w_grad || ws.act);
+           static_cast<int64_t>(d.EL) * d.I <= 2 * ws.rows_cap;
 }
 
 hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
                         const Ws& ws, int fuse, bool topk_w_grad, hipStream_t s) {
     if (topk_w_grad && (!ws.dtw_part || ws.dtw_cols != d.I / 128)) return hipErrorInvalidValue;
-    if (dgrad_nt_use(d, ws, fuse, topk_w_grad)) {
+    if (!ws.hgu || !ws.dact || !ws.dhgu || !ws.dhgu_lo || !ws.wact || !ws.wact_lo) return hipErrorInvalidValue;
+    if (dgrad_nt_use(d, ws)) {
         uint16_t* w2t = reinterpret_cast<uint16_t*>(ws.stage);
         repack_t_kernel<false><<<device_cu_count() * 8, 256, 0, s>>>(w2p, d.I, d.H, d.I, d.EL, w2t);
         const hipError_t e = hipGetLastError();
@@ -880,20 +947,22 @@ static hipError_t dgrad1_launch(const Dims& d, const uint16_t* w1p, const Ws& ws
 }
 
 // The L1 dgrad of experts with many rows runs as the forward's L2 (NT, with its combine into
-// token order, weight 1): K = 2I over the dhgu rows, B = W1 repacked by repack_w1_t_kernel into
-// ws dact (dead once dhgu exists; it holds EL * H * 2I elements when 2 * EL * H <= R_max).
+// token order, weight 1): K = 2I over the dhgu rows, B = W1 repacked by repack_t_kernel into
+// ws dact (dead once dhgu exists; its R_max * I fp32 hold the EL * H * 2I bf16 elements when
+// EL * H <= R_max).
 static bool dgrad1_nt_use(const Dims& d, const Ws& ws) {
     return ws.dact && ws.dhgu && static_cast<int64_t>(d.T) * d.k >= kWgradNtRows * d.E && d.H % 256 == 0 &&
-           (2 * d.I) % 64 == 0 && 2 * static_cast<int64_t>(d.EL) * d.H <= ws.rows_cap;
+           (2 * d.I) % 64 == 0 && static_cast<int64_t>(d.EL) * d.H <= ws.rows_cap;
 }
 
 hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s) {
     if (dgrad1_nt_use(d, ws)) {
-        repack_t_kernel<true><<<device_cu_count() * 8, 256, 0, s>>>(w1p, d.H, 2 * d.I, d.I, d.EL, ws.dact);
+        uint16_t* w1t = reinterpret_cast<uint16_t*>(ws.dact);
+        repack_t_kernel<true><<<device_cu_count() * 8, 256, 0, s>>>(w1p, d.H, 2 * d.I, d.I, d.EL, w1t);
         hipError_t e = hipGetLastError();
         Dims d2 = d;
         d2.I = 2 * d.I;   // the GEMM's K: dhgu rows are 2I wide
-        if (e == hipSuccess) e = launch_gemm2_combine(d2, ws.dhgu, ws.dact, nullptr, ws, dx, s);
+        if (e == hipSuccess) e = launch_gemm2_combine(d2, ws.dhgu, w1t, nullptr, ws, dx, s);
         if (e == hipSuccess) e = launch_combine_finish(d, ws, dx, s);
         return e;
     }
@@ -916,14 +985,15 @@ hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint1
 // for a row no pair holds), written column by column, either into At [W, R_max] (row c holds
 // column c of every ws row; PACKED false) or into MFMA fragments along the rows (PACKED true:
 // block (n / 32, r / 16) at (n / 32 * (R_max / 16) + r / 16) * 1 KB, lane n % 32 + 32 * ((r / 8) % 2)
-// holding the 8 rows of r's octet, n the packed column of c).  Sources: ws act rows, the token
-// rows of x or dy through row_pair (dy scaled by the routing weight and rounded to bf16, as the
-// streaming kernels do), or ws dhgu rows (packed by L1 column).
-enum RowsSrc { kActRows, kTokenRows, kWeightedTokenRows, kDhguRows };
+// holding the 8 rows of r's octet, n the packed column of c).  Sources: ws wact rows (the
+// weighted activation, hi part), the token rows of x or dy through row_pair, or ws dhgu rows
+// (hi part, packed by L1 column).  With hundreds of rows per expert the weight gradients sum
+// enough products that one bf16 rounding of the intermediate operand averages out, so these
+// paths take the hi parts only.
+enum RowsSrc { kWactRows, kTokenRows, kDhguRows };
 
 template <int SRC, bool PACKED>
-__global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __restrict__ tok,
-                                                              const float* __restrict__ topk_w, Dims d, Ws ws, int W,
+__global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __restrict__ tok, Dims d, Ws ws, int W,
                                                               uint16_t* __restrict__ dst) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
     const int tid = threadIdx.x;
@@ -944,11 +1014,10 @@ __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __
             const int p = r < R ? ws.row_pair[r] : -1;
             if (p >= 0 && p < npairs) {
                 const uint16_t* src;
-                if constexpr (SRC == kActRows) src = ws.act + r * W;
+                if constexpr (SRC == kWactRows) src = ws.wact + r * W;
                 else if constexpr (SRC == kDhguRows) src = ws.dhgu + r * W;
                 else src = tok + static_cast<int64_t>(p / d.k) * W;
                 v = *reinterpret_cast<const u32x4*>(src + c0 + 8 * ch);
-                if constexpr (SRC == kWeightedTokenRows) v = scale_bf16x8(v, topk_w[p]);
             }
             *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) = v;
         }
@@ -976,9 +1045,9 @@ __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __
 }
 
 template <int SRC, bool PACKED>
-static hipError_t rows_to_k_major(const Dims& d, const Ws& ws, const uint16_t* tok, const float* topk_w, int W,
-                                  uint16_t* dst, hipStream_t s) {
-    rows_to_k_major_kernel<SRC, PACKED><<<device_cu_count() * 8, 256, 0, s>>>(tok, topk_w, d, ws, W, dst);
+static hipError_t rows_to_k_major(const Dims& d, const Ws& ws, const uint16_t* tok, int W, uint16_t* dst,
+                                  hipStream_t s) {
+    rows_to_k_major_kernel<SRC, PACKED><<<device_cu_count() * 8, 256, 0, s>>>(tok, d, ws, W, dst);
     return hipGetLastError();
 }
 
@@ -991,19 +1060,19 @@ static bool wgrad_nt_use(const Dims& d, int M, int N) {
            static_cast<int64_t>(M) + N <= 2 * static_cast<int64_t>(d.H);
 }
 
-hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
-                         uint16_t* dw2p, hipStream_t s) {
+hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const Ws& ws, uint16_t* dw2p, hipStream_t s) {
+    if (!ws.wact || !ws.wact_lo) return hipErrorInvalidValue;
     if (wgrad_nt_use(d, d.I, d.H)) {   // dW2 packed like W2: reduction index i (M = I), column h (N = H)
         uint16_t* at = reinterpret_cast<uint16_t*>(ws.stage);
         uint16_t* bp = at + static_cast<int64_t>(d.I) * ws.rows_cap;
-        hipError_t e = rows_to_k_major<kActRows, false>(d, ws, nullptr, nullptr, d.I, at, s);
-        if (e == hipSuccess) e = rows_to_k_major<kWeightedTokenRows, true>(d, ws, dy, topk_w, d.H, bp, s);
+        hipError_t e = rows_to_k_major<kWactRows, false>(d, ws, nullptr, d.I, at, s);
+        if (e == hipSuccess) e = rows_to_k_major<kTokenRows, true>(d, ws, dy, d.H, bp, s);
         if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.I, d.H, ws, dw2p, s);
         return e;
     }
     const int blocks = d.EL * (d.H / WG::BN) * ((d.I / WG::BM + kWgradChunk - 1) / kWgradChunk);
     if (blocks <= 0) return hipSuccess;
-    wgrad2_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES, s>>>(dy, topk_w, d, ws, dw2p);
+    wgrad2_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES + WG::A_BYTES, s>>>(dy, d, ws, dw2p);
     return hipGetLastError();
 }
 
@@ -1011,20 +1080,22 @@ template <class C>
 static hipError_t wgrad1_launch(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
     const int blocks = d.EL * (d.H / C::BM) * ((2 * d.I / C::BN + kWgradChunk - 1) / kWgradChunk);
     if (blocks <= 0) return hipSuccess;
-    wgrad1_kernel<C><<<blocks, C::NT, C::LDS_BYTES, s>>>(x, d, ws, dw1p);
+    const size_t lds = C::LDS_BYTES + C::B_BYTES;   // A | B | lo part of B
+    allow_lds(wgrad1_kernel<C>, lds);
+    wgrad1_kernel<C><<<blocks, C::NT, lds, s>>>(x, d, ws, dw1p);
     return hipGetLastError();
 }
 
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
+    if (!ws.dhgu || !ws.dhgu_lo) return hipErrorInvalidValue;
     if (wgrad_nt_use(d, d.H, 2 * d.I)) {   // dW1 packed like W1: reduction index h (M = H), packed column (N = 2I)
         uint16_t* at = reinterpret_cast<uint16_t*>(ws.stage);
         uint16_t* bp = at + static_cast<int64_t>(d.H) * ws.rows_cap;
-        hipError_t e = rows_to_k_major<kTokenRows, false>(d, ws, x, nullptr, d.H, at, s);
-        if (e == hipSuccess) e = rows_to_k_major<kDhguRows, true>(d, ws, nullptr, nullptr, 2 * d.I, bp, s);
+        hipError_t e = rows_to_k_major<kTokenRows, false>(d, ws, x, d.H, at, s);
+        if (e == hipSuccess) e = rows_to_k_major<kDhguRows, true>(d, ws, nullptr, 2 * d.I, bp, s);
         if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.H, 2 * d.I, ws, dw1p, s);
         return e;
     }
-    if (d.H % WG1::BM == 0) return wgrad1_launch<WG1>(d, x, ws, dw1p, s);
     return wgrad1_launch<WG>(d, x, ws, dw1p, s);
 }
 

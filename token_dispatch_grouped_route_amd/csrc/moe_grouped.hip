@@ -453,7 +453,7 @@ struct L1Body {
     Dims d;
     Ws ws;
     uint16_t* act_out;
-    uint16_t* hgu_out;
+    float* hgu_out;
     char* smem;
 
     template <int MA>
@@ -493,8 +493,8 @@ struct L1Body {
                     const int64_t row = t.row0 + mi * 32 + acc_row(r, lane);
                     const float g = acc[mi][2 * q][r], u = acc[mi][2 * q + 1][r];
                     if (hgu_out) {
-                        hgu_out[row * 2 * I + col] = f32_to_bf16(g);
-                        hgu_out[row * 2 * I + I + col] = f32_to_bf16(u);
+                        hgu_out[row * 2 * I + col] = g;
+                        hgu_out[row * 2 * I + I + col] = u;
                     }
                     if (act_out) act_out[row * I + col] = f32_to_bf16(silu_f32(g) * u);
                 }
@@ -510,8 +510,11 @@ struct L1Body {
                 const u32x4 z = 0;
                 if (act_out) *reinterpret_cast<u32x4*>(act_out + row * I + c) = z;
                 if (hgu_out) {
-                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + c) = z;
-                    *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + I + c) = z;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + c + 4 * h) = z;
+                        *reinterpret_cast<u32x4*>(hgu_out + row * 2 * I + I + c + 4 * h) = z;
+                    }
                 }
             }
         }
@@ -521,7 +524,7 @@ struct L1Body {
 template <class C>
 __global__ __launch_bounds__(C::NT, C::OCC) void l1_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1f,
                                                      Dims d, Ws ws, uint16_t* __restrict__ act_out,
-                                                     uint16_t* __restrict__ hgu_out) {
+                                                     float* __restrict__ hgu_out) {
     static_assert(C::NI % 2 == 0, "a wave holds whole gate/up pairs");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     L1Body<C> body{x, w1f, d, ws, act_out, hgu_out, smem};
@@ -687,7 +690,7 @@ void allow_lds(K kernel, size_t bytes) {
 
 template <class C>
 hipError_t l1_launch(const Dims& d, const uint16_t* x, const uint16_t* w1f, const Ws& ws, uint16_t* act_out,
-                     uint16_t* hgu_out, hipStream_t s) {
+                     float* hgu_out, hipStream_t s) {
     auto k = l1_kernel<C>;
     allow_lds(k, C::LDS_BYTES);
     k<<<persistent_grid(k, C::NT, C::LDS_BYTES), C::NT, C::LDS_BYTES, s>>>(x, w1f, d, ws, act_out, hgu_out);
@@ -775,10 +778,12 @@ __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_nt_kernel(const uint16_t*
 // ---------------------------------------------------------------------------------------------
 // dA'[r] = dy[t] @ W2[e]^T (t the row's token) on the L1 tile loop: the dy rows gathered through
 // row_pair into the A ring, W2 repacked to an (N = i, K = h) operand streaming into B registers.
-// The epilogue is the streaming dgrad's: the row weight (dA = w * dA'), the SwiGLU transpose from
-// the saved pre-activation (fuse) or plain dA rows, and the routing-weight partials: for each
-// 128-column half of the 256-column tile (waves 2h and 2h + 1) the sum over its columns of
-// dA' * act, in the [R_max, I / 128] layout of ws dtw_part.
+// The epilogue is the streaming dgrad's: the row weight (dA = w * dA'), the activation
+// a = silu(g) * u recomputed in fp32 from the saved fp32 pre-activation and written as w * a (hi
+// and lo bf16, the dW2 operand), the SwiGLU transpose (fuse; dhgu hi and lo) or plain fp32 dA
+// rows, and the routing-weight partials: for each 128-column half of the 256-column tile (waves
+// 2h and 2h + 1) the sum over its columns of dA' * a, in the [R_max, I / 128] layout of ws
+// dtw_part.
 template <class C>
 struct DgradBody {
     const uint16_t* dy;
@@ -820,7 +825,7 @@ struct DgradBody {
         if (tid < 32 * MA) s_w[tid] = (pr_own >= 0 && pr_own < npairs) ? topk_w[pr_own] : 0.0f;
         // Epilogue through LDS, GP 32-row groups per pass: the waves drop dA' into a row-major fp32
         // tile, then each wave takes whole rows (64 lanes x 4 columns = the tile's 256 columns), so
-        // the act / hgu reads and the dhgu (or dact) writes are contiguous row segments, and a row's
+        // the hgu reads and the dhgu / dact / wact writes are contiguous row segments, and a row's
         // two 128-column routing-weight partials are the sums over lanes 0-31 and 32-63.
         constexpr int LD = C::BN + 4;   // floats per LDS row: rows r and r + 4 fall on different banks
         constexpr int GP = 2;
@@ -842,22 +847,19 @@ struct DgradBody {
                                 acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
             lds_barrier();
             const int rows = min(GP * 32, t.real_rows - 32 * m0);
-            // four rows per wave at a time: their act / hgu loads all go out before any is used
+            // four rows per wave at a time: their hgu loads all go out before any is used
             constexpr int RB = 4, WS = C::NT / 64;
             for (int rb = wave; rb < rows; rb += RB * WS) {
-                uint2 av[RB], gv[RB], uv[RB];
+                float4 gv[RB], uv[RB];
 #pragma unroll
                 for (int b = 0; b < RB; ++b) {
                     const int rr = rb + b * WS;
-                    av[b] = gv[b] = uv[b] = make_uint2(0, 0);
+                    gv[b] = uv[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                     if (rr < rows) {
                         const int64_t row = t.row0 + 32 * m0 + rr;
                         const int c = t.nt * C::BN + lane * 4;
-                        if (tw) av[b] = *reinterpret_cast<const uint2*>(ws.act + row * I + c);
-                        if (fuse) {
-                            gv[b] = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + c);
-                            uv[b] = *reinterpret_cast<const uint2*>(ws.hgu + row * 2 * I + I + c);
-                        }
+                        gv[b] = *reinterpret_cast<const float4*>(ws.hgu + row * 2 * I + c);
+                        uv[b] = *reinterpret_cast<const float4*>(ws.hgu + row * 2 * I + I + c);
                     }
                 }
 #pragma unroll
@@ -870,32 +872,36 @@ struct DgradBody {
                     const int c = t.nt * C::BN + lane * 4;
                     const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + lane * 4);
                     const float va[4] = {v.x, v.y, v.z, v.w};
+                    const float ga[4] = {gv[b].x, gv[b].y, gv[b].z, gv[b].w};
+                    const float ua[4] = {uv[b].x, uv[b].y, uv[b].z, uv[b].w};
                     float part = 0.0f;
-                    if (tw) {
-                        const uint32_t aw[2] = {av[b].x, av[b].y};
+                    uint16_t wh[4], wl[4], gh[4], gl[4], uh[4], ul[4];
+                    float dv[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            part += va[q] * bf16_to_f32(static_cast<uint16_t>(aw[q >> 1] >> (16 * (q & 1))));
+                    for (int q = 0; q < 4; ++q) {
+                        const float g = ga[q], u = ua[q];
+                        const float sg = 1.0f / (1.0f + __expf(-g));
+                        const float a = g * sg * u;
+                        const float da = w * va[q];
+                        part += va[q] * a;
+                        split_bf16(w * a, wh[q], wl[q]);
+                        split_bf16(da * u * sg * (1.0f + g * (1.0f - sg)), gh[q], gl[q]);
+                        split_bf16(da * g * sg, uh[q], ul[q]);
+                        dv[q] = da;
                     }
+                    auto pk = [](const uint16_t (&h)[4]) {
+                        return make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                                          h[2] | (static_cast<uint32_t>(h[3]) << 16));
+                    };
+                    *reinterpret_cast<uint2*>(ws.wact + row * I + c) = pk(wh);
+                    *reinterpret_cast<uint2*>(ws.wact_lo + row * I + c) = pk(wl);
                     if (fuse) {
-                        const uint32_t gw[2] = {gv[b].x, gv[b].y}, uw[2] = {uv[b].x, uv[b].y};
-                        uint32_t dg[2] = {0, 0}, du[2] = {0, 0};
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float g = bf16_to_f32(static_cast<uint16_t>(gw[q >> 1] >> (16 * (q & 1))));
-                            const float u = bf16_to_f32(static_cast<uint16_t>(uw[q >> 1] >> (16 * (q & 1))));
-                            const float da = w * va[q];
-                            const float sg = 1.0f / (1.0f + __expf(-g));
-                            dg[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)))) << (16 * (q & 1));
-                            du[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(da * g * sg)) << (16 * (q & 1));
-                        }
-                        *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + c) = make_uint2(dg[0], dg[1]);
-                        *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + I + c) = make_uint2(du[0], du[1]);
+                        *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + c) = pk(gh);
+                        *reinterpret_cast<uint2*>(ws.dhgu_lo + row * 2 * I + c) = pk(gl);
+                        *reinterpret_cast<uint2*>(ws.dhgu + row * 2 * I + I + c) = pk(uh);
+                        *reinterpret_cast<uint2*>(ws.dhgu_lo + row * 2 * I + I + c) = pk(ul);
                     } else {
-                        uint32_t o[2] = {0, 0};
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) o[q >> 1] |= static_cast<uint32_t>(f32_to_bf16(w * va[q])) << (16 * (q & 1));
-                        *reinterpret_cast<uint2*>(ws.dact + row * I + c) = make_uint2(o[0], o[1]);
+                        *reinterpret_cast<float4*>(ws.dact + row * I + c) = make_float4(dv[0], dv[1], dv[2], dv[3]);
                     }
                     if (tw) {   // uniform over the wave: its lanes hold one row
 #pragma unroll
@@ -950,7 +956,7 @@ hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp
 
 // L1 N tiles are 256 columns (2I is a multiple of 256); L2 N tiles 256 columns when H allows, else 128.
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1f, const Ws& ws, uint16_t* act_out,
-                        uint16_t* hgu_out, hipStream_t s) {
+                        float* hgu_out, hipStream_t s) {
     if (d.EL > kMaxEL) return hipErrorInvalidValue;
     return l1_launch<L1Tile>(d, x, w1f, ws, act_out, hgu_out, s);
 }

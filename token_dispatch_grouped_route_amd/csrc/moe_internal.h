@@ -30,9 +30,12 @@ struct Ws {
     int32_t* chunk_dropped; // [num_chunks]
     uint16_t* act;          // bf16 [R_max, I]
     float* stage;           // fp32 [R_max, H]
-    uint16_t* hgu;          // bf16 [R_max, 2I] (train)
-    uint16_t* dact;         // bf16 [R_max, I]  (train)
-    uint16_t* dhgu;         // bf16 [R_max, 2I] (train)
+    float* hgu;             // fp32 [R_max, 2I] saved pre-activation (train)
+    float* dact;            // fp32 [R_max, I]  L2 dgrad rows (train)
+    uint16_t* dhgu;         // bf16 [R_max, 2I] [gate | up] gradient rows, hi part (train)
+    uint16_t* dhgu_lo;      // bf16 [R_max, 2I] lo part: dhgu + dhgu_lo carries the fp32 value (train)
+    uint16_t* wact;         // bf16 [R_max, I]  w * act (routing weight times activation), hi part (train)
+    uint16_t* wact_lo;      // bf16 [R_max, I]  its lo part (train)
     float* dtw_part;        // fp32 [R_max, I / 128] per-row partials of d(topk_w) (train)
     uint16_t* zeros;        // a zero row of max(H, 2I) bf16 (written by the prologue)
     int32_t* tile_sync;     // [kMaxGrid] tile-scheduler counters of the forward GEMMs (zero between launches)
@@ -65,6 +68,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {   // round to nearest
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// v as two bf16 values hi + lo: hi = bf16(v), lo = bf16(v - hi) (the difference is exact in fp32),
+// about 16 significant bits together.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16(v);
+    lo = f32_to_bf16(v - bf16_to_f32(hi));
+}
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then s_barrier.
 // __syncthreads() also fences global memory, which waits for every global load in flight
@@ -129,8 +138,8 @@ hipError_t launch_pack(const Dims& d, const uint16_t* w1, const uint16_t* w2, ui
 hipError_t launch_unpack(const Dims& d, const uint16_t* w1p, const uint16_t* w2p, uint16_t* w1,
                          uint16_t* w2, hipStream_t s);
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1p, const Ws& ws,
-                        uint16_t* act_out, uint16_t* hgu_out, hipStream_t s);
-hipError_t launch_swiglu(const Dims& d, const uint16_t* hgu, const Ws& ws, uint16_t* act,
+                        uint16_t* act_out, float* hgu_out, hipStream_t s);
+hipError_t launch_swiglu(const Dims& d, const float* hgu, const Ws& ws, uint16_t* act,
                          hipStream_t s);
 hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16_t* w2p,
                                 const float* topk_w, const Ws& ws, uint16_t* y, hipStream_t s);
@@ -141,8 +150,7 @@ hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w,
 hipError_t launch_dtopk_w_finish(const Dims& d, const Ws& ws, float* dtopk_w, hipStream_t s);
 hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s);
 hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s);
-hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const float* topk_w, const Ws& ws,
-                         uint16_t* dw2p, hipStream_t s);
+hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const Ws& ws, uint16_t* dw2p, hipStream_t s);
 bool wgrad_nt_fits(int M, int N);
 bool dgrad_nt_fits(const Dims& d);
 hipError_t launch_dgrad_nt(const Dims& d, const uint16_t* dy, const uint16_t* w2t, const float* topk_w, const Ws& ws,
