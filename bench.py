@@ -210,6 +210,8 @@ def bench_backward(a):
     dtw = torch.empty_like(wts)
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    if a.copy_calibration:
+        copy_calibration()
     stages = (("forward_train", lambda: moe.forward(shape, x, idx, wts, W1p, W2p, ws, y)),
               ("dgrad_swiglu_bwd", lambda: moe.bwd_gemm2_dgrad(shape, dy, wts, W2p, ws, fuse_swiglu_bwd=True,
                                                                dtopk_w=dtw)),

@@ -9,6 +9,10 @@ known / measured on that copy, so the figures are in true HBM bytes whatever uni
         PASS_DIR [PASS_DIR ...] > profiles/forward_dsv3_share_counters.md
     python profile_counters.py --variant mx --trace TRACE_DIR \
         --out-json profiles/mx_gemm1_wide_share_traffic.json PASS_DIR [...] > profiles/forward_mx_wide_share_counters.md
+    python profile_counters.py --variant bwd --workload wide_share_fwd_bwd --trace TRACE_DIR \
+        --out-json gpurun_out/bwd.json PASS_DIR [...] > profiles/training_wide_share_counters.md
+
+    python profile_counters.py stats TRACE_DIR --title TITLE --command CMD > profiles/<kernel>_<workload>_kernel_stats.md
 
 Writes the L1 launch's HBM bytes (read + write) with the hash of the kernel source they were taken
 on (bench.py reports them only while that source is unchanged) and prints a markdown table.  With
@@ -30,6 +34,15 @@ COPY_BYTES = 1 << 30   # bench.py --copy-calibration: one 1 GiB buffer copied to
 COMMON = (("combine_finish", "combine finish (multi-pair tokens)"),
           ("route_count", "prologue: count"), ("route_scan", "prologue: scan"),
           ("route_place", "prologue: place"))
+BWD = (("dgrad_nt_kernel", "L2 dgrad NN on the forward pipeline + SwiGLU transpose (many rows)"),
+       ("wgrad_nt_kernel", "dW1 / dW2 TN on the forward pipeline (many rows)"),
+       ("dgrad1_kernel", "L1 dgrad NN + combine rows"),
+       ("dgrad_kernel", "L2 dgrad NN + SwiGLU transpose + d(topk_w) partials + w*act"),
+       ("wgrad2_kernel", "dW2 TN, variable K, hi/lo operand"),
+       ("wgrad1_kernel", "dW1 TN, variable K, hi/lo operand"),
+       ("repack_t_kernel", "weight repack (many rows)"),
+       ("rows_to_k_major_kernel", "row transposes (many rows)"),
+       ("dtopk_w_finish", "d(topk_w) finish"))
 VARIANTS = {
     "bf16": {"title": "DeepSeek-V3 share forward", "src": GEMM_SRC, "l1": "l1_kernel", "workload": "dsv3_share_fwd",
              "kinds": (("l1_kernel", "L1: dispatch gather + grouped GEMM + SwiGLU"),
@@ -38,6 +51,11 @@ VARIANTS = {
            "workload": "wide_share_mx_fwd",
            "kinds": (("mx_l1", "MX L1: dispatch gather + FP8 x FP4 GEMM + clamped SwiGLU + FP8 cast"),
                      ("mx_l2", "MX L2: FP8 x FP4 GEMM + weighted combine")) + COMMON},
+    "bwd": {"title": "training step", "src": os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc",
+                                                          "moe_gemm.hip"),
+            "l1": None, "workload": "wide_share_fwd_bwd",
+            "kinds": BWD + (("l1_kernel", "forward L1 (saves the fp32 pre-activation)"),
+                            ("l2_kernel", "forward L2 + combine (also the L1 dgrad of many rows)")) + COMMON},
 }
 KINDS = VARIANTS["bf16"]["kinds"]
 
@@ -45,7 +63,7 @@ KINDS = VARIANTS["bf16"]["kinds"]
 def kind_of(name):
     if "mx_gemm_kernel" in name:
         return "mx_l1" if ", true>" in name else "mx_l2"
-    for key, _ in KINDS + VARIANTS["mx"]["kinds"]:
+    for key, _ in BWD + KINDS + VARIANTS["mx"]["kinds"]:
         if key in name:
             return key
     if "copyBuffer" in name:   # the runtime's plain device copy (--copy-calibration); conversion copies do not count
@@ -82,12 +100,39 @@ def read_durations(trace_dir):
     return dur
 
 
+def stats_table(trace_dir, title, command, note):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (every kernel, by total time)."""
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("# rocprofv3 kernel statistics: %s\n" % title)
+    if command:
+        print("Command (run from /tmp with TMPDIR=/tmp, repository at $R):\n\n```\n%s\n```\n" % command)
+    if note:
+        print(note + "\n")
+    print("| kernel | calls | avg (us) | min (us) | max (us) | total (ms) | % |")
+    print("|---|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        t = float(r["TotalDurationNs"])
+        print("| `%s` | %s | %.1f | %.1f | %.1f | %.2f | %.1f |" % (
+            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            t / 1e6, 100.0 * t / total))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "stats":
+        ap = argparse.ArgumentParser(prog="profile_counters.py stats")
+        ap.add_argument("trace")
+        ap.add_argument("--title", required=True)
+        ap.add_argument("--command", default="")
+        ap.add_argument("--note", default="")
+        a = ap.parse_args(sys.argv[2:])
+        return stats_table(a.trace, a.title, a.command, a.note)
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--out-json", required=True)
     ap.add_argument("--command", default="", help="the command lines that made the passes, for the record")
     ap.add_argument("--variant", choices=sorted(VARIANTS), default="bf16")
+    ap.add_argument("--workload", default="", help="workload name recorded in the json (bwd variant)")
     ap.add_argument("passes", nargs="+")
     a = ap.parse_args()
     var = VARIANTS[a.variant]
@@ -99,7 +144,7 @@ def main():
     # counters are in KiB; scale each to the copy's known bytes
     fr = COPY_BYTES / (cp["FETCH_SIZE"] * 1024.0)
     fw = COPY_BYTES / (cp["WRITE_SIZE"] * 1024.0)
-    print("# rocprofv3 counters per kernel (%s)\n" % var["title"])
+    print("# rocprofv3 counters per kernel (%s)\n" % (var["title"] + (", " + a.workload if a.workload else "")))
     if a.command:
         print("Commands (run from /tmp with TMPDIR=/tmp, repository at $R):\n\n```\n%s\n```\n" % a.command)
     print("FETCH_SIZE and WRITE_SIZE are scaled by what they read on a plain 1 GiB device copy: "
@@ -123,6 +168,11 @@ def main():
         tf = "%.0f" % (fl / t / 1e12) if (fl is not None and t) else "-"
         print("| %s | %.1f | %.1f | %.1f | %.0f | %.1f | %s |" % (label, (t or 0) * 1e6, rd / 1e6, wr / 1e6, bw, busy, tf))
         rec[key] = {"read_bytes": rd, "write_bytes": wr, "avg_s": t, "mfma_busy_pct": busy, "mfma_bf16_flops": fl}
+    if var["l1"] is None:   # every kernel's figures, no single roofline kernel
+        with open(a.out_json, "w") as f:
+            json.dump({"workload": a.workload or var["workload"], "copy_scale_read": fr, "copy_scale_write": fw,
+                       "kernels": rec, "command": a.command}, f, indent=1)
+        return
     l1 = rec.get(var["l1"])
     if l1:
         out = {"kernel_source_sha256_16": hashlib.sha256(open(var["src"], "rb").read()).hexdigest()[:16],
