@@ -53,7 +53,8 @@ typedef enum moe_status {
     MOE_ERR_WORKSPACE = -4,  /* ws_bytes < moe_workspace_bytes(shape), or ws lacks train buffers */
     MOE_ERR_ALIGN = -5,      /* a pointer is not 16-byte aligned (ws: 256-byte) */
     MOE_ERR_LAUNCH = -6,     /* the HIP runtime rejected a launch */
-    MOE_ERR_DEVICE = -7      /* the current device is not a gfx950 GPU, or HIP failed */
+    MOE_ERR_DEVICE = -7,     /* the current device is not a gfx950 GPU, or HIP failed */
+    MOE_ERR_SCRATCH = -8     /* moe_forward_noalloc: the shape needs more than its fixed scratch */
 } moe_status;
 
 /*
@@ -202,6 +203,23 @@ int32_t moe_gemm2_combine(const moe_shape* shape, const uint16_t* act, const uin
 int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* topk_idx,
                     const float* topk_w, const uint16_t* w1p, const uint16_t* w2p, void* ws,
                     size_t ws_bytes, uint16_t* y, void* stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same stages as moe_forward, with the workspace in a fixed device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs on until the
+ * process ends.  Nothing is allocated or freed by the call.
+ *   Arguments as for moe_forward, without ws; shape->train must be 0 (MOE_ERR_SHAPE otherwise).
+ *   MOE_ERR_SCRATCH when moe_workspace_bytes(shape) exceeds MOE_NOALLOC_SCRATCH_BYTES (e.g.
+ *   256 tokens of the DeepSeek-V3 share with top-8 fit; 8192 do not).
+ * Every call on one GPU uses that GPU's one array and leaves its contents behind: calls that
+ * overlap on one GPU (two streams, or two threads) race and must be serialised by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (256u * 1024u * 1024u)
+int32_t moe_forward_noalloc(const moe_shape* shape, const uint16_t* x, const int32_t* topk_idx,
+                            const float* topk_w, const uint16_t* w1p, const uint16_t* w2p, uint16_t* y,
+                            void* stream);
 
 /*
  * Backward entry points ("Mega MoE" page, Pipeline, backward).  They need a workspace with

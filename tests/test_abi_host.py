@@ -31,7 +31,7 @@ def test_library_exports_every_declared_entry_point():
 
 def test_status_strings():
     L = moe.lib()
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert L.moe_status_string(code) and L.moe_status_string(code) != b"unknown status"
     assert L.moe_status_string(5) == b"unknown status"
 

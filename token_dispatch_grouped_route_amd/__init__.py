@@ -28,8 +28,9 @@ ENTRY_POINTS = (
     "moe_gemm2_combine", "moe_forward", "moe_bwd_gemm2_dgrad", "moe_swiglu_bwd",
     "moe_bwd_gemm1_dgrad_combine", "moe_wgrad2", "moe_wgrad1", "moe_backward",
     "moe_mx_cast_fp8", "moe_mx_pack_weights", "moe_forward_mx", "moe_mx_dispatch_gemm1",
-    "moe_mx_gemm2_combine",
+    "moe_mx_gemm2_combine", "moe_forward_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 256 * 1024 * 1024   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,7 @@ def lib():
         L.moe_swiglu.argtypes = [S, P, P, ctypes.c_size_t, P, P]
         L.moe_gemm2_combine.argtypes = [S, P, P, P, P, ctypes.c_size_t, P, P]
         L.moe_forward.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P, P]
+        L.moe_forward_noalloc.argtypes = [S, P, P, P, P, P, P, P]
         L.moe_bwd_gemm2_dgrad.argtypes = [S, P, P, P, P, ctypes.c_size_t, i32, P, P]
         L.moe_swiglu_bwd.argtypes = [S, P, ctypes.c_size_t, P]
         L.moe_bwd_gemm1_dgrad_combine.argtypes = [S, P, P, ctypes.c_size_t, P, P]
@@ -271,6 +273,18 @@ def forward(shape, x, topk_idx, topk_w, w1p, w2p, ws, y, stream=None):
                              _ptr(topk_idx, torch.int32, "topk_idx", nn["topk_idx"]), _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]),
                              _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]), _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]), p, n,
                              _ptr(y, torch.bfloat16, "y", nn["y"]), _stream(stream)), "moe_forward")
+
+
+def forward_noalloc(shape, x, topk_idx, topk_w, w1p, w2p, y, stream=None):
+    """moe_forward with the library's fixed device scratch instead of a workspace (allocates
+    nothing; shapes whose workspace exceeds NOALLOC_SCRATCH_BYTES raise MoeError)."""
+    nn = _n(shape)
+    _check(lib().moe_forward_noalloc(ctypes.byref(shape), _ptr(x, torch.bfloat16, "x", nn["x"]),
+                                     _ptr(topk_idx, torch.int32, "topk_idx", nn["topk_idx"]),
+                                     _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]),
+                                     _ptr(w1p, torch.bfloat16, "w1p", nn["w1p"]),
+                                     _ptr(w2p, torch.bfloat16, "w2p", nn["w2p"]),
+                                     _ptr(y, torch.bfloat16, "y", nn["y"]), _stream(stream)), "moe_forward_noalloc")
 
 
 def bwd_gemm2_dgrad(shape, dy, topk_w, w2p, ws, fuse_swiglu_bwd=True, dtopk_w=None, stream=None):

@@ -3,6 +3,8 @@
 // include/moe.h.  No entry point allocates, frees, copies to or from the host, or waits.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -147,6 +149,7 @@ const char* moe_status_string(int32_t status) {
         case MOE_ERR_ALIGN: return "misaligned pointer (16 bytes; workspace 256 bytes)";
         case MOE_ERR_LAUNCH: return "kernel launch failed";
         case MOE_ERR_DEVICE: return "current device is not gfx950 or HIP failed";
+        case MOE_ERR_SCRATCH: return "the shape needs more workspace than the fixed scratch of moe_forward_noalloc";
         default: return "unknown status";
     }
 }
@@ -261,6 +264,64 @@ int32_t moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* to
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_route(d, topk_idx, w, s);
     if (e == hipSuccess) e = launch_gemm1(d, x, w1p, w, w.act, w.hgu, s);
+    if (e == hipSuccess) e = launch_gemm2_combine(d, w.act, w2p, topk_w, w, y, s);
+    if (e == hipSuccess) e = launch_combine_finish(d, w, y, s);
+    return launched(e);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Allocation-free forward: the workspace is a fixed device array of this file
+// ---------------------------------------------------------------------------------------------
+// The array itself.  In host code its name is only a stand-in for the device symbol: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device, and only that
+// address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call per device).
+int32_t scratch_of_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+int32_t moe_forward_noalloc(const moe_shape* shape, const uint16_t* x, const int32_t* topk_idx, const float* topk_w,
+                            const uint16_t* w1p, const uint16_t* w2p, uint16_t* y, void* stream) {
+    moe_ws_layout L;
+    int32_t st = layout_of(shape, &L);
+    if (st != MOE_OK) return st;
+    if (shape->train) return MOE_ERR_SHAPE;
+    if (L.total_bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    if (!w1p || !w2p || ((!x || !topk_idx || !topk_w || !y) && shape->T > 0)) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned16(w1p) || !aligned16(w2p) ||
+        !aligned16(y))
+        return MOE_ERR_ALIGN;
+    if (!is_gfx950()) return MOE_ERR_DEVICE;
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != MOE_OK) return st;
+    Dims d;
+    Ws w;
+    st = prepare(shape, ws, MOE_NOALLOC_SCRATCH_BYTES, false, &d, &w, &L);
+    if (st != MOE_OK) return st;
+    // the same stages as moe_forward; the prologue rewrites every table, the tile counters and the
+    // zero row, and the GEMMs write every row they later read, so stale contents of the array
+    // from an earlier call do not matter
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_route(d, topk_idx, w, s);
+    if (e == hipSuccess) e = launch_gemm1(d, x, w1p, w, w.act, nullptr, s);
     if (e == hipSuccess) e = launch_gemm2_combine(d, w.act, w2p, topk_w, w, y, s);
     if (e == hipSuccess) e = launch_combine_finish(d, w, y, s);
     return launched(e);
