@@ -151,7 +151,7 @@ def main():
           "read x %.3f, write x %.3f.  Durations are the kernel-trace averages of the same workload; "
           "MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs.\n" % (fr, fw))
     print("| kernel | avg us | HBM read MB | HBM write MB | HBM GB/s | MFMA busy %% | %s |"
-          % ("bf16 MFMA TFLOP/s" if a.variant == "bf16" else "MFMA TFLOP/s (not counted)"))
+          % ("bf16 MFMA TFLOP/s" if a.variant in ("bf16", "bwd") else "MFMA TFLOP/s (not counted)"))
     print("|---|---|---|---|---|---|---|")
     rec = {}
     for key, label in var["kinds"]:
