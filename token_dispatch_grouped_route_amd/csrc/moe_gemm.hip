@@ -193,37 +193,40 @@ __device__ __forceinline__ void mma_step(const char* lA, const char* lB, f32x16_
 }
 
 // mma_step with one operand given as hi + lo bf16 tiles (the lo tile at lX, laid out like the
-// operand it completes): acc += A * B + X * B (SPLIT_A) or A * B + A * X.
+// operand it completes): acc += A * B + X * B (SPLIT_A) or A * B + A * X.  Each 16-deep substep
+// issues the hi products of every accumulator first, then the lo ones, so no MFMA waits on the
+// one just before it; the lo fragments are read at the start of their substep (the hi MFMAs cover
+// that latency), one buffer instead of two.
 template <class C, bool SPLIT_A>
 __device__ __forceinline__ void mma_step_split(const char* lA, const char* lB, const char* lX,
                                                f32x16_t (&acc)[C::MI][C::NI], int wm0, int wn0, int lane) {
     constexpr int KS = BK / 16;
     constexpr int NX = SPLIT_A ? C::MI : C::NI;
-    bf16x8_t a[2][C::MI], b[2][C::NI], x[2][NX];
-    auto read_x = [&](bf16x8_t (&xv)[NX], int s) {
-        const int ch = 2 * s + (lane >> 5);
-        const int w0 = SPLIT_A ? wm0 : wn0;
-#pragma unroll
-        for (int i = 0; i < NX; ++i)
-            xv[i] = *reinterpret_cast<const bf16x8_t*>(lX + lds_off(w0 + i * 32 + (lane & 31), ch));
-    };
+    bf16x8_t a[2][C::MI], b[2][C::NI], x[NX];
     read_frags<C>(lA, lB, a[0], b[0], 0, wm0, wn0, lane);
-    read_x(x[0], 0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) {
-            read_frags<C>(lA, lB, a[(s + 1) & 1], b[(s + 1) & 1], s + 1, wm0, wn0, lane);
-            read_x(x[(s + 1) & 1], s + 1);
+        {
+            const int ch = 2 * s + (lane >> 5);
+            const int w0 = SPLIT_A ? wm0 : wn0;
+#pragma unroll
+            for (int i = 0; i < NX; ++i)
+                x[i] = *reinterpret_cast<const bf16x8_t*>(lX + lds_off(w0 + i * 32 + (lane & 31), ch));
         }
+        if (s + 1 < KS) read_frags<C>(lA, lB, a[(s + 1) & 1], b[(s + 1) & 1], s + 1, wm0, wn0, lane);
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
 #pragma unroll
             for (int j = 0; j < C::NI; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
                 if constexpr (SPLIT_A)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i], b[s & 1][j], acc[i][j], 0, 0, 0);
                 else
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], x[s & 1][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], x[j], acc[i][j], 0, 0, 0);
             }
     }
 }
@@ -721,13 +724,13 @@ __device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, LX& lx, int count, i
 struct WgradWork {
     int e, fixed, t0, t1, count;
     int64_t seg0;
-    __device__ WgradWork(const Ws& ws, int n_fixed, int n_stream) {
-        const int chunks = (n_stream + kWgradChunk - 1) / kWgradChunk;
+    __device__ WgradWork(const Ws& ws, int n_fixed, int n_stream, int chunk = kWgradChunk) {
+        const int chunks = (n_stream + chunk - 1) / chunk;
         e = blockIdx.x / (n_fixed * chunks);
         const int rem = blockIdx.x - e * (n_fixed * chunks);
         fixed = rem / chunks;
-        t0 = (rem - fixed * chunks) * kWgradChunk;
-        t1 = min(n_stream, t0 + kWgradChunk);
+        t0 = (rem - fixed * chunks) * chunk;
+        t1 = min(n_stream, t0 + chunk);
         seg0 = ws.offsets[e];
         count = ws.counts[e];
         if (seg0 < 0 || seg0 > ws.rows_cap || count < 0) count = 0;
@@ -805,6 +808,148 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad1_kernel(const uint16_t* __rest
     wgrad_tiles<C, false>(la, lb, lx, wk.count, wk.fixed, wk.t0, wk.t1, out, H,
                           [&](int nt, int ni) { return l1_packed_col(nt * C::BN + wn0 + ni * 32, I); }, smem, tid,
                           wm0, wn0, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Weight gradients of experts with few rows, the intermediate operand streamed as fragments
+// ---------------------------------------------------------------------------------------------
+// The intermediate operand (w * act for dW2, dhgu for dW1), split into hi and lo parts, is first
+// rewritten (rows_to_k_major, PACKED) so that each 1 KB block is one MFMA operand: column group
+// n / 32 and 16 rows, lane L holding the 8 consecutive rows from 8 * (L / 32) of column n % 32.
+// The kernel then loads those fragments straight into registers, 16 bytes per lane, with no
+// LDS and no transposes; only the shared token-row operand (dy or x rows gathered through
+// row_pair) goes through LDS, once per workgroup.  A 128 x 128 output tile: with STREAM_A (dW2,
+// A = w act) the four waves split its M rows (each 32 rows x 128 columns), else (dW1, B = dhgu)
+// its N columns (each 128 rows x 32 columns), so every wave streams fragments no other wave
+// needs.  Each 16-deep substep issues the hi products, then the lo ones.  The fragments of tile
+// t + 1 are in flight while tile t multiplies and stores; with one K step of rows (the common
+// case) nothing synchronises the waves after the shared tile is loaded.
+template <bool STREAM_A>
+struct WgFrag {
+    static constexpr int FIX = 4;   // 32-wide blocks of the shared (non-streamed) tile dimension
+    static constexpr int BM = STREAM_A ? 128 : 32 * FIX, BN = STREAM_A ? 32 * FIX : 128, NT = 256;
+    static constexpr int MI = STREAM_A ? 1 : FIX, NI = STREAM_A ? FIX : 1;
+    static constexpr int SHARED_ROWS = STREAM_A ? BN : BM;   // rows (M or N index) of the LDS tile
+    static constexpr int LDS_BYTES = SHARED_ROWS * BK * 2;
+    static constexpr int NFRAG = 2 * (BK / 16);              // hi and lo fragment of each substep
+    static constexpr int CHUNK = 8;                           // output tiles per workgroup
+};
+
+template <bool STREAM_A>
+__global__ __launch_bounds__(256, 3) void wgrad_frag_kernel(const uint16_t* __restrict__ tok,
+                                                            const uint16_t* __restrict__ p_hi,
+                                                            const uint16_t* __restrict__ p_lo, Dims d, Ws ws,
+                                                            uint16_t* __restrict__ out) {
+    using W = WgFrag<STREAM_A>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = d.H, I = d.I;
+    const int M = STREAM_A ? I : H, N = STREAM_A ? H : 2 * I;   // packed reduction index, packed column
+    const WgradWork wk(ws, STREAM_A ? N / W::BN : M / W::BM, STREAM_A ? M / W::BM : N / W::BN, W::CHUNK);
+    // rows of the expert inside its segment (the tables keep count within it; clamped for safety)
+    int count = wk.count;
+    {
+        const int64_t seg1 = ws.offsets[wk.e + 1];
+        if (seg1 - wk.seg0 < count) count = static_cast<int>(max(seg1 - wk.seg0, static_cast<int64_t>(0)));
+    }
+    const int nk = (count + BK - 1) / BK;
+    const int64_t Rq = ws.rows_cap / 16;                        // fragment blocks per column group
+    uint16_t* o = out + static_cast<int64_t>(wk.e) * M * N;
+
+    TRows<W::SHARED_ROWS, W::NT, GatherTokenSrc> ls;
+    ls.src.base = tok;
+    ls.src.zeros = ws.zeros;
+    ls.src.row_pair = ws.row_pair;
+    ls.src.seg0 = wk.seg0;
+    ls.src.count = count;
+    ls.src.k = d.k;
+    ls.src.H = H;
+    ls.src.npairs = d.T * d.k;
+    ls.m_base = wk.fixed * W::SHARED_ROWS;
+
+    // fragment f = 2 * substep + part of K step kt of streamed tile t: the wave's column group of
+    // the streamed index (STREAM_A: M rows, else N columns); a substep past the expert's rows
+    // reads the zero row instead (its rows are not the expert's)
+    auto frag_addr = [&](int t, int kt, int f) -> const uint16_t* {
+        const int s16 = kt * BK + 16 * (f >> 1);
+        if (s16 >= count) return ws.zeros + (lane & 31) * 8;
+        const int64_t g = (static_cast<int64_t>(t) * (STREAM_A ? W::BM : W::BN) + 32 * wave) >> 5;
+        const int64_t blk = g * Rq + ((wk.seg0 + s16) >> 4);
+        return ((f & 1) ? p_lo : p_hi) + (blk * 64 + lane) * 8;
+    };
+    bf16x8_t fr[2][W::NFRAG];
+    auto load_frags = [&](int slot, int t, int kt) {
+#pragma unroll
+        for (int f = 0; f < W::NFRAG; ++f) fr[slot][f] = *reinterpret_cast<const bf16x8_t*>(frag_addr(t, kt, f));
+    };
+    f32x16_t acc[W::MI * W::NI];
+    auto compute = [&](int slot) {
+#pragma unroll
+        for (int sub = 0; sub < BK / 16; ++sub) {
+            bf16x8_t sh[W::MI * W::NI];   // shared-operand fragments of this substep (LDS)
+            const int ch = 2 * sub + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < W::MI * W::NI; ++i)
+                sh[i] = *reinterpret_cast<const bf16x8_t*>(smem + lds_off(i * 32 + (lane & 31), ch));
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+#pragma unroll
+                for (int i = 0; i < W::MI * W::NI; ++i) {
+                    const bf16x8_t f = fr[slot][2 * sub + part];
+                    acc[i] = STREAM_A ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, sh[i], acc[i], 0, 0, 0)
+                                      : __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[i], f, acc[i], 0, 0, 0);
+                }
+        }
+    };
+    auto zero = [&]() {
+#pragma unroll
+        for (int i = 0; i < W::MI * W::NI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+    };
+    auto store = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < W::MI * W::NI; ++i) {
+            // STREAM_A: M rows 32 * wave of streamed M tile t, N block i of the fixed N tile;
+            // else: M block i of the fixed M tile, N columns 32 * wave of streamed N tile t
+            const int64_t m0 = STREAM_A ? static_cast<int64_t>(t) * W::BM + 32 * wave
+                                        : static_cast<int64_t>(wk.fixed) * W::BM + 32 * i;
+            const int64_t n0 = STREAM_A ? static_cast<int64_t>(wk.fixed) * W::BN + 32 * i
+                                        : static_cast<int64_t>(t) * W::BN + 32 * wave;
+            store_packed_block(o, M, n0, m0, acc[i], lane);
+        }
+    };
+
+    if (nk <= 1) {
+        ls.template load<0>(0, tid);
+        load_frags(0, wk.t0, 0);
+        ls.template store<0>(smem, tid);
+        lds_barrier();
+        for (int t = wk.t0; t < wk.t1; t += 2) {
+            load_frags(1, min(t + 1, wk.t1 - 1), 0);   // unconditional: exact wait counts
+            zero();
+            if (nk == 1) compute(0);
+            store(t);
+            if (t + 1 >= wk.t1) break;
+            load_frags(0, min(t + 2, wk.t1 - 1), 0);
+            zero();
+            if (nk == 1) compute(1);
+            store(t + 1);
+        }
+    } else {
+        for (int t = wk.t0; t < wk.t1; ++t) {
+            zero();
+            for (int kt = 0; kt < nk; ++kt) {
+                ls.template load<0>(kt, tid);
+                load_frags(0, t, kt);
+                lds_barrier();   // every wave's reads of the previous step are done
+                ls.template store<0>(smem, tid);
+                lds_barrier();
+                compute(0);
+            }
+            store(t);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -987,10 +1132,11 @@ hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint1
 // block (n / 32, r / 16) at (n / 32 * (R_max / 16) + r / 16) * 1 KB, lane n % 32 + 32 * ((r / 8) % 2)
 // holding the 8 rows of r's octet, n the packed column of c).  Sources: ws wact rows (the
 // weighted activation, hi part), the token rows of x or dy through row_pair, or ws dhgu rows
-// (hi part, packed by L1 column).  With hundreds of rows per expert the weight gradients sum
-// enough products that one bf16 rounding of the intermediate operand averages out, so these
-// paths take the hi parts only.
-enum RowsSrc { kWactRows, kTokenRows, kDhguRows };
+// (packed by L1 column), hi or lo parts.  With hundreds of rows per expert the weight gradients
+// sum enough products that one bf16 rounding of the intermediate operand averages out, so the
+// forward-pipeline paths take the hi parts only; the few-rows kernels (wgrad_frag_kernel) take
+// both, in the PACKED layout.
+enum RowsSrc { kWactRows, kWactLoRows, kTokenRows, kDhguRows, kDhguLoRows };
 
 template <int SRC, bool PACKED>
 __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __restrict__ tok, Dims d, Ws ws, int W,
@@ -1015,7 +1161,9 @@ __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __
             if (p >= 0 && p < npairs) {
                 const uint16_t* src;
                 if constexpr (SRC == kWactRows) src = ws.wact + r * W;
+                else if constexpr (SRC == kWactLoRows) src = ws.wact_lo + r * W;
                 else if constexpr (SRC == kDhguRows) src = ws.dhgu + r * W;
+                else if constexpr (SRC == kDhguLoRows) src = ws.dhgu_lo + r * W;
                 else src = tok + static_cast<int64_t>(p / d.k) * W;
                 v = *reinterpret_cast<const u32x4*>(src + c0 + 8 * ch);
             }
@@ -1031,11 +1179,13 @@ __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __
             for (int j = 0; j < 4; ++j)
                 w4[j] = static_cast<uint32_t>(tile[8 * o + 2 * j][m]) | (static_cast<uint32_t>(tile[8 * o + 2 * j + 1][m]) << 16);
             const int64_t r = r0 + 8 * o;
+            if (r >= Rcap) continue;   // block_m 32: the last 64-row tile may pass R_max by 32 rows
             uint16_t* dp;
             if constexpr (!PACKED) {
                 dp = dst + static_cast<int64_t>(c0 + m) * Rcap + r;
             } else {
-                const int64_t n = SRC == kDhguRows ? l1_packed_col(c0 + m, d.I) : static_cast<int64_t>(c0 + m);
+                const int64_t n = (SRC == kDhguRows || SRC == kDhguLoRows) ? l1_packed_col(c0 + m, d.I)
+                                                                            : static_cast<int64_t>(c0 + m);
                 const int64_t blk = (n >> 5) * (Rcap / 16) + (r >> 4);
                 dp = dst + (blk * 64 + (n & 31) + 32 * ((r >> 3) & 1)) * 8;
             }
@@ -1060,6 +1210,14 @@ static bool wgrad_nt_use(const Dims& d, int M, int N) {
            static_cast<int64_t>(M) + N <= 2 * static_cast<int64_t>(d.H);
 }
 
+// The fragment-streaming weight gradients keep their operands in dead ws regions: dhgu hi (2I x
+// R_max bf16) in ws stage and its lo part in ws dact (R_max x I fp32, the same bytes); w act hi and
+// lo (2 x I x R_max bf16) in ws stage.  That needs I <= H (ws stage is R_max x H fp32) and tiles
+// of 128 (H and I multiples of 128, which the shape check requires).
+static bool wgrad_frag_fits(const Dims& d) {
+    return d.I <= d.H && d.H % WgFrag<false>::BM == 0 && d.H % WgFrag<true>::BN == 0 && d.I % 128 == 0;
+}
+
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const Ws& ws, uint16_t* dw2p, hipStream_t s) {
     if (!ws.wact || !ws.wact_lo) return hipErrorInvalidValue;
     if (wgrad_nt_use(d, d.I, d.H)) {   // dW2 packed like W2: reduction index i (M = I), column h (N = H)
@@ -1069,6 +1227,18 @@ hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const Ws& ws, uint16
         if (e == hipSuccess) e = rows_to_k_major<kTokenRows, true>(d, ws, dy, d.H, bp, s);
         if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.I, d.H, ws, dw2p, s);
         return e;
+    }
+    if (wgrad_frag_fits(d)) {   // w act (hi, lo) in fragment order: 4 * I * R_max bytes of ws stage
+        uint16_t* p_hi = reinterpret_cast<uint16_t*>(ws.stage);
+        uint16_t* p_lo = p_hi + static_cast<int64_t>(d.I) * ws.rows_cap;
+        hipError_t e = rows_to_k_major<kWactRows, true>(d, ws, nullptr, d.I, p_hi, s);
+        if (e == hipSuccess) e = rows_to_k_major<kWactLoRows, true>(d, ws, nullptr, d.I, p_lo, s);
+        if (e != hipSuccess) return e;
+        using W = WgFrag<true>;
+        const int blocks = d.EL * (d.H / W::BN) * ((d.I / W::BM + W::CHUNK - 1) / W::CHUNK);
+        if (blocks <= 0) return hipSuccess;
+        wgrad_frag_kernel<true><<<blocks, W::NT, W::LDS_BYTES, s>>>(dy, p_hi, p_lo, d, ws, dw2p);
+        return hipGetLastError();
     }
     const int blocks = d.EL * (d.H / WG::BN) * ((d.I / WG::BM + kWgradChunk - 1) / kWgradChunk);
     if (blocks <= 0) return hipSuccess;
@@ -1095,6 +1265,18 @@ hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_
         if (e == hipSuccess) e = rows_to_k_major<kDhguRows, true>(d, ws, nullptr, 2 * d.I, bp, s);
         if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.H, 2 * d.I, ws, dw1p, s);
         return e;
+    }
+    if (wgrad_frag_fits(d) && ws.dact) {   // dhgu hi in fragment order in ws stage, lo in ws dact
+        uint16_t* p_hi = reinterpret_cast<uint16_t*>(ws.stage);
+        uint16_t* p_lo = reinterpret_cast<uint16_t*>(ws.dact);
+        hipError_t e = rows_to_k_major<kDhguRows, true>(d, ws, nullptr, 2 * d.I, p_hi, s);
+        if (e == hipSuccess) e = rows_to_k_major<kDhguLoRows, true>(d, ws, nullptr, 2 * d.I, p_lo, s);
+        if (e != hipSuccess) return e;
+        using W = WgFrag<false>;
+        const int blocks = d.EL * (d.H / W::BM) * ((2 * d.I / W::BN + W::CHUNK - 1) / W::CHUNK);
+        if (blocks <= 0) return hipSuccess;
+        wgrad_frag_kernel<false><<<blocks, W::NT, W::LDS_BYTES, s>>>(x, p_hi, p_lo, d, ws, dw1p);
+        return hipGetLastError();
     }
     return wgrad1_launch<WG>(d, x, ws, dw1p, s);
 }
