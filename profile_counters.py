@@ -13,6 +13,7 @@ known / measured on that copy, so the figures are in true HBM bytes whatever uni
         --out-json gpurun_out/bwd.json PASS_DIR [...] > profiles/training_wide_share_counters.md
 
     python profile_counters.py stats TRACE_DIR --title TITLE --command CMD > profiles/<kernel>_<workload>_kernel_stats.md
+    python profile_counters.py occupancy --pass DIR WORKLOAD [--pass DIR WORKLOAD] > profiles/forward_..._occupancy.md
 
 Writes the L1 launch's HBM bytes (read + write) with the hash of the kernel source they were taken
 on (bench.py reports them only while that source is unchanged) and prints a markdown table.  With
@@ -100,9 +101,10 @@ def read_durations(trace_dir):
     return dur
 
 
-def stats_table(trace_dir, title, command, note):
-    """Markdown table of a rocprofv3 --kernel-trace --stats run (every kernel, by total time)."""
-    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+def stats_table(trace_dir, title, command, note, only=""):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (every kernel whose name contains
+    `only`, by total time; percentages of the listed kernels' total)."""
+    rows = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))) if only in r["Name"]]
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     print("# rocprofv3 kernel statistics: %s\n" % title)
     if command:
@@ -118,15 +120,65 @@ def stats_table(trace_dir, title, command, note):
             t / 1e6, 100.0 * t / total))
 
 
+def occupancy(dirs, workloads, command):
+    """CU occupancy of the forward GEMM launches from SQ_WAVE_CYCLES (4-cycle units), SQ_BUSY_CYCLES
+    (summed over the 32 shader engines) and GRBM_GUI_ACTIVE, one pass directory per workload, next
+    to the L1 tile list those workloads produce (M tiles of up to eight 32-row groups per expert, an
+    expert of g > 8 groups cut into ceil(g / 8) tiles of equal size, 256-column N tiles)."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import moe_workloads as mw
+    print("# CU occupancy of the forward GEMMs: uniform against Zipf-skewed routing\n")
+    if command:
+        print("Commands (run from /tmp with TMPDIR=/tmp, repository at $R):\n\n```\n%s\n```\n" % command)
+    print("Busy = 4 x SQ_WAVE_CYCLES / (4 waves x 256 CUs x kernel cycles), kernel cycles = SQ_BUSY_CYCLES / 32: "
+          "the share of the launch during which a CU holds its persistent workgroup's waves.\n")
+    print("| workload | local rows | largest expert | empty experts | L1 tiles by groups per M tile | L1 tiles per CU "
+          "| L1 busy | L2 busy | L1 kernel cycles |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for d, name in zip(dirs, workloads):
+        w = mw.get(name)
+        idx, _ = mw.routing(w, 0)
+        ids = idx.reshape(-1).astype(np.int64)
+        ids = ids[(ids >= w.e_lo) & (ids < w.e_lo + w.EL)] - w.e_lo
+        counts = np.bincount(ids, minlength=w.EL)
+        tiles = collections.Counter()
+        for g in (counts + 31) // 32:
+            if g:
+                mt = -(-int(g) // 8)
+                tiles[-(-int(g) // mt)] += mt * (2 * w.I // 256)
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            k = kind_of(r["Kernel_Name"])
+            if k in ("l1_kernel", "l2_kernel"):
+                agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        busy, cyc = {}, {}
+        for k, cs in agg.items():
+            v = {c: sum(x) / len(x) for c, x in cs.items()}
+            cyc[k] = v["SQ_BUSY_CYCLES"] / 32
+            busy[k] = 4 * v["SQ_WAVE_CYCLES"] / (4 * 256 * cyc[k])
+        print("| %s | %d | %d | %d | %s | %.2f | %.1f%% | %.1f%% | %.0f |" % (
+            name, counts.sum(), counts.max(), int((counts == 0).sum()),
+            ", ".join("%d: %d" % (q, n) for q, n in sorted(tiles.items())), sum(tiles.values()) / 256,
+            100 * busy.get("l1_kernel", float("nan")), 100 * busy.get("l2_kernel", float("nan")), cyc.get("l1_kernel", 0)))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "occupancy":
+        ap = argparse.ArgumentParser(prog="profile_counters.py occupancy")
+        ap.add_argument("--pass", dest="passes", nargs=2, action="append", metavar=("DIR", "WORKLOAD"), required=True)
+        ap.add_argument("--command", default="")
+        a = ap.parse_args(sys.argv[2:])
+        return occupancy([p[0] for p in a.passes], [p[1] for p in a.passes], a.command)
     if len(sys.argv) > 1 and sys.argv[1] == "stats":
         ap = argparse.ArgumentParser(prog="profile_counters.py stats")
         ap.add_argument("trace")
         ap.add_argument("--title", required=True)
         ap.add_argument("--command", default="")
         ap.add_argument("--note", default="")
+        ap.add_argument("--only", default="", help="list only kernels whose name contains this")
         a = ap.parse_args(sys.argv[2:])
-        return stats_table(a.trace, a.title, a.command, a.note)
+        return stats_table(a.trace, a.title, a.command, a.note, a.only)
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--out-json", required=True)
