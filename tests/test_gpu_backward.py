@@ -13,6 +13,8 @@ checked link by link: dhgu against the oracle's SwiGLU transpose evaluated on th
 pre-activation and dact.  Tokens with no local pair (dx) and pairs this GPU does not handle
 (d(topk_w)) must be exact zeros.
 """
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 import torch
@@ -325,3 +327,27 @@ def test_max_local_experts_forward_and_backward():
         check_bf16(g1[e], dW1[i], TOL, "dW1[%d] (EL = 1024)" % e)
         check_bf16(g2[e], dW2[i], TOL, "dW2[%d] (EL = 1024)" % e)
     check_token_grads(w, d, ns, np.arange(w.T), "(EL = 1024)")
+
+
+def test_autograd_op_matches_the_entry_points():
+    """moe_layer (one torch.autograd op over moe_forward / moe_backward) gives the entry points' y,
+    dx, d(topk_w), dW1 and dW2 bit for bit, and y and the gradients agree with the oracle."""
+    w = REDUCED[1]
+    d = mw.inputs(w, 17)
+    ns = run_forward_backward(w, d, 64)
+    x = ns.x.clone().requires_grad_(True)
+    tw = ns.wts.clone().requires_grad_(True)
+    W1p = ns.W1p.clone().requires_grad_(True)
+    W2p = ns.W2p.clone().requires_grad_(True)
+    ws = moe.alloc_workspace(ns.shape)
+    y = moe.moe_layer(x, ns.idx, tw, W1p, W2p, ns.shape, ws)
+    y.backward(ns.dy)
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach().view(torch.int16), ns.y.view(torch.int16))
+    assert torch.equal(x.grad.view(torch.int16), ns.dx.view(torch.int16))
+    assert torch.equal(tw.grad, ns.dtw)
+    assert torch.equal(W1p.grad.view(torch.int16), ns.dW1p.view(torch.int16))
+    assert torch.equal(W2p.grad.view(torch.int16), ns.dW2p.view(torch.int16))
+    ref = oracle.forward(d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], E=w.E, e_lo=w.e_lo)
+    check_bf16(f64_host(y.detach()), ref, TOL, "y (autograd op)")
+    check_token_grads(w, d, SimpleNamespace(dx=x.grad, dtw=tw.grad), np.arange(w.T), "(autograd op)")

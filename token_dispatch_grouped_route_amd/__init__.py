@@ -395,3 +395,44 @@ def mx_gemm2_combine(shape, w2q, w2s, topk_w, ws, y, stream=None):
     _check(lib().moe_mx_gemm2_combine(ctypes.byref(shape), _ptr(w2q, torch.uint8, "w2q", nn["w2q"]), _ptr(w2s, torch.uint8, "w2s", nn["w2s"]),
                                       _ptr(topk_w, torch.float32, "topk_w", nn["topk_w"]), p, n, _ptr(y, torch.bfloat16, "y", nn["y"]),
                                       _stream(stream)), "moe_mx_gemm2_combine")
+
+
+# ------------------------------------------------------------------------------------------------
+# One autograd op over the C ABI ("Mega MoE" page, Key points: the layer is one differentiable op
+# that takes the routing as an input)
+# ------------------------------------------------------------------------------------------------
+class _MoeLayer(torch.autograd.Function):
+    """y = moe_forward(x, topk_idx, topk_w, w1p, w2p) with shape.train set; backward runs
+    moe_backward for dx, d(topk_w), dW1p and dW2p.  Only marshalling: every step is a library call."""
+
+    @staticmethod
+    def forward(ctx, x, topk_w, w1p, w2p, topk_idx, shape, ws):
+        y = torch.empty(shape.T, shape.H, dtype=torch.bfloat16, device=x.device)
+        forward(shape, x, topk_idx, topk_w, w1p, w2p, ws, y)
+        ctx.save_for_backward(x, topk_w, w1p, w2p)
+        ctx.shape, ctx.ws = shape, ws
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, topk_w, w1p, w2p = ctx.saved_tensors
+        shape, ws = ctx.shape, ctx.ws
+        dy = dy.contiguous()
+        dw1p, dw2p = torch.empty_like(w1p), torch.empty_like(w2p)
+        dx = torch.empty_like(x)
+        dtw = torch.empty_like(topk_w)
+        backward(shape, x, dy, topk_w, w2p, ws, dw1p, dw2p, w1p=w1p, dx=dx, dtopk_w=dtw)
+        return dx, dtw, dw1p, dw2p, None, None, None
+
+
+def moe_layer(x, topk_idx, topk_w, w1p, w2p, shape, ws=None):
+    """The expert layer as one autograd op: y [T, H] bf16 from x [T, H] bf16, external routing
+    (topk_idx int32 [T, k], topk_w fp32 [T, k]) and the packed weights (pack_weights).  Gradients
+    flow to x, topk_w, w1p and w2p (the last two in the packed layout).  shape.train must be set;
+    ws (alloc_workspace(shape)) holds the saved activations until backward runs, so one ws serves
+    one layer call at a time."""
+    if not shape.train:
+        raise MoeError("moe_layer needs a train shape (the backward reads the saved activations)")
+    if ws is None:
+        ws = alloc_workspace(shape, x.device)
+    return _MoeLayer.apply(x, topk_w, w1p, w2p, topk_idx, shape, ws)
