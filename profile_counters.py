@@ -35,14 +35,17 @@ COPY_BYTES = 1 << 30   # bench.py --copy-calibration: one 1 GiB buffer copied to
 COMMON = (("combine_finish", "combine finish (multi-pair tokens)"),
           ("route_count", "prologue: count"), ("route_scan", "prologue: scan"),
           ("route_place", "prologue: place"))
-BWD = (("dgrad_nt_kernel", "L2 dgrad NN on the forward pipeline + SwiGLU transpose (many rows)"),
+BWD = (("dgrad_tile_kernel<moe::(anonymous namespace)::TrTile",
+        "L2 dgrad NN, packed W2 read transposed + SwiGLU transpose + d(topk_w) partials + w*act"),
+       ("dgrad_tile_kernel", "L2 dgrad NN on repacked W2 + SwiGLU transpose (many rows)"),
+       ("l2_kernel<moe::(anonymous namespace)::TrTile", "L1 dgrad NN, packed W1 read transposed + combine rows"),
        ("wgrad_nt_kernel", "dW1 / dW2 TN on the forward pipeline (many rows)"),
-       ("dgrad1_kernel", "L1 dgrad NN + combine rows"),
-       ("dgrad_kernel", "L2 dgrad NN + SwiGLU transpose + d(topk_w) partials + w*act"),
-       ("wgrad2_kernel", "dW2 TN, variable K, hi/lo operand"),
-       ("wgrad1_kernel", "dW1 TN, variable K, hi/lo operand"),
+       ("wgrad_frag_kernel<true>", "dW2 TN, variable K, hi/lo fragment operand"),
+       ("wgrad_frag_kernel<false>", "dW1 TN, variable K, hi/lo fragment operand"),
+       ("wgrad2_kernel", "dW2 TN, variable K, hi/lo operand (LDS tiles)"),
+       ("wgrad1_kernel", "dW1 TN, variable K, hi/lo operand (LDS tiles)"),
        ("repack_t_kernel", "weight repack (many rows)"),
-       ("rows_to_k_major_kernel", "row transposes (many rows)"),
+       ("rows_to_k_major_kernel", "row transforms of the weight-gradient operands"),
        ("dtopk_w_finish", "d(topk_w) finish"))
 VARIANTS = {
     "bf16": {"title": "DeepSeek-V3 share forward", "src": GEMM_SRC, "l1": "l1_kernel", "workload": "dsv3_share_fwd",

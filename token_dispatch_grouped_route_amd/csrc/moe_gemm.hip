@@ -1,30 +1,16 @@
-// Backward grouped GEMMs of the MoE expert layer on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation); the forward GEMMs are in moe_grouped.hip.
+// Weight gradients of the MoE expert layer on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation), the row transforms and weight repacks they and the many-rows dgrads use, and the
+// dispatch of the backward GEMMs ("Mega MoE" page, Pipeline, backward).  The dgrads and the
+// many-rows weight gradients run on the forward's pipeline in moe_grouped.hip.
 //
-// One core serves these GEMMs: a workgroup computes a BM x BN tile with WM x WN wavefronts, each
-// wave a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.  K advances 64 elements per step.  Both
-// operand tiles live in LDS K-contiguous (128 bytes per row, 16-byte chunks XOR-swizzled by
-// row so a wave's fragment reads spread over the banks), double-buffered so the global loads
-// of step k+1 are in flight while the MFMAs of step k run; one barrier per step.  The weight
-// gradients, whose K is one expert's rows (often a single step), use one LDS buffer instead, for
-// more resident workgroups per CU.
-//
-// Loaders differ per operand:
-//   KRows  rows that are K-contiguous in memory (token rows, activations); 16-byte vector
-//          loads, 8 lanes per 128-byte row segment.  A row may come from a gather (dy rows
-//          through row_pair) or be absent (zeros).
-//   TRows  operands stored with M (or N) contiguous in runs of 8 and K strided (the NN/TN
-//          products of the backward, and the packed W2 read transposed): each thread loads 4
-//          K-rows x 8 elements and transposes them in registers into 8 rows x 4 K before the
-//          LDS store.
-//
-// Kernels ("Mega MoE" page, Pipeline, backward):
-//   dgrad   L2 dgrad NN, row weight and optional SwiGLU transpose in the epilogue, which also
-//           writes the weighted activation rows w * act for dW2; optionally the per-row
-//           partials of d(topk_w) = <dy[t], o_p> = <dy[t] W2^T, act_p>
-//   dgrad1  L1 dgrad NN over the packed W1, rows summed back to token order (the combine)
-//   wgrad2  dW2 = (w act)^T dy, K = rows of the expert (variable K), TN
-//   wgrad1  dW1 = dHgu^T X with X re-gathered from x, TN
+// Kernels:
+//   wgrad_frag  dW2 = (w act)^T dy and dW1 = dHgu^T X (X re-gathered from x) of experts with few
+//               rows: K is one expert's rows; the streamed operand (w act, or dHgu) comes as
+//               hi/lo MFMA fragments prepared by rows_to_k_major, the token rows through LDS
+//   wgrad2, wgrad1  the same products with both operand tiles in LDS, for shapes the fragment
+//               kernel does not fit (I > H)
+//   rows_to_k_major, repack_t  operand transforms of the weight gradients and of the many-rows
+//               dgrads
 //
 // Precision of the intermediate operands.  The saved pre-activation is fp32, so the row gradients
 // (dHgu) and the weighted activation (w * act) are formed in fp32 and stored as two bf16 arrays,
@@ -37,11 +23,10 @@
 // Weight gradients are written in the packed layout of the weights they belong to, whole 1 KB
 // blocks per store instruction (the tile's M index runs along the packed reduction index).
 //
-// The dgrad launch is persistent: a fixed grid (CUs x occupancy) walks the tile list whose
-// length R / BM * n_tiles is read from the workspace on the device, so the host never needs R.
-// The list is ordered expert by expert, and inside an expert N-panel by N-panel with the
-// expert's M tiles adjacent; it is cut into one contiguous chunk per XCD (the hardware places
-// workgroup b on XCD b mod 8, each XCD with its own L2).
+// The LDS tiles of wgrad2 / wgrad1 are K-contiguous (128 bytes per row, 16-byte chunks
+// XOR-swizzled by row so a wave's fragment reads spread over the banks); their operands are stored
+// with M (or N) contiguous in runs of 8 and K strided, so the TRows loader moves 4 K-rows x 8
+// elements per thread and transposes them in registers into 8 rows x 4 K before the LDS store.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -49,6 +34,7 @@
 namespace moe {
 
 constexpr int BK = 64;
+constexpr int kXcds = 8;   // the hardware places workgroup b on XCD b mod 8, each with its own L2
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes of staged operand
 
@@ -62,11 +48,9 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 template <int BM_, int BN_, int WM_, int WN_, int PF_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    // K steps of global loads in flight ahead of the MFMAs (1 or 2; 0: one step, one LDS buffer,
-    // for launches of many short-K tiles where occupancy matters more than overlap)
+    // 0: one LDS buffer (launches of many short-K tiles, where occupancy matters more than
+    // overlap); else two
     static constexpr int PF = PF_;
-    // workgroups per CU the register allocation must allow (the LDS of two fits in 160 KB)
-    static constexpr int MIN_WG = (BM * BN <= 128 * 128) ? 2 : 1;
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int MI = TM / 32, NI = TN / 32;
@@ -80,34 +64,6 @@ struct Cfg {
 // ---------------------------------------------------------------------------------------------
 // Operand loaders
 // ---------------------------------------------------------------------------------------------
-template <int ROWS, int NT>
-struct KRows {
-    static constexpr int PER = ROWS * 8 / NT;   // 16-byte chunks per thread per K step
-    const char* base;                           // uniform base of every row of this operand
-    uint32_t off[PER];                          // byte offset of the thread's chunk of each row
-    uint32_t keep;                              // bit i clear: row i is padding and reads as zeros
-    u32x4 v[2][PER];                            // two register slots: steps k+1 and k+2 in flight
-
-    // chunk q = tid + i*NT covers row q/8, chunk q%8
-    __device__ __forceinline__ static int row_of(int tid, int i) { return (tid + i * NT) >> 3; }
-    __device__ __forceinline__ static int chunk_of(int tid, int i) { return (tid + i * NT) & 7; }
-
-    template <int S>
-    __device__ __forceinline__ void load(int kt, int) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            v[S][i] = *reinterpret_cast<const u32x4*>(base + off[i] + kt * (BK * 2));
-    }
-    template <int S>
-    __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const uint32_t m = ((keep >> i) & 1u) ? 0xffffffffu : 0u;
-            *reinterpret_cast<u32x4*>(lds + lds_off(row_of(tid, i), chunk_of(tid, i))) = v[S][i] & m;
-        }
-    }
-};
-
 // Operand tile of ROWS rows (the M or N index) x BK, stored in memory with the tile's index
 // contiguous in runs of 8: elements (m .. m+7, k) = Src::chunk(k, m_base + m) for m a multiple of
 // 8.  Every chunk is a valid address (absent rows point at the workspace's
@@ -174,24 +130,6 @@ __device__ __forceinline__ void read_frags(const char* lA, const char* lB, bf16x
         b[j] = *reinterpret_cast<const bf16x8_t*>(lB + lds_off(wn0 + j * 32 + (lane & 31), ch));
 }
 
-// The fragments of 16-k substep s+1 are read from LDS before the MFMAs of substep s.
-template <class C>
-__device__ __forceinline__ void mma_step(const char* lA, const char* lB, f32x16_t (&acc)[C::MI][C::NI],
-                                         int wm0, int wn0, int lane) {
-    constexpr int KS = BK / 16;
-    bf16x8_t a[2][C::MI], b[2][C::NI];
-    read_frags<C>(lA, lB, a[0], b[0], 0, wm0, wn0, lane);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) read_frags<C>(lA, lB, a[(s + 1) & 1], b[(s + 1) & 1], s + 1, wm0, wn0, lane);
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
-    }
-}
-
 // mma_step with one operand given as hi + lo bf16 tiles (the lo tile at lX, laid out like the
 // operand it completes): acc += A * B + X * B (SPLIT_A) or A * B + A * X.  Each 16-deep substep
 // issues the hi products of every accumulator first, then the lo ones, so no MFMA waits on the
@@ -227,325 +165,6 @@ __device__ __forceinline__ void mma_step_split(const char* lA, const char* lB, c
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i], b[s & 1][j], acc[i][j], 0, 0, 0);
                 else
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], x[j], acc[i][j], 0, 0, 0);
-            }
-    }
-}
-
-// One K step of the pipeline.  On entry LDS buffer S holds step kt, register slot S^1 holds step
-// kt+1 (loads in flight) and slot S is free: it receives step kt+2, then the MFMAs consume buffer
-// S, then slot S^1 moves to LDS buffer S^1 (read by nobody since the previous barrier).
-// The loads are unconditional (past the end they re-read the last step, which is never stored):
-// a load under a branch would make the compiler's wait counts conservative on the merged path and
-// wait for the loads just issued, serialising the pipeline.
-template <class C, int S, class LA, class LB>
-__device__ __forceinline__ void pipe_step(LA& la, LB& lb, int kt, int nk, char* smem,
-                                          f32x16_t (&acc)[C::MI][C::NI], int tid, int wm0, int wn0, int lane) {
-    const int kl = min(kt + 2, nk - 1);
-    la.template load<S>(kl, tid);
-    lb.template load<S>(kl, tid);
-    const char* cur = smem + S * C::STAGE_BYTES;
-    mma_step<C>(cur, cur + C::A_BYTES, acc, wm0, wn0, lane);
-    if (kt + 1 < nk) {
-        char* nxt = smem + (S ^ 1) * C::STAGE_BYTES;
-        la.template store<S ^ 1>(nxt, tid);
-        lb.template store<S ^ 1>(nxt + C::A_BYTES, tid);
-    }
-    lds_barrier();
-}
-
-template <class C, class LA, class LB>
-__device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, char* smem, f32x16_t (&acc)[C::MI][C::NI],
-                                          int tid, int wm0, int wn0, int lane) {
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    if (nk <= 0) return;
-    la.template load<0>(0, tid);
-    lb.template load<0>(0, tid);
-    if constexpr (C::PF == 2) {
-        la.template load<1>(min(1, nk - 1), tid);
-        lb.template load<1>(min(1, nk - 1), tid);
-    }
-    la.template store<0>(smem, tid);
-    lb.template store<0>(smem + C::A_BYTES, tid);
-    lds_barrier();
-    if constexpr (C::PF == 0) {
-        for (int kt = 0; kt < nk; ++kt) {
-            const bool more = kt + 1 < nk;
-            if (more) {
-                la.template load<0>(kt + 1, tid);
-                lb.template load<0>(kt + 1, tid);
-            }
-            mma_step<C>(smem, smem + C::A_BYTES, acc, wm0, wn0, lane);
-            if (more) {
-                lds_barrier();   // every wave's fragment reads of step kt are done
-                la.template store<0>(smem, tid);
-                lb.template store<0>(smem + C::A_BYTES, tid);
-                lds_barrier();
-            }
-        }
-    } else if constexpr (C::PF == 2) {
-        int kt = 0;
-        for (; kt + 1 < nk; kt += 2) {
-            pipe_step<C, 0>(la, lb, kt, nk, smem, acc, tid, wm0, wn0, lane);
-            pipe_step<C, 1>(la, lb, kt + 1, nk, smem, acc, tid, wm0, wn0, lane);
-        }
-        if (kt < nk) pipe_step<C, 0>(la, lb, kt, nk, smem, acc, tid, wm0, wn0, lane);
-    } else {
-        // one register slot: step kt+1 loads while step kt computes, then goes to the other buffer
-        for (int kt = 0; kt < nk; ++kt) {
-            const bool more = kt + 1 < nk;
-            if (more) {
-                la.template load<0>(kt + 1, tid);
-                lb.template load<0>(kt + 1, tid);
-            }
-            const char* cur = smem + (kt & 1) * C::STAGE_BYTES;
-            mma_step<C>(cur, cur + C::A_BYTES, acc, wm0, wn0, lane);
-            if (more) {
-                char* nxt = smem + ((kt + 1) & 1) * C::STAGE_BYTES;
-                la.template store<0>(nxt, tid);
-                lb.template store<0>(nxt + C::A_BYTES, tid);
-            }
-            lds_barrier();
-        }
-    }
-}
-
-// Row (within the tile) and column (within the wave's N range) of accumulator element r of
-// the 32x32 block: 4 groups of 8 rows, the lane's half picks 4 of them, lane%32 is the column.
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// ---------------------------------------------------------------------------------------------
-// Tile schedule of the row-tiled launches
-// ---------------------------------------------------------------------------------------------
-constexpr int kXcds = 8;
-
-// The positions [begin, end) (stride step) of the tile list that this workgroup runs: one
-// contiguous chunk per XCD when the grid covers the XCDs evenly, else a plain round robin.
-struct TileRange {
-    int begin, end, step;
-    __device__ explicit TileRange(int total) {
-        const int G = gridDim.x;
-        if (G % kXcds == 0) {
-            const int x = blockIdx.x % kXcds;
-            const int chunk = (total + kXcds - 1) / kXcds;
-            begin = x * chunk + blockIdx.x / kXcds;
-            end = min(total, (x + 1) * chunk);
-            step = G / kXcds;
-        } else {
-            begin = blockIdx.x;
-            end = total;
-            step = G;
-        }
-    }
-};
-
-// Position t of the tile list -> (M tile, N tile).  Expert e owns positions
-// [m0 * n_tiles, (m0 + mc) * n_tiles) where its segment is M tiles [m0, m0 + mc), so the expert
-// is found from the M tile at t / n_tiles; inside its run the M index varies fastest.
-__device__ __forceinline__ void tile_at(const Ws& ws, const Dims& d, int n_tiles, int t, int& mt, int& nt) {
-    const int m = t / n_tiles;
-    mt = m;
-    nt = t - m * n_tiles;
-    const int e = ws.tile_expert[m];
-    if (e < 0 || e >= d.EL) return;   // the caller skips this tile
-    const int m0 = ws.offsets[e] / d.BM;
-    const int mc = (ws.offsets[e + 1] - ws.offsets[e]) / d.BM;
-    if (mc < 1 || m < m0 || m >= m0 + mc) return;   // tables not from one prologue: keep M-major
-    const int local = t - m0 * n_tiles;
-    nt = local / mc;
-    mt = m0 + (local - nt * mc);
-}
-
-// ---------------------------------------------------------------------------------------------
-// dgrad: L2 dgrad (NN) with the row weight and optional SwiGLU transpose in the epilogue
-// ---------------------------------------------------------------------------------------------
-struct W2ColSrc {   // B operand of the dgrad: (K = h, N = i) of expert e's packed W2
-    const uint16_t* base;   // w2p + e*H*I
-    int I;
-    __device__ __forceinline__ const uint16_t* chunk(int k, int m) const { return base + frag_index(k, m, I); }
-};
-
-// The GEMM runs on the plain dy rows, so the accumulator is dA'[r] = dy[t] @ W2[e]^T and the
-// row weight enters in the epilogue (dA = w * dA').  The epilogue recomputes the activation
-// a = silu(g) * u in fp32 from the saved fp32 pre-activation and writes w * a as a hi/lo bf16
-// pair (the dW2 operand).  With topk_w_grad it also forms the sum over the tile's columns of
-// dA'[r, c] * a[r, c]: summed over the N tiles (in tile order, by the finish kernel) that is
-// <dy[t], o_p>, the gradient of the routing weight, because o_p = a_p @ W2[e].  64-row tiles fit
-// three waves per SIMD, which keeps more weight loads in flight per CU.
-template <class C>
-__global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad_kernel(const uint16_t* __restrict__ dy,
-                                                      const float* __restrict__ topk_w,
-                                                      const uint16_t* __restrict__ w2p, Dims d, Ws ws,
-                                                      int fuse, int topk_w_grad) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    float* s_w = reinterpret_cast<float*>(smem + C::LDS_BYTES);
-    float* s_part = s_w + C::BM;   // [WN][BM] row sums of dA' * act over each wave's columns
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
-    const int H = d.H, I = d.I;
-    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);   // R / BM, clamped to the tables
-    const int n_tiles = I / C::BN;
-    const int total = m_tiles * n_tiles;
-    const int npairs = d.T * d.k;
-
-    const TileRange tr(total);
-    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
-        int mt, nt;
-        tile_at(ws, d, n_tiles, tile, mt, nt);
-        const int e = ws.tile_expert[mt];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
-        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
-
-        KRows<C::BM, C::NT> la;
-        la.base = reinterpret_cast<const char*>(dy);
-        la.keep = 0;
-#pragma unroll
-        for (int i = 0; i < la.PER; ++i) {
-            const int p = ws.row_pair[row0 + la.row_of(tid, i)];
-            const bool ok = p >= 0 && p < npairs;
-            la.keep |= static_cast<uint32_t>(ok) << i;
-            la.off[i] = 2u * (static_cast<uint32_t>(ok ? p / d.k : 0) * H + 8 * la.chunk_of(tid, i));
-        }
-        TRows<C::BN, C::NT, W2ColSrc> lb;
-        lb.src.base = w2p + static_cast<int64_t>(e) * H * I;
-        lb.src.I = I;
-        lb.m_base = nt * C::BN;
-        f32x16_t acc[C::MI][C::NI];
-        lds_barrier();
-        for (int r = tid; r < C::BM; r += C::NT) {
-            const int p = ws.row_pair[row0 + r];
-            s_w[r] = (p >= 0 && p < npairs) ? topk_w[p] : 0.0f;
-        }
-        gemm_tile<C>(la, lb, H / BK, smem, acc, tid, wm0, wn0, lane);
-
-#pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = wm0 + mi * 32 + acc_row(r, lane);
-                const int64_t row = row0 + rl;
-                const float w = s_w[rl];
-                float part = 0.0f;
-#pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni) {
-                    const int c = nt * C::BN + wn0 + ni * 32 + (lane & 31);
-                    const float da = w * acc[mi][ni][r];
-                    const float g = ws.hgu[row * 2 * I + c];
-                    const float u = ws.hgu[row * 2 * I + I + c];
-                    const float sg = 1.0f / (1.0f + __expf(-g));
-                    const float a = g * sg * u;
-                    if (topk_w_grad) part += acc[mi][ni][r] * a;
-                    split_bf16(w * a, ws.wact[row * I + c], ws.wact_lo[row * I + c]);
-                    if (fuse) {
-                        split_bf16(da * u * sg * (1.0f + g * (1.0f - sg)), ws.dhgu[row * 2 * I + c],
-                                   ws.dhgu_lo[row * 2 * I + c]);
-                        split_bf16(da * g * sg, ws.dhgu[row * 2 * I + I + c], ws.dhgu_lo[row * 2 * I + I + c]);
-                    } else {
-                        ws.dact[row * I + c] = da;
-                    }
-                }
-                if (topk_w_grad) {   // uniform: every lane takes part in the shuffles
-                    // lanes 0-31 hold row rl of 32 columns, lanes 32-63 row rl + 4: sum each half
-#pragma unroll
-                    for (int o = 16; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-                    if ((lane & 31) == 0) s_part[(wave % C::WN) * C::BM + rl] = part;
-                }
-            }
-        if (topk_w_grad) {
-            lds_barrier();
-            for (int r = tid; r < C::BM; r += C::NT) {
-                float sum = 0.0f;
-#pragma unroll
-                for (int wn = 0; wn < C::WN; ++wn) sum += s_part[wn * C::BM + r];
-                ws.dtw_part[(row0 + r) * n_tiles + nt] = sum;
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
-// dgrad1: L1 dgrad (NN) and the combine of its rows back to token order
-// ---------------------------------------------------------------------------------------------
-struct W1ColSrc {   // B operand of the L1 dgrad: (K = L1 output column, N = h) of expert e's packed W1
-    const uint16_t* base;   // w1p + e*2I*H
-    int H, I;
-    __device__ __forceinline__ const uint16_t* chunk(int k, int m) const {
-        return base + frag_index(l1_packed_col(k, I), m, H);
-    }
-};
-
-// dX[r] = dhgu[r] @ W1[e]^T (K = 2I in the logical [gate | up] order of dhgu, N = H).  The row
-// of a token's only local pair is stored as bf16 straight into dx[t]; rows of tokens with several
-// local pairs go to their fp32 stage rows, which combine_finish sums in slot order (and it zeroes
-// tokens with no local pair), so dx is deterministic.
-template <class C>
-__global__ __launch_bounds__(C::NT, C::BM == 64 ? 3 : 1) void dgrad1_kernel(const uint16_t* __restrict__ w1p, Dims d, Ws ws,
-                                                       uint16_t* __restrict__ dx) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    int* s_tok = reinterpret_cast<int*>(smem + C::LDS_BYTES);   // token of each tile row, -1 padding
-    int* s_one = s_tok + C::BM;                                  // 1: the row is its token's only local pair
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
-    const int H = d.H, I = d.I, N2 = 2 * d.I;
-    const int m_tiles = min(ws.meta[0] / C::BM, ws.num_blocks);
-    const int n_tiles = H / C::BN;
-    const int total = m_tiles * n_tiles;
-    const int npairs = d.T * d.k;
-
-    const TileRange tr(total);
-    for (int tile = tr.begin; tile < tr.end; tile += tr.step) {
-        int mt, nt;
-        tile_at(ws, d, n_tiles, tile, mt, nt);
-        const int e = ws.tile_expert[mt];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
-        const int64_t row0 = static_cast<int64_t>(mt) * C::BM;
-
-        KRows<C::BM, C::NT> la;
-        la.base = reinterpret_cast<const char*>(ws.dhgu + row0 * N2);
-        la.keep = 0;
-#pragma unroll
-        for (int i = 0; i < la.PER; ++i) {
-            const int rl = la.row_of(tid, i);
-            const int p = ws.row_pair[row0 + rl];
-            la.keep |= static_cast<uint32_t>(p >= 0 && p < npairs) << i;
-            la.off[i] = 2u * (static_cast<uint32_t>(rl) * N2 + 8 * la.chunk_of(tid, i));
-        }
-        TRows<C::BN, C::NT, W1ColSrc> lb;
-        lb.src.base = w1p + static_cast<int64_t>(e) * N2 * H;
-        lb.src.H = H;
-        lb.src.I = I;
-        lb.m_base = nt * C::BN;
-        f32x16_t acc[C::MI][C::NI];
-        lds_barrier();
-        for (int r = tid; r < C::BM; r += C::NT) {
-            const int p = ws.row_pair[row0 + r];
-            const bool ok = p >= 0 && p < npairs;
-            const int t = ok ? p / d.k : -1;
-            s_tok[r] = t;
-            s_one[r] = ok && ws.tok_nloc[t] == 1;
-        }
-        gemm_tile<C>(la, lb, N2 / BK, smem, acc, tid, wm0, wn0, lane);
-
-#pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = wm0 + mi * 32 + acc_row(r, lane);
-                const int t = s_tok[rl];
-                if (t < 0) continue;
-                const int64_t row = row0 + rl;
-                const bool one = s_one[rl] != 0;
-#pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni) {
-                    const int c = nt * C::BN + wn0 + ni * 32 + (lane & 31);
-                    const float v = acc[mi][ni][r];
-                    if (one) dx[static_cast<int64_t>(t) * H + c] = f32_to_bf16(v);
-                    else ws.stage[row * H + c] = v;
-                }
             }
     }
 }
@@ -989,25 +608,7 @@ static void allow_lds(K kernel, size_t lds) {
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
 }
 
-using G32 = Cfg<32, 128, 1, 2>;
-using G64 = Cfg<64, 128, 2, 2>;
-using G128 = Cfg<128, 128, 2, 2>;
-using G256 = Cfg<256, 128, 4, 1>;
 using WG = Cfg<128, 128, 2, 2, 0>;   // weight-gradient tiles: K is an expert's rows, often one step
-
-template <class C0>
-static hipError_t dgrad_launch(const Dims& d, const uint16_t* dy, const float* topk_w, const uint16_t* w2p,
-                               const Ws& ws, int fuse, bool topk_w_grad, hipStream_t s) {
-    using C = Cfg<C0::BM, C0::BN, C0::WM, C0::WN, 1>;   // one staging slot: the transposing loader is register-heavy
-    static_assert(C::BN == 128, "d(topk_w) partials are laid out per 128-column N tile");
-    const size_t lds = C::LDS_BYTES + sizeof(float) * C::BM * (1 + C::WN);
-    auto k = dgrad_kernel<C>;
-    allow_lds(k, lds);
-    const int n_tiles = d.I / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
-    k<<<grid, C::NT, lds, s>>>(dy, topk_w, w2p, d, ws, fuse, topk_w_grad ? 1 : 0);
-    return hipGetLastError();
-}
 
 // Expected rows per local expert (T * k / E, uniform routing) from which the backward GEMMs of an
 // expert run on the forward's pipeline instead of the streaming kernels above.
@@ -1052,7 +653,7 @@ __global__ __launch_bounds__(256) void repack_t_kernel(const uint16_t* __restric
     }
 }
 
-// The L2 dgrad of experts with many rows runs on the forward's L1 tile loop (dgrad_nt_kernel) with W2
+// The L2 dgrad of experts with many rows runs on the forward's L1 tile loop (dgrad_tile_kernel) with W2
 // repacked to an (N = i, K = h) operand in ws stage (free during the backward's first GEMM; it
 // holds EL * I * H elements when EL * I <= 2 * R_max).
 static bool dgrad_nt_use(const Dims& d, const Ws& ws) {
@@ -1070,25 +671,7 @@ hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w, 
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? launch_dgrad_nt(d, dy, w2t, topk_w, ws, fuse, topk_w_grad, s) : e;
     }
-    switch (d.BM) {
-        case 32: return dgrad_launch<G32>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
-        case 64: return dgrad_launch<G64>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
-        case 128: return dgrad_launch<G128>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
-        case 256: return dgrad_launch<G256>(d, dy, topk_w, w2p, ws, fuse, topk_w_grad, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <class C0>
-static hipError_t dgrad1_launch(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s) {
-    using C = Cfg<C0::BM, C0::BN, C0::WM, C0::WN, 1>;
-    const size_t lds = C::LDS_BYTES + 2 * sizeof(int) * C::BM;
-    auto k = dgrad1_kernel<C>;
-    allow_lds(k, lds);
-    const int n_tiles = d.H / C::BN;
-    const int grid = persistent_grid(k, C::NT, lds, static_cast<int64_t>(ws.num_blocks) * n_tiles);
-    k<<<grid, C::NT, lds, s>>>(w1p, d, ws, dx);
-    return hipGetLastError();
+    return launch_dgrad_tr(d, dy, w2p, topk_w, ws, fuse, topk_w_grad, s);
 }
 
 // The L1 dgrad of experts with many rows runs as the forward's L2 (NT, with its combine into
@@ -1111,16 +694,8 @@ hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint1
         if (e == hipSuccess) e = launch_combine_finish(d, ws, dx, s);
         return e;
     }
-    hipError_t e;
-    switch (d.BM) {
-        case 32: e = dgrad1_launch<G32>(d, w1p, ws, dx, s); break;
-        case 64: e = dgrad1_launch<G64>(d, w1p, ws, dx, s); break;
-        case 128: e = dgrad1_launch<G128>(d, w1p, ws, dx, s); break;
-        case 256: e = dgrad1_launch<G256>(d, w1p, ws, dx, s); break;
-        default: return hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) return e;
-    return launch_combine_finish(d, ws, dx, s);
+    const hipError_t e = launch_dgrad1_tr(d, w1p, ws, dx, s);
+    return e == hipSuccess ? launch_combine_finish(d, ws, dx, s) : e;
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -27,11 +27,18 @@
 // are distinct noalias pointers of the K loop, so the compiler does not make fragment reads wait
 // for the DMA loads into other slots.
 //
+// The backward GEMMs run on the same pipeline: the L2 dgrad (dgrad_tile_kernel) and the L1 dgrad
+// (l2_kernel with dhgu rows as A) of experts with few rows read the packed weights themselves
+// through LDS, transposed (TrPipe); with many rows the dgrads take repacked weights and the weight
+// gradients transformed operands (wgrad_nt_kernel), all in registers.
+//
 // Schedule: a persistent grid of one workgroup per CU.  The tile list is ordered expert by
 // expert, then N tile by N tile with the M tiles of that panel adjacent, and cut into one
 // contiguous chunk per XCD (workgroup b runs on XCD b mod 8).  Workgroups take the next tile of
 // their XCD's chunk from an atomic counter, largest tiles first, and help other XCDs once their
 // own is done.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -55,9 +62,31 @@ struct Tile {
     static_assert(SLOTS == 3 || SLOTS == 4, "ring of three or four slots");
     static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
     static constexpr int NT = 64 * kWaves;
+    static constexpr bool kTrB = false;     // B straight into registers
     static constexpr int SLOT = BM * 128;   // bytes of one A slot: BM rows x 64 bf16
+    static constexpr int SLOT_A = SLOT;
     static constexpr int RING_BYTES = SLOTS * SLOT;
     static constexpr int ROWINFO_BYTES = 16 * BM;   // L2: per row (token, weight, direct)
+    static constexpr int LDS_BYTES = RING_BYTES + ROWINFO_BYTES;
+};
+
+// Tiles of the dgrads of experts with few rows, whose B operand is a packed weight read in the
+// other GEMM direction (the packed reduction index becomes the output column).  Each slot holds
+// the A rows and, per wave, the 4 NI packed 1 KB blocks its columns need for the slot's 64-deep K
+// step (two packed column groups x 2 NI blocks of 16 reduction elements), moved by DMA as they
+// are in memory; the MFMA B fragments are then read from them transposed (TrPipe).
+template <int NI_, int MAXMI_, int SLOTS_>
+struct TrTile {
+    static constexpr int NI = NI_, MAXMI = MAXMI_, OCC = 1, SLOTS = SLOTS_;
+    static_assert(MAXMI >= 1 && MAXMI <= 8 && (SLOTS == 3 || SLOTS == 4), "tile shape");
+    static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
+    static constexpr int NT = 64 * kWaves;
+    static constexpr bool kTrB = true;
+    static constexpr int SLOT_A = BM * 128;
+    static constexpr int WAVE_B = NI * 4096;   // one wave's packed blocks of a slot
+    static constexpr int SLOT = SLOT_A + kWaves * WAVE_B;
+    static constexpr int RING_BYTES = SLOTS * SLOT;
+    static constexpr int ROWINFO_BYTES = 16 * BM;
     static constexpr int LDS_BYTES = RING_BYTES + ROWINFO_BYTES;
 };
 
@@ -103,10 +132,89 @@ struct Pipe {
         for (int ni = 0; ni < C::NI; ++ni)
             b[buf][ni][q] = *reinterpret_cast<const bf16x8_t*>(b_src[ni] + (4 * jj + q) * 1024);
     }
+    __device__ __forceinline__ void b_issue(int j, int buf, char* __restrict__, int q) { b_issue(j, buf, q); }
     static constexpr int a_loads(int q) { return (MA + 3 - q) / 4; }
     static constexpr int kBLoads = 4 * C::NI;
     static constexpr int kLoadsPerSlot = MA + kBLoads;
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 l_v4i16;
+
+// The transposed-B pipe.  A as in Pipe, except that a row's slots may be a_step bytes apart (128:
+// K-contiguous rows; 64: rows in [gate | up] order whose slot j takes gate columns 32 j .. 32 j + 31
+// and the same up columns, the order of the packed W1 column groups 2 j and 2 j + 1).
+//
+// B: the dgrad's output column n is the packed weight's reduction index and its K index the packed
+// column.  A packed block (column group G, reduction block b) holds, in 16-byte chunk
+// c = g % 32 + 32 * ((n % 16) / 8), the 8 reduction elements n of column g.  The MFMA B operand of
+// 32 output columns x 16 K needs the transpose: lane L holds 8 consecutive K of column L % 32.
+// gfx950's ds_read_b64_tr_b16 gives it: in each 16-lane group, lane i receives in slot s element
+// i % 4 of the 8 bytes lane 4 s + i / 4 addresses, so if source lane j points at 4 consecutive n
+// (n0 + 4 (j % 4)) of K row k0 + j / 4, lane i gets K rows k0 .. k0 + 3 of column n0 + i.  Two such
+// reads make one operand.  The DMA places chunk c of a block with parity p (its reduction block's
+// index mod 2) at position c ^ (4 (c / 32)) ^ (8 p): a half-wave's 32 eight-byte reads then cover
+// the 64 banks once.  The swizzle is applied on the source side, since lane l of a DMA lands at
+// position l.
+template <class C, int MA>
+struct TrPipe {
+    const char* a_src[MA];
+    const char* b_src[2];   // the lane's chunk of the wave's first block pair of slot 0, even / odd block
+    int64_t b_grp;          // bytes of one packed column group
+    int a_step;
+    int nslot;
+    int wave;
+    uint32_t b_off;         // the lane's transposed-read offset inside a block pair
+
+    // w_e: the expert's packed weight, kp its reduction length (the dgrad's N), n0 the wave's first
+    // output column (a multiple of 32).
+    __device__ __forceinline__ void b_setup(const char* w_e, int kp, int n0, int lane) {
+        b_grp = static_cast<int64_t>(kp) * 64;
+        const int c0 = lane ^ ((lane >> 5) << 2);
+        b_src[0] = w_e + static_cast<int64_t>(n0 / 16) * 1024 + 16 * c0;
+        b_src[1] = w_e + static_cast<int64_t>(n0 / 16 + 1) * 1024 + 16 * (c0 ^ 8);
+        const int g = lane >> 4, j = lane & 15, q = (j & 3) >> 1;
+        const int c = 8 * (g >> 1) + (j >> 2) + 32 * q;
+        b_off = static_cast<uint32_t>((g & 1) * 1024 + 16 * (c ^ (q << 2) ^ ((g & 1) << 3)) + 8 * (j & 1));
+    }
+    __device__ __forceinline__ void a_issue(int j, char* __restrict__ slot, int q) const {
+        const int jj = min(j, nslot - 1);
+#pragma unroll
+        for (int i = 0; i < MA; ++i)
+            if (i % 4 == q)
+                __builtin_amdgcn_global_load_lds((g_void*)(a_src[i] + jj * a_step),
+                                                 (l_void*)(slot + 1024 * (wave + kWaves * i)), 16, 0, 0);
+    }
+    // part q of slot j's blocks: block u = q NI + v (K group u / (2 NI), reduction block u % (2 NI))
+    __device__ __forceinline__ void b_issue(int j, int, char* __restrict__ slot, int q) const {
+        const int jj = min(j, nslot - 1);
+#pragma unroll
+        for (int v = 0; v < C::NI; ++v) {
+            const int u = q * C::NI + v, kg = u / (2 * C::NI), nb = u % (2 * C::NI);
+            __builtin_amdgcn_global_load_lds(
+                (g_void*)(b_src[nb & 1] + (2 * jj + kg) * b_grp + (nb >> 1) * 2048),
+                (l_void*)(slot + C::SLOT_A + wave * C::WAVE_B + u * 1024), 16, 0, 0);
+        }
+    }
+    // B fragments of 16-deep step kb of a slot
+    __device__ __forceinline__ void read_b(bf16x8_t (&b)[C::NI], const char* __restrict__ slot, int kb) const {
+        const char* base = slot + C::SLOT_A + wave * C::WAVE_B + (kb >> 1) * (2 * C::NI * 1024) + (kb & 1) * 256;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni) {
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((l_v4i16*)(base + ni * 2048 + b_off));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((l_v4i16*)(base + ni * 2048 + (b_off ^ 64u)));
+            const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            b[ni] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+    static constexpr int a_loads(int q) { return (MA + 3 - q) / 4; }
+    static constexpr int kBLoads = 4 * C::NI;
+    static constexpr int kLoadsPerSlot = MA + kBLoads;
+};
+
+template <class C, int MA>
+using PipeOf = std::conditional_t<C::kTrB, TrPipe<C, MA>, Pipe<C, MA>>;
 
 template <class C, int MA>
 __device__ __forceinline__ void read_frags(bf16x8_t (&a)[MA], const char* __restrict__ slot, int kb, int lane) {
@@ -125,7 +233,7 @@ __device__ __forceinline__ void read_frags(bf16x8_t (&a)[MA], const char* __rest
 // issue order, so they must match what really went out.  WAIT is the number of this wave's loads
 // issued after slot j's, which may still be in flight.
 template <class C, int MA, int U, bool ISSUE, int WAIT>
-__device__ __forceinline__ void slot_step(Pipe<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+__device__ __forceinline__ void slot_step(PipeOf<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
                                           char* __restrict__ s2, char* __restrict__ s3,
                                           f32x16_t (&acc)[MA][C::NI], int lane) {
     char* const slots[4] = {s0, s1, s2, s3};
@@ -136,28 +244,53 @@ __device__ __forceinline__ void slot_step(Pipe<C, MA>& p, int j, char* __restric
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t a[2][MA];
+    bf16x8_t bt[2][C::NI];   // transposed B fragments (kTrB)
     read_frags<C, MA>(a[0], slots[U], 0, lane);
+    if constexpr (C::kTrB) p.read_b(bt[0], slots[U], 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         if (ISSUE) {
             p.a_issue(j + C::SLOTS - 1, slots[FAR], kb);
-            p.b_issue(j + C::SLOTS - 1, FAR, kb);
+            p.b_issue(j + C::SLOTS - 1, FAR, slots[FAR], kb);
         }
-        if (kb < 3) read_frags<C, MA>(a[(kb + 1) & 1], slots[U], kb + 1, lane);
+        if (kb < 3) {
+            read_frags<C, MA>(a[(kb + 1) & 1], slots[U], kb + 1, lane);
+            if constexpr (C::kTrB) p.read_b(bt[(kb + 1) & 1], slots[U], kb + 1);
+        }
 #pragma unroll
         for (int mi = 0; mi < MA; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb & 1][mi], p.b[U][ni][kb], acc[mi][ni], 0, 0, 0);
+            for (int ni = 0; ni < C::NI; ++ni) {
+                if constexpr (C::kTrB)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb & 1][mi], bt[kb & 1][ni], acc[mi][ni], 0, 0, 0);
+                else
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb & 1][mi], p.b[U][ni][kb], acc[mi][ni], 0, 0, 0);
+            }
         // order: MFMA, fragment read, global load alternating
         constexpr int NM = MA * C::NI;
-        const int nv = ISSUE ? Pipe<C, MA>::a_loads(kb) + C::NI : 0;
+        const int nv = ISSUE ? PipeOf<C, MA>::a_loads(kb) + C::NI : 0;
+        if constexpr (C::kTrB) {
+            // MA + 2 NI fragment reads (two per B operand) and nv loads spread over the NM MFMAs
+            constexpr int NR = MA + 2 * C::NI;
+            const int nr = kb < 3 ? NR : 0;
 #pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
-            if (kb < 3 && i < MA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // global load
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+#pragma unroll
+                for (int x = 0; x < (NR + NM - 1) / NM; ++x)
+                    if (x * NM + i < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+                    if (x * NM + i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
+                if (kb < 3 && i < MA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // global load
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -165,11 +298,11 @@ __device__ __forceinline__ void slot_step(Pipe<C, MA>& p, int j, char* __restric
 
 // Slots j + I .. j + SLOTS - 1 of one turn of the unrolled loop.
 template <class C, int MA, int I>
-__device__ __forceinline__ void loop_turn(Pipe<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+__device__ __forceinline__ void loop_turn(PipeOf<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
                                           char* __restrict__ s2, char* __restrict__ s3,
                                           f32x16_t (&acc)[MA][C::NI], int lane) {
     if constexpr (I < C::SLOTS) {
-        slot_step<C, MA, I, true, (C::SLOTS - 2) * Pipe<C, MA>::kLoadsPerSlot>(p, j + I, s0, s1, s2, s3, acc, lane);
+        slot_step<C, MA, I, true, (C::SLOTS - 2) * PipeOf<C, MA>::kLoadsPerSlot>(p, j + I, s0, s1, s2, s3, acc, lane);
         loop_turn<C, MA, I + 1>(p, j, s0, s1, s2, s3, acc, lane);
     }
 }
@@ -178,12 +311,12 @@ __device__ __forceinline__ void loop_turn(Pipe<C, MA>& p, int j, char* __restric
 // prologue or the loop, which issued through slot j + SLOTS - 2 (re-reading the last slot past
 // the end), so SLOTS - 2 - I slots' loads follow those of slot j + I.
 template <class C, int MA, int I>
-__device__ __forceinline__ void loop_tail(Pipe<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
+__device__ __forceinline__ void loop_tail(PipeOf<C, MA>& p, int j, char* __restrict__ s0, char* __restrict__ s1,
                                           char* __restrict__ s2, char* __restrict__ s3,
                                           f32x16_t (&acc)[MA][C::NI], int lane) {
     if constexpr (I < C::SLOTS - 1) {
         if (j + I < p.nslot) {
-            slot_step<C, MA, I, false, (C::SLOTS - 2 - I) * Pipe<C, MA>::kLoadsPerSlot>(p, j + I, s0, s1, s2, s3, acc, lane);
+            slot_step<C, MA, I, false, (C::SLOTS - 2 - I) * PipeOf<C, MA>::kLoadsPerSlot>(p, j + I, s0, s1, s2, s3, acc, lane);
             loop_tail<C, MA, I + 1>(p, j, s0, s1, s2, s3, acc, lane);
         }
     }
@@ -192,14 +325,14 @@ __device__ __forceinline__ void loop_tail(Pipe<C, MA>& p, int j, char* __restric
 // Issues the loads of slots I .. SLOTS - 2 (prologue), all of one slot before any of the next: the
 // waits count loads in issue order.
 template <class C, int MA, int I>
-__device__ __forceinline__ void prologue_issue(Pipe<C, MA>& p, char* __restrict__ s0, char* __restrict__ s1,
+__device__ __forceinline__ void prologue_issue(PipeOf<C, MA>& p, char* __restrict__ s0, char* __restrict__ s1,
                                                char* __restrict__ s2) {
     if constexpr (I < C::SLOTS - 1) {
         char* const slots[3] = {s0, s1, s2};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             p.a_issue(I, slots[I], q);
-            p.b_issue(I, I, q);
+            p.b_issue(I, I, slots[I], q);
         }
         __builtin_amdgcn_sched_barrier(0);
         prologue_issue<C, MA, I + 1>(p, s0, s1, s2);
@@ -210,7 +343,7 @@ __device__ __forceinline__ void prologue_issue(Pipe<C, MA>& p, char* __restrict_
 // waves past their last fragment read, so the caller may reuse the LDS.  s3 is unused with three
 // slots.
 template <class C, int MA>
-__device__ __forceinline__ void k_loop(Pipe<C, MA>& p, char* __restrict__ s0, char* __restrict__ s1,
+__device__ __forceinline__ void k_loop(PipeOf<C, MA>& p, char* __restrict__ s0, char* __restrict__ s1,
                                        char* __restrict__ s2, char* __restrict__ s3,
                                        f32x16_t (&acc)[MA][C::NI], int lane) {
 #pragma unroll
@@ -537,6 +670,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void l1_kernel(const uint16_t* __res
 // Row r of pair p = (t, j): o = act[r] @ W2[e]^T scaled by topk_w[p].  A token with one local
 // pair owns its y row, so the epilogue stores bf16(w * o) there; a token with several local
 // pairs gets fp32 rows in ws.stage that combine_finish sums in slot order.
+//
+// With a transposed-B tile (C::kTrB) the same body is the L1 dgrad of experts with few rows: A the
+// dhgu rows ([gate | up], K = d.I = 2 x the intermediate size), B the packed W1 read transposed
+// (its reduction index H is the output column), row weight 1.
 template <class C>
 struct L2Body {
     const uint16_t* act;
@@ -556,22 +693,29 @@ struct L2Body {
         // the row's pair now; what depends on it is loaded after the K loop, so the loop does not
         // start behind a chain of dependent loads
         const int pr = tid < t.real_rows ? ws.row_pair[t.row0 + tid] : -1;
-        Pipe<C, MA> p;
+        PipeOf<C, MA> p;
         p.nslot = I / 64;
         p.wave = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int i = 0; i < MA; ++i) {
             const int row = 32 * i + 8 * wave + (lane >> 3);
-            const int c16 = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+            const int lc = (lane & 7) ^ ((row >> 1) & 7);
+            // [gate | up] rows: logical chunks 0-3 are gate columns, 4-7 the same up columns
+            const int c16 = C::kTrB ? (lc < 4 ? 16 * lc : I + 16 * (lc - 4)) : 16 * lc;
             p.a_src[i] = row < t.real_rows
                              ? reinterpret_cast<const char*>(act + (t.row0 + row) * static_cast<int64_t>(I)) + c16
                              : reinterpret_cast<const char*>(ws.zeros) + c16;
         }
         const char* wb = reinterpret_cast<const char*>(w2f) + static_cast<int64_t>(t.e) * H * I * 2;
-        const int nb0 = t.nt * (C::BN / 32) + wave * C::NI;
+        if constexpr (C::kTrB) {
+            p.a_step = 64;
+            p.b_setup(wb, H, t.nt * C::BN + wave * 32 * C::NI, lane);
+        } else {
+            const int nb0 = t.nt * (C::BN / 32) + wave * C::NI;
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
-            p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (I / 16) * 1024 + lane * 16;
+            for (int ni = 0; ni < C::NI; ++ni)
+                p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (I / 16) * 1024 + lane * 16;
+        }
         f32x16_t acc[MA][C::NI];
         k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, smem + (C::SLOTS - 1) * C::SLOT, acc, lane);
 
@@ -774,10 +918,12 @@ __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_nt_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------------------------
-// L2 dgrad of experts with many rows, on the forward's pipeline
+// L2 dgrad on the forward's pipeline
 // ---------------------------------------------------------------------------------------------
 // dA'[r] = dy[t] @ W2[e]^T (t the row's token) on the L1 tile loop: the dy rows gathered through
-// row_pair into the A ring, W2 repacked to an (N = i, K = h) operand streaming into B registers.
+// row_pair into the A ring.  Experts with many rows (256-row tiles) take W2 repacked to an
+// (N = i, K = h) operand streaming into B registers; experts with few rows (C::kTrB) read the
+// packed W2 itself, transposed out of LDS, so nothing is repacked.
 // The epilogue is the streaming dgrad's: the row weight (dA = w * dA'), the activation
 // a = silu(g) * u recomputed in fp32 from the saved fp32 pre-activation and written as w * a (hi
 // and lo bf16, the dW2 operand), the SwiGLU transpose (fuse; dhgu hi and lo) or plain fp32 dA
@@ -787,7 +933,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_nt_kernel(const uint16_t*
 template <class C>
 struct DgradBody {
     const uint16_t* dy;
-    const uint16_t* w2t;
+    const uint16_t* w2b;   // repacked W2 (register B) or the packed W2 (kTrB)
     const float* topk_w;
     Dims d;
     Ws ws;
@@ -796,12 +942,12 @@ struct DgradBody {
 
     template <int MA>
     __device__ __forceinline__ void run(const TileRef& t) {
-        static_assert(C::BN == 256 && C::NI == 2, "two 128-column halves of two waves each");
+        static_assert(C::BN == 256 || C::BN == 128, "whole 128-column routing-weight partials");
         float* s_w = reinterpret_cast<float*>(smem + C::RING_BYTES);   // row weight (0: no pair)
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int H = d.H, I = d.I, npairs = d.T * d.k;
         const int pr_own = tid < t.real_rows ? ws.row_pair[t.row0 + tid] : -1;
-        Pipe<C, MA> p;
+        PipeOf<C, MA> p;
         p.nslot = H / 64;
         p.wave = __builtin_amdgcn_readfirstlane(wave);
         const char* zrow = reinterpret_cast<const char*>(ws.zeros);
@@ -814,24 +960,32 @@ struct DgradBody {
                              ? reinterpret_cast<const char*>(dy + static_cast<int64_t>(pr / d.k) * H) + c16
                              : zrow + c16;
         }
-        const char* wb = reinterpret_cast<const char*>(w2t) + static_cast<int64_t>(t.e) * I * H * 2;
-        const int nb0 = t.nt * (C::BN / 32) + wave * C::NI;
+        const char* wb = reinterpret_cast<const char*>(w2b) + static_cast<int64_t>(t.e) * I * H * 2;
+        if constexpr (C::kTrB) {
+            p.a_step = 128;
+            p.b_setup(wb, I, t.nt * C::BN + wave * 32 * C::NI, lane);
+        } else {
+            const int nb0 = t.nt * (C::BN / 32) + wave * C::NI;
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
-            p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (H / 16) * 1024 + lane * 16;
+            for (int ni = 0; ni < C::NI; ++ni)
+                p.b_src[ni] = wb + static_cast<int64_t>(nb0 + ni) * (H / 16) * 1024 + lane * 16;
+        }
         f32x16_t acc[MA][C::NI];
         k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, smem + (C::SLOTS - 1) * C::SLOT, acc, lane);
 
         if (tid < 32 * MA) s_w[tid] = (pr_own >= 0 && pr_own < npairs) ? topk_w[pr_own] : 0.0f;
         // Epilogue through LDS, GP 32-row groups per pass: the waves drop dA' into a row-major fp32
-        // tile, then each wave takes whole rows (64 lanes x 4 columns = the tile's 256 columns), so
-        // the hgu reads and the dhgu / dact / wact writes are contiguous row segments, and a row's
-        // two 128-column routing-weight partials are the sums over lanes 0-31 and 32-63.
+        // tile, then each wave takes whole rows (64 lanes x 4 columns: one 256-column row, or two
+        // 128-column rows), so the hgu reads and the dhgu / dact / wact writes are contiguous row
+        // segments, and each 32-lane half's sum is one 128-column routing-weight partial.
         constexpr int LD = C::BN + 4;   // floats per LDS row: rows r and r + 4 fall on different banks
         constexpr int GP = 2;
+        constexpr int LPR = C::BN / 4, RPI = 64 / LPR;   // lanes per row, rows per wave instruction
         static_assert(GP * 32 * LD * 4 <= C::RING_BYTES, "a pass fits in the ring");
         float* tile = reinterpret_cast<float*>(smem);
         const int cols_tw = I / 128;
+        const int lrow = lane / LPR, lcol = (lane % LPR) * 4;
+        const int half = C::BN == 256 ? (lane >> 5) : 0;   // the lane's 128-column partial in the tile
 #pragma unroll
         for (int m0 = 0; m0 < MA; m0 += GP) {
             if (32 * m0 >= t.real_rows) break;   // groups that belong to no row
@@ -846,31 +1000,32 @@ struct DgradBody {
                             tile[(mm * 32 + acc_row(r, lane)) * LD + wave * 32 * C::NI + ni * 32 + (lane & 31)] =
                                 acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
             lds_barrier();
+            // rows is a multiple of 32, so a wave instruction's RPI rows are all valid or none is
             const int rows = min(GP * 32, t.real_rows - 32 * m0);
-            // four rows per wave at a time: their hgu loads all go out before any is used
+            // four row steps per wave at a time: their hgu loads all go out before any is used
             constexpr int RB = 4, WS = C::NT / 64;
-            for (int rb = wave; rb < rows; rb += RB * WS) {
+            for (int rb = wave * RPI; rb < rows; rb += RB * WS * RPI) {
                 float4 gv[RB], uv[RB];
 #pragma unroll
                 for (int b = 0; b < RB; ++b) {
-                    const int rr = rb + b * WS;
+                    const int rr = rb + b * WS * RPI + lrow;
                     gv[b] = uv[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                     if (rr < rows) {
                         const int64_t row = t.row0 + 32 * m0 + rr;
-                        const int c = t.nt * C::BN + lane * 4;
+                        const int c = t.nt * C::BN + lcol;
                         gv[b] = *reinterpret_cast<const float4*>(ws.hgu + row * 2 * I + c);
                         uv[b] = *reinterpret_cast<const float4*>(ws.hgu + row * 2 * I + I + c);
                     }
                 }
 #pragma unroll
                 for (int b = 0; b < RB; ++b) {
-                    const int rr = rb + b * WS;
+                    const int rr = rb + b * WS * RPI + lrow;
                     if (rr >= rows) break;   // uniform over the wave
                     const int rl = 32 * m0 + rr;
                     const int64_t row = t.row0 + rl;
                     const float w = s_w[rl];
-                    const int c = t.nt * C::BN + lane * 4;
-                    const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + lane * 4);
+                    const int c = t.nt * C::BN + lcol;
+                    const float4 v = *reinterpret_cast<const float4*>(tile + rr * LD + lcol);
                     const float va[4] = {v.x, v.y, v.z, v.w};
                     const float ga[4] = {gv[b].x, gv[b].y, gv[b].z, gv[b].w};
                     const float ua[4] = {uv[b].x, uv[b].y, uv[b].z, uv[b].w};
@@ -903,24 +1058,49 @@ struct DgradBody {
                     } else {
                         *reinterpret_cast<float4*>(ws.dact + row * I + c) = make_float4(dv[0], dv[1], dv[2], dv[3]);
                     }
-                    if (tw) {   // uniform over the wave: its lanes hold one row
+                    if (tw) {   // uniform over the wave: each 32-lane half holds one 128-column partial
 #pragma unroll
                         for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-                        if ((lane & 31) == 0) ws.dtw_part[row * cols_tw + 2 * t.nt + (lane >> 5)] = part;
+                        if ((lane & 31) == 0) ws.dtw_part[row * cols_tw + t.nt * (C::BN / 128) + half] = part;
                     }
                 }
             }
+        }
+        if (t.last) {   // the segment's padding rows after its last real group hold zeros
+            const int64_t r0 = t.row0 + t.real_rows, r1 = min(static_cast<int64_t>(ws.offsets[t.e + 1]), ws.rows_cap);
+            const int c0 = t.nt * C::BN;
+            constexpr int CH = C::BN / 8;   // 8-column chunks of the tile's columns
+            const u32x4 z = 0;
+            for (int64_t u = tid; u < (r1 - r0) * CH; u += C::NT) {
+                const int64_t row = r0 + u / CH;
+                const int c = c0 + static_cast<int>(u % CH) * 8;
+                *reinterpret_cast<u32x4*>(ws.wact + row * I + c) = z;
+                *reinterpret_cast<u32x4*>(ws.wact_lo + row * I + c) = z;
+                if (fuse) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        *reinterpret_cast<u32x4*>(ws.dhgu + row * 2 * I + h * I + c) = z;
+                        *reinterpret_cast<u32x4*>(ws.dhgu_lo + row * 2 * I + h * I + c) = z;
+                    }
+                } else {
+                    *reinterpret_cast<u32x4*>(ws.dact + row * I + c) = z;
+                    *reinterpret_cast<u32x4*>(ws.dact + row * I + c + 4) = z;
+                }
+            }
+            if (tw)
+                for (int64_t u = tid; u < (r1 - r0) * (C::BN / 128); u += C::NT)
+                    ws.dtw_part[(r0 + u / (C::BN / 128)) * cols_tw + t.nt * (C::BN / 128) + u % (C::BN / 128)] = 0.0f;
         }
     }
 };
 
 template <class C>
-__global__ __launch_bounds__(C::NT, C::OCC) void dgrad_nt_kernel(const uint16_t* __restrict__ dy,
-                                                                 const uint16_t* __restrict__ w2t,
+__global__ __launch_bounds__(C::NT, C::OCC) void dgrad_tile_kernel(const uint16_t* __restrict__ dy,
+                                                                   const uint16_t* __restrict__ w2b,
                                                                  const float* __restrict__ topk_w, Dims d, Ws ws,
                                                                  int fuse, int tw) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    DgradBody<C> body{dy, w2t, topk_w, d, ws, fuse, tw, smem};
+    DgradBody<C> body{dy, w2b, topk_w, d, ws, fuse, tw, smem};
     run_tiles<C>(d, ws, d.I / C::BN, body);
 }
 
@@ -928,6 +1108,20 @@ using L1Tile = Tile<2, 8, 1, 4>;
 using L2Tile = Tile<2, 8, 1, 4>;
 using L2TileNarrow = Tile<1, 8, 1, 4>;
 using WgTile = Tile<2, 8, 1, 3>;   // three ring slots measured slightly faster than four here
+// Few-rows dgrads: M tiles of up to 96 rows (an expert of the wide share in one tile, its weights
+// streamed once), three ring slots of 44 KB.
+using DgTrTile = TrTile<2, 3, 3>;
+using DgTrTileNarrow = TrTile<1, 3, 3>;
+
+template <class C>
+hipError_t dgrad_tile_launch(const Dims& d, const uint16_t* dy, const uint16_t* w2b, const float* topk_w,
+                             const Ws& ws, int fuse, bool topk_w_grad, hipStream_t s) {
+    auto k = dgrad_tile_kernel<C>;
+    allow_lds(k, C::LDS_BYTES);
+    k<<<persistent_grid(k, C::NT, C::LDS_BYTES), C::NT, C::LDS_BYTES, s>>>(dy, w2b, topk_w, d, ws, fuse,
+                                                                           topk_w_grad ? 1 : 0);
+    return hipGetLastError();
+}
 
 }  // namespace
 
@@ -938,11 +1132,25 @@ bool dgrad_nt_fits(const Dims& d) { return d.I % L1Tile::BN == 0 && d.H % 64 == 
 hipError_t launch_dgrad_nt(const Dims& d, const uint16_t* dy, const uint16_t* w2t, const float* topk_w, const Ws& ws,
                            int fuse, bool topk_w_grad, hipStream_t s) {
     if (!dgrad_nt_fits(d)) return hipErrorInvalidValue;
-    auto k = dgrad_nt_kernel<L1Tile>;
-    allow_lds(k, L1Tile::LDS_BYTES);
-    k<<<persistent_grid(k, L1Tile::NT, L1Tile::LDS_BYTES), L1Tile::NT, L1Tile::LDS_BYTES, s>>>(
-        dy, w2t, topk_w, d, ws, fuse, topk_w_grad ? 1 : 0);
-    return hipGetLastError();
+    return dgrad_tile_launch<L1Tile>(d, dy, w2t, topk_w, ws, fuse, topk_w_grad, s);
+}
+
+// Few-rows dgrads (I and H are multiples of 128): 256-column tiles where the width allows.
+hipError_t launch_dgrad_tr(const Dims& d, const uint16_t* dy, const uint16_t* w2p, const float* topk_w, const Ws& ws,
+                           int fuse, bool topk_w_grad, hipStream_t s) {
+    if (d.EL > kMaxEL || d.I % 128 != 0 || d.H % 64 != 0) return hipErrorInvalidValue;
+    return d.I % 256 == 0 ? dgrad_tile_launch<DgTrTile>(d, dy, w2p, topk_w, ws, fuse, topk_w_grad, s)
+                          : dgrad_tile_launch<DgTrTileNarrow>(d, dy, w2p, topk_w, ws, fuse, topk_w_grad, s);
+}
+
+// dX rows of the L1 dgrad: the dhgu rows times the packed W1 read transposed, combined into dx
+// like the forward's L2 (weight 1); the caller runs combine_finish.
+hipError_t launch_dgrad1_tr(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s) {
+    if (d.EL > kMaxEL || d.H % 128 != 0 || d.I % 32 != 0 || !ws.dhgu) return hipErrorInvalidValue;
+    Dims d2 = d;
+    d2.I = 2 * d.I;   // the GEMM's K: dhgu rows are 2I wide
+    return d.H % 256 == 0 ? l2_launch<DgTrTile>(d2, ws.dhgu, w1p, nullptr, ws, dx, s)
+                          : l2_launch<DgTrTileNarrow>(d2, ws.dhgu, w1p, nullptr, ws, dx, s);
 }
 
 hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp, int M, int N, const Ws& ws,

@@ -155,6 +155,9 @@ bool wgrad_nt_fits(int M, int N);
 bool dgrad_nt_fits(const Dims& d);
 hipError_t launch_dgrad_nt(const Dims& d, const uint16_t* dy, const uint16_t* w2t, const float* topk_w, const Ws& ws,
                            int fuse, bool topk_w_grad, hipStream_t s);
+hipError_t launch_dgrad_tr(const Dims& d, const uint16_t* dy, const uint16_t* w2p, const float* topk_w, const Ws& ws,
+                           int fuse, bool topk_w_grad, hipStream_t s);
+hipError_t launch_dgrad1_tr(const Dims& d, const uint16_t* w1p, const Ws& ws, uint16_t* dx, hipStream_t s);
 hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp, int M, int N, const Ws& ws,
                            uint16_t* out, hipStream_t s);
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p,
