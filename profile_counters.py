@@ -9,6 +9,7 @@ known / measured on that copy, so the figures are in true HBM bytes whatever uni
         PASS_DIR [PASS_DIR ...] > profiles/forward_dsv3_share_counters.md
     python profile_counters.py --variant mx --trace TRACE_DIR \
         --out-json profiles/mx_gemm1_wide_share_traffic.json PASS_DIR [...] > profiles/forward_mx_wide_share_counters.md
+    python profile_counters.py latency PASS_DIR [...] > profiles/forward_dsv3_share_latency_counters.md
     python profile_counters.py --variant bwd --workload wide_share_fwd_bwd --trace TRACE_DIR \
         --out-json gpurun_out/bwd.json PASS_DIR [...] > profiles/training_wide_share_counters.md
 
@@ -166,7 +167,56 @@ def occupancy(dirs, workloads, command):
             100 * busy.get("l1_kernel", float("nan")), 100 * busy.get("l2_kernel", float("nan")), cyc.get("l1_kernel", 0)))
 
 
+LATENCY_ORDER = ("SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_INST_LEVEL_LDS", "SQ_INST_LEVEL_VMEM",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+                 "TA_BUSY_avr", "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum", "TCC_HIT_sum", "TCC_MISS_sum",
+                 "TCP_PENDING_STALL_CYCLES_sum", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum",
+                 "TCP_TCR_TCP_STALL_CYCLES_sum")
+
+
+def latency(dirs, command, title):
+    """Memory-path table of the forward GEMMs (l1_kernel, l2_kernel) from the pass directories of
+    the counters in LATENCY_ORDER: per-dispatch averages and the ratios derived from them."""
+    c = read_counters(dirs)
+    ks = [k for k in ("l1_kernel", "l2_kernel") if k in c]
+    v = {k: c[k] for k in ks}
+    print("# rocprofv3 memory-path counters of the forward GEMMs (%s)\n" % title)
+    if command:
+        print("Commands (run from /tmp with TMPDIR=/tmp, repository at $R), one pass each:\n\n```\n%s\n```\n" % command)
+    print("Averages per dispatch over every dispatch of each kernel in the passes.")
+    print("Derived: kernel cycles = SQ_BUSY_CYCLES / 32 shader engines; TCP pending-stall share = "
+          "TCP_PENDING_STALL_CYCLES / 256 CUs / kernel cycles;")
+    print("L1-to-L2 read latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ; L2 hit rate = TCC_HIT / "
+          "(TCC_HIT + TCC_MISS);")
+    print("L2-to-memory read latency = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ; wave time in s_waitcnt = "
+          "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.\n")
+    print("| kernel | kernel cycles | TCP pending-stall share | L1→L2 read latency (cycles) | L2 hit rate "
+          "| L2→memory read latency (cycles) | wave time waiting | LDS bank conflicts / LDS instruction |")
+    print("|---|---|---|---|---|---|---|---|")
+    for k in ks:
+        x = v[k]
+        cyc = x["SQ_BUSY_CYCLES"] / 32
+        print("| %s | %.0f | %.0f%% | %.0f | %.0f%% | %.0f | %.0f%% | %.4f |" % (
+            "L1" if k == "l1_kernel" else "L2", cyc, 100 * x["TCP_PENDING_STALL_CYCLES_sum"] / 256 / cyc,
+            x["TCP_TCC_READ_REQ_LATENCY_sum"] / x["TCP_TCC_READ_REQ_sum"],
+            100 * x["TCC_HIT_sum"] / (x["TCC_HIT_sum"] + x["TCC_MISS_sum"]),
+            x["TCC_EA0_RDREQ_LEVEL_sum"] / x["TCC_EA0_RDREQ_sum"], 100 * x["SQ_WAIT_INST_ANY"] / x["SQ_WAVE_CYCLES"],
+            x["SQ_LDS_BANK_CONFLICT"] / x["SQ_INSTS_LDS"]))
+    print("\nRaw averages:\n")
+    print("| counter | " + " | ".join("L1" if k == "l1_kernel" else "L2" for k in ks) + " |")
+    print("|---|" + "---|" * len(ks))
+    for n in LATENCY_ORDER:
+        print("| %s | %s |" % (n, " | ".join("%.0f" % v[k].get(n, float("nan")) for k in ks)))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "latency":
+        ap = argparse.ArgumentParser(prog="profile_counters.py latency")
+        ap.add_argument("passes", nargs="+")
+        ap.add_argument("--command", default="")
+        ap.add_argument("--title", default="DeepSeek-V3 share")
+        a = ap.parse_args(sys.argv[2:])
+        return latency(a.passes, a.command, a.title)
     if len(sys.argv) > 1 and sys.argv[1] == "occupancy":
         ap = argparse.ArgumentParser(prog="profile_counters.py occupancy")
         ap.add_argument("--pass", dest="passes", nargs=2, action="append", metavar=("DIR", "WORKLOAD"), required=True)
