@@ -227,10 +227,10 @@ int32_t moe_forward_noalloc(const moe_shape* shape, const uint16_t* x, const int
  * in this order on one stream: moe_bwd_gemm2_dgrad (or it without the SwiGLU transpose, then
  * moe_swiglu_bwd), then moe_wgrad2, moe_wgrad1 and moe_bwd_gemm1_dgrad_combine in any order.
  * They use ws regions that are dead at that point as scratch: moe_wgrad2 and moe_wgrad1 overwrite
- * ws stage (after the forward's combine has consumed it) and moe_wgrad1 also ws dact (after dhgu
- * exists), to hold their intermediate operand in MFMA-fragment order; when the expected rows per
- * local expert (T * k / E) are at least 256 (and the shape allows) the GEMMs run on the forward's
- * pipeline, moe_bwd_gemm2_dgrad then overwrites ws stage and moe_bwd_gemm1_dgrad_combine ws dact.
+ * ws stage (after the forward's combine has consumed it) to hold their operands in MFMA-fragment
+ * order; when the expected rows per local expert (T * k / E) are at least 256 (and the shape
+ * allows) the GEMMs run on the forward's pipeline, moe_bwd_gemm2_dgrad then overwrites ws stage
+ * and moe_bwd_gemm1_dgrad_combine ws dact.
  *
  * L2 dgrad, NN: dact[r] = topk_w[p] * (dy[t] @ W2[e]^T) with p = row_pair[r], t = p / k, read
  * from the packed w2p as the [K = H, N = I] operand.  With fuse_swiglu_bwd nonzero the

@@ -41,10 +41,8 @@ BWD = (("dgrad_tile_kernel<moe::(anonymous namespace)::TrTile",
        ("dgrad_tile_kernel", "L2 dgrad NN on repacked W2 + SwiGLU transpose (many rows)"),
        ("l2_kernel<moe::(anonymous namespace)::TrTile", "L1 dgrad NN, packed W1 read transposed + combine rows"),
        ("wgrad_nt_kernel", "dW1 / dW2 TN on the forward pipeline (many rows)"),
-       ("wgrad_frag_kernel<true>", "dW2 TN, variable K, hi/lo fragment operand"),
-       ("wgrad_frag_kernel<false>", "dW1 TN, variable K, hi/lo fragment operand"),
-       ("wgrad2_kernel", "dW2 TN, variable K, hi/lo operand (LDS tiles)"),
-       ("wgrad1_kernel", "dW1 TN, variable K, hi/lo operand (LDS tiles)"),
+       ("wgrad_tok_kernel<false>", "dW2 TN, variable K, dy fragments x hi/lo w*act in LDS"),
+       ("wgrad_tok_kernel<true>", "dW1 TN, variable K, x fragments x hi/lo dhgu in LDS"),
        ("repack_t_kernel", "weight repack (many rows)"),
        ("rows_to_k_major_kernel", "row transforms of the weight-gradient operands"),
        ("dtopk_w_finish", "d(topk_w) finish"))

@@ -4,29 +4,27 @@
 // many-rows weight gradients run on the forward's pipeline in moe_grouped.hip.
 //
 // Kernels:
-//   wgrad_frag  dW2 = (w act)^T dy and dW1 = dHgu^T X (X re-gathered from x) of experts with few
-//               rows: K is one expert's rows; the streamed operand (w act, or dHgu) comes as
-//               hi/lo MFMA fragments prepared by rows_to_k_major, the token rows through LDS
-//   wgrad2, wgrad1  the same products with both operand tiles in LDS, for shapes the fragment
-//               kernel does not fit (I > H)
+//   wgrad_tok  dW2 = (w act)^T dy and dW1 = dHgu^T X (X re-gathered from x) of experts with few
+//              rows: K is one expert's rows; the token rows stream as MFMA fragments prepared by
+//              rows_to_k_major, the hi / lo intermediate operand sits in LDS
 //   rows_to_k_major, repack_t  operand transforms of the weight gradients and of the many-rows
-//               dgrads
+//              dgrads
 //
 // Precision of the intermediate operands.  The saved pre-activation is fp32, so the row gradients
 // (dHgu) and the weighted activation (w * act) are formed in fp32 and stored as two bf16 arrays,
 // hi = bf16(v) and lo = bf16(v - hi), which together carry about 16 significant bits.  The weight
 // gradients of experts with few rows sum few products, so one bf16 rounding of an operand shows in
-// their largest elements; their streamed operand is that split pair, multiplied by the other
-// operand twice (hi, then lo) into the same accumulators.  x and dy enter unrounded (they are
-// bf16 inputs), and the routing weight rides on the activation, so dW1 and dW2 carry only the
-// fp32 accumulation and the output rounding.
-// Weight gradients are written in the packed layout of the weights they belong to, whole 1 KB
-// blocks per store instruction (the tile's M index runs along the packed reduction index).
+// their largest elements; they multiply the other operand by that split pair twice (hi, then lo)
+// into the same accumulators.  x and dy enter unrounded (they are bf16 inputs), and the routing
+// weight rides on the activation, so dW1 and dW2 carry only the fp32 accumulation and the output
+// rounding.  Weight gradients are written in the packed layout of the weights they belong to,
+// whole 1 KB blocks per store instruction (the tile's M index runs along the packed reduction
+// index).
 //
-// The LDS tiles of wgrad2 / wgrad1 are K-contiguous (128 bytes per row, 16-byte chunks
-// XOR-swizzled by row so a wave's fragment reads spread over the banks); their operands are stored
-// with M (or N) contiguous in runs of 8 and K strided, so the TRows loader moves 4 K-rows x 8
-// elements per thread and transposes them in registers into 8 rows x 4 K before the LDS store.
+// The LDS tiles are K-contiguous (128 bytes per row, 16-byte chunks XOR-swizzled by row so a
+// wave's fragment reads spread over the banks); their sources are stored with M (or N) contiguous
+// in runs of 8 and K strided, so the TRows loader moves 4 K-rows x 8 elements per thread and
+// transposes them in registers into 8 rows x 4 K before the LDS store.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -34,7 +32,6 @@
 namespace moe {
 
 constexpr int BK = 64;
-constexpr int kXcds = 8;   // the hardware places workgroup b on XCD b mod 8, each with its own L2
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes of staged operand
 
@@ -44,22 +41,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes of sta
 __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
-
-template <int BM_, int BN_, int WM_, int WN_, int PF_ = 1>
-struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    // 0: one LDS buffer (launches of many short-K tiles, where occupancy matters more than
-    // overlap); else two
-    static constexpr int PF = PF_;
-    static constexpr int NT = 64 * WM * WN;
-    static constexpr int TM = BM / WM, TN = BN / WN;
-    static constexpr int MI = TM / 32, NI = TN / 32;
-    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = (PF == 0 ? 1 : 2) * STAGE_BYTES;
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
-    static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "K-row chunks must split evenly");
-};
 
 // ---------------------------------------------------------------------------------------------
 // Operand loaders
@@ -116,76 +97,10 @@ struct TRows {
 };
 
 // ---------------------------------------------------------------------------------------------
-// MFMA core
-// ---------------------------------------------------------------------------------------------
-template <class C>
-__device__ __forceinline__ void read_frags(const char* lA, const char* lB, bf16x8_t (&a)[C::MI],
-                                           bf16x8_t (&b)[C::NI], int s, int wm0, int wn0, int lane) {
-    const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(lA + lds_off(wm0 + i * 32 + (lane & 31), ch));
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(lB + lds_off(wn0 + j * 32 + (lane & 31), ch));
-}
-
-// mma_step with one operand given as hi + lo bf16 tiles (the lo tile at lX, laid out like the
-// operand it completes): acc += A * B + X * B (SPLIT_A) or A * B + A * X.  Each 16-deep substep
-// issues the hi products of every accumulator first, then the lo ones, so no MFMA waits on the
-// one just before it; the lo fragments are read at the start of their substep (the hi MFMAs cover
-// that latency), one buffer instead of two.
-template <class C, bool SPLIT_A>
-__device__ __forceinline__ void mma_step_split(const char* lA, const char* lB, const char* lX,
-                                               f32x16_t (&acc)[C::MI][C::NI], int wm0, int wn0, int lane) {
-    constexpr int KS = BK / 16;
-    constexpr int NX = SPLIT_A ? C::MI : C::NI;
-    bf16x8_t a[2][C::MI], b[2][C::NI], x[NX];
-    read_frags<C>(lA, lB, a[0], b[0], 0, wm0, wn0, lane);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        {
-            const int ch = 2 * s + (lane >> 5);
-            const int w0 = SPLIT_A ? wm0 : wn0;
-#pragma unroll
-            for (int i = 0; i < NX; ++i)
-                x[i] = *reinterpret_cast<const bf16x8_t*>(lX + lds_off(w0 + i * 32 + (lane & 31), ch));
-        }
-        if (s + 1 < KS) read_frags<C>(lA, lB, a[(s + 1) & 1], b[(s + 1) & 1], s + 1, wm0, wn0, lane);
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NI; ++j) {
-                if constexpr (SPLIT_A)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i], b[s & 1][j], acc[i][j], 0, 0, 0);
-                else
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], x[j], acc[i][j], 0, 0, 0);
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
 // Weight gradients (TN, variable K = rows of the expert)
 // ---------------------------------------------------------------------------------------------
 // K index k is row seg0 + k of the expert's segment; k >= count reads the zero row, so the K tail
 // and an expert without rows contribute nothing (an empty expert's tile stores exact zeros).
-struct GatherTokenSrc {   // row k -> token row of x or dy through row_pair, optionally weighted
-    const uint16_t* base;
-    const uint16_t* zeros;   // ws.zeros: a zero row at least H long
-    const int32_t* row_pair;
-    int64_t seg0;
-    int count, k, H, npairs;
-    __device__ __forceinline__ int pair(int kk) const { return kk < count ? row_pair[seg0 + kk] : -1; }
-    __device__ __forceinline__ const uint16_t* chunk(int kk, int m) const {
-        const int p = pair(kk);
-        return (p >= 0 && p < npairs) ? base + static_cast<int64_t>(p / k) * H + m : zeros + m;
-    }
-};
 struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
     const uint16_t* base;
     const uint16_t* zeros;   // ws.zeros: a zero row at least width long
@@ -196,159 +111,19 @@ struct DirectRowSrc {   // row k -> ws row seg0 + k of a [R_max, width] buffer
     }
 };
 
-// The accumulator of a 32x32 MFMA block stored as one packed 1 KB block: store_packed_block in
-// moe_internal.h.
-__device__ __forceinline__ void store_grad_block(uint16_t* out, int64_t K, int64_t n0, int64_t k0,
-                                                 const f32x16_t& acc, int lane) {
-    store_packed_block(out, K, n0, k0, acc, lane);
-}
-
-constexpr int kWgradChunk = 8;   // output tiles per weight-gradient workgroup
-
-// Full K loop of one weight-gradient tile whose operand A (SPLIT_A) or B comes as hi (la / lb)
-// plus lo (lx) tiles; one LDS buffer: A | B | X.
-template <class C, bool SPLIT_A, class LA, class LB, class LX>
-__device__ __forceinline__ void gemm_tile_split(LA& la, LB& lb, LX& lx, int nk, char* smem,
-                                                f32x16_t (&acc)[C::MI][C::NI], int tid, int wm0, int wn0, int lane) {
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    if (nk <= 0) return;
-    char* lA = smem;
-    char* lB = smem + C::A_BYTES;
-    char* lX = lB + C::B_BYTES;
-    la.template load<0>(0, tid);
-    lb.template load<0>(0, tid);
-    lx.template load<0>(0, tid);
-    la.template store<0>(lA, tid);
-    lb.template store<0>(lB, tid);
-    lx.template store<0>(lX, tid);
-    lds_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.template load<0>(kt + 1, tid);
-            lb.template load<0>(kt + 1, tid);
-            lx.template load<0>(kt + 1, tid);
-        }
-        mma_step_split<C, SPLIT_A>(lA, lB, lX, acc, wm0, wn0, lane);
-        if (more) {
-            lds_barrier();   // every wave's fragment reads of step kt are done
-            la.template store<0>(lA, tid);
-            lb.template store<0>(lB, tid);
-            lx.template store<0>(lX, tid);
-            lds_barrier();
-        }
-    }
-}
-
-// A run of output tiles of one expert's weight gradient that share one operand tile: with
-// STREAM_A the M tiles [t0, t1) of N tile `fixed` (the N operand lb is shared), else the N tiles
-// [t0, t1) of M tile `fixed` (la is shared).  The streamed operand is the one given as a hi/lo
-// pair (lx loads its lo part into the third LDS tile).  When the expert has at most one K step of
-// rows (the common case: K is the expert's row count), the shared tile is loaded into LDS once and
-// the streamed one's loads for tile t + 1 go out before the MFMAs and stores of tile t, so the
-// launch streams its output.  With more rows every tile runs the full K loop.  n_col(nt, ni) gives
-// the packed column of block ni of the wave in N tile nt; K_out is the packed reduction length.
-template <class C, bool STREAM_A, class LA, class LB, class LX, class NCol>
-__device__ __forceinline__ void wgrad_tiles(LA& la, LB& lb, LX& lx, int count, int fixed, int t0, int t1,
-                                            uint16_t* out, int64_t K_out, NCol n_col, char* smem, int tid, int wm0,
-                                            int wn0, int lane) {
-    const int nk = (count + BK - 1) / BK;
-    f32x16_t acc[C::MI][C::NI];
-    auto store = [&](int t) {
-        const int mt = STREAM_A ? t : fixed, nt = STREAM_A ? fixed : t;
-#pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-                store_grad_block(out, K_out, n_col(nt, ni), mt * C::BM + wm0 + mi * 32, acc[mi][ni], lane);
-    };
-    auto aim = [&](int t) {   // point the streamed operand (both parts) at tile t
-        if constexpr (STREAM_A) la.m_base = t * C::BM;
-        else lb.m_base = t * C::BN;
-        lx.m_base = t * (STREAM_A ? C::BM : C::BN);
-    };
-    if constexpr (STREAM_A) lb.m_base = fixed * C::BN;
-    else la.m_base = fixed * C::BM;
-    if (nk <= 1) {
-        // Two tiles of the streamed operand are in flight (register slots 0 and 1) while tile t
-        // multiplies and stores: with one, every tile waited a whole memory latency for its
-        // operand.  The loads are unconditional (past the end they re-read the last tile, never
-        // stored to LDS), so the compiler's wait counts stay exact.
-        char* lA = smem;
-        char* lB = smem + C::A_BYTES;
-        char* lX = lB + C::B_BYTES;
-        auto stream_load = [&](int t, auto slot) {
-            aim(min(t, t1 - 1));
-            if constexpr (STREAM_A) la.template load<decltype(slot)::value>(0, tid);
-            else lb.template load<decltype(slot)::value>(0, tid);
-            lx.template load<decltype(slot)::value>(0, tid);
-        };
-        auto stream_store = [&](auto slot) {
-            lds_barrier();   // every wave's fragment reads of the previous tile are done
-            if constexpr (STREAM_A) la.template store<decltype(slot)::value>(lA, tid);
-            else lb.template store<decltype(slot)::value>(lB, tid);
-            lx.template store<decltype(slot)::value>(lX, tid);
-            lds_barrier();
-        };
-        auto compute = [&](int t) {
-#pragma unroll
-            for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-                for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-            if (nk == 1) mma_step_split<C, STREAM_A>(lA, lB, lX, acc, wm0, wn0, lane);
-            store(t);
-        };
-        using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
-        aim(t0);
-        la.template load<0>(0, tid);
-        lb.template load<0>(0, tid);
-        lx.template load<0>(0, tid);
-        stream_load(t0 + 1, S1{});
-        la.template store<0>(lA, tid);
-        lb.template store<0>(lB, tid);
-        lx.template store<0>(lX, tid);
-        lds_barrier();
-        for (int t = t0; t < t1; t += 2) {
-            // slot 1 holds tile t + 1, slot 0 is free
-            stream_load(t + 2, S0{});
-            compute(t);
-            if (t + 1 >= t1) break;
-            stream_store(S1{});
-            // slot 0 holds tile t + 2, slot 1 is free
-            stream_load(t + 3, S1{});
-            compute(t + 1);
-            if (t + 2 >= t1) break;
-            stream_store(S0{});
-        }
-    } else {
-        for (int t = t0; t < t1; ++t) {
-            aim(t);
-            gemm_tile_split<C, STREAM_A>(la, lb, lx, nk, smem, acc, tid, wm0, wn0, lane);
-            store(t);
-            lds_barrier();   // the next tile's first LDS stores follow every wave's last reads
-        }
-    }
-}
-
-// Workgroup b of a weight-gradient launch: expert, the fixed tile index and its chunk [t0, t1) of
-// streamed tiles; the row count of the expert, kept inside the row tables.
+// Work item of a weight-gradient workgroup: expert e, the tile `fixed` of the operand held in LDS
+// and streamed tiles [t0, t1).  Items run expert by expert, then chunk of streamed tiles, with the
+// fixed tiles fastest: neighbouring workgroups stream the same fragments, which stay in L2.
 struct WgradWork {
     int e, fixed, t0, t1, count;
     int64_t seg0;
-    __device__ WgradWork(const Ws& ws, int n_fixed, int n_stream, int chunk = kWgradChunk) {
+    __device__ WgradWork(const Ws& ws, int n_fixed, int n_stream, int chunk) {
         const int chunks = (n_stream + chunk - 1) / chunk;
         e = blockIdx.x / (n_fixed * chunks);
         const int rem = blockIdx.x - e * (n_fixed * chunks);
-        fixed = rem / chunks;
-        t0 = (rem - fixed * chunks) * chunk;
+        const int c = rem / n_fixed;
+        fixed = rem - c * n_fixed;
+        t0 = c * chunk;
         t1 = min(n_stream, t0 + chunk);
         seg0 = ws.offsets[e];
         count = ws.counts[e];
@@ -357,192 +132,122 @@ struct WgradWork {
     }
 };
 
-// dW2[e] (packed like W2: column h, reduction index i) = sum_k (w act)[k][i] * dy[t_k][h]:
-// M = I (the packed reduction index), N = H (the packed column).  The dy gather is the shared
-// operand; the weighted activation tiles (hi and lo, from the dgrad's epilogue) stream.
-// Two waves per SIMD: the lo tile's loads and fragments need more than the 168 registers of three.
-template <class C>
-__global__ __launch_bounds__(C::NT, 2) void wgrad2_kernel(const uint16_t* __restrict__ dy, Dims d, Ws ws,
-                                                          uint16_t* __restrict__ dw2p) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
-    const int H = d.H, I = d.I;
-    const WgradWork wk(ws, H / C::BN, I / C::BM);
-
-    TRows<C::BM, C::NT, DirectRowSrc> la, lx;
-    la.src.base = ws.wact;
-    la.src.zeros = ws.zeros;
-    la.src.seg0 = wk.seg0;
-    la.src.count = wk.count;
-    la.src.width = I;
-    lx.src = la.src;
-    lx.src.base = ws.wact_lo;
-    TRows<C::BN, C::NT, GatherTokenSrc> lb;
-    lb.src.base = dy;
-    lb.src.zeros = ws.zeros;
-    lb.src.row_pair = ws.row_pair;
-    lb.src.seg0 = wk.seg0;
-    lb.src.count = wk.count;
-    lb.src.k = d.k;
-    lb.src.H = H;
-    lb.src.npairs = d.T * d.k;
-    uint16_t* out = dw2p + static_cast<int64_t>(wk.e) * H * I;
-    wgrad_tiles<C, true>(la, lb, lx, wk.count, wk.fixed, wk.t0, wk.t1, out, I,
-                         [&](int nt, int ni) { return static_cast<int64_t>(nt * C::BN + wn0 + ni * 32); }, smem,
-                         tid, wm0, wn0, lane);
-}
-
-// dW1[e] (packed like W1: L1 column n, reduction index h) = sum_k x[t_k][h] * dhgu[k][n]:
-// M = H (the packed reduction index), N = 2I (logical L1 columns; 32-column groups map to packed
-// column groups whole).  The x gather is the shared operand; dhgu tiles (hi and lo) stream.
-template <class C>
-__global__ __launch_bounds__(C::NT, 2) void wgrad1_kernel(const uint16_t* __restrict__ x, Dims d, Ws ws,
-                                                          uint16_t* __restrict__ dw1p) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / C::WN) * C::TM, wn0 = (wave % C::WN) * C::TN;
-    const int H = d.H, N2 = 2 * d.I;
-    const WgradWork wk(ws, H / C::BM, N2 / C::BN);
-
-    TRows<C::BM, C::NT, GatherTokenSrc> la;
-    la.src.base = x;
-    la.src.zeros = ws.zeros;
-    la.src.row_pair = ws.row_pair;
-    la.src.seg0 = wk.seg0;
-    la.src.count = wk.count;
-    la.src.k = d.k;
-    la.src.H = H;
-    la.src.npairs = d.T * d.k;
-    TRows<C::BN, C::NT, DirectRowSrc> lb, lx;
-    lb.src.base = ws.dhgu;
-    lb.src.zeros = ws.zeros;
-    lb.src.seg0 = wk.seg0;
-    lb.src.count = wk.count;
-    lb.src.width = N2;
-    lx.src = lb.src;
-    lx.src.base = ws.dhgu_lo;
-    uint16_t* out = dw1p + static_cast<int64_t>(wk.e) * N2 * H;
-    const int I = d.I;
-    wgrad_tiles<C, false>(la, lb, lx, wk.count, wk.fixed, wk.t0, wk.t1, out, H,
-                          [&](int nt, int ni) { return l1_packed_col(nt * C::BN + wn0 + ni * 32, I); }, smem, tid,
-                          wm0, wn0, lane);
-}
-
 // ---------------------------------------------------------------------------------------------
-// Weight gradients of experts with few rows, the intermediate operand streamed as fragments
+// Weight gradients of experts with few rows, the token rows streamed as fragments
 // ---------------------------------------------------------------------------------------------
-// The intermediate operand (w * act for dW2, dhgu for dW1), split into hi and lo parts, is first
-// rewritten (rows_to_k_major, PACKED) so that each 1 KB block is one MFMA operand: column group
-// n / 32 and 16 rows, lane L holding the 8 consecutive rows from 8 * (L / 32) of column n % 32.
-// The kernel then loads those fragments straight into registers, 16 bytes per lane, with no
-// LDS and no transposes; only the shared token-row operand (dy or x rows gathered through
-// row_pair) goes through LDS, once per workgroup.  A 128 x 128 output tile: with STREAM_A (dW2,
-// A = w act) the four waves split its M rows (each 32 rows x 128 columns), else (dW1, B = dhgu)
-// its N columns (each 128 rows x 32 columns), so every wave streams fragments no other wave
-// needs.  Each 16-deep substep issues the hi products, then the lo ones.  The fragments of tile
-// t + 1 are in flight while tile t multiplies and stores; with one K step of rows (the common
-// case) nothing synchronises the waves after the shared tile is loaded.
-template <bool STREAM_A>
-struct WgFrag {
-    static constexpr int FIX = 4;   // 32-wide blocks of the shared (non-streamed) tile dimension
-    static constexpr int BM = STREAM_A ? 128 : 32 * FIX, BN = STREAM_A ? 32 * FIX : 128, NT = 256;
-    static constexpr int MI = STREAM_A ? 1 : FIX, NI = STREAM_A ? FIX : 1;
-    static constexpr int SHARED_ROWS = STREAM_A ? BN : BM;   // rows (M or N index) of the LDS tile
-    static constexpr int LDS_BYTES = SHARED_ROWS * BK * 2;
-    static constexpr int NFRAG = 2 * (BK / 16);              // hi and lo fragment of each substep
-    static constexpr int CHUNK = 8;                           // output tiles per workgroup
+// The token rows (x for dW1, dy for dW2), gathered once into MFMA-fragment order
+// (rows_to_k_major<kTokenRows, PACKED>), stream into registers 16 bytes per lane, with no LDS and no
+// transposes, and the intermediate operand (dhgu or w act, hi and lo) stays in LDS, loaded from its
+// row-major ws rows once per workgroup of CHUNK output tiles.  A 128 x 128 output tile streams one
+// bf16 operand tile (the other choice, streaming the hi/lo pair and keeping the token rows in LDS,
+// streams twice the bytes and measured 5% slower for dW1).  The fragments of tile t + 1 are in
+// flight while tile t multiplies and stores; with one K step of rows (the common case) nothing
+// synchronises the waves after the LDS tiles are loaded.  The four waves split the token dimension H (A_TOK, dW1: each 32 rows of M = H x
+// 128 dhgu columns; else dW2: 128 rows of M = I x 32 columns of N = H).  The dhgu tile is in its
+// logical [gate | up] column order, so dW1's stores map each 32-column group to its packed column.
+template <bool A_TOK>
+struct WgTok {
+    static constexpr int FIX = 4;   // 32-wide blocks of the intermediate (LDS) tile dimension
+    static constexpr int NT = 256;
+    static constexpr int TILE_ROWS = 32 * FIX;                 // rows (M or N index) of each LDS tile
+    static constexpr int TILE_BYTES = TILE_ROWS * BK * 2;
+    static constexpr int LDS_BYTES = 2 * TILE_BYTES;           // hi and lo tiles
+    static constexpr int NFRAG = BK / 16;                      // one streamed fragment per substep
+    static constexpr int CHUNK = 8;                            // output tiles per workgroup
 };
 
-template <bool STREAM_A>
-__global__ __launch_bounds__(256, 3) void wgrad_frag_kernel(const uint16_t* __restrict__ tok,
-                                                            const uint16_t* __restrict__ p_hi,
-                                                            const uint16_t* __restrict__ p_lo, Dims d, Ws ws,
-                                                            uint16_t* __restrict__ out) {
-    using W = WgFrag<STREAM_A>;
+template <bool A_TOK>
+__global__ __launch_bounds__(256, 3) void wgrad_tok_kernel(const uint16_t* __restrict__ tp, Dims d, Ws ws,
+                                                           uint16_t* __restrict__ out) {
+    using W = WgTok<A_TOK>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = d.H, I = d.I;
-    const int M = STREAM_A ? I : H, N = STREAM_A ? H : 2 * I;   // packed reduction index, packed column
-    const WgradWork wk(ws, STREAM_A ? N / W::BN : M / W::BM, STREAM_A ? M / W::BM : N / W::BN, W::CHUNK);
-    // rows of the expert inside its segment (the tables keep count within it; clamped for safety)
-    int count = wk.count;
+    const int M = A_TOK ? H : I, N = A_TOK ? 2 * I : H;   // packed reduction index, packed column
+    const int F = A_TOK ? 2 * I : I;                      // the intermediate operand's width
+    const WgradWork wk(ws, F / W::TILE_ROWS, H / 128, W::CHUNK);
+    int count = wk.count;   // rows of the expert inside its segment (clamped for safety)
     {
         const int64_t seg1 = ws.offsets[wk.e + 1];
         if (seg1 - wk.seg0 < count) count = static_cast<int>(max(seg1 - wk.seg0, static_cast<int64_t>(0)));
     }
     const int nk = (count + BK - 1) / BK;
-    const int64_t Rq = ws.rows_cap / 16;                        // fragment blocks per column group
+    const int64_t Rq = ws.rows_cap / 16;   // fragment blocks per column group of the token rows
     uint16_t* o = out + static_cast<int64_t>(wk.e) * M * N;
 
-    TRows<W::SHARED_ROWS, W::NT, GatherTokenSrc> ls;
-    ls.src.base = tok;
-    ls.src.zeros = ws.zeros;
-    ls.src.row_pair = ws.row_pair;
-    ls.src.seg0 = wk.seg0;
-    ls.src.count = count;
-    ls.src.k = d.k;
-    ls.src.H = H;
-    ls.src.npairs = d.T * d.k;
-    ls.m_base = wk.fixed * W::SHARED_ROWS;
+    TRows<W::TILE_ROWS, W::NT, DirectRowSrc> lh, ll;
+    lh.src.base = A_TOK ? ws.dhgu : ws.wact;
+    lh.src.zeros = ws.zeros;
+    lh.src.seg0 = wk.seg0;
+    lh.src.count = count;
+    lh.src.width = F;
+    lh.m_base = wk.fixed * W::TILE_ROWS;
+    ll.src = lh.src;
+    ll.src.base = A_TOK ? ws.dhgu_lo : ws.wact_lo;
+    ll.m_base = lh.m_base;
+    char* const lH = smem;
+    char* const lL = smem + W::TILE_BYTES;
 
-    // fragment f = 2 * substep + part of K step kt of streamed tile t: the wave's column group of
-    // the streamed index (STREAM_A: M rows, else N columns); a substep past the expert's rows
-    // reads the zero row instead (its rows are not the expert's)
+    // substep f of K step kt of token tile t: the wave's 32 columns h of the tile; a substep past
+    // the expert's rows reads the zero row instead
     auto frag_addr = [&](int t, int kt, int f) -> const uint16_t* {
-        const int s16 = kt * BK + 16 * (f >> 1);
+        const int s16 = kt * BK + 16 * f;
         if (s16 >= count) return ws.zeros + (lane & 31) * 8;
-        const int64_t g = (static_cast<int64_t>(t) * (STREAM_A ? W::BM : W::BN) + 32 * wave) >> 5;
-        const int64_t blk = g * Rq + ((wk.seg0 + s16) >> 4);
-        return ((f & 1) ? p_lo : p_hi) + (blk * 64 + lane) * 8;
+        const int64_t g = (static_cast<int64_t>(t) * 128 + 32 * wave) >> 5;
+        return tp + ((g * Rq + ((wk.seg0 + s16) >> 4)) * 64 + lane) * 8;
     };
     bf16x8_t fr[2][W::NFRAG];
     auto load_frags = [&](int slot, int t, int kt) {
 #pragma unroll
         for (int f = 0; f < W::NFRAG; ++f) fr[slot][f] = *reinterpret_cast<const bf16x8_t*>(frag_addr(t, kt, f));
     };
-    f32x16_t acc[W::MI * W::NI];
+    f32x16_t acc[W::FIX];
     auto compute = [&](int slot) {
 #pragma unroll
         for (int sub = 0; sub < BK / 16; ++sub) {
-            bf16x8_t sh[W::MI * W::NI];   // shared-operand fragments of this substep (LDS)
+            bf16x8_t hi[W::FIX], lo[W::FIX];
             const int ch = 2 * sub + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < W::MI * W::NI; ++i)
-                sh[i] = *reinterpret_cast<const bf16x8_t*>(smem + lds_off(i * 32 + (lane & 31), ch));
+            for (int i = 0; i < W::FIX; ++i) {
+                hi[i] = *reinterpret_cast<const bf16x8_t*>(lH + lds_off(i * 32 + (lane & 31), ch));
+                lo[i] = *reinterpret_cast<const bf16x8_t*>(lL + lds_off(i * 32 + (lane & 31), ch));
+            }
+            const bf16x8_t f = fr[slot][sub];
 #pragma unroll
-            for (int part = 0; part < 2; ++part)
+            for (int i = 0; i < W::FIX; ++i)
+                acc[i] = A_TOK ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, hi[i], acc[i], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi[i], f, acc[i], 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < W::MI * W::NI; ++i) {
-                    const bf16x8_t f = fr[slot][2 * sub + part];
-                    acc[i] = STREAM_A ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, sh[i], acc[i], 0, 0, 0)
-                                      : __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[i], f, acc[i], 0, 0, 0);
-                }
+            for (int i = 0; i < W::FIX; ++i)
+                acc[i] = A_TOK ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, lo[i], acc[i], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo[i], f, acc[i], 0, 0, 0);
         }
     };
     auto zero = [&]() {
 #pragma unroll
-        for (int i = 0; i < W::MI * W::NI; ++i)
+        for (int i = 0; i < W::FIX; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
     };
     auto store = [&](int t) {
 #pragma unroll
-        for (int i = 0; i < W::MI * W::NI; ++i) {
-            // STREAM_A: M rows 32 * wave of streamed M tile t, N block i of the fixed N tile;
-            // else: M block i of the fixed M tile, N columns 32 * wave of streamed N tile t
-            const int64_t m0 = STREAM_A ? static_cast<int64_t>(t) * W::BM + 32 * wave
-                                        : static_cast<int64_t>(wk.fixed) * W::BM + 32 * i;
-            const int64_t n0 = STREAM_A ? static_cast<int64_t>(wk.fixed) * W::BN + 32 * i
-                                        : static_cast<int64_t>(t) * W::BN + 32 * wave;
+        for (int i = 0; i < W::FIX; ++i) {
+            // A_TOK: M rows h = 32 * wave of token tile t, N = the packed group of dhgu columns
+            // [32 i, 32 i + 32) of the fixed tile; else M rows i of the fixed tile, N columns h
+            const int64_t hcol = static_cast<int64_t>(t) * 128 + 32 * wave;
+            const int fcol = wk.fixed * W::TILE_ROWS + 32 * i;
+            const int64_t m0 = A_TOK ? hcol : static_cast<int64_t>(fcol);
+            const int64_t n0 = A_TOK ? l1_packed_col(fcol, I) : hcol;
             store_packed_block(o, M, n0, m0, acc[i], lane);
         }
     };
 
     if (nk <= 1) {
-        ls.template load<0>(0, tid);
+        lh.template load<0>(0, tid);
+        ll.template load<0>(0, tid);
         load_frags(0, wk.t0, 0);
-        ls.template store<0>(smem, tid);
+        lh.template store<0>(lH, tid);
+        ll.template store<0>(lL, tid);
         lds_barrier();
         for (int t = wk.t0; t < wk.t1; t += 2) {
             load_frags(1, min(t + 1, wk.t1 - 1), 0);   // unconditional: exact wait counts
@@ -559,10 +264,12 @@ __global__ __launch_bounds__(256, 3) void wgrad_frag_kernel(const uint16_t* __re
         for (int t = wk.t0; t < wk.t1; ++t) {
             zero();
             for (int kt = 0; kt < nk; ++kt) {
-                ls.template load<0>(kt, tid);
+                lh.template load<0>(kt, tid);
+                ll.template load<0>(kt, tid);
                 load_frags(0, t, kt);
                 lds_barrier();   // every wave's reads of the previous step are done
-                ls.template store<0>(smem, tid);
+                lh.template store<0>(lH, tid);
+                ll.template store<0>(lL, tid);
                 lds_barrier();
                 compute(0);
             }
@@ -586,29 +293,6 @@ int device_cu_count() {
     }
     return cached[dev];
 }
-
-// Persistent grid for a kernel: resident workgroups on the whole device, capped by the most
-// tiles the launch can have, rounded down to a multiple of the XCD count.
-template <class K>
-static int persistent_grid(K kernel, int threads, size_t lds, int64_t max_tiles) {
-    static_assert(sizeof(K) > 0, "");
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
-        per_cu = 1;
-    int64_t g = static_cast<int64_t>(per_cu) * device_cu_count();
-    if (g > max_tiles) g = max_tiles;
-    if (g >= kXcds) g -= g % kXcds;   // the same number of workgroups on every XCD
-    return static_cast<int>(g < 1 ? 1 : g);
-}
-
-template <class K>
-static void allow_lds(K kernel, size_t lds) {
-    if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-}
-
-using WG = Cfg<128, 128, 2, 2, 0>;   // weight-gradient tiles: K is an expert's rows, often one step
 
 // Expected rows per local expert (T * k / E, uniform routing) from which the backward GEMMs of an
 // expert run on the forward's pipeline instead of the streaming kernels above.
@@ -706,12 +390,12 @@ hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint1
 // column c of every ws row; PACKED false) or into MFMA fragments along the rows (PACKED true:
 // block (n / 32, r / 16) at (n / 32 * (R_max / 16) + r / 16) * 1 KB, lane n % 32 + 32 * ((r / 8) % 2)
 // holding the 8 rows of r's octet, n the packed column of c).  Sources: ws wact rows (the
-// weighted activation, hi part), the token rows of x or dy through row_pair, or ws dhgu rows
-// (packed by L1 column), hi or lo parts.  With hundreds of rows per expert the weight gradients
-// sum enough products that one bf16 rounding of the intermediate operand averages out, so the
-// forward-pipeline paths take the hi parts only; the few-rows kernels (wgrad_frag_kernel) take
-// both, in the PACKED layout.
-enum RowsSrc { kWactRows, kWactLoRows, kTokenRows, kDhguRows, kDhguLoRows };
+// weighted activation, hi part), the token rows of x or dy through row_pair (also the streamed
+// operand of wgrad_tok_kernel), or ws dhgu rows (packed by L1 column), hi part.  With hundreds of
+// rows per expert the weight gradients sum enough products that one bf16 rounding of the
+// intermediate operand averages out, so the forward-pipeline paths take the hi parts only; the
+// few-rows kernel takes both, from the ws rows.
+enum RowsSrc { kWactRows, kTokenRows, kDhguRows };
 
 template <int SRC, bool PACKED>
 __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __restrict__ tok, Dims d, Ws ws, int W,
@@ -736,9 +420,7 @@ __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __
             if (p >= 0 && p < npairs) {
                 const uint16_t* src;
                 if constexpr (SRC == kWactRows) src = ws.wact + r * W;
-                else if constexpr (SRC == kWactLoRows) src = ws.wact_lo + r * W;
                 else if constexpr (SRC == kDhguRows) src = ws.dhgu + r * W;
-                else if constexpr (SRC == kDhguLoRows) src = ws.dhgu_lo + r * W;
                 else src = tok + static_cast<int64_t>(p / d.k) * W;
                 v = *reinterpret_cast<const u32x4*>(src + c0 + 8 * ch);
             }
@@ -759,8 +441,7 @@ __global__ __launch_bounds__(256) void rows_to_k_major_kernel(const uint16_t* __
             if constexpr (!PACKED) {
                 dp = dst + static_cast<int64_t>(c0 + m) * Rcap + r;
             } else {
-                const int64_t n = (SRC == kDhguRows || SRC == kDhguLoRows) ? l1_packed_col(c0 + m, d.I)
-                                                                            : static_cast<int64_t>(c0 + m);
+                const int64_t n = SRC == kDhguRows ? l1_packed_col(c0 + m, d.I) : static_cast<int64_t>(c0 + m);
                 const int64_t blk = (n >> 5) * (Rcap / 16) + (r >> 4);
                 dp = dst + (blk * 64 + (n & 31) + 32 * ((r >> 3) & 1)) * 8;
             }
@@ -785,12 +466,21 @@ static bool wgrad_nt_use(const Dims& d, int M, int N) {
            static_cast<int64_t>(M) + N <= 2 * static_cast<int64_t>(d.H);
 }
 
-// The fragment-streaming weight gradients keep their operands in dead ws regions: dhgu hi (2I x
-// R_max bf16) in ws stage and its lo part in ws dact (R_max x I fp32, the same bytes); w act hi and
-// lo (2 x I x R_max bf16) in ws stage.  That needs I <= H (ws stage is R_max x H fp32) and tiles
-// of 128 (H and I multiples of 128, which the shape check requires).
-static bool wgrad_frag_fits(const Dims& d) {
-    return d.I <= d.H && d.H % WgFrag<false>::BM == 0 && d.H % WgFrag<true>::BN == 0 && d.I % 128 == 0;
+// Weight gradients of experts with few rows: the token rows (dy for dW2, x for dW1) in fragment
+// order in ws stage (2 * H * R_max of its 4 * H * R_max bytes, dead after the forward's combine)
+// stream through wgrad_tok_kernel; the hi / lo intermediate operand is read from its ws rows.
+template <bool A_TOK>
+static hipError_t wgrad_tok_launch(const Dims& d, const uint16_t* tok, const Ws& ws, uint16_t* out, hipStream_t s) {
+    if (!ws.stage) return hipErrorInvalidValue;
+    uint16_t* tp = reinterpret_cast<uint16_t*>(ws.stage);
+    const hipError_t e = rows_to_k_major<kTokenRows, true>(d, ws, tok, d.H, tp, s);
+    if (e != hipSuccess) return e;
+    using W = WgTok<A_TOK>;
+    const int F = A_TOK ? 2 * d.I : d.I;   // multiples of 128 (the shape check), as is H
+    const int blocks = d.EL * (F / W::TILE_ROWS) * ((d.H / 128 + W::CHUNK - 1) / W::CHUNK);
+    if (blocks <= 0) return hipSuccess;
+    wgrad_tok_kernel<A_TOK><<<blocks, W::NT, W::LDS_BYTES, s>>>(tp, d, ws, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const Ws& ws, uint16_t* dw2p, hipStream_t s) {
@@ -803,32 +493,7 @@ hipError_t launch_wgrad2(const Dims& d, const uint16_t* dy, const Ws& ws, uint16
         if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.I, d.H, ws, dw2p, s);
         return e;
     }
-    if (wgrad_frag_fits(d)) {   // w act (hi, lo) in fragment order: 4 * I * R_max bytes of ws stage
-        uint16_t* p_hi = reinterpret_cast<uint16_t*>(ws.stage);
-        uint16_t* p_lo = p_hi + static_cast<int64_t>(d.I) * ws.rows_cap;
-        hipError_t e = rows_to_k_major<kWactRows, true>(d, ws, nullptr, d.I, p_hi, s);
-        if (e == hipSuccess) e = rows_to_k_major<kWactLoRows, true>(d, ws, nullptr, d.I, p_lo, s);
-        if (e != hipSuccess) return e;
-        using W = WgFrag<true>;
-        const int blocks = d.EL * (d.H / W::BN) * ((d.I / W::BM + W::CHUNK - 1) / W::CHUNK);
-        if (blocks <= 0) return hipSuccess;
-        wgrad_frag_kernel<true><<<blocks, W::NT, W::LDS_BYTES, s>>>(dy, p_hi, p_lo, d, ws, dw2p);
-        return hipGetLastError();
-    }
-    const int blocks = d.EL * (d.H / WG::BN) * ((d.I / WG::BM + kWgradChunk - 1) / kWgradChunk);
-    if (blocks <= 0) return hipSuccess;
-    wgrad2_kernel<WG><<<blocks, WG::NT, WG::LDS_BYTES + WG::A_BYTES, s>>>(dy, d, ws, dw2p);
-    return hipGetLastError();
-}
-
-template <class C>
-static hipError_t wgrad1_launch(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
-    const int blocks = d.EL * (d.H / C::BM) * ((2 * d.I / C::BN + kWgradChunk - 1) / kWgradChunk);
-    if (blocks <= 0) return hipSuccess;
-    const size_t lds = C::LDS_BYTES + C::B_BYTES;   // A | B | lo part of B
-    allow_lds(wgrad1_kernel<C>, lds);
-    wgrad1_kernel<C><<<blocks, C::NT, lds, s>>>(x, d, ws, dw1p);
-    return hipGetLastError();
+    return wgrad_tok_launch<false>(d, dy, ws, dw2p, s);
 }
 
 hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_t* dw1p, hipStream_t s) {
@@ -841,19 +506,7 @@ hipError_t launch_wgrad1(const Dims& d, const uint16_t* x, const Ws& ws, uint16_
         if (e == hipSuccess) e = launch_wgrad_nt(d, at, bp, d.H, 2 * d.I, ws, dw1p, s);
         return e;
     }
-    if (wgrad_frag_fits(d) && ws.dact) {   // dhgu hi in fragment order in ws stage, lo in ws dact
-        uint16_t* p_hi = reinterpret_cast<uint16_t*>(ws.stage);
-        uint16_t* p_lo = reinterpret_cast<uint16_t*>(ws.dact);
-        hipError_t e = rows_to_k_major<kDhguRows, true>(d, ws, nullptr, 2 * d.I, p_hi, s);
-        if (e == hipSuccess) e = rows_to_k_major<kDhguLoRows, true>(d, ws, nullptr, 2 * d.I, p_lo, s);
-        if (e != hipSuccess) return e;
-        using W = WgFrag<false>;
-        const int blocks = d.EL * (d.H / W::BM) * ((2 * d.I / W::BN + W::CHUNK - 1) / W::CHUNK);
-        if (blocks <= 0) return hipSuccess;
-        wgrad_frag_kernel<false><<<blocks, W::NT, W::LDS_BYTES, s>>>(x, p_hi, p_lo, d, ws, dw1p);
-        return hipGetLastError();
-    }
-    return wgrad1_launch<WG>(d, x, ws, dw1p, s);
+    return wgrad_tok_launch<true>(d, x, ws, dw1p, s);
 }
 
 }  // namespace moe
