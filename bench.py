@@ -86,7 +86,7 @@ def copy_calibration():
     del src, dst
 
 
-def cpu_baseline(w, d, budget_s=15.0):
+def cpu_baseline(w, d, budget_s=20.0):
     """The oracle (test infrastructure) timed on the host cores on a bounded sample of tokens."""
     import oracle
     idx = d["topk_idx"]
