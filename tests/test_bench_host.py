@@ -1,0 +1,29 @@
+"""bench.py on the host: the one-GPU contract and where the oracle may enter (CPU only)."""
+import ast
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr and "one GPU" in r.stderr
+    assert r.stdout == ""   # no JSON line for a refused run
+
+
+def test_oracle_is_imported_only_by_the_cpu_baseline_legs():
+    tree = ast.parse(open(BENCH).read())
+    top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
+    assert not any("oracle" in ast.dump(n) for n in top), "bench.py imports the oracle at module level"
+    users = set()
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef):
+            for n in ast.walk(fn):
+                if isinstance(n, (ast.Import, ast.ImportFrom)) and "oracle" in ast.dump(n):
+                    users.add(fn.name)
+    assert users and all(u.startswith("cpu_baseline") for u in users), users
