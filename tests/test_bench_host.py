@@ -1,4 +1,4 @@
-"""bench.py on the host: the one-GPU contract and where the oracle may enter (CPU only)."""
+"""bench.py and the product sources on the host: the one-GPU contract and where the oracle may enter."""
 import ast
 import os
 import subprocess
@@ -27,3 +27,17 @@ def test_oracle_is_imported_only_by_the_cpu_baseline_legs():
                 if isinstance(n, (ast.Import, ast.ImportFrom)) and "oracle" in ast.dump(n):
                     users.add(fn.name)
     assert users and all(u.startswith("cpu_baseline") for u in users), users
+
+
+def test_product_sources_never_reference_the_oracle():
+    """The library, its headers and the binding stand alone: no file of the product path names the
+    oracle, so no step can route through it."""
+    hits = []
+    for base in ("token_dispatch_grouped_route_amd", "include"):
+        for dirpath, _, files in os.walk(os.path.join(ROOT, base)):
+            for f in files:
+                if f.endswith((".py", ".hip", ".h", ".cpp", ".c")):
+                    path = os.path.join(dirpath, f)
+                    if "oracle" in open(path, errors="replace").read():
+                        hits.append(os.path.relpath(path, ROOT))
+    assert not hits, hits
