@@ -25,8 +25,6 @@
 // wave's fragment reads spread over the banks); their sources are stored with M (or N) contiguous
 // in runs of 8 and K strided, so the TRows loader moves 4 K-rows x 8 elements per thread and
 // transposes them in registers into 8 rows x 4 K before the LDS store.
-#include <type_traits>
-
 #include "moe_internal.h"
 
 namespace moe {
