@@ -244,7 +244,12 @@ __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws w
 #pragma unroll
             for (int i = 0; i < kFinishChunks; ++i) {
                 const int c = c0 + 64 * i;
-                if (c < v8) *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * d.H + 8 * c) = pack8(acc[i]);
+                if (c < v8) {   // nontemporal, as the L2 epilogue's direct rows
+                    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+                    const uint4 p = pack8(acc[i]);
+                    const v4u val = {p.x, p.y, p.z, p.w};
+                    __builtin_nontemporal_store(val, reinterpret_cast<v4u*>(y + static_cast<int64_t>(t) * d.H + 8 * c));
+                }
             }
         }
     }

@@ -625,9 +625,9 @@ struct L1Body {
                 for (int r = 0; r < 16; ++r) {
                     const int64_t row = t.row0 + mi * 32 + acc_row(r, lane);
                     const float g = acc[mi][2 * q][r], u = acc[mi][2 * q + 1][r];
-                    if (hgu_out) {
-                        hgu_out[row * 2 * I + col] = g;
-                        hgu_out[row * 2 * I + I + col] = u;
+                    if (hgu_out) {   // nontemporal: read back only by the backward, after L2
+                        __builtin_nontemporal_store(g, hgu_out + row * 2 * I + col);
+                        __builtin_nontemporal_store(u, hgu_out + row * 2 * I + I + col);
                     }
                     if (act_out) act_out[row * I + col] = f32_to_bf16(silu_f32(g) * u);
                 }
@@ -785,7 +785,10 @@ struct L2Body {
                     if (ri[k].z) {
                         const uint32_t lo = f32_to_bf16(w * v[k].x) | (static_cast<uint32_t>(f32_to_bf16(w * v[k].y)) << 16);
                         const uint32_t hi = f32_to_bf16(w * v[k].z) | (static_cast<uint32_t>(f32_to_bf16(w * v[k].w)) << 16);
-                        *reinterpret_cast<uint2*>(y + static_cast<int64_t>(ri[k].x) * H + col) = make_uint2(lo, hi);
+                        // nontemporal: the layer's output is not read again by this layer's kernels
+                        typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+                        const v2u val = {lo, hi};
+                        __builtin_nontemporal_store(val, reinterpret_cast<v2u*>(y + static_cast<int64_t>(ri[k].x) * H + col));
                     } else {
                         *reinterpret_cast<float4*>(ws.stage + (t.row0 + m0 * 32 + rr) * static_cast<int64_t>(H) + col) =
                             make_float4(w * v[k].x, w * v[k].y, w * v[k].z, w * v[k].w);

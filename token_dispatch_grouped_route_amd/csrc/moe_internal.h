@@ -109,7 +109,7 @@ __host__ __device__ __forceinline__ int64_t l1_packed_col(int64_t n, int64_t I) 
 // 8*(L/32) of each 16-deep step; so lanes L and L^32 trade four values per step (one
 // v_permlane32_swap each, a VALU exchange of the two half-waves: lane L < 32 keeps a and gets the a
 // of lane L + 32, lane L >= 32 gets the b of lane L - 32 and keeps b), and every lane then stores
-// 16 bytes: one store instruction writes a whole 1 KB block.
+// 16 bytes: one store instruction writes a whole 1 KB block, with a nontemporal hint.
 __device__ __forceinline__ void store_packed_block(uint16_t* out, int64_t K, int64_t n0, int64_t k0,
                                                  const f32x16_t& acc, int lane) {
 #pragma unroll
@@ -127,7 +127,11 @@ __device__ __forceinline__ void store_packed_block(uint16_t* out, int64_t K, int
         for (int q = 0; q < 4; ++q)
             pk[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
         const int64_t blk = (n0 >> 5) * (K >> 4) + ((k0 >> 4) + st);
-        *reinterpret_cast<uint4*>(out + (blk * 64 + lane) * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        // nontemporal: the gradient is written once and not read again in the step, so it should
+        // not evict what the following kernels read
+        typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+        const v4u val = {pk[0], pk[1], pk[2], pk[3]};
+        __builtin_nontemporal_store(val, reinterpret_cast<v4u*>(out + (blk * 64 + lane) * 8));
     }
 }
 
