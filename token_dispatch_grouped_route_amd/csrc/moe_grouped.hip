@@ -54,10 +54,13 @@ constexpr int kMaxEL = 1024;
 constexpr int kEpiBatch = 4;   // L2 epilogue: LDS chunks read before their stores go out
 
 // NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most; OCC: workgroups per CU;
-// SLOTS: LDS slots of A and register stages of B (64-deep K each), loaded SLOTS - 1 slots ahead.
-template <int NI_, int MAXMI_, int OCC_, int SLOTS_>
+// SLOTS: LDS slots of A and register stages of B (64-deep K each), loaded SLOTS - 1 slots ahead;
+// NTB: B loads with a nontemporal hint (for launches whose weight panels are read by one or two M
+// tiles: the panel then does not evict the token rows that every N tile re-reads).
+template <int NI_, int MAXMI_, int OCC_, int SLOTS_, bool NTB_ = false>
 struct Tile {
     static constexpr int NI = NI_, MAXMI = MAXMI_, OCC = OCC_, SLOTS = SLOTS_;
+    static constexpr bool kNtB = NTB_;
     static_assert(MAXMI >= 1 && MAXMI <= 8, "M tile of 1..8 groups");
     static_assert(SLOTS == 3 || SLOTS == 4, "ring of three or four slots");
     static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
@@ -130,7 +133,8 @@ struct Pipe {
         const int jj = min(j, nslot - 1);
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni)
-            b[buf][ni][q] = *reinterpret_cast<const bf16x8_t*>(b_src[ni] + (4 * jj + q) * 1024);
+            b[buf][ni][q] = C::kNtB ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(b_src[ni] + (4 * jj + q) * 1024))
+                                    : *reinterpret_cast<const bf16x8_t*>(b_src[ni] + (4 * jj + q) * 1024);
     }
     __device__ __forceinline__ void b_issue(int j, int buf, char* __restrict__, int q) { b_issue(j, buf, q); }
     static constexpr int a_loads(int q) { return (MA + 3 - q) / 4; }
@@ -194,7 +198,7 @@ struct TrPipe {
             const int u = q * C::NI + v, kg = u / (2 * C::NI), nb = u % (2 * C::NI);
             __builtin_amdgcn_global_load_lds(
                 (g_void*)(b_src[nb & 1] + (2 * jj + kg) * b_grp + (nb >> 1) * 2048),
-                (l_void*)(slot + C::SLOT_A + wave * C::WAVE_B + u * 1024), 16, 0, 0);
+                (l_void*)(slot + C::SLOT_A + wave * C::WAVE_B + u * 1024), 16, 0, 2);   // nontemporal
         }
     }
     // B fragments of 16-deep step kb of a slot
@@ -1110,6 +1114,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void dgrad_tile_kernel(const uint16_
 using L1Tile = Tile<2, 8, 1, 4>;
 using L2Tile = Tile<2, 8, 1, 4>;
 using L2TileNarrow = Tile<1, 8, 1, 4>;
+using L1TileNt = Tile<2, 8, 1, 4, true>;
+using L2TileNt = Tile<2, 8, 1, 4, true>;
+using L2TileNarrowNt = Tile<1, 8, 1, 4, true>;
 using WgTile = Tile<2, 8, 1, 3>;   // three ring slots measured slightly faster than four here
 // Few-rows dgrads: M tiles of up to 96 rows (an expert of the wide share in one tile, its weights
 // streamed once), three ring slots of 44 KB.
@@ -1165,18 +1172,29 @@ hipError_t launch_wgrad_nt(const Dims& d, const uint16_t* at, const uint16_t* bp
     return hipGetLastError();
 }
 
+// Weight panels stream with a nontemporal hint when an expert's rows fill at most two 256-row M
+// tiles (expected rows T * k / E <= 512, uniform routing): with more M tiles re-reading each panel
+// from L2 the hint costs more than it saves (measured at page scale).
+static bool weights_nontemporal(const Dims& d) {
+    return static_cast<int64_t>(d.T) * d.k <= 512 * static_cast<int64_t>(d.E);
+}
+
 // L1 N tiles are 256 columns (2I is a multiple of 256); L2 N tiles 256 columns when H allows, else 128.
 hipError_t launch_gemm1(const Dims& d, const uint16_t* x, const uint16_t* w1f, const Ws& ws, uint16_t* act_out,
                         float* hgu_out, hipStream_t s) {
     if (d.EL > kMaxEL) return hipErrorInvalidValue;
-    return l1_launch<L1Tile>(d, x, w1f, ws, act_out, hgu_out, s);
+    return weights_nontemporal(d) ? l1_launch<L1TileNt>(d, x, w1f, ws, act_out, hgu_out, s)
+                                  : l1_launch<L1Tile>(d, x, w1f, ws, act_out, hgu_out, s);
 }
 
 hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16_t* w2f, const float* topk_w,
                                 const Ws& ws, uint16_t* y, hipStream_t s) {
     if (d.EL > kMaxEL) return hipErrorInvalidValue;
-    return d.H % L2Tile::BN == 0 ? l2_launch<L2Tile>(d, act, w2f, topk_w, ws, y, s)
-                                 : l2_launch<L2TileNarrow>(d, act, w2f, topk_w, ws, y, s);
+    const bool nt = weights_nontemporal(d), wide = d.H % L2Tile::BN == 0;
+    if (nt) return wide ? l2_launch<L2TileNt>(d, act, w2f, topk_w, ws, y, s)
+                        : l2_launch<L2TileNarrowNt>(d, act, w2f, topk_w, ws, y, s);
+    return wide ? l2_launch<L2Tile>(d, act, w2f, topk_w, ws, y, s)
+                : l2_launch<L2TileNarrow>(d, act, w2f, topk_w, ws, y, s);
 }
 
 }  // namespace moe
