@@ -203,9 +203,11 @@ hipError_t launch_swiglu_bwd(const Dims& d, const Ws& ws, hipStream_t s) {
 // pairs in slot order, so a token costs one dependent load before its stage rows stream.  A pass
 // covers up to kFinishChunks 32-byte chunks per lane: all of one pair row's chunks are loaded
 // before they are added, so a pass waits once per local pair, not once per chunk; each element is
-// still summed in slot order.
+// still summed in slot order.  With NT the staged rows are read with a nontemporal hint (the L1
+// dgrad's, which its few-rows kernel also stores nontemporally).
 constexpr int kFinishChunks = 4;
 
+template <bool NT>
 __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws ws, uint16_t* __restrict__ y) {
     const int lane = threadIdx.x & 63;
     const int waves = gridDim.x * (kEwThreads / 64);
@@ -229,8 +231,16 @@ __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws w
                 for (int i = 0; i < kFinishChunks; ++i) {
                     const int c = c0 + 64 * i;
                     if (c < v8) {
-                        lo[i] = src[2 * c];
-                        hi[i] = src[2 * c + 1];
+                        if constexpr (NT) {
+                            typedef float v4f __attribute__((ext_vector_type(4)));
+                            const v4f l4 = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + 2 * c));
+                            const v4f h4 = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + 2 * c + 1));
+                            lo[i] = make_float4(l4.x, l4.y, l4.z, l4.w);
+                            hi[i] = make_float4(h4.x, h4.y, h4.z, h4.w);
+                        } else {
+                            lo[i] = src[2 * c];
+                            hi[i] = src[2 * c + 1];
+                        }
                     }
                 }
 #pragma unroll
@@ -255,10 +265,11 @@ __global__ __launch_bounds__(kEwThreads) void combine_finish_kernel(Dims d, Ws w
     }
 }
 
-hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s) {
+hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s, bool nt_rows) {
     if (d.T <= 0) return hipSuccess;
     const int cap = device_cu_count() * 8, want = (d.T + kEwThreads / 64 - 1) / (kEwThreads / 64);
-    combine_finish_kernel<<<want < cap ? want : cap, kEwThreads, 0, s>>>(d, ws, y);
+    if (nt_rows) combine_finish_kernel<true><<<want < cap ? want : cap, kEwThreads, 0, s>>>(d, ws, y);
+    else combine_finish_kernel<false><<<want < cap ? want : cap, kEwThreads, 0, s>>>(d, ws, y);
     return hipGetLastError();
 }
 

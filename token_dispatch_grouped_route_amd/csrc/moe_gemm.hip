@@ -377,7 +377,7 @@ hipError_t launch_dgrad1(const Dims& d, const uint16_t* w1p, const Ws& ws, uint1
         return e;
     }
     const hipError_t e = launch_dgrad1_tr(d, w1p, ws, dx, s);
-    return e == hipSuccess ? launch_combine_finish(d, ws, dx, s) : e;
+    return e == hipSuccess ? launch_combine_finish(d, ws, dx, s, true) : e;
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -61,6 +61,7 @@ template <int NI_, int MAXMI_, int OCC_, int SLOTS_, bool NTB_ = false>
 struct Tile {
     static constexpr int NI = NI_, MAXMI = MAXMI_, OCC = OCC_, SLOTS = SLOTS_;
     static constexpr bool kNtB = NTB_;
+    static constexpr bool kNtStage = false;   // fp32 combine rows stored temporally (read back soon)
     static_assert(MAXMI >= 1 && MAXMI <= 8, "M tile of 1..8 groups");
     static_assert(SLOTS == 3 || SLOTS == 4, "ring of three or four slots");
     static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
@@ -85,6 +86,7 @@ struct TrTile {
     static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
     static constexpr int NT = 64 * kWaves;
     static constexpr bool kTrB = true;
+    static constexpr bool kNtStage = true;   // the L1 dgrad's combine rows: nontemporal (measured faster)
     static constexpr int SLOT_A = BM * 128;
     static constexpr int WAVE_B = NI * 4096;   // one wave's packed blocks of a slot
     static constexpr int SLOT = SLOT_A + kWaves * WAVE_B;
@@ -794,8 +796,14 @@ struct L2Body {
                         const v2u val = {lo, hi};
                         __builtin_nontemporal_store(val, reinterpret_cast<v2u*>(y + static_cast<int64_t>(ri[k].x) * H + col));
                     } else {
-                        *reinterpret_cast<float4*>(ws.stage + (t.row0 + m0 * 32 + rr) * static_cast<int64_t>(H) + col) =
-                            make_float4(w * v[k].x, w * v[k].y, w * v[k].z, w * v[k].w);
+                        float* dst = ws.stage + (t.row0 + m0 * 32 + rr) * static_cast<int64_t>(H) + col;
+                        if constexpr (C::kNtStage) {
+                            typedef float v4f __attribute__((ext_vector_type(4)));
+                            const v4f sv = {w * v[k].x, w * v[k].y, w * v[k].z, w * v[k].w};
+                            __builtin_nontemporal_store(sv, reinterpret_cast<v4f*>(dst));
+                        } else {
+                            *reinterpret_cast<float4*>(dst) = make_float4(w * v[k].x, w * v[k].y, w * v[k].z, w * v[k].w);
+                        }
                     }
                 }
             }

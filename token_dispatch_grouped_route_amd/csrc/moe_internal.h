@@ -147,7 +147,7 @@ hipError_t launch_swiglu(const Dims& d, const float* hgu, const Ws& ws, uint16_t
                          hipStream_t s);
 hipError_t launch_gemm2_combine(const Dims& d, const uint16_t* act, const uint16_t* w2p,
                                 const float* topk_w, const Ws& ws, uint16_t* y, hipStream_t s);
-hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s);
+hipError_t launch_combine_finish(const Dims& d, const Ws& ws, uint16_t* y, hipStream_t s, bool nt_rows = false);
 hipError_t launch_dgrad(const Dims& d, const uint16_t* dy, const float* topk_w,
                         const uint16_t* w2p, const Ws& ws, int fuse_swiglu_bwd, bool topk_w_grad,
                         hipStream_t s);
