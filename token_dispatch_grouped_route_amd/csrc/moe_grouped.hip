@@ -770,16 +770,36 @@ struct L2Body {
                                 acc[m0 + mm < MA ? m0 + mm : 0][ni][r];
             lds_barrier();   // also publishes s_row (first pass)
             const int rows = (m0 + GP <= MA ? GP : MA - m0) * 32;
+            // The pass's row records: lane j reads row j's (one contiguous 16-byte-per-lane LDS
+            // read; the empty asm keeps the unused fourth word in it), and readlane hands each
+            // row's record out, since a row is wave-uniform (half-wave-uniform on 128-column
+            // tiles). Every lane reading the same 12-byte record, row by row, costs LDS bank
+            // conflicts.
+            static_assert(GP * 32 == 64, "one record per lane");
+            int4 rin = make_int4(-1, 0, 0, 0);
+            if (lane < rows) rin = s_row[m0 * 32 + lane];
+            asm volatile("" : "+v"(rin.w));
+            const int r_lo = __builtin_amdgcn_readfirstlane(rrow);   // the first half-wave's row
 #pragma unroll
             for (int k0 = 0; k0 < ITER; k0 += kEpiBatch) {
-                float4 v[kEpiBatch];
+                typedef float v4f __attribute__((ext_vector_type(4)));   // read as one ds_read_b128
+                v4f v[kEpiBatch];
                 int4 ri[kEpiBatch];
 #pragma unroll
                 for (int k = 0; k < kEpiBatch; ++k) {
                     const int rr = rrow + (k0 + k) * RSTEP;
                     if ((k0 + k) * RSTEP < rows) {   // rows is a multiple of 32 >= RSTEP
-                        v[k] = *reinterpret_cast<const float4*>(tile + rr * LD + rcol);
-                        ri[k] = s_row[m0 * 32 + rr];
+                        v[k] = *reinterpret_cast<const v4f*>(tile + rr * LD + rcol);
+                        const int sl = r_lo + (k0 + k) * RSTEP;
+                        if constexpr (CH == 64) {   // a wave is one row
+                            ri[k] = make_int4(__builtin_amdgcn_readlane(rin.x, sl), __builtin_amdgcn_readlane(rin.y, sl),
+                                              __builtin_amdgcn_readlane(rin.z, sl), 0);
+                        } else {                    // the second half-wave's row is the next one
+                            const int x0 = __builtin_amdgcn_readlane(rin.x, sl), x1 = __builtin_amdgcn_readlane(rin.x, sl + 1);
+                            const int y0 = __builtin_amdgcn_readlane(rin.y, sl), y1 = __builtin_amdgcn_readlane(rin.y, sl + 1);
+                            const int z0 = __builtin_amdgcn_readlane(rin.z, sl), z1 = __builtin_amdgcn_readlane(rin.z, sl + 1);
+                            ri[k] = lane < 32 ? make_int4(x0, y0, z0, 0) : make_int4(x1, y1, z1, 0);
+                        }
                     }
                 }
 #pragma unroll
@@ -798,7 +818,6 @@ struct L2Body {
                     } else {
                         float* dst = ws.stage + (t.row0 + m0 * 32 + rr) * static_cast<int64_t>(H) + col;
                         if constexpr (C::kNtStage) {
-                            typedef float v4f __attribute__((ext_vector_type(4)));
                             const v4f sv = {w * v[k].x, w * v[k].y, w * v[k].z, w * v[k].w};
                             __builtin_nontemporal_store(sv, reinterpret_cast<v4f*>(dst));
                         } else {
