@@ -121,6 +121,47 @@ def test_forward_reduced_full_compare(w, bm):
     assert np.all(got[nloc == 0] == 0.0)
 
 
+# Experts of 9 and 18 groups of 32 rows (one and two M tiles of nine groups in the L1 tile that
+# takes nine, the ninth group's MFMAs in VGPR form) next to experts of 7-13 and 26 groups (tiles
+# of 5-8 groups).  H = 640: a K loop with a tail slot and 128-column L2 tiles.
+NINE = mw.Workload("reduced_nine", T=1500, H=640, I=256, E=8, EL=8, k=2, zipf_s=0.6)
+
+
+def nine_group_tiles(counts):
+    """M tiles of nine 32-row groups: an expert of g <= 18 groups is cut into ceil(g / 9) tiles,
+    a larger one into ceil(g / 8), the group counts of its tiles differing by at most one."""
+    g = -(-np.asarray(counts) // 32)
+    tiles = np.where(g <= 18, -(-g // 9), -(-g // 8))
+    base, rem = g // np.maximum(tiles, 1), g % np.maximum(tiles, 1)
+    return int(np.sum(np.where(base == 9, tiles, np.where(base == 8, rem, 0))))
+
+
+@pytest.mark.parametrize("bm", [32, 128])
+def test_forward_nine_group_tiles(bm):
+    d = mw.inputs(NINE, 5)
+    assert NINE.T * NINE.k <= 512 * NINE.E   # the launch that uses nine-group tiles
+    counts = np.bincount(d["topk_idx"].ravel(), minlength=NINE.E)
+    assert nine_group_tiles(counts) >= 3, counts
+    ns = layer(NINE, d, bm)
+    s = ns.shape
+    R = moe.workspace_layout(s)["rows_capacity"]
+    hgu = torch.zeros(R, 2 * NINE.I, dtype=torch.float32, device="cuda")
+    act = torch.zeros(R, NINE.I, dtype=torch.bfloat16, device="cuda")
+    moe.route_prologue(s, ns.idx, ns.ws)
+    moe.dispatch_gemm1(s, ns.x, ns.W1p, ns.ws, act_out=act, hgu_out=hgu)
+    moe.forward(s, ns.x, ns.idx, ns.wts, ns.W1p, ns.W2p, ns.ws, ns.y)
+    torch.cuda.synchronize()
+    t = tables(ns)
+    real = np.nonzero(t["row_pair"] >= 0)[0]
+    h_ref, a_ref = oracle.l1_rows(d["x"], d["topk_idx"], d["W1"], NINE.E, NINE.e_lo, t["row_pair"][real])
+    check_f32(f64_host(hgu)[real], h_ref, TOL, "hgu (nine-group tiles, bm %d)" % bm)
+    check_bf16(f64_host(act)[real], a_ref, TOL, "act (nine-group tiles, bm %d)" % bm)
+    pad = np.setdiff1d(np.arange(t["num_rows"]), real)
+    assert np.all(f64_host(act)[pad] == 0.0) and np.all(f64_host(hgu)[pad] == 0.0)
+    ref = oracle.forward(d["x"], d["topk_idx"], d["topk_weights"], d["W1"], d["W2"], E=NINE.E)
+    check_bf16(f64_host(ns.y), ref, TOL, "y (nine-group tiles, bm %d)" % bm)
+
+
 def test_forward_tiny_workload_full_compare():
     w = mw.get(0)
     d = mw.inputs(w, 0)

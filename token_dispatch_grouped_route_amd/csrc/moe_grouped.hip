@@ -2,11 +2,13 @@
 // accumulation), reading fragment-packed weights ("Mega MoE" page, Pipeline: the L1 grouped
 // GEMM with the dispatch gather and SwiGLU, and the L2 grouped GEMM with the top-k combine).
 //
-// Tiles.  An M tile is up to eight 32-row groups of one expert's segment (256 rows), covering only
-// the groups that hold real rows: rows past the last real group are padding and get no MFMA work.
-// An expert with more than eight groups is cut into M tiles of equal size (the last one padded
-// with zero rows), so the workgroups that stream the same weight panel progress at the same rate
-// and the later reads of the panel hit L2.  An N tile is BN = 4 waves
+// Tiles.  An M tile is up to eight 32-row groups of one expert's segment (256 rows; nine, for
+// experts of at most 18 groups, in the forward L1 of launches whose experts average at most 512
+// rows), covering only the groups that
+// hold real rows: rows past the last real group are padding and get no MFMA work.  An expert with
+// more groups is cut into M tiles whose group counts differ by at most one, so the workgroups
+// that stream the same weight panel progress at nearly the same rate and the later reads of the
+// panel hit L2.  An N tile is BN = 4 waves
 // x 32*NI columns; every wave (one per SIMD) computes all rows of its own 32*NI columns.  So a
 // weight panel (expert, N tile) is streamed by one workgroup per M tile, and an expert's token
 // rows are read by the workgroups of all its N tiles at the same time, from L2.
@@ -16,14 +18,14 @@
 //      the waves, so it goes through LDS, straight from memory (global_load_lds_dwordx4: no
 //      staging registers, no LDS store instructions) into a ring of three 64-deep K slots; each
 //      load instruction fills 8 rows x 128 bytes, chunks XOR-swizzled so fragment reads spread
-//      over the banks.
+//      over the banks.  The ring has SLOTS 64-deep K slots (four; three for 288-row tiles).
 //   B  packed expert weights (moe_pack_weights): every 1 KB block is one MFMA B operand of a
 //      32-column group and a 16-deep K step.  Each wave owns its column groups, so B never
 //      touches LDS: a wave streams its blocks straight into registers, one contiguous 1 KB load
-//      per block, through a ring of three 64-deep K stages.
-// Both are loaded two slots ahead of their MFMAs.  Per slot: wait for this wave's loads of the
-// slot, one barrier, then the slot's four 16-deep MFMA steps, each issuing a quarter of the loads
-// of slot + 2 and reading the next step's fragments between its MFMAs.  The LDS slots
+//      per block, through a ring of SLOTS 64-deep K stages.
+// Both are loaded SLOTS - 1 slots ahead of their MFMAs.  Per slot: wait for this wave's loads of
+// the slot, one barrier, then the slot's four 16-deep MFMA steps, each issuing a quarter of the
+// loads of slot + SLOTS - 1 and reading the next step's fragments between its MFMAs.  The LDS slots
 // are distinct noalias pointers of the K loop, so the compiler does not make fragment reads wait
 // for the DMA loads into other slots.
 //
@@ -53,7 +55,8 @@ constexpr int kXcds = 8;
 constexpr int kMaxEL = 1024;
 constexpr int kEpiBatch = 4;   // L2 epilogue: LDS chunks read before their stores go out
 
-// NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most; OCC: workgroups per CU;
+// NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most (nine only for the L1
+// tile, whose ninth group runs in VGPR-form MFMAs, see slot_step); OCC: workgroups per CU;
 // SLOTS: LDS slots of A and register stages of B (64-deep K each), loaded SLOTS - 1 slots ahead;
 // NTB: B loads with a nontemporal hint (for launches whose weight panels are read by one or two M
 // tiles: the panel then does not evict the token rows that every N tile re-reads).
@@ -62,7 +65,7 @@ struct Tile {
     static constexpr int NI = NI_, MAXMI = MAXMI_, OCC = OCC_, SLOTS = SLOTS_;
     static constexpr bool kNtB = NTB_;
     static constexpr bool kNtStage = false;   // fp32 combine rows stored temporally (read back soon)
-    static_assert(MAXMI >= 1 && MAXMI <= 8, "M tile of 1..8 groups");
+    static_assert(MAXMI >= 1 && MAXMI <= 9, "M tile of 1..9 groups");
     static_assert(SLOTS == 3 || SLOTS == 4, "ring of three or four slots");
     static constexpr int BM = 32 * MAXMI, BN = kWaves * 32 * NI;
     static constexpr int NT = 64 * kWaves;
@@ -249,6 +252,49 @@ __device__ __forceinline__ void slot_step(PipeOf<C, MA>& p, int j, char* __restr
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's fragment reads are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!C::kTrB && MA == 9) {
+        // Nine groups: 288 accumulator registers, more than the 256 AGPRs, and the compiler keeps
+        // every MFMA it emits in AGPR form (it then moves accumulators through scratch).  So
+        // groups 0-7 use the builtin (AGPRs) and group 8 an inline MFMA in VGPR form; k_loop adds
+        // the wait states the compiler cannot see.  Dependent accumulation into the same
+        // registers needs none.  The fragments roll: group mi's fragment of step kb + 1 is read
+        // as soon as its MFMAs of step kb are issued (MA + 1 fragments live, not 2 MA).
+        bf16x8_t a[MA];
+        read_frags<C, MA>(a, slots[U], 0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (ISSUE) {
+                p.a_issue(j + C::SLOTS - 1, slots[FAR], kb);
+                p.b_issue(j + C::SLOTS - 1, FAR, slots[FAR], kb);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MA; ++mi) {
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni) {
+                    if (mi < 8)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], p.b[U][ni][kb], acc[mi][ni], 0, 0, 0);
+                    else
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                                     : "+v"(acc[mi][ni])
+                                     : "v"(a[mi]), "v"(p.b[U][ni][kb]));
+                }
+                if (kb < 3)
+                    a[mi] = *reinterpret_cast<const bf16x8_t*>(slots[U] + lds_off(mi * 32 + (lane & 31), 2 * (kb + 1) + (lane >> 5)));
+            }
+            // the builtin MFMAs, each group's fragment read after its last one, the loads
+            constexpr int NM = 8 * C::NI;
+            const int nv = ISSUE ? PipeOf<C, MA>::a_loads(kb) + C::NI : 0;
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         // MFMA
+                if (kb < 3 && i % C::NI == C::NI - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                             // global load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+    }
     bf16x8_t a[2][MA];
     bf16x8_t bt[2][C::NI];   // transposed B fragments (kTrB)
     read_frags<C, MA>(a[0], slots[U], 0, lane);
@@ -358,11 +404,19 @@ __device__ __forceinline__ void k_loop(PipeOf<C, MA>& p, char* __restrict__ s0, 
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    if constexpr (!C::kTrB && MA == 9) {
+        // VALU write -> MFMA SrcC read of the VGPR-form group: 2 wait states (the operands tie
+        // the wait to those registers, so no access to them moves across it)
+        static_assert(C::NI == 2, "two VGPR-form accumulators");
+        asm volatile("s_nop 4" : "+v"(acc[8][0]), "+v"(acc[8][1]));
+    }
     __builtin_amdgcn_sched_barrier(0);
     prologue_issue<C, MA, 0>(p, s0, s1, s2);
     int j = 0;
     for (; j + C::SLOTS <= p.nslot; j += C::SLOTS) loop_turn<C, MA, 0>(p, j, s0, s1, s2, s3, acc, lane);
     loop_tail<C, MA, 0>(p, j, s0, s1, s2, s3, acc, lane);
+    // MFMA (16 passes) write -> VALU, LDS or memory read of the result: 18 wait states (19 given)
+    if constexpr (!C::kTrB && MA == 9) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[8][0]), "+v"(acc[8][1]));
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
@@ -377,8 +431,15 @@ __device__ __forceinline__ int real_groups(const Ws& ws, int e) {
     const int c = ws.counts[e];
     return c > 0 ? (c + 31) >> 5 : 0;
 }
+// M tiles of an expert of `groups` 32-row groups.  Nine-group tiles cost a few percent more per
+// group than eight-group ones (three ring slots, rolling fragments), which pays where they save a
+// weight-panel stream on an expert of at most two tiles (9, 17 or 18 groups); larger experts keep
+// tiles of at most eight groups.
 template <int MAXMI>
-__device__ __forceinline__ int m_tiles_of(int groups) { return (groups + MAXMI - 1) / MAXMI; }
+__device__ __forceinline__ int m_tiles_of(int groups) {
+    if constexpr (MAXMI == 9) return groups <= 18 ? (groups + 8) / 9 : (groups + 7) / 8;
+    return (groups + MAXMI - 1) / MAXMI;
+}
 
 // s_pref[e] = M tiles of experts [0, e), e in [0, EL]; s_q[e] = groups per M tile of expert e
 // (0: no rows); returns the total.
@@ -417,8 +478,9 @@ __device__ int m_tile_prefix(const Ws& ws, int EL, int* s_pref, int* s_q, int* s
 }
 
 struct TileRef {
-    int e, nt, row0, groups, real_rows, last;   // groups computed (some may be zero rows); rows that
-                                                // belong to the tile; last: holds the expert's last group
+    int e, nt, row0, groups, real_rows, last;   // groups (each holds real rows; the expert's last may
+                                                // end in padding rows), 32 x groups; last: holds the
+                                                // expert's last group
 };
 
 // Expert owning list position pos: expert e owns positions [n_tiles * s_pref[e],
@@ -442,11 +504,12 @@ __device__ __forceinline__ TileRef decode(const Ws& ws, int EL, int n_tiles, int
     const int local = pos - s_pref[lo] * n_tiles;
     t.nt = local / mt_e;
     const int mt = local - t.nt * mt_e;
-    const int g = real_groups(ws, lo), q = (g + mt_e - 1) / mt_e;   // groups per M tile
-    const int g0 = mt * q;
+    // the expert's g groups cut as evenly as possible: the first g % mt_e tiles take one more
+    const int g = real_groups(ws, lo), base = g / mt_e, rem = g - base * mt_e;
+    const int q = base + (mt < rem ? 1 : 0);
     t.groups = q;
-    t.row0 = ws.offsets[lo] + 32 * g0;
-    t.real_rows = 32 * max(0, min(q, g - g0));
+    t.row0 = ws.offsets[lo] + 32 * (mt * base + min(mt, rem));
+    t.real_rows = 32 * q;
     t.last = mt == mt_e - 1;
     return t;
 }
@@ -568,6 +631,7 @@ __device__ __forceinline__ void run_tiles(const Dims& d, const Ws& ws, int n_til
                 case 6: if constexpr (C::MAXMI >= 6) body.template run<6>(t); break;
                 case 7: if constexpr (C::MAXMI >= 7) body.template run<7>(t); break;
                 case 8: if constexpr (C::MAXMI >= 8) body.template run<8>(t); break;
+                case 9: if constexpr (C::MAXMI >= 9) body.template run<9>(t); break;
                 default: break;
             }
         }
@@ -1141,7 +1205,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void dgrad_tile_kernel(const uint16_
 using L1Tile = Tile<2, 8, 1, 4>;
 using L2Tile = Tile<2, 8, 1, 4>;
 using L2TileNarrow = Tile<1, 8, 1, 4>;
-using L1TileNt = Tile<2, 8, 1, 4, true>;
+// Nine-group L1 tiles (three ring slots: 288-row slots): an expert of 257-288 rows, about half
+// of them when rows per expert average 256, runs as one tile, so its weight panels stream once
+// instead of twice (two tiles of five and four groups).
+using L1TileNt = Tile<2, 9, 1, 3, true>;
 using L2TileNt = Tile<2, 8, 1, 4, true>;
 using L2TileNarrowNt = Tile<1, 8, 1, 4, true>;
 using WgTile = Tile<2, 8, 1, 3>;   // three ring slots measured slightly faster than four here
