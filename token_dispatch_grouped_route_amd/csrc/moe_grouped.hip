@@ -3,8 +3,8 @@
 // GEMM with the dispatch gather and SwiGLU, and the L2 grouped GEMM with the top-k combine).
 //
 // Tiles.  An M tile is up to eight 32-row groups of one expert's segment (256 rows; nine, for
-// experts of at most 18 groups, in the forward L1 of launches whose experts average at most 512
-// rows), covering only the groups that
+// experts of at most 18 groups, in the forward GEMMs of launches whose experts average at most
+// 512 rows), covering only the groups that
 // hold real rows: rows past the last real group are padding and get no MFMA work.  An expert with
 // more groups is cut into M tiles whose group counts differ by at most one, so the workgroups
 // that stream the same weight panel progress at nearly the same rate and the later reads of the
@@ -55,8 +55,8 @@ constexpr int kXcds = 8;
 constexpr int kMaxEL = 1024;
 constexpr int kEpiBatch = 4;   // L2 epilogue: LDS chunks read before their stores go out
 
-// NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most (nine only for the L1
-// tile, whose ninth group runs in VGPR-form MFMAs, see slot_step); OCC: workgroups per CU;
+// NI: 32-column groups per wave; MAXMI: 32-row groups per M tile, at most (nine only for the
+// forward tiles, whose ninth group runs in VGPR-form MFMAs, see slot_step); OCC: workgroups per CU;
 // SLOTS: LDS slots of A and register stages of B (64-deep K each), loaded SLOTS - 1 slots ahead;
 // NTB: B loads with a nontemporal hint (for launches whose weight panels are read by one or two M
 // tiles: the panel then does not evict the token rows that every N tile re-reads).
@@ -757,12 +757,14 @@ struct L2Body {
     template <int MA>
     __device__ __forceinline__ void run(const TileRef& t) {
         int4* s_row = reinterpret_cast<int4*>(smem + C::RING_BYTES);   // token (-1: none), weight, direct
-        static_assert(C::BM <= C::NT, "one row per thread");
+        constexpr int RPT = (C::BM + C::NT - 1) / C::NT;   // rows per thread
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int H = d.H, I = d.I, npairs = d.T * d.k;
         // the row's pair now; what depends on it is loaded after the K loop, so the loop does not
         // start behind a chain of dependent loads
-        const int pr = tid < t.real_rows ? ws.row_pair[t.row0 + tid] : -1;
+        int pr[RPT];
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) pr[u] = tid + u * C::NT < t.real_rows ? ws.row_pair[t.row0 + tid + u * C::NT] : -1;
         PipeOf<C, MA> p;
         p.nslot = I / 64;
         p.wave = __builtin_amdgcn_readfirstlane(wave);
@@ -789,16 +791,18 @@ struct L2Body {
         f32x16_t acc[MA][C::NI];
         k_loop<C, MA>(p, smem, smem + C::SLOT, smem + 2 * C::SLOT, smem + (C::SLOTS - 1) * C::SLOT, acc, lane);
 
-        if (tid < 32 * MA) {
-            int tok = -1, direct = 0;
-            float w = 0.0f;
-            if (pr >= 0 && pr < npairs) {
-                tok = pr / d.k;
-                w = topk_w ? topk_w[pr] : 1.0f;   // no weights: the L1 dgrad's combine into dx
-                direct = ws.tok_nloc[tok] == 1;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u)
+            if (tid + u * C::NT < 32 * MA) {
+                int tok = -1, direct = 0;
+                float w = 0.0f;
+                if (pr[u] >= 0 && pr[u] < npairs) {
+                    tok = pr[u] / d.k;
+                    w = topk_w ? topk_w[pr[u]] : 1.0f;   // no weights: the L1 dgrad's combine into dx
+                    direct = ws.tok_nloc[tok] == 1;
+                }
+                s_row[tid + u * C::NT] = make_int4(tok, __float_as_int(w), direct, 0);
             }
-            s_row[tid] = make_int4(tok, __float_as_int(w), direct, 0);
-        }
 
         // Epilogue through LDS (the ring is free after the K loop), GP 32-row groups per pass: the
         // waves drop their accumulators into a row-major fp32 tile, then each wave takes whole
@@ -1205,11 +1209,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void dgrad_tile_kernel(const uint16_
 using L1Tile = Tile<2, 8, 1, 4>;
 using L2Tile = Tile<2, 8, 1, 4>;
 using L2TileNarrow = Tile<1, 8, 1, 4>;
-// Nine-group L1 tiles (three ring slots: 288-row slots): an expert of 257-288 rows, about half
-// of them when rows per expert average 256, runs as one tile, so its weight panels stream once
-// instead of twice (two tiles of five and four groups).
+// Nine-group forward tiles (three ring slots: 288-row slots): an expert of 257-288 rows, about
+// half of them when rows per expert average 256, runs as one tile, so its weight panels stream
+// once instead of twice (two tiles of five and four groups).
 using L1TileNt = Tile<2, 9, 1, 3, true>;
-using L2TileNt = Tile<2, 8, 1, 4, true>;
+using L2TileNt = Tile<2, 9, 1, 3, true>;
 using L2TileNarrowNt = Tile<1, 8, 1, 4, true>;
 using WgTile = Tile<2, 8, 1, 3>;   // three ring slots measured slightly faster than four here
 // Few-rows dgrads: M tiles of up to 96 rows (an expert of the wide share in one tile, its weights
