@@ -58,8 +58,16 @@ def bf16_dev(u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+# headers every GEMM source includes (the tile schedule lives in moe_tiles.h)
+KERNEL_HEADERS = [os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", f) for f in ("moe_tiles.h", "moe_internal.h")]
+
+
 def kernel_source_hash(src=GEMM_SRC):
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 of the kernel source followed by the headers it includes."""
+    h = hashlib.sha256()
+    for f in [src] + KERNEL_HEADERS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, path=TRAFFIC_FILE, src=GEMM_SRC):
@@ -329,7 +337,7 @@ def bench_mx(a):
     log("generating %s inputs (seed 0)" % w.name)
     d = mw.inputs(w, 0)
     P = mw.local_pairs(w, d["topk_idx"])
-    bm = a.block_m or 64   # 64-row MX tiles: an expert's ~62 rows of this share in one tile, its weights streamed once
+    bm = a.block_m or 64   # MX tiles follow the real 32-row groups (an expert of this share in one tile) at any block_m
     shape = moe.make_shape(w.T, w.H, w.I, w.E, w.EL, w.k, block_m=bm, e_lo=w.e_lo)
     x = bf16_dev(d["x"])
     idx = torch.from_numpy(d["topk_idx"]).cuda()

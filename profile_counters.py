@@ -46,6 +46,18 @@ BWD = (("dgrad_tile_kernel<moe::(anonymous namespace)::TrTile",
        ("repack_t_kernel", "weight repack (many rows)"),
        ("rows_to_k_major_kernel", "row transforms of the weight-gradient operands"),
        ("dtopk_w_finish", "d(topk_w) finish"))
+KERNEL_HEADERS = [os.path.join(ROOT, "token_dispatch_grouped_route_amd", "csrc", f) for f in ("moe_tiles.h", "moe_internal.h")]
+
+
+def source_hash(src):
+    """First 16 hex digits of the sha256 of the kernel source followed by the headers it includes
+    (the same digest bench.py checks before it reports the traffic)."""
+    h = hashlib.sha256()
+    for f in [src] + KERNEL_HEADERS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
 VARIANTS = {
     "bf16": {"title": "DeepSeek-V3 share forward", "src": GEMM_SRC, "l1": "l1_kernel", "workload": "dsv3_share_fwd",
              "kinds": (("l1_kernel", "L1: dispatch gather + grouped GEMM + SwiGLU"),
@@ -278,7 +290,7 @@ def main():
         return
     l1 = rec.get(var["l1"])
     if l1:
-        out = {"kernel_source_sha256_16": hashlib.sha256(open(var["src"], "rb").read()).hexdigest()[:16],
+        out = {"kernel_source_sha256_16": source_hash(var["src"]),
                "workload": var["workload"],
                "hbm_bytes_per_launch": l1["read_bytes"] + l1["write_bytes"],
                "hbm_read_bytes_per_launch": l1["read_bytes"], "hbm_write_bytes_per_launch": l1["write_bytes"],

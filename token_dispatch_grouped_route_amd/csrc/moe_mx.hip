@@ -14,6 +14,7 @@
 //   Scale of (row or column x, 32-block b of the K step): the scale byte of lane x + 32 b.
 //   Accumulator: as the 32 x 32 bf16 MFMA (row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
 #include "moe_internal.h"
+#include "moe_tiles.h"
 
 namespace moe {
 namespace {
@@ -375,40 +376,52 @@ __device__ __forceinline__ void mx_k_loop(MxPipe<MG>& p, char* __restrict__ s0, 
 // the activation rows (codes [R_max, I] and scale bytes [R_max, I / 32] in ws.act).
 // L2: GEMM of the FP8 activation rows against the FP4 W2, then the combine of the bf16 path
 // (bf16(w * o) into y for a token's only local pair, fp32 w * o into its stage row otherwise).
-// A tile is BM = 32 MG rows; block_m (d.BM) is a multiple of it, so a tile lies in one expert's block.
-// L2 runs two waves per SIMD (at most 256 registers; its 64-row tiles then spill a few values
-// outside the K loop), which measured faster than one; L1 measured slower with two.
-template <int MG, bool L1>
-__global__ __launch_bounds__(kMxThreads, L1 ? 1 : 2) void mx_gemm_kernel(const uint8_t* __restrict__ a_codes,
-                                                             const uint8_t* __restrict__ a_scales,
-                                                             const uint8_t* __restrict__ wq,
-                                                             const uint8_t* __restrict__ wsc,
-                                                             const float* __restrict__ topk_w, Dims d, Ws ws,
-                                                             float clamp, uint16_t* __restrict__ y) {
-    using G = MxGemm<MG>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* const s0 = smem;
-    char* const s1 = smem + G::SLOT;
-    char* const s2 = smem + 2 * G::SLOT;
-    char* const s3 = smem + (kMxSlots - 1) * G::SLOT;   // the fourth slot (unused with three)
-    int4* s_row = reinterpret_cast<int4*>(smem + kMxSlots * G::SLOT);   // token (-1 padding), weight, single
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = L1 ? d.H : d.I, N = L1 ? 2 * d.I : d.H;
-    const int n_tiles = N / kMxBN;
-    const int npairs = d.T * d.k;
-    const int64_t R = min(static_cast<int64_t>(ws.meta[0]), ws.rows_cap);
-    const int total = static_cast<int>(R / G::BM) * n_tiles;
-    uint8_t* act_codes = reinterpret_cast<uint8_t*>(ws.act);
-    uint8_t* act_scales = act_codes + ws.rows_cap * d.I;
-    const uint8_t* zrow = reinterpret_cast<const uint8_t*>(ws.zeros);
-    MxPipe<MG> p;
-    p.nslot = K / kMxSK;
-    p.wave = wave;
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const int mt = tile / n_tiles, nt = tile - mt * n_tiles;   // N tiles of an M tile adjacent: its rows stay in L2
-        const int64_t row0 = static_cast<int64_t>(mt) * G::BM;
-        const int e = ws.tile_expert[row0 / d.BM];
-        if (e < 0 || e >= d.EL) continue;   // uniform per workgroup
+// Tiles come from the shared tile list (moe_tiles.h): up to MAXG real 32-row groups of one expert
+// (BM = 32 MG rows for a tile of MG groups), so an expert of the wide share (41-76 rows) is one
+// tile and its weights stream once, whatever block_m is.  The ring slots are sized for MAXG.  One
+// workgroup per CU: the LDS of three-group tiles allows one (tiles of at most two groups at two
+// workgroups per CU measured slower for L2, their tile loop spilling).
+template <int MAXG>
+struct MxSched {
+    static constexpr int NT = kMxThreads;
+    static constexpr int MAXMI = MAXG;
+    static constexpr int SLOT = MxGemm<MAXG>::SLOT;   // ring slot stride
+    static constexpr int LDS = MxGemm<MAXG>::LDS;
+};
+
+template <int MAXG, bool L1>
+struct MxBody {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    const uint8_t* wq;
+    const uint8_t* wsc;
+    const float* topk_w;
+    Dims d;
+    Ws ws;
+    float clamp;
+    uint16_t* y;
+    char* smem;
+
+    template <int MG>
+    __device__ __forceinline__ void run(const TileRef& t) {
+        using G = MxGemm<MG>;
+        constexpr int SLOT = MxSched<MAXG>::SLOT;
+        char* const s0 = smem;
+        char* const s1 = smem + SLOT;
+        char* const s2 = smem + 2 * SLOT;
+        char* const s3 = smem + (kMxSlots - 1) * SLOT;   // the fourth slot (unused with three)
+        int4* s_row = reinterpret_cast<int4*>(smem + kMxSlots * SLOT);   // token (-1 padding), weight, single
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int K = L1 ? d.H : d.I, N = L1 ? 2 * d.I : d.H;
+        const int npairs = d.T * d.k;
+        uint8_t* act_codes = reinterpret_cast<uint8_t*>(ws.act);
+        uint8_t* act_scales = act_codes + ws.rows_cap * d.I;
+        const uint8_t* zrow = reinterpret_cast<const uint8_t*>(ws.zeros);
+        MxPipe<MG> p;
+        p.nslot = K / kMxSK;
+        p.wave = wave;
+        const int nt = t.nt, e = t.e;
+        const int64_t row0 = t.row0;
         // sources (padding rows read the zero row)
 #pragma unroll
         for (int i = 0; i < G::A_DMA; ++i) {
@@ -433,14 +446,13 @@ __global__ __launch_bounds__(kMxThreads, L1 ? 1 : 2) void mx_gemm_kernel(const u
             p.b_src[g] = wq + grp * 1024 + lane * 16;
             p.bs_src[g] = wsc + grp * 64 + lane * 4;
         }
-        __syncthreads();   // the previous tile's epilogue is done with s_row
         if (tid < G::BM) {   // read in the epilogue, after the K loop's barriers
             const int pr = ws.row_pair[row0 + tid];
             const bool ok = pr >= 0 && pr < npairs;
-            const int t = ok ? pr / d.k : -1;
+            const int tok = ok ? pr / d.k : -1;
             const float w = ok && !L1 ? topk_w[pr] : 0.0f;
-            const int single = ok && !L1 ? (ws.tok_nloc[t] == 1) : 0;
-            s_row[tid] = make_int4(t, __float_as_int(w), single, 0);
+            const int single = ok && !L1 ? (ws.tok_nloc[tok] == 1) : 0;
+            s_row[tid] = make_int4(tok, __float_as_int(w), single, 0);
         }
         f32x16_t acc[MG][2];
         mx_k_loop<MG>(p, s0, s1, s2, s3, acc, lane);
@@ -492,34 +504,35 @@ __global__ __launch_bounds__(kMxThreads, L1 ? 1 : 2) void mx_gemm_kernel(const u
                 }
         }
     }
+};
+
+template <int MAXG, bool L1>
+__global__ __launch_bounds__(kMxThreads, 1) void mx_gemm_kernel(const uint8_t* __restrict__ a_codes,
+                                                             const uint8_t* __restrict__ a_scales,
+                                                             const uint8_t* __restrict__ wq,
+                                                             const uint8_t* __restrict__ wsc,
+                                                             const float* __restrict__ topk_w, Dims d, Ws ws,
+                                                             float clamp, uint16_t* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    MxBody<MAXG, L1> body{a_codes, a_scales, wq, wsc, topk_w, d, ws, clamp, y, smem};
+    run_tiles<MxSched<MAXG>>(d, ws, (L1 ? 2 * d.I : d.H) / kMxBN, body);
 }
 
-template <int MG, bool L1>
+template <int MAXG, bool L1>
 hipError_t mx_gemm_launch(const Dims& d, const uint8_t* ac, const uint8_t* as, const uint8_t* wq, const uint8_t* wsc,
                           const float* topk_w, const Ws& ws, float clamp, uint16_t* y, hipStream_t s) {
-    using G = MxGemm<MG>;
-    auto k = mx_gemm_kernel<MG, L1>;
-    if (G::LDS > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kMxThreads, G::LDS) != hipSuccess || per_cu <= 0)
-        per_cu = 1;
-    const int n_tiles = (L1 ? 2 * d.I : d.H) / kMxBN;
-    int64_t grid = static_cast<int64_t>(per_cu) * device_cu_count();
-    const int64_t tiles = ws.rows_cap / G::BM * n_tiles;
-    if (grid > tiles) grid = tiles;
-    if (grid < 1) grid = 1;
-    k<<<static_cast<int>(grid), kMxThreads, G::LDS, s>>>(ac, as, wq, wsc, topk_w, d, ws, clamp, y);
+    using S = MxSched<MAXG>;
+    auto k = mx_gemm_kernel<MAXG, L1>;
+    allow_lds(k, S::LDS);
+    k<<<persistent_grid(k, kMxThreads, S::LDS), kMxThreads, S::LDS, s>>>(ac, as, wq, wsc, topk_w, d, ws, clamp, y);
     return hipGetLastError();
 }
 
 template <bool L1>
 hipError_t mx_gemm(const Dims& d, const uint8_t* ac, const uint8_t* as, const uint8_t* wq, const uint8_t* wsc,
                    const float* topk_w, const Ws& ws, float clamp, uint16_t* y, hipStream_t s) {
-    // 32-row tiles for block_m 32; 64-row tiles otherwise (block_m is 64, 128 or 256)
-    if (d.BM == 32) return mx_gemm_launch<1, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
-    if (d.BM % 64 == 0) return mx_gemm_launch<2, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
-    return hipErrorInvalidValue;
+    if (d.EL > kMaxEL) return hipErrorInvalidValue;
+    return mx_gemm_launch<3, L1>(d, ac, as, wq, wsc, topk_w, ws, clamp, y, s);
 }
 
 int grid_for(int64_t items) {
