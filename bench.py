@@ -118,6 +118,50 @@ def cpu_baseline(w, d, budget_s=20.0):
             "sample": "%d of %d tokens (%d local pairs), fp64 per-token loop, %.1f s" % (len(sample), w.T, pairs, dt)}
 
 
+def cpu_baseline_bwd(w, d, budget_s=20.0):
+    """The oracle (test infrastructure) timed on the host cores on a bounded sample of the training
+    step: one local expert per oracle thread (its weight-gradient loop runs one expert per thread)
+    and a sample of the tokens routed to them; for those tokens the forward and the token-side
+    backward (dx, d(topk_w)), and dW1, dW2 of the sampled experts over the sampled tokens' rows (the
+    other routing ids set to -1, which the layer drops).  Credited with the step's algorithmic
+    FLOPs of that work: forward 6, L2 dgrad 2 and L1 dgrad 4 x H x I per local pair of the tokens,
+    dW2 2 and dW1 4 x H x I per kept pair."""
+    import oracle
+    idx, dy = d["topk_idx"], d["dy"]
+    local = (idx >= w.e_lo) & (idx < w.e_lo + w.EL)
+    rng = np.random.default_rng(0)
+    nthr = max(1, oracle.num_threads())
+    ex = rng.permutation(np.unique(idx[local] - w.e_lo))[:nthr]
+    on_ex = local & np.isin(idx - w.e_lo, ex)
+    toks = rng.permutation(np.nonzero(on_ex.any(axis=1))[0])
+    x, tw, W1, W2 = d["x"], d["topk_weights"], d["W1"], d["W2"]
+
+    def run(tk):
+        sub = np.full_like(idx, -1)
+        sub[tk] = np.where(on_ex[tk], idx[tk], -1)
+        t0 = time.perf_counter()
+        oracle.forward(x, idx, tw, W1, W2, E=w.E, e_lo=w.e_lo, tokens=tk)
+        oracle.backward_tokens(x, idx, tw, W1, W2, dy, E=w.E, e_lo=w.e_lo, tokens=tk)
+        oracle.backward(x, sub, tw, W1, W2, dy, E=w.E, e_lo=w.e_lo, experts=ex)
+        return time.perf_counter() - t0
+
+    # a run costs a + b x tokens (a: the experts' fp64 gradient arrays); calibrate on one and on
+    # two tokens per thread
+    n = min(len(toks), nthr)
+    t1, t2 = run(toks[:n]), run(toks[:2 * n])
+    per_tok = max((t2 - t1) / max(min(len(toks), 2 * n) - n, 1), 1e-6)
+    fixed = max(t1 - per_tok * n, 0.0)
+    n2 = int(min(len(toks), max(2 * n, (budget_s - fixed) / per_tok)))
+    sample = toks[:n2]
+    dt = run(sample)
+    pairs, kept = int(local[sample].sum()), int(on_ex[sample].sum())
+    flops = (12.0 * pairs + 6.0 * kept) * w.H * w.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "forward, dx, d(topk_w) of %d of %d tokens (%d local pairs); dW1, dW2 of %d of %d experts "
+                      "over their %d rows among those tokens; fp64 loops, %.1f s"
+                      % (len(sample), w.T, pairs, len(ex), w.EL, kept, dt)}
+
+
 def stage_rates(ms, flops, nbytes):
     t = ms / 1e3
     return {"ms": round(ms, 4), "tflops": round(flops / t / 1e12, 1),
@@ -291,6 +335,9 @@ def bench_backward(a):
         "stages_ms": {name: round(st_ms[j], 4) for j, (name, _) in enumerate(stages)},
         "roofline": roof,
     }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle, bounded sample of the training step)")
+        out["cpu_baseline"] = cpu_baseline_bwd(w, d)
     print(json.dumps(out), flush=True)
 
 
