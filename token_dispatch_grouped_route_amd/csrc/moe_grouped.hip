@@ -695,7 +695,8 @@ hipError_t l1_launch(const Dims& d, const uint16_t* x, const uint16_t* w1f, cons
                      float* hgu_out, hipStream_t s) {
     auto k = l1_kernel<C>;
     allow_lds(k, C::LDS_BYTES);
-    k<<<persistent_grid(k, C::NT, C::LDS_BYTES), C::NT, C::LDS_BYTES, s>>>(x, w1f, d, ws, act_out, hgu_out);
+    k<<<tile_grid(k, C::NT, C::LDS_BYTES, d, C::MAXMI, 2 * d.I / C::BN), C::NT, C::LDS_BYTES, s>>>(x, w1f, d, ws, act_out,
+                                                                                            hgu_out);
     return hipGetLastError();
 }
 
@@ -704,7 +705,7 @@ hipError_t l2_launch(const Dims& d, const uint16_t* act, const uint16_t* w2f, co
                      uint16_t* y, hipStream_t s) {
     auto k = l2_kernel<C>;
     allow_lds(k, C::LDS_BYTES);
-    k<<<persistent_grid(k, C::NT, C::LDS_BYTES), C::NT, C::LDS_BYTES, s>>>(act, w2f, topk_w, d, ws, y);
+    k<<<tile_grid(k, C::NT, C::LDS_BYTES, d, C::MAXMI, d.H / C::BN), C::NT, C::LDS_BYTES, s>>>(act, w2f, topk_w, d, ws, y);
     return hipGetLastError();
 }
 
@@ -982,7 +983,7 @@ hipError_t dgrad_tile_launch(const Dims& d, const uint16_t* dy, const uint16_t* 
                              const Ws& ws, int fuse, bool topk_w_grad, hipStream_t s) {
     auto k = dgrad_tile_kernel<C>;
     allow_lds(k, C::LDS_BYTES);
-    k<<<persistent_grid(k, C::NT, C::LDS_BYTES), C::NT, C::LDS_BYTES, s>>>(dy, w2b, topk_w, d, ws, fuse,
+    k<<<tile_grid(k, C::NT, C::LDS_BYTES, d, C::MAXMI, d.I / C::BN), C::NT, C::LDS_BYTES, s>>>(dy, w2b, topk_w, d, ws, fuse,
                                                                            topk_w_grad ? 1 : 0);
     return hipGetLastError();
 }

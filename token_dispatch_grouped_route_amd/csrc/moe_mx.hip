@@ -524,7 +524,9 @@ hipError_t mx_gemm_launch(const Dims& d, const uint8_t* ac, const uint8_t* as, c
     using S = MxSched<MAXG>;
     auto k = mx_gemm_kernel<MAXG, L1>;
     allow_lds(k, S::LDS);
-    k<<<persistent_grid(k, kMxThreads, S::LDS), kMxThreads, S::LDS, s>>>(ac, as, wq, wsc, topk_w, d, ws, clamp, y);
+    const int n_tiles = (L1 ? 2 * d.I : d.H) / kMxBN;
+    k<<<tile_grid(k, kMxThreads, S::LDS, d, MAXG, n_tiles), kMxThreads, S::LDS, s>>>(ac, as, wq, wsc, topk_w, d, ws, clamp,
+                                                                                    y);
     return hipGetLastError();
 }
 

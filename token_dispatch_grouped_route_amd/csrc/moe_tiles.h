@@ -247,6 +247,24 @@ int persistent_grid(K kernel, int threads, size_t lds) {
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
+// Workgroups of a tile-list launch: persistent_grid, but no more than the tiles the launch can
+// hold (rounded up to a multiple of the XCD count), so a launch with few tiles does not start
+// workgroups that only look for work (each spends a round trip per chunk counter before it exits,
+// which set the duration of launches with a few tiles).  The local pairs (at most T * k) fill at
+// most ceil(T * k / 32) + EL groups of 32 rows, and tiles of up to m groups cut them into at most
+// ceil(groups / m) + EL M tiles (m = min(maxmi, 8): nine-group tiles are used only where they
+// replace tiles of eight).
+template <class K>
+int tile_grid(K kernel, int threads, size_t lds, const Dims& d, int maxmi, int n_tiles) {
+    const int g = persistent_grid(kernel, threads, lds);
+    const int m = maxmi < 8 ? maxmi : 8;
+    const int64_t groups = (static_cast<int64_t>(d.T) * d.k + 31) / 32 + d.EL;
+    const int64_t tiles = ((groups + m - 1) / m + d.EL) * n_tiles;
+    int64_t cap = (tiles + kXcds - 1) / kXcds * kXcds;
+    if (cap < kXcds) cap = kXcds;
+    return static_cast<int>(cap < g ? cap : g);
+}
+
 template <class K>
 void allow_lds(K kernel, size_t bytes) {
     static bool done[64] = {};   // per instantiation and device
