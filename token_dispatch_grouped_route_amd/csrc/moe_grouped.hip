@@ -34,11 +34,11 @@
 // through LDS, transposed (TrPipe); with many rows the dgrads take repacked weights and the weight
 // gradients transformed operands (wgrad_nt_kernel), all in registers.
 //
-// Schedule: a persistent grid of one workgroup per CU.  The tile list is ordered expert by
-// expert, then N tile by N tile with the M tiles of that panel adjacent, and cut into one
-// contiguous chunk per XCD (workgroup b runs on XCD b mod 8).  Workgroups take the next tile of
-// their XCD's chunk from an atomic counter, largest tiles first, and help other XCDs once their
-// own is done.
+// Schedule (moe_tiles.h): a persistent grid of one workgroup per CU, capped at the tiles the
+// shape allows.  The tile list is ordered expert by expert, then in blocks of eight M tiles, N
+// tile by N tile with the M tiles of that panel adjacent, and cut into one contiguous chunk per
+// XCD (workgroup b runs on XCD b mod 8).  Workgroups take the next tile of their XCD's chunk from
+// an atomic counter, largest tiles first, and help other XCDs once their own is done.
 #include <type_traits>
 
 #include "moe_internal.h"
