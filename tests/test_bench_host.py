@@ -41,3 +41,17 @@ def test_product_sources_never_reference_the_oracle():
                     if "oracle" in open(path, errors="replace").read():
                         hits.append(os.path.relpath(path, ROOT))
     assert not hits, hits
+
+
+def test_training_step_cpu_baseline_runs_on_a_small_workload():
+    """The training step's CPU baseline leg end to end on a reduced wide-expert share: a positive
+    rate, the host's thread count, and a sample no larger than the workload."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import moe_workloads as mw
+    w = mw.scaled(mw.get("wide_share_fwd_bwd"), T=96, H=128, I=64, E=16, EL=8, k=4)
+    r = bench.cpu_baseline_bwd(w, mw.inputs(w, 0), budget_s=0.5)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    n_tok = int(r["sample"].split(" of ")[1].split()[-1])
+    assert 1 <= n_tok <= w.T
