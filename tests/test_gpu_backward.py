@@ -271,6 +271,30 @@ def test_degenerate_routing_forward_and_backward(case):
         dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
         check_bf16(g1, dW1, TOL, "dW1 (%s)" % case)
         check_bf16(g2, dW2, TOL, "dW2 (%s)" % case)
+@pytest.mark.parametrize("bm", [32, 64])
+def test_weight_gradients_at_the_row_depth_boundaries(bm):
+    """Experts whose rows sit at the edges of the few-rows weight gradients' K depths: at most
+    one 64-deep step (64), a second, 32-deep step held in LDS with the first (65, 96), and the
+    general loop that reloads the LDS tiles per step (97), next to an expert without rows and one
+    with a single row."""
+    w = mw.Workload("wgrad_depths", T=200, H=256, I=128, E=8, EL=6, k=2, backward=True)
+    want = [64, 65, 96, 97, 0, 1]
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(want)])
+    ids = np.concatenate([ids, np.full(w.T * w.k - ids.size, w.E - 1, np.int32)])
+    ids = np.random.default_rng(15).permutation(ids).reshape(w.T, w.k)
+    d = dict(mw.inputs(w, 15), topk_idx=ids)
+    ns = run_forward_backward(w, d, bm)
+    assert tables(ns)["counts"][:w.EL].tolist() == want
+    args = (d["x"], ids, d["topk_weights"], d["W1"], d["W2"], d["dy"])
+    dW1, dW2 = oracle.backward(*args, E=w.E, e_lo=w.e_lo)
+    g1, g2 = unpacked(ns, ns.dW1p, ns.dW2p)
+    tag = "(row depths, bm %d)" % bm
+    check_bf16(g1, dW1, TOL, "dW1 " + tag)
+    check_bf16(g2, dW2, TOL, "dW2 " + tag)
+    assert np.all(g1[4] == 0.0) and np.all(g2[4] == 0.0), "expert without rows must get exact zeros"
+    check_token_grads(w, d, ns, np.arange(w.T), tag)
+
+
 def test_backward_is_graph_capturable():
     """The fused backward (dgrad with d(topk_w), dW2, dW1, dx) captured into a HIP graph replays
     bit-identically to the eager call, with eager work and a stale workspace between replays."""

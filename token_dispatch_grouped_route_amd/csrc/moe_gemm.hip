@@ -40,35 +40,49 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
+// A 32-deep tile has 64-byte rows, four of which span the banks: chunk c of row r sits at position
+// c ^ ((r >> 2) & 3), so the 16 rows of a 16-lane group again hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int lds_off32(int row, int chunk) {
+    return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+template <int KR>
+__device__ __forceinline__ int lds_off_k(int row, int chunk) {
+    static_assert(KR == BK || KR == 32, "tile depth");
+    if constexpr (KR == BK) return lds_off(row, chunk);
+    else return lds_off32(row, chunk);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Operand loaders
 // ---------------------------------------------------------------------------------------------
-// Operand tile of ROWS rows (the M or N index) x BK, stored in memory with the tile's index
+// Operand tile of ROWS rows (the M or N index) x KR (BK or 32), stored in memory with the tile's index
 // contiguous in runs of 8: elements (m .. m+7, k) = Src::chunk(k, m_base + m) for m a multiple of
 // 8.  Every chunk is a valid address (absent rows point at the workspace's
 // zero row), so the loads carry no branch and the compiler's wait counts stay exact: a load under
 // a branch makes it wait for every load in flight before the next one.
 // Unit u moves K rows 4*kq..4*kq+3 of the 16-byte column mc; kq varies fastest across lanes so
 // the transposed 8-byte LDS writes of a wave fill whole rows without bank conflicts.
-template <int ROWS, int NT, class Src>
+template <int ROWS, int NT, class Src, int KR = BK>
 struct TRows {
     static constexpr int MCH = ROWS / 8;
-    static constexpr int UNITS = MCH * (BK / 4);
+    static constexpr int UNITS = MCH * (KR / 4);
     static constexpr int PER = (UNITS + NT - 1) / NT;
     Src src;
     int m_base;
     u32x4 v[2][PER][4];
 
+    // K rows k0 .. k0 + KR - 1
     template <int S>
-    __device__ __forceinline__ void load(int kt, int tid) {
+    __device__ __forceinline__ void load(int k0, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int u = tid + i * NT;
             if (u < UNITS) {
-                const int kq = u % (BK / 4), mc = u / (BK / 4);
+                const int kq = u % (KR / 4), mc = u / (KR / 4);
                 const uint16_t* p[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = src.chunk(kt * BK + 4 * kq + r, m_base + 8 * mc);
+                for (int r = 0; r < 4; ++r) p[r] = src.chunk(k0 + 4 * kq + r, m_base + 8 * mc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[S][i][r] = *reinterpret_cast<const u32x4*>(p[r]);
             }
@@ -80,14 +94,14 @@ struct TRows {
         for (int i = 0; i < PER; ++i) {
             const int u = tid + i * NT;
             if (u < UNITS) {
-                const int kq = u % (BK / 4), mc = u / (BK / 4);
+                const int kq = u % (KR / 4), mc = u / (KR / 4);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int dw = j >> 1, sh = (j & 1) * 16;
                     const uint32_t k0 = (v[S][i][0][dw] >> sh) & 0xffffu, k1 = (v[S][i][1][dw] >> sh) & 0xffffu;
                     const uint32_t k2 = (v[S][i][2][dw] >> sh) & 0xffffu, k3 = (v[S][i][3][dw] >> sh) & 0xffffu;
                     uint2 out = make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
-                    *reinterpret_cast<uint2*>(lds + lds_off(8 * mc + j, kq >> 1) + (kq & 1) * 8) = out;
+                    *reinterpret_cast<uint2*>(lds + lds_off_k<KR>(8 * mc + j, kq >> 1) + (kq & 1) * 8) = out;
                 }
             }
         }
@@ -148,8 +162,11 @@ struct WgTok {
     static constexpr int FIX = 4;   // 32-wide blocks of the intermediate (LDS) tile dimension
     static constexpr int NT = 256;
     static constexpr int TILE_ROWS = 32 * FIX;                 // rows (M or N index) of each LDS tile
-    static constexpr int TILE_BYTES = TILE_ROWS * BK * 2;
-    static constexpr int LDS_BYTES = 2 * TILE_BYTES;           // hi and lo tiles
+    static constexpr int TILE_BYTES = TILE_ROWS * BK * 2;      // one 64-deep K step
+    static constexpr int KR1 = 32;                             // depth of the second, shallower step
+    static constexpr int TILE1_BYTES = TILE_ROWS * KR1 * 2;
+    static constexpr int KRES = BK + KR1;                      // expert rows the LDS holds at once
+    static constexpr int LDS_BYTES = 2 * (TILE_BYTES + TILE1_BYTES);   // hi and lo of both steps
     static constexpr int NFRAG = BK / 16;                      // one streamed fragment per substep
     static constexpr int CHUNK = 8;                            // output tiles per workgroup
 };
@@ -185,6 +202,9 @@ __global__ __launch_bounds__(256, 3) void wgrad_tok_kernel(const uint16_t* __res
     ll.m_base = lh.m_base;
     char* const lH = smem;
     char* const lL = smem + W::TILE_BYTES;
+    // the second step (expert rows BK .. KRES - 1) of an expert with more than BK rows
+    char* const lH1 = smem + 2 * W::TILE_BYTES;
+    char* const lL1 = lH1 + W::TILE1_BYTES;
 
     // substep f of K step kt of token tile t: the wave's 32 columns h of the tile; a substep past
     // the expert's rows reads the zero row instead
@@ -200,15 +220,27 @@ __global__ __launch_bounds__(256, 3) void wgrad_tok_kernel(const uint16_t* __res
         for (int f = 0; f < W::NFRAG; ++f) fr[slot][f] = *reinterpret_cast<const bf16x8_t*>(frag_addr(t, kt, f));
     };
     f32x16_t acc[W::FIX];
-    auto compute = [&](int slot) {
+    // the products of the fragments in `slot` with the LDS tiles of step 0 (64 deep) or of step 1
+    // (32 deep: its fragments past the second substep are never used)
+    auto compute = [&](int slot, int step) {
+        const int subs = step == 0 ? BK / 16 : W::KR1 / 16;
+        const char* const tH = step == 0 ? lH : lH1;
+        const char* const tL = step == 0 ? lL : lL1;
+        // opaque per call: the tiles do not change inside the tile loops, and reads the compiler
+        // hoists out of them would need registers for every substep at once
+        int row = lane & 31;
+        asm volatile("" : "+v"(row));
 #pragma unroll
         for (int sub = 0; sub < BK / 16; ++sub) {
+            if (sub >= subs) break;
             bf16x8_t hi[W::FIX], lo[W::FIX];
             const int ch = 2 * sub + (lane >> 5);
 #pragma unroll
             for (int i = 0; i < W::FIX; ++i) {
-                hi[i] = *reinterpret_cast<const bf16x8_t*>(lH + lds_off(i * 32 + (lane & 31), ch));
-                lo[i] = *reinterpret_cast<const bf16x8_t*>(lL + lds_off(i * 32 + (lane & 31), ch));
+                const int r = i * 32 + row;
+                const int off = step == 0 ? lds_off(r, ch) : lds_off32(r, ch);
+                hi[i] = *reinterpret_cast<const bf16x8_t*>(tH + off);
+                lo[i] = *reinterpret_cast<const bf16x8_t*>(tL + off);
             }
             const bf16x8_t f = fr[slot][sub];
 #pragma unroll
@@ -250,26 +282,52 @@ __global__ __launch_bounds__(256, 3) void wgrad_tok_kernel(const uint16_t* __res
         for (int t = wk.t0; t < wk.t1; t += 2) {
             load_frags(1, min(t + 1, wk.t1 - 1), 0);   // unconditional: exact wait counts
             zero();
-            if (nk == 1) compute(0);
+            if (nk == 1) compute(0, 0);
             store(t);
             if (t + 1 >= wk.t1) break;
             load_frags(0, min(t + 2, wk.t1 - 1), 0);
             zero();
-            if (nk == 1) compute(1);
+            if (nk == 1) compute(1, 0);
             store(t + 1);
+        }
+    } else if (count <= W::KRES) {
+        // both steps stay in LDS for the whole work item; a tile's second-step fragments are in
+        // flight while its first step multiplies, the next tile's first step while its second does
+        TRows<W::TILE_ROWS, W::NT, DirectRowSrc, W::KR1> lh1, ll1;
+        lh1.src = lh.src;
+        lh1.m_base = lh.m_base;
+        ll1.src = ll.src;
+        ll1.m_base = ll.m_base;
+        lh.template load<0>(0, tid);
+        ll.template load<0>(0, tid);
+        lh1.template load<0>(BK, tid);
+        ll1.template load<0>(BK, tid);
+        load_frags(0, wk.t0, 0);
+        lh.template store<0>(lH, tid);
+        ll.template store<0>(lL, tid);
+        lh1.template store<0>(lH1, tid);
+        ll1.template store<0>(lL1, tid);
+        lds_barrier();
+        for (int t = wk.t0; t < wk.t1; ++t) {
+            load_frags(1, t, 1);
+            zero();
+            compute(0, 0);
+            load_frags(0, min(t + 1, wk.t1 - 1), 0);   // unconditional: exact wait counts
+            compute(1, 1);
+            store(t);
         }
     } else {
         for (int t = wk.t0; t < wk.t1; ++t) {
             zero();
             for (int kt = 0; kt < nk; ++kt) {
-                lh.template load<0>(kt, tid);
-                ll.template load<0>(kt, tid);
+                lh.template load<0>(kt * BK, tid);
+                ll.template load<0>(kt * BK, tid);
                 load_frags(0, t, kt);
                 lds_barrier();   // every wave's reads of the previous step are done
                 lh.template store<0>(lH, tid);
                 ll.template store<0>(lL, tid);
                 lds_barrier();
-                compute(0);
+                compute(0, 0);
             }
             store(t);
         }
