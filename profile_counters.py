@@ -14,7 +14,7 @@ known / measured on that copy, so the figures are in true HBM bytes whatever uni
         --out-json gpurun_out/bwd.json PASS_DIR [...] > profiles/training_wide_share_counters.md
 
     python profile_counters.py stats TRACE_DIR --title TITLE --command CMD > profiles/<kernel>_<workload>_kernel_stats.md
-    python profile_counters.py occupancy --pass DIR WORKLOAD [--pass DIR WORKLOAD] > profiles/forward_..._occupancy.md
+    python profile_counters.py occupancy --pass DIR WORKLOAD [--pass DIR WORKLOAD] > profiles/forward_gemm_occupancy.md
 
 Writes the L1 launch's HBM bytes (read + write) with the hash of the kernel source they were taken
 on (bench.py reports them only while that source is unchanged) and prints a markdown table.  With
@@ -134,47 +134,75 @@ def stats_table(trace_dir, title, command, note, only=""):
             t / 1e6, 100.0 * t / total))
 
 
+def m_tiles_of(groups, max_groups):
+    """M tiles of an expert of `groups` 32-row groups on the forward tile list: tiles of at most
+    nine groups up to 18 groups and of eight beyond (bf16 GEMMs), of at most three (MX GEMMs)."""
+    if max_groups == 9:
+        return -(-groups // 9) if groups <= 18 else -(-groups // 8)
+    return -(-groups // max_groups)
+
+
+def occupancy_kind(name):
+    """The forward GEMM launches of a run: bf16 L1 / L2 (the transposed-B l2_kernel is the L1 dgrad
+    of a training step, not a forward launch) and the MX L1 / L2."""
+    if "mx_gemm_kernel" in name:
+        return "l1" if ", true>" in name else "l2"
+    if "l1_kernel" in name:
+        return "l1"
+    if "l2_kernel" in name and "TrTile" not in name:
+        return "l2"
+    return None
+
+
 def occupancy(dirs, workloads, command):
     """CU occupancy of the forward GEMM launches from SQ_WAVE_CYCLES (4-cycle units), SQ_BUSY_CYCLES
     (summed over the 32 shader engines) and GRBM_GUI_ACTIVE, one pass directory per workload, next
-    to the L1 tile list those workloads produce (M tiles of up to eight 32-row groups per expert, an
-    expert of g > 8 groups cut into ceil(g / 8) tiles of equal size, 256-column N tiles)."""
+    to the L1 tile list those workloads produce: each expert's 32-row groups cut evenly into M tiles
+    (m_tiles_of), 256-column N tiles.  A workload whose name contains "mx" is the MX forward (tiles
+    of at most three groups)."""
     sys.path.insert(0, ROOT)
     import numpy as np
     import moe_workloads as mw
-    print("# CU occupancy of the forward GEMMs: uniform against Zipf-skewed routing\n")
+    print("# CU occupancy of the forward GEMMs: tile lists and the tail of the persistent launches\n")
     if command:
         print("Commands (run from /tmp with TMPDIR=/tmp, repository at $R):\n\n```\n%s\n```\n" % command)
     print("Busy = 4 x SQ_WAVE_CYCLES / (4 waves x 256 CUs x kernel cycles), kernel cycles = SQ_BUSY_CYCLES / 32: "
           "the share of the launch during which a CU holds its persistent workgroup's waves.\n")
     print("| workload | local rows | largest expert | empty experts | L1 tiles by groups per M tile | L1 tiles per CU "
-          "| L1 busy | L2 busy | L1 kernel cycles |")
-    print("|---|---|---|---|---|---|---|---|---|")
+          "| L1 busy | L2 tiles per CU | L2 busy | L1 kernel cycles |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
     for d, name in zip(dirs, workloads):
         w = mw.get(name)
+        max_groups = 3 if "mx" in name else 9
         idx, _ = mw.routing(w, 0)
         ids = idx.reshape(-1).astype(np.int64)
         ids = ids[(ids >= w.e_lo) & (ids < w.e_lo + w.EL)] - w.e_lo
         counts = np.bincount(ids, minlength=w.EL)
         tiles = collections.Counter()
+        m_tiles = 0
         for g in (counts + 31) // 32:
             if g:
-                mt = -(-int(g) // 8)
-                tiles[-(-int(g) // mt)] += mt * (2 * w.I // 256)
+                mt = m_tiles_of(int(g), max_groups)
+                base, rem = divmod(int(g), mt)
+                tiles[base + 1] += rem * (2 * w.I // 256)
+                tiles[base] += (mt - rem) * (2 * w.I // 256)
+                m_tiles += mt
+        tiles = collections.Counter({q: n for q, n in tiles.items() if n})
         agg = collections.defaultdict(lambda: collections.defaultdict(list))
         for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
-            k = kind_of(r["Kernel_Name"])
-            if k in ("l1_kernel", "l2_kernel"):
+            k = occupancy_kind(r["Kernel_Name"])
+            if k:
                 agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
         busy, cyc = {}, {}
         for k, cs in agg.items():
             v = {c: sum(x) / len(x) for c, x in cs.items()}
             cyc[k] = v["SQ_BUSY_CYCLES"] / 32
             busy[k] = 4 * v["SQ_WAVE_CYCLES"] / (4 * 256 * cyc[k])
-        print("| %s | %d | %d | %d | %s | %.2f | %.1f%% | %.1f%% | %.0f |" % (
+        print("| %s | %d | %d | %d | %s | %.2f | %.1f%% | %.2f | %.1f%% | %.0f |" % (
             name, counts.sum(), counts.max(), int((counts == 0).sum()),
             ", ".join("%d: %d" % (q, n) for q, n in sorted(tiles.items())), sum(tiles.values()) / 256,
-            100 * busy.get("l1_kernel", float("nan")), 100 * busy.get("l2_kernel", float("nan")), cyc.get("l1_kernel", 0)))
+            100 * busy.get("l1", float("nan")), m_tiles * (w.H // 256) / 256, 100 * busy.get("l2", float("nan")),
+            cyc.get("l1", 0)))
 
 
 LATENCY_ORDER = ("SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_INST_LEVEL_LDS", "SQ_INST_LEVEL_VMEM",
