@@ -213,11 +213,12 @@ LATENCY_ORDER = ("SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_INST_LEV
 
 
 def latency(dirs, command, title):
-    """Memory-path table of the forward GEMMs (l1_kernel, l2_kernel) from the pass directories of
+    """Memory-path table of the forward GEMMs (l1_kernel, l2_kernel, or the MX ones) from the pass directories of
     the counters in LATENCY_ORDER: per-dispatch averages and the ratios derived from them."""
     c = read_counters(dirs)
-    ks = [k for k in ("l1_kernel", "l2_kernel") if k in c]
+    ks = [k for k in ("l1_kernel", "l2_kernel", "mx_l1", "mx_l2") if k in c]
     v = {k: c[k] for k in ks}
+    label = {"l1_kernel": "L1", "l2_kernel": "L2", "mx_l1": "MX L1", "mx_l2": "MX L2"}
     print("# rocprofv3 memory-path counters of the forward GEMMs (%s)\n" % title)
     if command:
         print("Commands (run from /tmp with TMPDIR=/tmp, repository at $R), one pass each:\n\n```\n%s\n```\n" % command)
@@ -235,13 +236,13 @@ def latency(dirs, command, title):
         x = v[k]
         cyc = x["SQ_BUSY_CYCLES"] / 32
         print("| %s | %.0f | %.0f%% | %.0f | %.0f%% | %.0f | %.0f%% | %.4f |" % (
-            "L1" if k == "l1_kernel" else "L2", cyc, 100 * x["TCP_PENDING_STALL_CYCLES_sum"] / 256 / cyc,
+            label[k], cyc, 100 * x["TCP_PENDING_STALL_CYCLES_sum"] / 256 / cyc,
             x["TCP_TCC_READ_REQ_LATENCY_sum"] / x["TCP_TCC_READ_REQ_sum"],
             100 * x["TCC_HIT_sum"] / (x["TCC_HIT_sum"] + x["TCC_MISS_sum"]),
             x["TCC_EA0_RDREQ_LEVEL_sum"] / x["TCC_EA0_RDREQ_sum"], 100 * x["SQ_WAIT_INST_ANY"] / x["SQ_WAVE_CYCLES"],
             x["SQ_LDS_BANK_CONFLICT"] / x["SQ_INSTS_LDS"]))
     print("\nRaw averages:\n")
-    print("| counter | " + " | ".join("L1" if k == "l1_kernel" else "L2" for k in ks) + " |")
+    print("| counter | " + " | ".join(label[k] for k in ks) + " |")
     print("|---|" + "---|" * len(ks))
     for n in LATENCY_ORDER:
         print("| %s | %s |" % (n, " | ".join("%.0f" % v[k].get(n, float("nan")) for k in ks)))
