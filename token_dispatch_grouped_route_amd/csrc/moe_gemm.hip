@@ -168,7 +168,9 @@ struct WgTok {
     static constexpr int KRES = BK + KR1;                      // expert rows the LDS holds at once
     static constexpr int LDS_BYTES = 2 * (TILE_BYTES + TILE1_BYTES);   // hi and lo of both steps
     static constexpr int NFRAG = BK / 16;                      // one streamed fragment per substep
-    static constexpr int CHUNK = 8;                            // output tiles per workgroup
+    // output tiles per workgroup (the LDS tiles are loaded once per workgroup); measured on the
+    // wide share: 4 for dW1 and 8 for dW2 (2, 6 and 8 for dW1, 4, 7 and 14 for dW2 slower)
+    static constexpr int CHUNK = A_TOK ? 4 : 8;
 };
 
 template <bool A_TOK>
