@@ -152,10 +152,12 @@ struct WgradWork {
 // transposes, and the intermediate operand (dhgu or w act, hi and lo) stays in LDS, loaded from its
 // row-major ws rows once per workgroup of CHUNK output tiles.  A 128 x 128 output tile streams one
 // bf16 operand tile (the other choice, streaming the hi/lo pair and keeping the token rows in LDS,
-// streams twice the bytes and measured 5% slower for dW1).  The fragments of tile t + 1 are in
-// flight while tile t multiplies and stores; with one K step of rows (the common case) nothing
-// synchronises the waves after the LDS tiles are loaded.  The four waves split the token dimension H (A_TOK, dW1: each 32 rows of M = H x
-// 128 dhgu columns; else dW2: 128 rows of M = I x 32 columns of N = H).  The dhgu tile is in its
+// streams twice the bytes and measured 5% slower for dW1).  The LDS holds the expert's first 64
+// rows and, for an expert of 65 to 96 rows, a second 32-deep step beside them, so up to 96 rows
+// (the common case) nothing synchronises the waves after the LDS tiles are loaded, and the next
+// fragments are in flight while the current ones multiply and store; more rows take a loop that
+// reloads the 64-deep tiles per step.  The four waves split the token dimension H (A_TOK, dW1:
+// each 32 rows of M = H x 128 dhgu columns; else dW2: 128 rows of M = I x 32 columns of N = H).  The dhgu tile is in its
 // logical [gate | up] column order, so dW1's stores map each 32-column group to its packed column.
 template <bool A_TOK>
 struct WgTok {
