@@ -332,7 +332,9 @@ int32_t moe_mx_pack_weights(const moe_shape* shape, const uint16_t* w1, const ui
  *   xq [device] uint8 [T, H], xs [device] uint8 [T, H / 32]  (moe_mx_cast_fp8 of x)
  *   w1q, w1s, w2q, w2s [device]                              (moe_mx_pack_weights)
  *   topk_idx, topk_w, ws, y as for moe_forward.  The act region of ws holds the FP8 activation
- *   codes [R_max, I] followed by their scale bytes [R_max, I / 32].
+ *   codes [R_max, I] followed by their scale bytes slot-major, [I / 256][R_max][8]: byte b of row r
+ *   in slot j is the scale of columns 32 (8 j + b) .. 32 (8 j + b) + 31 of row r (0 for a padding
+ *   row of a tile).  The stage region is scratch (x's scale bytes in row order during L1).
  * H and I must be multiples of 256.
  */
 int32_t moe_forward_mx(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs, const int32_t* topk_idx,

@@ -124,11 +124,13 @@ def mx_layer(w, d, bm, x_scale=1.0, experts=None):
 
 def gpu_act(ws, s, w):
     """The FP8 activation rows the MX forward leaves in the workspace's act region (codes
-    [R_max, I], then scales [R_max, I / 32]) and the pair id of each row."""
+    [R_max, I], then the scale bytes slot-major, [I / 256][R_max][8]), as [R_max, I] codes and
+    [R_max, I / 32] scales, and the pair id of each row."""
     L = moe.workspace_layout(s)
     R, off = L["rows_capacity"], L["act"]
     codes = ws[off:off + R * w.I].cpu().numpy().reshape(R, w.I)
-    scales = ws[off + R * w.I:off + R * w.I + R * (w.I // 32)].cpu().numpy().reshape(R, w.I // 32)
+    slots = ws[off + R * w.I:off + R * w.I + R * (w.I // 32)].cpu().numpy().reshape(w.I // 256, R, 8)
+    scales = np.ascontiguousarray(slots.transpose(1, 0, 2)).reshape(R, w.I // 32)
     return codes, scales, moe.ws_region(ws, s, "row_pair").cpu().numpy()
 
 

@@ -117,6 +117,26 @@ __global__ __launch_bounds__(256) void cast_fp8_kernel(int64_t nblocks, const ui
 }
 
 // ---------------------------------------------------------------------------------------------
+// x's scale bytes in dispatch-row order for L1, slot-major: [H / 256][R_max][8], row r holding the
+// eight bytes (one 256-deep K slot) of its pair's token, a row no pair takes zeros.  One slot's
+// scales of 32 consecutive rows are then 256 contiguous bytes, where the token rows would put
+// each in a cache line of its own.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_scales_kernel(Dims d, Ws ws, const uint8_t* __restrict__ xs,
+                                                            uint8_t* __restrict__ out) {
+    const int64_t R = ws.rows_cap, n = R * (d.H / 256), npairs = static_cast<int64_t>(d.T) * d.k;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t j = i / R, r = i - j * R;   // consecutive threads: consecutive rows of one slot
+        const int pr = ws.row_pair[r];
+        uint2 v = make_uint2(0u, 0u);
+        if (pr >= 0 && pr < npairs)
+            v = *reinterpret_cast<const uint2*>(xs + static_cast<int64_t>(pr / d.k) * (d.H / 32) + 8 * j);
+        *reinterpret_cast<uint2*>(out + i * 8) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // FP4 pack of the weights: one (expert, output column, 32-block along K) per thread
 // ---------------------------------------------------------------------------------------------
 // Packed layout (per expert, N output columns, reduction length K, K a multiple of 256): the data
@@ -204,7 +224,8 @@ struct MxGemm {
 template <int MG>
 struct MxPipe {
     const char* a_src[MxGemm<MG>::A_DMA];   // the lane's chunk of its row of DMA load i, at K 0
-    const uint8_t* as_src[MG];              // scale bytes of row 32 mi + lane % 32, at K 0
+    const uint8_t* as_src[MG];              // scale bytes of row 32 mi + lane % 32, slot 0
+    int64_t as_slot;                        // bytes from one slot's scale rows to the next's
     const uint8_t* b_src[2];                // the lane's 16 bytes of group g's block, K step 0
     const uint8_t* bs_src[2];               // the lane's scale dword of group g, slot 0
     uint4 b[kMxSlots][2][4];
@@ -230,7 +251,7 @@ struct MxPipe {
         }
         if (q == 1) {
 #pragma unroll
-            for (int mi = 0; mi < MG; ++mi) as[buf][mi] = *reinterpret_cast<const uint2*>(as_src[mi] + jj * 8);
+            for (int mi = 0; mi < MG; ++mi) as[buf][mi] = *reinterpret_cast<const uint2*>(as_src[mi] + jj * as_slot);
         }
     }
     static constexpr int loads(int q) {
@@ -431,14 +452,11 @@ struct MxBody {
             const uint8_t* src = !ok ? zrow : (L1 ? a_codes + static_cast<int64_t>(pr / d.k) * K : a_codes + (row0 + r) * K);
             p.a_src[i] = reinterpret_cast<const char*>(src) + 16 * ((lane & 15) ^ (r & 15));
         }
+        // scale bytes by row, slot-major ([K / 256][R_max][8]: x's gathered into row order, the
+        // activation's as L1 writes them), so a slot's scales of 32 rows are 256 contiguous bytes
+        p.as_slot = static_cast<int64_t>(ws.rows_cap) * 8;
 #pragma unroll
-        for (int mi = 0; mi < MG; ++mi) {
-            const int r = 32 * mi + (lane & 31);
-            const int pr = ws.row_pair[row0 + r];
-            const bool ok = pr >= 0 && pr < npairs;
-            p.as_src[mi] = !ok ? zrow
-                               : (L1 ? a_scales + static_cast<int64_t>(pr / d.k) * (K / 32) : a_scales + (row0 + r) * (K / 32));
-        }
+        for (int mi = 0; mi < MG; ++mi) p.as_src[mi] = a_scales + (row0 + 32 * mi + (lane & 31)) * 8;
         const int64_t ebase = static_cast<int64_t>(e) * (N / 32) * (K / 64);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
@@ -478,11 +496,14 @@ struct MxBody {
                     for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
                     const int E = block_exponent(amax, 1.75f, 8);
                     const uint32_t code = fp8_code(a * pow2f(-E));
-                    if (s_row[rl].x >= 0) {
-                        const int64_t row = row0 + rl;
-                        act_codes[row * d.I + col] = static_cast<uint8_t>(code);
-                        if ((lane & 31) == 0) act_scales[row * (d.I / 32) + q] = static_cast<uint8_t>(E + 127);
-                    }
+                    const int64_t row = row0 + rl;
+                    const bool real = s_row[rl].x >= 0;
+                    if (real) act_codes[row * d.I + col] = static_cast<uint8_t>(code);
+                    // slot-major like the gathered x scales; a padding row gets scale byte 0
+                    // (L2 reads its codes from the zero row)
+                    if ((lane & 31) == 0)
+                        act_scales[((q >> 3) * static_cast<int64_t>(ws.rows_cap) + row) * 8 + (q & 7)] =
+                            real ? static_cast<uint8_t>(E + 127) : static_cast<uint8_t>(0);
                 }
         } else {
 #pragma unroll
@@ -554,7 +575,17 @@ hipError_t launch_mx_cast_fp8(int64_t rows, int cols, const uint16_t* x, uint8_t
 
 hipError_t launch_mx_gemm1(const Dims& d, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q, const uint8_t* w1s,
                            const Ws& ws, float clamp, hipStream_t s) {
-    return mx_gemm<true>(d, xq, xs, w1q, w1s, nullptr, ws, clamp, nullptr, s);
+    // the gathered scales (R_max * H / 32 bytes) go into ws stage (4 * R_max * H bytes), which L2's
+    // combine rows reuse only after L1
+    if (!ws.stage) return hipErrorInvalidValue;
+    uint8_t* rs = reinterpret_cast<uint8_t*>(ws.stage);
+    const int64_t n = static_cast<int64_t>(ws.rows_cap) * (d.H / 256);
+    if (n > 0) {
+        gather_scales_kernel<<<grid_for(n), 256, 0, s>>>(d, ws, xs, rs);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return mx_gemm<true>(d, xq, rs, w1q, w1s, nullptr, ws, clamp, nullptr, s);
 }
 
 hipError_t launch_mx_gemm2(const Dims& d, const uint8_t* w2q, const uint8_t* w2s, const float* topk_w, const Ws& ws,
