@@ -454,7 +454,8 @@ def bench_mx(a):
         roof = {"bound": "mfma", "achieved": l1_flops / l1_s / 1e12, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": l1_flops / l1_s / 1e12 / PEAK_FP8_TFLOPS}
     roof.update({"traffic": measured_traffic(w.name, MX_TRAFFIC_FILE, MX_SRC),
-                 "kernel": "MX gemm1 (dispatch gather of FP8 x + L1 + clamped SwiGLU + FP8 cast)",
+                 "kernel": "MX gemm1 stage: x scale bytes into row order, then one launch of dispatch gather "
+                           "of FP8 x + L1 + clamped SwiGLU + FP8 cast",
                  "alg_bytes_per_launch": l1_bytes, "alg_flops_per_launch": l1_flops,
                  "intensity_flop_per_byte": round(l1_flops / l1_bytes, 1),
                  "hbm_frac": l1_bytes / l1_s / 1e9 / PEAK_HBM_GBS,

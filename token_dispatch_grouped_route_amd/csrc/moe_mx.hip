@@ -118,13 +118,15 @@ __global__ __launch_bounds__(256) void cast_fp8_kernel(int64_t nblocks, const ui
 
 // ---------------------------------------------------------------------------------------------
 // x's scale bytes in dispatch-row order for L1, slot-major: [H / 256][R_max][8], row r holding the
-// eight bytes (one 256-deep K slot) of its pair's token, a row no pair takes zeros.  One slot's
-// scales of 32 consecutive rows are then 256 contiguous bytes, where the token rows would put
-// each in a cache line of its own.
+// eight bytes (one 256-deep K slot) of its pair's token, a padding row zeros; only the rows the
+// prologue laid out (meta[0]) are written, the ones the tiles read.  One slot's scales of 32
+// consecutive rows are then 256 contiguous bytes, where the token rows would put each in a cache
+// line of its own.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gather_scales_kernel(Dims d, Ws ws, const uint8_t* __restrict__ xs,
                                                             uint8_t* __restrict__ out) {
-    const int64_t R = ws.rows_cap, n = R * (d.H / 256), npairs = static_cast<int64_t>(d.T) * d.k;
+    const int64_t cap = ws.rows_cap, npairs = static_cast<int64_t>(d.T) * d.k;
+    const int64_t R = min(static_cast<int64_t>(max(ws.meta[0], 0)), cap), n = R * (d.H / 256);
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int64_t j = i / R, r = i - j * R;   // consecutive threads: consecutive rows of one slot
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(Dims d, Ws ws, const
         uint2 v = make_uint2(0u, 0u);
         if (pr >= 0 && pr < npairs)
             v = *reinterpret_cast<const uint2*>(xs + static_cast<int64_t>(pr / d.k) * (d.H / 32) + 8 * j);
-        *reinterpret_cast<uint2*>(out + i * 8) = v;
+        *reinterpret_cast<uint2*>(out + (j * cap + r) * 8) = v;
     }
 }
 
@@ -579,9 +581,10 @@ hipError_t launch_mx_gemm1(const Dims& d, const uint8_t* xq, const uint8_t* xs, 
     // combine rows reuse only after L1
     if (!ws.stage) return hipErrorInvalidValue;
     uint8_t* rs = reinterpret_cast<uint8_t*>(ws.stage);
-    const int64_t n = static_cast<int64_t>(ws.rows_cap) * (d.H / 256);
+    const int64_t n = static_cast<int64_t>(ws.rows_cap) * (d.H / 256);   // at most; the kernel reads R
     if (n > 0) {
-        gather_scales_kernel<<<grid_for(n), 256, 0, s>>>(d, ws, xs, rs);
+        const int grid = std::min(grid_for(n), 2 * device_cu_count());
+        gather_scales_kernel<<<grid, 256, 0, s>>>(d, ws, xs, rs);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
