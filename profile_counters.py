@@ -11,7 +11,7 @@ known / measured on that copy, so the figures are in true HBM bytes whatever uni
         --out-json profiles/mx_gemm1_wide_share_traffic.json PASS_DIR [...] > profiles/forward_mx_wide_share_counters.md
     python profile_counters.py latency PASS_DIR [...] > profiles/forward_dsv3_share_latency_counters.md
     python profile_counters.py --variant bwd --workload wide_share_fwd_bwd --trace TRACE_DIR \
-        --out-json gpurun_out/bwd.json PASS_DIR [...] > profiles/training_wide_share_counters.md
+        --out-json OUT.json PASS_DIR [...] > profiles/training_wide_share_counters.md
 
     python profile_counters.py stats TRACE_DIR --title TITLE --command CMD > profiles/<kernel>_<workload>_kernel_stats.md
     python profile_counters.py occupancy --pass DIR WORKLOAD [--pass DIR WORKLOAD] > profiles/forward_gemm_occupancy.md
